@@ -1,0 +1,235 @@
+"""Throughput of batched speculative-sampling verification on one MI355X.
+
+One step = one spec_verify call (statistics pass over every target and draft
+row, accept / first-reject, residual or bonus draw) over one batch of the
+bf16 headline workload: B=64 sequences, gamma=8 drafted tokens, V=128256,
+temperature 0.8. Inputs are seeded synthetic logits already resident in HBM;
+two input sets alternate so that every step reads data the previous step did
+not touch (each set is 279 MB, above the 256 MB last-level cache).
+
+Prints one JSON line: verified draft rows/s (B*gamma per step), the statistics
+kernel's achieved HBM bandwidth against the 8 TB/s peak, and the fp64 CPU
+oracle timed on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "verified draft rows/sec and achieved HBM GB/s (% of peak) at B=64,γ=8,V=128256"
+PEAK_HBM_GBPS = 8000.0
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime's C API (timing plumbing)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        self.hip.hipEventSynchronize(ctypes.c_void_p(b))
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(inp, seed, sample_b, gpu_tokens=None, gpu_n=None, reps=3):
+    """The fp64 oracle, as it stands, on the first `sample_b` sequences of the
+    workload (same seed, same b indices), timed on the host cores."""
+    import oracle
+    from oracle.compare import compare_tokens
+    wl = inp.wl.scaled(B=sample_b)
+    sub = W.Inputs(wl, inp.seed, inp.target[:sample_b], inp.draft[:sample_b], inp.tokens[:sample_b])
+    oracle.lib()
+    times = []
+    res = None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        res = oracle.verify(sub.target, sub.draft if wl.T > 0 else None, sub.tokens, wl.dtype, wl.T, seed,
+                            diag=True)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    out = {"value": sample_b * wl.gamma / t, "unit": "verified draft rows/s", "cores": oracle.max_threads(),
+           "kind": "oracle",
+           "sample": f"first {sample_b} of {inp.wl.B} sequences of the timed workload, median of {reps} runs "
+                     f"({t:.2f} s per run, fp64, OpenMP over sequences)"}
+    if gpu_tokens is not None:
+        rep = compare_tokens(sub, res, gpu_tokens[:sample_b], gpu_n[:sample_b], seed)
+        out["parity_vs_gpu"] = {"hard_failures": len(rep.hard_fail), "near_boundary": rep.mismatches,
+                                "draws": rep.draws}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default=W.HEADLINE, choices=list(W.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the oracle sample (0: auto)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the verification step has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_sampling_verification_05_amd as sv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    tdt = torch.float32 if wl.dtype == W.F32 else torch.bfloat16
+
+    def to_dev(a):
+        if wl.dtype == W.BF16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+        return torch.from_numpy(a).to(dev)
+
+    t_gen = time.perf_counter()
+    sets, host0 = [], None
+    for k in range(args.sets):
+        inp = W.make_inputs(wl, args.seed + k)
+        if k == 0:
+            host0 = inp
+        sets.append((to_dev(inp.target), to_dev(inp.draft), torch.from_numpy(inp.tokens).to(dev)))
+        print(f"[bench] input set {k} ready ({time.perf_counter() - t_gen:.1f} s)", file=sys.stderr, flush=True)
+    B, g, V = wl.B, wl.gamma, wl.V
+    outs = [(torch.empty((B, g + 1), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+            for _ in range(args.sets)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    dtc = sv.SPEC_F32 if wl.dtype == W.F32 else sv.SPEC_BF16
+
+    def call(step, extras=None):
+        tgt, dft, tok = sets[step % args.sets]
+        ot, on = outs[step % args.sets]
+        rc = sv.verify_raw(tgt.data_ptr(), dft.data_ptr(), tok.data_ptr(), B, g, V, dtc, wl.T,
+                           args.seed + (step % args.sets), ot.data_ptr(), on.data_ptr(), sh, extras)
+        if rc != 0:
+            raise RuntimeError(f"spec_verify returned {rc}: {sv.last_error()}")
+
+    hip = HipEvents()
+    K, Wm = args.steps, args.warmup
+    for s in range(Wm):
+        call(s)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({Wm} steps)", file=sys.stderr, flush=True)
+
+    # timed region: K steps; HIP events around the statistics kernel of every step
+    ev = hip.create(2 * K)
+    extras = [sv.Extras() for _ in range(K)]
+    for i, e in enumerate(extras):
+        e.events[0] = ev[2 * i]
+        e.events[1] = ev[2 * i + 1]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(K):
+        call(Wm + s, extras[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    k1_ms = [hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]
+    hip.destroy(ev)
+    ms_per_step = total_ms / K
+
+    # kernel split (a separate pass with all five events per step; not the timed value)
+    nsplit = min(K, 100)
+    ev5 = hip.create(5 * nsplit)
+    ex5 = [sv.Extras() for _ in range(nsplit)]
+    for i, e in enumerate(ex5):
+        for j in range(5):
+            e.events[j] = ev5[5 * i + j]
+    torch.cuda.synchronize()
+    for s in range(nsplit):
+        call(s, ex5[s])
+    torch.cuda.synchronize()
+    names = ["stats", "accept", "resid_sums", "draw"] if wl.T > 0 else ["argmax", "accept"]
+    split = {}
+    for j, nm in enumerate(names):
+        split[nm] = float(np.mean([hip.ms(ev5[5 * i + j], ev5[5 * i + j + 1]) for i in range(nsplit)])) * 1e3
+    hip.destroy(ev5)
+
+    rows_per_step = B * g
+    value = rows_per_step / (ms_per_step * 1e-3)
+    compulsory = wl.compulsory_bytes()
+    read_bytes = wl.bytes_read()
+    k1_avg_ms = float(np.mean(k1_ms))
+    achieved = read_bytes / (k1_avg_ms * 1e-3) / 1e9
+    call_gbps = compulsory / (ms_per_step * 1e-3) / 1e9
+
+    # one validation of the last outputs of set 0 against the oracle (outside the timed region)
+    call(0)
+    torch.cuda.synchronize()
+    gpu_t = outs[0][0].cpu().numpy()
+    gpu_n = outs[0][1].cpu().numpy()
+    n_hist = np.bincount(gpu_n[gpu_n >= 0], minlength=g + 1).tolist()
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verified draft rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "gamma": g, "V": V, "temperature": wl.T,
+                   "logits": W.DTYPE_NAMES[wl.dtype], "input_sets": args.sets},
+        "call_gbps": call_gbps,
+        "call_hbm_frac": call_gbps / PEAK_HBM_GBPS,
+        "kernel_us": split,
+        "accepted_hist": n_hist,
+        "roofline": {"bound": "hbm", "kernel": "k_stats" if wl.T > 0 else "k_argmax",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "bytes_per_launch": read_bytes, "avg_launch_us": k1_avg_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or min(B, 64)
+        result["cpu_baseline"] = cpu_baseline(host0, args.seed, sample, gpu_t, gpu_n)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

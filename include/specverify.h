@@ -1,0 +1,146 @@
+/* specverify.h - C ABI of libspecverify: batched speculative-sampling
+ * verification on one AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (pages cited by title and section):
+ *  [Ch15] "Chapter 15: Decoding acceleration techniques" (zsc.github.io, LLM
+ *         edge inference), 15.1.2 "The mathematical framework of speculative
+ *         decoding": step 2 (one target pass scores every drafted position;
+ *         p_i = softmax(logits of row i)), step 3 (accept draft token i with
+ *         probability min(1, p_i/q_i); stop at the first rejection), step 4
+ *         (at the rejected row resample from max(0, p - q)/Z), and the main
+ *         theorem (the emitted tokens are distributed as p).
+ *  [CSDN] devpress.csdn.net speculative-inference post, 2.1: the same loop as
+ *         a PyTorch listing, returning the emitted tokens and the accepted count.
+ *  [HSD]  "LLM inference optimisation: hidden-state speculative decoding"
+ *         (jsqmd.com), 3.3: after full acceptance the target's last row yields
+ *         one more (bonus) token.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees or retains them. Rows are contiguous and row-major.
+ *  - dtype: SPEC_F32 (float) or SPEC_BF16 (bfloat16 bits, uint16). Both logits
+ *    tensors share it.
+ *  - stream: a hipStream_t passed as void* (NULL = the legacy default
+ *    stream). Every kernel is enqueued on it and the call returns without
+ *    waiting; buffers must stay alive until the stream reaches the work.
+ *  - Randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key =
+ *    (seed low 32 bits, seed high 32 bits) and counter (b, i, purpose, 0);
+ *    purpose 0 = accept test at position i, purpose 1 = correction draw at the
+ *    rejected row k or the bonus draw (i = k = gamma). The uniform is
+ *    ((x1 << 32 | x0) >> 11) * 2^-53 in [0, 1). Results are a pure function of
+ *    (inputs, seed): no state is carried between calls.
+ *  - Host-detectable errors return a negative status before anything is
+ *    launched; spec_verify_last_error() gives the message (thread-local).
+ *    Input errors only visible on the device are reported in band: a sequence
+ *    whose verification reaches a position with an unusable row (NaN, +inf, or
+ *    no finite entry; at T > 0 both rows of the position, at T == 0 the target
+ *    row) or an out-of-range draft token gets out_n_accepted[b] = -1 and an
+ *    all -1 out_tokens row. -inf logits are legal (masked tokens).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = -1,  /* bad pointer, size, temperature or dtype combination */
+    SPEC_EDTYPE = -2,  /* dtype is neither SPEC_F32 nor SPEC_BF16 */
+    SPEC_EHIP = -3,    /* a HIP runtime call or kernel launch failed */
+    SPEC_ENOMEM = -4   /* the library's device workspace could not be allocated */
+} spec_status_t;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+
+#define SPEC_MAX_GAMMA 63
+
+/* spec_verify: one batched verification step ([Ch15] 15.1.2 steps 2-4,
+ * [CSDN] 2.1, bonus token [HSD] 3.3).
+ *
+ *  target_logits  [B, gamma+1, V] dtype. Row i < gamma scores draft token i;
+ *                 row gamma is the bonus row.
+ *  draft_logits   [B, gamma, V] dtype: row i is the distribution draft token i
+ *                 was drawn from. May be NULL iff temperature == 0.
+ *  draft_tokens   [B, gamma] int32.
+ *  B >= 1, 1 <= gamma <= SPEC_MAX_GAMMA, V >= 1.
+ *  temperature    > 0: p = softmax(target/T), q = softmax(draft/T), accept
+ *                 token i iff u_i < min(1, p_i(x_i)/q_i(x_i)) (alpha = 0 when
+ *                 p_i(x_i) = 0, 1 when q_i(x_i) = 0 < p_i(x_i)); at the first
+ *                 rejected row k draw from max(0, p_k - q_k)/Z (from p_k if Z
+ *                 rounds to 0); if none is rejected draw the bonus token from
+ *                 p_gamma. A draw takes the smallest j whose ascending
+ *                 cumulative mass exceeds u*Z.
+ *                 == 0: greedy; accept while draft token i equals the argmax of
+ *                 target row i (lowest index on ties), then emit that argmax
+ *                 (the bonus row's argmax when all are accepted).
+ *                 < 0 or NaN: SPEC_EINVAL.
+ *  seed           Philox key.
+ *  out_tokens     [B, gamma+1] int32: the n accepted draft tokens, then the
+ *                 correction (or bonus) token, then -1 padding.
+ *  out_n_accepted [B] int32: n in 0..gamma, or -1 (invalid input, see above).
+ *  Returns SPEC_OK or a negative spec_status_t. The library keeps a device
+ *  workspace per (device, stream), grown on demand under a lock; concurrent
+ *  calls on different streams are safe, calls on one stream are ordered. */
+int spec_verify(const void* target_logits, const void* draft_logits,
+                const int32_t* draft_tokens, int32_t B, int32_t gamma, int32_t V,
+                int32_t dtype, float temperature, uint64_t seed,
+                int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
+
+/* Optional extras of spec_verify_ex. Every pointer may be NULL; device
+ * pointers unless stated. */
+typedef struct {
+    float* row_max;        /* [B, 2*gamma+1]: max logit of target rows 0..gamma, then
+                              draft rows 0..gamma-1 (T > 0: every row; T == 0: target
+                              rows only, draft slots untouched) */
+    double* row_sumexp;    /* [B, 2*gamma+1]: sum_j exp((l_j - max)/T) (T > 0 only) */
+    double* p_draft;       /* [B, gamma]: p_i(x_i) (T > 0; NaN if the position is unusable) */
+    double* q_draft;       /* [B, gamma]: q_i(x_i) */
+    double* Z;             /* [B]: residual mass at row k, or sum of p at the bonus row
+                              (T > 0 only; NaN for an invalid sequence) */
+    int32_t* argmax;       /* [B, gamma+1]: argmax of each target row (T == 0 only) */
+    int64_t b_offset;      /* added to b in the Philox counter, so that a shard of a
+                              larger batch draws the same uniforms as the whole batch */
+    void* events[5];       /* optional hipEvent_t (host handles) recorded on `stream`:
+                              [0] before the statistics kernel, [1] after it, [2] after
+                              the accept kernel, [3] after the residual-sum kernel,
+                              [4] after the draw kernel (T > 0) */
+} spec_extras_t;
+
+/* spec_verify with extras (NULL extras == spec_verify). Same kernels. */
+int spec_verify_ex(const void* target_logits, const void* draft_logits,
+                   const int32_t* draft_tokens, int32_t B, int32_t gamma, int32_t V,
+                   int32_t dtype, float temperature, uint64_t seed,
+                   int32_t* out_tokens, int32_t* out_n_accepted, void* stream,
+                   const spec_extras_t* extras);
+
+/* spec_row_stats: the softmax statistics pass alone ([Ch15] 15.1.2 step 2).
+ *  logits [rows, V] dtype; T > 0.
+ *  row_max [rows] float  : max_j l_j;
+ *  row_sumexp [rows] double : sum_j exp((l_j - row_max)/T); NaN when the row
+ *  holds NaN or +inf or no finite entry. Same kernel as spec_verify. */
+int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype,
+                   float temperature, float* row_max, double* row_sumexp, void* stream);
+
+/* Bytes of device workspace one call of this shape needs (the library
+ * allocates and owns it). */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
+                                   float temperature);
+
+/* Frees every cached workspace after synchronising the streams that own them. */
+void spec_verify_release_workspace(void);
+
+/* Message of the last non-OK return on this thread ("" if none). */
+const char* spec_verify_last_error(void);
+
+/* ABI version: 1. */
+int32_t spec_verify_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,113 @@
+"""Element-by-element comparison of a verification result with the oracle.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark validation). The GPU
+result comes in as plain numpy arrays; nothing here imports the HIP path.
+
+Token parity rule (the tolerance the contract states): accepted counts and
+tokens are bit-exact, except for draws whose uniform lies within 1e-6 of a
+boundary of the oracle's decision (alpha for an accept draw; the emitted
+token's CDF interval for a correction or bonus draw). Such draws are counted,
+and must stay under 0.1% of all draws the oracle consumes. Any other
+disagreement fails outright. Greedy (T == 0) results must match exactly.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+from . import ACCEPT, SAMPLE, residual_cdf, uniform
+
+BAND = 1e-6
+
+
+@dataclasses.dataclass
+class TokenReport:
+    sequences: int = 0
+    accept_draws: int = 0
+    sample_draws: int = 0
+    accept_mismatch: int = 0
+    sample_mismatch: int = 0
+    hard_fail: list = dataclasses.field(default_factory=list)
+    max_boundary_dist: float = 0.0
+
+    @property
+    def draws(self):
+        return self.accept_draws + self.sample_draws
+
+    @property
+    def mismatches(self):
+        return self.accept_mismatch + self.sample_mismatch
+
+    def merge(self, o: "TokenReport"):
+        for f in ("sequences", "accept_draws", "sample_draws", "accept_mismatch", "sample_mismatch"):
+            setattr(self, f, getattr(self, f) + getattr(o, f))
+        self.hard_fail += o.hard_fail
+        self.max_boundary_dist = max(self.max_boundary_dist, o.max_boundary_dist)
+
+    def ok(self, max_rate=1e-3):
+        return not self.hard_fail and self.mismatches <= max_rate * max(self.draws, 1)
+
+    def __str__(self):
+        return (f"seqs={self.sequences} draws={self.draws} (accept {self.accept_draws}, sample "
+                f"{self.sample_draws}) near-boundary mismatches: accept {self.accept_mismatch}, "
+                f"sample {self.sample_mismatch}; max dist {self.max_boundary_dist:.2e}; "
+                f"hard failures {len(self.hard_fail)}")
+
+
+def compare_tokens(inp, orc, gpu_tokens, gpu_n, seed, b_offset=0) -> TokenReport:
+    """inp: workloads.Inputs; orc: oracle.Result with diagnostics."""
+    wl = inp.wl
+    g = wl.gamma
+    rep = TokenReport()
+    greedy = wl.T == 0.0
+    for b in range(wl.B):
+        ko, kg = int(orc.n[b]), int(gpu_n[b])
+        rep.sequences += 1
+        if ko >= 0 and not greedy:
+            rep.accept_draws += min(ko + 1, g)
+            rep.sample_draws += 1
+        if ko == kg and np.array_equal(orc.tokens[b], gpu_tokens[b]):
+            continue
+        if greedy or ko < 0 or kg < 0:
+            rep.hard_fail.append((b, "greedy/invalid mismatch", ko, kg))
+            continue
+        if ko != kg:
+            f = min(ko, kg)
+            u = uniform(seed, b + b_offset, f, ACCEPT)
+            alpha = orc.alpha[b, f]
+            dist = abs(u - alpha)
+            same_prefix = np.array_equal(orc.tokens[b, :f], gpu_tokens[b, :f])
+            if dist < BAND and same_prefix:
+                rep.accept_mismatch += 1
+                rep.max_boundary_dist = max(rep.max_boundary_dist, dist)
+            else:
+                rep.hard_fail.append((b, "accept", f, float(u), float(alpha), ko, kg))
+            continue
+        # same k: the accepted prefix must agree exactly; the drawn token may differ near a boundary
+        k = ko
+        if not np.array_equal(orc.tokens[b, :k], gpu_tokens[b, :k]) or \
+                not np.array_equal(orc.tokens[b, k + 1:], gpu_tokens[b, k + 1:]):
+            rep.hard_fail.append((b, "prefix/padding", k))
+            continue
+        j = int(gpu_tokens[b, k])
+        if not (0 <= j < wl.V):
+            rep.hard_fail.append((b, "token out of range", j))
+            continue
+        u = uniform(seed, b + b_offset, k, SAMPLE)
+        q_row = inp.draft[b, k] if k < g else None
+        _, cdf = residual_cdf(inp.target[b, k], q_row, wl.dtype, wl.T)
+        lo = cdf[j - 1] if j > 0 else 0.0
+        hi = cdf[j]
+        dist = 0.0 if lo <= u < hi else min(abs(u - lo), abs(u - hi))
+        if dist < BAND:
+            rep.sample_mismatch += 1
+            rep.max_boundary_dist = max(rep.max_boundary_dist, dist)
+        else:
+            rep.hard_fail.append((b, "sample", k, j, int(orc.tokens[b, k]), float(u), float(lo), float(hi)))
+    return rep
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.abs(a - b) / np.maximum(np.abs(b), 1e-300)

@@ -1,0 +1,186 @@
+"""Python binding of libspecverify (batched speculative-sampling verification on gfx950).
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels behind the C ABI declared in include/specverify.h. PyTorch provides
+device memory and the current stream. There is no fallback: if the shared
+library is missing, importing the entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EHIP, SPEC_ENOMEM = 0, -1, -2, -3, -4
+SPEC_F32, SPEC_BF16 = 0, 1
+MAX_GAMMA = 63
+
+# every symbol include/specverify.h declares
+EXPORTS = (
+    "spec_verify",
+    "spec_verify_ex",
+    "spec_row_stats",
+    "spec_verify_workspace_bytes",
+    "spec_verify_release_workspace",
+    "spec_verify_last_error",
+    "spec_verify_abi_version",
+)
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"spec_verify failed ({code}): {msg}")
+        self.code = code
+
+
+class Extras(ctypes.Structure):
+    """Mirror of spec_extras_t."""
+    _fields_ = [
+        ("row_max", ctypes.c_void_p),
+        ("row_sumexp", ctypes.c_void_p),
+        ("p_draft", ctypes.c_void_p),
+        ("q_draft", ctypes.c_void_p),
+        ("Z", ctypes.c_void_p),
+        ("argmax", ctypes.c_void_p),
+        ("b_offset", ctypes.c_int64),
+        ("events", ctypes.c_void_p * 5),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libspecverify.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, u64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+    L.spec_verify.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, u64, vp, vp, vp]
+    L.spec_verify.restype = ctypes.c_int
+    L.spec_verify_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, u64, vp, vp, vp,
+                                 ctypes.POINTER(Extras)]
+    L.spec_verify_ex.restype = ctypes.c_int
+    L.spec_row_stats.argtypes = [vp, i64, i32, i32, f32, vp, vp, vp]
+    L.spec_row_stats.restype = ctypes.c_int
+    L.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
+    L.spec_verify_workspace_bytes.restype = ctypes.c_size_t
+    L.spec_verify_release_workspace.argtypes = []
+    L.spec_verify_release_workspace.restype = None
+    L.spec_verify_last_error.argtypes = []
+    L.spec_verify_last_error.restype = ctypes.c_char_p
+    L.spec_verify_abi_version.argtypes = []
+    L.spec_verify_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return load_library().spec_verify_last_error().decode()
+
+
+def _check(rc):
+    if rc != SPEC_OK:
+        raise SpecVerifyError(rc, last_error())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def verify(target_logits, draft_logits, draft_tokens, temperature: float, seed: int,
+           out_tokens=None, out_n_accepted=None, stream=None, extras: Extras | None = None):
+    """One verification step.
+
+    target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (float32 or
+    bfloat16, contiguous, on the GPU; draft_logits may be None at temperature 0),
+    draft_tokens [B, gamma] int32. Returns (out_tokens [B, gamma+1] int32,
+    out_n_accepted [B] int32), enqueued on `stream` (default: torch's current
+    stream)."""
+    import torch
+    L = load_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, V]")
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    dt = _dtype_code(target_logits)
+    for name, t in (("target_logits", target_logits), ("draft_logits", draft_logits),
+                    ("draft_tokens", draft_tokens)):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if draft_logits is not None:
+        if draft_logits.dtype != target_logits.dtype or tuple(draft_logits.shape) != (B, gamma, V):
+            raise ValueError("draft_logits must be [B, gamma, V] with the target's dtype")
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, gamma):
+        raise ValueError("draft_tokens must be int32 [B, gamma]")
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    if out_n_accepted is None:
+        out_n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    args = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), B, gamma, V, dt,
+            float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out_tokens),
+            _ptr(out_n_accepted), _stream_handle(stream))
+    if extras is None:
+        _check(L.spec_verify(*args))
+    else:
+        _check(L.spec_verify_ex(*args, ctypes.byref(extras)))
+    return out_tokens, out_n_accepted
+
+
+def verify_raw(target_ptr, draft_ptr, tokens_ptr, B, gamma, V, dtype, temperature, seed,
+               out_tokens_ptr, out_n_ptr, stream_handle, extras: Extras | None = None) -> int:
+    """Direct C-ABI call on raw device pointers; returns the status code."""
+    L = load_library()
+    args = (ctypes.c_void_p(target_ptr), ctypes.c_void_p(draft_ptr) if draft_ptr else None,
+            ctypes.c_void_p(tokens_ptr), B, gamma, V, dtype, float(temperature),
+            int(seed) & 0xFFFFFFFFFFFFFFFF, ctypes.c_void_p(out_tokens_ptr),
+            ctypes.c_void_p(out_n_ptr), ctypes.c_void_p(stream_handle))
+    if extras is None:
+        return L.spec_verify(*args)
+    return L.spec_verify_ex(*args, ctypes.byref(extras))
+
+
+def row_stats(logits, temperature: float, stream=None):
+    """Softmax statistics of every row of a [rows, V] tensor: (row_max float32,
+    row_sumexp float64)."""
+    import torch
+    L = load_library()
+    if logits.dim() != 2 or not logits.is_cuda or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [rows, V] GPU tensor")
+    rows, V = logits.shape
+    m = torch.empty(rows, dtype=torch.float32, device=logits.device)
+    s = torch.empty(rows, dtype=torch.float64, device=logits.device)
+    _check(L.spec_row_stats(_ptr(logits), rows, V, _dtype_code(logits), float(temperature),
+                            _ptr(m), _ptr(s), _stream_handle(stream)))
+    return m, s
+
+
+def workspace_bytes(B, gamma, V, dtype, temperature) -> int:
+    return int(load_library().spec_verify_workspace_bytes(B, gamma, V, dtype, float(temperature)))
+
+
+def release_workspace():
+    load_library().spec_verify_release_workspace()
