@@ -105,10 +105,9 @@ typedef struct {
     int32_t* argmax;       /* [B, gamma+1]: argmax of each target row (T == 0 only) */
     int64_t b_offset;      /* added to b in the Philox counter, so that a shard of a
                               larger batch draws the same uniforms as the whole batch */
-    void* events[5];       /* optional hipEvent_t (host handles) recorded on `stream`:
+    void* events[3];       /* optional hipEvent_t (host handles) recorded on `stream`:
                               [0] before the statistics kernel, [1] after it, [2] after
-                              the accept kernel, [3] after the residual-sum kernel,
-                              [4] after the draw kernel (T > 0) */
+                              the last kernel of the call (accept, residual sums, draw) */
 } spec_extras_t;
 
 /* spec_verify with extras (NULL extras == spec_verify). Same kernels. */

@@ -45,7 +45,7 @@ class Extras(ctypes.Structure):
         ("Z", ctypes.c_void_p),
         ("argmax", ctypes.c_void_p),
         ("b_offset", ctypes.c_int64),
-        ("events", ctypes.c_void_p * 5),
+        ("events", ctypes.c_void_p * 3),
     ]
 
 

@@ -12,24 +12,29 @@
 //  [HSD]  "LLM inference optimisation: hidden-state speculative decoding", 3.3:
 //         the bonus token drawn from the last target row.
 //
-// The path is four stream-ordered kernels:
-//  K1 k_stats      one streaming pass over every target and draft row (all the
-//                  compulsory bytes). Each wavefront owns a contiguous range of
-//                  1 KiB chunks of the concatenated rows, keeps a per-lane
-//                  online max / sum of 2^(x*c - ref) and flushes one (max, sum)
-//                  partial per row piece with wave reductions. No LDS, no
-//                  barriers, no atomics. At T == 0 it tracks the argmax instead.
-//  K2 k_accept     one wavefront per sequence, one lane per drafted position:
-//                  merges the partials, gathers the two logits of the draft
-//                  token, forms alpha in fp64, draws the Philox uniform and
-//                  finds the first rejection with a ballot.
-//  K3a k_resid     per (segment, sequence) fp64 sums of r = max(0, p - q) over
-//                  the rejected row (or of p over the bonus row).
-//  K3b k_draw      per sequence: pick the segment whose running sum crosses
-//                  u*Z, recompute r there, block prefix scan (wave shuffles +
-//                  LDS), emit the first index whose cumulative mass exceeds u*Z.
-// Exponentials are fp32 (v_exp_f32 through exp2 with c = log2(e)/T folded
-// into one FMA); every sum that decides a token is fp64.
+// Three stream-ordered kernels per call (two at T == 0); no kernel waits on
+// another work-group and none hands work over through atomics:
+//  k_stats   one streaming pass over every target and draft row (all the
+//            compulsory bytes). Each wavefront owns a contiguous range of
+//            1 KiB chunks of the concatenated rows, keeps per lane an online
+//            max and a sum of 2^(x*c - R) (R an integer reference, c =
+//            log2(e)/T), software-pipelines its 16-byte loads, and flushes one
+//            partial per row piece with wave reductions. At T == 0 it tracks
+//            the argmax (first index of the maximum) instead.
+//  k_accept  one block per (residual segment, sequence). The block merges the
+//            sequence's partials through LDS and its first wavefront decides
+//            the accept step: lane i gathers the two logits of draft token i,
+//            forms alpha in fp64, draws its Philox uniform, and a ballot finds
+//            the first rejection k. Every block of the sequence repeats this
+//            (a few kilobytes of loads); block 0 writes the accepted tokens and
+//            k. Then each block sums the residual max(0, p - q) of row k (or p
+//            of the bonus row) over its segment in fp64.
+//  k_draw    one block per sequence: a block scan of the segment sums gives
+//            Z and the segment holding u*Z; a second scan over that segment's
+//            elements, held in registers, gives the first index whose
+//            cumulative mass exceeds u*Z.
+// Exponentials are fp32 (v_exp_f32 on one FMA); every sum and comparison that
+// decides a token is fp64.
 
 #include <hip/hip_runtime.h>
 
@@ -40,18 +45,28 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <utility>
 
 #include "specverify.h"
 
 namespace {
 
+#ifndef SPECVERIFY_STATS_UNROLL
+#define SPECVERIFY_STATS_UNROLL 4
+#endif
+#ifndef SPECVERIFY_CHUNKS_PER_WAVE
+#define SPECVERIFY_CHUNKS_PER_WAVE 16
+#endif
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kUnroll = 4;          // chunks loaded before any is consumed (K1)
-constexpr int kMinChunksPerWave = 4;
-constexpr int kSeg3 = 4096;         // elements per residual segment (K3)
+constexpr int kUnroll = SPECVERIFY_STATS_UNROLL;          // chunks per pipelined load group
+constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE; // 1 KiB chunks per stats wavefront
+constexpr int kSeg3 = 4096;                               // elements per residual segment
+constexpr int kPerThread = kSeg3 / kBlock;                // segment elements per draw thread
+constexpr int kMaxMergeSlots = 2048;                      // partials staged in LDS per row run
+constexpr float kRUnset = -1.0e30f;                       // lane reference before the first finite value
 
 enum : int { kAcc = 0, kRej = 1, kBad = 2 };
 
@@ -99,55 +114,57 @@ __device__ inline float load_one(const char* row, int64_t j) {
 }
 
 // A chunk is 64 lanes x EPL elements. Vector path (rows 16-byte aligned): lane l
-// holds elements [l*EPL, l*EPL+EPL) from one 16-byte load. Scalar path: lane l
-// holds elements l, l+64, l+128, l+192. Either way each lane sees its elements
-// in ascending index order.
+// holds elements [l*EPL, l*EPL+EPL) from one 16-byte load, kept raw until
+// consumed. Scalar path: lane l holds elements l, l+64, l+128, l+192, converted
+// at load time. Either way each lane sees its elements in ascending order.
 template <int DT, bool VEC> struct Chunk {
     static constexpr int EPL = VEC ? 16 / ElemBytes<DT>::value : 4;
     static constexpr int CH = kWave * EPL;
-    float x[EPL];
+    using Raw = typename std::conditional<VEC, uint4, float4>::type;
 
-    __device__ inline void load_full(const char* row, int64_t c, int lane) {
+    __device__ static inline Raw load_full(const char* row, int64_t c, int lane) {
         if constexpr (VEC) {
-            const uint4 w = *reinterpret_cast<const uint4*>(row + (c * CH + lane * EPL) * ElemBytes<DT>::value);
-            if constexpr (DT == SPEC_F32) {
-                x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
-                x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
-            } else {
-                x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xFFFF0000u);
-                x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xFFFF0000u);
-                x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xFFFF0000u);
-                x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xFFFF0000u);
-            }
+            return *reinterpret_cast<const uint4*>(row + (c * CH + lane * EPL) * ElemBytes<DT>::value);
         } else {
-#pragma unroll
-            for (int v = 0; v < EPL; ++v) x[v] = load_one<DT>(row, c * CH + lane + kWave * v);
+            const int64_t j = c * CH + lane;
+            return make_float4(load_one<DT>(row, j), load_one<DT>(row, j + kWave),
+                               load_one<DT>(row, j + 2 * kWave), load_one<DT>(row, j + 3 * kWave));
         }
     }
     // Elements at or beyond V read as -inf (no mass, never a maximum).
-    __device__ inline void load_masked(const char* row, int64_t c, int lane, int32_t V) {
+    __device__ static inline Raw load_masked(const char* row, int64_t c, int lane, int32_t V) {
         if constexpr (VEC) {
-            if (c * CH + lane * EPL < V) {  // V is a multiple of EPL on this path
-                load_full(row, c, lane);
-            } else {
-#pragma unroll
-                for (int v = 0; v < EPL; ++v) x[v] = -INFINITY;
-            }
+            if (c * CH + lane * EPL < V) return load_full(row, c, lane);  // V % EPL == 0 here
+            const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;
+            return make_uint4(ninf, ninf, ninf, ninf);
         } else {
+            const int64_t j = c * CH + lane;
+            float v[4];
 #pragma unroll
-            for (int v = 0; v < EPL; ++v) {
-                const int64_t j = c * CH + lane + kWave * v;
-                x[v] = j < V ? load_one<DT>(row, j) : -INFINITY;
-            }
+            for (int k = 0; k < 4; ++k) v[k] = j + k * kWave < V ? load_one<DT>(row, j + k * kWave) : -INFINITY;
+            return make_float4(v[0], v[1], v[2], v[3]);
         }
     }
-    __device__ inline int64_t index_of(int64_t c, int lane, int v) const {
+    __device__ static inline void expand(const Raw& w, float* x) {
+        if constexpr (!VEC) {
+            x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+        } else if constexpr (DT == SPEC_F32) {
+            x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+            x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+        } else {
+            x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+            x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+            x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xFFFF0000u);
+            x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xFFFF0000u);
+        }
+    }
+    __device__ static inline int64_t index_of(int64_t c, int lane, int v) {
         return VEC ? c * CH + lane * EPL + v : c * CH + lane + kWave * v;
     }
 };
 
 // --------------------------------------------------------------------------
-// Wave reductions (64 lanes)
+// Wave and block reductions
 // --------------------------------------------------------------------------
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -160,11 +177,53 @@ __device__ inline double wave_sum(double v) {
     return v;
 }
 
+// Block-wide fp64 sum (256 threads); the result is returned to every thread.
+__device__ inline double block_sum(double v, double* lds) {
+    v = wave_sum(v);
+    const int wid = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) lds[wid] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWavesPerBlock; ++k) t += lds[k];
+    return t;
+}
+
+// Block-wide inclusive scan (256 threads) of fp64 values; also returns the
+// exclusive prefix (the previous thread's inclusive value) and the block total.
+__device__ inline void block_scan(double v, double* lds, double& incl, double& excl, double& total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    double x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) lds[wid] = x;
+    __syncthreads();
+    double base = 0.0;
+    total = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWavesPerBlock; ++k) {
+        if (k < wid) base += lds[k];
+        total += lds[k];
+    }
+    incl = base + x;
+    const double prev = __shfl_up(incl, 1, kWave);
+    excl = lane == 0 ? base : prev;
+}
+
+// --------------------------------------------------------------------------
 // Geometry of the statistics pass: rows [0, rows_t) are target rows in memory
-// order, rows [rows_t, rows) draft rows; each row is nchunk chunks; wave w owns
-// chunks [w*cpw, (w+1)*cpw) of the concatenation; row r's partials sit at
+// order, rows [rows_t, rows) draft rows (absent at T == 0 and for the
+// stand-alone row statistics); each row is nchunk chunks; wave w owns chunks
+// [w*cpw, (w+1)*cpw) of the concatenation; row r's partials sit at
 // r*maxp + (w - first wave of r).
-struct StatsGeom {
+// --------------------------------------------------------------------------
+struct Geom {
     int64_t rows_t;
     int64_t rows;
     int32_t V;
@@ -175,213 +234,284 @@ struct StatsGeom {
 };
 
 template <int DT>
-__device__ inline const char* row_ptr(const void* tgt, const void* dft, const StatsGeom& g, int64_t r) {
+__device__ inline const char* row_ptr(const void* tgt, const void* dft, const Geom& g, int64_t r) {
     return r < g.rows_t ? row_at<DT>(tgt, r * g.V) : row_at<DT>(dft, (r - g.rows_t) * g.V);
 }
 
+__device__ inline int64_t first_wave(const Geom& g, int64_t r) { return (r * g.nchunk) / g.cpw; }
+__device__ inline int pieces_of(const Geom& g, int64_t r) {
+    return static_cast<int>(((r + 1) * g.nchunk - 1) / g.cpw - first_wave(g, r) + 1);
+}
+
+struct StatsArgs {
+    float c32;
+    float* part_m;    // max of the piece
+    float* part_r;    // integer reference of the piece (T > 0)
+    double* part_s;   // sum of 2^(x*c - reference) (T > 0)
+    int32_t* part_i;  // first index of the maximum (T == 0)
+};
+
 // --------------------------------------------------------------------------
-// K1, T > 0: per-lane online softmax statistics. Lane state: m = max seen,
-// mc = fl(m*c) (the reference; 0 while m = -inf), S = sum 2^(fl(x*c - mc)) in
-// fp64 (fp32 per chunk group). The wave flush rebases every lane to the wave
-// max M exactly in fp64: S_lane * 2^(mc - M*c), M*c formed exactly in fp64.
+// k_stats. Lane state at T > 0: m = max seen; R = integer reference (kRUnset
+// until the first finite value); S = sum of 2^(fl(x*c - R)) in fp64, fp32 per
+// load group. A group's exponentials use the current R while its max is
+// formed; if the group's max exceeds R + 1 the reference moves up to
+// ceil(max*c), S is rescaled exactly with ldexp and the group is redone. The
+// wave flush rebases every lane onto the largest lane reference, exactly.
 // --------------------------------------------------------------------------
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt,
-                                                  const void* __restrict__ dft, StatsGeom g,
-                                                  float c32, float* __restrict__ part_m,
-                                                  double* __restrict__ part_s) {
+struct SoftLane {
+    float m;
+    float R;
+    double S;
+    __device__ inline void init() { m = -INFINITY; R = kRUnset; S = 0.0; }
+};
+struct ArgLane {
+    float best;
+    int32_t at;
+    bool nan;
+    __device__ inline void init() { best = -INFINITY; at = INT32_MAX; nan = false; }
+};
+
+__device__ inline double rebase(double S, float R, float Rto) {
+    return S == 0.0 ? 0.0 : ldexp(S, static_cast<int>(fmaxf(R - Rto, -1100.0f)));
+}
+
+// Sum of 2^(fl(x*c - R)) over a load group, expanding each 16-byte load as it
+// is consumed (the raw loads stay live for the rare redo).
+template <int DT, bool VEC, int N>
+__device__ inline void group_sum(const typename Chunk<DT, VEC>::Raw* raw, float c, float R, float& gmax,
+                                 float& acc) {
     using C = Chunk<DT, VEC>;
+    float a0 = 0.0f, a1 = 0.0f, mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float x[C::EPL];
+        C::expand(raw[u], x);
+#pragma unroll
+        for (int v = 0; v < C::EPL; ++v) {
+            mx = fmaxf(mx, x[v]);
+            const float e = __builtin_amdgcn_exp2f(fmaf(x[v], c, -R));
+            if (v & 1) a1 += e;
+            else a0 += e;
+        }
+    }
+    gmax = mx;
+    acc = a0 + a1;
+}
+
+template <int DT, bool VEC, int N>
+__device__ inline void consume_group(SoftLane& s, const typename Chunk<DT, VEC>::Raw* raw, int64_t, int,
+                                     float c) {
+    float gmax, acc;
+    group_sum<DT, VEC, N>(raw, c, s.R, gmax, acc);
+    if (gmax * c > s.R + 1.0f) {  // rare: a new maximum well above the reference
+        const float Rn = ceilf(gmax * c);
+        if (!(Rn < 3.0e38f)) {     // +inf logit (or an overflowing one): the row is unusable
+            s.S = NAN;
+            acc = 0.0f;
+        } else {
+            if (s.R > kRUnset) s.S = ldexp(s.S, static_cast<int>(fmaxf(s.R - Rn, -1100.0f)));
+            s.R = Rn;
+            float unused;
+            group_sum<DT, VEC, N>(raw, c, s.R, unused, acc);
+        }
+    }
+    s.m = fmaxf(s.m, gmax);
+    s.S += static_cast<double>(acc);
+}
+
+template <int DT, bool VEC, int N>
+__device__ inline void consume_group(ArgLane& s, const typename Chunk<DT, VEC>::Raw* raw, int64_t c0,
+                                     int lane, float) {
+    using C = Chunk<DT, VEC>;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float x[C::EPL];
+        C::expand(raw[u], x);
+#pragma unroll
+        for (int v = 0; v < C::EPL; ++v) {
+            s.nan |= (x[v] != x[v]);
+            if (x[v] > s.best) { s.best = x[v]; s.at = static_cast<int32_t>(C::index_of(c0 + u, lane, v)); }
+        }
+    }
+}
+
+template <int DT, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, const void* __restrict__ dft,
+                                                  Geom g, StatsArgs sa) {
+    using C = Chunk<DT, VEC>;
+    using Raw = typename C::Raw;
+    using Lane = typename std::conditional<GREEDY, ArgLane, SoftLane>::type;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
     if (w >= g.nwaves) return;
+    const float c = sa.c32;
     const int64_t total = g.rows * g.nchunk;
-    int64_t c = w * g.cpw;
-    const int64_t c_end = c + g.cpw < total ? c + g.cpw : total;
-    const int32_t nfull = g.V / C::CH;  // chunks of a row that are entirely in bounds
-    while (c < c_end) {
-        const int64_t r = c / g.nchunk;
+    int64_t cc = w * g.cpw;
+    const int64_t c_end = cc + g.cpw < total ? cc + g.cpw : total;
+    const int64_t nfull = g.V / C::CH;  // chunks of a row that are entirely in bounds
+    while (cc < c_end) {
+        const int64_t r = cc / g.nchunk;
         const int64_t first = r * g.nchunk;
         const int64_t ce = first + g.nchunk < c_end ? first + g.nchunk : c_end;
         const char* row = row_ptr<DT>(tgt, dft, g, r);
-        float m = -INFINITY, mc = 0.0f;
-        double S = 0.0;
-        int64_t cr = c - first;
+        int64_t cr = cc - first;
         const int64_t cr_end = ce - first;
         const int64_t cr_full = cr_end < nfull ? cr_end : nfull;
-        for (; cr + kUnroll <= cr_full; cr += kUnroll) {
-            C ch[kUnroll];
+        Lane st;
+        st.init();
+        if (cr + kUnroll <= cr_full) {
+            // software pipeline: the next group's loads are in flight while this one is consumed
+            Raw cur[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) ch[u].load_full(row, cr + u, lane);
-            float cm = ch[0].x[0];
+            for (int u = 0; u < kUnroll; ++u) cur[u] = C::load_full(row, cr + u, lane);
+            int64_t c0 = cr;
+            cr += kUnroll;
+            while (cr + kUnroll <= cr_full) {
+                Raw nxt[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+                for (int u = 0; u < kUnroll; ++u) nxt[u] = C::load_full(row, cr + u, lane);
+                consume_group<DT, VEC, kUnroll>(st, cur, c0, lane, c);
 #pragma unroll
-                for (int v = 0; v < C::EPL; ++v) cm = fmaxf(cm, ch[u].x[v]);
-            if (cm > m) {
-                const float nmc = cm * c32;
-                if (S != 0.0) S *= exp2(static_cast<double>(mc) - static_cast<double>(nmc));
-                m = cm;
-                mc = nmc;
+                for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+                c0 = cr;
+                cr += kUnroll;
             }
-            float acc = 0.0f;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-                for (int v = 0; v < C::EPL; ++v) acc += __builtin_amdgcn_exp2f(fmaf(ch[u].x[v], c32, -mc));
-            S += static_cast<double>(acc);
+            consume_group<DT, VEC, kUnroll>(st, cur, c0, lane, c);
         }
         for (; cr < cr_end; ++cr) {
-            C ch;
-            ch.load_masked(row, cr, lane, g.V);
-            float cm = ch.x[0];
+            Raw one[1] = {C::load_masked(row, cr, lane, g.V)};
+            consume_group<DT, VEC, 1>(st, one, cr, lane, c);
+        }
+        const int64_t slot = r * g.maxp + (w - first_wave(g, r));
+        if constexpr (GREEDY) {
 #pragma unroll
-            for (int v = 1; v < C::EPL; ++v) cm = fmaxf(cm, ch.x[v]);
-            if (cm > m) {
-                const float nmc = cm * c32;
-                if (S != 0.0) S *= exp2(static_cast<double>(mc) - static_cast<double>(nmc));
-                m = cm;
-                mc = nmc;
+            for (int o = 32; o > 0; o >>= 1) {  // (value desc, index asc) across the wave
+                const float ob = __shfl_xor(st.best, o, kWave);
+                const int32_t oa = __shfl_xor(st.at, o, kWave);
+                if (ob > st.best || (ob == st.best && oa < st.at)) { st.best = ob; st.at = oa; }
             }
-            float acc = 0.0f;
-#pragma unroll
-            for (int v = 0; v < C::EPL; ++v) acc += __builtin_amdgcn_exp2f(fmaf(ch.x[v], c32, -mc));
-            S += static_cast<double>(acc);
+            const bool any_nan = __ballot(st.nan) != 0;
+            if (lane == 0) {
+                sa.part_m[slot] = any_nan ? NAN : st.best;
+                sa.part_i[slot] = st.at;
+            }
+        } else {
+            const float M = wave_max(st.m);
+            const float Rw = wave_max(st.S > 0.0 ? st.R : kRUnset);
+            const double Sw = wave_sum(rebase(st.S, st.R, Rw));
+            if (lane == 0) {
+                sa.part_m[slot] = M;
+                sa.part_r[slot] = Rw;
+                sa.part_s[slot] = Sw;
+            }
         }
-        const float M = wave_max(m);
-        const double contrib =
-            S == 0.0 ? 0.0
-                     : S * exp2(static_cast<double>(mc) - static_cast<double>(M) * static_cast<double>(c32));
-        const double Ssum = wave_sum(contrib);
-        if (lane == 0) {
-            const int64_t slot = r * g.maxp + (w - first / g.cpw);
-            part_m[slot] = M;
-            part_s[slot] = Ssum;
-        }
-        c = ce;
+        cc = ce;
     }
 }
 
 // --------------------------------------------------------------------------
-// K1, T == 0: per-lane argmax (first index of the maximum) and a NaN flag.
+// Merging partials. A row's partials (M_p, R_p, S_p) combine exactly with
+// ldexp onto the largest reference R; the result is rebased once to the row
+// max: S * 2^(R - M*c), the exponent formed exactly in fp64. The argmax
+// partials combine as (value desc, index asc); any NaN marks the row.
 // --------------------------------------------------------------------------
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_argmax(const void* __restrict__ tgt, StatsGeom g,
-                                                   float* __restrict__ part_m,
-                                                   int32_t* __restrict__ part_i) {
-    using C = Chunk<DT, VEC>;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
-    if (w >= g.nwaves) return;
-    const int64_t total = g.rows * g.nchunk;
-    int64_t c = w * g.cpw;
-    const int64_t c_end = c + g.cpw < total ? c + g.cpw : total;
-    const int32_t nfull = g.V / C::CH;
-    while (c < c_end) {
-        const int64_t r = c / g.nchunk;
-        const int64_t first = r * g.nchunk;
-        const int64_t ce = first + g.nchunk < c_end ? first + g.nchunk : c_end;
-        const char* row = row_at<DT>(tgt, r * g.V);
+struct RowStat {
+    float m;
+    int32_t arg;
+    double s;
+};
+
+__device__ inline bool usable(float M, double S) { return isfinite(M) && isfinite(S) && S > 0.0; }
+
+template <bool GREEDY>
+__device__ inline RowStat fold_row(int np, const float* pm, const float* pr, const double* ps, const int32_t* pi,
+                                   float c32) {
+    RowStat o;
+    if constexpr (GREEDY) {
         float best = -INFINITY;
-        int32_t at = INT32_MAX;
+        int32_t arg = INT32_MAX;
         bool nan = false;
-        int64_t cr = c - first;
-        const int64_t cr_end = ce - first;
-        const int64_t cr_full = cr_end < nfull ? cr_end : nfull;
-        for (; cr + kUnroll <= cr_full; cr += kUnroll) {
-            C ch[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) ch[u].load_full(row, cr + u, lane);
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-                for (int v = 0; v < C::EPL; ++v) {
-                    const float x = ch[u].x[v];
-                    nan |= (x != x);
-                    if (x > best) { best = x; at = static_cast<int32_t>(ch[u].index_of(cr + u, lane, v)); }
-                }
+        for (int k = 0; k < np; ++k) {
+            const float v = pm[k];
+            const int32_t a = pi[k];
+            nan |= (v != v);
+            if (v > best || (v == best && a < arg)) { best = v; arg = a; }
         }
-        for (; cr < cr_end; ++cr) {
-            C ch;
-            ch.load_masked(row, cr, lane, g.V);
-#pragma unroll
-            for (int v = 0; v < C::EPL; ++v) {
-                const float x = ch.x[v];
-                nan |= (x != x);
-                if (x > best) { best = x; at = static_cast<int32_t>(ch.index_of(cr, lane, v)); }
+        o.m = nan ? NAN : best;
+        o.arg = arg;
+        o.s = 1.0;
+    } else {
+        float M = -INFINITY, R = kRUnset;
+        for (int k = 0; k < np; ++k) {
+            M = fmaxf(M, pm[k]);
+            R = fmaxf(R, pr[k]);
+        }
+        double acc = 0.0;
+        for (int k = 0; k < np; ++k) acc += rebase(ps[k], pr[k], R);
+        o.m = M;
+        o.arg = 0;
+        o.s = acc * exp2(static_cast<double>(R) - static_cast<double>(M) * static_cast<double>(c32));
+    }
+    return o;
+}
+
+// Merge rows [r0, r0 + n) into rs[out0 + j]. When their partials fit the
+// staging buffer (cap entries) every thread loads one partial, so all loads are
+// in flight together; then thread j folds row r0 + j from LDS. Otherwise each
+// row is folded straight from memory.
+template <bool GREEDY>
+__device__ void merge_rows(const Geom& g, const StatsArgs& sa, int64_t r0, int n, int out0, int cap, float* lm,
+                           float* lr, double* ls, int32_t* li, RowStat* rs) {
+    const int slots = n * g.maxp;
+    if (slots <= cap) {
+        for (int t = threadIdx.x; t < slots; t += kBlock) {
+            const int j = t / g.maxp, k = t % g.maxp;
+            const int64_t r = r0 + j;
+            const bool live = k < pieces_of(g, r);
+            const int64_t at = r * g.maxp + k;
+            lm[t] = live ? sa.part_m[at] : -INFINITY;
+            if constexpr (GREEDY) {
+                li[t] = live ? sa.part_i[at] : INT32_MAX;
+            } else {
+                lr[t] = live ? sa.part_r[at] : kRUnset;
+                ls[t] = live ? sa.part_s[at] : 0.0;
             }
         }
-        // (value desc, index asc) across the wave
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ob = __shfl_xor(best, o, kWave);
-            const int32_t oa = __shfl_xor(at, o, kWave);
-            if (ob > best || (ob == best && oa < at)) { best = ob; at = oa; }
+        __syncthreads();
+        for (int j = threadIdx.x; j < n; j += kBlock) {
+            const int base = j * g.maxp;
+            rs[out0 + j] = fold_row<GREEDY>(g.maxp, lm + base, lr + base, ls + base, li + base, sa.c32);
         }
-        const bool any_nan = __ballot(nan) != 0;
-        if (lane == 0) {
-            const int64_t slot = r * g.maxp + (w - first / g.cpw);
-            part_m[slot] = any_nan ? NAN : best;
-            part_i[slot] = at;
+    } else {
+        for (int j = threadIdx.x; j < n; j += kBlock) {
+            const int64_t at = (r0 + j) * g.maxp;
+            rs[out0 + j] = fold_row<GREEDY>(pieces_of(g, r0 + j), sa.part_m + at, sa.part_r + at,
+                                            sa.part_s + at, sa.part_i + at, sa.c32);
         }
-        c = ce;
     }
+    __syncthreads();
 }
 
-// --------------------------------------------------------------------------
-// Merging a row's partials
-// --------------------------------------------------------------------------
-__device__ inline void merge_stats(const StatsGeom& g, int64_t r, float c32, const float* part_m,
-                                   const double* part_s, float& M, double& S) {
-    const int64_t w0 = (r * g.nchunk) / g.cpw;
-    const int64_t w1 = ((r + 1) * g.nchunk - 1) / g.cpw;
-    const int64_t base = r * g.maxp;
-    M = -INFINITY;
-    for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, part_m[base + (w - w0)]);
-    S = 0.0;
-    const double Mc = static_cast<double>(M) * static_cast<double>(c32);
-    for (int64_t w = w0; w <= w1; ++w) {
-        const double pm = static_cast<double>(part_m[base + (w - w0)]);
-        S += part_s[base + (w - w0)] * exp2(pm * static_cast<double>(c32) - Mc);
-    }
-}
-
-__device__ inline void merge_argmax(const StatsGeom& g, int64_t r, const float* part_m,
-                                    const int32_t* part_i, float& best, int32_t& at, bool& nan) {
-    const int64_t w0 = (r * g.nchunk) / g.cpw;
-    const int64_t w1 = ((r + 1) * g.nchunk - 1) / g.cpw;
-    const int64_t base = r * g.maxp;
-    best = -INFINITY;
-    at = INT32_MAX;
-    nan = false;
-    for (int64_t w = w0; w <= w1; ++w) {
-        const float v = part_m[base + (w - w0)];
-        const int32_t a = part_i[base + (w - w0)];
-        nan |= (v != v);
-        if (v > best || (v == best && a < at)) { best = v; at = a; }
-    }
-}
-
-__device__ inline bool usable(float M, double S) {
-    return isfinite(M) && isfinite(S) && S > 0.0;
-}
-
-// What the residual kernels need about the row they resample.
+// What the draw needs about the row it resamples.
 struct SeqInfo {
     int32_t k;      // emitted position (0..gamma), -1 = invalid sequence
-    float mp, mq;   // max logit of the target row k / draft row k
+    float mp, mq;   // max logit of target row k / draft row k
     int32_t pad;
-    double sp, sq;  // sum-exp of those rows
+    double sp, sq;  // sum-exp of those rows (relative to their max)
 };
 
 struct AcceptArgs {
     const int32_t* tokens;
-    int32_t B, gamma, V;
+    int32_t B, gamma, V, nseg;
+    int32_t stage;  // staged partials per row run (LDS), 0 = none
     float c32;
     uint64_t seed;
     int64_t b_offset;
     int32_t* out_tokens;
     int32_t* out_n;
     SeqInfo* info;
+    double* seg;
     float* dbg_row_max;
     double* dbg_row_sumexp;
     double* dbg_p;
@@ -390,111 +520,24 @@ struct AcceptArgs {
 };
 
 // --------------------------------------------------------------------------
-// K2: gather, accept, first rejection. One wave per sequence; lane i < gamma
-// is drafted position i, lane gamma the bonus row.
+// Residual in t units. With e_j = 2^(fl(x_j*c - mc)) for the target (p) and
+// draft (q) rows, p_j = e_pj * scale_p and q_j = e_qj * scale_q (scale =
+// 2^(mc - m*c)/S). Then max(0, p_j - q_j) = scale_p * t_j with
+// t_j = max(0, e_pj - rho*e_qj), rho = scale_q/scale_p (one fp64 FMA). The
+// inverse-CDF draw is invariant to the common factor; at the bonus row
+// t_j = e_pj.
 // --------------------------------------------------------------------------
-template <int DT, bool GREEDY>
-__global__ __launch_bounds__(kBlock) void k_accept(const void* __restrict__ tgt,
-                                                   const void* __restrict__ dft, StatsGeom g,
-                                                   AcceptArgs a, const float* __restrict__ part_m,
-                                                   const double* __restrict__ part_s,
-                                                   const int32_t* __restrict__ part_i) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
-    if (b >= a.B) return;
-    const int32_t gamma = a.gamma;
-    const int i = lane;
-    const int64_t R = 2 * gamma + 1;
-    int status = kAcc;
-    float mt = NAN, md = NAN;
-    double st = NAN, sd = NAN;
-    bool ut = false;
-    int32_t amax = -1;
-    int32_t x = 0;
-    if (i <= gamma) {
-        const int64_t rt = b * (gamma + 1) + i;
-        if constexpr (GREEDY) {
-            bool nan;
-            merge_argmax(g, rt, part_m, part_i, mt, amax, nan);
-            ut = !nan && isfinite(mt);
-            if (a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
-            if (a.dbg_argmax) a.dbg_argmax[b * (gamma + 1) + i] = amax;
-        } else {
-            merge_stats(g, rt, a.c32, part_m, part_s, mt, st);
-            ut = usable(mt, st);
-            if (a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
-            if (a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + i] = st;
-        }
-    }
-    if (i < gamma) {
-        x = a.tokens[b * gamma + i];
-        const bool tok_ok = x >= 0 && x < a.V;
-        if constexpr (GREEDY) {
-            status = (!ut || !tok_ok) ? kBad : (x == amax ? kAcc : kRej);
-        } else {
-            const int64_t rd = g.rows_t + b * gamma + i;
-            merge_stats(g, rd, a.c32, part_m, part_s, md, sd);
-            const bool ud = usable(md, sd);
-            if (a.dbg_row_max) a.dbg_row_max[b * R + gamma + 1 + i] = md;
-            if (a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + gamma + 1 + i] = sd;
-            double p = NAN, q = NAN;
-            if (!ut || !ud || !tok_ok) {
-                status = kBad;
-            } else {
-                const double c = static_cast<double>(a.c32);
-                const double lt = load_one<DT>(row_at<DT>(tgt, (b * (gamma + 1) + i) * a.V), x);
-                const double ld = load_one<DT>(row_at<DT>(dft, (b * gamma + i) * a.V), x);
-                p = exp2((lt - static_cast<double>(mt)) * c) / st;
-                q = exp2((ld - static_cast<double>(md)) * c) / sd;
-                const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
-                const double u = philox_uniform(a.seed, static_cast<uint32_t>(b + a.b_offset),
-                                                static_cast<uint32_t>(i), 0u);
-                status = u < alpha ? kAcc : kRej;
-            }
-            if (a.dbg_p) a.dbg_p[b * gamma + i] = p;
-            if (a.dbg_q) a.dbg_q[b * gamma + i] = q;
-        }
-    }
-    const uint64_t stop = __ballot(i < gamma && status != kAcc);
-    const int f = stop ? __ffsll(static_cast<unsigned long long>(stop)) - 1 : gamma;
-    const int fstat = __shfl(status, f, kWave);
-    const bool bonus_ok = __shfl(ut ? 1 : 0, gamma, kWave) != 0;
-    const bool invalid = f < gamma ? (fstat == kBad) : !bonus_ok;
-    const int k = invalid ? -1 : f;
-    if (i <= gamma) {
-        int32_t o = -1;
-        if (!invalid) {
-            if (i < k) o = x;
-            else if (GREEDY && i == k) o = amax;
-        }
-        a.out_tokens[b * (gamma + 1) + i] = o;
-    }
-    if (i == 0) a.out_n[b] = k;
-    if constexpr (!GREEDY) {
-        if (!invalid && i == k) {
-            SeqInfo s;
-            s.k = k; s.mp = mt; s.mq = k < gamma ? md : 0.0f; s.pad = 0;
-            s.sp = st; s.sq = k < gamma ? sd : 1.0;
-            a.info[b] = s;
-        } else if (invalid && i == 0) {
-            SeqInfo s;
-            s.k = -1; s.mp = 0.0f; s.mq = 0.0f; s.pad = 0; s.sp = 1.0; s.sq = 1.0;
-            a.info[b] = s;
-        }
-    }
-}
-
-// Per-row constants of the residual kernels: p_j = 2^(fl(x_j*c - mcp)) * scale_p.
 struct ResidRow {
     const char* prow;
     const char* qrow;  // nullptr at the bonus row
     float mcp, mcq;
-    double scale_p, scale_q;
+    double rho;
+    double scale_p;
 };
 
 template <int DT>
-__device__ inline ResidRow resid_row(const void* tgt, const void* dft, const SeqInfo& s,
-                                     int64_t b, int32_t gamma, int32_t V, float c32) {
+__device__ inline ResidRow resid_row(const void* tgt, const void* dft, const SeqInfo& s, int64_t b,
+                                     int32_t gamma, int32_t V, float c32) {
     ResidRow rr;
     rr.prow = row_at<DT>(tgt, (b * (gamma + 1) + s.k) * V);
     rr.qrow = s.k < gamma ? row_at<DT>(dft, (b * gamma + s.k) * V) : nullptr;
@@ -502,220 +545,327 @@ __device__ inline ResidRow resid_row(const void* tgt, const void* dft, const Seq
     rr.mcp = s.mp * c32;
     rr.scale_p = exp2(static_cast<double>(rr.mcp) - static_cast<double>(s.mp) * c) / s.sp;
     rr.mcq = s.mq * c32;
-    rr.scale_q = exp2(static_cast<double>(rr.mcq) - static_cast<double>(s.mq) * c) / s.sq;
+    const double scale_q = exp2(static_cast<double>(rr.mcq) - static_cast<double>(s.mq) * c) / s.sq;
+    rr.rho = scale_q / rr.scale_p;
     return rr;
 }
 
-__device__ inline void resid_val(float xp, float xq, bool has_q, float c32, const ResidRow& rr,
-                                 double& r, double& p) {
-    p = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xp, c32, -rr.mcp))) * rr.scale_p;
-    if (has_q) {
-        const double q = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xq, c32, -rr.mcq))) * rr.scale_q;
-        r = fmax(0.0, p - q);
-    } else {
-        r = p;
-    }
-}
-
-// Block-wide fp64 sum (256 threads); result valid in thread 0.
-__device__ inline double block_sum(double v, double* lds) {
-    v = wave_sum(v);
-    const int wid = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) lds[wid] = v;
-    __syncthreads();
-    double t = 0.0;
-    if (threadIdx.x == 0)
-        for (int k = 0; k < kWavesPerBlock; ++k) t += lds[k];
-    __syncthreads();
-    return t;
+__device__ inline double resid_t(float xp, float xq, bool has_q, float c32, const ResidRow& rr) {
+    const double ep = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xp, c32, -rr.mcp)));
+    if (!has_q) return ep;
+    const double eq = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xq, c32, -rr.mcq)));
+    return fmax(0.0, fma(-eq, rr.rho, ep));
 }
 
 // --------------------------------------------------------------------------
-// K3a: per (segment, sequence) sums of r and of p over the resampled row.
+// k_accept. Dynamic LDS holds the staged partials of one row run (doubles
+// first, then the float/int arrays) and the merged stats of the sequence.
 // --------------------------------------------------------------------------
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_resid(const void* __restrict__ tgt,
-                                                  const void* __restrict__ dft, int32_t gamma,
-                                                  int32_t V, int32_t nseg, float c32,
-                                                  const SeqInfo* __restrict__ info,
-                                                  double* __restrict__ seg_r,
-                                                  double* __restrict__ seg_p) {
-    __shared__ double lds[kWavesPerBlock];
+struct AcceptShared {
+    double red[kWavesPerBlock];
+    SeqInfo si;
+};
+
+template <int DT, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kBlock) void k_accept(const void* __restrict__ tgt, const void* __restrict__ dft,
+                                                   Geom g, StatsArgs sa, AcceptArgs a) {
+    extern __shared__ __align__(16) char dyn[];
+    __shared__ AcceptShared sh;
+    const int32_t gamma = a.gamma, V = a.V;
+    const int nseg = GREEDY ? 1 : a.nseg;
     const int64_t b = blockIdx.x / nseg;
     const int32_t s = static_cast<int32_t>(blockIdx.x % nseg);
-    const SeqInfo in = info[b];
-    if (in.k < 0) return;
-    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V, c32);
-    const bool has_q = rr.qrow != nullptr;
-    const int64_t e0 = static_cast<int64_t>(s) * kSeg3;
-    const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-    double sr = 0.0, sp = 0.0;
-    if constexpr (VEC) {
-        constexpr int EPL = 16 / ElemBytes<DT>::value;
-        for (int64_t e = e0 + threadIdx.x * EPL; e < e1; e += kBlock * EPL) {
-            const uint4 wp = *reinterpret_cast<const uint4*>(rr.prow + e * ElemBytes<DT>::value);
-            uint4 wq = wp;
-            if (has_q) wq = *reinterpret_cast<const uint4*>(rr.qrow + e * ElemBytes<DT>::value);
-            const uint32_t pw[4] = {wp.x, wp.y, wp.z, wp.w};
-            const uint32_t qw[4] = {wq.x, wq.y, wq.z, wq.w};
-#pragma unroll
-            for (int v = 0; v < EPL; ++v) {
-                float xp, xq;
-                if constexpr (DT == SPEC_F32) {
-                    xp = __uint_as_float(pw[v]);
-                    xq = __uint_as_float(qw[v]);
-                } else {
-                    xp = __uint_as_float((v & 1) ? (pw[v >> 1] & 0xFFFF0000u) : (pw[v >> 1] << 16));
-                    xq = __uint_as_float((v & 1) ? (qw[v >> 1] & 0xFFFF0000u) : (qw[v >> 1] << 16));
-                }
-                double r, p;
-                resid_val(xp, xq, has_q, c32, rr, r, p);
-                sr += r;
-                sp += p;
-            }
-        }
-    } else {
-        for (int64_t e = e0 + threadIdx.x; e < e1; e += kBlock) {
-            const float xp = load_one<DT>(rr.prow, e);
-            const float xq = has_q ? load_one<DT>(rr.qrow, e) : 0.0f;
-            double r, p;
-            resid_val(xp, xq, has_q, c32, rr, r, p);
-            sr += r;
-            sp += p;
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool wave0 = threadIdx.x < kWave;
+    const int nt = gamma + 1, nd = GREEDY ? 0 : gamma;
+    const int stage = a.stage;
+    double* ls = reinterpret_cast<double*>(dyn);
+    float* lm = reinterpret_cast<float*>(ls + stage);
+    float* lr = lm + stage;
+    int32_t* li = reinterpret_cast<int32_t*>(lr + stage);
+    RowStat* rs = reinterpret_cast<RowStat*>(dyn + ((static_cast<size_t>(stage) * 20 + 15) / 16) * 16);
+
+    // draft token i and its two logits, loaded while the partials are staged
+    int32_t x = 0;
+    float lt = 0.0f, ld = 0.0f;
+    bool tok_ok = false;
+    if (wave0 && lane < gamma) {
+        x = a.tokens[b * gamma + lane];
+        tok_ok = x >= 0 && x < V;
+        if (tok_ok) {
+            lt = load_one<DT>(row_at<DT>(tgt, (b * (gamma + 1) + lane) * V), x);
+            if constexpr (!GREEDY) ld = load_one<DT>(row_at<DT>(dft, (b * gamma + lane) * V), x);
         }
     }
-    const double tr = block_sum(sr, lds);
-    const double tp = block_sum(sp, lds);
-    if (threadIdx.x == 0) {
-        seg_r[b * nseg + s] = tr;
-        seg_p[b * nseg + s] = tp;
+    merge_rows<GREEDY>(g, sa, b * (gamma + 1), nt, 0, stage, lm, lr, ls, li, rs);
+    if constexpr (!GREEDY) merge_rows<GREEDY>(g, sa, g.rows_t + b * gamma, nd, nt, stage, lm, lr, ls, li, rs);
+
+    if (wave0) {
+        const int i = lane;
+        const int64_t R = 2 * gamma + 1;
+        const bool dbg = s == 0;
+        int status = kAcc;
+        float mt = NAN, md = NAN;
+        double st = NAN, sd = NAN;
+        bool ut = false;
+        int32_t amax = -1;
+        if (i <= gamma) {
+            const RowStat t = rs[i];
+            mt = t.m;
+            if constexpr (GREEDY) {
+                amax = t.arg;
+                ut = isfinite(mt);
+                if (dbg && a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
+                if (dbg && a.dbg_argmax) a.dbg_argmax[b * (gamma + 1) + i] = amax;
+            } else {
+                st = t.s;
+                ut = usable(mt, st);
+                if (dbg && a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
+                if (dbg && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + i] = st;
+            }
+        }
+        if (i < gamma) {
+            if constexpr (GREEDY) {
+                status = (!ut || !tok_ok) ? kBad : (x == amax ? kAcc : kRej);
+            } else {
+                const RowStat dr = rs[nt + i];
+                md = dr.m;
+                sd = dr.s;
+                const bool ud = usable(md, sd);
+                if (dbg && a.dbg_row_max) a.dbg_row_max[b * R + gamma + 1 + i] = md;
+                if (dbg && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + gamma + 1 + i] = sd;
+                double p = NAN, q = NAN;
+                if (!ut || !ud || !tok_ok) {
+                    status = kBad;
+                } else {
+                    const double c = static_cast<double>(a.c32);
+                    p = exp2((static_cast<double>(lt) - static_cast<double>(mt)) * c) / st;
+                    q = exp2((static_cast<double>(ld) - static_cast<double>(md)) * c) / sd;
+                    const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+                    const double u = philox_uniform(a.seed, static_cast<uint32_t>(b + a.b_offset),
+                                                    static_cast<uint32_t>(i), 0u);
+                    status = u < alpha ? kAcc : kRej;
+                }
+                if (dbg && a.dbg_p) a.dbg_p[b * gamma + i] = p;
+                if (dbg && a.dbg_q) a.dbg_q[b * gamma + i] = q;
+            }
+        }
+        const uint64_t stop = __ballot(i < gamma && status != kAcc);
+        const int f = stop ? __ffsll(static_cast<unsigned long long>(stop)) - 1 : gamma;
+        const int fstat = __shfl(status, f, kWave);
+        const bool bonus_ok = __shfl(ut ? 1 : 0, gamma, kWave) != 0;
+        const bool invalid = f < gamma ? (fstat == kBad) : !bonus_ok;
+        const int k = invalid ? -1 : f;
+        if (s == 0) {
+            if (i <= gamma) {
+                int32_t o = -1;
+                if (!invalid) {
+                    if (i < k) o = x;
+                    else if (GREEDY && i == k) o = amax;
+                }
+                a.out_tokens[b * (gamma + 1) + i] = o;
+            }
+            if (i == 0) a.out_n[b] = k;
+        }
+        if constexpr (!GREEDY) {
+            if (!invalid && i == k) {
+                SeqInfo si;
+                si.k = k; si.mp = mt; si.mq = k < gamma ? md : 0.0f; si.pad = 0;
+                si.sp = st; si.sq = k < gamma ? sd : 1.0;
+                sh.si = si;
+                if (s == 0) a.info[b] = si;
+            } else if (invalid && i == 0) {
+                SeqInfo si;
+                si.k = -1; si.mp = 0.0f; si.mq = 0.0f; si.pad = 0; si.sp = 1.0; si.sq = 1.0;
+                sh.si = si;
+                if (s == 0) a.info[b] = si;
+            }
+        }
+    }
+    if constexpr (!GREEDY) {
+        __syncthreads();
+        const SeqInfo in = sh.si;
+        if (in.k < 0) return;
+        // this block's segment of the residual (t units)
+        const float c32 = a.c32;
+        const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V, c32);
+        const bool has_q = rr.qrow != nullptr;
+        const int64_t e0 = static_cast<int64_t>(s) * kSeg3;
+        const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
+        double sum = 0.0;
+        if constexpr (VEC) {
+            constexpr int EPL = 16 / ElemBytes<DT>::value;
+            for (int64_t e = e0 + threadIdx.x * EPL; e < e1; e += kBlock * EPL) {
+                const uint4 wp = *reinterpret_cast<const uint4*>(rr.prow + e * ElemBytes<DT>::value);
+                uint4 wq = wp;
+                if (has_q) wq = *reinterpret_cast<const uint4*>(rr.qrow + e * ElemBytes<DT>::value);
+                float xp[EPL], xq[EPL];
+                Chunk<DT, true>::expand(wp, xp);
+                Chunk<DT, true>::expand(wq, xq);
+#pragma unroll
+                for (int v = 0; v < EPL; ++v) sum += resid_t(xp[v], xq[v], has_q, c32, rr);
+            }
+        } else {
+            for (int64_t e = e0 + threadIdx.x; e < e1; e += kBlock)
+                sum += resid_t(load_one<DT>(rr.prow, e), has_q ? load_one<DT>(rr.qrow, e) : 0.0f, has_q, c32, rr);
+        }
+        const double tot = block_sum(sum, sh.red);
+        if (threadIdx.x == 0) a.seg[b * nseg + s] = tot;
     }
 }
 
 // --------------------------------------------------------------------------
-// K3b: the inverse-CDF draw. One block per sequence.
+// k_draw: one block per sequence.
 // --------------------------------------------------------------------------
+struct DrawArgs {
+    int32_t gamma, V, nseg;
+    float c32;
+    uint64_t seed;
+    int64_t b_offset;
+    const SeqInfo* info;
+    const double* seg;
+    int32_t* out_tokens;
+    double* dbg_z;
+};
+
+struct DrawShared {
+    double red[kWavesPerBlock];
+    double before;
+    int seg, found, last_pos;
+};
+
+// Whole block: the first j in [e0, e1) (e1 - e0 <= kSeg3, ascending) whose
+// cumulative mass exceeds t; if rounding leaves none, the last j with mass.
+// Thread k owns kPerThread consecutive elements, loaded together and kept in
+// registers; a block scan locates the owner, which walks its registers.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_draw(const void* __restrict__ tgt,
-                                                 const void* __restrict__ dft, int32_t gamma,
-                                                 int32_t V, int32_t nseg, float c32, uint64_t seed,
-                                                 int64_t b_offset, const SeqInfo* __restrict__ info,
-                                                 const double* __restrict__ seg_r,
-                                                 const double* __restrict__ seg_p,
-                                                 int32_t* __restrict__ out_tokens,
-                                                 double* __restrict__ dbg_z) {
-    __shared__ double wave_tot[kWavesPerBlock];
-    __shared__ double sh_t;
-    __shared__ int sh_seg, sh_use_p, sh_found, sh_last;
-    const int64_t b = blockIdx.x;
-    const SeqInfo in = info[b];
-    if (in.k < 0) {
-        if (dbg_z && threadIdx.x == 0) dbg_z[b] = NAN;
-        return;
+__device__ void draw_in_range(const ResidRow& rr, bool has_q, float c32, int64_t e0, int64_t e1, double t,
+                              DrawShared& sh, int32_t* out) {
+    const int64_t j0 = e0 + static_cast<int64_t>(threadIdx.x) * kPerThread;
+    float xp[kPerThread], xq[kPerThread];
+#pragma unroll
+    for (int v = 0; v < kPerThread; ++v) {
+        const bool in = j0 + v < e1;
+        xp[v] = in ? load_one<DT>(rr.prow, j0 + v) : -INFINITY;
+        xq[v] = in && has_q ? load_one<DT>(rr.qrow, j0 + v) : 0.0f;
     }
-    if (threadIdx.x == 0) {
-        double Z = 0.0;
-        for (int s = 0; s < nseg; ++s) Z += seg_r[b * nseg + s];
-        if (dbg_z) dbg_z[b] = Z;
-        const bool use_p = !(Z > 0.0);  // rounding left no residual mass: draw from p
-        const double* seg = use_p ? seg_p + b * nseg : seg_r + b * nseg;
-        if (use_p) {
-            Z = 0.0;
-            for (int s = 0; s < nseg; ++s) Z += seg[s];
-        }
-        const double u = philox_uniform(seed, static_cast<uint32_t>(b + b_offset),
-                                        static_cast<uint32_t>(in.k), 1u);
-        const double t = u * Z;
-        double run = 0.0;
-        int chosen = -1, last_pos = 0;
-        double before = 0.0;
-        for (int s = 0; s < nseg; ++s) {
-            const double nxt = run + seg[s];
-            if (seg[s] > 0.0) last_pos = s;
-            if (chosen < 0 && nxt > t) { chosen = s; before = run; }
-            run = nxt;
-        }
-        if (chosen < 0) {  // rounding guard: the last segment with mass
-            chosen = last_pos;
-            before = 0.0;
-            for (int s = 0; s < chosen; ++s) before += seg[s];
-        }
-        sh_seg = chosen;
-        sh_t = t - before;
-        sh_use_p = use_p ? 1 : 0;
-        sh_found = 0;
-        sh_last = -1;
-    }
-    __syncthreads();
-    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V, c32);
-    const bool has_q = rr.qrow != nullptr && !sh_use_p;
-    const int64_t e0 = static_cast<int64_t>(sh_seg) * kSeg3;
-    const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-    const int64_t per = (e1 - e0 + kBlock - 1) / kBlock;
-    const int64_t j0 = e0 + threadIdx.x * per;
-    const int64_t j1 = j0 + per < e1 ? j0 + per : e1;
-    // this thread's mass, in ascending index order
+    double m[kPerThread];
     double local = 0.0;
     int32_t mylast = -1;
-    for (int64_t j = j0; j < j1; ++j) {
-        double r, p;
-        resid_val(load_one<DT>(rr.prow, j), has_q ? load_one<DT>(rr.qrow, j) : 0.0f, has_q, c32, rr, r, p);
-        const double m = sh_use_p ? p : r;
-        local += m;
-        if (m > 0.0) mylast = static_cast<int32_t>(j);
-    }
-    // inclusive scan over the block: within the wave, then across waves
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
-    double incl = local;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
+    for (int v = 0; v < kPerThread; ++v) {
+        m[v] = j0 + v < e1 ? resid_t(xp[v], xq[v], has_q, c32, rr) : 0.0;
+        local += m[v];
+        if (m[v] > 0.0) mylast = static_cast<int32_t>(j0 + v);
     }
-    if (lane == kWave - 1) wave_tot[wid] = incl;
-    __syncthreads();
-    double wave_base = 0.0;
-    for (int k = 0; k < wid; ++k) wave_base += wave_tot[k];
-    incl += wave_base;
-    double excl = __shfl_up(incl, 1, kWave);
-    if (lane == 0) excl = wave_base;
-    const double t = sh_t;
-    if (mylast >= 0) atomicMax(&sh_last, mylast);
+    if (threadIdx.x == 0) { sh.found = 0; sh.last_pos = -1; }
+    double incl, excl, tot;
+    block_scan(local, sh.red, incl, excl, tot);  // its barriers also publish the resets above
+    if (mylast >= 0) atomicMax(&sh.last_pos, mylast);
     if (excl <= t && t < incl) {
-        // the crossing lies in this thread's elements
         double run = excl;
         int32_t pick = -1;
-        for (int64_t j = j0; j < j1; ++j) {
-            double r, p;
-            resid_val(load_one<DT>(rr.prow, j), has_q ? load_one<DT>(rr.qrow, j) : 0.0f, has_q, c32, rr, r, p);
-            const double m = sh_use_p ? p : r;
-            run += m;
-            if (m > 0.0 && run > t) { pick = static_cast<int32_t>(j); break; }
+#pragma unroll
+        for (int v = 0; v < kPerThread; ++v) {
+            run += m[v];
+            if (pick < 0 && m[v] > 0.0 && run > t) pick = static_cast<int32_t>(j0 + v);
         }
-        if (pick < 0) pick = mylast;  // rounding guard inside the thread's range
-        out_tokens[b * (gamma + 1) + in.k] = pick;
-        sh_found = 1;
+        *out = pick >= 0 ? pick : mylast;
+        sh.found = 1;
     }
     __syncthreads();
-    if (threadIdx.x == 0 && !sh_found) out_tokens[b * (gamma + 1) + in.k] = sh_last;
+    if (threadIdx.x == 0 && !sh.found) *out = sh.last_pos;
+}
+
+// Segment holding `target` among per-segment masses mass(t), t < nseg: sets
+// sh.seg and sh.before (the mass of the segments before it). Guard: the last
+// segment with mass.
+template <typename F>
+__device__ void find_segment(int nseg, double target, F mass, DrawShared& sh) {
+    if (threadIdx.x == 0) { sh.seg = -1; sh.last_pos = 0; sh.before = 0.0; }
+    double base = 0.0;
+    for (int t0 = 0; t0 < nseg; t0 += kBlock) {
+        const int t = t0 + threadIdx.x;
+        const double v = t < nseg ? mass(t) : 0.0;
+        double incl, excl, tot;
+        block_scan(v, sh.red, incl, excl, tot);
+        incl += base;
+        excl += base;
+        if (t < nseg && v > 0.0) atomicMax(&sh.last_pos, t);
+        if (t < nseg && excl <= target && target < incl) { sh.seg = t; sh.before = excl; }
+        base += tot;
+        __syncthreads();
+        if (sh.seg >= 0) break;
+    }
+    if (sh.seg < 0) {  // rounding: the last segment with mass and the mass before it
+        const int chosen = sh.last_pos;
+        double bz = 0.0;
+        for (int t = threadIdx.x; t < chosen; t += kBlock) bz += mass(t);
+        const double before = block_sum(bz, sh.red);
+        if (threadIdx.x == 0) { sh.seg = chosen; sh.before = before; }
+        __syncthreads();
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_draw(const void* __restrict__ tgt, const void* __restrict__ dft,
+                                                 DrawArgs d) {
+    __shared__ DrawShared sh;
+    const int64_t b = blockIdx.x;
+    const SeqInfo in = d.info[b];
+    if (in.k < 0) {
+        if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = NAN;
+        return;
+    }
+    const int32_t gamma = d.gamma, V = d.V, nseg = d.nseg;
+    const float c32 = d.c32;
+    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V, c32);
+    const bool has_q = rr.qrow != nullptr;
+    const double* seg = d.seg + b * nseg;
+    int32_t* out = d.out_tokens + b * (gamma + 1) + in.k;
+    double z = 0.0;
+    for (int t = threadIdx.x; t < nseg; t += kBlock) z += seg[t];
+    const double Z = block_sum(z, sh.red);
+    if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = Z * rr.scale_p;
+    const double u = philox_uniform(d.seed, static_cast<uint32_t>(b + d.b_offset), static_cast<uint32_t>(in.k), 1u);
+    bool draw_p = false;
+    double target = u * Z;
+    auto segmass = [&](int t) -> double { return seg[t]; };
+    // rounding left no residual mass at a rejected row: draw from p_k, with the
+    // segment masses of p formed here (a rare, slow path)
+    auto pmass = [&](int t) -> double {
+        const int64_t e0 = static_cast<int64_t>(t) * kSeg3;
+        const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
+        double acc = 0.0;
+        for (int64_t j = e0; j < e1; ++j) acc += resid_t(load_one<DT>(rr.prow, j), 0.0f, false, c32, rr);
+        return acc;
+    };
+    if (!(Z > 0.0)) {
+        draw_p = true;
+        double zp = 0.0;
+        for (int t = threadIdx.x; t < nseg; t += kBlock) zp += pmass(t);
+        target = u * block_sum(zp, sh.red);
+        find_segment(nseg, target, pmass, sh);
+    } else {
+        find_segment(nseg, target, segmass, sh);
+    }
+    const int64_t e0 = static_cast<int64_t>(sh.seg) * kSeg3;
+    const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
+    draw_in_range<DT>(rr, has_q && !draw_p, c32, e0, e1, target - sh.before, sh, out);
 }
 
 // --------------------------------------------------------------------------
 // Row statistics output for spec_row_stats: one thread per row.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_merge_rows(StatsGeom g, float c32,
-                                                       const float* __restrict__ part_m,
-                                                       const double* __restrict__ part_s,
-                                                       float* __restrict__ row_max,
+__global__ __launch_bounds__(kBlock) void k_merge_rows(Geom g, StatsArgs sa, float* __restrict__ row_max,
                                                        double* __restrict__ row_sumexp) {
     const int64_t r = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
     if (r >= g.rows) return;
-    float M;
-    double S;
-    merge_stats(g, r, c32, part_m, part_s, M, S);
-    row_max[r] = M;
-    row_sumexp[r] = usable(M, S) ? S : NAN;
+    const int64_t at = r * g.maxp;
+    const RowStat o = fold_row<false>(pieces_of(g, r), sa.part_m + at, sa.part_r + at, sa.part_s + at,
+                                      sa.part_i + at, sa.c32);
+    row_max[r] = o.m;
+    row_sumexp[r] = usable(o.m, o.s) ? o.s : NAN;
 }
 
 // ==========================================================================
@@ -736,14 +886,13 @@ struct Workspace {
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> buffer
 std::map<int, int> g_cus;                         // device -> compute units
-std::map<std::pair<int, const void*>, int> g_occ; // (device, kernel) -> resident blocks per CU
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    StatsGeom g;
+    Geom g;
     int32_t nseg3;
-    size_t off_pm, off_ps, off_pi, off_info, off_segr, off_segp, total;
+    size_t off_pm, off_pr, off_ps, off_pi, off_info, off_seg, bytes;
 };
 
 int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
@@ -751,43 +900,37 @@ int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
 // Chunk geometry: vector chunks are 1 KiB; scalar chunks are 64 x 4 elements.
 int32_t chunk_elems(int32_t dtype, bool vec) { return vec ? kWave * (16 / elem_bytes(dtype)) : kWave * 4; }
 
-Layout plan(int64_t rows_t, int64_t rows, int32_t V, int32_t dtype, bool vec, int64_t B,
-            int64_t wave_slots) {
+// Wave ranges of about kChunksPerWave chunks (many more waves than the chip
+// holds at once, which keeps its tail short), but at least 16 wavefronts per
+// compute unit so that small problems still spread over the chip.
+Layout plan(int64_t rows_t, int64_t rows, int32_t V, int32_t dtype, bool vec, int32_t B, int cus) {
     Layout L{};
-    StatsGeom& g = L.g;
+    Geom& g = L.g;
     g.rows_t = rows_t;
     g.rows = rows;
     g.V = V;
     const int32_t CH = chunk_elems(dtype, vec);
     g.nchunk = (V + CH - 1) / CH;
     const int64_t total = rows * g.nchunk;
-    int64_t cpw = (total + wave_slots - 1) / wave_slots;
-    if (cpw < kMinChunksPerWave) cpw = kMinChunksPerWave;
+    const int64_t min_waves = static_cast<int64_t>(cus) * 16;
+    int64_t cpw = kChunksPerWave;
+    if ((total + cpw - 1) / cpw < min_waves) cpw = (total + min_waves - 1) / min_waves;
+    if (cpw < 1) cpw = 1;
     g.cpw = cpw;
     g.nwaves = (total + cpw - 1) / cpw;
     g.maxp = static_cast<int32_t>((g.nchunk + cpw - 1) / cpw + 1);
     L.nseg3 = (V + kSeg3 - 1) / kSeg3;
     const size_t slots = static_cast<size_t>(rows) * g.maxp;
+    const size_t nb = static_cast<size_t>(B > 0 ? B : 1);
     size_t o = 0;
     L.off_pm = o; o = align_up(o + slots * sizeof(float), 256);
+    L.off_pr = o; o = align_up(o + slots * sizeof(float), 256);
     L.off_ps = o; o = align_up(o + slots * sizeof(double), 256);
     L.off_pi = o; o = align_up(o + slots * sizeof(int32_t), 256);
-    L.off_info = o; o = align_up(o + static_cast<size_t>(B) * sizeof(SeqInfo), 256);
-    L.off_segr = o; o = align_up(o + static_cast<size_t>(B) * L.nseg3 * sizeof(double), 256);
-    L.off_segp = o; o = align_up(o + static_cast<size_t>(B) * L.nseg3 * sizeof(double), 256);
-    L.total = o;
+    L.off_info = o; o = align_up(o + nb * sizeof(SeqInfo), 256);
+    L.off_seg = o; o = align_up(o + nb * L.nseg3 * sizeof(double), 256);
+    L.bytes = o;
     return L;
-}
-
-// Resident blocks per CU for a kernel (queried once per device and kernel).
-int resident_blocks(int dev, const void* kernel) {
-    auto key = std::make_pair(dev, kernel);
-    auto it = g_occ.find(key);
-    if (it != g_occ.end()) return it->second;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) n = 1;
-    g_occ[key] = n;
-    return n;
 }
 
 int compute_units(int dev) {
@@ -806,12 +949,11 @@ int get_workspace(int dev, hipStream_t stream, size_t bytes, char** out) {
         if (ws.ptr) {
             if (hipStreamSynchronize(stream) != hipSuccess) return fail(SPEC_EHIP, "hipStreamSynchronize failed");
             (void)hipFree(ws.ptr);
-            ws.ptr = nullptr;
-            ws.bytes = 0;
+            ws = Workspace{};
         }
         const size_t want = align_up(bytes + bytes / 4, 1 << 20);
         if (hipMalloc(&ws.ptr, want) != hipSuccess) {
-            ws.ptr = nullptr;
+            ws = Workspace{};
             (void)hipGetLastError();
             return fail(SPEC_ENOMEM, "hipMalloc of the workspace failed");
         }
@@ -821,45 +963,54 @@ int get_workspace(int dev, hipStream_t stream, size_t bytes, char** out) {
     return SPEC_OK;
 }
 
-template <typename K>
-const void* kptr(K k) { return reinterpret_cast<const void*>(k); }
+StatsArgs stats_args(const Layout& L, char* ws, float c32) {
+    StatsArgs sa{};
+    sa.c32 = c32;
+    sa.part_m = reinterpret_cast<float*>(ws + L.off_pm);
+    sa.part_r = reinterpret_cast<float*>(ws + L.off_pr);
+    sa.part_s = reinterpret_cast<double*>(ws + L.off_ps);
+    sa.part_i = reinterpret_cast<int32_t*>(ws + L.off_pi);
+    return sa;
+}
 
-const void* stats_kernel(int32_t dtype, bool vec, bool greedy) {
+template <int DT, bool VEC>
+void launch_stats_t(bool greedy, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
+                    hipStream_t st) {
+    const unsigned blocks = static_cast<unsigned>((g.nwaves + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (greedy) k_stats<DT, VEC, true><<<blocks, kBlock, 0, st>>>(tgt, dft, g, sa);
+    else k_stats<DT, VEC, false><<<blocks, kBlock, 0, st>>>(tgt, dft, g, sa);
+}
+
+void launch_stats(int32_t dtype, bool vec, bool greedy, const void* tgt, const void* dft, const Geom& g,
+                  const StatsArgs& sa, hipStream_t st) {
+    if (dtype == SPEC_F32) {
+        if (vec) launch_stats_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, st);
+        else launch_stats_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, st);
+    } else {
+        if (vec) launch_stats_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, st);
+        else launch_stats_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, st);
+    }
+}
+
+template <int DT, bool VEC>
+void launch_accept_t(bool greedy, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
+                     const AcceptArgs& a, size_t lds, hipStream_t st) {
     if (greedy) {
-        if (dtype == SPEC_F32) return vec ? kptr(k_argmax<SPEC_F32, true>) : kptr(k_argmax<SPEC_F32, false>);
-        return vec ? kptr(k_argmax<SPEC_BF16, true>) : kptr(k_argmax<SPEC_BF16, false>);
-    }
-    if (dtype == SPEC_F32) return vec ? kptr(k_stats<SPEC_F32, true>) : kptr(k_stats<SPEC_F32, false>);
-    return vec ? kptr(k_stats<SPEC_BF16, true>) : kptr(k_stats<SPEC_BF16, false>);
-}
-
-int64_t wave_slots_for(int dev, int32_t dtype, bool vec, bool greedy) {
-    const int cus = compute_units(dev);
-    const int occ = resident_blocks(dev, stats_kernel(dtype, vec, greedy));
-    return static_cast<int64_t>(cus) * occ * kWavesPerBlock;
-}
-
-void launch_stats(int32_t dtype, bool vec, const void* tgt, const void* dft, const StatsGeom& g,
-                  float c32, float* pm, double* ps, hipStream_t st) {
-    const unsigned blocks = static_cast<unsigned>((g.nwaves + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (dtype == SPEC_F32) {
-        if (vec) k_stats<SPEC_F32, true><<<blocks, kBlock, 0, st>>>(tgt, dft, g, c32, pm, ps);
-        else k_stats<SPEC_F32, false><<<blocks, kBlock, 0, st>>>(tgt, dft, g, c32, pm, ps);
+        k_accept<DT, VEC, true><<<static_cast<unsigned>(a.B), kBlock, lds, st>>>(tgt, dft, g, sa, a);
     } else {
-        if (vec) k_stats<SPEC_BF16, true><<<blocks, kBlock, 0, st>>>(tgt, dft, g, c32, pm, ps);
-        else k_stats<SPEC_BF16, false><<<blocks, kBlock, 0, st>>>(tgt, dft, g, c32, pm, ps);
+        const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.nseg);
+        k_accept<DT, VEC, false><<<blocks, kBlock, lds, st>>>(tgt, dft, g, sa, a);
     }
 }
 
-void launch_argmax(int32_t dtype, bool vec, const void* tgt, const StatsGeom& g, float* pm,
-                   int32_t* pi, hipStream_t st) {
-    const unsigned blocks = static_cast<unsigned>((g.nwaves + kWavesPerBlock - 1) / kWavesPerBlock);
+void launch_accept(int32_t dtype, bool vec, bool greedy, const void* tgt, const void* dft, const Geom& g,
+                   const StatsArgs& sa, const AcceptArgs& a, size_t lds, hipStream_t st) {
     if (dtype == SPEC_F32) {
-        if (vec) k_argmax<SPEC_F32, true><<<blocks, kBlock, 0, st>>>(tgt, g, pm, pi);
-        else k_argmax<SPEC_F32, false><<<blocks, kBlock, 0, st>>>(tgt, g, pm, pi);
+        if (vec) launch_accept_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, a, lds, st);
+        else launch_accept_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, a, lds, st);
     } else {
-        if (vec) k_argmax<SPEC_BF16, true><<<blocks, kBlock, 0, st>>>(tgt, g, pm, pi);
-        else k_argmax<SPEC_BF16, false><<<blocks, kBlock, 0, st>>>(tgt, g, pm, pi);
+        if (vec) launch_accept_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, a, lds, st);
+        else launch_accept_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, a, lds, st);
     }
 }
 
@@ -872,6 +1023,8 @@ int check_launch(const char* what) {
     if (e != hipSuccess) return fail(SPEC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
     return SPEC_OK;
 }
+
+constexpr int64_t kMaxChunks = int64_t(1) << 31;
 
 }  // namespace
 
@@ -894,7 +1047,7 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t 
     const int64_t rows_t = static_cast<int64_t>(B) * (gamma + 1);
     const int64_t rows = greedy ? rows_t : rows_t + static_cast<int64_t>(B) * gamma;
     std::lock_guard<std::mutex> lk(g_mu);
-    return plan(rows_t, rows, V, dtype, vec, B, wave_slots_for(dev, dtype, vec, greedy)).total;
+    return plan(rows_t, rows, V, dtype, vec, B, compute_units(dev)).bytes;
 }
 
 void spec_verify_release_workspace(void) {
@@ -930,8 +1083,8 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     const int64_t es = elem_bytes(dtype);
     const int64_t rows_t = static_cast<int64_t>(B) * (gamma + 1);
     const int64_t rows = greedy ? rows_t : rows_t + static_cast<int64_t>(B) * gamma;
-    if (rows > (int64_t(1) << 40) / V) return fail(SPEC_EINVAL, "problem too large");
-    if (static_cast<int64_t>(B) * ((V + kSeg3 - 1) / kSeg3) > INT32_MAX)
+    const int64_t nseg3 = (V + kSeg3 - 1) / kSeg3;
+    if (rows * ((V + 255) / 256) >= kMaxChunks || static_cast<int64_t>(B) * nseg3 > INT32_MAX)
         return fail(SPEC_EINVAL, "problem too large");
     const bool vec = (static_cast<int64_t>(V) * es) % 16 == 0 && aligned16(target_logits) &&
                      (greedy || aligned16(draft_logits));
@@ -940,35 +1093,24 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
 
     std::lock_guard<std::mutex> lk(g_mu);
-    const Layout L = plan(rows_t, rows, V, dtype, vec, B, wave_slots_for(dev, dtype, vec, greedy));
+    const Layout L = plan(rows_t, rows, V, dtype, vec, B, compute_units(dev));
     char* ws = nullptr;
-    if (int rc = get_workspace(dev, st, L.total, &ws)) return rc;
-    float* pm = reinterpret_cast<float*>(ws + L.off_pm);
-    double* ps = reinterpret_cast<double*>(ws + L.off_ps);
-    int32_t* pi = reinterpret_cast<int32_t*>(ws + L.off_pi);
+    if (int rc = get_workspace(dev, st, L.bytes, &ws)) return rc;
+    const StatsArgs sa = stats_args(L, ws, c32);
     SeqInfo* info = reinterpret_cast<SeqInfo*>(ws + L.off_info);
-    double* segr = reinterpret_cast<double*>(ws + L.off_segr);
-    double* segp = reinterpret_cast<double*>(ws + L.off_segp);
-
-    auto ev = [&](int k) {
-        if (extras && extras->events[k]) (void)hipEventRecord(static_cast<hipEvent_t>(extras->events[k]), st);
-    };
-
-    ev(0);
-    if (greedy) launch_argmax(dtype, vec, target_logits, L.g, pm, pi, st);
-    else launch_stats(dtype, vec, target_logits, draft_logits, L.g, c32, pm, ps, st);
-    if (int rc = check_launch("statistics kernel")) return rc;
-    ev(1);
 
     AcceptArgs a{};
     a.tokens = draft_tokens;
-    a.B = B; a.gamma = gamma; a.V = V;
+    a.B = B; a.gamma = gamma; a.V = V; a.nseg = L.nseg3;
+    const int run_slots = (gamma + 1) * L.g.maxp;  // the larger of the two row runs
+    a.stage = run_slots <= kMaxMergeSlots ? run_slots : 0;
     a.c32 = c32;
     a.seed = seed;
     a.b_offset = extras ? extras->b_offset : 0;
     a.out_tokens = out_tokens;
     a.out_n = out_n_accepted;
     a.info = info;
+    a.seg = reinterpret_cast<double*>(ws + L.off_seg);
     if (extras) {
         a.dbg_row_max = extras->row_max;
         a.dbg_row_sumexp = extras->row_sumexp;
@@ -976,35 +1118,35 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
         a.dbg_q = extras->q_draft;
         a.dbg_argmax = extras->argmax;
     }
-    const unsigned kb = static_cast<unsigned>((B + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (dtype == SPEC_F32) {
-        if (greedy) k_accept<SPEC_F32, true><<<kb, kBlock, 0, st>>>(target_logits, draft_logits, L.g, a, pm, ps, pi);
-        else k_accept<SPEC_F32, false><<<kb, kBlock, 0, st>>>(target_logits, draft_logits, L.g, a, pm, ps, pi);
-    } else {
-        if (greedy) k_accept<SPEC_BF16, true><<<kb, kBlock, 0, st>>>(target_logits, draft_logits, L.g, a, pm, ps, pi);
-        else k_accept<SPEC_BF16, false><<<kb, kBlock, 0, st>>>(target_logits, draft_logits, L.g, a, pm, ps, pi);
-    }
+    const int nrows_seq = greedy ? gamma + 1 : 2 * gamma + 1;
+    const size_t lds = align_up(static_cast<size_t>(a.stage) * 20, 16) + static_cast<size_t>(nrows_seq) * sizeof(RowStat);
+    auto ev = [&](int k) {
+        if (extras && extras->events[k]) (void)hipEventRecord(static_cast<hipEvent_t>(extras->events[k]), st);
+    };
+
+    ev(0);
+    launch_stats(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, st);
+    if (int rc = check_launch("statistics kernel")) return rc;
+    ev(1);
+    launch_accept(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, a, lds, st);
     if (int rc = check_launch("accept kernel")) return rc;
-    ev(2);
-    if (greedy) return SPEC_OK;
-    const unsigned g3 = static_cast<unsigned>(static_cast<int64_t>(L.nseg3) * B);
-    double* dz = extras ? extras->Z : nullptr;
-    const int64_t boff = extras ? extras->b_offset : 0;
-    if (dtype == SPEC_F32) {
-        if (vec) k_resid<SPEC_F32, true><<<g3, kBlock, 0, st>>>(target_logits, draft_logits, gamma, V, L.nseg3, c32, info, segr, segp);
-        else k_resid<SPEC_F32, false><<<g3, kBlock, 0, st>>>(target_logits, draft_logits, gamma, V, L.nseg3, c32, info, segr, segp);
-    } else {
-        if (vec) k_resid<SPEC_BF16, true><<<g3, kBlock, 0, st>>>(target_logits, draft_logits, gamma, V, L.nseg3, c32, info, segr, segp);
-        else k_resid<SPEC_BF16, false><<<g3, kBlock, 0, st>>>(target_logits, draft_logits, gamma, V, L.nseg3, c32, info, segr, segp);
+    if (!greedy) {
+        DrawArgs d{};
+        d.gamma = gamma;
+        d.V = V;
+        d.nseg = L.nseg3;
+        d.c32 = c32;
+        d.seed = seed;
+        d.b_offset = a.b_offset;
+        d.info = info;
+        d.seg = a.seg;
+        d.out_tokens = out_tokens;
+        d.dbg_z = extras ? extras->Z : nullptr;
+        if (dtype == SPEC_F32) k_draw<SPEC_F32><<<static_cast<unsigned>(B), kBlock, 0, st>>>(target_logits, draft_logits, d);
+        else k_draw<SPEC_BF16><<<static_cast<unsigned>(B), kBlock, 0, st>>>(target_logits, draft_logits, d);
+        if (int rc = check_launch("draw kernel")) return rc;
     }
-    if (int rc = check_launch("residual kernel")) return rc;
-    ev(3);
-    if (dtype == SPEC_F32)
-        k_draw<SPEC_F32><<<static_cast<unsigned>(B), kBlock, 0, st>>>(target_logits, draft_logits, gamma, V, L.nseg3, c32, seed, boff, info, segr, segp, out_tokens, dz);
-    else
-        k_draw<SPEC_BF16><<<static_cast<unsigned>(B), kBlock, 0, st>>>(target_logits, draft_logits, gamma, V, L.nseg3, c32, seed, boff, info, segr, segp, out_tokens, dz);
-    if (int rc = check_launch("draw kernel")) return rc;
-    ev(4);
+    ev(2);
     return SPEC_OK;
 }
 
@@ -1023,21 +1165,20 @@ int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype, f
     if (!logits || !row_max || !row_sumexp) return fail(SPEC_EINVAL, "null pointer argument");
     const float c32 = fold_temperature(temperature);
     if (!(std::isfinite(c32) && c32 > 0.0f)) return fail(SPEC_EINVAL, "temperature out of range");
-    if (rows > (int64_t(1) << 40) / V) return fail(SPEC_EINVAL, "problem too large");
+    if (rows * ((V + 255) / 256) >= kMaxChunks) return fail(SPEC_EINVAL, "problem too large");
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(logits);
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
-    const Layout L = plan(rows, rows, V, dtype, vec, 1, wave_slots_for(dev, dtype, vec, false));
+    const Layout L = plan(rows, rows, V, dtype, vec, 0, compute_units(dev));
     char* ws = nullptr;
-    if (int rc = get_workspace(dev, st, L.total, &ws)) return rc;
-    float* pm = reinterpret_cast<float*>(ws + L.off_pm);
-    double* ps = reinterpret_cast<double*>(ws + L.off_ps);
-    launch_stats(dtype, vec, logits, nullptr, L.g, c32, pm, ps, st);
+    if (int rc = get_workspace(dev, st, L.bytes, &ws)) return rc;
+    const StatsArgs sa = stats_args(L, ws, c32);
+    launch_stats(dtype, vec, false, logits, nullptr, L.g, sa, st);
     if (int rc = check_launch("statistics kernel")) return rc;
     const unsigned blocks = static_cast<unsigned>((rows + kBlock - 1) / kBlock);
-    k_merge_rows<<<blocks, kBlock, 0, st>>>(L.g, c32, pm, ps, row_max, row_sumexp);
+    k_merge_rows<<<blocks, kBlock, 0, st>>>(L.g, sa, row_max, row_sumexp);
     return check_launch("merge kernel");
 }
 
