@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the oracle sample (0: auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the benchmark, run --steps plain device-to-device copies of the "
+                         "workload's compulsory byte count (the reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the verification step has no multi-GPU path "
@@ -116,6 +119,22 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.workload]
+    if args.copy_calibration:
+        nbytes = wl.compulsory_bytes()
+        src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / args.steps * 1e3
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": args.steps,
+                          "us_per_copy": us, "GBps_read_plus_write": 2 * nbytes / us / 1e3}), flush=True)
+        return
     tdt = torch.float32 if wl.dtype == W.F32 else torch.bfloat16
 
     def to_dev(a):

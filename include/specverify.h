@@ -105,9 +105,10 @@ typedef struct {
     int32_t* argmax;       /* [B, gamma+1]: argmax of each target row (T == 0 only) */
     int64_t b_offset;      /* added to b in the Philox counter, so that a shard of a
                               larger batch draws the same uniforms as the whole batch */
-    void* events[3];       /* optional hipEvent_t (host handles) recorded on `stream`:
-                              [0] before the statistics kernel, [1] after it, [2] after
-                              the last kernel of the call (accept, residual sums, draw) */
+    void* events[3];       /* optional hipEvent_t (host handles), bound to the kernel
+                              dispatches themselves (no extra stream packets): [0] start
+                              and [1] end of the statistics kernel, [2] end of the call's
+                              last kernel */
 } spec_extras_t;
 
 /* spec_verify with extras (NULL extras == spec_verify). Same kernels. */

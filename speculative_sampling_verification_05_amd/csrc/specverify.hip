@@ -36,6 +36,7 @@
 // Exponentials are fp32 (v_exp_f32 on one FMA); every sum and comparison that
 // decides a token is fp64.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -113,6 +114,14 @@ __device__ inline float load_one(const char* row, int64_t j) {
     }
 }
 
+// Logits are streamed exactly once by the statistics pass: 16-byte
+// non-temporal loads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_stream(const char* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // A chunk is 64 lanes x EPL elements. Vector path (rows 16-byte aligned): lane l
 // holds elements [l*EPL, l*EPL+EPL) from one 16-byte load, kept raw until
 // consumed. Scalar path: lane l holds elements l, l+64, l+128, l+192, converted
@@ -124,7 +133,7 @@ template <int DT, bool VEC> struct Chunk {
 
     __device__ static inline Raw load_full(const char* row, int64_t c, int lane) {
         if constexpr (VEC) {
-            return *reinterpret_cast<const uint4*>(row + (c * CH + lane * EPL) * ElemBytes<DT>::value);
+            return load_stream(row + (c * CH + lane * EPL) * ElemBytes<DT>::value);
         } else {
             const int64_t j = c * CH + lane;
             return make_float4(load_one<DT>(row, j), load_one<DT>(row, j + kWave),
@@ -231,7 +240,16 @@ struct Geom {
     int64_t cpw;
     int64_t nwaves;
     int32_t maxp;
+    int32_t gamma;
+    const int32_t* tokens;  // draft tokens, or nullptr (no logit gather)
 };
+
+// Index into draft_tokens of the token row r scores (-1: the bonus row).
+__device__ inline int64_t token_of_row(const Geom& g, int64_t r) {
+    if (r >= g.rows_t) return r - g.rows_t;  // draft row b*gamma + i
+    const int64_t b = r / (g.gamma + 1), i = r - b * (g.gamma + 1);
+    return i < g.gamma ? b * g.gamma + i : -1;
+}
 
 template <int DT>
 __device__ inline const char* row_ptr(const void* tgt, const void* dft, const Geom& g, int64_t r) {
@@ -249,15 +267,17 @@ struct StatsArgs {
     float* part_r;    // integer reference of the piece (T > 0)
     double* part_s;   // sum of 2^(x*c - reference) (T > 0)
     int32_t* part_i;  // first index of the maximum (T == 0)
+    float* gath;      // per row: the logit at the row's draft token (written by the piece holding it)
 };
 
 // --------------------------------------------------------------------------
-// k_stats. Lane state at T > 0: m = max seen; R = integer reference (kRUnset
-// until the first finite value); S = sum of 2^(fl(x*c - R)) in fp64, fp32 per
-// load group. A group's exponentials use the current R while its max is
-// formed; if the group's max exceeds R + 1 the reference moves up to
-// ceil(max*c), S is rescaled exactly with ldexp and the group is redone. The
-// wave flush rebases every lane onto the largest lane reference, exactly.
+// k_stats. State at T > 0: per lane m = max seen and S = sum of
+// 2^(fl(x*c - R)) in fp64 (fp32 per load group); R is one integer reference
+// for the whole wavefront (kRUnset until the first finite value), set from the
+// wave's first group max. A group's exponentials use the current R while its
+// max is formed; only if some lane's group max exceeds R + 1 (a ballot) does
+// the wave move R up to ceil(wave max * c), rescale S exactly with ldexp and
+// redo the group. The flush is then a plain wave sum: every lane shares R.
 // --------------------------------------------------------------------------
 struct SoftLane {
     float m;
@@ -300,13 +320,34 @@ __device__ inline void group_sum(const typename Chunk<DT, VEC>::Raw* raw, float 
 }
 
 template <int DT, bool VEC, int N>
+__device__ inline float group_max(const typename Chunk<DT, VEC>::Raw* raw) {
+    using C = Chunk<DT, VEC>;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float x[C::EPL];
+        C::expand(raw[u], x);
+#pragma unroll
+        for (int v = 0; v < C::EPL; ++v) mx = fmaxf(mx, x[v]);
+    }
+    return mx;
+}
+
+template <int DT, bool VEC, int N>
 __device__ inline void consume_group(SoftLane& s, const typename Chunk<DT, VEC>::Raw* raw, int64_t, int,
                                      float c) {
+    if (s.R == kRUnset) {  // no reference yet: take it from the wave's max of this group first
+        const float mx = wave_max(group_max<DT, VEC, N>(raw));
+        if (mx * c > kRUnset + 1.0f) {
+            const float Rn = ceilf(mx * c);
+            if (Rn < 3.0e38f) s.R = Rn;
+        }
+    }
     float gmax, acc;
     group_sum<DT, VEC, N>(raw, c, s.R, gmax, acc);
-    if (gmax * c > s.R + 1.0f) {  // rare: a new maximum well above the reference
-        const float Rn = ceilf(gmax * c);
-        if (!(Rn < 3.0e38f)) {     // +inf logit (or an overflowing one): the row is unusable
+    if (__any(gmax * c > s.R + 1.0f)) {  // rare: a new maximum well above the wave's reference
+        const float Rn = ceilf(wave_max(gmax) * c);
+        if (!(Rn < 3.0e38f)) {  // +inf logit (or an overflowing one): the row is unusable
             s.S = NAN;
             acc = 0.0f;
         } else {
@@ -360,24 +401,39 @@ __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, 
         const int64_t cr_full = cr_end < nfull ? cr_end : nfull;
         Lane st;
         st.init();
+        // the logit at this row's draft token, if this piece holds it (K2 gathers nothing)
+        const int64_t tix = g.tokens ? token_of_row(g, r) : -1;
+        const int32_t tok = tix >= 0 ? g.tokens[tix] : -1;
+        const bool holds_tok = tok >= 0 && tok < g.V && tok >= cr * C::CH && tok < cr_end * C::CH;
+        const float tok_logit = holds_tok ? load_one<DT>(row, tok) : 0.0f;
         if (cr + kUnroll <= cr_full) {
-            // software pipeline: the next group's loads are in flight while this one is consumed
-            Raw cur[kUnroll];
+            // software pipeline with two register buffers used in turn (no copies):
+            // one group's loads are in flight while the other is consumed
+            Raw qa[kUnroll], qb[kUnroll];
+            int64_t ca = cr, cb = 0;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) cur[u] = C::load_full(row, cr + u, lane);
-            int64_t c0 = cr;
+            for (int u = 0; u < kUnroll; ++u) qa[u] = C::load_full(row, cr + u, lane);
             cr += kUnroll;
-            while (cr + kUnroll <= cr_full) {
-                Raw nxt[kUnroll];
+            while (true) {
+                const bool hb = cr + kUnroll <= cr_full;
+                if (hb) {
+                    cb = cr;
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) nxt[u] = C::load_full(row, cr + u, lane);
-                consume_group<DT, VEC, kUnroll>(st, cur, c0, lane, c);
+                    for (int u = 0; u < kUnroll; ++u) qb[u] = C::load_full(row, cr + u, lane);
+                    cr += kUnroll;
+                }
+                consume_group<DT, VEC, kUnroll>(st, qa, ca, lane, c);
+                if (!hb) break;
+                const bool ha = cr + kUnroll <= cr_full;
+                if (ha) {
+                    ca = cr;
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
-                c0 = cr;
-                cr += kUnroll;
+                    for (int u = 0; u < kUnroll; ++u) qa[u] = C::load_full(row, cr + u, lane);
+                    cr += kUnroll;
+                }
+                consume_group<DT, VEC, kUnroll>(st, qb, cb, lane, c);
+                if (!ha) break;
             }
-            consume_group<DT, VEC, kUnroll>(st, cur, c0, lane, c);
         }
         for (; cr < cr_end; ++cr) {
             Raw one[1] = {C::load_masked(row, cr, lane, g.V)};
@@ -395,15 +451,17 @@ __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, 
             if (lane == 0) {
                 sa.part_m[slot] = any_nan ? NAN : st.best;
                 sa.part_i[slot] = st.at;
+                if (holds_tok) sa.gath[r] = tok_logit;
             }
         } else {
             const float M = wave_max(st.m);
-            const float Rw = wave_max(st.S > 0.0 ? st.R : kRUnset);
-            const double Sw = wave_sum(rebase(st.S, st.R, Rw));
+            const float Rw = st.R;  // shared by the wave
+            const double Sw = wave_sum(st.S);
             if (lane == 0) {
                 sa.part_m[slot] = M;
                 sa.part_r[slot] = Rw;
                 sa.part_s[slot] = Sw;
+                if (holds_tok) sa.gath[r] = tok_logit;
             }
         }
         cc = ce;
@@ -493,16 +551,19 @@ __device__ void merge_rows(const Geom& g, const StatsArgs& sa, int64_t r0, int n
     __syncthreads();
 }
 
-// What the draw needs about the row it resamples.
+// What the residual sums and the draw need about the row a sequence resamples
+// (see the residual section below for the t units).
 struct SeqInfo {
-    int32_t k;      // emitted position (0..gamma), -1 = invalid sequence
-    float mp, mq;   // max logit of target row k / draft row k
-    int32_t pad;
-    double sp, sq;  // sum-exp of those rows (relative to their max)
+    int32_t k;       // emitted position (0..gamma), -1 = invalid sequence
+    float mcp, mcq;  // fl(max*c) of the target row k / draft row k
+    int32_t has_q;   // 0 at the bonus row (k == gamma)
+    double rho;      // scale_q / scale_p
+    double scale_p;  // 2^(mcp - max_p*c) / S_p: probability per t unit
 };
 
 struct AcceptArgs {
     const int32_t* tokens;
+    const float* gath;  // per row: logit at its draft token (from the statistics pass)
     int32_t B, gamma, V, nseg;
     int32_t stage;  // staged partials per row run (LDS), 0 = none
     float c32;
@@ -532,22 +593,31 @@ struct ResidRow {
     const char* qrow;  // nullptr at the bonus row
     float mcp, mcq;
     double rho;
-    double scale_p;
 };
 
 template <int DT>
 __device__ inline ResidRow resid_row(const void* tgt, const void* dft, const SeqInfo& s, int64_t b,
-                                     int32_t gamma, int32_t V, float c32) {
+                                     int32_t gamma, int32_t V) {
     ResidRow rr;
     rr.prow = row_at<DT>(tgt, (b * (gamma + 1) + s.k) * V);
-    rr.qrow = s.k < gamma ? row_at<DT>(dft, (b * gamma + s.k) * V) : nullptr;
-    const double c = static_cast<double>(c32);
-    rr.mcp = s.mp * c32;
-    rr.scale_p = exp2(static_cast<double>(rr.mcp) - static_cast<double>(s.mp) * c) / s.sp;
-    rr.mcq = s.mq * c32;
-    const double scale_q = exp2(static_cast<double>(rr.mcq) - static_cast<double>(s.mq) * c) / s.sq;
-    rr.rho = scale_q / rr.scale_p;
+    rr.qrow = s.has_q ? row_at<DT>(dft, (b * gamma + s.k) * V) : nullptr;
+    rr.mcp = s.mcp;
+    rr.mcq = s.mcq;
+    rr.rho = s.rho;
     return rr;
+}
+
+// The residual constants of a row pair from its merged stats (max m, sum S).
+__device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float mq, double sq, float c32) {
+    SeqInfo si;
+    const double c = static_cast<double>(c32);
+    si.k = k;
+    si.has_q = has_q ? 1 : 0;
+    si.mcp = mp * c32;
+    si.scale_p = exp2(static_cast<double>(si.mcp) - static_cast<double>(mp) * c) / sp;
+    si.mcq = has_q ? mq * c32 : 0.0f;
+    si.rho = has_q ? exp2(static_cast<double>(si.mcq) - static_cast<double>(mq) * c) / sq / si.scale_p : 0.0;
+    return si;
 }
 
 __device__ inline double resid_t(float xp, float xq, bool has_q, float c32, const ResidRow& rr) {
@@ -585,18 +655,18 @@ __global__ __launch_bounds__(kBlock) void k_accept(const void* __restrict__ tgt,
     int32_t* li = reinterpret_cast<int32_t*>(lr + stage);
     RowStat* rs = reinterpret_cast<RowStat*>(dyn + ((static_cast<size_t>(stage) * 20 + 15) / 16) * 16);
 
-    // draft token i and its two logits, loaded while the partials are staged
+    // draft token i and its two logits (gathered by the statistics pass), loaded
+    // together with the staged partials
     int32_t x = 0;
     float lt = 0.0f, ld = 0.0f;
-    bool tok_ok = false;
     if (wave0 && lane < gamma) {
         x = a.tokens[b * gamma + lane];
-        tok_ok = x >= 0 && x < V;
-        if (tok_ok) {
-            lt = load_one<DT>(row_at<DT>(tgt, (b * (gamma + 1) + lane) * V), x);
-            if constexpr (!GREEDY) ld = load_one<DT>(row_at<DT>(dft, (b * gamma + lane) * V), x);
+        if constexpr (!GREEDY) {
+            lt = a.gath[b * (gamma + 1) + lane];
+            ld = a.gath[g.rows_t + b * gamma + lane];
         }
     }
+    const bool tok_ok = x >= 0 && x < V;
     merge_rows<GREEDY>(g, sa, b * (gamma + 1), nt, 0, stage, lm, lr, ls, li, rs);
     if constexpr (!GREEDY) merge_rows<GREEDY>(g, sa, g.rows_t + b * gamma, nd, nt, stage, lm, lr, ls, li, rs);
 
@@ -669,14 +739,12 @@ __global__ __launch_bounds__(kBlock) void k_accept(const void* __restrict__ tgt,
         }
         if constexpr (!GREEDY) {
             if (!invalid && i == k) {
-                SeqInfo si;
-                si.k = k; si.mp = mt; si.mq = k < gamma ? md : 0.0f; si.pad = 0;
-                si.sp = st; si.sq = k < gamma ? sd : 1.0;
+                const SeqInfo si = seq_info(k, k < gamma, mt, st, md, sd, a.c32);
                 sh.si = si;
                 if (s == 0) a.info[b] = si;
             } else if (invalid && i == 0) {
                 SeqInfo si;
-                si.k = -1; si.mp = 0.0f; si.mq = 0.0f; si.pad = 0; si.sp = 1.0; si.sq = 1.0;
+                si.k = -1; si.mcp = 0.0f; si.mcq = 0.0f; si.has_q = 0; si.rho = 0.0; si.scale_p = 0.0;
                 sh.si = si;
                 if (s == 0) a.info[b] = si;
             }
@@ -688,20 +756,31 @@ __global__ __launch_bounds__(kBlock) void k_accept(const void* __restrict__ tgt,
         if (in.k < 0) return;
         // this block's segment of the residual (t units)
         const float c32 = a.c32;
-        const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V, c32);
+        const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V);
         const bool has_q = rr.qrow != nullptr;
         const int64_t e0 = static_cast<int64_t>(s) * kSeg3;
         const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
         double sum = 0.0;
         if constexpr (VEC) {
+            // every load of the segment issued before any is consumed
             constexpr int EPL = 16 / ElemBytes<DT>::value;
-            for (int64_t e = e0 + threadIdx.x * EPL; e < e1; e += kBlock * EPL) {
-                const uint4 wp = *reinterpret_cast<const uint4*>(rr.prow + e * ElemBytes<DT>::value);
-                uint4 wq = wp;
-                if (has_q) wq = *reinterpret_cast<const uint4*>(rr.qrow + e * ElemBytes<DT>::value);
+            constexpr int NI = kSeg3 / (kBlock * EPL);
+            uint4 wp[NI], wq[NI];
+#pragma unroll
+            for (int it = 0; it < NI; ++it) {
+                const int64_t e = e0 + (static_cast<int64_t>(it) * kBlock + threadIdx.x) * EPL;
+                const bool in_seg = e < e1;
+                wp[it] = in_seg ? *reinterpret_cast<const uint4*>(rr.prow + e * ElemBytes<DT>::value) : make_uint4(0, 0, 0, 0);
+                wq[it] = in_seg && has_q ? *reinterpret_cast<const uint4*>(rr.qrow + e * ElemBytes<DT>::value)
+                                         : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int it = 0; it < NI; ++it) {
+                const int64_t e = e0 + (static_cast<int64_t>(it) * kBlock + threadIdx.x) * EPL;
+                if (e >= e1) continue;
                 float xp[EPL], xq[EPL];
-                Chunk<DT, true>::expand(wp, xp);
-                Chunk<DT, true>::expand(wq, xq);
+                Chunk<DT, true>::expand(wp[it], xp);
+                Chunk<DT, true>::expand(wq[it], xq);
 #pragma unroll
                 for (int v = 0; v < EPL; ++v) sum += resid_t(xp[v], xq[v], has_q, c32, rr);
             }
@@ -812,25 +891,57 @@ __global__ __launch_bounds__(kBlock) void k_draw(const void* __restrict__ tgt, c
                                                  DrawArgs d) {
     __shared__ DrawShared sh;
     const int64_t b = blockIdx.x;
+    const int32_t gamma = d.gamma, V = d.V, nseg = d.nseg;
+    const double* seg = d.seg + b * nseg;
+    // the sequence's record and (for up to 256 segments) its segment sums, loaded together
     const SeqInfo in = d.info[b];
+    const double v0 = threadIdx.x < nseg ? seg[threadIdx.x] : 0.0;
     if (in.k < 0) {
         if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = NAN;
         return;
     }
-    const int32_t gamma = d.gamma, V = d.V, nseg = d.nseg;
     const float c32 = d.c32;
-    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V, c32);
+    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V);
     const bool has_q = rr.qrow != nullptr;
-    const double* seg = d.seg + b * nseg;
     int32_t* out = d.out_tokens + b * (gamma + 1) + in.k;
-    double z = 0.0;
-    for (int t = threadIdx.x; t < nseg; t += kBlock) z += seg[t];
-    const double Z = block_sum(z, sh.red);
-    if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = Z * rr.scale_p;
     const double u = philox_uniform(d.seed, static_cast<uint32_t>(b + d.b_offset), static_cast<uint32_t>(in.k), 1u);
-    bool draw_p = false;
-    double target = u * Z;
-    auto segmass = [&](int t) -> double { return seg[t]; };
+    double Z;
+    if (nseg <= kBlock) {
+        double incl, excl;
+        block_scan(v0, sh.red, incl, excl, Z);
+        if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = Z * in.scale_p;
+        if (Z > 0.0) {
+            const double target = u * Z;
+            if (threadIdx.x == 0) { sh.seg = -1; sh.last_pos = 0; }
+            __syncthreads();
+            if (threadIdx.x < nseg && v0 > 0.0) atomicMax(&sh.last_pos, static_cast<int>(threadIdx.x));
+            if (threadIdx.x < nseg && excl <= target && target < incl) { sh.seg = threadIdx.x; sh.before = excl; }
+            __syncthreads();
+            if (sh.seg < 0) {  // rounding: the last segment with mass and the mass before it
+                const int chosen = sh.last_pos;
+                const double before = block_sum(threadIdx.x < chosen ? v0 : 0.0, sh.red);
+                if (threadIdx.x == 0) { sh.seg = chosen; sh.before = before; }
+                __syncthreads();
+            }
+            const int64_t e0 = static_cast<int64_t>(sh.seg) * kSeg3;
+            const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
+            draw_in_range<DT>(rr, has_q, c32, e0, e1, target - sh.before, sh, out);
+            return;
+        }
+    } else {
+        double z = 0.0;
+        for (int t = threadIdx.x; t < nseg; t += kBlock) z += seg[t];
+        Z = block_sum(z, sh.red);
+        if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = Z * in.scale_p;
+        if (Z > 0.0) {
+            const double target = u * Z;
+            find_segment(nseg, target, [&](int t) -> double { return seg[t]; }, sh);
+            const int64_t e0 = static_cast<int64_t>(sh.seg) * kSeg3;
+            const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
+            draw_in_range<DT>(rr, has_q, c32, e0, e1, target - sh.before, sh, out);
+            return;
+        }
+    }
     // rounding left no residual mass at a rejected row: draw from p_k, with the
     // segment masses of p formed here (a rare, slow path)
     auto pmass = [&](int t) -> double {
@@ -840,18 +951,13 @@ __global__ __launch_bounds__(kBlock) void k_draw(const void* __restrict__ tgt, c
         for (int64_t j = e0; j < e1; ++j) acc += resid_t(load_one<DT>(rr.prow, j), 0.0f, false, c32, rr);
         return acc;
     };
-    if (!(Z > 0.0)) {
-        draw_p = true;
-        double zp = 0.0;
-        for (int t = threadIdx.x; t < nseg; t += kBlock) zp += pmass(t);
-        target = u * block_sum(zp, sh.red);
-        find_segment(nseg, target, pmass, sh);
-    } else {
-        find_segment(nseg, target, segmass, sh);
-    }
+    double zp = 0.0;
+    for (int t = threadIdx.x; t < nseg; t += kBlock) zp += pmass(t);
+    const double target = u * block_sum(zp, sh.red);
+    find_segment(nseg, target, pmass, sh);
     const int64_t e0 = static_cast<int64_t>(sh.seg) * kSeg3;
     const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-    draw_in_range<DT>(rr, has_q && !draw_p, c32, e0, e1, target - sh.before, sh, out);
+    draw_in_range<DT>(rr, false, c32, e0, e1, target - sh.before, sh, out);
 }
 
 // --------------------------------------------------------------------------
@@ -892,7 +998,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct Layout {
     Geom g;
     int32_t nseg3;
-    size_t off_pm, off_pr, off_ps, off_pi, off_info, off_seg, bytes;
+    size_t off_pm, off_pr, off_ps, off_pi, off_gath, off_info, off_seg, bytes;
 };
 
 int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
@@ -927,6 +1033,7 @@ Layout plan(int64_t rows_t, int64_t rows, int32_t V, int32_t dtype, bool vec, in
     L.off_pr = o; o = align_up(o + slots * sizeof(float), 256);
     L.off_ps = o; o = align_up(o + slots * sizeof(double), 256);
     L.off_pi = o; o = align_up(o + slots * sizeof(int32_t), 256);
+    L.off_gath = o; o = align_up(o + static_cast<size_t>(rows) * sizeof(float), 256);
     L.off_info = o; o = align_up(o + nb * sizeof(SeqInfo), 256);
     L.off_seg = o; o = align_up(o + nb * L.nseg3 * sizeof(double), 256);
     L.bytes = o;
@@ -970,47 +1077,60 @@ StatsArgs stats_args(const Layout& L, char* ws, float c32) {
     sa.part_r = reinterpret_cast<float*>(ws + L.off_pr);
     sa.part_s = reinterpret_cast<double*>(ws + L.off_ps);
     sa.part_i = reinterpret_cast<int32_t*>(ws + L.off_pi);
+    sa.gath = reinterpret_cast<float*>(ws + L.off_gath);
     return sa;
 }
 
+// Timing events, when asked for, are bound to the kernel dispatches themselves
+// (their start and end timestamps), so they add no packets to the stream.
+struct Events {
+    hipEvent_t stats_start = nullptr, stats_stop = nullptr, last_stop = nullptr;
+};
+
 template <int DT, bool VEC>
 void launch_stats_t(bool greedy, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
-                    hipStream_t st) {
-    const unsigned blocks = static_cast<unsigned>((g.nwaves + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (greedy) k_stats<DT, VEC, true><<<blocks, kBlock, 0, st>>>(tgt, dft, g, sa);
-    else k_stats<DT, VEC, false><<<blocks, kBlock, 0, st>>>(tgt, dft, g, sa);
+                    hipStream_t st, const Events& ev) {
+    const dim3 blocks(static_cast<unsigned>((g.nwaves + kWavesPerBlock - 1) / kWavesPerBlock));
+    if (greedy)
+        hipExtLaunchKernelGGL((k_stats<DT, VEC, true>), blocks, dim3(kBlock), 0, st, ev.stats_start, ev.stats_stop, 0,
+                              tgt, dft, g, sa);
+    else
+        hipExtLaunchKernelGGL((k_stats<DT, VEC, false>), blocks, dim3(kBlock), 0, st, ev.stats_start, ev.stats_stop,
+                              0, tgt, dft, g, sa);
 }
 
 void launch_stats(int32_t dtype, bool vec, bool greedy, const void* tgt, const void* dft, const Geom& g,
-                  const StatsArgs& sa, hipStream_t st) {
+                  const StatsArgs& sa, hipStream_t st, const Events& ev = Events{}) {
     if (dtype == SPEC_F32) {
-        if (vec) launch_stats_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, st);
-        else launch_stats_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, st);
+        if (vec) launch_stats_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, st, ev);
+        else launch_stats_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, st, ev);
     } else {
-        if (vec) launch_stats_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, st);
-        else launch_stats_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, st);
+        if (vec) launch_stats_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, st, ev);
+        else launch_stats_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, st, ev);
     }
 }
 
 template <int DT, bool VEC>
 void launch_accept_t(bool greedy, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
-                     const AcceptArgs& a, size_t lds, hipStream_t st) {
+                     const AcceptArgs& a, size_t lds, hipStream_t st, hipEvent_t stop) {
     if (greedy) {
-        k_accept<DT, VEC, true><<<static_cast<unsigned>(a.B), kBlock, lds, st>>>(tgt, dft, g, sa, a);
+        hipExtLaunchKernelGGL((k_accept<DT, VEC, true>), dim3(static_cast<unsigned>(a.B)), dim3(kBlock),
+                              static_cast<uint32_t>(lds), st, nullptr, stop, 0, tgt, dft, g, sa, a);
     } else {
         const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.nseg);
-        k_accept<DT, VEC, false><<<blocks, kBlock, lds, st>>>(tgt, dft, g, sa, a);
+        hipExtLaunchKernelGGL((k_accept<DT, VEC, false>), dim3(blocks), dim3(kBlock), static_cast<uint32_t>(lds), st,
+                              nullptr, nullptr, 0, tgt, dft, g, sa, a);
     }
 }
 
 void launch_accept(int32_t dtype, bool vec, bool greedy, const void* tgt, const void* dft, const Geom& g,
-                   const StatsArgs& sa, const AcceptArgs& a, size_t lds, hipStream_t st) {
+                   const StatsArgs& sa, const AcceptArgs& a, size_t lds, hipStream_t st, hipEvent_t stop) {
     if (dtype == SPEC_F32) {
-        if (vec) launch_accept_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, a, lds, st);
-        else launch_accept_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, a, lds, st);
+        if (vec) launch_accept_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, a, lds, st, stop);
+        else launch_accept_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, a, lds, st, stop);
     } else {
-        if (vec) launch_accept_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, a, lds, st);
-        else launch_accept_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, a, lds, st);
+        if (vec) launch_accept_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, a, lds, st, stop);
+        else launch_accept_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, a, lds, st, stop);
     }
 }
 
@@ -1093,7 +1213,9 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
 
     std::lock_guard<std::mutex> lk(g_mu);
-    const Layout L = plan(rows_t, rows, V, dtype, vec, B, compute_units(dev));
+    Layout L = plan(rows_t, rows, V, dtype, vec, B, compute_units(dev));
+    L.g.gamma = gamma;
+    L.g.tokens = draft_tokens;
     char* ws = nullptr;
     if (int rc = get_workspace(dev, st, L.bytes, &ws)) return rc;
     const StatsArgs sa = stats_args(L, ws, c32);
@@ -1101,6 +1223,7 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
 
     AcceptArgs a{};
     a.tokens = draft_tokens;
+    a.gath = sa.gath;
     a.B = B; a.gamma = gamma; a.V = V; a.nseg = L.nseg3;
     const int run_slots = (gamma + 1) * L.g.maxp;  // the larger of the two row runs
     a.stage = run_slots <= kMaxMergeSlots ? run_slots : 0;
@@ -1120,15 +1243,16 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     }
     const int nrows_seq = greedy ? gamma + 1 : 2 * gamma + 1;
     const size_t lds = align_up(static_cast<size_t>(a.stage) * 20, 16) + static_cast<size_t>(nrows_seq) * sizeof(RowStat);
-    auto ev = [&](int k) {
-        if (extras && extras->events[k]) (void)hipEventRecord(static_cast<hipEvent_t>(extras->events[k]), st);
-    };
+    Events ev;
+    if (extras) {
+        ev.stats_start = static_cast<hipEvent_t>(extras->events[0]);
+        ev.stats_stop = static_cast<hipEvent_t>(extras->events[1]);
+        ev.last_stop = static_cast<hipEvent_t>(extras->events[2]);
+    }
 
-    ev(0);
-    launch_stats(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, st);
+    launch_stats(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, st, ev);
     if (int rc = check_launch("statistics kernel")) return rc;
-    ev(1);
-    launch_accept(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, a, lds, st);
+    launch_accept(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, a, lds, st, greedy ? ev.last_stop : nullptr);
     if (int rc = check_launch("accept kernel")) return rc;
     if (!greedy) {
         DrawArgs d{};
@@ -1142,11 +1266,14 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
         d.seg = a.seg;
         d.out_tokens = out_tokens;
         d.dbg_z = extras ? extras->Z : nullptr;
-        if (dtype == SPEC_F32) k_draw<SPEC_F32><<<static_cast<unsigned>(B), kBlock, 0, st>>>(target_logits, draft_logits, d);
-        else k_draw<SPEC_BF16><<<static_cast<unsigned>(B), kBlock, 0, st>>>(target_logits, draft_logits, d);
+        if (dtype == SPEC_F32)
+            hipExtLaunchKernelGGL(k_draw<SPEC_F32>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, st, nullptr,
+                                  ev.last_stop, 0, target_logits, draft_logits, d);
+        else
+            hipExtLaunchKernelGGL(k_draw<SPEC_BF16>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, st, nullptr,
+                                  ev.last_stop, 0, target_logits, draft_logits, d);
         if (int rc = check_launch("draw kernel")) return rc;
     }
-    ev(2);
     return SPEC_OK;
 }
 
