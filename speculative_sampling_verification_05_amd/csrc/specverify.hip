@@ -14,25 +14,28 @@
 //
 // Three stream-ordered kernels per call (two at T == 0); no kernel waits on
 // another work-group and none hands work over through atomics:
-//  k_stats   one streaming pass over every target and draft row (all the
-//            compulsory bytes). Each wavefront owns a contiguous range of
-//            1 KiB chunks of the concatenated rows, keeps per lane an online
-//            max and a sum of 2^(x*c - R) (R an integer reference, c =
-//            log2(e)/T), software-pipelines its 16-byte loads, and flushes one
-//            partial per row piece with wave reductions. At T == 0 it tracks
-//            the argmax (first index of the maximum) instead.
-//  k_accept  one block per (residual segment, sequence). The block merges the
-//            sequence's partials through LDS and its first wavefront decides
-//            the accept step: lane i gathers the two logits of draft token i,
-//            forms alpha in fp64, draws its Philox uniform, and a ballot finds
-//            the first rejection k. Every block of the sequence repeats this
-//            (a few kilobytes of loads); block 0 writes the accepted tokens and
-//            k. Then each block sums the residual max(0, p - q) of row k (or p
-//            of the bonus row) over its segment in fp64.
-//  k_draw    one block per sequence: a block scan of the segment sums gives
-//            Z and the segment holding u*Z; a second scan over that segment's
-//            elements, held in registers, gives the first index whose
-//            cumulative mass exceeds u*Z.
+//  k_stats         one streaming pass over every target and draft row (all
+//                  the compulsory bytes). Each wavefront owns a contiguous
+//                  range of 1 KiB chunks of the concatenated rows, keeps per
+//                  lane an online max and a sum of 2^(x*c - R) (R an integer
+//                  reference, c = log2(e)/T), software-pipelines its 16-byte
+//                  loads, and flushes one partial per row piece with wave
+//                  reductions. At T == 0 it tracks the argmax (first index of
+//                  the maximum) instead.
+//  k_accept_resid  a few blocks per sequence. Each block folds the sequence's
+//                  partials (one wavefront per row) and repeats the accept
+//                  step: lane i takes the two logits of draft token i
+//                  (gathered by k_stats), forms alpha in fp64, draws its
+//                  Philox uniform, and a ballot finds the first rejection k.
+//                  Block 0 writes the accepted tokens and k. Then every
+//                  wavefront sums, in fp64, the residual max(0, p - q) of row
+//                  k (or p of the bonus row) over 1024-element subsegments.
+//                  (k_accept_greedy is its T == 0 counterpart: argmax merge and
+//                  accept only.)
+//  k_draw          one wavefront per sequence: wave scans of the subsegment
+//                  sums give Z and the subsegment holding u*Z; a scan over its
+//                  1024 elements, held in registers, gives the first index
+//                  whose cumulative mass exceeds u*Z.
 // Exponentials are fp32 (v_exp_f32 on one FMA); every sum and comparison that
 // decides a token is fp64.
 
@@ -59,15 +62,20 @@ namespace {
 #ifndef SPECVERIFY_CHUNKS_PER_WAVE
 #define SPECVERIFY_CHUNKS_PER_WAVE 16
 #endif
+
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kUnroll = SPECVERIFY_STATS_UNROLL;          // chunks per pipelined load group
 constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE; // 1 KiB chunks per stats wavefront
-constexpr int kSeg3 = 4096;                               // elements per residual segment
-constexpr int kPerThread = kSeg3 / kBlock;                // segment elements per draw thread
-constexpr int kMaxMergeSlots = 2048;                      // partials staged in LDS per row run
 constexpr float kRUnset = -1.0e30f;                       // lane reference before the first finite value
+constexpr int kSub = kWave * 16;  // elements per residual subsegment (one wavefront, 16 per lane)
+#ifndef SPECVERIFY_TAIL_BLOCK
+#define SPECVERIFY_TAIL_BLOCK 512
+#endif
+constexpr int kTailBlock = SPECVERIFY_TAIL_BLOCK;  // threads per accept/residual block
+constexpr int kMaxStage = 2048;                    // partials staged in LDS per sequence (20 bytes each)
+constexpr int kMergeBatch = 2;                     // staged partial loads in flight per thread
 
 enum : int { kAcc = 0, kRej = 1, kBad = 2 };
 
@@ -140,18 +148,35 @@ template <int DT, bool VEC> struct Chunk {
                                load_one<DT>(row, j + 2 * kWave), load_one<DT>(row, j + 3 * kWave));
         }
     }
-    // Elements at or beyond V read as -inf (no mass, never a maximum).
-    __device__ static inline Raw load_masked(const char* row, int64_t c, int lane, int32_t V) {
+    // The last load group of a piece, with no branch around its loads: a chunk
+    // past c_last, and elements at or beyond V, load from a valid address of
+    // chunk min(c, c_last); mask() then replaces them by -inf where the group
+    // is consumed.
+    __device__ static inline Raw load_clamped(const char* row, int64_t c, int64_t c_last, int lane, int32_t V) {
+        const int64_t cc = c <= c_last ? c : c_last;
         if constexpr (VEC) {
-            if (c * CH + lane * EPL < V) return load_full(row, c, lane);  // V % EPL == 0 here
-            const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;
-            return make_uint4(ninf, ninf, ninf, ninf);
+            const int64_t e = cc * CH + lane * EPL;
+            return load_stream(row + (e < V ? e : cc * CH) * ElemBytes<DT>::value);  // V % EPL == 0 here
         } else {
-            const int64_t j = c * CH + lane;
             float v[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = j + k * kWave < V ? load_one<DT>(row, j + k * kWave) : -INFINITY;
+            for (int k = 0; k < 4; ++k) {
+                const int64_t j = cc * CH + lane + k * kWave;
+                v[k] = load_one<DT>(row, j < V ? j : cc * CH);
+            }
             return make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+    __device__ static inline Raw mask(const Raw& w, int64_t c, int64_t c_last, int lane, int32_t V) {
+        const bool cin = c <= c_last;
+        if constexpr (VEC) {
+            const bool ok = cin && c * CH + lane * EPL < V;
+            const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;
+            return make_uint4(ok ? w.x : ninf, ok ? w.y : ninf, ok ? w.z : ninf, ok ? w.w : ninf);
+        } else {
+            const int64_t j = c * CH + lane;
+            return make_float4(cin && j < V ? w.x : -INFINITY, cin && j + kWave < V ? w.y : -INFINITY,
+                               cin && j + 2 * kWave < V ? w.z : -INFINITY, cin && j + 3 * kWave < V ? w.w : -INFINITY);
         }
     }
     __device__ static inline void expand(const Raw& w, float* x) {
@@ -186,45 +211,6 @@ __device__ inline double wave_sum(double v) {
     return v;
 }
 
-// Block-wide fp64 sum (256 threads); the result is returned to every thread.
-__device__ inline double block_sum(double v, double* lds) {
-    v = wave_sum(v);
-    const int wid = threadIdx.x / kWave;
-    __syncthreads();
-    if ((threadIdx.x & (kWave - 1)) == 0) lds[wid] = v;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int k = 0; k < kWavesPerBlock; ++k) t += lds[k];
-    return t;
-}
-
-// Block-wide inclusive scan (256 threads) of fp64 values; also returns the
-// exclusive prefix (the previous thread's inclusive value) and the block total.
-__device__ inline void block_scan(double v, double* lds, double& incl, double& excl, double& total) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
-    double x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
-    __syncthreads();
-    if (lane == kWave - 1) lds[wid] = x;
-    __syncthreads();
-    double base = 0.0;
-    total = 0.0;
-#pragma unroll
-    for (int k = 0; k < kWavesPerBlock; ++k) {
-        if (k < wid) base += lds[k];
-        total += lds[k];
-    }
-    incl = base + x;
-    const double prev = __shfl_up(incl, 1, kWave);
-    excl = lane == 0 ? base : prev;
-}
-
 // --------------------------------------------------------------------------
 // Geometry of the statistics pass: rows [0, rows_t) are target rows in memory
 // order, rows [rows_t, rows) draft rows (absent at T == 0 and for the
@@ -244,22 +230,11 @@ struct Geom {
     const int32_t* tokens;  // draft tokens, or nullptr (no logit gather)
 };
 
-// Index into draft_tokens of the token row r scores (-1: the bonus row).
-__device__ inline int64_t token_of_row(const Geom& g, int64_t r) {
-    if (r >= g.rows_t) return r - g.rows_t;  // draft row b*gamma + i
-    const int64_t b = r / (g.gamma + 1), i = r - b * (g.gamma + 1);
-    return i < g.gamma ? b * g.gamma + i : -1;
-}
-
 template <int DT>
 __device__ inline const char* row_ptr(const void* tgt, const void* dft, const Geom& g, int64_t r) {
     return r < g.rows_t ? row_at<DT>(tgt, r * g.V) : row_at<DT>(dft, (r - g.rows_t) * g.V);
 }
 
-__device__ inline int64_t first_wave(const Geom& g, int64_t r) { return (r * g.nchunk) / g.cpw; }
-__device__ inline int pieces_of(const Geom& g, int64_t r) {
-    return static_cast<int>(((r + 1) * g.nchunk - 1) / g.cpw - first_wave(g, r) + 1);
-}
 
 struct StatsArgs {
     float c32;
@@ -377,69 +352,158 @@ __device__ inline void consume_group(ArgLane& s, const typename Chunk<DT, VEC>::
     }
 }
 
-template <int DT, bool VEC, bool GREEDY>
+// The logit at index tok, if the load group starting at chunk c0 holds it
+// (tok < c_end*CH keeps padding chunks of other pieces out): the lane that
+// holds it selects the word from its registers.
+template <int DT, bool VEC, int N>
+__device__ inline void pick_token(const typename Chunk<DT, VEC>::Raw* raw, int64_t c0, int64_t c_end, int lane,
+                                  int64_t tok, float& val, bool& found) {
+    using C = Chunk<DT, VEC>;
+    const int64_t off = tok - c0 * C::CH;
+    if (off >= 0 && off < N * C::CH && tok < c_end * C::CH) {  // wave-uniform, once per row
+        const int u = static_cast<int>(off / C::CH);
+        const int in = static_cast<int>(off - static_cast<int64_t>(u) * C::CH);
+        const int holder = VEC ? in / C::EPL : in % kWave;
+        const int v = VEC ? in % C::EPL : in / kWave;
+        // word index of the element within the lane's N loads, then a select chain
+        const int word = VEC ? u * 4 + (DT == SPEC_F32 ? v : v >> 1) : u * 4 + v;
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            uint32_t b4[4];
+            if constexpr (VEC) {
+                b4[0] = raw[k].x; b4[1] = raw[k].y; b4[2] = raw[k].z; b4[3] = raw[k].w;
+            } else {
+                b4[0] = __float_as_uint(raw[k].x); b4[1] = __float_as_uint(raw[k].y);
+                b4[2] = __float_as_uint(raw[k].z); b4[3] = __float_as_uint(raw[k].w);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bits = word == k * 4 + q ? b4[q] : bits;
+        }
+        const float x = (!VEC || DT == SPEC_F32) ? __uint_as_float(bits)
+                                                 : __uint_as_float((v & 1) ? (bits & 0xFFFF0000u) : (bits << 16));
+        if (lane == holder) {
+            val = x;
+            found = true;
+        }
+    }
+}
+
+template <int DT, bool VEC, bool GREEDY, bool GATHER>
 __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, const void* __restrict__ dft,
                                                   Geom g, StatsArgs sa) {
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
     using Lane = typename std::conditional<GREEDY, ArgLane, SoftLane>::type;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
-    if (w >= g.nwaves) return;
+    // wave-uniform bookkeeping in 32-bit scalar registers (the host keeps the
+    // chunk count below 2^31): one division per wave finds the first row
+    const uint32_t w = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (w >= static_cast<uint32_t>(g.nwaves)) return;
     const float c = sa.c32;
-    const int64_t total = g.rows * g.nchunk;
-    int64_t cc = w * g.cpw;
-    const int64_t c_end = cc + g.cpw < total ? cc + g.cpw : total;
-    const int64_t nfull = g.V / C::CH;  // chunks of a row that are entirely in bounds
+    const uint32_t nchunk = static_cast<uint32_t>(g.nchunk), cpw = static_cast<uint32_t>(g.cpw);
+    const uint32_t total = static_cast<uint32_t>(g.rows) * nchunk;
+    uint32_t cc = w * cpw;
+    const uint32_t c_end = cc + cpw < total ? cc + cpw : total;
+    uint32_t r = cc / nchunk;
+    uint32_t first = r * nchunk;
+    int32_t k = static_cast<int32_t>(w - first / cpw);  // partial slot of this wave's first piece
+    const uint32_t nt_row = static_cast<uint32_t>(g.gamma) + 1u;
     while (cc < c_end) {
-        const int64_t r = cc / g.nchunk;
-        const int64_t first = r * g.nchunk;
-        const int64_t ce = first + g.nchunk < c_end ? first + g.nchunk : c_end;
+        const uint32_t ce = first + nchunk < c_end ? first + nchunk : c_end;
         const char* row = row_ptr<DT>(tgt, dft, g, r);
-        int64_t cr = cc - first;
-        const int64_t cr_end = ce - first;
-        const int64_t cr_full = cr_end < nfull ? cr_end : nfull;
+        const int64_t c0 = cc - first, c1 = ce - first;  // this piece: chunks [c0, c1) of row r
+        // the draft token this row scores (T > 0), picked from registers as its
+        // chunk streams by
+        // (branch-free, and nothing reads the loaded value before tok_ready():
+        // the bonus row loads token 0 and has_tok drops it)
+        int32_t tok = -1;
+        bool has_tok = false;
+        if constexpr (GATHER) {
+            // index into draft_tokens of the token row r scores (none: the bonus row)
+            uint32_t tix;
+            if (r >= static_cast<uint32_t>(g.rows_t)) {
+                tix = r - static_cast<uint32_t>(g.rows_t);
+                has_tok = true;
+            } else {
+                const uint32_t b = r / nt_row, i = r - b * nt_row;
+                tix = b * (nt_row - 1u) + i;
+                has_tok = i + 1u < nt_row;
+            }
+            tok = g.tokens[has_tok ? tix : 0u];
+        }
+        float tok_logit = 0.0f;
+        bool tok_found = false;
         Lane st;
         st.init();
-        // the logit at this row's draft token, if this piece holds it (K2 gathers nothing)
-        const int64_t tix = g.tokens ? token_of_row(g, r) : -1;
-        const int32_t tok = tix >= 0 ? g.tokens[tix] : -1;
-        const bool holds_tok = tok >= 0 && tok < g.V && tok >= cr * C::CH && tok < cr_end * C::CH;
-        const float tok_logit = holds_tok ? load_one<DT>(row, tok) : 0.0f;
-        if (cr + kUnroll <= cr_full) {
-            // software pipeline with two register buffers used in turn (no copies):
-            // one group's loads are in flight while the other is consumed
-            Raw qa[kUnroll], qb[kUnroll];
-            int64_t ca = cr, cb = 0;
+        // load groups of kUnroll chunks. Every group but the last lies wholly in
+        // the piece and in the row; the last may run past c1 or V (clamped
+        // loads, masked where consumed). Two register buffers are used in turn:
+        // one group's loads are in flight while the other is consumed, and no
+        // load sits under a branch, so each wait covers exactly one group.
+        const int64_t ng = (c1 - c0 + kUnroll - 1) / kUnroll;
+        const int64_t c_last = c1 - 1;
+        Raw qa[kUnroll], qb[kUnroll];
+        // (a scheduling barrier after each group keeps its loads ahead of the
+        // consumption of the previous group)
+        auto load = [&](Raw* q, int64_t gi) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) qa[u] = C::load_full(row, cr + u, lane);
-            cr += kUnroll;
-            while (true) {
-                const bool hb = cr + kUnroll <= cr_full;
-                if (hb) {
-                    cb = cr;
+            for (int u = 0; u < kUnroll; ++u) q[u] = C::load_full(row, c0 + gi * kUnroll + u, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto load_last = [&](Raw* q, int64_t gi) {
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) qb[u] = C::load_full(row, cr + u, lane);
-                    cr += kUnroll;
-                }
-                consume_group<DT, VEC, kUnroll>(st, qa, ca, lane, c);
-                if (!hb) break;
-                const bool ha = cr + kUnroll <= cr_full;
-                if (ha) {
-                    ca = cr;
+            for (int u = 0; u < kUnroll; ++u) q[u] = C::load_clamped(row, c0 + gi * kUnroll + u, c_last, lane, g.V);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // the token is first needed once the first group is in flight: nothing
+        // that reads it may be placed before those loads
+        auto tok_ready = [&]() {
+            if constexpr (GATHER) asm volatile("" : "+v"(tok) : : "memory");
+        };
+        auto eat = [&](const Raw* q, int64_t gi) {
+            const int64_t cg = c0 + gi * kUnroll;
+            consume_group<DT, VEC, kUnroll>(st, q, cg, lane, c);
+            if constexpr (GATHER) {
+                if (has_tok) pick_token<DT, VEC, kUnroll>(q, cg, c1, lane, tok, tok_logit, tok_found);
+            }
+        };
+        auto eat_last = [&](Raw* q, int64_t gi) {
+            const int64_t cg = c0 + gi * kUnroll;
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) qa[u] = C::load_full(row, cr + u, lane);
-                    cr += kUnroll;
-                }
-                consume_group<DT, VEC, kUnroll>(st, qb, cb, lane, c);
-                if (!ha) break;
+            for (int u = 0; u < kUnroll; ++u) q[u] = C::mask(q[u], cg + u, c_last, lane, g.V);
+            eat(q, gi);
+        };
+        if (ng == 1) {
+            load_last(qa, 0);
+            tok_ready();
+            eat_last(qa, 0);
+        } else {
+            load(qa, 0);
+            tok_ready();
+            int64_t gi = 1;  // next group to load; qa holds group gi - 1
+            for (; gi + 2 < ng; gi += 2) {  // groups gi and gi + 1 are not the last
+                load(qb, gi);
+                eat(qa, gi - 1);
+                load(qa, gi + 1);
+                eat(qb, gi);
+            }
+            if (gi + 1 == ng) {  // gi is the last group
+                load_last(qb, gi);
+                eat(qa, gi - 1);
+                eat_last(qb, gi);
+            } else {             // gi, then the last group gi + 1
+                load(qb, gi);
+                eat(qa, gi - 1);
+                load_last(qa, gi + 1);
+                eat(qb, gi);
+                eat_last(qa, gi + 1);
             }
         }
-        for (; cr < cr_end; ++cr) {
-            Raw one[1] = {C::load_masked(row, cr, lane, g.V)};
-            consume_group<DT, VEC, 1>(st, one, cr, lane, c);
-        }
-        const int64_t slot = r * g.maxp + (w - first_wave(g, r));
+        const int64_t slot = static_cast<int64_t>(r) * g.maxp + k;
+        // the wave that ends the row also neutralises the row's unused slots
+        // (a row spans maxp - 1 or maxp waves), so merges read every slot
+        const bool pad = ce == first + nchunk && lane > 0 && k + lane < g.maxp;
         if constexpr (GREEDY) {
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {  // (value desc, index asc) across the wave
@@ -451,7 +515,9 @@ __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, 
             if (lane == 0) {
                 sa.part_m[slot] = any_nan ? NAN : st.best;
                 sa.part_i[slot] = st.at;
-                if (holds_tok) sa.gath[r] = tok_logit;
+            } else if (pad) {
+                sa.part_m[slot + lane] = -INFINITY;
+                sa.part_i[slot + lane] = INT32_MAX;
             }
         } else {
             const float M = wave_max(st.m);
@@ -461,10 +527,17 @@ __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, 
                 sa.part_m[slot] = M;
                 sa.part_r[slot] = Rw;
                 sa.part_s[slot] = Sw;
-                if (holds_tok) sa.gath[r] = tok_logit;
+            } else if (pad) {
+                sa.part_m[slot + lane] = -INFINITY;
+                sa.part_r[slot + lane] = kRUnset;
+                sa.part_s[slot + lane] = 0.0;
             }
+            if (tok_found) sa.gath[r] = tok_logit;
         }
         cc = ce;
+        ++r;  // a later piece of this wave starts its row: slot 0
+        first += nchunk;
+        k = 0;
     }
 }
 
@@ -472,7 +545,9 @@ __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, 
 // Merging partials. A row's partials (M_p, R_p, S_p) combine exactly with
 // ldexp onto the largest reference R; the result is rebased once to the row
 // max: S * 2^(R - M*c), the exponent formed exactly in fp64. The argmax
-// partials combine as (value desc, index asc); any NaN marks the row.
+// partials combine as (value desc, index asc); any NaN marks the row. A row
+// has maxp partial slots; the statistics pass fills the one it may leave
+// unused with a neutral entry, so every slot can be read blindly.
 // --------------------------------------------------------------------------
 struct RowStat {
     float m;
@@ -482,6 +557,59 @@ struct RowStat {
 
 __device__ inline bool usable(float M, double S) { return isfinite(M) && isfinite(S) && S > 0.0; }
 
+// Row j of sequence b as the accept step sees it: target rows 0..gamma first,
+// then (T > 0) draft rows 0..gamma-1.
+__device__ inline int64_t seq_row(const Geom& g, int64_t b, int j) {
+    const int nt = g.gamma + 1;
+    return j < nt ? b * nt + j : g.rows_t + b * g.gamma + (j - nt);
+}
+
+// One wavefront folds one row: lane k takes slots k, k+64, ...; the lanes
+// then combine with butterfly reductions. Every lane returns the row's stats.
+template <bool GREEDY>
+__device__ inline RowStat fold_row_wave(const Geom& g, const StatsArgs& sa, int64_t r, int lane) {
+    const int64_t base = r * g.maxp;
+    RowStat o;
+    if constexpr (GREEDY) {
+        float best = -INFINITY;
+        int32_t arg = INT32_MAX;
+        bool nan = false;
+        for (int k = lane; k < g.maxp; k += kWave) {
+            const float v = sa.part_m[base + k];
+            const int32_t a = sa.part_i[base + k];
+            nan |= (v != v);
+            if (v > best || (v == best && a < arg)) { best = v; arg = a; }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ob = __shfl_xor(best, off, kWave);
+            const int32_t oa = __shfl_xor(arg, off, kWave);
+            if (ob > best || (ob == best && oa < arg)) { best = ob; arg = oa; }
+        }
+        o.m = __any(nan) ? NAN : best;
+        o.arg = arg;
+        o.s = 1.0;
+    } else {
+        float M = -INFINITY, R = kRUnset;
+        double S = 0.0;
+        for (int k = lane; k < g.maxp; k += kWave) {
+            const float mk = sa.part_m[base + k], rk = sa.part_r[base + k];
+            const double sk = sa.part_s[base + k];
+            const float Rn = fmaxf(R, rk);
+            S = rebase(S, R, Rn) + rebase(sk, rk, Rn);
+            R = Rn;
+            M = fmaxf(M, mk);
+        }
+        const float Mw = wave_max(M), Rw = wave_max(R);
+        const double Sw = wave_sum(rebase(S, R, Rw));
+        o.m = Mw;
+        o.arg = 0;
+        o.s = Sw * exp2(static_cast<double>(Rw) - static_cast<double>(Mw) * static_cast<double>(sa.c32));
+    }
+    return o;
+}
+
+// One thread folds one row from partials staged in LDS (np slots).
 template <bool GREEDY>
 __device__ inline RowStat fold_row(int np, const float* pm, const float* pr, const double* ps, const int32_t* pi,
                                    float c32) {
@@ -514,38 +642,64 @@ __device__ inline RowStat fold_row(int np, const float* pm, const float* pr, con
     return o;
 }
 
-// Merge rows [r0, r0 + n) into rs[out0 + j]. When their partials fit the
-// staging buffer (cap entries) every thread loads one partial, so all loads are
-// in flight together; then thread j folds row r0 + j from LDS. Otherwise each
-// row is folded straight from memory.
-template <bool GREEDY>
-__device__ void merge_rows(const Geom& g, const StatsArgs& sa, int64_t r0, int n, int out0, int cap, float* lm,
-                           float* lr, double* ls, int32_t* li, RowStat* rs) {
-    const int slots = n * g.maxp;
+// The nrows rows of sequence b folded into rs[0, nrows) (LDS), by a block of
+// NT threads. If their nrows*maxp partials fit the staging buffer (cap
+// entries of 20 bytes in dynamic LDS), every thread loads kMergeBatch of them
+// at a time, so the merge costs one round trip; then thread j folds row j.
+// Otherwise one wavefront folds each row straight from memory.
+template <bool GREEDY, int NT>
+__device__ inline void merge_seq(const Geom& g, const StatsArgs& sa, int64_t b, int nrows, int cap, char* dyn,
+                                 RowStat* rs) {
+    const int maxp = g.maxp;
+    const int slots = nrows * maxp;
     if (slots <= cap) {
-        for (int t = threadIdx.x; t < slots; t += kBlock) {
-            const int j = t / g.maxp, k = t % g.maxp;
-            const int64_t r = r0 + j;
-            const bool live = k < pieces_of(g, r);
-            const int64_t at = r * g.maxp + k;
-            lm[t] = live ? sa.part_m[at] : -INFINITY;
-            if constexpr (GREEDY) {
-                li[t] = live ? sa.part_i[at] : INT32_MAX;
-            } else {
-                lr[t] = live ? sa.part_r[at] : kRUnset;
-                ls[t] = live ? sa.part_s[at] : 0.0;
+        double* ls = reinterpret_cast<double*>(dyn);
+        float* lm = reinterpret_cast<float*>(ls + cap);
+        float* lr = lm + cap;
+        int32_t* li = reinterpret_cast<int32_t*>(lr + cap);
+        for (int t0 = 0; t0 < slots; t0 += kMergeBatch * NT) {
+            float vm[kMergeBatch], vr[kMergeBatch];
+            double vs[kMergeBatch];
+            int32_t vi[kMergeBatch];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const int t = t0 + u * NT + static_cast<int>(threadIdx.x);
+                if (t < slots) {
+                    const int j = t / maxp;
+                    const int64_t at = seq_row(g, b, j) * maxp + (t - j * maxp);
+                    vm[u] = sa.part_m[at];
+                    if constexpr (GREEDY) {
+                        vi[u] = sa.part_i[at];
+                    } else {
+                        vr[u] = sa.part_r[at];
+                        vs[u] = sa.part_s[at];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const int t = t0 + u * NT + static_cast<int>(threadIdx.x);
+                if (t < slots) {
+                    lm[t] = vm[u];
+                    if constexpr (GREEDY) {
+                        li[t] = vi[u];
+                    } else {
+                        lr[t] = vr[u];
+                        ls[t] = vs[u];
+                    }
+                }
             }
         }
         __syncthreads();
-        for (int j = threadIdx.x; j < n; j += kBlock) {
-            const int base = j * g.maxp;
-            rs[out0 + j] = fold_row<GREEDY>(g.maxp, lm + base, lr + base, ls + base, li + base, sa.c32);
+        for (int j = threadIdx.x; j < nrows; j += NT) {
+            const int base = j * maxp;
+            rs[j] = fold_row<GREEDY>(maxp, lm + base, lr + base, ls + base, li + base, sa.c32);
         }
     } else {
-        for (int j = threadIdx.x; j < n; j += kBlock) {
-            const int64_t at = (r0 + j) * g.maxp;
-            rs[out0 + j] = fold_row<GREEDY>(pieces_of(g, r0 + j), sa.part_m + at, sa.part_r + at,
-                                            sa.part_s + at, sa.part_i + at, sa.c32);
+        const int lane = threadIdx.x & (kWave - 1);
+        for (int j = threadIdx.x / kWave; j < nrows; j += NT / kWave) {
+            const RowStat o = fold_row_wave<GREEDY>(g, sa, seq_row(g, b, j), lane);
+            if (lane == 0) rs[j] = o;
         }
     }
     __syncthreads();
@@ -561,18 +715,23 @@ struct SeqInfo {
     double scale_p;  // 2^(mcp - max_p*c) / S_p: probability per t unit
 };
 
+
 struct AcceptArgs {
     const int32_t* tokens;
     const float* gath;  // per row: logit at its draft token (from the statistics pass)
-    int32_t B, gamma, V, nseg;
-    int32_t stage;  // staged partials per row run (LDS), 0 = none
+    int32_t B, gamma, V;
+    int32_t nsub;       // subsegments per row: ceil(V / kSub)
+    int32_t nblk;       // blocks per sequence (T > 0)
+    int32_t spb;        // subsegments per block
+    int32_t stage;      // partial slots staged in LDS per sequence (0: fold from memory)
     float c32;
     uint64_t seed;
     int64_t b_offset;
     int32_t* out_tokens;
     int32_t* out_n;
     SeqInfo* info;
-    double* seg;
+    double* sub_r;      // [B, nsub] residual mass per subsegment (t units)
+    double* sub_p;      // [B, nsub] mass of p per subsegment (t units)
     float* dbg_row_max;
     double* dbg_row_sumexp;
     double* dbg_p;
@@ -620,358 +779,438 @@ __device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float
     return si;
 }
 
-__device__ inline double resid_t(float xp, float xq, bool has_q, float c32, const ResidRow& rr) {
-    const double ep = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xp, c32, -rr.mcp)));
+__device__ inline float t_of_p(float xp, const ResidRow& rr, float c32) {
+    return __builtin_amdgcn_exp2f(fmaf(xp, c32, -rr.mcp));
+}
+
+__device__ inline double resid_t(double ep, float xq, bool has_q, float c32, const ResidRow& rr) {
     if (!has_q) return ep;
     const double eq = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xq, c32, -rr.mcq)));
     return fmax(0.0, fma(-eq, rr.rho, ep));
 }
 
-// --------------------------------------------------------------------------
-// k_accept. Dynamic LDS holds the staged partials of one row run (doubles
-// first, then the float/int arrays) and the merged stats of the sequence.
-// --------------------------------------------------------------------------
-struct AcceptShared {
-    double red[kWavesPerBlock];
-    SeqInfo si;
-};
-
-template <int DT, bool VEC, bool GREEDY>
-__global__ __launch_bounds__(kBlock) void k_accept(const void* __restrict__ tgt, const void* __restrict__ dft,
-                                                   Geom g, StatsArgs sa, AcceptArgs a) {
-    extern __shared__ __align__(16) char dyn[];
-    __shared__ AcceptShared sh;
-    const int32_t gamma = a.gamma, V = a.V;
-    const int nseg = GREEDY ? 1 : a.nseg;
-    const int64_t b = blockIdx.x / nseg;
-    const int32_t s = static_cast<int32_t>(blockIdx.x % nseg);
-    const int lane = threadIdx.x & (kWave - 1);
-    const bool wave0 = threadIdx.x < kWave;
-    const int nt = gamma + 1, nd = GREEDY ? 0 : gamma;
-    const int stage = a.stage;
-    double* ls = reinterpret_cast<double*>(dyn);
-    float* lm = reinterpret_cast<float*>(ls + stage);
-    float* lr = lm + stage;
-    int32_t* li = reinterpret_cast<int32_t*>(lr + stage);
-    RowStat* rs = reinterpret_cast<RowStat*>(dyn + ((static_cast<size_t>(stage) * 20 + 15) / 16) * 16);
-
-    // draft token i and its two logits (gathered by the statistics pass), loaded
-    // together with the staged partials
-    int32_t x = 0;
-    float lt = 0.0f, ld = 0.0f;
-    if (wave0 && lane < gamma) {
-        x = a.tokens[b * gamma + lane];
-        if constexpr (!GREEDY) {
-            lt = a.gath[b * (gamma + 1) + lane];
-            ld = a.gath[g.rows_t + b * gamma + lane];
-        }
-    }
-    const bool tok_ok = x >= 0 && x < V;
-    merge_rows<GREEDY>(g, sa, b * (gamma + 1), nt, 0, stage, lm, lr, ls, li, rs);
-    if constexpr (!GREEDY) merge_rows<GREEDY>(g, sa, g.rows_t + b * gamma, nd, nt, stage, lm, lr, ls, li, rs);
-
-    if (wave0) {
-        const int i = lane;
-        const int64_t R = 2 * gamma + 1;
-        const bool dbg = s == 0;
-        int status = kAcc;
-        float mt = NAN, md = NAN;
-        double st = NAN, sd = NAN;
-        bool ut = false;
-        int32_t amax = -1;
-        if (i <= gamma) {
-            const RowStat t = rs[i];
-            mt = t.m;
-            if constexpr (GREEDY) {
-                amax = t.arg;
-                ut = isfinite(mt);
-                if (dbg && a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
-                if (dbg && a.dbg_argmax) a.dbg_argmax[b * (gamma + 1) + i] = amax;
-            } else {
-                st = t.s;
-                ut = usable(mt, st);
-                if (dbg && a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
-                if (dbg && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + i] = st;
-            }
-        }
-        if (i < gamma) {
-            if constexpr (GREEDY) {
-                status = (!ut || !tok_ok) ? kBad : (x == amax ? kAcc : kRej);
-            } else {
-                const RowStat dr = rs[nt + i];
-                md = dr.m;
-                sd = dr.s;
-                const bool ud = usable(md, sd);
-                if (dbg && a.dbg_row_max) a.dbg_row_max[b * R + gamma + 1 + i] = md;
-                if (dbg && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + gamma + 1 + i] = sd;
-                double p = NAN, q = NAN;
-                if (!ut || !ud || !tok_ok) {
-                    status = kBad;
-                } else {
-                    const double c = static_cast<double>(a.c32);
-                    p = exp2((static_cast<double>(lt) - static_cast<double>(mt)) * c) / st;
-                    q = exp2((static_cast<double>(ld) - static_cast<double>(md)) * c) / sd;
-                    const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
-                    const double u = philox_uniform(a.seed, static_cast<uint32_t>(b + a.b_offset),
-                                                    static_cast<uint32_t>(i), 0u);
-                    status = u < alpha ? kAcc : kRej;
-                }
-                if (dbg && a.dbg_p) a.dbg_p[b * gamma + i] = p;
-                if (dbg && a.dbg_q) a.dbg_q[b * gamma + i] = q;
-            }
-        }
-        const uint64_t stop = __ballot(i < gamma && status != kAcc);
-        const int f = stop ? __ffsll(static_cast<unsigned long long>(stop)) - 1 : gamma;
-        const int fstat = __shfl(status, f, kWave);
-        const bool bonus_ok = __shfl(ut ? 1 : 0, gamma, kWave) != 0;
-        const bool invalid = f < gamma ? (fstat == kBad) : !bonus_ok;
-        const int k = invalid ? -1 : f;
-        if (s == 0) {
-            if (i <= gamma) {
-                int32_t o = -1;
-                if (!invalid) {
-                    if (i < k) o = x;
-                    else if (GREEDY && i == k) o = amax;
-                }
-                a.out_tokens[b * (gamma + 1) + i] = o;
-            }
-            if (i == 0) a.out_n[b] = k;
-        }
-        if constexpr (!GREEDY) {
-            if (!invalid && i == k) {
-                const SeqInfo si = seq_info(k, k < gamma, mt, st, md, sd, a.c32);
-                sh.si = si;
-                if (s == 0) a.info[b] = si;
-            } else if (invalid && i == 0) {
-                SeqInfo si;
-                si.k = -1; si.mcp = 0.0f; si.mcq = 0.0f; si.has_q = 0; si.rho = 0.0; si.scale_p = 0.0;
-                sh.si = si;
-                if (s == 0) a.info[b] = si;
-            }
-        }
-    }
-    if constexpr (!GREEDY) {
-        __syncthreads();
-        const SeqInfo in = sh.si;
-        if (in.k < 0) return;
-        // this block's segment of the residual (t units)
-        const float c32 = a.c32;
-        const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V);
-        const bool has_q = rr.qrow != nullptr;
-        const int64_t e0 = static_cast<int64_t>(s) * kSeg3;
-        const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-        double sum = 0.0;
-        if constexpr (VEC) {
-            // every load of the segment issued before any is consumed
-            constexpr int EPL = 16 / ElemBytes<DT>::value;
-            constexpr int NI = kSeg3 / (kBlock * EPL);
-            uint4 wp[NI], wq[NI];
+// The 16 elements of lane `lane` in subsegment i: j0 = i*kSub + 16*lane, ...
+// (p row; q row when has_q). Vector path: 16-byte loads, each taken only if it
+// starts below V, which puts it wholly inside the row (V % EPL == 0 there).
+// Elements at or beyond V read as -inf in p (no mass).
+template <int DT, bool VEC>
+__device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int32_t V, float* xp, float* xq) {
+    if constexpr (VEC) {
+        constexpr int EPL = 16 / ElemBytes<DT>::value;
+        constexpr int NV = 16 / EPL;
+        uint4 wp[NV], wq[NV];
+        const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;
 #pragma unroll
-            for (int it = 0; it < NI; ++it) {
-                const int64_t e = e0 + (static_cast<int64_t>(it) * kBlock + threadIdx.x) * EPL;
-                const bool in_seg = e < e1;
-                wp[it] = in_seg ? *reinterpret_cast<const uint4*>(rr.prow + e * ElemBytes<DT>::value) : make_uint4(0, 0, 0, 0);
-                wq[it] = in_seg && has_q ? *reinterpret_cast<const uint4*>(rr.qrow + e * ElemBytes<DT>::value)
-                                         : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int it = 0; it < NI; ++it) {
-                const int64_t e = e0 + (static_cast<int64_t>(it) * kBlock + threadIdx.x) * EPL;
-                if (e >= e1) continue;
-                float xp[EPL], xq[EPL];
-                Chunk<DT, true>::expand(wp[it], xp);
-                Chunk<DT, true>::expand(wq[it], xq);
-#pragma unroll
-                for (int v = 0; v < EPL; ++v) sum += resid_t(xp[v], xq[v], has_q, c32, rr);
-            }
-        } else {
-            for (int64_t e = e0 + threadIdx.x; e < e1; e += kBlock)
-                sum += resid_t(load_one<DT>(rr.prow, e), has_q ? load_one<DT>(rr.qrow, e) : 0.0f, has_q, c32, rr);
+        for (int u = 0; u < NV; ++u) {
+            const int64_t j = j0 + u * EPL;
+            const bool in = j < V;
+            wp[u] = in ? *reinterpret_cast<const uint4*>(rr.prow + j * ElemBytes<DT>::value)
+                       : make_uint4(ninf, ninf, ninf, ninf);
+            wq[u] = in && has_q ? *reinterpret_cast<const uint4*>(rr.qrow + j * ElemBytes<DT>::value)
+                                : make_uint4(0, 0, 0, 0);
         }
-        const double tot = block_sum(sum, sh.red);
-        if (threadIdx.x == 0) a.seg[b * nseg + s] = tot;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            Chunk<DT, true>::expand(wp[u], xp + u * EPL);
+            Chunk<DT, true>::expand(wq[u], xq + u * EPL);
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const bool in = j0 + v < V;
+            xp[v] = in ? load_one<DT>(rr.prow, j0 + v) : -INFINITY;
+            xq[v] = in && has_q ? load_one<DT>(rr.qrow, j0 + v) : 0.0f;
+        }
     }
 }
 
 // --------------------------------------------------------------------------
-// k_draw: one block per sequence.
+// The accept step, run by the first wavefront after merge_seq: lane i takes
+// draft token i, forms alpha in fp64, draws its Philox uniform, and a ballot
+// finds the first rejection k. Writes the accepted tokens and k (when `emit`),
+// and returns the sequence record for the residual.
+// --------------------------------------------------------------------------
+template <bool GREEDY>
+__device__ inline SeqInfo accept_wave(const Geom& g, const AcceptArgs& a, int64_t b, const RowStat* rs, int32_t x,
+                                      float lt, float ld, bool emit) {
+    const int32_t gamma = a.gamma, V = a.V;
+    const int nt = gamma + 1;
+    const int i = threadIdx.x;  // lane of wave 0
+    const int64_t R = 2 * gamma + 1;
+    const bool tok_ok = x >= 0 && x < V;
+    int status = kAcc;
+    float mt = NAN, md = NAN;
+    double st = NAN, sd = NAN;
+    bool ut = false;
+    int32_t amax = -1;
+    if (i <= gamma) {
+        const RowStat t = rs[i];
+        mt = t.m;
+        if (emit && a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
+        if constexpr (GREEDY) {
+            amax = t.arg;
+            ut = isfinite(mt);
+            if (emit && a.dbg_argmax) a.dbg_argmax[b * nt + i] = amax;
+        } else {
+            st = t.s;
+            ut = usable(mt, st);
+            if (emit && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + i] = st;
+        }
+    }
+    if (i < gamma) {
+        if constexpr (GREEDY) {
+            status = (!ut || !tok_ok) ? kBad : (x == amax ? kAcc : kRej);
+        } else {
+            const RowStat dr = rs[nt + i];
+            md = dr.m;
+            sd = dr.s;
+            const bool ud = usable(md, sd);
+            if (emit && a.dbg_row_max) a.dbg_row_max[b * R + nt + i] = md;
+            if (emit && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + nt + i] = sd;
+            double p = NAN, q = NAN;
+            if (!ut || !ud || !tok_ok) {
+                status = kBad;
+            } else {
+                const double c = static_cast<double>(a.c32);
+                p = exp2((static_cast<double>(lt) - static_cast<double>(mt)) * c) / st;
+                q = exp2((static_cast<double>(ld) - static_cast<double>(md)) * c) / sd;
+                const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+                const double u = philox_uniform(a.seed, static_cast<uint32_t>(b + a.b_offset),
+                                                static_cast<uint32_t>(i), 0u);
+                status = u < alpha ? kAcc : kRej;
+            }
+            if (emit && a.dbg_p) a.dbg_p[b * gamma + i] = p;
+            if (emit && a.dbg_q) a.dbg_q[b * gamma + i] = q;
+        }
+    }
+    SeqInfo mine{};
+    if constexpr (!GREEDY) {
+        if (i <= gamma) mine = seq_info(i, i < gamma, mt, st, md, sd, a.c32);
+    }
+    const uint64_t stop = __ballot(i < gamma && status != kAcc);
+    const int f = stop ? __ffsll(static_cast<unsigned long long>(stop)) - 1 : gamma;
+    const int fstat = __shfl(status, f, kWave);
+    const bool bonus_ok = __shfl(ut ? 1 : 0, gamma, kWave) != 0;
+    const bool invalid = f < gamma ? (fstat == kBad) : !bonus_ok;
+    const int k = invalid ? -1 : f;
+    if (emit) {
+        if (i <= gamma) {
+            int32_t o = -1;
+            if (!invalid) {
+                if (i < k) o = x;
+                else if (GREEDY && i == k) o = amax;
+            }
+            a.out_tokens[b * nt + i] = o;
+        }
+        if (i == 0) a.out_n[b] = k;
+    }
+    SeqInfo si;
+    si.k = -1; si.mcp = 0.0f; si.mcq = 0.0f; si.has_q = 0; si.rho = 0.0; si.scale_p = 0.0;
+    if constexpr (!GREEDY) {
+        // lane k holds the constants of row k (every lane formed its own
+        // before the ballot); broadcast them
+        const int src = invalid ? 0 : k;
+        const float mcp = __shfl(mine.mcp, src, kWave), mcq = __shfl(mine.mcq, src, kWave);
+        const double rho = __shfl(mine.rho, src, kWave), scale_p = __shfl(mine.scale_p, src, kWave);
+        if (!invalid) {
+            si.k = k;
+            si.has_q = k < gamma ? 1 : 0;
+            si.mcp = mcp;
+            si.mcq = mcq;
+            si.rho = rho;
+            si.scale_p = scale_p;
+        }
+    }
+    return si;
+}
+
+// Draft token i and its two logits (gathered by the statistics pass).
+template <bool GREEDY>
+__device__ inline void load_tokens(const Geom& g, const AcceptArgs& a, int64_t b, int32_t& x, float& lt, float& ld) {
+    x = 0;
+    lt = 0.0f;
+    ld = 0.0f;
+    const int i = threadIdx.x;
+    if (i < a.gamma) {
+        x = a.tokens[b * a.gamma + i];
+        if constexpr (!GREEDY) {
+            lt = a.gath[b * (a.gamma + 1) + i];
+            ld = a.gath[g.rows_t + b * a.gamma + i];
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// k_accept (T == 0): one block per sequence: argmax merge and the accept step.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void k_accept_greedy(Geom g, StatsArgs sa, AcceptArgs a) {
+    extern __shared__ __align__(16) char dyn[];
+    __shared__ RowStat rs[SPEC_MAX_GAMMA + 1];
+    const int64_t b = blockIdx.x;
+    int32_t x;
+    float lt, ld;
+    if (threadIdx.x < kWave) load_tokens<true>(g, a, b, x, lt, ld);
+    merge_seq<true, kBlock>(g, sa, b, a.gamma + 1, a.stage, dyn, rs);
+    if (threadIdx.x < kWave) (void)accept_wave<true>(g, a, b, rs, x, lt, ld, true);
+}
+
+// --------------------------------------------------------------------------
+// k_accept_resid (T > 0): nblk blocks per sequence. Every block merges the
+// sequence's partials and repeats the accept step (a few kilobytes of loads
+// and a few hundred instructions); block 0 writes the tokens, k and the
+// sequence record. Then each wavefront takes subsegments of row k and writes
+// their fp64 residual mass and p mass (t units).
+// --------------------------------------------------------------------------
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTailBlock) void k_accept_resid(const void* __restrict__ tgt,
+                                                             const void* __restrict__ dft, Geom g, StatsArgs sa,
+                                                             AcceptArgs a) {
+    extern __shared__ __align__(16) char dyn[];
+    __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
+    __shared__ SeqInfo shi;
+    constexpr int kTailWaves = kTailBlock / kWave;
+    const int64_t b = blockIdx.x / a.nblk;
+    const int32_t s = static_cast<int32_t>(blockIdx.x - b * a.nblk);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    int32_t x;
+    float lt, ld;
+    if (w == 0) load_tokens<false>(g, a, b, x, lt, ld);
+    merge_seq<false, kTailBlock>(g, sa, b, 2 * a.gamma + 1, a.stage, dyn, rs);
+    if (w == 0) {
+        const SeqInfo si = accept_wave<false>(g, a, b, rs, x, lt, ld, s == 0);
+        if (lane == 0) {
+            shi = si;
+            if (s == 0) a.info[b] = si;
+        }
+    }
+    __syncthreads();
+    const SeqInfo in = shi;
+    if (in.k < 0) return;  // block-uniform
+    const float c32 = a.c32;
+    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, a.gamma, a.V);
+    const bool has_q = rr.qrow != nullptr;
+    const int32_t i_end = (s + 1) * a.spb < a.nsub ? (s + 1) * a.spb : a.nsub;
+    for (int32_t i = s * a.spb + w; i < i_end; i += kTailWaves) {
+        float xp[16], xq[16];
+        load_sub<DT, VEC>(rr, has_q, static_cast<int64_t>(i) * kSub + 16 * lane, a.V, xp, xq);
+        double tr = 0.0;
+        float tpf = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float ep = t_of_p(xp[v], rr, c32);
+            tpf += ep;
+            tr += resid_t(static_cast<double>(ep), xq[v], has_q, c32, rr);
+        }
+        tr = wave_sum(tr);
+        const double tp = wave_sum(static_cast<double>(tpf));
+        if (lane == 0) {
+            a.sub_r[b * a.nsub + i] = tr;
+            a.sub_p[b * a.nsub + i] = tp;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// k_draw: one wavefront per sequence. Wave scans of the subsegment masses
+// give Z and the subsegment holding u*Z; a scan over that subsegment's 1024
+// elements (16 per lane, in registers) gives the first index whose cumulative
+// mass exceeds u*Z. If rounding leaves no residual mass at a rejected row the
+// draw is made from p_k instead (its masses come from the same pass).
 // --------------------------------------------------------------------------
 struct DrawArgs {
-    int32_t gamma, V, nseg;
+    int32_t gamma, V, nsub;
     float c32;
     uint64_t seed;
     int64_t b_offset;
     const SeqInfo* info;
-    const double* seg;
+    const double* sub_r;
+    const double* sub_p;
     int32_t* out_tokens;
     double* dbg_z;
 };
 
-struct DrawShared {
-    double red[kWavesPerBlock];
-    double before;
-    int seg, found, last_pos;
-};
-
-// Whole block: the first j in [e0, e1) (e1 - e0 <= kSeg3, ascending) whose
-// cumulative mass exceeds t; if rounding leaves none, the last j with mass.
-// Thread k owns kPerThread consecutive elements, loaded together and kept in
-// registers; a block scan locates the owner, which walks its registers.
-template <int DT>
-__device__ void draw_in_range(const ResidRow& rr, bool has_q, float c32, int64_t e0, int64_t e1, double t,
-                              DrawShared& sh, int32_t* out) {
-    const int64_t j0 = e0 + static_cast<int64_t>(threadIdx.x) * kPerThread;
-    float xp[kPerThread], xq[kPerThread];
+__device__ inline double wave_scan(double v, int lane) {
 #pragma unroll
-    for (int v = 0; v < kPerThread; ++v) {
-        const bool in = j0 + v < e1;
-        xp[v] = in ? load_one<DT>(rr.prow, j0 + v) : -INFINITY;
-        xq[v] = in && has_q ? load_one<DT>(rr.qrow, j0 + v) : 0.0f;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double y = __shfl_up(v, o, kWave);
+        if (lane >= o) v += y;
     }
-    double m[kPerThread];
+    return v;
+}
+
+// Total of m[0, n) in the order the search below accumulates it.
+__device__ inline double scan_total(const double* m, int32_t n, int lane) {
+    double base = 0.0;
+    for (int32_t t0 = 0; t0 < n; t0 += kWave) {
+        const double v = t0 + lane < n ? m[t0 + lane] : 0.0;
+        base += __shfl(wave_scan(v, lane), kWave - 1, kWave);
+    }
+    return base;
+}
+
+// First index i in [0, n) whose cumulative mass exceeds t, and the mass before
+// it; if rounding leaves none, the last index with mass.
+__device__ inline int32_t scan_find(const double* m, int32_t n, double t, int lane, double& before) {
+    double base = 0.0;
+    int32_t last = -1;
+    double last_before = 0.0;
+    for (int32_t t0 = 0; t0 < n; t0 += kWave) {
+        const double v = t0 + lane < n ? m[t0 + lane] : 0.0;
+        const double incl = base + wave_scan(v, lane);
+        const double prev = __shfl_up(incl, 1, kWave);
+        const double excl = lane == 0 ? base : prev;
+        const uint64_t hit = __ballot(v > 0.0 && excl <= t && t < incl);
+        if (hit) {
+            const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+            before = __shfl(excl, l, kWave);
+            return t0 + l;
+        }
+        const uint64_t mass = __ballot(v > 0.0);
+        if (mass) {
+            const int l = 63 - __clzll(static_cast<unsigned long long>(mass));
+            last = t0 + l;
+            last_before = __shfl(excl, l, kWave);
+        }
+        base = __shfl(incl, kWave - 1, kWave);
+    }
+    before = last_before;
+    return last;
+}
+
+// The same two steps on up to kDrawTiles*64 masses held in registers (one
+// load round trip); the totals and prefix sums are formed exactly as above.
+constexpr int kDrawTiles = 4;
+
+__device__ inline double regs_scan(const double* v, double* incl, int lane) {
+    double base = 0.0;
+#pragma unroll
+    for (int t = 0; t < kDrawTiles; ++t) {
+        incl[t] = base + wave_scan(v[t], lane);
+        base = __shfl(incl[t], kWave - 1, kWave);
+    }
+    return base;
+}
+
+__device__ inline int32_t regs_find(const double* v, const double* incl, double t, int lane, double& before) {
+    int32_t last = -1;
+    double last_before = 0.0;
+#pragma unroll
+    for (int k = 0; k < kDrawTiles; ++k) {
+        const double prev = __shfl_up(incl[k], 1, kWave);
+        const double base = k == 0 ? 0.0 : __shfl(incl[k - 1], kWave - 1, kWave);
+        const double excl = lane == 0 ? base : prev;
+        const uint64_t hit = __ballot(v[k] > 0.0 && excl <= t && t < incl[k]);
+        if (hit) {
+            const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+            before = __shfl(excl, l, kWave);
+            return k * kWave + l;
+        }
+        const uint64_t mass = __ballot(v[k] > 0.0);
+        if (mass) {
+            const int l = 63 - __clzll(static_cast<unsigned long long>(mass));
+            last = k * kWave + l;
+            last_before = __shfl(excl, l, kWave);
+        }
+    }
+    before = last_before;
+    return last;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) void k_draw(const void* __restrict__ tgt, const void* __restrict__ dft,
+                                                DrawArgs d) {
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const SeqInfo in = d.info[b];
+    if (in.k < 0) {
+        if (d.dbg_z && lane == 0) d.dbg_z[b] = NAN;
+        return;
+    }
+    const int32_t nsub = d.nsub;
+    const double* sr = d.sub_r + b * nsub;
+    const double* sp = d.sub_p + b * nsub;
+    const double u = philox_uniform(d.seed, static_cast<uint32_t>(b + d.b_offset), static_cast<uint32_t>(in.k), 1u);
+    double Z, target, before = 0.0;
+    int32_t sel;
+    bool from_p = false;  // no residual mass left by rounding: draw from p_k
+    if (nsub <= kDrawTiles * kWave) {
+        double v[kDrawTiles], incl[kDrawTiles];
+#pragma unroll
+        for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? sr[t * kWave + lane] : 0.0;
+        Z = regs_scan(v, incl, lane);
+        from_p = !(Z > 0.0);
+        if (from_p) {
+#pragma unroll
+            for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? sp[t * kWave + lane] : 0.0;
+            target = u * regs_scan(v, incl, lane);
+        } else {
+            target = u * Z;
+        }
+        sel = regs_find(v, incl, target, lane, before);
+    } else {
+        Z = scan_total(sr, nsub, lane);
+        from_p = !(Z > 0.0);
+        const double* m = from_p ? sp : sr;
+        target = u * (from_p ? scan_total(sp, nsub, lane) : Z);
+        sel = scan_find(m, nsub, target, lane, before);
+    }
+    if (d.dbg_z && lane == 0) d.dbg_z[b] = Z * in.scale_p;
+    int32_t* out = d.out_tokens + b * (d.gamma + 1) + in.k;
+    if (sel < 0) {  // no mass at all (cannot happen for a usable row); keep the output defined
+        if (lane == 0) *out = -1;
+        return;
+    }
+    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, d.gamma, d.V);
+    const bool has_q = rr.qrow != nullptr && !from_p;
+    const int64_t j0 = static_cast<int64_t>(sel) * kSub + 16 * lane;
+    float xp[16], xq[16];
+    load_sub<DT, VEC>(rr, has_q, j0, d.V, xp, xq);
+    double mv[16];
     double local = 0.0;
     int32_t mylast = -1;
 #pragma unroll
-    for (int v = 0; v < kPerThread; ++v) {
-        m[v] = j0 + v < e1 ? resid_t(xp[v], xq[v], has_q, c32, rr) : 0.0;
-        local += m[v];
-        if (m[v] > 0.0) mylast = static_cast<int32_t>(j0 + v);
+    for (int v = 0; v < 16; ++v) {
+        mv[v] = resid_t(static_cast<double>(t_of_p(xp[v], rr, d.c32)), xq[v], has_q, d.c32, rr);
+        local += mv[v];
+        if (mv[v] > 0.0) mylast = static_cast<int32_t>(j0 + v);
     }
-    if (threadIdx.x == 0) { sh.found = 0; sh.last_pos = -1; }
-    double incl, excl, tot;
-    block_scan(local, sh.red, incl, excl, tot);  // its barriers also publish the resets above
-    if (mylast >= 0) atomicMax(&sh.last_pos, mylast);
-    if (excl <= t && t < incl) {
-        double run = excl;
-        int32_t pick = -1;
+    const double incl = before + wave_scan(local, lane);
+    const double prev = __shfl_up(incl, 1, kWave);
+    const double excl = lane == 0 ? before : prev;
+    const uint64_t hit = __ballot(local > 0.0 && excl <= target && target < incl);
+    if (hit) {
+        const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        if (lane == l) {
+            double run = excl;
+            int32_t pick = -1;
 #pragma unroll
-        for (int v = 0; v < kPerThread; ++v) {
-            run += m[v];
-            if (pick < 0 && m[v] > 0.0 && run > t) pick = static_cast<int32_t>(j0 + v);
-        }
-        *out = pick >= 0 ? pick : mylast;
-        sh.found = 1;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && !sh.found) *out = sh.last_pos;
-}
-
-// Segment holding `target` among per-segment masses mass(t), t < nseg: sets
-// sh.seg and sh.before (the mass of the segments before it). Guard: the last
-// segment with mass.
-template <typename F>
-__device__ void find_segment(int nseg, double target, F mass, DrawShared& sh) {
-    if (threadIdx.x == 0) { sh.seg = -1; sh.last_pos = 0; sh.before = 0.0; }
-    double base = 0.0;
-    for (int t0 = 0; t0 < nseg; t0 += kBlock) {
-        const int t = t0 + threadIdx.x;
-        const double v = t < nseg ? mass(t) : 0.0;
-        double incl, excl, tot;
-        block_scan(v, sh.red, incl, excl, tot);
-        incl += base;
-        excl += base;
-        if (t < nseg && v > 0.0) atomicMax(&sh.last_pos, t);
-        if (t < nseg && excl <= target && target < incl) { sh.seg = t; sh.before = excl; }
-        base += tot;
-        __syncthreads();
-        if (sh.seg >= 0) break;
-    }
-    if (sh.seg < 0) {  // rounding: the last segment with mass and the mass before it
-        const int chosen = sh.last_pos;
-        double bz = 0.0;
-        for (int t = threadIdx.x; t < chosen; t += kBlock) bz += mass(t);
-        const double before = block_sum(bz, sh.red);
-        if (threadIdx.x == 0) { sh.seg = chosen; sh.before = before; }
-        __syncthreads();
-    }
-}
-
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_draw(const void* __restrict__ tgt, const void* __restrict__ dft,
-                                                 DrawArgs d) {
-    __shared__ DrawShared sh;
-    const int64_t b = blockIdx.x;
-    const int32_t gamma = d.gamma, V = d.V, nseg = d.nseg;
-    const double* seg = d.seg + b * nseg;
-    // the sequence's record and (for up to 256 segments) its segment sums, loaded together
-    const SeqInfo in = d.info[b];
-    const double v0 = threadIdx.x < nseg ? seg[threadIdx.x] : 0.0;
-    if (in.k < 0) {
-        if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = NAN;
-        return;
-    }
-    const float c32 = d.c32;
-    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, gamma, V);
-    const bool has_q = rr.qrow != nullptr;
-    int32_t* out = d.out_tokens + b * (gamma + 1) + in.k;
-    const double u = philox_uniform(d.seed, static_cast<uint32_t>(b + d.b_offset), static_cast<uint32_t>(in.k), 1u);
-    double Z;
-    if (nseg <= kBlock) {
-        double incl, excl;
-        block_scan(v0, sh.red, incl, excl, Z);
-        if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = Z * in.scale_p;
-        if (Z > 0.0) {
-            const double target = u * Z;
-            if (threadIdx.x == 0) { sh.seg = -1; sh.last_pos = 0; }
-            __syncthreads();
-            if (threadIdx.x < nseg && v0 > 0.0) atomicMax(&sh.last_pos, static_cast<int>(threadIdx.x));
-            if (threadIdx.x < nseg && excl <= target && target < incl) { sh.seg = threadIdx.x; sh.before = excl; }
-            __syncthreads();
-            if (sh.seg < 0) {  // rounding: the last segment with mass and the mass before it
-                const int chosen = sh.last_pos;
-                const double before = block_sum(threadIdx.x < chosen ? v0 : 0.0, sh.red);
-                if (threadIdx.x == 0) { sh.seg = chosen; sh.before = before; }
-                __syncthreads();
+            for (int v = 0; v < 16; ++v) {
+                run += mv[v];
+                if (pick < 0 && mv[v] > 0.0 && run > target) pick = static_cast<int32_t>(j0 + v);
             }
-            const int64_t e0 = static_cast<int64_t>(sh.seg) * kSeg3;
-            const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-            draw_in_range<DT>(rr, has_q, c32, e0, e1, target - sh.before, sh, out);
-            return;
+            *out = pick >= 0 ? pick : mylast;
         }
-    } else {
-        double z = 0.0;
-        for (int t = threadIdx.x; t < nseg; t += kBlock) z += seg[t];
-        Z = block_sum(z, sh.red);
-        if (d.dbg_z && threadIdx.x == 0) d.dbg_z[b] = Z * in.scale_p;
-        if (Z > 0.0) {
-            const double target = u * Z;
-            find_segment(nseg, target, [&](int t) -> double { return seg[t]; }, sh);
-            const int64_t e0 = static_cast<int64_t>(sh.seg) * kSeg3;
-            const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-            draw_in_range<DT>(rr, has_q, c32, e0, e1, target - sh.before, sh, out);
-            return;
-        }
+    } else {  // rounding: the last element with mass in the subsegment
+        const uint64_t mass = __ballot(mylast >= 0);
+        const int l = mass ? 63 - __clzll(static_cast<unsigned long long>(mass)) : 0;
+        const int32_t pick = __shfl(mylast, l, kWave);
+        if (lane == 0) *out = pick;
     }
-    // rounding left no residual mass at a rejected row: draw from p_k, with the
-    // segment masses of p formed here (a rare, slow path)
-    auto pmass = [&](int t) -> double {
-        const int64_t e0 = static_cast<int64_t>(t) * kSeg3;
-        const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-        double acc = 0.0;
-        for (int64_t j = e0; j < e1; ++j) acc += resid_t(load_one<DT>(rr.prow, j), 0.0f, false, c32, rr);
-        return acc;
-    };
-    double zp = 0.0;
-    for (int t = threadIdx.x; t < nseg; t += kBlock) zp += pmass(t);
-    const double target = u * block_sum(zp, sh.red);
-    find_segment(nseg, target, pmass, sh);
-    const int64_t e0 = static_cast<int64_t>(sh.seg) * kSeg3;
-    const int64_t e1 = e0 + kSeg3 < V ? e0 + kSeg3 : V;
-    draw_in_range<DT>(rr, false, c32, e0, e1, target - sh.before, sh, out);
 }
 
 // --------------------------------------------------------------------------
-// Row statistics output for spec_row_stats: one thread per row.
+// Row statistics output for spec_row_stats: one wavefront per row.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_merge_rows(Geom g, StatsArgs sa, float* __restrict__ row_max,
                                                        double* __restrict__ row_sumexp) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
     if (r >= g.rows) return;
-    const int64_t at = r * g.maxp;
-    const RowStat o = fold_row<false>(pieces_of(g, r), sa.part_m + at, sa.part_r + at, sa.part_s + at,
-                                      sa.part_i + at, sa.c32);
-    row_max[r] = o.m;
-    row_sumexp[r] = usable(o.m, o.s) ? o.s : NAN;
+    const RowStat o = fold_row_wave<false>(g, sa, r, threadIdx.x & (kWave - 1));
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        row_max[r] = o.m;
+        row_sumexp[r] = usable(o.m, o.s) ? o.s : NAN;
+    }
 }
 
 // ==========================================================================
@@ -997,8 +1236,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
     Geom g;
-    int32_t nseg3;
-    size_t off_pm, off_pr, off_ps, off_pi, off_gath, off_info, off_seg, bytes;
+    int32_t nsub, nblk, spb;
+    size_t off_pm, off_pr, off_ps, off_pi, off_gath, off_info, off_subr, off_subp, bytes;
 };
 
 int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
@@ -1025,17 +1264,29 @@ Layout plan(int64_t rows_t, int64_t rows, int32_t V, int32_t dtype, bool vec, in
     g.cpw = cpw;
     g.nwaves = (total + cpw - 1) / cpw;
     g.maxp = static_cast<int32_t>((g.nchunk + cpw - 1) / cpw + 1);
-    L.nseg3 = (V + kSeg3 - 1) / kSeg3;
+    // residual pass: one wavefront per subsegment, about as many blocks as the
+    // chip holds at once (32 wavefronts per compute unit), split evenly per
+    // sequence
+    constexpr int tail_waves = kTailBlock / kWave;
+    L.nsub = static_cast<int32_t>((static_cast<int64_t>(V) + kSub - 1) / kSub);
+    const int64_t nb = B > 0 ? B : 1;
+    int64_t nblk = (static_cast<int64_t>(cus) * (32 / tail_waves)) / nb;
+    const int64_t max_blk = (L.nsub + tail_waves - 1) / tail_waves;
+    if (nblk > max_blk) nblk = max_blk;
+    if (nblk < 1) nblk = 1;
+    L.spb = static_cast<int32_t>((L.nsub + nblk - 1) / nblk);
+    L.nblk = (L.nsub + L.spb - 1) / L.spb;
     const size_t slots = static_cast<size_t>(rows) * g.maxp;
-    const size_t nb = static_cast<size_t>(B > 0 ? B : 1);
+    const size_t subs = static_cast<size_t>(nb) * L.nsub;
     size_t o = 0;
     L.off_pm = o; o = align_up(o + slots * sizeof(float), 256);
     L.off_pr = o; o = align_up(o + slots * sizeof(float), 256);
     L.off_ps = o; o = align_up(o + slots * sizeof(double), 256);
     L.off_pi = o; o = align_up(o + slots * sizeof(int32_t), 256);
     L.off_gath = o; o = align_up(o + static_cast<size_t>(rows) * sizeof(float), 256);
-    L.off_info = o; o = align_up(o + nb * sizeof(SeqInfo), 256);
-    L.off_seg = o; o = align_up(o + nb * L.nseg3 * sizeof(double), 256);
+    L.off_info = o; o = align_up(o + static_cast<size_t>(nb) * sizeof(SeqInfo), 256);
+    L.off_subr = o; o = align_up(o + subs * sizeof(double), 256);
+    L.off_subp = o; o = align_up(o + subs * sizeof(double), 256);
     L.bytes = o;
     return L;
 }
@@ -1092,11 +1343,14 @@ void launch_stats_t(bool greedy, const void* tgt, const void* dft, const Geom& g
                     hipStream_t st, const Events& ev) {
     const dim3 blocks(static_cast<unsigned>((g.nwaves + kWavesPerBlock - 1) / kWavesPerBlock));
     if (greedy)
-        hipExtLaunchKernelGGL((k_stats<DT, VEC, true>), blocks, dim3(kBlock), 0, st, ev.stats_start, ev.stats_stop, 0,
-                              tgt, dft, g, sa);
+        hipExtLaunchKernelGGL((k_stats<DT, VEC, true, false>), blocks, dim3(kBlock), 0, st, ev.stats_start,
+                              ev.stats_stop, 0, tgt, dft, g, sa);
+    else if (g.tokens)
+        hipExtLaunchKernelGGL((k_stats<DT, VEC, false, true>), blocks, dim3(kBlock), 0, st, ev.stats_start,
+                              ev.stats_stop, 0, tgt, dft, g, sa);
     else
-        hipExtLaunchKernelGGL((k_stats<DT, VEC, false>), blocks, dim3(kBlock), 0, st, ev.stats_start, ev.stats_stop,
-                              0, tgt, dft, g, sa);
+        hipExtLaunchKernelGGL((k_stats<DT, VEC, false, false>), blocks, dim3(kBlock), 0, st, ev.stats_start,
+                              ev.stats_stop, 0, tgt, dft, g, sa);
 }
 
 void launch_stats(int32_t dtype, bool vec, bool greedy, const void* tgt, const void* dft, const Geom& g,
@@ -1111,26 +1365,24 @@ void launch_stats(int32_t dtype, bool vec, bool greedy, const void* tgt, const v
 }
 
 template <int DT, bool VEC>
-void launch_accept_t(bool greedy, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
-                     const AcceptArgs& a, size_t lds, hipStream_t st, hipEvent_t stop) {
-    if (greedy) {
-        hipExtLaunchKernelGGL((k_accept<DT, VEC, true>), dim3(static_cast<unsigned>(a.B)), dim3(kBlock),
-                              static_cast<uint32_t>(lds), st, nullptr, stop, 0, tgt, dft, g, sa, a);
-    } else {
-        const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.nseg);
-        hipExtLaunchKernelGGL((k_accept<DT, VEC, false>), dim3(blocks), dim3(kBlock), static_cast<uint32_t>(lds), st,
-                              nullptr, nullptr, 0, tgt, dft, g, sa, a);
-    }
+void launch_tail_t(const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa, const AcceptArgs& a,
+                   const DrawArgs& d, hipStream_t st, hipEvent_t stop) {
+    const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.nblk);
+    hipExtLaunchKernelGGL((k_accept_resid<DT, VEC>), dim3(blocks), dim3(kTailBlock), a.stage * 20u, st, nullptr,
+                          nullptr, 0, tgt, dft, g, sa, a);
+    hipExtLaunchKernelGGL((k_draw<DT, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0, st, nullptr, stop, 0,
+                          tgt, dft, d);
 }
 
-void launch_accept(int32_t dtype, bool vec, bool greedy, const void* tgt, const void* dft, const Geom& g,
-                   const StatsArgs& sa, const AcceptArgs& a, size_t lds, hipStream_t st, hipEvent_t stop) {
+// T > 0: accept + residual masses, then the draw.
+void launch_tail(int32_t dtype, bool vec, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
+                 const AcceptArgs& a, const DrawArgs& d, hipStream_t st, hipEvent_t stop) {
     if (dtype == SPEC_F32) {
-        if (vec) launch_accept_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, a, lds, st, stop);
-        else launch_accept_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, a, lds, st, stop);
+        if (vec) launch_tail_t<SPEC_F32, true>(tgt, dft, g, sa, a, d, st, stop);
+        else launch_tail_t<SPEC_F32, false>(tgt, dft, g, sa, a, d, st, stop);
     } else {
-        if (vec) launch_accept_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, a, lds, st, stop);
-        else launch_accept_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, a, lds, st, stop);
+        if (vec) launch_tail_t<SPEC_BF16, true>(tgt, dft, g, sa, a, d, st, stop);
+        else launch_tail_t<SPEC_BF16, false>(tgt, dft, g, sa, a, d, st, stop);
     }
 }
 
@@ -1203,9 +1455,7 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     const int64_t es = elem_bytes(dtype);
     const int64_t rows_t = static_cast<int64_t>(B) * (gamma + 1);
     const int64_t rows = greedy ? rows_t : rows_t + static_cast<int64_t>(B) * gamma;
-    const int64_t nseg3 = (V + kSeg3 - 1) / kSeg3;
-    if (rows * ((V + 255) / 256) >= kMaxChunks || static_cast<int64_t>(B) * nseg3 > INT32_MAX)
-        return fail(SPEC_EINVAL, "problem too large");
+    if (rows * ((V + 255) / 256) >= kMaxChunks) return fail(SPEC_EINVAL, "problem too large");
     const bool vec = (static_cast<int64_t>(V) * es) % 16 == 0 && aligned16(target_logits) &&
                      (greedy || aligned16(draft_logits));
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1224,16 +1474,19 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     AcceptArgs a{};
     a.tokens = draft_tokens;
     a.gath = sa.gath;
-    a.B = B; a.gamma = gamma; a.V = V; a.nseg = L.nseg3;
-    const int run_slots = (gamma + 1) * L.g.maxp;  // the larger of the two row runs
-    a.stage = run_slots <= kMaxMergeSlots ? run_slots : 0;
+    a.B = B; a.gamma = gamma; a.V = V;
+    a.nsub = L.nsub; a.nblk = L.nblk; a.spb = L.spb;
+    const int seq_slots = (greedy ? gamma + 1 : 2 * gamma + 1) * L.g.maxp;
+    a.stage = seq_slots <= kMaxStage ? seq_slots : 0;
+    const uint32_t lds = static_cast<uint32_t>(a.stage) * 20u;
     a.c32 = c32;
     a.seed = seed;
     a.b_offset = extras ? extras->b_offset : 0;
     a.out_tokens = out_tokens;
     a.out_n = out_n_accepted;
     a.info = info;
-    a.seg = reinterpret_cast<double*>(ws + L.off_seg);
+    a.sub_r = reinterpret_cast<double*>(ws + L.off_subr);
+    a.sub_p = reinterpret_cast<double*>(ws + L.off_subp);
     if (extras) {
         a.dbg_row_max = extras->row_max;
         a.dbg_row_sumexp = extras->row_sumexp;
@@ -1241,8 +1494,6 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
         a.dbg_q = extras->q_draft;
         a.dbg_argmax = extras->argmax;
     }
-    const int nrows_seq = greedy ? gamma + 1 : 2 * gamma + 1;
-    const size_t lds = align_up(static_cast<size_t>(a.stage) * 20, 16) + static_cast<size_t>(nrows_seq) * sizeof(RowStat);
     Events ev;
     if (extras) {
         ev.stats_start = static_cast<hipEvent_t>(extras->events[0]);
@@ -1252,27 +1503,25 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
 
     launch_stats(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, st, ev);
     if (int rc = check_launch("statistics kernel")) return rc;
-    launch_accept(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, a, lds, st, greedy ? ev.last_stop : nullptr);
-    if (int rc = check_launch("accept kernel")) return rc;
-    if (!greedy) {
+    if (greedy) {
+        hipExtLaunchKernelGGL(k_accept_greedy, dim3(static_cast<unsigned>(B)), dim3(kBlock), lds, st, nullptr,
+                              ev.last_stop, 0, L.g, sa, a);
+        if (int rc = check_launch("accept kernel")) return rc;
+    } else {
         DrawArgs d{};
         d.gamma = gamma;
         d.V = V;
-        d.nseg = L.nseg3;
+        d.nsub = L.nsub;
         d.c32 = c32;
         d.seed = seed;
         d.b_offset = a.b_offset;
         d.info = info;
-        d.seg = a.seg;
+        d.sub_r = a.sub_r;
+        d.sub_p = a.sub_p;
         d.out_tokens = out_tokens;
         d.dbg_z = extras ? extras->Z : nullptr;
-        if (dtype == SPEC_F32)
-            hipExtLaunchKernelGGL(k_draw<SPEC_F32>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, st, nullptr,
-                                  ev.last_stop, 0, target_logits, draft_logits, d);
-        else
-            hipExtLaunchKernelGGL(k_draw<SPEC_BF16>, dim3(static_cast<unsigned>(B)), dim3(kBlock), 0, st, nullptr,
-                                  ev.last_stop, 0, target_logits, draft_logits, d);
-        if (int rc = check_launch("draw kernel")) return rc;
+        launch_tail(dtype, vec, target_logits, draft_logits, L.g, sa, a, d, st, ev.last_stop);
+        if (int rc = check_launch("accept/residual and draw kernels")) return rc;
     }
     return SPEC_OK;
 }
@@ -1304,7 +1553,7 @@ int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype, f
     const StatsArgs sa = stats_args(L, ws, c32);
     launch_stats(dtype, vec, false, logits, nullptr, L.g, sa, st);
     if (int rc = check_launch("statistics kernel")) return rc;
-    const unsigned blocks = static_cast<unsigned>((rows + kBlock - 1) / kBlock);
+    const unsigned blocks = static_cast<unsigned>((rows + kWavesPerBlock - 1) / kWavesPerBlock);
     k_merge_rows<<<blocks, kBlock, 0, st>>>(L.g, sa, row_max, row_sumexp);
     return check_launch("merge kernel");
 }
