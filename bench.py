@@ -7,9 +7,10 @@ temperature 0.8. Inputs are seeded synthetic logits already resident in HBM;
 two input sets alternate so that every step reads data the previous step did
 not touch (each set is 279 MB, above the 256 MB last-level cache).
 
-Prints one JSON line: verified draft rows/s (B*gamma per step), the statistics
-kernel's achieved HBM bandwidth against the 8 TB/s peak, and the fp64 CPU
-oracle timed on the host cores on a bounded sample of the same workload.
+Prints one JSON line: verified draft rows/s (B*gamma per step), the
+verification kernel's achieved HBM bandwidth (compulsory bytes over its
+duration) against the 8 TB/s peak, and the fp64 CPU oracle timed on the host
+cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -30,6 +31,23 @@ import workloads as W  # noqa: E402
 
 METRIC = "verified draft rows/sec and achieved HBM GB/s (% of peak) at B=64,γ=8,V=128256"
 PEAK_HBM_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "speculative_sampling_verification_05_amd", "csrc", "specverify.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the verification kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy's counts),
+    or None if they were taken on another workload or another kernel source."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))["k_verify"]
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != sha:
+        return None
+    return rec["traffic_bytes"]
 
 
 class HipEvents:
@@ -174,18 +192,18 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({Wm} steps)", file=sys.stderr, flush=True)
 
-    # timed region: K steps. Every `event_stride`-th step carries HIP events bound
-    # to its own kernel dispatches (start and end of the statistics kernel, end
-    # of the last kernel), so they time the kernels inside the timed region
-    # without adding packets to the stream.
+    # timed region: K steps. Every `event_stride`-th step carries two HIP events
+    # bound to its kernel dispatch (start and end of the verification kernel), so
+    # they time the kernel inside the timed region without adding packets to the
+    # stream.
     E = max(1, args.event_stride)
     evd = [i for i in range(K) if i % E == 0]
-    ev = hip.create(3 * len(evd))
+    ev = hip.create(2 * len(evd))
     extras = {}
     for n, i in enumerate(evd):
         e = sv.Extras()
-        for j in range(3):
-            e.events[j] = ev[3 * n + j]
+        e.events[0] = ev[2 * n]
+        e.events[1] = ev[2 * n + 1]
         extras[i] = e
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -195,8 +213,7 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    k1_ms = [hip.ms(ev[3 * n], ev[3 * n + 1]) for n in range(len(evd))]
-    tail_ms = [hip.ms(ev[3 * n + 1], ev[3 * n + 2]) for n in range(len(evd))]
+    k_ms = [hip.ms(ev[2 * n], ev[2 * n + 1]) for n in range(len(evd))]
     hip.destroy(ev)
     ms_per_step = total_ms / K
 
@@ -207,15 +224,13 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_plain = start.elapsed_time(end) / K
-    names = ["stats", "accept_resid_draw"] if wl.T > 0 else ["argmax", "accept"]
-    split = {names[0]: float(np.mean(k1_ms)) * 1e3, names[1]: float(np.mean(tail_ms)) * 1e3}
 
     rows_per_step = B * g
     value = rows_per_step / (ms_per_step * 1e-3)
     compulsory = wl.compulsory_bytes()
     read_bytes = wl.bytes_read()
-    k1_avg_ms = float(np.mean(k1_ms))
-    achieved = read_bytes / (k1_avg_ms * 1e-3) / 1e9
+    k_avg_ms = float(np.mean(k_ms))
+    achieved = read_bytes / (k_avg_ms * 1e-3) / 1e9
     call_gbps = compulsory / (ms_per_step * 1e-3) / 1e9
 
     # one validation of the last outputs of set 0 against the oracle (outside the timed region)
@@ -242,15 +257,15 @@ def main():
                    "logits": W.DTYPE_NAMES[wl.dtype], "input_sets": args.sets},
         "call_gbps": call_gbps,
         "call_hbm_frac": call_gbps / PEAK_HBM_GBPS,
-        "kernel_us": split,
+        "kernel_us": {"k_verify": k_avg_ms * 1e3},
         "ms_per_step_no_events": ms_plain,
         "event_stride": E,
         "accepted_hist": n_hist,
-        "roofline": {"bound": "hbm", "kernel": "k_stats",
+        "roofline": {"bound": "hbm", "kernel": "k_verify",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
-                     "bytes_per_launch": read_bytes, "avg_launch_us": k1_avg_ms * 1e3,
-                     "launches_timed": len(k1_ms)},
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name),
+                     "bytes_per_launch": read_bytes, "avg_launch_us": k_avg_ms * 1e3,
+                     "launches_timed": len(k_ms)},
     }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or min(B, 64)

@@ -83,9 +83,14 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
  *  out_tokens     [B, gamma+1] int32: the n accepted draft tokens, then the
  *                 correction (or bonus) token, then -1 padding.
  *  out_n_accepted [B] int32: n in 0..gamma, or -1 (invalid input, see above).
- *  Returns SPEC_OK or a negative spec_status_t. The library keeps a device
- *  workspace per (device, stream), grown on demand under a lock; concurrent
- *  calls on different streams are safe, calls on one stream are ordered. */
+ *  Returns SPEC_OK or a negative spec_status_t (SPEC_EINVAL also when the
+ *  problem exceeds the kernel's 32-bit chunk and dispatch counts). The
+ *  library keeps a device workspace per (device, stream), grown on demand
+ *  under a lock; concurrent calls on different streams are safe, calls on one
+ *  stream are ordered. One kernel is launched per call. Inside it, blocks
+ *  that resample a sequence wait (bounded, about 2 s) for the blocks that
+ *  stream the sequence's rows; should that bound ever run out the sequence is
+ *  reported as -1 rather than the kernel waiting on. */
 int spec_verify(const void* target_logits, const void* draft_logits,
                 const int32_t* draft_tokens, int32_t B, int32_t gamma, int32_t V,
                 int32_t dtype, float temperature, uint64_t seed,
@@ -105,10 +110,10 @@ typedef struct {
     int32_t* argmax;       /* [B, gamma+1]: argmax of each target row (T == 0 only) */
     int64_t b_offset;      /* added to b in the Philox counter, so that a shard of a
                               larger batch draws the same uniforms as the whole batch */
-    void* events[3];       /* optional hipEvent_t (host handles), bound to the kernel
-                              dispatches themselves (no extra stream packets): [0] start
-                              and [1] end of the statistics kernel, [2] end of the call's
-                              last kernel */
+    void* events[3];       /* optional hipEvent_t (host handles): [0] and [1] are bound to
+                              the start and end of the call's verification kernel
+                              dispatch itself (no extra stream packets); [2] is
+                              reserved and ignored */
 } spec_extras_t;
 
 /* spec_verify with extras (NULL extras == spec_verify). Same kernels. */
@@ -119,10 +124,11 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits,
                    const spec_extras_t* extras);
 
 /* spec_row_stats: the softmax statistics pass alone ([Ch15] 15.1.2 step 2).
- *  logits [rows, V] dtype; T > 0.
+ *  logits [rows, V] dtype; 1 <= rows < 2^31; T > 0.
  *  row_max [rows] float  : max_j l_j;
  *  row_sumexp [rows] double : sum_j exp((l_j - row_max)/T); NaN when the row
- *  holds NaN or +inf or no finite entry. Same kernel as spec_verify. */
+ *  holds NaN or +inf or no finite entry. Same kernel and statistics code as
+ *  spec_verify. */
 int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype,
                    float temperature, float* row_max, double* row_sumexp, void* stream);
 

@@ -12,30 +12,35 @@
 //  [HSD]  "LLM inference optimisation: hidden-state speculative decoding", 3.3:
 //         the bonus token drawn from the last target row.
 //
-// Three stream-ordered kernels per call (two at T == 0); no kernel waits on
-// another work-group and none hands work over through atomics:
-//  k_stats         one streaming pass over every target and draft row (all
-//                  the compulsory bytes). Each wavefront owns a contiguous
-//                  range of 1 KiB chunks of the concatenated rows, keeps per
-//                  lane an online max and a sum of 2^(x*c - R) (R an integer
-//                  reference, c = log2(e)/T), software-pipelines its 16-byte
-//                  loads, and flushes one partial per row piece with wave
-//                  reductions. At T == 0 it tracks the argmax (first index of
-//                  the maximum) instead.
-//  k_accept_resid  a few blocks per sequence. Each block folds the sequence's
-//                  partials (one wavefront per row) and repeats the accept
-//                  step: lane i takes the two logits of draft token i
-//                  (gathered by k_stats), forms alpha in fp64, draws its
-//                  Philox uniform, and a ballot finds the first rejection k.
-//                  Block 0 writes the accepted tokens and k. Then every
-//                  wavefront sums, in fp64, the residual max(0, p - q) of row
-//                  k (or p of the bonus row) over 1024-element subsegments.
-//                  (k_accept_greedy is its T == 0 counterpart: argmax merge and
-//                  accept only.)
-//  k_draw          one wavefront per sequence: wave scans of the subsegment
-//                  sums give Z and the subsegment holding u*Z; a scan over its
-//                  1024 elements, held in registers, gives the first index
-//                  whose cumulative mass exceeds u*Z.
+// One kernel launch per call. Its grid holds two kinds of 256-thread blocks,
+// laid out group by group (a group is one sequence; for the stand-alone row
+// statistics it is one row):
+//  statistics blocks  stream the group's rows once (all the compulsory bytes).
+//                     Each wavefront owns a contiguous range of 1 KiB chunks of
+//                     the group's concatenated rows, keeps per lane an online
+//                     max and a sum of 2^(x*c - R) (R an integer reference,
+//                     c = log2(e)/T), software-pipelines its 16-byte loads and
+//                     writes one partial per row piece; at T == 0 it tracks the
+//                     argmax (first index of the maximum) instead. Each
+//                     wavefront then counts itself in at its group's counter;
+//                     the last one publishes the group (T > 0) or finishes it
+//                     (T == 0: the greedy accept step; row statistics: the
+//                     row's max and sum).
+//  residual blocks    (T > 0) sit a few groups after their group's statistics
+//                     blocks, so they usually start after it is published. A
+//                     block folds the group's partials, repeats the accept step
+//                     (lane i: alpha in fp64 from the two logits of draft token
+//                     i, its Philox uniform; a ballot finds the first rejection
+//                     k) and its wavefronts sum, in fp64, the residual
+//                     max(0, p - q) of row k (or p of the bonus row) over
+//                     1024-element subsegments. The group's last wavefront to
+//                     finish draws the token: wave scans of the subsegment sums,
+//                     then of the chosen subsegment.
+// A residual block waits only for statistics blocks of lower index, which the
+// in-order dispatch has already started, and its wait is bounded in time.
+// Data crossing blocks moves through device-coherent (agent-scope) atomic loads
+// and stores, which bypass the per-XCD L2 caches, ordered by waiting for their
+// completion; no cache flush or invalidate is issued.
 // Exponentials are fp32 (v_exp_f32 on one FMA); every sum and comparison that
 // decides a token is fp64.
 
@@ -60,24 +65,34 @@ namespace {
 #define SPECVERIFY_STATS_UNROLL 4
 #endif
 #ifndef SPECVERIFY_CHUNKS_PER_WAVE
-#define SPECVERIFY_CHUNKS_PER_WAVE 16
+#define SPECVERIFY_CHUNKS_PER_WAVE 32
+#endif
+#ifndef SPECVERIFY_LAG
+#define SPECVERIFY_LAG 1024
+#endif
+#ifndef SPECVERIFY_SLEEP
+#define SPECVERIFY_SLEEP 8
+#endif
+#ifndef SPECVERIFY_SYNC_STRIDE
+#define SPECVERIFY_SYNC_STRIDE 64
 #endif
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kUnroll = SPECVERIFY_STATS_UNROLL;          // chunks per pipelined load group
-constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE; // 1 KiB chunks per stats wavefront
-constexpr float kRUnset = -1.0e30f;                       // lane reference before the first finite value
-constexpr int kSub = kWave * 16;  // elements per residual subsegment (one wavefront, 16 per lane)
-#ifndef SPECVERIFY_TAIL_BLOCK
-#define SPECVERIFY_TAIL_BLOCK 512
-#endif
-constexpr int kTailBlock = SPECVERIFY_TAIL_BLOCK;  // threads per accept/residual block
-constexpr int kMaxStage = 2048;                    // partials staged in LDS per sequence (20 bytes each)
-constexpr int kMergeBatch = 2;                     // staged partial loads in flight per thread
+constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE; // 1 KiB chunks per statistics wavefront
+constexpr int kLag = SPECVERIFY_LAG;                       // groups between statistics and residual blocks
+constexpr float kRUnset = -1.0e30f;                        // lane reference before the first finite value
+constexpr int kSub = kWave * 16;      // elements per residual subsegment (one wavefront, 16 per lane)
+constexpr int kMaxStage = 1024;       // partial slots of one group staged in LDS (20 bytes each)
+constexpr uint64_t kWaitTicks = 200000000ull;  // bound on a residual block's wait: 2 s at 100 MHz
+constexpr int kSleep = SPECVERIFY_SLEEP;            // s_sleep argument between polls (64 cycles each)
+constexpr int kSyncStride = SPECVERIFY_SYNC_STRIDE; // words between one group's counters and the next's
 
 enum : int { kAcc = 0, kRej = 1, kBad = 2 };
+enum : int { kSample = 0, kGreedy = 1, kRows = 2 };
+enum : int { kStatsBlock = 0, kResidBlock = 1 };
 
 // --------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11). Each round maps
@@ -205,55 +220,200 @@ __device__ inline float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
     return v;
 }
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// fp64 moves across lanes with DPP (each 32-bit half), lanes without a source
+// reading 0: row_shr:n = 0x110 + n, wave_shr:1 = 0x138, row_bcast:15 = 0x142
+// (lane 15 of each row into the next row), row_bcast:31 = 0x143 (lane 31 into
+// rows 2 and 3). ROWS selects the 16-lane rows that receive.
+template <int CTRL, int ROWS>
+__device__ inline double dpp_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, ROWS, 0xF, false);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+__device__ inline double lane_f64(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), l);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), l);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+// Inclusive prefix sum over the 64 lanes (all lanes active): Hillis-Steele
+// within each row of 16, then the row totals carried across rows.
+__device__ inline double wave_scan_incl(double v) {
+    v += dpp_f64<0x111, 0xF>(v);
+    v += dpp_f64<0x112, 0xF>(v);
+    v += dpp_f64<0x114, 0xF>(v);
+    v += dpp_f64<0x118, 0xF>(v);
+    v += dpp_f64<0x142, 0xA>(v);
+    v += dpp_f64<0x143, 0xC>(v);
     return v;
 }
+// Sum over the 64 lanes (all lanes active), returned to every lane.
+__device__ inline double wave_sum(double v) { return lane_f64(wave_scan_incl(v), kWave - 1); }
 
 // --------------------------------------------------------------------------
-// Geometry of the statistics pass: rows [0, rows_t) are target rows in memory
-// order, rows [rows_t, rows) draft rows (absent at T == 0 and for the
-// stand-alone row statistics); each row is nchunk chunks; wave w owns chunks
-// [w*cpw, (w+1)*cpw) of the concatenation; row r's partials sit at
-// r*maxp + (w - first wave of r).
+// Device-coherent access. Agent-scope atomic loads and stores bypass the L2
+// cache of the XCD that issues them, so what one block publishes is read
+// unchanged by a block on another XCD.
 // --------------------------------------------------------------------------
-struct Geom {
-    int64_t rows_t;
-    int64_t rows;
-    int32_t V;
-    int32_t nchunk;
-    int64_t cpw;
-    int64_t nwaves;
-    int32_t maxp;
-    int32_t gamma;
-    const int32_t* tokens;  // draft tokens, or nullptr (no logit gather)
-};
-
-template <int DT>
-__device__ inline const char* row_ptr(const void* tgt, const void* dft, const Geom& g, int64_t r) {
-    return r < g.rows_t ? row_at<DT>(tgt, r * g.V) : row_at<DT>(dft, (r - g.rows_t) * g.V);
+__device__ inline void cst(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void cst(double* p, double v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       static_cast<unsigned long long>(__double_as_longlong(v)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void cst(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void cst(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float cld(const float* p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ inline double cld(const double* p) {
+    return __longlong_as_double(static_cast<long long>(
+        __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT)));
+}
+__device__ inline int32_t cld(const int32_t* p) {
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t cld(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Every memory operation this wavefront issued so far has completed (so its
+// coherent stores are visible device-wide) before anything after this point.
+__device__ inline void complete_before() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited on
+}
+// Loads after this point are issued after everything before it has completed.
+__device__ inline void after_complete() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+// Cross-lane exchange through LDS inside one wavefront.
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
-struct StatsArgs {
-    float c32;
-    float* part_m;    // max of the piece
-    float* part_r;    // integer reference of the piece (T > 0)
-    double* part_s;   // sum of 2^(x*c - reference) (T > 0)
-    int32_t* part_i;  // first index of the maximum (T == 0)
-    float* gath;      // per row: the logit at the row's draft token (written by the piece holding it)
+// Counts the calling wavefront in at a group counter once its coherent stores
+// have completed. Returns true to the last of `total` arrivals, which then sees
+// every earlier arrival's stores through coherent loads, and which resets the
+// counter for the next call (stream order makes the reset visible to it).
+__device__ inline bool arrive_last(uint32_t* cnt, uint32_t total, int lane) {
+    complete_before();
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, kWave);
+    if (old + 1u != total) return false;
+    after_complete();
+    if (lane == 0) cst(cnt, 0u);
+    return true;
+}
+
+// --------------------------------------------------------------------------
+// Launch geometry and arguments
+// --------------------------------------------------------------------------
+struct Params {
+    int32_t G;      // groups: sequences, or rows for the stand-alone statistics
+    int32_t rps;    // rows per group: 2*gamma+1 (T > 0), gamma+1 (T == 0), 1 (row statistics)
+    int32_t gamma;
+    int32_t V;
+    int32_t nchunk; // chunks per row
+    int32_t cpw;    // chunks per statistics wavefront
+    int32_t nw;     // statistics wavefronts per group
+    int32_t sb;     // statistics blocks per group
+    int32_t rb;     // residual blocks per group (0 at T == 0)
+    int32_t lag;    // groups between a group's statistics blocks and its residual blocks
+    int32_t maxp;   // partial slots per row (a row spans at most maxp wavefronts)
+    int32_t nsub;   // residual subsegments per row
+    int32_t stage;  // a group's partial slots staged in LDS, or 0 (fold from memory)
+    float c32;      // log2(e)/T
+    uint64_t seed;
+    int64_t b_offset;
+    const void* tgt;
+    const void* dft;
+    const int32_t* tokens;
+    int32_t* out_tokens;
+    int32_t* out_n;
+    float* rows_max;      // row statistics outputs
+    double* rows_sumexp;
+    float* part_m;        // per partial slot: max of the piece
+    float* part_r;        // integer reference of the piece (T > 0)
+    double* part_s;       // sum of 2^(x*c - reference) (T > 0)
+    int32_t* part_i;      // first index of the maximum (T == 0)
+    double* sub_r;        // [G, nsub] residual mass per subsegment (t units)
+    double* sub_p;        // [G, nsub] mass of p per subsegment (t units)
+    uint32_t* cnt_s;      // [G] statistics blocks counted in
+    uint32_t* cnt_r;      // [G] residual blocks counted in (T > 0)
+    uint32_t* err;        // sticky: a residual block's wait ran out
+    float* dbg_row_max;
+    double* dbg_row_sumexp;
+    double* dbg_p;
+    double* dbg_q;
+    double* dbg_z;
+    int32_t* dbg_argmax;
 };
 
-// --------------------------------------------------------------------------
-// k_stats. State at T > 0: per lane m = max seen and S = sum of
-// 2^(fl(x*c - R)) in fp64 (fp32 per load group); R is one integer reference
-// for the whole wavefront (kRUnset until the first finite value), set from the
-// wave's first group max. A group's exponentials use the current R while its
-// max is formed; only if some lane's group max exceeds R + 1 (a ballot) does
-// the wave move R up to ceil(wave max * c), rescale S exactly with ldexp and
-// redo the group. The flush is then a plain wave sum: every lane shares R.
-// --------------------------------------------------------------------------
+// Grid order: groups [0, lag) contribute their statistics blocks; each group
+// j in [lag, G) then contributes its statistics blocks followed by the
+// residual blocks of group j - lag; the residual blocks of the last lag groups
+// close the grid. A group's residual blocks thus always follow all of its
+// statistics blocks.
+__device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint32_t& g, uint32_t& idx) {
+    const uint32_t S = static_cast<uint32_t>(P.sb), R = static_cast<uint32_t>(P.rb);
+    const uint32_t D = static_cast<uint32_t>(P.lag), G = static_cast<uint32_t>(P.G);
+    const uint32_t head = D * S;
+    if (x < head) {
+        kind = kStatsBlock;
+        g = x / S;
+        idx = x - g * S;
+        return;
+    }
+    x -= head;
+    const uint32_t per = S + R;
+    const uint32_t mid = (G - D) * per;
+    if (x < mid) {
+        const uint32_t t = x / per, o = x - t * per;
+        if (o < S) {
+            kind = kStatsBlock;
+            g = D + t;
+            idx = o;
+        } else {
+            kind = kResidBlock;
+            g = t;
+            idx = o - S;
+        }
+        return;
+    }
+    x -= mid;  // only reached when R > 0
+    kind = kResidBlock;
+    const uint32_t t = x / R;
+    g = (G - D) + t;
+    idx = x - t * R;
+}
+
+// Row j of group g: target rows 0..gamma, then (T > 0) draft rows 0..gamma-1.
+template <int DT, int MODE>
+__device__ inline const char* group_row(const Params& P, uint32_t g, uint32_t j) {
+    if constexpr (MODE == kRows) {
+        return row_at<DT>(P.tgt, static_cast<int64_t>(g) * P.V);
+    } else {
+        const uint32_t nt = static_cast<uint32_t>(P.gamma) + 1u;
+        if (MODE == kGreedy || j < nt) return row_at<DT>(P.tgt, (static_cast<int64_t>(g) * nt + j) * P.V);
+        return row_at<DT>(P.dft, (static_cast<int64_t>(g) * P.gamma + (j - nt)) * P.V);
+    }
+}
+
 struct SoftLane {
     float m;
     float R;
@@ -352,88 +512,48 @@ __device__ inline void consume_group(ArgLane& s, const typename Chunk<DT, VEC>::
     }
 }
 
-// The logit at index tok, if the load group starting at chunk c0 holds it
-// (tok < c_end*CH keeps padding chunks of other pieces out): the lane that
-// holds it selects the word from its registers.
-template <int DT, bool VEC, int N>
-__device__ inline void pick_token(const typename Chunk<DT, VEC>::Raw* raw, int64_t c0, int64_t c_end, int lane,
-                                  int64_t tok, float& val, bool& found) {
-    using C = Chunk<DT, VEC>;
-    const int64_t off = tok - c0 * C::CH;
-    if (off >= 0 && off < N * C::CH && tok < c_end * C::CH) {  // wave-uniform, once per row
-        const int u = static_cast<int>(off / C::CH);
-        const int in = static_cast<int>(off - static_cast<int64_t>(u) * C::CH);
-        const int holder = VEC ? in / C::EPL : in % kWave;
-        const int v = VEC ? in % C::EPL : in / kWave;
-        // word index of the element within the lane's N loads, then a select chain
-        const int word = VEC ? u * 4 + (DT == SPEC_F32 ? v : v >> 1) : u * 4 + v;
-        uint32_t bits = 0u;
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            uint32_t b4[4];
-            if constexpr (VEC) {
-                b4[0] = raw[k].x; b4[1] = raw[k].y; b4[2] = raw[k].z; b4[3] = raw[k].w;
-            } else {
-                b4[0] = __float_as_uint(raw[k].x); b4[1] = __float_as_uint(raw[k].y);
-                b4[2] = __float_as_uint(raw[k].z); b4[3] = __float_as_uint(raw[k].w);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) bits = word == k * 4 + q ? b4[q] : bits;
-        }
-        const float x = (!VEC || DT == SPEC_F32) ? __uint_as_float(bits)
-                                                 : __uint_as_float((v & 1) ? (bits & 0xFFFF0000u) : (bits << 16));
-        if (lane == holder) {
-            val = x;
-            found = true;
-        }
-    }
-}
 
-template <int DT, bool VEC, bool GREEDY, bool GATHER>
-__global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, const void* __restrict__ dft,
-                                                  Geom g, StatsArgs sa) {
+// One row piece's partial, handed through LDS to the block's last wavefront,
+// which writes the block's pieces to memory.
+struct Piece {
+    int64_t slot;  // (g*rps + j)*maxp + k
+    double s;      // sum of 2^(x*c - r) (T > 0)
+    float m;       // max of the piece
+    float r;       // integer reference (T > 0)
+    int32_t i;     // first index of the maximum (T == 0)
+    int32_t npad;  // neutral slots after this one (the piece that ends its row)
+};
+constexpr int kMaxPieces = 4;  // row pieces per wavefront (the host keeps cpw <= 3 rows of chunks)
+struct BlockPieces {
+    Piece p[kWavesPerBlock][kMaxPieces];
+    int32_t n[kWavesPerBlock];
+    uint32_t done;
+};
+
+// Statistics of one wavefront's chunk range [wl*cpw, (wl+1)*cpw) of group g's
+// concatenated rows: one partial per row piece, for slot (g*rps + j)*maxp + k,
+// k = wl minus the first wavefront touching row j. The piece that ends a row
+// also covers the row's unused slots (a row spans maxp - 1 or maxp
+// wavefronts), which are written with neutral values, so folds read every
+// slot. Returns the number of pieces placed in `out` (lane 0 writes them).
+template <int DT, bool VEC, int MODE>
+__device__ inline int stats_wave(const Params& P, uint32_t g, uint32_t wl, int lane, Piece* out) {
+    int npieces = 0;
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
-    using Lane = typename std::conditional<GREEDY, ArgLane, SoftLane>::type;
-    const int lane = threadIdx.x & (kWave - 1);
-    // wave-uniform bookkeeping in 32-bit scalar registers (the host keeps the
-    // chunk count below 2^31): one division per wave finds the first row
-    const uint32_t w = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (w >= static_cast<uint32_t>(g.nwaves)) return;
-    const float c = sa.c32;
-    const uint32_t nchunk = static_cast<uint32_t>(g.nchunk), cpw = static_cast<uint32_t>(g.cpw);
-    const uint32_t total = static_cast<uint32_t>(g.rows) * nchunk;
-    uint32_t cc = w * cpw;
+    using Lane = typename std::conditional<MODE == kGreedy, ArgLane, SoftLane>::type;
+    const float c = P.c32;
+    const uint32_t nchunk = static_cast<uint32_t>(P.nchunk), cpw = static_cast<uint32_t>(P.cpw);
+    const uint32_t total = static_cast<uint32_t>(P.rps) * nchunk;
+    uint32_t cc = wl * cpw;
     const uint32_t c_end = cc + cpw < total ? cc + cpw : total;
-    uint32_t r = cc / nchunk;
-    uint32_t first = r * nchunk;
-    int32_t k = static_cast<int32_t>(w - first / cpw);  // partial slot of this wave's first piece
-    const uint32_t nt_row = static_cast<uint32_t>(g.gamma) + 1u;
+    uint32_t j = cc / nchunk;
+    uint32_t first = j * nchunk;
+    int32_t k = static_cast<int32_t>(wl - first / cpw);
     while (cc < c_end) {
         const uint32_t ce = first + nchunk < c_end ? first + nchunk : c_end;
-        const char* row = row_ptr<DT>(tgt, dft, g, r);
-        const int64_t c0 = cc - first, c1 = ce - first;  // this piece: chunks [c0, c1) of row r
-        // the draft token this row scores (T > 0), picked from registers as its
-        // chunk streams by
-        // (branch-free, and nothing reads the loaded value before tok_ready():
-        // the bonus row loads token 0 and has_tok drops it)
-        int32_t tok = -1;
-        bool has_tok = false;
-        if constexpr (GATHER) {
-            // index into draft_tokens of the token row r scores (none: the bonus row)
-            uint32_t tix;
-            if (r >= static_cast<uint32_t>(g.rows_t)) {
-                tix = r - static_cast<uint32_t>(g.rows_t);
-                has_tok = true;
-            } else {
-                const uint32_t b = r / nt_row, i = r - b * nt_row;
-                tix = b * (nt_row - 1u) + i;
-                has_tok = i + 1u < nt_row;
-            }
-            tok = g.tokens[has_tok ? tix : 0u];
-        }
-        float tok_logit = 0.0f;
-        bool tok_found = false;
+        const char* row = group_row<DT, MODE>(P, g, j);
+        const int64_t c0 = cc - first, c1 = ce - first;  // this piece: chunks [c0, c1) of row j
         Lane st;
         st.init();
         // load groups of kUnroll chunks. Every group but the last lies wholly in
@@ -453,34 +573,21 @@ __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, 
         };
         auto load_last = [&](Raw* q, int64_t gi) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) q[u] = C::load_clamped(row, c0 + gi * kUnroll + u, c_last, lane, g.V);
+            for (int u = 0; u < kUnroll; ++u) q[u] = C::load_clamped(row, c0 + gi * kUnroll + u, c_last, lane, P.V);
             __builtin_amdgcn_sched_barrier(0);
         };
-        // the token is first needed once the first group is in flight: nothing
-        // that reads it may be placed before those loads
-        auto tok_ready = [&]() {
-            if constexpr (GATHER) asm volatile("" : "+v"(tok) : : "memory");
-        };
-        auto eat = [&](const Raw* q, int64_t gi) {
-            const int64_t cg = c0 + gi * kUnroll;
-            consume_group<DT, VEC, kUnroll>(st, q, cg, lane, c);
-            if constexpr (GATHER) {
-                if (has_tok) pick_token<DT, VEC, kUnroll>(q, cg, c1, lane, tok, tok_logit, tok_found);
-            }
-        };
+        auto eat = [&](const Raw* q, int64_t gi) { consume_group<DT, VEC, kUnroll>(st, q, c0 + gi * kUnroll, lane, c); };
         auto eat_last = [&](Raw* q, int64_t gi) {
             const int64_t cg = c0 + gi * kUnroll;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) q[u] = C::mask(q[u], cg + u, c_last, lane, g.V);
+            for (int u = 0; u < kUnroll; ++u) q[u] = C::mask(q[u], cg + u, c_last, lane, P.V);
             eat(q, gi);
         };
         if (ng == 1) {
             load_last(qa, 0);
-            tok_ready();
             eat_last(qa, 0);
         } else {
             load(qa, 0);
-            tok_ready();
             int64_t gi = 1;  // next group to load; qa holds group gi - 1
             for (; gi + 2 < ng; gi += 2) {  // groups gi and gi + 1 are not the last
                 load(qb, gi);
@@ -500,54 +607,71 @@ __global__ __launch_bounds__(kBlock) void k_stats(const void* __restrict__ tgt, 
                 eat_last(qa, gi + 1);
             }
         }
-        const int64_t slot = static_cast<int64_t>(r) * g.maxp + k;
-        // the wave that ends the row also neutralises the row's unused slots
-        // (a row spans maxp - 1 or maxp waves), so merges read every slot
-        const bool pad = ce == first + nchunk && lane > 0 && k + lane < g.maxp;
-        if constexpr (GREEDY) {
+        Piece pc;
+        pc.slot = (static_cast<int64_t>(g) * P.rps + j) * P.maxp + k;
+        pc.npad = ce == first + nchunk ? P.maxp - 1 - k : 0;
+        if constexpr (MODE == kGreedy) {
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {  // (value desc, index asc) across the wave
                 const float ob = __shfl_xor(st.best, o, kWave);
                 const int32_t oa = __shfl_xor(st.at, o, kWave);
-                if (ob > st.best || (ob == st.best && oa < st.at)) { st.best = ob; st.at = oa; }
+                if (ob > st.best || (ob == st.best && oa < st.at)) {
+                    st.best = ob;
+                    st.at = oa;
+                }
             }
-            const bool any_nan = __ballot(st.nan) != 0;
-            if (lane == 0) {
-                sa.part_m[slot] = any_nan ? NAN : st.best;
-                sa.part_i[slot] = st.at;
-            } else if (pad) {
-                sa.part_m[slot + lane] = -INFINITY;
-                sa.part_i[slot + lane] = INT32_MAX;
-            }
+            pc.m = __ballot(st.nan) != 0 ? NAN : st.best;
+            pc.i = st.at;
+            pc.r = 0.0f;
+            pc.s = 0.0;
         } else {
-            const float M = wave_max(st.m);
-            const float Rw = st.R;  // shared by the wave
-            const double Sw = wave_sum(st.S);
-            if (lane == 0) {
-                sa.part_m[slot] = M;
-                sa.part_r[slot] = Rw;
-                sa.part_s[slot] = Sw;
-            } else if (pad) {
-                sa.part_m[slot + lane] = -INFINITY;
-                sa.part_r[slot + lane] = kRUnset;
-                sa.part_s[slot + lane] = 0.0;
-            }
-            if (tok_found) sa.gath[r] = tok_logit;
+            pc.m = wave_max(st.m);
+            pc.r = st.R;  // shared by the wave
+            pc.s = wave_sum(st.S);
+            pc.i = 0;
         }
+        if (lane == 0 && npieces < kMaxPieces) out[npieces] = pc;
+        ++npieces;
         cc = ce;
-        ++r;  // a later piece of this wave starts its row: slot 0
+        ++j;  // a later piece of this wave starts its row: slot 0
         first += nchunk;
         k = 0;
+    }
+    return npieces;
+}
+
+// The block's last statistics wavefront writes every piece of the block (and
+// the neutral slots after row-ending pieces) with coherent stores: lane e
+// takes piece e % kMaxPieces of wavefront e / kMaxPieces.
+template <int MODE>
+__device__ inline void write_pieces(const Params& P, const BlockPieces& bp, int nwaves, int lane) {
+    const int ww = lane / kMaxPieces, q = lane - ww * kMaxPieces;
+    if (ww >= nwaves || q >= bp.n[ww]) return;
+    const Piece pc = bp.p[ww][q];
+    if constexpr (MODE == kGreedy) {
+        cst(P.part_m + pc.slot, pc.m);
+        cst(P.part_i + pc.slot, pc.i);
+        for (int t = 1; t <= pc.npad; ++t) {
+            cst(P.part_m + pc.slot + t, -INFINITY);
+            cst(P.part_i + pc.slot + t, INT32_MAX);
+        }
+    } else {
+        cst(P.part_m + pc.slot, pc.m);
+        cst(P.part_r + pc.slot, pc.r);
+        cst(P.part_s + pc.slot, pc.s);
+        for (int t = 1; t <= pc.npad; ++t) {
+            cst(P.part_m + pc.slot + t, -INFINITY);
+            cst(P.part_r + pc.slot + t, kRUnset);
+            cst(P.part_s + pc.slot + t, 0.0);
+        }
     }
 }
 
 // --------------------------------------------------------------------------
-// Merging partials. A row's partials (M_p, R_p, S_p) combine exactly with
+// Folding partials. A row's partials (M_p, R_p, S_p) combine exactly with
 // ldexp onto the largest reference R; the result is rebased once to the row
 // max: S * 2^(R - M*c), the exponent formed exactly in fp64. The argmax
-// partials combine as (value desc, index asc); any NaN marks the row. A row
-// has maxp partial slots; the statistics pass fills the one it may leave
-// unused with a neutral entry, so every slot can be read blindly.
+// partials combine as (value desc, index asc); any NaN marks the row.
 // --------------------------------------------------------------------------
 struct RowStat {
     float m;
@@ -557,62 +681,10 @@ struct RowStat {
 
 __device__ inline bool usable(float M, double S) { return isfinite(M) && isfinite(S) && S > 0.0; }
 
-// Row j of sequence b as the accept step sees it: target rows 0..gamma first,
-// then (T > 0) draft rows 0..gamma-1.
-__device__ inline int64_t seq_row(const Geom& g, int64_t b, int j) {
-    const int nt = g.gamma + 1;
-    return j < nt ? b * nt + j : g.rows_t + b * g.gamma + (j - nt);
-}
-
-// One wavefront folds one row: lane k takes slots k, k+64, ...; the lanes
-// then combine with butterfly reductions. Every lane returns the row's stats.
+// One thread folds one row's np slots, staged in LDS, in slot order.
 template <bool GREEDY>
-__device__ inline RowStat fold_row_wave(const Geom& g, const StatsArgs& sa, int64_t r, int lane) {
-    const int64_t base = r * g.maxp;
-    RowStat o;
-    if constexpr (GREEDY) {
-        float best = -INFINITY;
-        int32_t arg = INT32_MAX;
-        bool nan = false;
-        for (int k = lane; k < g.maxp; k += kWave) {
-            const float v = sa.part_m[base + k];
-            const int32_t a = sa.part_i[base + k];
-            nan |= (v != v);
-            if (v > best || (v == best && a < arg)) { best = v; arg = a; }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ob = __shfl_xor(best, off, kWave);
-            const int32_t oa = __shfl_xor(arg, off, kWave);
-            if (ob > best || (ob == best && oa < arg)) { best = ob; arg = oa; }
-        }
-        o.m = __any(nan) ? NAN : best;
-        o.arg = arg;
-        o.s = 1.0;
-    } else {
-        float M = -INFINITY, R = kRUnset;
-        double S = 0.0;
-        for (int k = lane; k < g.maxp; k += kWave) {
-            const float mk = sa.part_m[base + k], rk = sa.part_r[base + k];
-            const double sk = sa.part_s[base + k];
-            const float Rn = fmaxf(R, rk);
-            S = rebase(S, R, Rn) + rebase(sk, rk, Rn);
-            R = Rn;
-            M = fmaxf(M, mk);
-        }
-        const float Mw = wave_max(M), Rw = wave_max(R);
-        const double Sw = wave_sum(rebase(S, R, Rw));
-        o.m = Mw;
-        o.arg = 0;
-        o.s = Sw * exp2(static_cast<double>(Rw) - static_cast<double>(Mw) * static_cast<double>(sa.c32));
-    }
-    return o;
-}
-
-// One thread folds one row from partials staged in LDS (np slots).
-template <bool GREEDY>
-__device__ inline RowStat fold_row(int np, const float* pm, const float* pr, const double* ps, const int32_t* pi,
-                                   float c32) {
+__device__ inline RowStat fold_slots(int np, const float* pm, const float* pr, const double* ps, const int32_t* pi,
+                                     float c32) {
     RowStat o;
     if constexpr (GREEDY) {
         float best = -INFINITY;
@@ -622,7 +694,10 @@ __device__ inline RowStat fold_row(int np, const float* pm, const float* pr, con
             const float v = pm[k];
             const int32_t a = pi[k];
             nan |= (v != v);
-            if (v > best || (v == best && a < arg)) { best = v; arg = a; }
+            if (v > best || (v == best && a < arg)) {
+                best = v;
+                arg = a;
+            }
         }
         o.m = nan ? NAN : best;
         o.arg = arg;
@@ -642,71 +717,205 @@ __device__ inline RowStat fold_row(int np, const float* pm, const float* pr, con
     return o;
 }
 
-// The nrows rows of sequence b folded into rs[0, nrows) (LDS), by a block of
-// NT threads. If their nrows*maxp partials fit the staging buffer (cap
-// entries of 20 bytes in dynamic LDS), every thread loads kMergeBatch of them
-// at a time, so the merge costs one round trip; then thread j folds row j.
-// Otherwise one wavefront folds each row straight from memory.
+// The same fold straight from memory (coherent loads, eight slots in flight),
+// for groups whose slots do not fit the LDS stage. The running sum is rebased
+// by powers of two as the reference grows, which gives the staged fold's value.
+template <bool GREEDY>
+__device__ inline RowStat fold_slots_mem(const Params& P, int64_t base) {
+    constexpr int kB = 8;
+    const int np = P.maxp;
+    RowStat o;
+    if constexpr (GREEDY) {
+        float best = -INFINITY;
+        int32_t arg = INT32_MAX;
+        bool nan = false;
+        for (int k0 = 0; k0 < np; k0 += kB) {
+            float v[kB];
+            int32_t a[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                v[u] = k0 + u < np ? cld(P.part_m + base + k0 + u) : -INFINITY;
+                a[u] = k0 + u < np ? cld(P.part_i + base + k0 + u) : INT32_MAX;
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                nan |= (v[u] != v[u]);
+                if (v[u] > best || (v[u] == best && a[u] < arg)) {
+                    best = v[u];
+                    arg = a[u];
+                }
+            }
+        }
+        o.m = nan ? NAN : best;
+        o.arg = arg;
+        o.s = 1.0;
+    } else {
+        float M = -INFINITY, R = kRUnset;
+        double S = 0.0;
+        for (int k0 = 0; k0 < np; k0 += kB) {
+            float m[kB], r[kB];
+            double s[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const bool in = k0 + u < np;
+                m[u] = in ? cld(P.part_m + base + k0 + u) : -INFINITY;
+                r[u] = in ? cld(P.part_r + base + k0 + u) : kRUnset;
+                s[u] = in ? cld(P.part_s + base + k0 + u) : 0.0;
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const float Rn = fmaxf(R, r[u]);
+                S = rebase(S, R, Rn) + rebase(s[u], r[u], Rn);
+                R = Rn;
+                M = fmaxf(M, m[u]);
+            }
+        }
+        o.m = M;
+        o.arg = 0;
+        o.s = S * exp2(static_cast<double>(R) - static_cast<double>(M) * static_cast<double>(P.c32));
+    }
+    return o;
+}
+
+// One wavefront folds one row (the stand-alone row statistics): lane k takes
+// slots k, k+64, ...; butterfly reductions combine the lanes.
+__device__ inline RowStat fold_row_wave(const Params& P, int64_t base, int lane) {
+    float M = -INFINITY, R = kRUnset;
+    double S = 0.0;
+    for (int k = lane; k < P.maxp; k += kWave) {
+        const float mk = cld(P.part_m + base + k), rk = cld(P.part_r + base + k);
+        const double sk = cld(P.part_s + base + k);
+        const float Rn = fmaxf(R, rk);
+        S = rebase(S, R, Rn) + rebase(sk, rk, Rn);
+        R = Rn;
+        M = fmaxf(M, mk);
+    }
+    const float Mw = wave_max(M), Rw = wave_max(R);
+    const double Sw = wave_sum(rebase(S, R, Rw));
+    RowStat o;
+    o.m = Mw;
+    o.arg = 0;
+    o.s = Sw * exp2(static_cast<double>(Rw) - static_cast<double>(Mw) * static_cast<double>(P.c32));
+    return o;
+}
+
+// Running fold state of a set of partials: soft (max m, reference r, sum s of
+// 2^(x*c - r)) or argmax (best value, its first index, any NaN).
+struct Fold {
+    float m, r;
+    double s;
+    int32_t arg;
+    bool nan;
+};
+__device__ inline Fold fold_init() { return Fold{-INFINITY, kRUnset, 0.0, INT32_MAX, false}; }
+template <bool GREEDY>
+__device__ inline void fold_add(Fold& f, float m, float r, double s, int32_t arg) {
+    if constexpr (GREEDY) {
+        f.nan |= (m != m);
+        if (m > f.m || (m == f.m && arg < f.arg)) {
+            f.m = m;
+            f.arg = arg;
+        }
+    } else {
+        const float rn = fmaxf(f.r, r);
+        f.s = rebase(f.s, f.r, rn) + rebase(s, r, rn);
+        f.r = rn;
+        f.m = fmaxf(f.m, m);
+    }
+}
+
+// The rps rows of group g folded into rs[0, rps) (LDS) by NT threads (a block,
+// or one wavefront). If the group's rps*maxp slots fit the stage, each thread
+// loads its share of them at once into LDS (one round trip), then q threads
+// per row (a power of two up to 16, q*rps <= NT) fold strided slots and
+// combine with butterfly shuffles; otherwise thread j folds row j from memory.
 template <bool GREEDY, int NT>
-__device__ inline void merge_seq(const Geom& g, const StatsArgs& sa, int64_t b, int nrows, int cap, char* dyn,
-                                 RowStat* rs) {
-    const int maxp = g.maxp;
+__device__ inline void merge_group(const Params& P, uint32_t g, char* dyn, RowStat* rs) {
+    constexpr int kPer = (kMaxStage + NT - 1) / NT;  // staged slots per thread
+    const int maxp = P.maxp, nrows = P.rps;
     const int slots = nrows * maxp;
-    if (slots <= cap) {
+    const int tid = NT == kWave ? static_cast<int>(threadIdx.x & (kWave - 1)) : static_cast<int>(threadIdx.x);
+    const int64_t base = static_cast<int64_t>(g) * slots;
+    auto sync = [] {
+        if constexpr (NT == kWave) wave_lds_sync();
+        else __syncthreads();
+    };
+    if (P.stage > 0) {
+        const int cap = P.stage;
         double* ls = reinterpret_cast<double*>(dyn);
         float* lm = reinterpret_cast<float*>(ls + cap);
         float* lr = lm + cap;
         int32_t* li = reinterpret_cast<int32_t*>(lr + cap);
-        for (int t0 = 0; t0 < slots; t0 += kMergeBatch * NT) {
-            float vm[kMergeBatch], vr[kMergeBatch];
-            double vs[kMergeBatch];
-            int32_t vi[kMergeBatch];
+        float vm[kPer], vr[kPer];
+        double vs[kPer];
+        int32_t vi[kPer];
 #pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u) {
-                const int t = t0 + u * NT + static_cast<int>(threadIdx.x);
-                if (t < slots) {
-                    const int j = t / maxp;
-                    const int64_t at = seq_row(g, b, j) * maxp + (t - j * maxp);
-                    vm[u] = sa.part_m[at];
-                    if constexpr (GREEDY) {
-                        vi[u] = sa.part_i[at];
-                    } else {
-                        vr[u] = sa.part_r[at];
-                        vs[u] = sa.part_s[at];
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u) {
-                const int t = t0 + u * NT + static_cast<int>(threadIdx.x);
-                if (t < slots) {
-                    lm[t] = vm[u];
-                    if constexpr (GREEDY) {
-                        li[t] = vi[u];
-                    } else {
-                        lr[t] = vr[u];
-                        ls[t] = vs[u];
-                    }
+        for (int u = 0; u < kPer; ++u) {
+            const int t = u * NT + tid;
+            if (t < slots) {
+                vm[u] = cld(P.part_m + base + t);
+                if constexpr (GREEDY) {
+                    vi[u] = cld(P.part_i + base + t);
+                } else {
+                    vr[u] = cld(P.part_r + base + t);
+                    vs[u] = cld(P.part_s + base + t);
                 }
             }
         }
-        __syncthreads();
-        for (int j = threadIdx.x; j < nrows; j += NT) {
-            const int base = j * maxp;
-            rs[j] = fold_row<GREEDY>(maxp, lm + base, lr + base, ls + base, li + base, sa.c32);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int t = u * NT + tid;
+            if (t < slots) {
+                lm[t] = vm[u];
+                if constexpr (GREEDY) {
+                    li[t] = vi[u];
+                } else {
+                    lr[t] = vr[u];
+                    ls[t] = vs[u];
+                }
+            }
+        }
+        sync();
+        int q = 1;
+        while (q < 16 && 2 * q * nrows <= NT) q *= 2;
+        const int rows_per_pass = NT / q;
+        for (int j0 = 0; j0 < nrows; j0 += rows_per_pass) {
+            const int j = j0 + tid / q, part = tid % q;
+            Fold f = fold_init();
+            if (j < nrows)
+                for (int k = part; k < maxp; k += q) {
+                    const int t = j * maxp + k;
+                    fold_add<GREEDY>(f, lm[t], GREEDY ? 0.0f : lr[t], GREEDY ? 0.0 : ls[t], GREEDY ? li[t] : 0);
+                }
+            for (int o = q / 2; o > 0; o >>= 1) {  // combine the q threads of the row (same wavefront)
+                const float om = __shfl_xor(f.m, o, kWave);
+                if constexpr (GREEDY) {
+                    const int32_t oa = __shfl_xor(f.arg, o, kWave);
+                    const bool on = __shfl_xor(f.nan ? 1 : 0, o, kWave) != 0;
+                    fold_add<true>(f, om, 0.0f, 0.0, oa);
+                    f.nan |= on;
+                } else {
+                    const float orr = __shfl_xor(f.r, o, kWave);
+                    const double os = __shfl_xor(f.s, o, kWave);
+                    fold_add<false>(f, om, orr, os, 0);
+                }
+            }
+            if (j < nrows && part == 0) {
+                RowStat o;
+                o.m = GREEDY && f.nan ? NAN : f.m;
+                o.arg = GREEDY ? f.arg : 0;
+                o.s = GREEDY ? 1.0
+                             : f.s * exp2(static_cast<double>(f.r) - static_cast<double>(f.m) * static_cast<double>(P.c32));
+                rs[j] = o;
+            }
         }
     } else {
-        const int lane = threadIdx.x & (kWave - 1);
-        for (int j = threadIdx.x / kWave; j < nrows; j += NT / kWave) {
-            const RowStat o = fold_row_wave<GREEDY>(g, sa, seq_row(g, b, j), lane);
-            if (lane == 0) rs[j] = o;
-        }
+        for (int j = tid; j < nrows; j += NT) rs[j] = fold_slots_mem<GREEDY>(P, base + static_cast<int64_t>(j) * maxp);
     }
-    __syncthreads();
+    sync();
 }
 
-// What the residual sums and the draw need about the row a sequence resamples
-// (see the residual section below for the t units).
+// What the residual sums and the draw need about the row a sequence resamples.
 struct SeqInfo {
     int32_t k;       // emitted position (0..gamma), -1 = invalid sequence
     float mcp, mcq;  // fl(max*c) of the target row k / draft row k
@@ -715,29 +924,129 @@ struct SeqInfo {
     double scale_p;  // 2^(mcp - max_p*c) / S_p: probability per t unit
 };
 
+// The residual constants of a row pair from its folded stats (max m, sum S).
+__device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float mq, double sq, float c32) {
+    SeqInfo si;
+    const double c = static_cast<double>(c32);
+    si.k = k;
+    si.has_q = has_q ? 1 : 0;
+    si.mcp = mp * c32;
+    si.scale_p = exp2(static_cast<double>(si.mcp) - static_cast<double>(mp) * c) / sp;
+    si.mcq = has_q ? mq * c32 : 0.0f;
+    si.rho = has_q ? exp2(static_cast<double>(si.mcq) - static_cast<double>(mq) * c) / sq / si.scale_p : 0.0;
+    return si;
+}
 
-struct AcceptArgs {
-    const int32_t* tokens;
-    const float* gath;  // per row: logit at its draft token (from the statistics pass)
-    int32_t B, gamma, V;
-    int32_t nsub;       // subsegments per row: ceil(V / kSub)
-    int32_t nblk;       // blocks per sequence (T > 0)
-    int32_t spb;        // subsegments per block
-    int32_t stage;      // partial slots staged in LDS per sequence (0: fold from memory)
-    float c32;
-    uint64_t seed;
-    int64_t b_offset;
-    int32_t* out_tokens;
-    int32_t* out_n;
-    SeqInfo* info;
-    double* sub_r;      // [B, nsub] residual mass per subsegment (t units)
-    double* sub_p;      // [B, nsub] mass of p per subsegment (t units)
-    float* dbg_row_max;
-    double* dbg_row_sumexp;
-    double* dbg_p;
-    double* dbg_q;
-    int32_t* dbg_argmax;
-};
+// --------------------------------------------------------------------------
+// The accept step, by one wavefront after the group's rows are folded into rs
+// (target rows 0..gamma, then draft rows at T > 0): lane i takes draft token
+// i, forms alpha in fp64 (greedy: compares the token with the row's argmax),
+// draws its Philox uniform, and a ballot finds the first rejection k. With
+// `emit` it writes k, the accepted tokens and the -1 padding (greedy also the
+// emitted argmax; the sampled token at k is left to the draw) and the debug
+// values. Returns the sequence record the residual needs.
+// --------------------------------------------------------------------------
+template <bool GREEDY>
+__device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat* rs, int32_t x, float lt, float ld,
+                                      bool emit) {
+    const int32_t gamma = P.gamma, V = P.V;
+    const int nt = gamma + 1;
+    const int i = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int64_t b = g;
+    const int64_t R = 2 * gamma + 1;
+    const bool tok_ok = x >= 0 && x < V;
+    int status = kAcc;
+    float mt = NAN, md = NAN;
+    double st = NAN, sd = NAN;
+    bool ut = false;
+    int32_t amax = -1;
+    if (i <= gamma) {
+        const RowStat t = rs[i];
+        mt = t.m;
+        if (emit && P.dbg_row_max) P.dbg_row_max[b * R + i] = mt;
+        if constexpr (GREEDY) {
+            amax = t.arg;
+            ut = isfinite(mt);
+            if (emit && P.dbg_argmax) P.dbg_argmax[b * nt + i] = amax;
+        } else {
+            st = t.s;
+            ut = usable(mt, st);
+            if (emit && P.dbg_row_sumexp) P.dbg_row_sumexp[b * R + i] = st;
+        }
+    }
+    if (i < gamma) {
+        if constexpr (GREEDY) {
+            status = (!ut || !tok_ok) ? kBad : (x == amax ? kAcc : kRej);
+        } else {
+            const RowStat dr = rs[nt + i];
+            md = dr.m;
+            sd = dr.s;
+            const bool ud = usable(md, sd);
+            if (emit && P.dbg_row_max) P.dbg_row_max[b * R + nt + i] = md;
+            if (emit && P.dbg_row_sumexp) P.dbg_row_sumexp[b * R + nt + i] = sd;
+            double p = NAN, q = NAN;
+            if (!ut || !ud || !tok_ok) {
+                status = kBad;
+            } else {
+                const double c = static_cast<double>(P.c32);
+                p = exp2((static_cast<double>(lt) - static_cast<double>(mt)) * c) / st;
+                q = exp2((static_cast<double>(ld) - static_cast<double>(md)) * c) / sd;
+                const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+                const double u = philox_uniform(P.seed, static_cast<uint32_t>(b + P.b_offset),
+                                                static_cast<uint32_t>(i), 0u);
+                status = u < alpha ? kAcc : kRej;
+            }
+            if (emit && P.dbg_p) P.dbg_p[b * gamma + i] = p;
+            if (emit && P.dbg_q) P.dbg_q[b * gamma + i] = q;
+        }
+    }
+    SeqInfo mine{};
+    if constexpr (!GREEDY) {
+        if (i <= gamma) mine = seq_info(i, i < gamma, mt, st, md, sd, P.c32);
+    }
+    const uint64_t stop = __ballot(i < gamma && status != kAcc);
+    const int f = stop ? __ffsll(static_cast<unsigned long long>(stop)) - 1 : gamma;
+    const int fstat = __shfl(status, f, kWave);
+    const bool bonus_ok = __shfl(ut ? 1 : 0, gamma, kWave) != 0;
+    const bool invalid = f < gamma ? (fstat == kBad) : !bonus_ok;
+    const int k = invalid ? -1 : f;
+    if (emit) {
+        if (i <= gamma) {
+            int32_t o = -1;
+            bool write = true;
+            if (!invalid) {
+                if (i < k) o = x;
+                else if (i == k) {
+                    if constexpr (GREEDY) o = amax;
+                    else write = false;
+                }
+            }
+            if (write) cst(P.out_tokens + b * nt + i, o);
+        }
+        if (i == 0) {
+            cst(P.out_n + b, k);
+            if (!GREEDY && invalid && P.dbg_z) P.dbg_z[b] = NAN;
+        }
+    }
+    SeqInfo si;
+    si.k = -1; si.mcp = 0.0f; si.mcq = 0.0f; si.has_q = 0; si.rho = 0.0; si.scale_p = 0.0;
+    if constexpr (!GREEDY) {
+        // lane k holds the constants of row k (every lane formed its own
+        // before the ballot); broadcast them
+        const int src = invalid ? 0 : k;
+        const float mcp = __shfl(mine.mcp, src, kWave), mcq = __shfl(mine.mcq, src, kWave);
+        const double rho = __shfl(mine.rho, src, kWave), scale_p = __shfl(mine.scale_p, src, kWave);
+        if (!invalid) {
+            si.k = k;
+            si.has_q = k < gamma ? 1 : 0;
+            si.mcp = mcp;
+            si.mcq = mcq;
+            si.rho = rho;
+            si.scale_p = scale_p;
+        }
+    }
+    return si;
+}
 
 // --------------------------------------------------------------------------
 // Residual in t units. With e_j = 2^(fl(x_j*c - mc)) for the target (p) and
@@ -755,28 +1064,14 @@ struct ResidRow {
 };
 
 template <int DT>
-__device__ inline ResidRow resid_row(const void* tgt, const void* dft, const SeqInfo& s, int64_t b,
-                                     int32_t gamma, int32_t V) {
+__device__ inline ResidRow resid_row(const Params& P, const SeqInfo& s, uint32_t g) {
     ResidRow rr;
-    rr.prow = row_at<DT>(tgt, (b * (gamma + 1) + s.k) * V);
-    rr.qrow = s.has_q ? row_at<DT>(dft, (b * gamma + s.k) * V) : nullptr;
+    rr.prow = group_row<DT, kSample>(P, g, static_cast<uint32_t>(s.k));
+    rr.qrow = s.has_q ? group_row<DT, kSample>(P, g, static_cast<uint32_t>(P.gamma + 1 + s.k)) : nullptr;
     rr.mcp = s.mcp;
     rr.mcq = s.mcq;
     rr.rho = s.rho;
     return rr;
-}
-
-// The residual constants of a row pair from its merged stats (max m, sum S).
-__device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float mq, double sq, float c32) {
-    SeqInfo si;
-    const double c = static_cast<double>(c32);
-    si.k = k;
-    si.has_q = has_q ? 1 : 0;
-    si.mcp = mp * c32;
-    si.scale_p = exp2(static_cast<double>(si.mcp) - static_cast<double>(mp) * c) / sp;
-    si.mcq = has_q ? mq * c32 : 0.0f;
-    si.rho = has_q ? exp2(static_cast<double>(si.mcq) - static_cast<double>(mq) * c) / sq / si.scale_p : 0.0;
-    return si;
 }
 
 __device__ inline float t_of_p(float xp, const ResidRow& rr, float c32) {
@@ -788,6 +1083,33 @@ __device__ inline double resid_t(double ep, float xq, bool has_q, float c32, con
     const double eq = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xq, c32, -rr.mcq)));
     return fmax(0.0, fma(-eq, rr.rho, ep));
 }
+
+// Residual subsegments one wavefront keeps in flight: 64 VGPRs of raw 16-byte
+// loads (vector path), one subsegment on the scalar path.
+template <int DT, bool VEC>
+__host__ __device__ constexpr int subs_per_wave() { return VEC ? (DT == SPEC_BF16 ? 4 : 2) : 1; }
+
+// Raw loads of one lane's 16 elements of a subsegment (vector path): each
+// 16-byte load is taken only if it starts below V, which puts it wholly inside
+// the row (V % EPL == 0 there); the rest read as -inf in p (no mass) and 0 in q.
+template <int DT>
+struct SubRaw {
+    static constexpr int EPL = 16 / ElemBytes<DT>::value;
+    static constexpr int NV = 16 / EPL;
+    uint4 p[NV], q[NV];
+    __device__ inline void load(const ResidRow& rr, bool has_q, int64_t j0, int32_t V) {
+        const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int64_t j = j0 + u * EPL;
+            const bool in = j < V;
+            p[u] = in ? *reinterpret_cast<const uint4*>(rr.prow + j * ElemBytes<DT>::value)
+                      : make_uint4(ninf, ninf, ninf, ninf);
+            q[u] = in && has_q ? *reinterpret_cast<const uint4*>(rr.qrow + j * ElemBytes<DT>::value)
+                               : make_uint4(0, 0, 0, 0);
+        }
+    }
+};
 
 // The 16 elements of lane `lane` in subsegment i: j0 = i*kSub + 16*lane, ...
 // (p row; q row when has_q). Vector path: 16-byte loads, each taken only if it
@@ -825,226 +1147,23 @@ __device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int3
 }
 
 // --------------------------------------------------------------------------
-// The accept step, run by the first wavefront after merge_seq: lane i takes
-// draft token i, forms alpha in fp64, draws its Philox uniform, and a ballot
-// finds the first rejection k. Writes the accepted tokens and k (when `emit`),
-// and returns the sequence record for the residual.
+// The draw, by the group's last residual wavefront: wave scans of the
+// subsegment masses give Z and the subsegment holding u*Z; a scan over that
+// subsegment's 1024 elements (16 per lane, in registers) gives the first index
+// whose cumulative mass exceeds u*Z. If rounding leaves no residual mass at a
+// rejected row the draw is made from p_k instead (its masses come from the
+// same pass).
 // --------------------------------------------------------------------------
-template <bool GREEDY>
-__device__ inline SeqInfo accept_wave(const Geom& g, const AcceptArgs& a, int64_t b, const RowStat* rs, int32_t x,
-                                      float lt, float ld, bool emit) {
-    const int32_t gamma = a.gamma, V = a.V;
-    const int nt = gamma + 1;
-    const int i = threadIdx.x;  // lane of wave 0
-    const int64_t R = 2 * gamma + 1;
-    const bool tok_ok = x >= 0 && x < V;
-    int status = kAcc;
-    float mt = NAN, md = NAN;
-    double st = NAN, sd = NAN;
-    bool ut = false;
-    int32_t amax = -1;
-    if (i <= gamma) {
-        const RowStat t = rs[i];
-        mt = t.m;
-        if (emit && a.dbg_row_max) a.dbg_row_max[b * R + i] = mt;
-        if constexpr (GREEDY) {
-            amax = t.arg;
-            ut = isfinite(mt);
-            if (emit && a.dbg_argmax) a.dbg_argmax[b * nt + i] = amax;
-        } else {
-            st = t.s;
-            ut = usable(mt, st);
-            if (emit && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + i] = st;
-        }
-    }
-    if (i < gamma) {
-        if constexpr (GREEDY) {
-            status = (!ut || !tok_ok) ? kBad : (x == amax ? kAcc : kRej);
-        } else {
-            const RowStat dr = rs[nt + i];
-            md = dr.m;
-            sd = dr.s;
-            const bool ud = usable(md, sd);
-            if (emit && a.dbg_row_max) a.dbg_row_max[b * R + nt + i] = md;
-            if (emit && a.dbg_row_sumexp) a.dbg_row_sumexp[b * R + nt + i] = sd;
-            double p = NAN, q = NAN;
-            if (!ut || !ud || !tok_ok) {
-                status = kBad;
-            } else {
-                const double c = static_cast<double>(a.c32);
-                p = exp2((static_cast<double>(lt) - static_cast<double>(mt)) * c) / st;
-                q = exp2((static_cast<double>(ld) - static_cast<double>(md)) * c) / sd;
-                const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
-                const double u = philox_uniform(a.seed, static_cast<uint32_t>(b + a.b_offset),
-                                                static_cast<uint32_t>(i), 0u);
-                status = u < alpha ? kAcc : kRej;
-            }
-            if (emit && a.dbg_p) a.dbg_p[b * gamma + i] = p;
-            if (emit && a.dbg_q) a.dbg_q[b * gamma + i] = q;
-        }
-    }
-    SeqInfo mine{};
-    if constexpr (!GREEDY) {
-        if (i <= gamma) mine = seq_info(i, i < gamma, mt, st, md, sd, a.c32);
-    }
-    const uint64_t stop = __ballot(i < gamma && status != kAcc);
-    const int f = stop ? __ffsll(static_cast<unsigned long long>(stop)) - 1 : gamma;
-    const int fstat = __shfl(status, f, kWave);
-    const bool bonus_ok = __shfl(ut ? 1 : 0, gamma, kWave) != 0;
-    const bool invalid = f < gamma ? (fstat == kBad) : !bonus_ok;
-    const int k = invalid ? -1 : f;
-    if (emit) {
-        if (i <= gamma) {
-            int32_t o = -1;
-            if (!invalid) {
-                if (i < k) o = x;
-                else if (GREEDY && i == k) o = amax;
-            }
-            a.out_tokens[b * nt + i] = o;
-        }
-        if (i == 0) a.out_n[b] = k;
-    }
-    SeqInfo si;
-    si.k = -1; si.mcp = 0.0f; si.mcq = 0.0f; si.has_q = 0; si.rho = 0.0; si.scale_p = 0.0;
-    if constexpr (!GREEDY) {
-        // lane k holds the constants of row k (every lane formed its own
-        // before the ballot); broadcast them
-        const int src = invalid ? 0 : k;
-        const float mcp = __shfl(mine.mcp, src, kWave), mcq = __shfl(mine.mcq, src, kWave);
-        const double rho = __shfl(mine.rho, src, kWave), scale_p = __shfl(mine.scale_p, src, kWave);
-        if (!invalid) {
-            si.k = k;
-            si.has_q = k < gamma ? 1 : 0;
-            si.mcp = mcp;
-            si.mcq = mcq;
-            si.rho = rho;
-            si.scale_p = scale_p;
-        }
-    }
-    return si;
-}
-
-// Draft token i and its two logits (gathered by the statistics pass).
-template <bool GREEDY>
-__device__ inline void load_tokens(const Geom& g, const AcceptArgs& a, int64_t b, int32_t& x, float& lt, float& ld) {
-    x = 0;
-    lt = 0.0f;
-    ld = 0.0f;
-    const int i = threadIdx.x;
-    if (i < a.gamma) {
-        x = a.tokens[b * a.gamma + i];
-        if constexpr (!GREEDY) {
-            lt = a.gath[b * (a.gamma + 1) + i];
-            ld = a.gath[g.rows_t + b * a.gamma + i];
-        }
-    }
-}
-
-// --------------------------------------------------------------------------
-// k_accept (T == 0): one block per sequence: argmax merge and the accept step.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_accept_greedy(Geom g, StatsArgs sa, AcceptArgs a) {
-    extern __shared__ __align__(16) char dyn[];
-    __shared__ RowStat rs[SPEC_MAX_GAMMA + 1];
-    const int64_t b = blockIdx.x;
-    int32_t x;
-    float lt, ld;
-    if (threadIdx.x < kWave) load_tokens<true>(g, a, b, x, lt, ld);
-    merge_seq<true, kBlock>(g, sa, b, a.gamma + 1, a.stage, dyn, rs);
-    if (threadIdx.x < kWave) (void)accept_wave<true>(g, a, b, rs, x, lt, ld, true);
-}
-
-// --------------------------------------------------------------------------
-// k_accept_resid (T > 0): nblk blocks per sequence. Every block merges the
-// sequence's partials and repeats the accept step (a few kilobytes of loads
-// and a few hundred instructions); block 0 writes the tokens, k and the
-// sequence record. Then each wavefront takes subsegments of row k and writes
-// their fp64 residual mass and p mass (t units).
-// --------------------------------------------------------------------------
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kTailBlock) void k_accept_resid(const void* __restrict__ tgt,
-                                                             const void* __restrict__ dft, Geom g, StatsArgs sa,
-                                                             AcceptArgs a) {
-    extern __shared__ __align__(16) char dyn[];
-    __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
-    __shared__ SeqInfo shi;
-    constexpr int kTailWaves = kTailBlock / kWave;
-    const int64_t b = blockIdx.x / a.nblk;
-    const int32_t s = static_cast<int32_t>(blockIdx.x - b * a.nblk);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    int32_t x;
-    float lt, ld;
-    if (w == 0) load_tokens<false>(g, a, b, x, lt, ld);
-    merge_seq<false, kTailBlock>(g, sa, b, 2 * a.gamma + 1, a.stage, dyn, rs);
-    if (w == 0) {
-        const SeqInfo si = accept_wave<false>(g, a, b, rs, x, lt, ld, s == 0);
-        if (lane == 0) {
-            shi = si;
-            if (s == 0) a.info[b] = si;
-        }
-    }
-    __syncthreads();
-    const SeqInfo in = shi;
-    if (in.k < 0) return;  // block-uniform
-    const float c32 = a.c32;
-    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, a.gamma, a.V);
-    const bool has_q = rr.qrow != nullptr;
-    const int32_t i_end = (s + 1) * a.spb < a.nsub ? (s + 1) * a.spb : a.nsub;
-    for (int32_t i = s * a.spb + w; i < i_end; i += kTailWaves) {
-        float xp[16], xq[16];
-        load_sub<DT, VEC>(rr, has_q, static_cast<int64_t>(i) * kSub + 16 * lane, a.V, xp, xq);
-        double tr = 0.0;
-        float tpf = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float ep = t_of_p(xp[v], rr, c32);
-            tpf += ep;
-            tr += resid_t(static_cast<double>(ep), xq[v], has_q, c32, rr);
-        }
-        tr = wave_sum(tr);
-        const double tp = wave_sum(static_cast<double>(tpf));
-        if (lane == 0) {
-            a.sub_r[b * a.nsub + i] = tr;
-            a.sub_p[b * a.nsub + i] = tp;
-        }
-    }
-}
-
-// --------------------------------------------------------------------------
-// k_draw: one wavefront per sequence. Wave scans of the subsegment masses
-// give Z and the subsegment holding u*Z; a scan over that subsegment's 1024
-// elements (16 per lane, in registers) gives the first index whose cumulative
-// mass exceeds u*Z. If rounding leaves no residual mass at a rejected row the
-// draw is made from p_k instead (its masses come from the same pass).
-// --------------------------------------------------------------------------
-struct DrawArgs {
-    int32_t gamma, V, nsub;
-    float c32;
-    uint64_t seed;
-    int64_t b_offset;
-    const SeqInfo* info;
-    const double* sub_r;
-    const double* sub_p;
-    int32_t* out_tokens;
-    double* dbg_z;
-};
-
-__device__ inline double wave_scan(double v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(v, o, kWave);
-        if (lane >= o) v += y;
-    }
-    return v;
-}
+__device__ inline double wave_scan(double v, int) { return wave_scan_incl(v); }
+// The value of lane l - 1 (0 in lane 0).
+__device__ inline double lane_before(double v) { return dpp_f64<0x138, 0xF>(v); }
 
 // Total of m[0, n) in the order the search below accumulates it.
 __device__ inline double scan_total(const double* m, int32_t n, int lane) {
     double base = 0.0;
     for (int32_t t0 = 0; t0 < n; t0 += kWave) {
-        const double v = t0 + lane < n ? m[t0 + lane] : 0.0;
-        base += __shfl(wave_scan(v, lane), kWave - 1, kWave);
+        const double v = t0 + lane < n ? cld(m + t0 + lane) : 0.0;
+        base += lane_f64(wave_scan(v, lane), kWave - 1);
     }
     return base;
 }
@@ -1056,9 +1175,9 @@ __device__ inline int32_t scan_find(const double* m, int32_t n, double t, int la
     int32_t last = -1;
     double last_before = 0.0;
     for (int32_t t0 = 0; t0 < n; t0 += kWave) {
-        const double v = t0 + lane < n ? m[t0 + lane] : 0.0;
+        const double v = t0 + lane < n ? cld(m + t0 + lane) : 0.0;
         const double incl = base + wave_scan(v, lane);
-        const double prev = __shfl_up(incl, 1, kWave);
+        const double prev = lane_before(incl);
         const double excl = lane == 0 ? base : prev;
         const uint64_t hit = __ballot(v > 0.0 && excl <= t && t < incl);
         if (hit) {
@@ -1072,7 +1191,7 @@ __device__ inline int32_t scan_find(const double* m, int32_t n, double t, int la
             last = t0 + l;
             last_before = __shfl(excl, l, kWave);
         }
-        base = __shfl(incl, kWave - 1, kWave);
+        base = lane_f64(incl, kWave - 1);
     }
     before = last_before;
     return last;
@@ -1087,7 +1206,7 @@ __device__ inline double regs_scan(const double* v, double* incl, int lane) {
 #pragma unroll
     for (int t = 0; t < kDrawTiles; ++t) {
         incl[t] = base + wave_scan(v[t], lane);
-        base = __shfl(incl[t], kWave - 1, kWave);
+        base = lane_f64(incl[t], kWave - 1);
     }
     return base;
 }
@@ -1097,8 +1216,8 @@ __device__ inline int32_t regs_find(const double* v, const double* incl, double 
     double last_before = 0.0;
 #pragma unroll
     for (int k = 0; k < kDrawTiles; ++k) {
-        const double prev = __shfl_up(incl[k], 1, kWave);
-        const double base = k == 0 ? 0.0 : __shfl(incl[k - 1], kWave - 1, kWave);
+        const double prev = lane_before(incl[k]);
+        const double base = k == 0 ? 0.0 : lane_f64(incl[k - 1], kWave - 1);
         const double excl = lane == 0 ? base : prev;
         const uint64_t hit = __ballot(v[k] > 0.0 && excl <= t && t < incl[k]);
         if (hit) {
@@ -1118,31 +1237,23 @@ __device__ inline int32_t regs_find(const double* v, const double* incl, double 
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kWave) void k_draw(const void* __restrict__ tgt, const void* __restrict__ dft,
-                                                DrawArgs d) {
-    const int64_t b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const SeqInfo in = d.info[b];
-    if (in.k < 0) {
-        if (d.dbg_z && lane == 0) d.dbg_z[b] = NAN;
-        return;
-    }
-    const int32_t nsub = d.nsub;
-    const double* sr = d.sub_r + b * nsub;
-    const double* sp = d.sub_p + b * nsub;
-    const double u = philox_uniform(d.seed, static_cast<uint32_t>(b + d.b_offset), static_cast<uint32_t>(in.k), 1u);
+__device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int lane) {
+    const int32_t nsub = P.nsub;
+    const double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
+    const double* sp = P.sub_p + static_cast<int64_t>(g) * nsub;
+    const double u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(in.k), 1u);
     double Z, target, before = 0.0;
     int32_t sel;
     bool from_p = false;  // no residual mass left by rounding: draw from p_k
     if (nsub <= kDrawTiles * kWave) {
         double v[kDrawTiles], incl[kDrawTiles];
 #pragma unroll
-        for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? sr[t * kWave + lane] : 0.0;
+        for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? cld(sr + t * kWave + lane) : 0.0;
         Z = regs_scan(v, incl, lane);
         from_p = !(Z > 0.0);
         if (from_p) {
 #pragma unroll
-            for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? sp[t * kWave + lane] : 0.0;
+            for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? cld(sp + t * kWave + lane) : 0.0;
             target = u * regs_scan(v, incl, lane);
         } else {
             target = u * Z;
@@ -1155,28 +1266,28 @@ __global__ __launch_bounds__(kWave) void k_draw(const void* __restrict__ tgt, co
         target = u * (from_p ? scan_total(sp, nsub, lane) : Z);
         sel = scan_find(m, nsub, target, lane, before);
     }
-    if (d.dbg_z && lane == 0) d.dbg_z[b] = Z * in.scale_p;
-    int32_t* out = d.out_tokens + b * (d.gamma + 1) + in.k;
+    if (P.dbg_z && lane == 0) P.dbg_z[g] = Z * in.scale_p;
+    int32_t* out = P.out_tokens + static_cast<int64_t>(g) * (P.gamma + 1) + in.k;
     if (sel < 0) {  // no mass at all (cannot happen for a usable row); keep the output defined
-        if (lane == 0) *out = -1;
+        if (lane == 0) cst(out, -1);
         return;
     }
-    const ResidRow rr = resid_row<DT>(tgt, dft, in, b, d.gamma, d.V);
+    const ResidRow rr = resid_row<DT>(P, in, g);
     const bool has_q = rr.qrow != nullptr && !from_p;
     const int64_t j0 = static_cast<int64_t>(sel) * kSub + 16 * lane;
     float xp[16], xq[16];
-    load_sub<DT, VEC>(rr, has_q, j0, d.V, xp, xq);
+    load_sub<DT, VEC>(rr, has_q, j0, P.V, xp, xq);
     double mv[16];
     double local = 0.0;
     int32_t mylast = -1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        mv[v] = resid_t(static_cast<double>(t_of_p(xp[v], rr, d.c32)), xq[v], has_q, d.c32, rr);
+        mv[v] = resid_t(static_cast<double>(t_of_p(xp[v], rr, P.c32)), xq[v], has_q, P.c32, rr);
         local += mv[v];
         if (mv[v] > 0.0) mylast = static_cast<int32_t>(j0 + v);
     }
     const double incl = before + wave_scan(local, lane);
-    const double prev = __shfl_up(incl, 1, kWave);
+    const double prev = lane_before(incl);
     const double excl = lane == 0 ? before : prev;
     const uint64_t hit = __ballot(local > 0.0 && excl <= target && target < incl);
     if (hit) {
@@ -1189,27 +1300,211 @@ __global__ __launch_bounds__(kWave) void k_draw(const void* __restrict__ tgt, co
                 run += mv[v];
                 if (pick < 0 && mv[v] > 0.0 && run > target) pick = static_cast<int32_t>(j0 + v);
             }
-            *out = pick >= 0 ? pick : mylast;
+            cst(out, pick >= 0 ? pick : mylast);
         }
     } else {  // rounding: the last element with mass in the subsegment
         const uint64_t mass = __ballot(mylast >= 0);
         const int l = mass ? 63 - __clzll(static_cast<unsigned long long>(mass)) : 0;
         const int32_t pick = __shfl(mylast, l, kWave);
-        if (lane == 0) *out = pick;
+        if (lane == 0) cst(out, pick);
     }
 }
 
 // --------------------------------------------------------------------------
-// Row statistics output for spec_row_stats: one wavefront per row.
+// Group finishers and the residual block
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_merge_rows(Geom g, StatsArgs sa, float* __restrict__ row_max,
-                                                       double* __restrict__ row_sumexp) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
-    if (r >= g.rows) return;
-    const RowStat o = fold_row_wave<false>(g, sa, r, threadIdx.x & (kWave - 1));
-    if ((threadIdx.x & (kWave - 1)) == 0) {
-        row_max[r] = o.m;
-        row_sumexp[r] = usable(o.m, o.s) ? o.s : NAN;
+// Waits until every statistics block of group g has counted in; false if the
+// bounded wait ran out (then the sticky error word is set).
+__device__ inline bool wait_published(const Params& P, uint32_t g) {
+    const uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
+    const uint32_t want = static_cast<uint32_t>(P.sb);
+    if (cld(cnt) == want) return true;
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+        __builtin_amdgcn_s_sleep(kSleep);
+        if (cld(cnt) == want) return true;
+        if (wall_clock64() - t0 > kWaitTicks) {
+            cst(P.err, 1u);
+            return false;
+        }
+    }
+}
+
+// T == 0: the group's last statistics block folds the argmax partials of the
+// gamma+1 target rows and runs the greedy accept step (one wavefront).
+__device__ inline void finish_greedy(const Params& P, uint32_t g, int lane, char* dyn) {
+    __shared__ RowStat rsg[SPEC_MAX_GAMMA + 1];
+    const int32_t x = lane < P.gamma ? P.tokens[static_cast<int64_t>(g) * P.gamma + lane] : 0;
+    merge_group<true, kWave>(P, g, dyn, rsg);
+    (void)accept_wave<true>(P, g, rsg, x, 0.0f, 0.0f, true);
+}
+
+// Row statistics: the row's last statistics block folds its partials (one wavefront).
+__device__ inline void finish_rows(const Params& P, uint32_t g, int lane) {
+    const RowStat o = fold_row_wave(P, static_cast<int64_t>(g) * P.maxp, lane);
+    if (lane == 0) {
+        P.rows_max[g] = o.m;
+        P.rows_sumexp[g] = usable(o.m, o.s) ? o.s : NAN;
+    }
+}
+
+// T > 0: one residual block of group g (idx in [0, rb)). Once every
+// statistics block of g has counted in, the block folds g's partials and
+// repeats the accept step (block 0 writes the results); then wavefront w takes
+// subsegments idx*4 + w + t*rb*4, t < subs_per_wave(), loading all of them
+// before summing. The group's last residual block draws the token and resets
+// the group's counters for the next call.
+template <int DT, bool VEC>
+__device__ inline void resid_block(const Params& P, uint32_t g, uint32_t idx, char* dyn) {
+    __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
+    __shared__ SeqInfo shi;
+    __shared__ int s_ok;
+    __shared__ uint32_t s_last;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(threadIdx.x / kWave);
+    const int32_t gamma = P.gamma;
+    // the draft tokens and their two logits do not depend on the statistics:
+    // they are loaded before the wait
+    int32_t x = 0;
+    float lt = 0.0f, ld = 0.0f;
+    if (w == 0 && lane < gamma) {
+        x = P.tokens[static_cast<int64_t>(g) * gamma + lane];
+        if (x >= 0 && x < P.V) {
+            lt = load_one<DT>(group_row<DT, kSample>(P, g, static_cast<uint32_t>(lane)), x);
+            ld = load_one<DT>(group_row<DT, kSample>(P, g, static_cast<uint32_t>(gamma + 1 + lane)), x);
+        }
+    }
+    if (threadIdx.x == 0) s_ok = wait_published(P, g) ? 1 : 0;
+    __syncthreads();
+    after_complete();
+    SeqInfo in;
+    in.k = -1;
+    if (s_ok) {
+        merge_group<false, kBlock>(P, g, dyn, rs);
+        if (w == 0) {
+            const SeqInfo si = accept_wave<false>(P, g, rs, x, lt, ld, idx == 0);
+            if (lane == 0) shi = si;
+        }
+        __syncthreads();
+        in = shi;
+    } else if (idx == 0 && w == 0) {
+        // the wait ran out (not expected): the sequence is reported invalid
+        if (lane <= gamma) cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, -1);
+        if (lane == 0) cst(P.out_n + g, -1);
+    }
+    if (in.k >= 0) {
+        constexpr int NS = subs_per_wave<DT, VEC>();
+        const float c32 = P.c32;
+        const ResidRow rr = resid_row<DT>(P, in, g);
+        const bool has_q = rr.qrow != nullptr;
+        const int32_t stride = P.rb * kWavesPerBlock;
+        const int32_t i0 = static_cast<int32_t>(idx) * kWavesPerBlock + w;
+        // sums of one lane's 16 elements (t units): residual in fp64, p in fp32
+        auto lane_sums = [&](const float* xp, const float* xq, int n, double& tr, float& tpf) {
+            for (int v = 0; v < n; ++v) {
+                const float ep = t_of_p(xp[v], rr, c32);
+                tpf += ep;
+                tr += resid_t(static_cast<double>(ep), xq[v], has_q, c32, rr);
+            }
+        };
+        auto flush = [&](int32_t i, double tr, float tpf) {
+            tr = wave_sum(tr);
+            const double tp = wave_sum(static_cast<double>(tpf));
+            if (lane == 0) {
+                cst(P.sub_r + static_cast<int64_t>(g) * P.nsub + i, tr);
+                cst(P.sub_p + static_cast<int64_t>(g) * P.nsub + i, tp);
+            }
+        };
+        if constexpr (VEC) {
+            using SR = SubRaw<DT>;
+            SR raw[NS];
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                const int32_t i = i0 + t * stride;
+                if (i < P.nsub) raw[t].load(rr, has_q, static_cast<int64_t>(i) * kSub + 16 * lane, P.V);
+            }
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                const int32_t i = i0 + t * stride;
+                if (i >= P.nsub) break;
+                double tr = 0.0;
+                float tpf = 0.0f;
+#pragma unroll
+                for (int u = 0; u < SR::NV; ++u) {
+                    float xp[SR::EPL], xq[SR::EPL];
+                    Chunk<DT, true>::expand(raw[t].p[u], xp);
+                    Chunk<DT, true>::expand(raw[t].q[u], xq);
+                    lane_sums(xp, xq, SR::EPL, tr, tpf);
+                }
+                flush(i, tr, tpf);
+            }
+        } else {
+            for (int32_t i = i0; i < P.nsub; i += stride) {
+                float xp[16], xq[16];
+                load_sub<DT, false>(rr, has_q, static_cast<int64_t>(i) * kSub + 16 * lane, P.V, xp, xq);
+                double tr = 0.0;
+                float tpf = 0.0f;
+                lane_sums(xp, xq, 16, tr, tpf);
+                flush(i, tr, tpf);
+            }
+        }
+    }
+    // block arrival: every wavefront's stores have completed before thread 0 counts the block in
+    complete_before();
+    __syncthreads();
+    uint32_t* cnt_r = P.cnt_r + static_cast<int64_t>(g) * kSyncStride;
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(cnt_r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u ==
+                 static_cast<uint32_t>(P.rb);
+    __syncthreads();
+    if (!s_last || w != 0) return;
+    after_complete();
+    if (lane == 0) {  // every statistics and residual block of g has counted in
+        cst(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 0u);
+        cst(cnt_r, 0u);
+    }
+    if (in.k >= 0) draw<DT, VEC>(P, g, in, lane);
+}
+
+// --------------------------------------------------------------------------
+// The kernel: one launch per call.
+// --------------------------------------------------------------------------
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kBlock) void k_verify(Params P) {
+    extern __shared__ __align__(16) char dyn[];
+    int kind;
+    uint32_t g, idx;
+    decode_block(P, blockIdx.x, kind, g, idx);
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    if (kind == kStatsBlock) {
+        __shared__ BlockPieces bp;
+        const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+        const int nwb = min(kWavesPerBlock, P.nw - static_cast<int>(idx) * kWavesPerBlock);  // wavefronts with work
+        if (threadIdx.x == 0) bp.done = 0u;
+        __syncthreads();
+        if (w >= nwb) return;
+        const int n = stats_wave<DT, VEC, MODE>(P, g, idx * kWavesPerBlock + w, lane, bp.p[w]);
+        // count this wavefront in at the block; the last one writes the block's pieces
+        if (lane == 0) bp.n[w] = n;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(&bp.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        old = __shfl(old, 0, kWave);
+        if (old + 1u != static_cast<uint32_t>(nwb)) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        write_pieces<MODE>(P, bp, nwb, lane);
+        uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
+        if constexpr (MODE == kSample) {
+            // the residual blocks of g watch this count reach sb
+            complete_before();
+            if (lane == 0) (void)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (!arrive_last(cnt, static_cast<uint32_t>(P.sb), lane)) return;
+            if constexpr (MODE == kGreedy) finish_greedy(P, g, lane, dyn);
+            else finish_rows(P, g, lane);
+        }
+    } else {
+        if constexpr (MODE == kSample) resid_block<DT, VEC>(P, g, idx, dyn);
     }
 }
 
@@ -1223,21 +1518,29 @@ int fail(int code, const std::string& msg) {
     return code;
 }
 
+// Library-owned device memory of one (device, stream). `data` holds the
+// partial slots and residual masses, laid out per call shape. `sync` holds the
+// group counters at fixed addresses (capacity `groups`): it is cleared when
+// allocated and every call leaves its counters at zero again, so calls of any
+// shape can follow one another on it.
 struct Workspace {
-    void* ptr = nullptr;
+    void* data = nullptr;
     size_t bytes = 0;
+    uint32_t* sync = nullptr;
+    int64_t groups = 0;
 };
 
 std::mutex g_mu;
-std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> buffer
+std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> buffers
 std::map<int, int> g_cus;                         // device -> compute units
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    Geom g;
-    int32_t nsub, nblk, spb;
-    size_t off_pm, off_pr, off_ps, off_pi, off_gath, off_info, off_subr, off_subp, bytes;
+    Params p;  // geometry filled; pointers added at launch
+    size_t off_pm, off_pr, off_ps, off_pi, off_subr, off_subp, bytes;
+    int64_t blocks;
+    uint32_t lds;
 };
 
 int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
@@ -1245,46 +1548,48 @@ int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
 // Chunk geometry: vector chunks are 1 KiB; scalar chunks are 64 x 4 elements.
 int32_t chunk_elems(int32_t dtype, bool vec) { return vec ? kWave * (16 / elem_bytes(dtype)) : kWave * 4; }
 
-// Wave ranges of about kChunksPerWave chunks (many more waves than the chip
-// holds at once, which keeps its tail short), but at least 16 wavefronts per
-// compute unit so that small problems still spread over the chip.
-Layout plan(int64_t rows_t, int64_t rows, int32_t V, int32_t dtype, bool vec, int32_t B, int cus) {
+// Statistics wavefronts take about kChunksPerWave chunks (many more wavefronts
+// than the chip holds at once, which keeps its tail short), but the whole
+// problem gets at least 16 wavefronts per compute unit so that small problems
+// still spread over the chip. Residual wavefronts take subs_per_wave()
+// subsegments of row k each.
+Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus) {
     Layout L{};
-    Geom& g = L.g;
-    g.rows_t = rows_t;
-    g.rows = rows;
-    g.V = V;
+    Params& p = L.p;
+    const int32_t rps = mode == kSample ? 2 * gamma + 1 : (mode == kGreedy ? gamma + 1 : 1);
+    p.G = static_cast<int32_t>(G);
+    p.rps = rps;
+    p.gamma = gamma;
+    p.V = V;
     const int32_t CH = chunk_elems(dtype, vec);
-    g.nchunk = (V + CH - 1) / CH;
-    const int64_t total = rows * g.nchunk;
+    p.nchunk = (V + CH - 1) / CH;
+    const int64_t per_group = static_cast<int64_t>(rps) * p.nchunk;
+    const int64_t total = G * per_group;
     const int64_t min_waves = static_cast<int64_t>(cus) * 16;
     int64_t cpw = kChunksPerWave;
     if ((total + cpw - 1) / cpw < min_waves) cpw = (total + min_waves - 1) / min_waves;
+    if (cpw > static_cast<int64_t>(kMaxPieces - 1) * p.nchunk) cpw = static_cast<int64_t>(kMaxPieces - 1) * p.nchunk;
     if (cpw < 1) cpw = 1;
-    g.cpw = cpw;
-    g.nwaves = (total + cpw - 1) / cpw;
-    g.maxp = static_cast<int32_t>((g.nchunk + cpw - 1) / cpw + 1);
-    // residual pass: one wavefront per subsegment, about as many blocks as the
-    // chip holds at once (32 wavefronts per compute unit), split evenly per
-    // sequence
-    constexpr int tail_waves = kTailBlock / kWave;
-    L.nsub = static_cast<int32_t>((static_cast<int64_t>(V) + kSub - 1) / kSub);
-    const int64_t nb = B > 0 ? B : 1;
-    int64_t nblk = (static_cast<int64_t>(cus) * (32 / tail_waves)) / nb;
-    const int64_t max_blk = (L.nsub + tail_waves - 1) / tail_waves;
-    if (nblk > max_blk) nblk = max_blk;
-    if (nblk < 1) nblk = 1;
-    L.spb = static_cast<int32_t>((L.nsub + nblk - 1) / nblk);
-    L.nblk = (L.nsub + L.spb - 1) / L.spb;
-    const size_t slots = static_cast<size_t>(rows) * g.maxp;
-    const size_t subs = static_cast<size_t>(nb) * L.nsub;
+    p.cpw = static_cast<int32_t>(cpw);
+    p.nw = static_cast<int32_t>((per_group + cpw - 1) / cpw);
+    p.sb = (p.nw + kWavesPerBlock - 1) / kWavesPerBlock;
+    p.maxp = static_cast<int32_t>((p.nchunk + cpw - 1) / cpw + 1);
+    p.nsub = static_cast<int32_t>((static_cast<int64_t>(V) + kSub - 1) / kSub);
+    const int spw = vec ? (dtype == SPEC_BF16 ? subs_per_wave<SPEC_BF16, true>() : subs_per_wave<SPEC_F32, true>())
+                        : subs_per_wave<SPEC_F32, false>();
+    p.rb = mode == kSample ? (p.nsub + kWavesPerBlock * spw - 1) / (kWavesPerBlock * spw) : 0;
+    p.lag = p.rb > 0 ? static_cast<int32_t>(G < kLag ? G : kLag) : 0;
+    const int64_t gslots = static_cast<int64_t>(rps) * p.maxp;
+    p.stage = mode != kRows && gslots <= kMaxStage ? static_cast<int32_t>(gslots) : 0;
+    L.blocks = G * (p.sb + p.rb);
+    L.lds = static_cast<uint32_t>(p.stage) * 20u;
+    const size_t slots = static_cast<size_t>(G) * gslots;
+    const size_t subs = mode == kSample ? static_cast<size_t>(G) * p.nsub : 0;
     size_t o = 0;
     L.off_pm = o; o = align_up(o + slots * sizeof(float), 256);
-    L.off_pr = o; o = align_up(o + slots * sizeof(float), 256);
-    L.off_ps = o; o = align_up(o + slots * sizeof(double), 256);
-    L.off_pi = o; o = align_up(o + slots * sizeof(int32_t), 256);
-    L.off_gath = o; o = align_up(o + static_cast<size_t>(rows) * sizeof(float), 256);
-    L.off_info = o; o = align_up(o + static_cast<size_t>(nb) * sizeof(SeqInfo), 256);
+    L.off_pr = o; o = align_up(o + (mode == kGreedy ? 0 : slots) * sizeof(float), 256);
+    L.off_ps = o; o = align_up(o + (mode == kGreedy ? 0 : slots) * sizeof(double), 256);
+    L.off_pi = o; o = align_up(o + (mode == kGreedy ? slots : 0) * sizeof(int32_t), 256);
     L.off_subr = o; o = align_up(o + subs * sizeof(double), 256);
     L.off_subp = o; o = align_up(o + subs * sizeof(double), 256);
     L.bytes = o;
@@ -1300,89 +1605,84 @@ int compute_units(int dev) {
     return n;
 }
 
-// Caller holds g_mu.
-int get_workspace(int dev, hipStream_t stream, size_t bytes, char** out) {
+// Caller holds g_mu. Grows the buffers of (dev, stream) to `bytes` of data and
+// `groups` groups of counters; a new sync buffer is cleared on the stream.
+int get_workspace(int dev, hipStream_t stream, size_t bytes, int64_t groups, Workspace** out) {
     Workspace& ws = g_ws[std::make_pair(dev, static_cast<void*>(stream))];
-    if (ws.bytes < bytes) {
-        if (ws.ptr) {
+    if (ws.bytes < bytes || ws.groups < groups) {
+        if (ws.data || ws.sync)
             if (hipStreamSynchronize(stream) != hipSuccess) return fail(SPEC_EHIP, "hipStreamSynchronize failed");
-            (void)hipFree(ws.ptr);
-            ws = Workspace{};
-        }
+    }
+    if (ws.bytes < bytes) {
+        if (ws.data) (void)hipFree(ws.data);
+        ws.data = nullptr;
+        ws.bytes = 0;
         const size_t want = align_up(bytes + bytes / 4, 1 << 20);
-        if (hipMalloc(&ws.ptr, want) != hipSuccess) {
-            ws = Workspace{};
+        if (hipMalloc(&ws.data, want) != hipSuccess) {
+            ws.data = nullptr;
             (void)hipGetLastError();
             return fail(SPEC_ENOMEM, "hipMalloc of the workspace failed");
         }
         ws.bytes = want;
     }
-    *out = static_cast<char*>(ws.ptr);
+    if (ws.groups < groups) {
+        if (ws.sync) (void)hipFree(ws.sync);
+        ws.sync = nullptr;
+        ws.groups = 0;
+        const int64_t want = static_cast<int64_t>(align_up(static_cast<size_t>(groups + groups / 4), 1024));
+        const size_t sbytes = (2 * static_cast<size_t>(want) * kSyncStride + 64) * sizeof(uint32_t);
+        if (hipMalloc(reinterpret_cast<void**>(&ws.sync), sbytes) != hipSuccess) {
+            ws.sync = nullptr;
+            (void)hipGetLastError();
+            return fail(SPEC_ENOMEM, "hipMalloc of the workspace failed");
+        }
+        if (hipMemsetAsync(ws.sync, 0, sbytes, stream) != hipSuccess) {
+            (void)hipFree(ws.sync);
+            ws.sync = nullptr;
+            return fail(SPEC_EHIP, "hipMemsetAsync of the workspace failed");
+        }
+        ws.groups = want;
+    }
+    *out = &ws;
     return SPEC_OK;
 }
 
-StatsArgs stats_args(const Layout& L, char* ws, float c32) {
-    StatsArgs sa{};
-    sa.c32 = c32;
-    sa.part_m = reinterpret_cast<float*>(ws + L.off_pm);
-    sa.part_r = reinterpret_cast<float*>(ws + L.off_pr);
-    sa.part_s = reinterpret_cast<double*>(ws + L.off_ps);
-    sa.part_i = reinterpret_cast<int32_t*>(ws + L.off_pi);
-    sa.gath = reinterpret_cast<float*>(ws + L.off_gath);
-    return sa;
+void bind_workspace(Layout& L, Workspace& ws) {
+    char* base = static_cast<char*>(ws.data);
+    Params& p = L.p;
+    p.part_m = reinterpret_cast<float*>(base + L.off_pm);
+    p.part_r = reinterpret_cast<float*>(base + L.off_pr);
+    p.part_s = reinterpret_cast<double*>(base + L.off_ps);
+    p.part_i = reinterpret_cast<int32_t*>(base + L.off_pi);
+    p.sub_r = reinterpret_cast<double*>(base + L.off_subr);
+    p.sub_p = reinterpret_cast<double*>(base + L.off_subp);
+    const int64_t words = ws.groups * kSyncStride;
+    p.cnt_s = ws.sync;
+    p.cnt_r = ws.sync + words;
+    p.err = ws.sync + 2 * words;
 }
 
-// Timing events, when asked for, are bound to the kernel dispatches themselves
-// (their start and end timestamps), so they add no packets to the stream.
-struct Events {
-    hipEvent_t stats_start = nullptr, stats_stop = nullptr, last_stop = nullptr;
-};
-
+// Timing events, when given, are bound to the kernel dispatch itself (its
+// start and end timestamps), so they add no packets to the stream.
 template <int DT, bool VEC>
-void launch_stats_t(bool greedy, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
-                    hipStream_t st, const Events& ev) {
-    const dim3 blocks(static_cast<unsigned>((g.nwaves + kWavesPerBlock - 1) / kWavesPerBlock));
-    if (greedy)
-        hipExtLaunchKernelGGL((k_stats<DT, VEC, true, false>), blocks, dim3(kBlock), 0, st, ev.stats_start,
-                              ev.stats_stop, 0, tgt, dft, g, sa);
-    else if (g.tokens)
-        hipExtLaunchKernelGGL((k_stats<DT, VEC, false, true>), blocks, dim3(kBlock), 0, st, ev.stats_start,
-                              ev.stats_stop, 0, tgt, dft, g, sa);
+void launch_t(int mode, const Layout& L, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const dim3 grid(static_cast<unsigned>(L.blocks)), block(kBlock);
+    if (mode == kSample)
+        hipExtLaunchKernelGGL((k_verify<DT, VEC, kSample>), grid, block, L.lds, st, e0, e1, 0, L.p);
+    else if (mode == kGreedy)
+        hipExtLaunchKernelGGL((k_verify<DT, VEC, kGreedy>), grid, block, L.lds, st, e0, e1, 0, L.p);
     else
-        hipExtLaunchKernelGGL((k_stats<DT, VEC, false, false>), blocks, dim3(kBlock), 0, st, ev.stats_start,
-                              ev.stats_stop, 0, tgt, dft, g, sa);
+        hipExtLaunchKernelGGL((k_verify<DT, VEC, kRows>), grid, block, L.lds, st, e0, e1, 0, L.p);
 }
 
-void launch_stats(int32_t dtype, bool vec, bool greedy, const void* tgt, const void* dft, const Geom& g,
-                  const StatsArgs& sa, hipStream_t st, const Events& ev = Events{}) {
+void launch(int32_t dtype, bool vec, int mode, const Layout& L, hipStream_t st, hipEvent_t e0 = nullptr,
+            hipEvent_t e1 = nullptr) {
     if (dtype == SPEC_F32) {
-        if (vec) launch_stats_t<SPEC_F32, true>(greedy, tgt, dft, g, sa, st, ev);
-        else launch_stats_t<SPEC_F32, false>(greedy, tgt, dft, g, sa, st, ev);
+        if (vec) launch_t<SPEC_F32, true>(mode, L, st, e0, e1);
+        else launch_t<SPEC_F32, false>(mode, L, st, e0, e1);
     } else {
-        if (vec) launch_stats_t<SPEC_BF16, true>(greedy, tgt, dft, g, sa, st, ev);
-        else launch_stats_t<SPEC_BF16, false>(greedy, tgt, dft, g, sa, st, ev);
-    }
-}
-
-template <int DT, bool VEC>
-void launch_tail_t(const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa, const AcceptArgs& a,
-                   const DrawArgs& d, hipStream_t st, hipEvent_t stop) {
-    const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.nblk);
-    hipExtLaunchKernelGGL((k_accept_resid<DT, VEC>), dim3(blocks), dim3(kTailBlock), a.stage * 20u, st, nullptr,
-                          nullptr, 0, tgt, dft, g, sa, a);
-    hipExtLaunchKernelGGL((k_draw<DT, VEC>), dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0, st, nullptr, stop, 0,
-                          tgt, dft, d);
-}
-
-// T > 0: accept + residual masses, then the draw.
-void launch_tail(int32_t dtype, bool vec, const void* tgt, const void* dft, const Geom& g, const StatsArgs& sa,
-                 const AcceptArgs& a, const DrawArgs& d, hipStream_t st, hipEvent_t stop) {
-    if (dtype == SPEC_F32) {
-        if (vec) launch_tail_t<SPEC_F32, true>(tgt, dft, g, sa, a, d, st, stop);
-        else launch_tail_t<SPEC_F32, false>(tgt, dft, g, sa, a, d, st, stop);
-    } else {
-        if (vec) launch_tail_t<SPEC_BF16, true>(tgt, dft, g, sa, a, d, st, stop);
-        else launch_tail_t<SPEC_BF16, false>(tgt, dft, g, sa, a, d, st, stop);
+        if (vec) launch_t<SPEC_BF16, true>(mode, L, st, e0, e1);
+        else launch_t<SPEC_BF16, false>(mode, L, st, e0, e1);
     }
 }
 
@@ -1396,7 +1696,14 @@ int check_launch(const char* what) {
     return SPEC_OK;
 }
 
-constexpr int64_t kMaxChunks = int64_t(1) << 31;
+// Size limits: chunk counts are 32-bit on the device, and a dispatch holds
+// fewer than 2^32 work-items.
+int check_size(const Layout& L) {
+    const int64_t chunks = static_cast<int64_t>(L.p.G) * L.p.rps * L.p.nchunk;
+    if (chunks >= (int64_t(1) << 31) || L.blocks * kBlock >= (int64_t(1) << 32) || L.blocks < 1)
+        return fail(SPEC_EINVAL, "problem too large");
+    return SPEC_OK;
+}
 
 }  // namespace
 
@@ -1414,12 +1721,10 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t 
         return 0;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const bool greedy = temperature == 0.0f;
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0;
-    const int64_t rows_t = static_cast<int64_t>(B) * (gamma + 1);
-    const int64_t rows = greedy ? rows_t : rows_t + static_cast<int64_t>(B) * gamma;
     std::lock_guard<std::mutex> lk(g_mu);
-    return plan(rows_t, rows, V, dtype, vec, B, compute_units(dev)).bytes;
+    const Layout L = plan(temperature == 0.0f ? kGreedy : kSample, B, gamma, V, dtype, vec, compute_units(dev));
+    return L.bytes + (2 * static_cast<size_t>(B) * kSyncStride + 64) * sizeof(uint32_t);
 }
 
 void spec_verify_release_workspace(void) {
@@ -1427,10 +1732,11 @@ void spec_verify_release_workspace(void) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     for (auto& kv : g_ws) {
-        if (!kv.second.ptr) continue;
+        if (!kv.second.data && !kv.second.sync) continue;
         (void)hipSetDevice(kv.first.first);
         (void)hipStreamSynchronize(static_cast<hipStream_t>(kv.first.second));
-        (void)hipFree(kv.second.ptr);
+        if (kv.second.data) (void)hipFree(kv.second.data);
+        if (kv.second.sync) (void)hipFree(kv.second.sync);
     }
     g_ws.clear();
     (void)hipSetDevice(cur);
@@ -1452,78 +1758,41 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     const float c32 = greedy ? 0.0f : fold_temperature(temperature);
     if (!greedy && !(std::isfinite(c32) && c32 > 0.0f))
         return fail(SPEC_EINVAL, "temperature too small or too large for fp32 exponent scaling");
-    const int64_t es = elem_bytes(dtype);
-    const int64_t rows_t = static_cast<int64_t>(B) * (gamma + 1);
-    const int64_t rows = greedy ? rows_t : rows_t + static_cast<int64_t>(B) * gamma;
-    if (rows * ((V + 255) / 256) >= kMaxChunks) return fail(SPEC_EINVAL, "problem too large");
-    const bool vec = (static_cast<int64_t>(V) * es) % 16 == 0 && aligned16(target_logits) &&
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
                      (greedy || aligned16(draft_logits));
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
+    const int mode = greedy ? kGreedy : kSample;
 
     std::lock_guard<std::mutex> lk(g_mu);
-    Layout L = plan(rows_t, rows, V, dtype, vec, B, compute_units(dev));
-    L.g.gamma = gamma;
-    L.g.tokens = draft_tokens;
-    char* ws = nullptr;
-    if (int rc = get_workspace(dev, st, L.bytes, &ws)) return rc;
-    const StatsArgs sa = stats_args(L, ws, c32);
-    SeqInfo* info = reinterpret_cast<SeqInfo*>(ws + L.off_info);
-
-    AcceptArgs a{};
-    a.tokens = draft_tokens;
-    a.gath = sa.gath;
-    a.B = B; a.gamma = gamma; a.V = V;
-    a.nsub = L.nsub; a.nblk = L.nblk; a.spb = L.spb;
-    const int seq_slots = (greedy ? gamma + 1 : 2 * gamma + 1) * L.g.maxp;
-    a.stage = seq_slots <= kMaxStage ? seq_slots : 0;
-    const uint32_t lds = static_cast<uint32_t>(a.stage) * 20u;
-    a.c32 = c32;
-    a.seed = seed;
-    a.b_offset = extras ? extras->b_offset : 0;
-    a.out_tokens = out_tokens;
-    a.out_n = out_n_accepted;
-    a.info = info;
-    a.sub_r = reinterpret_cast<double*>(ws + L.off_subr);
-    a.sub_p = reinterpret_cast<double*>(ws + L.off_subp);
+    Layout L = plan(mode, B, gamma, V, dtype, vec, compute_units(dev));
+    if (int rc = check_size(L)) return rc;
+    Workspace* ws = nullptr;
+    if (int rc = get_workspace(dev, st, L.bytes, L.p.G, &ws)) return rc;
+    bind_workspace(L, *ws);
+    Params& p = L.p;
+    p.c32 = c32;
+    p.seed = seed;
+    p.b_offset = extras ? extras->b_offset : 0;
+    p.tgt = target_logits;
+    p.dft = greedy ? nullptr : draft_logits;
+    p.tokens = draft_tokens;
+    p.out_tokens = out_tokens;
+    p.out_n = out_n_accepted;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
     if (extras) {
-        a.dbg_row_max = extras->row_max;
-        a.dbg_row_sumexp = extras->row_sumexp;
-        a.dbg_p = extras->p_draft;
-        a.dbg_q = extras->q_draft;
-        a.dbg_argmax = extras->argmax;
+        p.dbg_row_max = extras->row_max;
+        p.dbg_row_sumexp = extras->row_sumexp;
+        p.dbg_p = extras->p_draft;
+        p.dbg_q = extras->q_draft;
+        p.dbg_z = extras->Z;
+        p.dbg_argmax = extras->argmax;
+        e0 = static_cast<hipEvent_t>(extras->events[0]);
+        e1 = static_cast<hipEvent_t>(extras->events[1]);
     }
-    Events ev;
-    if (extras) {
-        ev.stats_start = static_cast<hipEvent_t>(extras->events[0]);
-        ev.stats_stop = static_cast<hipEvent_t>(extras->events[1]);
-        ev.last_stop = static_cast<hipEvent_t>(extras->events[2]);
-    }
-
-    launch_stats(dtype, vec, greedy, target_logits, draft_logits, L.g, sa, st, ev);
-    if (int rc = check_launch("statistics kernel")) return rc;
-    if (greedy) {
-        hipExtLaunchKernelGGL(k_accept_greedy, dim3(static_cast<unsigned>(B)), dim3(kBlock), lds, st, nullptr,
-                              ev.last_stop, 0, L.g, sa, a);
-        if (int rc = check_launch("accept kernel")) return rc;
-    } else {
-        DrawArgs d{};
-        d.gamma = gamma;
-        d.V = V;
-        d.nsub = L.nsub;
-        d.c32 = c32;
-        d.seed = seed;
-        d.b_offset = a.b_offset;
-        d.info = info;
-        d.sub_r = a.sub_r;
-        d.sub_p = a.sub_p;
-        d.out_tokens = out_tokens;
-        d.dbg_z = extras ? extras->Z : nullptr;
-        launch_tail(dtype, vec, target_logits, draft_logits, L.g, sa, a, d, st, ev.last_stop);
-        if (int rc = check_launch("accept/residual and draw kernels")) return rc;
-    }
-    return SPEC_OK;
+    launch(dtype, vec, mode, L, st, e0, e1);
+    return check_launch("verification kernel");
 }
 
 int spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -1537,25 +1806,27 @@ int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype, f
                    float* row_max, double* row_sumexp, void* stream) {
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EDTYPE, "dtype must be SPEC_F32 or SPEC_BF16");
     if (rows < 1 || V < 1) return fail(SPEC_EINVAL, "rows and V must be >= 1");
+    if (rows >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
     if (!(temperature > 0.0f)) return fail(SPEC_EINVAL, "temperature must be > 0");
     if (!logits || !row_max || !row_sumexp) return fail(SPEC_EINVAL, "null pointer argument");
     const float c32 = fold_temperature(temperature);
     if (!(std::isfinite(c32) && c32 > 0.0f)) return fail(SPEC_EINVAL, "temperature out of range");
-    if (rows * ((V + 255) / 256) >= kMaxChunks) return fail(SPEC_EINVAL, "problem too large");
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(logits);
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
-    const Layout L = plan(rows, rows, V, dtype, vec, 0, compute_units(dev));
-    char* ws = nullptr;
-    if (int rc = get_workspace(dev, st, L.bytes, &ws)) return rc;
-    const StatsArgs sa = stats_args(L, ws, c32);
-    launch_stats(dtype, vec, false, logits, nullptr, L.g, sa, st);
-    if (int rc = check_launch("statistics kernel")) return rc;
-    const unsigned blocks = static_cast<unsigned>((rows + kWavesPerBlock - 1) / kWavesPerBlock);
-    k_merge_rows<<<blocks, kBlock, 0, st>>>(L.g, sa, row_max, row_sumexp);
-    return check_launch("merge kernel");
+    Layout L = plan(kRows, rows, 1, V, dtype, vec, compute_units(dev));
+    if (int rc = check_size(L)) return rc;
+    Workspace* ws = nullptr;
+    if (int rc = get_workspace(dev, st, L.bytes, L.p.G, &ws)) return rc;
+    bind_workspace(L, *ws);
+    L.p.c32 = c32;
+    L.p.tgt = logits;
+    L.p.rows_max = row_max;
+    L.p.rows_sumexp = row_sumexp;
+    launch(dtype, vec, kRows, L, st);
+    return check_launch("statistics kernel");
 }
 
 }  // extern "C"
