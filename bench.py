@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE, choices=list(W.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
-    ap.add_argument("--event-stride", type=int, default=8,
+    ap.add_argument("--event-stride", type=int, default=16,
                     help="time the kernels of every N-th step of the timed region with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the oracle sample (0: auto)")

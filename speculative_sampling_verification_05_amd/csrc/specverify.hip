@@ -65,13 +65,16 @@ namespace {
 #define SPECVERIFY_STATS_UNROLL 4
 #endif
 #ifndef SPECVERIFY_CHUNKS_PER_WAVE
-#define SPECVERIFY_CHUNKS_PER_WAVE 32
+#define SPECVERIFY_CHUNKS_PER_WAVE 16
 #endif
 #ifndef SPECVERIFY_LAG
 #define SPECVERIFY_LAG 1024
 #endif
+#ifndef SPECVERIFY_BF16_SUBS
+#define SPECVERIFY_BF16_SUBS 2
+#endif
 #ifndef SPECVERIFY_SLEEP
-#define SPECVERIFY_SLEEP 8
+#define SPECVERIFY_SLEEP 2
 #endif
 #ifndef SPECVERIFY_SYNC_STRIDE
 #define SPECVERIFY_SYNC_STRIDE 64
@@ -352,7 +355,6 @@ struct Params {
     double* part_s;       // sum of 2^(x*c - reference) (T > 0)
     int32_t* part_i;      // first index of the maximum (T == 0)
     double* sub_r;        // [G, nsub] residual mass per subsegment (t units)
-    double* sub_p;        // [G, nsub] mass of p per subsegment (t units)
     uint32_t* cnt_s;      // [G] statistics blocks counted in
     uint32_t* cnt_r;      // [G] residual blocks counted in (T > 0)
     uint32_t* err;        // sticky: a residual block's wait ran out
@@ -1052,15 +1054,16 @@ __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat
 // Residual in t units. With e_j = 2^(fl(x_j*c - mc)) for the target (p) and
 // draft (q) rows, p_j = e_pj * scale_p and q_j = e_qj * scale_q (scale =
 // 2^(mc - m*c)/S). Then max(0, p_j - q_j) = scale_p * t_j with
-// t_j = max(0, e_pj - rho*e_qj), rho = scale_q/scale_p (one fp64 FMA). The
-// inverse-CDF draw is invariant to the common factor; at the bonus row
-// t_j = e_pj.
+// t_j = max(0, e_pj - rho*e_qj), rho = scale_q/scale_p. t_j is formed in fp32
+// with rho split into an fp32 pair (hi + lo, two FMAs), so the product keeps
+// about 48 bits; the sums over elements are fp64. The inverse-CDF draw is
+// invariant to the common factor; at the bonus row t_j = e_pj.
 // --------------------------------------------------------------------------
 struct ResidRow {
     const char* prow;
     const char* qrow;  // nullptr at the bonus row
     float mcp, mcq;
-    double rho;
+    float rhi, rlo;    // rho = rhi + rlo
 };
 
 template <int DT>
@@ -1070,28 +1073,28 @@ __device__ inline ResidRow resid_row(const Params& P, const SeqInfo& s, uint32_t
     rr.qrow = s.has_q ? group_row<DT, kSample>(P, g, static_cast<uint32_t>(P.gamma + 1 + s.k)) : nullptr;
     rr.mcp = s.mcp;
     rr.mcq = s.mcq;
-    rr.rho = s.rho;
+    rr.rhi = static_cast<float>(s.rho);
+    rr.rlo = static_cast<float>(s.rho - static_cast<double>(rr.rhi));
     return rr;
 }
 
-__device__ inline float t_of_p(float xp, const ResidRow& rr, float c32) {
-    return __builtin_amdgcn_exp2f(fmaf(xp, c32, -rr.mcp));
-}
-
-__device__ inline double resid_t(double ep, float xq, bool has_q, float c32, const ResidRow& rr) {
+// One element's residual mass in t units (its p mass when !has_q). Masked
+// elements carry -inf logits on both rows and give 0.
+__device__ inline float resid_t(float xp, float xq, bool has_q, float c32, const ResidRow& rr) {
+    const float ep = __builtin_amdgcn_exp2f(fmaf(xp, c32, -rr.mcp));
     if (!has_q) return ep;
-    const double eq = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xq, c32, -rr.mcq)));
-    return fmax(0.0, fma(-eq, rr.rho, ep));
+    const float eq = __builtin_amdgcn_exp2f(fmaf(xq, c32, -rr.mcq));
+    return fmaxf(0.0f, fmaf(-eq, rr.rlo, fmaf(-eq, rr.rhi, ep)));
 }
 
 // Residual subsegments one wavefront keeps in flight: 64 VGPRs of raw 16-byte
 // loads (vector path), one subsegment on the scalar path.
 template <int DT, bool VEC>
-__host__ __device__ constexpr int subs_per_wave() { return VEC ? (DT == SPEC_BF16 ? 4 : 2) : 1; }
+__host__ __device__ constexpr int subs_per_wave() { return VEC ? (DT == SPEC_BF16 ? SPECVERIFY_BF16_SUBS : 2) : 1; }
 
 // Raw loads of one lane's 16 elements of a subsegment (vector path): each
 // 16-byte load is taken only if it starts below V, which puts it wholly inside
-// the row (V % EPL == 0 there); the rest read as -inf in p (no mass) and 0 in q.
+// the row (V % EPL == 0 there); the rest read as -inf (no mass).
 template <int DT>
 struct SubRaw {
     static constexpr int EPL = 16 / ElemBytes<DT>::value;
@@ -1106,7 +1109,7 @@ struct SubRaw {
             p[u] = in ? *reinterpret_cast<const uint4*>(rr.prow + j * ElemBytes<DT>::value)
                       : make_uint4(ninf, ninf, ninf, ninf);
             q[u] = in && has_q ? *reinterpret_cast<const uint4*>(rr.qrow + j * ElemBytes<DT>::value)
-                               : make_uint4(0, 0, 0, 0);
+                               : make_uint4(ninf, ninf, ninf, ninf);
         }
     }
 };
@@ -1114,7 +1117,7 @@ struct SubRaw {
 // The 16 elements of lane `lane` in subsegment i: j0 = i*kSub + 16*lane, ...
 // (p row; q row when has_q). Vector path: 16-byte loads, each taken only if it
 // starts below V, which puts it wholly inside the row (V % EPL == 0 there).
-// Elements at or beyond V read as -inf in p (no mass).
+// Elements at or beyond V read as -inf (no mass).
 template <int DT, bool VEC>
 __device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int32_t V, float* xp, float* xq) {
     if constexpr (VEC) {
@@ -1129,7 +1132,7 @@ __device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int3
             wp[u] = in ? *reinterpret_cast<const uint4*>(rr.prow + j * ElemBytes<DT>::value)
                        : make_uint4(ninf, ninf, ninf, ninf);
             wq[u] = in && has_q ? *reinterpret_cast<const uint4*>(rr.qrow + j * ElemBytes<DT>::value)
-                                : make_uint4(0, 0, 0, 0);
+                                : make_uint4(ninf, ninf, ninf, ninf);
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -1141,7 +1144,7 @@ __device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int3
         for (int v = 0; v < 16; ++v) {
             const bool in = j0 + v < V;
             xp[v] = in ? load_one<DT>(rr.prow, j0 + v) : -INFINITY;
-            xq[v] = in && has_q ? load_one<DT>(rr.qrow, j0 + v) : 0.0f;
+            xq[v] = in && has_q ? load_one<DT>(rr.qrow, j0 + v) : -INFINITY;
         }
     }
 }
@@ -1236,11 +1239,27 @@ __device__ inline int32_t regs_find(const double* v, const double* incl, double 
     return last;
 }
 
+// p masses per subsegment of the target row k, written over the residual
+// masses (only when those are all zero, so nothing is lost): the draw's
+// fallback from p_k, one wavefront, never on the common path.
+template <int DT, bool VEC>
+__device__ inline void p_masses(const Params& P, uint32_t g, const SeqInfo& in, double* sr, int lane) {
+    const ResidRow rr = resid_row<DT>(P, in, g);
+    for (int32_t i = 0; i < P.nsub; ++i) {
+        float xp[16], xq[16];
+        load_sub<DT, VEC>(rr, false, static_cast<int64_t>(i) * kSub + 16 * lane, P.V, xp, xq);
+        double t = 0.0;
+        for (int v = 0; v < 16; ++v) t += static_cast<double>(resid_t(xp[v], xq[v], false, P.c32, rr));
+        t = wave_sum(t);
+        if (lane == 0) cst(sr + i, t);
+    }
+    complete_before();
+}
+
 template <int DT, bool VEC>
 __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int lane) {
     const int32_t nsub = P.nsub;
-    const double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
-    const double* sp = P.sub_p + static_cast<int64_t>(g) * nsub;
+    double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
     const double u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(in.k), 1u);
     double Z, target, before = 0.0;
     int32_t sel;
@@ -1252,8 +1271,9 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
         Z = regs_scan(v, incl, lane);
         from_p = !(Z > 0.0);
         if (from_p) {
+            p_masses<DT, VEC>(P, g, in, sr, lane);
 #pragma unroll
-            for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? cld(sp + t * kWave + lane) : 0.0;
+            for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? cld(sr + t * kWave + lane) : 0.0;
             target = u * regs_scan(v, incl, lane);
         } else {
             target = u * Z;
@@ -1262,9 +1282,9 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
     } else {
         Z = scan_total(sr, nsub, lane);
         from_p = !(Z > 0.0);
-        const double* m = from_p ? sp : sr;
-        target = u * (from_p ? scan_total(sp, nsub, lane) : Z);
-        sel = scan_find(m, nsub, target, lane, before);
+        if (from_p) p_masses<DT, VEC>(P, g, in, sr, lane);
+        target = u * (from_p ? scan_total(sr, nsub, lane) : Z);
+        sel = scan_find(sr, nsub, target, lane, before);
     }
     if (P.dbg_z && lane == 0) P.dbg_z[g] = Z * in.scale_p;
     int32_t* out = P.out_tokens + static_cast<int64_t>(g) * (P.gamma + 1) + in.k;
@@ -1282,7 +1302,7 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
     int32_t mylast = -1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        mv[v] = resid_t(static_cast<double>(t_of_p(xp[v], rr, P.c32)), xq[v], has_q, P.c32, rr);
+        mv[v] = static_cast<double>(resid_t(xp[v], xq[v], has_q, P.c32, rr));
         local += mv[v];
         if (mv[v] > 0.0) mylast = static_cast<int32_t>(j0 + v);
     }
@@ -1399,21 +1419,14 @@ __device__ inline void resid_block(const Params& P, uint32_t g, uint32_t idx, ch
         const bool has_q = rr.qrow != nullptr;
         const int32_t stride = P.rb * kWavesPerBlock;
         const int32_t i0 = static_cast<int32_t>(idx) * kWavesPerBlock + w;
-        // sums of one lane's 16 elements (t units): residual in fp64, p in fp32
-        auto lane_sums = [&](const float* xp, const float* xq, int n, double& tr, float& tpf) {
-            for (int v = 0; v < n; ++v) {
-                const float ep = t_of_p(xp[v], rr, c32);
-                tpf += ep;
-                tr += resid_t(static_cast<double>(ep), xq[v], has_q, c32, rr);
-            }
+        // a lane's 16 elements summed in fp64, in element order (the draw
+        // recomputes one subsegment the same way)
+        auto lane_sums = [&](const float* xp, const float* xq, int n, double& tr) {
+            for (int v = 0; v < n; ++v) tr += static_cast<double>(resid_t(xp[v], xq[v], has_q, c32, rr));
         };
-        auto flush = [&](int32_t i, double tr, float tpf) {
+        auto flush = [&](int32_t i, double tr) {
             tr = wave_sum(tr);
-            const double tp = wave_sum(static_cast<double>(tpf));
-            if (lane == 0) {
-                cst(P.sub_r + static_cast<int64_t>(g) * P.nsub + i, tr);
-                cst(P.sub_p + static_cast<int64_t>(g) * P.nsub + i, tp);
-            }
+            if (lane == 0) cst(P.sub_r + static_cast<int64_t>(g) * P.nsub + i, tr);
         };
         if constexpr (VEC) {
             using SR = SubRaw<DT>;
@@ -1428,24 +1441,22 @@ __device__ inline void resid_block(const Params& P, uint32_t g, uint32_t idx, ch
                 const int32_t i = i0 + t * stride;
                 if (i >= P.nsub) break;
                 double tr = 0.0;
-                float tpf = 0.0f;
 #pragma unroll
                 for (int u = 0; u < SR::NV; ++u) {
                     float xp[SR::EPL], xq[SR::EPL];
                     Chunk<DT, true>::expand(raw[t].p[u], xp);
                     Chunk<DT, true>::expand(raw[t].q[u], xq);
-                    lane_sums(xp, xq, SR::EPL, tr, tpf);
+                    lane_sums(xp, xq, SR::EPL, tr);
                 }
-                flush(i, tr, tpf);
+                flush(i, tr);
             }
         } else {
             for (int32_t i = i0; i < P.nsub; i += stride) {
                 float xp[16], xq[16];
                 load_sub<DT, false>(rr, has_q, static_cast<int64_t>(i) * kSub + 16 * lane, P.V, xp, xq);
                 double tr = 0.0;
-                float tpf = 0.0f;
-                lane_sums(xp, xq, 16, tr, tpf);
-                flush(i, tr, tpf);
+                lane_sums(xp, xq, 16, tr);
+                flush(i, tr);
             }
         }
     }
@@ -1538,7 +1549,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
     Params p;  // geometry filled; pointers added at launch
-    size_t off_pm, off_pr, off_ps, off_pi, off_subr, off_subp, bytes;
+    size_t off_pm, off_pr, off_ps, off_pi, off_subr, bytes;
     int64_t blocks;
     uint32_t lds;
 };
@@ -1591,7 +1602,6 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
     L.off_ps = o; o = align_up(o + (mode == kGreedy ? 0 : slots) * sizeof(double), 256);
     L.off_pi = o; o = align_up(o + (mode == kGreedy ? slots : 0) * sizeof(int32_t), 256);
     L.off_subr = o; o = align_up(o + subs * sizeof(double), 256);
-    L.off_subp = o; o = align_up(o + subs * sizeof(double), 256);
     L.bytes = o;
     return L;
 }
@@ -1655,7 +1665,6 @@ void bind_workspace(Layout& L, Workspace& ws) {
     p.part_s = reinterpret_cast<double*>(base + L.off_ps);
     p.part_i = reinterpret_cast<int32_t*>(base + L.off_pi);
     p.sub_r = reinterpret_cast<double*>(base + L.off_subr);
-    p.sub_p = reinterpret_cast<double*>(base + L.off_subp);
     const int64_t words = ws.groups * kSyncStride;
     p.cnt_s = ws.sync;
     p.cnt_r = ws.sync + words;
