@@ -247,3 +247,27 @@ def test_row_stats_entry_point(dt):
             continue
         assert m[r] == om
         assert abs(s[r] - oS) <= 1e-5 * oS
+
+
+def test_workspace_reuse_across_shapes_and_modes():
+    """Calls of different shapes and modes, back to back on one stream, share
+    the library's workspace (group counters are left at zero by every call):
+    each still matches the oracle."""
+    cases = [
+        W.small_random_inputs(6, 4, 3000, W.BF16, 0.9, seed=31),
+        W.small_random_inputs(5, 3, 1003, W.F32, 1.0, seed=32),
+        W.small_random_inputs(9, 7, 4096, W.BF16, 0.0, seed=33),
+        W.small_random_inputs(40, 2, 520, W.F32, 1.3, seed=34),
+        W.small_random_inputs(3, 9, 9000, W.BF16, 0.7, seed=35),
+        W.small_random_inputs(6, 4, 3000, W.BF16, 0.9, seed=31),
+    ]
+    for rep in range(2):
+        for n, inp in enumerate(cases):
+            parity(inp, seed=100 * rep + n)
+        rng = np.random.default_rng(rep)
+        logits = W.to_storage(rng.normal(0, 2, (7, 2048)), W.BF16)
+        m, s = sv.row_stats(G.to_device(logits, W.BF16), 0.9)
+        m, s = m.cpu().numpy(), s.cpu().numpy()
+        for r in range(7):
+            ok, _, om, oS = oracle.row_softmax(logits[r], W.BF16, 0.9)
+            assert ok and m[r] == om and abs(s[r] - oS) <= 1e-5 * oS

@@ -93,13 +93,13 @@ class Workload:
         return 4 if self.dtype == F32 else 2
 
     def compulsory_bytes(self) -> int:
-        """(2*gamma+1)*B*V*sizeof(dtype): every target and draft row is read once."""
-        return (2 * self.gamma + 1) * self.B * self.V * self.elem_bytes
+        """Bytes the method must read once: every target and draft row at T > 0,
+        the target rows alone at T == 0 (greedy verification never looks at q)."""
+        rows = self.gamma + 1 if self.T == 0.0 else 2 * self.gamma + 1
+        return rows * self.B * self.V * self.elem_bytes
 
     def bytes_read(self) -> int:
-        """Bytes the statistics pass streams: at T == 0 draft logits are not read."""
-        if self.T == 0.0:
-            return (self.gamma + 1) * self.B * self.V * self.elem_bytes
+        """Bytes the statistics pass streams (the compulsory bytes)."""
         return self.compulsory_bytes()
 
     def scaled(self, **kw) -> "Workload":
