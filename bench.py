@@ -1,16 +1,21 @@
 """Throughput of batched speculative-sampling verification on one MI355X.
 
-One step = one spec_verify call (statistics pass over every target and draft
-row, accept / first-reject, residual or bonus draw) over one batch of the
-bf16 headline workload: B=64 sequences, gamma=8 drafted tokens, V=128256,
-temperature 0.8. Inputs are seeded synthetic logits already resident in HBM;
-two input sets alternate so that every step reads data the previous step did
-not touch (each set is 279 MB, above the 256 MB last-level cache).
+One step = one spec_verify call (softmax statistics, accept / first-reject,
+residual or bonus draw, with the early stop: rows after a sequence's first
+rejection are not needed) over one batch of the bf16 headline workload:
+B=64 sequences, gamma=8 drafted tokens, V=128256, temperature 0.8. Inputs are
+seeded synthetic logits already resident in HBM; two input sets alternate so
+that every step reads data the previous step did not touch (each set is
+279 MB, above the 256 MB last-level cache).
 
-Prints one JSON line: verified draft rows/s (B*gamma per step), the
-verification kernel's achieved HBM bandwidth (compulsory bytes over its
-duration) against the 8 TB/s peak, and the fp64 CPU oracle timed on the host
-cores on a bounded sample of the same workload.
+Prints one JSON line: verified draft rows/s (B*gamma per step) with the
+library's automatic schedule; the verification kernel's achieved HBM
+bandwidth against the 8 TB/s peak on that schedule's algorithmic bytes (every
+row, (2*gamma+1)*B*V*sizeof, for the group-major and position-major orders;
+for the early stop the rows it needs: target and draft rows up to each
+sequence's stopping position, plus the bonus row after gamma acceptances);
+the same figures for each schedule forced in turn; and the fp64 CPU oracle
+timed on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -192,32 +197,43 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({Wm} steps)", file=sys.stderr, flush=True)
 
-    # timed region: K steps. Every `event_stride`-th step carries two HIP events
-    # bound to its kernel dispatch (start and end of the verification kernel), so
-    # they time the kernel inside the timed region without adding packets to the
-    # stream.
+    def timed(make_extras):
+        """K steps of the call (the timed region, bracketed by stream events);
+        every E-th step carries two HIP events bound to its kernel dispatch
+        (start and end of the verification kernel), which time the kernel
+        inside the timed region without adding packets to the stream."""
+        evd = [i for i in range(K) if i % E == 0]
+        ev = hip.create(2 * len(evd))
+        ex = {}
+        for n, i in enumerate(evd):
+            e = make_extras()
+            e.events[0] = ev[2 * n]
+            e.events[1] = ev[2 * n + 1]
+            ex[i] = e
+        plain = make_extras()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(K):
+            call(Wm + s, ex.get(s, plain))
+        end.record(stream)
+        torch.cuda.synchronize()
+        kms = [hip.ms(ev[2 * n], ev[2 * n + 1]) for n in range(len(evd))]
+        hip.destroy(ev)
+        return start.elapsed_time(end) / K, kms, evd
+
+    def with_schedule(sched):
+        def make():
+            e = sv.Extras()
+            e.schedule = sched
+            return e
+        return make
+
     E = max(1, args.event_stride)
-    evd = [i for i in range(K) if i % E == 0]
-    ev = hip.create(2 * len(evd))
-    extras = {}
-    for n, i in enumerate(evd):
-        e = sv.Extras()
-        e.events[0] = ev[2 * n]
-        e.events[1] = ev[2 * n + 1]
-        extras[i] = e
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(K):
-        call(Wm + s, extras.get(s))
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    k_ms = [hip.ms(ev[2 * n], ev[2 * n + 1]) for n in range(len(evd))]
-    hip.destroy(ev)
-    ms_per_step = total_ms / K
+    ms_per_step, k_ms, evd = timed(with_schedule(sv.SCHEDULE_AUTO))
 
     # the same steps with no events at all (reported beside the timed value)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for s in range(K):
         call(Wm + s)
@@ -225,15 +241,50 @@ def main():
     torch.cuda.synchronize()
     ms_plain = start.elapsed_time(end) / K
 
+    # bytes the early-stopping algorithm needs for each input set (its outputs
+    # are the same on every step: same inputs, same seed)
+    def needed_bytes(n):
+        row = V * (4 if wl.dtype == W.F32 else 2)
+        if wl.T == 0.0:
+            rows = np.where(n < 0, g + 1, np.minimum(n, g) + 1)
+        else:
+            rows = np.where((n < 0) | (n >= g), 2 * g + 1, 2 * (n + 1))
+        return int(rows.sum()) * row
+
+    set_bytes = []
+    for k in range(args.sets):
+        call(k)
+        torch.cuda.synchronize()
+        set_bytes.append(needed_bytes(outs[k][1].cpu().numpy()))
+    compulsory = wl.compulsory_bytes()
+
+    def algo_bytes(sched, steps):
+        """Algorithmic bytes of each listed step: the early stop needs the rows
+        up to each sequence's stopping position, the other schedules read every
+        row (the compulsory bytes)."""
+        if sched == sv.SCHEDULE_EARLY_STOP:
+            return [set_bytes[(Wm + i) % args.sets] for i in steps]
+        return [compulsory for _ in steps]
+
+    auto = sv.auto_schedule(B, g, V, dtc, wl.T)
+    names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position"}
+    k_bytes = algo_bytes(auto, evd)
     rows_per_step = B * g
     value = rows_per_step / (ms_per_step * 1e-3)
-    compulsory = wl.compulsory_bytes()
-    read_bytes = wl.bytes_read()
     k_avg_ms = float(np.mean(k_ms))
-    achieved = read_bytes / (k_avg_ms * 1e-3) / 1e9
-    call_gbps = compulsory / (ms_per_step * 1e-3) / 1e9
+    achieved = float(np.sum(k_bytes)) / (float(np.sum(k_ms)) * 1e-3) / 1e9
 
-    # one validation of the last outputs of set 0 against the oracle (outside the timed region)
+    schedules = {}
+    for sched in ((sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION) if wl.T == 0.0 else
+                  (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION)):
+        ms_s, km_s, ev_s = timed(with_schedule(sched))
+        a_s = float(np.sum(algo_bytes(sched, ev_s))) / (float(np.sum(km_s)) * 1e-3) / 1e9
+        schedules[names[sched]] = {"ms_per_step": ms_s, "kernel_us": float(np.mean(km_s)) * 1e3,
+                                   "rows_per_s": rows_per_step / (ms_s * 1e-3), "achieved_GBps": a_s,
+                                   "frac": a_s / PEAK_HBM_GBPS,
+                                   "bytes_per_launch": float(np.mean(algo_bytes(sched, ev_s)))}
+
+    # one validation of the outputs of set 0 against the oracle (outside the timed region)
     call(0)
     torch.cuda.synchronize()
     gpu_t = outs[0][0].cpu().numpy()
@@ -255,17 +306,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "gamma": g, "V": V, "temperature": wl.T,
                    "logits": W.DTYPE_NAMES[wl.dtype], "input_sets": args.sets},
-        "call_gbps": call_gbps,
-        "call_hbm_frac": call_gbps / PEAK_HBM_GBPS,
         "kernel_us": {"k_verify": k_avg_ms * 1e3},
         "ms_per_step_no_events": ms_plain,
         "event_stride": E,
+        "schedule": names[auto],
         "accepted_hist": n_hist,
-        "roofline": {"bound": "hbm", "kernel": "k_verify",
+        "needed_bytes_per_set": set_bytes,
+        "compulsory_bytes": compulsory,
+        "roofline": {"bound": "hbm", "kernel": "k_verify" if auto != sv.SCHEDULE_GROUP else "k_group",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name),
-                     "bytes_per_launch": read_bytes, "avg_launch_us": k_avg_ms * 1e3,
+                     "bytes_per_launch": float(np.mean(k_bytes)), "avg_launch_us": k_avg_ms * 1e3,
                      "launches_timed": len(k_ms)},
+        "schedules": schedules,
     }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or min(B, 64)

@@ -84,13 +84,13 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
  *                 correction (or bonus) token, then -1 padding.
  *  out_n_accepted [B] int32: n in 0..gamma, or -1 (invalid input, see above).
  *  Returns SPEC_OK or a negative spec_status_t (SPEC_EINVAL also when the
- *  problem exceeds the kernel's 32-bit chunk and dispatch counts). The
+ *  problem exceeds the kernel's dispatch size). The
  *  library keeps a device workspace per (device, stream), grown on demand
  *  under a lock; concurrent calls on different streams are safe, calls on one
  *  stream are ordered. One kernel is launched per call. Inside it, blocks
- *  that resample a sequence wait (bounded, about 2 s) for the blocks that
- *  stream the sequence's rows; should that bound ever run out the sequence is
- *  reported as -1 rather than the kernel waiting on. */
+ *  wait (bounded, about 2 s) for other blocks of the same sequence; should
+ *  that bound ever run out the sequence is reported as -1 rather than the
+ *  kernel waiting on. */
 int spec_verify(const void* target_logits, const void* draft_logits,
                 const int32_t* draft_tokens, int32_t B, int32_t gamma, int32_t V,
                 int32_t dtype, float temperature, uint64_t seed,
@@ -114,9 +114,36 @@ typedef struct {
                               the start and end of the call's verification kernel
                               dispatch itself (no extra stream packets); [2] is
                               reserved and ignored */
+    int32_t schedule;      /* a spec_schedule_t (0 = SPEC_SCHEDULE_AUTO), see below */
 } spec_extras_t;
 
-/* spec_verify with extras (NULL extras == spec_verify). Same kernels. */
+/* Grid schedules of the T > 0 kernel (T == 0 always takes the position-major
+ * schedule with the early stop). Outputs do not depend on the schedule.
+ *  SPEC_SCHEDULE_GROUP       group-major: a sequence's 2*gamma+1 rows are
+ *                            streamed together, every row is read; the
+ *                            sequence's residual blocks (at the end of the
+ *                            grid) take the accept step and the draw.
+ *  SPEC_SCHEDULE_EARLY_STOP  position-major: all sequences' position 0, then
+ *                            position 1, ...; each position is decided as soon
+ *                            as its rows are streamed, and a block whose
+ *                            sequence already stopped at an earlier position
+ *                            reads nothing (the early stop of [Ch15] 15.1.2
+ *                            step 3) and helps with that sequence's draw.
+ *  SPEC_SCHEDULE_POSITION    the same order, reading every row.
+ *  SPEC_SCHEDULE_AUTO        EARLY_STOP once one position's blocks fill the
+ *                            chip (B times the blocks of one row pair at least
+ *                            four per compute unit), else GROUP.
+ * Any of row_max, row_sumexp, p_draft, q_draft or argmax turns EARLY_STOP into
+ * POSITION (the per-row values are then defined for every row). */
+typedef enum {
+    SPEC_SCHEDULE_AUTO = 0,
+    SPEC_SCHEDULE_GROUP = 1,
+    SPEC_SCHEDULE_EARLY_STOP = 2,
+    SPEC_SCHEDULE_POSITION = 3
+} spec_schedule_t;
+
+/* spec_verify with extras (NULL extras == spec_verify, SPEC_SCHEDULE_AUTO).
+ * SPEC_EINVAL for a schedule outside spec_schedule_t. */
 int spec_verify_ex(const void* target_logits, const void* draft_logits,
                    const int32_t* draft_tokens, int32_t B, int32_t gamma, int32_t V,
                    int32_t dtype, float temperature, uint64_t seed,
@@ -132,6 +159,10 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits,
 int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype,
                    float temperature, float* row_max, double* row_sumexp, void* stream);
 
+/* The schedule SPEC_SCHEDULE_AUTO takes for this shape on the current device
+ * (SPEC_SCHEDULE_GROUP or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
+int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature);
+
 /* Bytes of device workspace one call of this shape needs (the library
  * allocates and owns it). */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
@@ -143,7 +174,7 @@ void spec_verify_release_workspace(void);
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* spec_verify_last_error(void);
 
-/* ABI version: 1. */
+/* ABI version: 2 (spec_extras_t gained schedule). */
 int32_t spec_verify_abi_version(void);
 
 #ifdef __cplusplus

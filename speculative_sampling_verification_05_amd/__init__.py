@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EHIP, SPEC_ENOMEM = 0, -1, -2, -3, -4
 SPEC_F32, SPEC_BF16 = 0, 1
+SCHEDULE_AUTO, SCHEDULE_GROUP, SCHEDULE_EARLY_STOP, SCHEDULE_POSITION = 0, 1, 2, 3
 MAX_GAMMA = 63
 
 # every symbol include/specverify.h declares
@@ -22,6 +23,7 @@ EXPORTS = (
     "spec_verify",
     "spec_verify_ex",
     "spec_row_stats",
+    "spec_verify_schedule",
     "spec_verify_workspace_bytes",
     "spec_verify_release_workspace",
     "spec_verify_last_error",
@@ -46,6 +48,7 @@ class Extras(ctypes.Structure):
         ("argmax", ctypes.c_void_p),
         ("b_offset", ctypes.c_int64),
         ("events", ctypes.c_void_p * 3),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -68,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     L.spec_verify_ex.restype = ctypes.c_int
     L.spec_row_stats.argtypes = [vp, i64, i32, i32, f32, vp, vp, vp]
     L.spec_row_stats.restype = ctypes.c_int
+    L.spec_verify_schedule.argtypes = [i32, i32, i32, i32, f32]
+    L.spec_verify_schedule.restype = i32
     L.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
     L.spec_verify_workspace_bytes.restype = ctypes.c_size_t
     L.spec_verify_release_workspace.argtypes = []
@@ -176,6 +181,14 @@ def row_stats(logits, temperature: float, stream=None):
     _check(L.spec_row_stats(_ptr(logits), rows, V, _dtype_code(logits), float(temperature),
                             _ptr(m), _ptr(s), _stream_handle(stream)))
     return m, s
+
+
+def auto_schedule(B, gamma, V, dtype, temperature) -> int:
+    """The schedule SCHEDULE_AUTO takes for this shape on the current device."""
+    rc = load_library().spec_verify_schedule(B, gamma, V, dtype, float(temperature))
+    if rc < 0:
+        raise SpecVerifyError(rc, last_error())
+    return rc
 
 
 def workspace_bytes(B, gamma, V, dtype, temperature) -> int:

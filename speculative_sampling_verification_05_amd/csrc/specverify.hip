@@ -4,49 +4,58 @@
 //  [Ch15] "Chapter 15: Decoding acceleration techniques" (zsc.github.io, LLM
 //         edge inference), 15.1.2: step 2 (softmax of every verified row),
 //         step 3 (accept with probability min(1, p/q), stop at the first
-//         rejection), step 4 (resample from max(0, p - q)/Z); 15.1.4 (the
-//         probability gather); 15.4.2 (fused kernels, low-precision inputs
-//         with fp32 accumulation, coalesced loads).
+//         rejection: the early stop), step 4 (resample from max(0, p - q)/Z);
+//         15.1.4 (the probability gather); 15.4.2 (fused kernels, low-precision
+//         inputs with fp32 accumulation, coalesced loads).
 //  [CSDN] devpress.csdn.net speculative-inference post, 2.1: the
 //         speculative_decode() loop (strict u < alpha, residual clamp).
 //  [HSD]  "LLM inference optimisation: hidden-state speculative decoding", 3.3:
 //         the bonus token drawn from the last target row.
 //
-// One kernel launch per call. Its grid holds two kinds of 256-thread blocks,
-// laid out group by group (a group is one sequence; for the stand-alone row
-// statistics it is one row):
-//  statistics blocks  stream the group's rows once (all the compulsory bytes).
-//                     Each wavefront owns a contiguous range of 1 KiB chunks of
-//                     the group's concatenated rows, keeps per lane an online
-//                     max and a sum of 2^(x*c - R) (R an integer reference,
-//                     c = log2(e)/T), software-pipelines its 16-byte loads and
-//                     writes one partial per row piece; at T == 0 it tracks the
-//                     argmax (first index of the maximum) instead. Each
-//                     wavefront then counts itself in at its group's counter;
-//                     the last one publishes the group (T > 0) or finishes it
-//                     (T == 0: the greedy accept step; row statistics: the
-//                     row's max and sum).
-//  residual blocks    (T > 0) sit a few groups after their group's statistics
-//                     blocks, so they usually start after it is published. A
-//                     block folds the group's partials, repeats the accept step
-//                     (lane i: alpha in fp64 from the two logits of draft token
-//                     i, its Philox uniform; a ballot finds the first rejection
-//                     k) and its wavefronts sum, in fp64, the residual
-//                     max(0, p - q) of row k (or p of the bonus row) over
-//                     1024-element subsegments. The group's last wavefront to
-//                     finish draws the token: wave scans of the subsegment sums,
-//                     then of the chosen subsegment.
-// A residual block waits only for statistics blocks of lower index, which the
-// in-order dispatch has already started, and its wait is bounded in time.
-// Data crossing blocks moves through device-coherent (agent-scope) atomic loads
-// and stores, which bypass the per-XCD L2 caches, ordered by waiting for their
-// completion; no cache flush or invalidate is issued.
+// One kernel launch per call. Its grid is laid out position by position: a
+// unit is one (position i, sequence b) - at T > 0 the pair (target row i,
+// draft row i) for i < gamma and the bonus row gamma alone, at T == 0 target
+// row i, for the stand-alone row statistics one row - and the units of
+// position 0 come first, then position 1, and so on.
+//  statistics blocks  stream a unit's rows once. Each wavefront owns a
+//                     contiguous range of 1 KiB chunks of the unit's rows,
+//                     keeps per lane an online max and a sum of 2^(x*c - R)
+//                     (R an integer reference, c = log2(e)/T), software-
+//                     pipelines its 16-byte non-temporal loads and writes one
+//                     partial per row piece; at T == 0 it tracks the first
+//                     index of the maximum instead. The unit's last block to
+//                     count in folds the partials and takes the accept step of
+//                     position i (alpha in fp64 from the draft token's two
+//                     logits, the Philox uniform), then reads the decision
+//                     words of the sequence's earlier positions: if they were
+//                     all accepted it publishes its own, and if position i ends
+//                     the sequence (a rejection, an unusable row, or the bonus
+//                     row after gamma acceptances) it writes the outputs and
+//                     the sequence's draw record.
+//  early stop         a wavefront whose sequence is already known to have
+//                     stopped at an earlier position loads nothing, so rows
+//                     after a sequence's first rejection are mostly never read.
+//  residual blocks    (T > 0) close the grid, one set per sequence. Once the
+//                     sequence's draw record is out they load the stopping
+//                     row's target and draft columns into registers, sum the
+//                     residual max(0, p - q) (or p for the bonus row) in fp64,
+//                     exchange block sums, and the block, wavefront, lane and
+//                     element where the cumulative mass crosses u*Z are found
+//                     in ascending index order from the registers.
+// A block waits only for blocks of lower index (earlier positions, or its own
+// sequence's residual blocks, which follow one another), which the in-order
+// dispatch has already started, and every wait is bounded in time. Data
+// crossing blocks moves through device-coherent (agent-scope) atomic loads and
+// stores, which bypass the per-XCD L2 caches, ordered by waiting for their
+// completion; decision words and draw records carry the call's epoch, so
+// nothing of them has to be cleared between calls.
 // Exponentials are fp32 (v_exp_f32 on one FMA); every sum and comparison that
 // decides a token is fp64.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -83,19 +92,30 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kUnroll = SPECVERIFY_STATS_UNROLL;          // chunks per pipelined load group
-constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE; // 1 KiB chunks per statistics wavefront
-constexpr int kLag = SPECVERIFY_LAG;                       // groups between statistics and residual blocks
-constexpr float kRUnset = -1.0e30f;                        // lane reference before the first finite value
-constexpr int kSub = kWave * 16;      // elements per residual subsegment (one wavefront, 16 per lane)
-constexpr int kMaxStage = 1024;       // partial slots of one group staged in LDS (20 bytes each)
-constexpr uint64_t kWaitTicks = 200000000ull;  // bound on a residual block's wait: 2 s at 100 MHz
-constexpr int kSleep = SPECVERIFY_SLEEP;            // s_sleep argument between polls (64 cycles each)
-constexpr int kSyncStride = SPECVERIFY_SYNC_STRIDE; // words between one group's counters and the next's
+constexpr int kUnroll = SPECVERIFY_STATS_UNROLL;           // chunks per pipelined load group
+constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE;  // 1 KiB chunks per statistics wavefront
+constexpr int kLag = SPECVERIFY_LAG;        // group-major: groups between statistics and residual blocks
+constexpr int kSub = kWave * 16;            // group-major: elements per residual subsegment
+constexpr int kMaxStage = 1024;             // group-major: partial slots of one group staged in LDS
+constexpr int kHold = 8;                    // chunks a draw wavefront holds in registers
+constexpr int kPairCw = kHold / 2;          // of each row: target and draft
+constexpr float kRUnset = -1.0e30f;         // reference before the first finite value
+constexpr uint64_t kWaitTicks = 200000000ull;        // bound on any wait: 2 s at 100 MHz
+constexpr int kSleep = SPECVERIFY_SLEEP;             // s_sleep argument between polls (64 cycles each)
+constexpr int kSyncStride = SPECVERIFY_SYNC_STRIDE;  // words between two counters
+constexpr int kRecWords = 32;               // per sequence: draw record (tag + 3 data words), then its two
+                                            // ticket counters, each on a 128-byte line of its own
+constexpr int kClaimWord = 16;              // tickets handed out for the draw's pieces
+constexpr int kPieceWord = 24;              // pieces counted in
 
-enum : int { kAcc = 0, kRej = 1, kBad = 2 };
 enum : int { kSample = 0, kGreedy = 1, kRows = 2 };
 enum : int { kStatsBlock = 0, kResidBlock = 1 };
+// decision word status (low bits; the high 32 bits hold the call's epoch)
+enum : uint32_t { kPending = 0, kAcc = 1, kRej = 2, kBad = 3 };
+// what the decision words of positions < i say about a sequence
+enum : int { kLive = 0, kStopped = 1, kUnknown = 2, kTimedOut = 3 };
+// draw record kinds
+enum : uint32_t { kNoDraw = 0, kDrawResidual = 1, kDrawP = 2 };
 
 // --------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11). Each round maps
@@ -140,8 +160,7 @@ __device__ inline float load_one(const char* row, int64_t j) {
     }
 }
 
-// Logits are streamed exactly once by the statistics pass: 16-byte
-// non-temporal loads.
+// Logits are read once, straight into registers: 16-byte non-temporal loads.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline uint4 load_stream(const char* p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -210,6 +229,15 @@ template <int DT, bool VEC> struct Chunk {
             x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xFFFF0000u);
         }
     }
+    // A chunk past the end of the row: -inf everywhere (no mass, never a maximum).
+    __device__ static inline Raw blank() {
+        if constexpr (VEC) {
+            const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;
+            return make_uint4(ninf, ninf, ninf, ninf);
+        } else {
+            return make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+    }
     __device__ static inline int64_t index_of(int64_t c, int lane, int v) {
         return VEC ? c * CH + lane * EPL + v : c * CH + lane + kWave * v;
     }
@@ -253,12 +281,21 @@ __device__ inline double wave_scan_incl(double v) {
 }
 // Sum over the 64 lanes (all lanes active), returned to every lane.
 __device__ inline double wave_sum(double v) { return lane_f64(wave_scan_incl(v), kWave - 1); }
+// The value of lane l - 1 (0 in lane 0).
+__device__ inline double lane_before(double v) { return dpp_f64<0x138, 0xF>(v); }
 
 // --------------------------------------------------------------------------
 // Device-coherent access. Agent-scope atomic loads and stores bypass the L2
 // cache of the XCD that issues them, so what one block publishes is read
 // unchanged by a block on another XCD.
 // --------------------------------------------------------------------------
+__device__ inline float cld(const float* p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ inline int32_t cld(const int32_t* p) {
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ inline void cst(float* p, float v) {
     __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -274,18 +311,19 @@ __device__ inline void cst(int32_t* p, int32_t v) {
 __device__ inline void cst(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline float cld(const float* p) {
-    return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT));
-}
 __device__ inline double cld(const double* p) {
     return __longlong_as_double(static_cast<long long>(
         __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<double*>(p)), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT)));
 }
-__device__ inline int32_t cld(const int32_t* p) {
-    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+__device__ inline void cst64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ inline uint64_t cld64(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ inline uint32_t cld(const uint32_t* p) {
     return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -301,46 +339,32 @@ __device__ inline void after_complete() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
-// Cross-lane exchange through LDS inside one wavefront.
-__device__ inline void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// Counts the calling wavefront in at a group counter once its coherent stores
-// have completed. Returns true to the last of `total` arrivals, which then sees
-// every earlier arrival's stores through coherent loads, and which resets the
-// counter for the next call (stream order makes the reset visible to it).
-__device__ inline bool arrive_last(uint32_t* cnt, uint32_t total, int lane) {
-    complete_before();
-    uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, kWave);
-    if (old + 1u != total) return false;
-    after_complete();
-    if (lane == 0) cst(cnt, 0u);
-    return true;
-}
-
 // --------------------------------------------------------------------------
 // Launch geometry and arguments
 // --------------------------------------------------------------------------
 struct Params {
-    int32_t G;      // groups: sequences, or rows for the stand-alone statistics
-    int32_t rps;    // rows per group: 2*gamma+1 (T > 0), gamma+1 (T == 0), 1 (row statistics)
+    int32_t B;       // sequences (rows for the stand-alone statistics)
     int32_t gamma;
     int32_t V;
-    int32_t nchunk; // chunks per row
-    int32_t cpw;    // chunks per statistics wavefront
-    int32_t nw;     // statistics wavefronts per group
-    int32_t sb;     // statistics blocks per group
-    int32_t rb;     // residual blocks per group (0 at T == 0)
-    int32_t lag;    // groups between a group's statistics blocks and its residual blocks
-    int32_t maxp;   // partial slots per row (a row spans at most maxp wavefronts)
-    int32_t nsub;   // residual subsegments per row
-    int32_t stage;  // a group's partial slots staged in LDS, or 0 (fold from memory)
-    float c32;      // log2(e)/T
+    int32_t nchunk;  // chunks per row
+    int32_t cpw;     // chunks per statistics wavefront
+    int32_t maxp;    // partial slots per row (a row spans at most maxp wavefronts)
+    int32_t nw2;     // statistics wavefronts of a two-row unit
+    int32_t nb2;     //   and its blocks
+    int32_t nw1;     // statistics wavefronts of a one-row unit
+    int32_t nb1;     //   and its blocks
+    int32_t nbr;     // pieces of a draw, and closing blocks per sequence (T > 0)
+    int32_t cstride; // words between two counters
+    int32_t rps;     // group-major: rows per group (2*gamma+1)
+    int32_t nw;      // group-major: statistics wavefronts per group
+    int32_t sb;      //   statistics blocks per group
+    int32_t rb;      //   residual blocks per group
+    int32_t lag;     //   groups between a group's statistics blocks and its residual blocks
+    int32_t nsub;    //   residual subsegments per row
+    int32_t stage;   //   a group's partial slots staged in LDS, or 0 (fold from memory)
+    int32_t skip;    // early stop: wavefronts of sequences already stopped load nothing
+    uint32_t epoch;  // tag of this call's decision words and draw records (never 0)
+    float c32;       // log2(e)/T
     uint64_t seed;
     int64_t b_offset;
     const void* tgt;
@@ -350,14 +374,19 @@ struct Params {
     int32_t* out_n;
     float* rows_max;      // row statistics outputs
     double* rows_sumexp;
-    float* part_m;        // per partial slot: max of the piece
-    float* part_r;        // integer reference of the piece (T > 0)
-    double* part_s;       // sum of 2^(x*c - reference) (T > 0)
-    int32_t* part_i;      // first index of the maximum (T == 0)
-    double* sub_r;        // [G, nsub] residual mass per subsegment (t units)
-    uint32_t* cnt_s;      // [G] statistics blocks counted in
-    uint32_t* cnt_r;      // [G] residual blocks counted in (T > 0)
-    uint32_t* err;        // sticky: a residual block's wait ran out
+    float* part_m;        // [units][2][maxp] per partial slot: max of the piece
+    float* part_r;        //   integer reference of the piece (T > 0)
+    double* part_s;       //   sum of 2^(x*c - reference) (T > 0)
+    int32_t* part_i;      //   first index of the maximum (T == 0)
+    float* tok_l;         // [units][2] the draft token's target and draft logits (T > 0)
+    double* msum;         // [B][nbr*4] masses of the draw's wavefronts
+    uint32_t* cnt;        // unit counters, `cstride` words apart
+    uint64_t* dec;        // [B][gamma+1] decision words: epoch << 32 | status
+    uint64_t* rec;        // [B][kRecWords] draw records and their ticket counters
+    double* sub_r;        // group-major: [B][nsub] residual mass per subsegment (t units)
+    uint32_t* cnt_s;      // group-major: [B] statistics blocks counted in, kSyncStride words apart
+    uint32_t* cnt_r;      // group-major: [B] residual blocks counted in
+    uint32_t* err;        // sticky: a wait ran out
     float* dbg_row_max;
     double* dbg_row_sumexp;
     double* dbg_p;
@@ -366,14 +395,110 @@ struct Params {
     int32_t* dbg_argmax;
 };
 
-// Grid order: groups [0, lag) contribute their statistics blocks; each group
+// A block's role. Statistics units are numbered i*B + b (position-major; the
+// row index for the stand-alone statistics) and take nb consecutive blocks:
+// nb2 for a target/draft pair (T > 0, i < gamma), nb1 for one row. At T > 0
+// the residual blocks of sequence 0, 1, ... follow, nbr each.
+struct Role {
+    int kind;
+    uint32_t unit;  // statistics unit, or sequence of a residual block
+    int32_t i;      // position (0..gamma)
+    int32_t b;      // sequence, or row
+    int32_t r;      // block within the unit (or the sequence's residual blocks)
+    int32_t rows;   // rows of the unit (1 or 2)
+    int32_t nw;     // wavefronts of the unit
+    int32_t nb;     // blocks of the unit
+};
+template <int MODE>
+__device__ inline Role role_of(const Params& P) {
+    uint32_t x = blockIdx.x;
+    const uint32_t B = static_cast<uint32_t>(P.B);
+    Role o;
+    o.kind = kStatsBlock;
+    if constexpr (MODE == kRows) {
+        const uint32_t nb = static_cast<uint32_t>(P.nb1);
+        o.unit = x / nb;
+        o.r = static_cast<int32_t>(x - o.unit * nb);
+        o.i = 0;
+        o.b = static_cast<int32_t>(o.unit);
+        o.rows = 1;
+        o.nw = P.nw1;
+        o.nb = P.nb1;
+        return o;
+    }
+    const uint32_t G = static_cast<uint32_t>(P.gamma);
+    if constexpr (MODE == kSample) {
+        const uint32_t nb2 = static_cast<uint32_t>(P.nb2), pairs = G * B * nb2;
+        if (x < pairs) {
+            o.unit = x / nb2;
+            o.r = static_cast<int32_t>(x - o.unit * nb2);
+            o.i = static_cast<int32_t>(o.unit / B);
+            o.b = static_cast<int32_t>(o.unit - static_cast<uint32_t>(o.i) * B);
+            o.rows = 2;
+            o.nw = P.nw2;
+            o.nb = P.nb2;
+            return o;
+        }
+        x -= pairs;
+        const uint32_t nb1 = static_cast<uint32_t>(P.nb1), bonus = B * nb1;
+        if (x >= bonus) {
+            x -= bonus;
+            const uint32_t nbr = static_cast<uint32_t>(P.nbr);
+            o.kind = kResidBlock;
+            o.b = static_cast<int32_t>(x / nbr);
+            o.unit = static_cast<uint32_t>(o.b);
+            o.r = static_cast<int32_t>(x - static_cast<uint32_t>(o.b) * nbr);
+            o.i = 0;
+            o.rows = 2;
+            o.nw = 0;
+            o.nb = P.nbr;
+            return o;
+        }
+        const uint32_t bb = x / nb1;
+        o.unit = G * B + bb;
+        o.r = static_cast<int32_t>(x - bb * nb1);
+        o.i = static_cast<int32_t>(G);
+        o.b = static_cast<int32_t>(bb);
+        o.rows = 1;
+        o.nw = P.nw1;
+        o.nb = P.nb1;
+        return o;
+    } else {  // greedy: every unit is one target row
+        const uint32_t nb1 = static_cast<uint32_t>(P.nb1);
+        o.unit = x / nb1;
+        o.r = static_cast<int32_t>(x - o.unit * nb1);
+        o.i = static_cast<int32_t>(o.unit / B);
+        o.b = static_cast<int32_t>(o.unit - static_cast<uint32_t>(o.i) * B);
+        o.rows = 1;
+        o.nw = P.nw1;
+        o.nb = P.nb1;
+        return o;
+    }
+}
+
+// Row j of a unit: the target row i, then (two-row units) the draft row i.
+template <int DT, int MODE>
+__device__ inline const char* unit_row(const Params& P, const Role& U, int32_t j) {
+    if constexpr (MODE == kRows) {
+        return row_at<DT>(P.tgt, static_cast<int64_t>(U.b) * P.V);
+    } else {
+        if (j == 0) return row_at<DT>(P.tgt, (static_cast<int64_t>(U.b) * (P.gamma + 1) + U.i) * P.V);
+        return row_at<DT>(P.dft, (static_cast<int64_t>(U.b) * P.gamma + U.i) * P.V);
+    }
+}
+__device__ inline int64_t slot_base(const Params& P, uint32_t unit, int32_t j) {
+    return (static_cast<int64_t>(unit) * 2 + j) * P.maxp;
+}
+
+// Group-major grid (a group is one sequence, all 2*gamma+1 rows). Grid order:
+// groups [0, lag) contribute their statistics blocks; each group
 // j in [lag, G) then contributes its statistics blocks followed by the
 // residual blocks of group j - lag; the residual blocks of the last lag groups
 // close the grid. A group's residual blocks thus always follow all of its
 // statistics blocks.
 __device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint32_t& g, uint32_t& idx) {
     const uint32_t S = static_cast<uint32_t>(P.sb), R = static_cast<uint32_t>(P.rb);
-    const uint32_t D = static_cast<uint32_t>(P.lag), G = static_cast<uint32_t>(P.G);
+    const uint32_t D = static_cast<uint32_t>(P.lag), G = static_cast<uint32_t>(P.B);
     const uint32_t head = D * S;
     if (x < head) {
         kind = kStatsBlock;
@@ -404,16 +529,65 @@ __device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint
     idx = x - t * R;
 }
 
-// Row j of group g: target rows 0..gamma, then (T > 0) draft rows 0..gamma-1.
-template <int DT, int MODE>
+// Row j of group g: target rows 0..gamma, then draft rows 0..gamma-1.
+template <int DT>
 __device__ inline const char* group_row(const Params& P, uint32_t g, uint32_t j) {
-    if constexpr (MODE == kRows) {
-        return row_at<DT>(P.tgt, static_cast<int64_t>(g) * P.V);
-    } else {
-        const uint32_t nt = static_cast<uint32_t>(P.gamma) + 1u;
-        if (MODE == kGreedy || j < nt) return row_at<DT>(P.tgt, (static_cast<int64_t>(g) * nt + j) * P.V);
-        return row_at<DT>(P.dft, (static_cast<int64_t>(g) * P.gamma + (j - nt)) * P.V);
+    const uint32_t nt = static_cast<uint32_t>(P.gamma) + 1u;
+    if (j < nt) return row_at<DT>(P.tgt, (static_cast<int64_t>(g) * nt + j) * P.V);
+    return row_at<DT>(P.dft, (static_cast<int64_t>(g) * P.gamma + (j - nt)) * P.V);
+}
+
+
+// --------------------------------------------------------------------------
+// Waits and decision words
+// --------------------------------------------------------------------------
+// What the decision words of positions 0..i-1 of sequence b say (one
+// wavefront, lane j reads position j): kLive if all were accepted, kStopped if
+// the first that was not is a rejection or an unusable row, kUnknown if that
+// one is still pending.
+// (Split in two so that the load can be issued early: lane j < i loads
+// position j's word, state_of reads the loaded words.)
+__device__ inline uint64_t decision_word(const Params& P, int32_t b, int32_t i, int lane) {
+    return lane < i ? cld64(P.dec + static_cast<int64_t>(b) * (P.gamma + 1) + lane) : 0ull;
+}
+__device__ inline int state_of(const Params& P, uint64_t w, int32_t i, int lane) {
+    uint32_t st = kAcc;
+    if (lane < i) st = static_cast<uint32_t>(w >> 32) == P.epoch ? static_cast<uint32_t>(w & 3u) : kPending;
+    const uint64_t open = __ballot(st != kAcc);
+    if (!open) return kLive;
+    const int f = __ffsll(static_cast<unsigned long long>(open)) - 1;
+    return __shfl(static_cast<int>(st), f, kWave) == static_cast<int>(kPending) ? kUnknown : kStopped;
+}
+__device__ inline int sequence_state(const Params& P, int32_t b, int32_t i, int lane) {
+    return state_of(P, decision_word(P, b, i, lane), i, lane);
+}
+// `s` is the state from an earlier read (kUnknown: read again until known).
+__device__ inline int wait_sequence_state(const Params& P, int32_t b, int32_t i, int lane, int s) {
+    if (s != kUnknown) return s;
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+        __builtin_amdgcn_s_sleep(kSleep);
+        s = sequence_state(P, b, i, lane);
+        if (s != kUnknown) return s;
+        if (wall_clock64() - t0 > kWaitTicks) {
+            cst(P.err, 1u);
+            return kTimedOut;
+        }
     }
+}
+__device__ inline void publish(const Params& P, int32_t b, int32_t i, uint32_t status) {
+    cst64(P.dec + static_cast<int64_t>(b) * (P.gamma + 1) + i, (static_cast<uint64_t>(P.epoch) << 32) | status);
+}
+
+// The outputs of sequence b when it stops at position k (lane j writes
+// out_tokens[b, j]; x = draft token j): n = k, the k accepted draft tokens,
+// -1 after k; the token at k itself is written by whoever computes it. With
+// invalid, n = -1 and the whole row -1.
+__device__ inline void write_outputs(const Params& P, int32_t b, int32_t k, bool invalid, int32_t x, int lane) {
+    const int nt = P.gamma + 1;
+    if (lane < nt && (invalid || lane != k))
+        cst(P.out_tokens + static_cast<int64_t>(b) * nt + lane, (!invalid && lane < k) ? x : -1);
+    if (lane == 0) cst(P.out_n + b, invalid ? -1 : k);
 }
 
 struct SoftLane {
@@ -518,7 +692,7 @@ __device__ inline void consume_group(ArgLane& s, const typename Chunk<DT, VEC>::
 // One row piece's partial, handed through LDS to the block's last wavefront,
 // which writes the block's pieces to memory.
 struct Piece {
-    int64_t slot;  // (g*rps + j)*maxp + k
+    int64_t slot;  // (unit*2 + j)*maxp + k
     double s;      // sum of 2^(x*c - r) (T > 0)
     float m;       // max of the piece
     float r;       // integer reference (T > 0)
@@ -532,21 +706,23 @@ struct BlockPieces {
     uint32_t done;
 };
 
-// Statistics of one wavefront's chunk range [wl*cpw, (wl+1)*cpw) of group g's
-// concatenated rows: one partial per row piece, for slot (g*rps + j)*maxp + k,
+// Statistics of one wavefront's chunk range [wl*cpw, (wl+1)*cpw) of the unit's
+// (group-major: the group's) concatenated rows: one partial per row piece, for
+// slot (unit*2 + j)*maxp + k (group-major: (g*rps + j)*maxp + k),
 // k = wl minus the first wavefront touching row j. The piece that ends a row
 // also covers the row's unused slots (a row spans maxp - 1 or maxp
 // wavefronts), which are written with neutral values, so folds read every
 // slot. Returns the number of pieces placed in `out` (lane 0 writes them).
-template <int DT, bool VEC, int MODE>
-__device__ inline int stats_wave(const Params& P, uint32_t g, uint32_t wl, int lane, Piece* out) {
+template <int DT, bool VEC, int MODE, bool GROUP = false>
+__device__ inline int stats_wave(const Params& P, const Role& U, uint32_t wl, int lane, Piece* out) {
     int npieces = 0;
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
     using Lane = typename std::conditional<MODE == kGreedy, ArgLane, SoftLane>::type;
     const float c = P.c32;
+    const bool watch = !GROUP && MODE != kRows && P.skip && U.i > 0;
     const uint32_t nchunk = static_cast<uint32_t>(P.nchunk), cpw = static_cast<uint32_t>(P.cpw);
-    const uint32_t total = static_cast<uint32_t>(P.rps) * nchunk;
+    const uint32_t total = static_cast<uint32_t>(U.rows) * nchunk;
     uint32_t cc = wl * cpw;
     const uint32_t c_end = cc + cpw < total ? cc + cpw : total;
     uint32_t j = cc / nchunk;
@@ -554,7 +730,7 @@ __device__ inline int stats_wave(const Params& P, uint32_t g, uint32_t wl, int l
     int32_t k = static_cast<int32_t>(wl - first / cpw);
     while (cc < c_end) {
         const uint32_t ce = first + nchunk < c_end ? first + nchunk : c_end;
-        const char* row = group_row<DT, MODE>(P, g, j);
+        const char* row = GROUP ? group_row<DT>(P, U.unit, j) : unit_row<DT, MODE>(P, U, static_cast<int32_t>(j));
         const int64_t c0 = cc - first, c1 = ce - first;  // this piece: chunks [c0, c1) of row j
         Lane st;
         st.init();
@@ -592,10 +768,15 @@ __device__ inline int stats_wave(const Params& P, uint32_t g, uint32_t wl, int l
             load(qa, 0);
             int64_t gi = 1;  // next group to load; qa holds group gi - 1
             for (; gi + 2 < ng; gi += 2) {  // groups gi and gi + 1 are not the last
+                // early stop: the sequence's earlier decision words are read
+                // with this round's loads; if it stopped meanwhile, the rest of
+                // the range is left unread (the wavefront returns no pieces)
+                const uint64_t wd = watch ? decision_word(P, U.b, U.i, lane) : 0ull;
                 load(qb, gi);
                 eat(qa, gi - 1);
                 load(qa, gi + 1);
                 eat(qb, gi);
+                if (watch && state_of(P, wd, U.i, lane) == kStopped) return 0;
             }
             if (gi + 1 == ng) {  // gi is the last group
                 load_last(qb, gi);
@@ -610,7 +791,8 @@ __device__ inline int stats_wave(const Params& P, uint32_t g, uint32_t wl, int l
             }
         }
         Piece pc;
-        pc.slot = (static_cast<int64_t>(g) * P.rps + j) * P.maxp + k;
+        pc.slot = (GROUP ? (static_cast<int64_t>(U.unit) * P.rps + j) * P.maxp
+                         : slot_base(P, U.unit, static_cast<int32_t>(j))) + k;
         pc.npad = ce == first + nchunk ? P.maxp - 1 - k : 0;
         if constexpr (MODE == kGreedy) {
 #pragma unroll
@@ -670,54 +852,733 @@ __device__ inline void write_pieces(const Params& P, const BlockPieces& bp, int 
 }
 
 // --------------------------------------------------------------------------
-// Folding partials. A row's partials (M_p, R_p, S_p) combine exactly with
-// ldexp onto the largest reference R; the result is rebased once to the row
-// max: S * 2^(R - M*c), the exponent formed exactly in fp64. The argmax
-// partials combine as (value desc, index asc); any NaN marks the row.
+// Folding partials. A row's partials (m, r, s) combine exactly with ldexp onto
+// the larger reference r; the row's sum in exp((x - max)/T) units is
+// s * 2^(r - max*c), the exponent formed exactly in fp64. Argmax partials
+// combine as (value desc, index asc); a NaN marks the row.
 // --------------------------------------------------------------------------
+
+struct RowPart {
+    float m;
+    float r;
+    double s;
+};
+__device__ inline RowPart row_none() { return RowPart{-INFINITY, kRUnset, 0.0}; }
+__device__ inline RowPart fold(const RowPart& a, const RowPart& b) {
+    const float r = fmaxf(a.r, b.r);
+    return RowPart{fmaxf(a.m, b.m), r, rebase(a.s, a.r, r) + rebase(b.s, b.r, r)};
+}
+__device__ inline double row_sum(const RowPart& f, float c32) {
+    return f.s * exp2(static_cast<double>(f.r) - static_cast<double>(f.m) * static_cast<double>(c32));
+}
+__device__ inline bool usable(float M, double S) { return isfinite(M) && isfinite(S) && S > 0.0; }
+__device__ inline RowPart wave_fold_rows(RowPart f) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const RowPart g{__shfl_xor(f.m, o, kWave), __shfl_xor(f.r, o, kWave), __shfl_xor(f.s, o, kWave)};
+        f = fold(f, g);
+    }
+    return f;
+}
+
+struct ArgPart {
+    float m;
+    int32_t at;
+};
+__device__ inline ArgPart fold_arg(const ArgPart& a, const ArgPart& b) {
+    const bool nan = a.m != a.m || b.m != b.m;
+    const bool tb = b.m > a.m || (b.m == a.m && b.at < a.at);
+    ArgPart o;
+    o.m = nan ? NAN : (tb ? b.m : a.m);
+    o.at = tb ? b.at : a.at;
+    return o;
+}
+
+// The unit's rows folded from their slots by one wavefront (lane k takes slots
+// k, k + 64, ...; both rows' loads are issued together), the same in every
+// wavefront that folds them.
+__device__ inline void merge_rows(const Params& P, uint32_t unit, int rows, int lane, RowPart* out) {
+    RowPart f0 = row_none(), f1 = row_none();
+    for (int k = lane; k < P.maxp; k += kWave) {
+        const int64_t a = slot_base(P, unit, 0) + k, b = slot_base(P, unit, 1) + k;
+        const float m0 = cld(P.part_m + a), r0 = cld(P.part_r + a);
+        const double s0 = cld(P.part_s + a);
+        float m1 = -INFINITY, r1 = kRUnset;
+        double s1 = 0.0;
+        if (rows > 1) {
+            m1 = cld(P.part_m + b);
+            r1 = cld(P.part_r + b);
+            s1 = cld(P.part_s + b);
+        }
+        f0 = fold(f0, RowPart{m0, r0, s0});
+        f1 = fold(f1, RowPart{m1, r1, s1});
+    }
+    out[0] = wave_fold_rows(f0);
+    out[1] = wave_fold_rows(f1);
+}
+__device__ inline ArgPart merge_arg(const Params& P, uint32_t unit, int lane) {
+    ArgPart f{-INFINITY, INT32_MAX};
+    for (int k = lane; k < P.maxp; k += kWave) {
+        const int64_t a = slot_base(P, unit, 0) + k;
+        f = fold_arg(f, ArgPart{cld(P.part_m + a), cld(P.part_i + a)});
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) f = fold_arg(f, ArgPart{__shfl_xor(f.m, o, kWave), __shfl_xor(f.at, o, kWave)});
+    return f;
+}
+
+// Makes the compiler forget what it knows about a held chunk, so values
+// expanded from it in one pass are formed again in the next rather than kept
+// live (which would need 128 more registers for bf16).
+__device__ inline void opaque(uint4& r) { asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w)); }
+__device__ inline void opaque(float4& r) { asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w)); }
+
+
+// --------------------------------------------------------------------------
+// Registers: N chunk slots starting at chunk c0 of a row. Chunks before the
+// row's last are loaded whole; the last one from valid addresses only (its
+// elements at or beyond V are set to -inf by mask_slots once loaded); slots
+// past the row read as -inf without a load. All loads are issued before any
+// is consumed.
+// --------------------------------------------------------------------------
+template <int DT, bool VEC, int N>
+__device__ inline void load_slots(typename Chunk<DT, VEC>::Raw* q, const char* row, int64_t c0, int32_t nchunk,
+                                  int32_t V, int lane) {
+    using C = Chunk<DT, VEC>;
+    const int64_t c_last = nchunk - 1;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const int64_t c = c0 + u;
+        if (c < c_last) q[u] = C::load_full(row, c, lane);
+        else if (c == c_last) q[u] = C::load_clamped(row, c, c_last, lane, V);
+        else q[u] = C::blank();
+    }
+}
+template <int DT, bool VEC, int N>
+__device__ inline void mask_slots(typename Chunk<DT, VEC>::Raw* q, int64_t c0, int32_t nchunk, int32_t V, int lane) {
+    using C = Chunk<DT, VEC>;
+    const int64_t c_last = nchunk - 1;
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+        if (c0 + u == c_last) q[u] = C::mask(q[u], c_last, c_last, lane, V);
+}
+
+// --------------------------------------------------------------------------
+// Draw masses in t units. With e_j = 2^(fl(x_j*c) - mc) for the target (p) and
+// draft (q) rows, p_j = e_pj * scale_p and q_j = e_qj * scale_q (scale =
+// 2^(mc - m*c)/S). Then max(0, p_j - q_j) = scale_p * t_j with
+// t_j = max(0, e_pj - rho*e_qj), rho = scale_q/scale_p. t_j is formed in fp32
+// with rho split into an fp32 pair (hi + lo, two FMAs), so the product keeps
+// about 48 bits; every sum over elements is fp64. The inverse-CDF draw is
+// invariant to the common factor; drawing from p, t_j = e_pj.
+// --------------------------------------------------------------------------
+struct MassRow {
+    float mcp, mcq;  // fl(max*c) of the target / draft row
+    float rhi, rlo;  // rho = rhi + rlo
+    float c32;
+    int32_t has_q;   // 0: masses of p alone
+};
+__device__ inline float elem_mass(float xp, float xq, const MassRow& m) {
+    const float ep = __builtin_amdgcn_exp2f(fmaf(xp, m.c32, -m.mcp));
+    if (!m.has_q) return ep;
+    const float eq = __builtin_amdgcn_exp2f(fmaf(xq, m.c32, -m.mcq));
+    return fmaxf(0.0f, fmaf(-eq, m.rlo, fmaf(-eq, m.rhi, ep)));
+}
+
+// A wavefront's held pair (target chunks in slots [0, kPairCw), the draft's
+// same chunks in [kPairCw, 2*kPairCw)) is visited in ascending index order as
+// tiles: one chunk per tile on the vector path (each lane's EPL consecutive
+// elements), one element per lane per tile on the scalar path (element v of
+// every lane, then v + 1). A tile's lane mass is the fp64 sum of its elements'
+// masses in index order; tile totals are wave scans of the lane masses, added
+// in tile order. wave_mass and wave_draw form these sums identically.
+template <int DT, bool VEC>
+struct Tiles {
+    using C = Chunk<DT, VEC>;
+    static constexpr int PER_CHUNK = VEC ? 1 : C::EPL;  // tiles per chunk
+    static constexpr int EPT = VEC ? C::EPL : 1;        // elements per lane per tile
+};
+
+template <int DT, bool VEC>
+__device__ inline double wave_mass(typename Chunk<DT, VEC>::Raw* q, const MassRow& m) {
+    using C = Chunk<DT, VEC>;
+    using T = Tiles<DT, VEC>;
+#pragma unroll
+    for (int u = 0; u < kHold; ++u) opaque(q[u]);
+    double base = 0.0;
+#pragma unroll
+    for (int u = 0; u < kPairCw; ++u) {
+        float xp[C::EPL], xq[C::EPL];
+        C::expand(q[u], xp);
+        C::expand(q[kPairCw + u], xq);
+#pragma unroll
+        for (int t = 0; t < T::PER_CHUNK; ++t) {
+            double lm = 0.0;
+#pragma unroll
+            for (int e = 0; e < T::EPT; ++e) {
+                const int v = VEC ? e : t;
+                lm += static_cast<double>(elem_mass(xp[v], xq[v], m));
+            }
+            base += wave_sum(lm);
+        }
+    }
+    return base;
+}
+
+// The element of this wavefront's range where the cumulative mass, starting
+// at `base`, first exceeds `target` (smallest index); if rounding leaves no
+// crossing, the last element with mass; -1 if the range has none.
+template <int DT, bool VEC>
+__device__ inline int32_t wave_draw(typename Chunk<DT, VEC>::Raw* q, const MassRow& m, int64_t c0,
+                                    double base, double target, int lane) {
+    using C = Chunk<DT, VEC>;
+    using T = Tiles<DT, VEC>;
+#pragma unroll
+    for (int u = 0; u < kHold; ++u) opaque(q[u]);
+    int32_t last = -1;
+#pragma unroll
+    for (int u = 0; u < kPairCw; ++u) {
+        float xp[C::EPL], xq[C::EPL];
+        C::expand(q[u], xp);
+        C::expand(q[kPairCw + u], xq);
+#pragma unroll
+        for (int t = 0; t < T::PER_CHUNK; ++t) {
+            float mv[T::EPT];
+            double lm = 0.0;
+            int32_t mylast = -1;
+#pragma unroll
+            for (int e = 0; e < T::EPT; ++e) {
+                const int v = VEC ? e : t;
+                mv[e] = elem_mass(xp[v], xq[v], m);
+                lm += static_cast<double>(mv[e]);
+                if (mv[e] > 0.0f) mylast = static_cast<int32_t>(C::index_of(c0 + u, lane, v));
+            }
+            const double incl = base + wave_scan_incl(lm);
+            const double prev = lane_before(incl);
+            const double excl = lane == 0 ? base : prev;
+            const uint64_t hit = __ballot(lm > 0.0 && excl <= target && target < incl);
+            if (hit) {
+                const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                int32_t pick = -1;
+                if (lane == l) {
+                    double run = excl;
+#pragma unroll
+                    for (int e = 0; e < T::EPT; ++e) {
+                        run += static_cast<double>(mv[e]);
+                        if (pick < 0 && mv[e] > 0.0f && run > target)
+                            pick = static_cast<int32_t>(C::index_of(c0 + u, lane, VEC ? e : t));
+                    }
+                    if (pick < 0) pick = mylast;
+                }
+                return __shfl(pick, l, kWave);
+            }
+            const uint64_t mass = __ballot(mylast >= 0);
+            if (mass) last = __shfl(mylast, 63 - __clzll(static_cast<unsigned long long>(mass)), kWave);
+            base = lane_f64(incl, kWave - 1);
+        }
+    }
+    return last;
+}
+
+// --------------------------------------------------------------------------
+// The unit's last block
+// --------------------------------------------------------------------------
+// Counts the calling wavefront in at a unit counter once its coherent stores
+// have completed. Returns true to the last of `total` arrivals, which then sees
+// every earlier arrival's stores through coherent loads, and which resets the
+// counter for the next call (stream order makes the reset visible to it).
+__device__ inline bool arrive_last(uint32_t* cnt, uint32_t total, int lane) {
+    complete_before();
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, kWave);
+    if (old + 1u != total) return false;
+    after_complete();
+    if (lane == 0) cst(cnt, 0u);
+    return true;
+}
+
+// Draw record of sequence b: words 0..5 each carry the call's epoch in their
+// high half, so a reader that sees the epoch in all six has the whole record
+// (one round trip, no separate tag): kind << 8 | k, then mcp, mcq, rhi, rlo
+// and scale_p (as fp32). Its ticket counters are zeroed and complete before
+// any word goes out (lane 0 writes).
+constexpr int kRecFields = 6;
+__device__ inline uint64_t tagged(const Params& P, uint32_t v) { return (static_cast<uint64_t>(P.epoch) << 32) | v; }
+// The draw's two ticket counters live beside its record: the record's writer
+// sets them to zero before the tag goes out and no block touches them before
+// seeing the tag, so they need no clearing between calls.
+__device__ inline uint32_t* claim_counter(const Params& P, int32_t b) {
+    return reinterpret_cast<uint32_t*>(P.rec + static_cast<int64_t>(b) * kRecWords + kClaimWord);
+}
+__device__ inline uint32_t* piece_counter(const Params& P, int32_t b) {
+    return reinterpret_cast<uint32_t*>(P.rec + static_cast<int64_t>(b) * kRecWords + kPieceWord);
+}
+
+__device__ inline void write_record(const Params& P, int32_t b, uint32_t kind, int32_t k, const MassRow& m,
+                                    double scale_p) {
+    uint64_t* r = P.rec + static_cast<int64_t>(b) * kRecWords;
+    cst(claim_counter(P, b), 0u);
+    cst(piece_counter(P, b), 0u);
+    complete_before();
+    cst64(r, tagged(P, (kind << 8) | static_cast<uint32_t>(k)));
+    cst64(r + 1, tagged(P, __float_as_uint(m.mcp)));
+    cst64(r + 2, tagged(P, __float_as_uint(m.mcq)));
+    cst64(r + 3, tagged(P, __float_as_uint(m.rhi)));
+    cst64(r + 4, tagged(P, __float_as_uint(m.rlo)));
+    cst64(r + 5, tagged(P, __float_as_uint(static_cast<float>(scale_p))));
+}
+
+// T > 0: the accept step of position i from the unit's folded rows (one
+// wavefront). The bonus unit (i == gamma) only checks that its row is usable.
+template <int DT>
+__device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
+    const int32_t gamma = P.gamma, V = P.V, nt = gamma + 1;
+    const bool pair = U.i < gamma;
+    int32_t xj = 0;
+    if (lane < gamma) xj = P.tokens[static_cast<int64_t>(U.b) * gamma + lane];
+    const int32_t x = pair ? __shfl(xj, U.i, kWave) : 0;
+    const bool tok_ok = x >= 0 && x < V;
+    float lt = 0.0f, ld = 0.0f;
+    if (pair) {
+        lt = cld(P.tok_l + static_cast<int64_t>(U.unit) * 2);
+        ld = cld(P.tok_l + static_cast<int64_t>(U.unit) * 2 + 1);
+    }
+    // the earlier positions' words are read with the unit's slots (one round
+    // trip); they are needed only if position i ends the sequence
+    const uint64_t wd = decision_word(P, U.b, U.i, lane);
+    RowPart rs[2];
+    merge_rows(P, U.unit, U.rows, lane, rs);
+    const float c = P.c32;
+    const double cd = static_cast<double>(c);
+    const float Mt = rs[0].m, Md = rs[1].m;
+    const double st = row_sum(rs[0], c), sd = row_sum(rs[1], c);
+    const bool ut = usable(Mt, st), ud = usable(Md, sd);
+    uint32_t status = kAcc;
+    double p = NAN, qv = NAN;
+    if (pair) {
+        if (!ut || !ud || !tok_ok) {
+            status = kBad;
+        } else {
+            p = exp2((static_cast<double>(lt) - static_cast<double>(Mt)) * cd) / st;
+            qv = exp2((static_cast<double>(ld) - static_cast<double>(Md)) * cd) / sd;
+            const double alpha = p == 0.0 ? 0.0 : (qv == 0.0 ? 1.0 : fmin(1.0, p / qv));
+            const double u = philox_uniform(P.seed, static_cast<uint32_t>(U.b + P.b_offset),
+                                            static_cast<uint32_t>(U.i), 0u);
+            status = u < alpha ? kAcc : kRej;
+        }
+    } else if (!ut) {
+        status = kBad;
+    }
+    if (lane == 0) {
+        const int64_t R = 2 * gamma + 1;
+        if (P.dbg_row_max) P.dbg_row_max[U.b * R + U.i] = Mt;
+        if (P.dbg_row_sumexp) P.dbg_row_sumexp[U.b * R + U.i] = st;
+        if (pair) {
+            if (P.dbg_row_max) P.dbg_row_max[U.b * R + nt + U.i] = Md;
+            if (P.dbg_row_sumexp) P.dbg_row_sumexp[U.b * R + nt + U.i] = sd;
+            if (P.dbg_p) P.dbg_p[static_cast<int64_t>(U.b) * gamma + U.i] = p;
+            if (P.dbg_q) P.dbg_q[static_cast<int64_t>(U.b) * gamma + U.i] = qv;
+        }
+    }
+    // every position's outcome is published at once; only the position that
+    // ends the sequence (its first non-accepted one, or the bonus row) waits
+    // for the earlier positions' outcomes
+    if (pair && lane == 0) publish(P, U.b, U.i, status);
+    if (pair && status == kAcc) return;
+    const int state = U.i > 0 ? wait_sequence_state(P, U.b, U.i, lane, state_of(P, wd, U.i, lane)) : kLive;
+    if (state == kStopped) return;
+    MassRow mr;
+    mr.c32 = c;
+    mr.has_q = pair ? 1 : 0;
+    mr.mcp = Mt * c;
+    const double scale_p = exp2(static_cast<double>(mr.mcp) - static_cast<double>(Mt) * cd) / st;
+    mr.mcq = pair ? Md * c : 0.0f;
+    const double rho = pair ? exp2(static_cast<double>(mr.mcq) - static_cast<double>(Md) * cd) / sd / scale_p : 0.0;
+    mr.rhi = static_cast<float>(rho);
+    mr.rlo = static_cast<float>(rho - static_cast<double>(mr.rhi));
+    if (state == kTimedOut) {
+        write_outputs(P, U.b, U.i, true, xj, lane);
+        if (lane == 0) write_record(P, U.b, kNoDraw, U.i, mr, scale_p);
+        return;
+    }
+    if (status == kBad) {
+        write_outputs(P, U.b, U.i, true, xj, lane);
+        if (lane == 0) {
+            if (P.dbg_z) P.dbg_z[U.b] = NAN;
+            write_record(P, U.b, kNoDraw, U.i, mr, scale_p);
+        }
+        return;
+    }
+    // position i ends the sequence: a rejection (draw from the residual) or the
+    // bonus row after gamma acceptances (draw from p); the token is drawn by the
+    // sequence's residual blocks
+    write_outputs(P, U.b, U.i, false, xj, lane);
+    if (lane == 0) {
+        write_record(P, U.b, pair ? kDrawResidual : kDrawP, U.i, mr, scale_p);
+    }
+}
+
+// T == 0: the greedy step of position i (one wavefront): accept while the
+// draft token is the row's argmax (lowest index on ties), else emit the
+// argmax; at the bonus row (all gamma accepted) emit its argmax.
+__device__ inline void decide_greedy(const Params& P, const Role& U, int lane) {
+    const int32_t gamma = P.gamma, V = P.V, nt = gamma + 1;
+    int32_t xj = 0;
+    if (lane < gamma) xj = P.tokens[static_cast<int64_t>(U.b) * gamma + lane];
+    const ArgPart f = merge_arg(P, U.unit, lane);
+    if (lane == 0) {
+        if (P.dbg_row_max) P.dbg_row_max[U.b * static_cast<int64_t>(2 * gamma + 1) + U.i] = f.m;
+        if (P.dbg_argmax) P.dbg_argmax[static_cast<int64_t>(U.b) * nt + U.i] = f.at;
+    }
+    const bool ut = isfinite(f.m);
+    const uint64_t wd = decision_word(P, U.b, U.i, lane);
+    uint32_t status;
+    if (U.i < gamma) {
+        const int32_t x = __shfl(xj, U.i, kWave);
+        status = (!ut || !(x >= 0 && x < V)) ? kBad : (x == f.at ? kAcc : kRej);
+        if (lane == 0) publish(P, U.b, U.i, status);  // at once; see decide_sample
+    } else {
+        status = ut ? kRej : kBad;  // the bonus row ends the sequence either way
+    }
+    if (status == kAcc) return;
+    const int state = U.i > 0 ? wait_sequence_state(P, U.b, U.i, lane, state_of(P, wd, U.i, lane)) : kLive;
+    if (state == kStopped) return;
+    if (state == kTimedOut) {
+        write_outputs(P, U.b, U.i, true, xj, lane);
+        return;
+    }
+    write_outputs(P, U.b, U.i, status == kBad, xj, lane);
+    if (status != kBad && lane == 0) cst(P.out_tokens + static_cast<int64_t>(U.b) * nt + U.i, f.at);
+}
+
+// Row statistics: the row's max and sum (one wavefront).
+__device__ inline void finish_rows(const Params& P, const Role& U, int lane) {
+    RowPart rs[2];
+    merge_rows(P, U.unit, 1, lane, rs);
+    if (lane == 0) {
+        const double s = row_sum(rs[0], P.c32);
+        P.rows_max[U.b] = rs[0].m;
+        P.rows_sumexp[U.b] = usable(rs[0].m, s) ? s : NAN;
+    }
+}
+
+// A statistics block: each wavefront streams its chunk range (nothing if its
+// sequence already stopped), the block's last wavefront writes the block's
+// pieces and counts the block in, and the unit's last block decides.
+// --------------------------------------------------------------------------
+// T > 0: the draw of a sequence that stopped at position k. Its stopping rows
+// are split into nbr pieces of kWavesPerBlock*kPairCw chunks of each row; a
+// block claims a piece (an atomic ticket), loads it into registers, stores one
+// mass per wavefront and counts the piece in; the block that counts in the
+// last piece draws the token: scans of the per-wavefront masses give Z and the
+// wavefront holding u*Z, whose chunks it loads again and scans. Blocks of the
+// sequence's later positions (which the early stop leaves idle) and the
+// grid's closing blocks claim pieces until none is left.
+// --------------------------------------------------------------------------
+struct DrawInfo {
+    int32_t kind;  // kNoDraw, kDrawResidual or kDrawP
+    int32_t k;     // stopping position
+    MassRow mr;
+    double scale_p;
+};
+
+// One read of sequence b's draw record (one wavefront): false until all of
+// its words carry this call's epoch.
+__device__ inline bool read_record(const Params& P, int32_t b, int lane, DrawInfo& d) {
+    const uint64_t* r = P.rec + static_cast<int64_t>(b) * kRecWords;
+    const uint64_t v = lane < kRecFields ? cld64(r + lane) : tagged(P, 0u);
+    if (__ballot(static_cast<uint32_t>(v >> 32) != P.epoch) != 0) return false;
+    const uint32_t x = static_cast<uint32_t>(v);
+    const uint32_t w0 = __shfl(x, 0, kWave);
+    d.kind = static_cast<int32_t>((w0 >> 8) & 0xFFu);
+    d.k = static_cast<int32_t>(w0 & 0xFFu);
+    d.mr.mcp = __uint_as_float(__shfl(x, 1, kWave));
+    d.mr.mcq = __uint_as_float(__shfl(x, 2, kWave));
+    d.mr.rhi = __uint_as_float(__shfl(x, 3, kWave));
+    d.mr.rlo = __uint_as_float(__shfl(x, 4, kWave));
+    d.scale_p = static_cast<double>(__uint_as_float(__shfl(x, 5, kWave)));
+    d.mr.c32 = P.c32;
+    d.mr.has_q = d.kind == kDrawResidual ? 1 : 0;
+    return true;
+}
+
+// Wavefront `gw` of the stopping rows: chunks [gw*kPairCw, (gw+1)*kPairCw) of
+// the target row k (slots [0, kPairCw)) and of the draft row k when has_q.
+template <int DT, bool VEC>
+__device__ inline void load_wave_chunks(const Params& P, int32_t b, int32_t k, bool has_q, int64_t gw,
+                                        typename Chunk<DT, VEC>::Raw* q, int lane) {
+    using C = Chunk<DT, VEC>;
+    const int64_t c0 = gw * kPairCw;
+    const char* trow = row_at<DT>(P.tgt, (static_cast<int64_t>(b) * (P.gamma + 1) + k) * P.V);
+    load_slots<DT, VEC, kPairCw>(q, trow, c0, P.nchunk, P.V, lane);
+    if (has_q) {
+        const char* drow = row_at<DT>(P.dft, (static_cast<int64_t>(b) * P.gamma + k) * P.V);
+        load_slots<DT, VEC, kPairCw>(q + kPairCw, drow, c0, P.nchunk, P.V, lane);
+    } else {
+#pragma unroll
+        for (int u = kPairCw; u < kHold; ++u) q[u] = C::blank();
+    }
+    mask_slots<DT, VEC, kPairCw>(q, c0, P.nchunk, P.V, lane);
+    if (has_q) mask_slots<DT, VEC, kPairCw>(q + kPairCw, c0, P.nchunk, P.V, lane);
+}
+
+// Total of m[0, n) in the order the search below accumulates it.
+__device__ inline double scan_total(const double* m, int32_t n, int lane) {
+    double base = 0.0;
+    for (int32_t t0 = 0; t0 < n; t0 += kWave) {
+        const double v = t0 + lane < n ? cld(m + t0 + lane) : 0.0;
+        base += lane_f64(wave_scan_incl(v), kWave - 1);
+    }
+    return base;
+}
+
+// First index i in [0, n) whose cumulative mass exceeds t, and the mass before
+// it; if rounding leaves none, the last index with mass.
+__device__ inline int32_t scan_find(const double* m, int32_t n, double t, int lane, double& before) {
+    double base = 0.0;
+    int32_t last = -1;
+    double last_before = 0.0;
+    for (int32_t t0 = 0; t0 < n; t0 += kWave) {
+        const double v = t0 + lane < n ? cld(m + t0 + lane) : 0.0;
+        const double incl = base + wave_scan_incl(v);
+        const double prev = lane_before(incl);
+        const double excl = lane == 0 ? base : prev;
+        const uint64_t hit = __ballot(v > 0.0 && excl <= t && t < incl);
+        if (hit) {
+            const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+            before = __shfl(excl, l, kWave);
+            return t0 + l;
+        }
+        const uint64_t mass = __ballot(v > 0.0);
+        if (mass) {
+            const int l = 63 - __clzll(static_cast<unsigned long long>(mass));
+            last = t0 + l;
+            last_before = __shfl(excl, l, kWave);
+        }
+        base = lane_f64(incl, kWave - 1);
+    }
+    before = last_before;
+    return last;
+}
+
+
+// The token of sequence b, by the block that counted in its last piece: Z and
+// the wavefront holding u*Z from the per-wavefront masses (wavefront 0), then
+// that wavefront's chunks scanned again. A rejected row whose residual rounds
+// to zero draws from p_k instead: the block recomputes every wavefront's p
+// mass first (never on the common path).
+template <int DT, bool VEC>
+__device__ inline void draw_sequence(const Params& P, int32_t b, DrawInfo d, int w, int lane) {
+    using Raw = typename Chunk<DT, VEC>::Raw;
+    __shared__ double s_z;
+    const int32_t n = P.nbr * kWavesPerBlock;
+    double* m = P.msum + static_cast<int64_t>(b) * n;
+    if (w == 0) {
+        after_complete();
+        const double z = scan_total(m, n, lane);
+        if (lane == 0) {
+            s_z = z;
+            if (P.dbg_z) P.dbg_z[b] = z * d.scale_p;
+        }
+    }
+    __syncthreads();
+    double z = s_z;
+    if (d.mr.has_q && !(z > 0.0)) {
+        d.mr.has_q = 0;
+        for (int32_t gw = w; gw < n; gw += kWavesPerBlock) {
+            Raw q[kHold];
+            load_wave_chunks<DT, VEC>(P, b, d.k, false, gw, q, lane);
+            const double wm = wave_mass<DT, VEC>(q, d.mr);
+            if (lane == 0) cst(m + gw, wm);
+        }
+        complete_before();
+        __syncthreads();
+        if (w == 0) {
+            after_complete();
+            const double zp = scan_total(m, n, lane);
+            if (lane == 0) s_z = zp;
+        }
+        __syncthreads();
+        z = s_z;
+    }
+    if (w != 0) return;
+    const int32_t nt = P.gamma + 1;
+    const double u = philox_uniform(P.seed, static_cast<uint32_t>(b + P.b_offset), static_cast<uint32_t>(d.k), 1u);
+    const double target = u * z;
+    double before = 0.0;
+    const int32_t sel = scan_find(m, n, target, lane, before);
+    int32_t tok = -1;  // no mass at all (cannot happen for a usable row): keep the output defined
+    if (sel >= 0) {
+        Raw q[kHold];
+        load_wave_chunks<DT, VEC>(P, b, d.k, d.mr.has_q != 0, sel, q, lane);
+        tok = wave_draw<DT, VEC>(q, d.mr, static_cast<int64_t>(sel) * kPairCw, before, target, lane);
+    }
+    if (lane == 0) cst(P.out_tokens + static_cast<int64_t>(b) * nt + d.k, tok);
+}
+
+// Claims pieces of sequence b's stopping rows until none is left (every
+// thread of the block; d.kind is a draw).
+template <int DT, bool VEC>
+__device__ inline void claim_pieces(const Params& P, int32_t b, const DrawInfo& d) {
+    using Raw = typename Chunk<DT, VEC>::Raw;
+    __shared__ uint32_t s_piece, s_last;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+    const uint32_t np = static_cast<uint32_t>(P.nbr);
+    uint32_t* claim = claim_counter(P, b);
+    uint32_t* done = piece_counter(P, b);
+    for (;;) {
+        if (threadIdx.x == 0) s_piece = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint32_t piece = s_piece;
+        if (piece >= np) return;
+        Raw q[kHold];
+        const int64_t gw = static_cast<int64_t>(piece) * kWavesPerBlock + w;
+        load_wave_chunks<DT, VEC>(P, b, d.k, d.mr.has_q != 0, gw, q, lane);
+        const double wm = wave_mass<DT, VEC>(q, d.mr);
+        if (lane == 0) cst(P.msum + static_cast<int64_t>(b) * np * kWavesPerBlock + gw, wm);
+        complete_before();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == np ? 1u : 0u;
+        __syncthreads();
+        if (s_last) draw_sequence<DT, VEC>(P, b, d, w, lane);
+        __syncthreads();
+    }
+}
+
+// A closing block of sequence b: waits for the draw record, then claims.
+template <int DT, bool VEC>
+__device__ inline void resid_block(const Params& P, const Role& U) {
+    __shared__ int32_t s_ok;
+    __shared__ DrawInfo s_d;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+    const int32_t b = U.b;
+    if (w == 0) {
+        DrawInfo d;
+        d.kind = kNoDraw;
+        bool ok = read_record(P, b, lane, d);
+        if (!ok) {
+            const uint64_t t0 = wall_clock64();
+            for (;;) {
+                __builtin_amdgcn_s_sleep(kSleep);
+                if (read_record(P, b, lane, d)) {
+                    ok = true;
+                    break;
+                }
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    cst(P.err, 1u);
+                    break;
+                }
+            }
+        }
+        if (lane == 0) {
+            s_ok = ok ? 1 : 0;
+            s_d = d;
+        }
+    }
+    __syncthreads();
+    if (!s_ok) {  // the record never came (not expected): report the sequence invalid
+        if (U.r == 0 && w == 0) write_outputs(P, b, 0, true, 0, lane);
+        return;
+    }
+    const DrawInfo d = s_d;
+    if (d.kind != kNoDraw) claim_pieces<DT, VEC>(P, b, d);
+}
+
+// A statistics block. Wavefront 0 first reads the decision words of the
+// sequence's earlier positions: if the sequence already stopped, the block
+// loads none of its rows, counts itself in and (T > 0) spends itself on the
+// sequence's draw instead. Otherwise each wavefront streams its chunk range,
+// the block's last wavefront writes the block's pieces and counts the block
+// in, and the unit's last block decides.
+template <int DT, bool VEC, int MODE>
+__device__ inline void stats_block(const Params& P, const Role& U) {
+    __shared__ BlockPieces bp;
+    __shared__ int32_t s_stop;
+    __shared__ DrawInfo s_d;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+    if (threadIdx.x == 0) {
+        bp.done = 0u;
+        s_stop = 0;
+    }
+    if constexpr (MODE != kRows) {
+        if (P.skip && U.i > 0) {
+            __syncthreads();
+            if (w == 0) {
+                const bool stop = sequence_state(P, U.b, U.i, lane) == kStopped;
+                DrawInfo d;
+                d.kind = kNoDraw;
+                if (MODE == kSample && stop && !read_record(P, U.b, lane, d)) d.kind = kNoDraw;
+                if (lane == 0) {
+                    s_stop = stop ? 1 : 0;
+                    s_d = d;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t* cnt = P.cnt + static_cast<int64_t>(U.unit) * P.cstride;
+    if (s_stop) {
+        // counted in; the unit decides nothing (the sequence stopped earlier)
+        if (threadIdx.x == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1u == static_cast<uint32_t>(U.nb)) cst(cnt, 0u);
+        }
+        if constexpr (MODE == kSample) {
+            const DrawInfo d = s_d;
+            if (d.kind != kNoDraw) claim_pieces<DT, VEC>(P, U.b, d);
+        }
+        return;
+    }
+    const int nwb = min(kWavesPerBlock, U.nw - U.r * kWavesPerBlock);  // wavefronts with work
+    if (w >= nwb) return;
+    // T > 0: the unit's first wavefront also fetches the draft token's two
+    // logits for the decision (off the decider's path)
+    const bool fetch = MODE == kSample && U.rows == 2 && U.r == 0 && w == 0;
+    int32_t x = -1;
+    if (fetch && lane == 0) x = P.tokens[static_cast<int64_t>(U.b) * P.gamma + U.i];
+    const int n = stats_wave<DT, VEC, MODE>(P, U, U.r * kWavesPerBlock + w, lane, bp.p[w]);
+    if (fetch) {
+        if (lane == 0) {
+            const bool ok = x >= 0 && x < P.V;
+            const float lt = ok ? load_one<DT>(unit_row<DT, MODE>(P, U, 0), x) : 0.0f;
+            const float ld = ok ? load_one<DT>(unit_row<DT, MODE>(P, U, 1), x) : 0.0f;
+            cst(P.tok_l + static_cast<int64_t>(U.unit) * 2, lt);
+            cst(P.tok_l + static_cast<int64_t>(U.unit) * 2 + 1, ld);
+        }
+        complete_before();  // visible before the block counts in
+    }
+    if (lane == 0) bp.n[w] = n;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(&bp.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __shfl(old, 0, kWave);
+    if (old + 1u != static_cast<uint32_t>(nwb)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    write_pieces<MODE>(P, bp, nwb, lane);
+    if (!arrive_last(cnt, static_cast<uint32_t>(U.nb), lane)) return;
+    if constexpr (MODE == kSample) decide_sample<DT>(P, U, lane);
+    else if constexpr (MODE == kGreedy) decide_greedy(P, U, lane);
+    else finish_rows(P, U, lane);
+}
+
+// ==========================================================================
+// Group-major schedule (T > 0): a group is one sequence's 2*gamma+1 rows; its
+// residual blocks (at the end of the grid by default) fold the group's
+// partials, repeat the accept step for all gamma positions, sum the residual
+// of row k over 1024-element subsegments and draw.
+// ==========================================================================
+// Folding a group's partials (the same exact ldexp combination as above).
 struct RowStat {
     float m;
     int32_t arg;
     double s;
 };
 
-__device__ inline bool usable(float M, double S) { return isfinite(M) && isfinite(S) && S > 0.0; }
-
-// One thread folds one row's np slots, staged in LDS, in slot order.
-template <bool GREEDY>
-__device__ inline RowStat fold_slots(int np, const float* pm, const float* pr, const double* ps, const int32_t* pi,
-                                     float c32) {
-    RowStat o;
-    if constexpr (GREEDY) {
-        float best = -INFINITY;
-        int32_t arg = INT32_MAX;
-        bool nan = false;
-        for (int k = 0; k < np; ++k) {
-            const float v = pm[k];
-            const int32_t a = pi[k];
-            nan |= (v != v);
-            if (v > best || (v == best && a < arg)) {
-                best = v;
-                arg = a;
-            }
-        }
-        o.m = nan ? NAN : best;
-        o.arg = arg;
-        o.s = 1.0;
-    } else {
-        float M = -INFINITY, R = kRUnset;
-        for (int k = 0; k < np; ++k) {
-            M = fmaxf(M, pm[k]);
-            R = fmaxf(R, pr[k]);
-        }
-        double acc = 0.0;
-        for (int k = 0; k < np; ++k) acc += rebase(ps[k], pr[k], R);
-        o.m = M;
-        o.arg = 0;
-        o.s = acc * exp2(static_cast<double>(R) - static_cast<double>(M) * static_cast<double>(c32));
-    }
-    return o;
-}
 
 // The same fold straight from memory (coherent loads, eight slots in flight),
 // for groups whose slots do not fit the LDS stage. The running sum is rebased
@@ -779,28 +1640,6 @@ __device__ inline RowStat fold_slots_mem(const Params& P, int64_t base) {
     return o;
 }
 
-// One wavefront folds one row (the stand-alone row statistics): lane k takes
-// slots k, k+64, ...; butterfly reductions combine the lanes.
-__device__ inline RowStat fold_row_wave(const Params& P, int64_t base, int lane) {
-    float M = -INFINITY, R = kRUnset;
-    double S = 0.0;
-    for (int k = lane; k < P.maxp; k += kWave) {
-        const float mk = cld(P.part_m + base + k), rk = cld(P.part_r + base + k);
-        const double sk = cld(P.part_s + base + k);
-        const float Rn = fmaxf(R, rk);
-        S = rebase(S, R, Rn) + rebase(sk, rk, Rn);
-        R = Rn;
-        M = fmaxf(M, mk);
-    }
-    const float Mw = wave_max(M), Rw = wave_max(R);
-    const double Sw = wave_sum(rebase(S, R, Rw));
-    RowStat o;
-    o.m = Mw;
-    o.arg = 0;
-    o.s = Sw * exp2(static_cast<double>(Rw) - static_cast<double>(Mw) * static_cast<double>(P.c32));
-    return o;
-}
-
 // Running fold state of a set of partials: soft (max m, reference r, sum s of
 // 2^(x*c - r)) or argmax (best value, its first index, any NaN).
 struct Fold {
@@ -838,10 +1677,8 @@ __device__ inline void merge_group(const Params& P, uint32_t g, char* dyn, RowSt
     const int slots = nrows * maxp;
     const int tid = NT == kWave ? static_cast<int>(threadIdx.x & (kWave - 1)) : static_cast<int>(threadIdx.x);
     const int64_t base = static_cast<int64_t>(g) * slots;
-    auto sync = [] {
-        if constexpr (NT == kWave) wave_lds_sync();
-        else __syncthreads();
-    };
+    static_assert(NT == kBlock, "one block folds a group");
+    auto sync = [] { __syncthreads(); };
     if (P.stage > 0) {
         const int cap = P.stage;
         double* ls = reinterpret_cast<double*>(dyn);
@@ -1069,8 +1906,8 @@ struct ResidRow {
 template <int DT>
 __device__ inline ResidRow resid_row(const Params& P, const SeqInfo& s, uint32_t g) {
     ResidRow rr;
-    rr.prow = group_row<DT, kSample>(P, g, static_cast<uint32_t>(s.k));
-    rr.qrow = s.has_q ? group_row<DT, kSample>(P, g, static_cast<uint32_t>(P.gamma + 1 + s.k)) : nullptr;
+    rr.prow = group_row<DT>(P, g, static_cast<uint32_t>(s.k));
+    rr.qrow = s.has_q ? group_row<DT>(P, g, static_cast<uint32_t>(P.gamma + 1 + s.k)) : nullptr;
     rr.mcp = s.mcp;
     rr.mcq = s.mcq;
     rr.rhi = static_cast<float>(s.rho);
@@ -1157,49 +1994,6 @@ __device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int3
 // rejected row the draw is made from p_k instead (its masses come from the
 // same pass).
 // --------------------------------------------------------------------------
-__device__ inline double wave_scan(double v, int) { return wave_scan_incl(v); }
-// The value of lane l - 1 (0 in lane 0).
-__device__ inline double lane_before(double v) { return dpp_f64<0x138, 0xF>(v); }
-
-// Total of m[0, n) in the order the search below accumulates it.
-__device__ inline double scan_total(const double* m, int32_t n, int lane) {
-    double base = 0.0;
-    for (int32_t t0 = 0; t0 < n; t0 += kWave) {
-        const double v = t0 + lane < n ? cld(m + t0 + lane) : 0.0;
-        base += lane_f64(wave_scan(v, lane), kWave - 1);
-    }
-    return base;
-}
-
-// First index i in [0, n) whose cumulative mass exceeds t, and the mass before
-// it; if rounding leaves none, the last index with mass.
-__device__ inline int32_t scan_find(const double* m, int32_t n, double t, int lane, double& before) {
-    double base = 0.0;
-    int32_t last = -1;
-    double last_before = 0.0;
-    for (int32_t t0 = 0; t0 < n; t0 += kWave) {
-        const double v = t0 + lane < n ? cld(m + t0 + lane) : 0.0;
-        const double incl = base + wave_scan(v, lane);
-        const double prev = lane_before(incl);
-        const double excl = lane == 0 ? base : prev;
-        const uint64_t hit = __ballot(v > 0.0 && excl <= t && t < incl);
-        if (hit) {
-            const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-            before = __shfl(excl, l, kWave);
-            return t0 + l;
-        }
-        const uint64_t mass = __ballot(v > 0.0);
-        if (mass) {
-            const int l = 63 - __clzll(static_cast<unsigned long long>(mass));
-            last = t0 + l;
-            last_before = __shfl(excl, l, kWave);
-        }
-        base = lane_f64(incl, kWave - 1);
-    }
-    before = last_before;
-    return last;
-}
-
 // The same two steps on up to kDrawTiles*64 masses held in registers (one
 // load round trip); the totals and prefix sums are formed exactly as above.
 constexpr int kDrawTiles = 4;
@@ -1208,7 +2002,7 @@ __device__ inline double regs_scan(const double* v, double* incl, int lane) {
     double base = 0.0;
 #pragma unroll
     for (int t = 0; t < kDrawTiles; ++t) {
-        incl[t] = base + wave_scan(v[t], lane);
+        incl[t] = base + wave_scan_incl(v[t]);
         base = lane_f64(incl[t], kWave - 1);
     }
     return base;
@@ -1306,7 +2100,7 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
         local += mv[v];
         if (mv[v] > 0.0) mylast = static_cast<int32_t>(j0 + v);
     }
-    const double incl = before + wave_scan(local, lane);
+    const double incl = before + wave_scan_incl(local);
     const double prev = lane_before(incl);
     const double excl = lane == 0 ? before : prev;
     const uint64_t hit = __ballot(local > 0.0 && excl <= target && target < incl);
@@ -1350,24 +2144,6 @@ __device__ inline bool wait_published(const Params& P, uint32_t g) {
     }
 }
 
-// T == 0: the group's last statistics block folds the argmax partials of the
-// gamma+1 target rows and runs the greedy accept step (one wavefront).
-__device__ inline void finish_greedy(const Params& P, uint32_t g, int lane, char* dyn) {
-    __shared__ RowStat rsg[SPEC_MAX_GAMMA + 1];
-    const int32_t x = lane < P.gamma ? P.tokens[static_cast<int64_t>(g) * P.gamma + lane] : 0;
-    merge_group<true, kWave>(P, g, dyn, rsg);
-    (void)accept_wave<true>(P, g, rsg, x, 0.0f, 0.0f, true);
-}
-
-// Row statistics: the row's last statistics block folds its partials (one wavefront).
-__device__ inline void finish_rows(const Params& P, uint32_t g, int lane) {
-    const RowStat o = fold_row_wave(P, static_cast<int64_t>(g) * P.maxp, lane);
-    if (lane == 0) {
-        P.rows_max[g] = o.m;
-        P.rows_sumexp[g] = usable(o.m, o.s) ? o.s : NAN;
-    }
-}
-
 // T > 0: one residual block of group g (idx in [0, rb)). Once every
 // statistics block of g has counted in, the block folds g's partials and
 // repeats the accept step (block 0 writes the results); then wavefront w takes
@@ -1375,7 +2151,7 @@ __device__ inline void finish_rows(const Params& P, uint32_t g, int lane) {
 // before summing. The group's last residual block draws the token and resets
 // the group's counters for the next call.
 template <int DT, bool VEC>
-__device__ inline void resid_block(const Params& P, uint32_t g, uint32_t idx, char* dyn) {
+__device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t idx, char* dyn) {
     __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
     __shared__ SeqInfo shi;
     __shared__ int s_ok;
@@ -1390,8 +2166,8 @@ __device__ inline void resid_block(const Params& P, uint32_t g, uint32_t idx, ch
     if (w == 0 && lane < gamma) {
         x = P.tokens[static_cast<int64_t>(g) * gamma + lane];
         if (x >= 0 && x < P.V) {
-            lt = load_one<DT>(group_row<DT, kSample>(P, g, static_cast<uint32_t>(lane)), x);
-            ld = load_one<DT>(group_row<DT, kSample>(P, g, static_cast<uint32_t>(gamma + 1 + lane)), x);
+            lt = load_one<DT>(group_row<DT>(P, g, static_cast<uint32_t>(lane)), x);
+            ld = load_one<DT>(group_row<DT>(P, g, static_cast<uint32_t>(gamma + 1 + lane)), x);
         }
     }
     if (threadIdx.x == 0) s_ok = wait_published(P, g) ? 1 : 0;
@@ -1477,11 +2253,10 @@ __device__ inline void resid_block(const Params& P, uint32_t g, uint32_t idx, ch
     if (in.k >= 0) draw<DT, VEC>(P, g, in, lane);
 }
 
-// --------------------------------------------------------------------------
-// The kernel: one launch per call.
-// --------------------------------------------------------------------------
-template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kBlock) void k_verify(Params P) {
+// The group-major kernel (T > 0): statistics blocks stream whole groups, the
+// group's residual blocks take the accept step and the draw.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_group(Params P) {
     extern __shared__ __align__(16) char dyn[];
     int kind;
     uint32_t g, idx;
@@ -1494,7 +2269,16 @@ __global__ __launch_bounds__(kBlock) void k_verify(Params P) {
         if (threadIdx.x == 0) bp.done = 0u;
         __syncthreads();
         if (w >= nwb) return;
-        const int n = stats_wave<DT, VEC, MODE>(P, g, idx * kWavesPerBlock + w, lane, bp.p[w]);
+        Role U;
+        U.kind = kStatsBlock;
+        U.unit = g;
+        U.i = 0;
+        U.b = static_cast<int32_t>(g);
+        U.r = static_cast<int32_t>(idx);
+        U.rows = P.rps;
+        U.nw = P.nw;
+        U.nb = P.sb;
+        const int n = stats_wave<DT, VEC, kSample, true>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
         // count this wavefront in at the block; the last one writes the block's pieces
         if (lane == 0) bp.n[w] = n;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1503,21 +2287,32 @@ __global__ __launch_bounds__(kBlock) void k_verify(Params P) {
         old = __shfl(old, 0, kWave);
         if (old + 1u != static_cast<uint32_t>(nwb)) return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        write_pieces<MODE>(P, bp, nwb, lane);
-        uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
-        if constexpr (MODE == kSample) {
-            // the residual blocks of g watch this count reach sb
-            complete_before();
-            if (lane == 0) (void)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            if (!arrive_last(cnt, static_cast<uint32_t>(P.sb), lane)) return;
-            if constexpr (MODE == kGreedy) finish_greedy(P, g, lane, dyn);
-            else finish_rows(P, g, lane);
-        }
+        write_pieces<kSample>(P, bp, nwb, lane);
+        // the residual blocks of g watch this count reach sb
+        complete_before();
+        if (lane == 0)
+            (void)__hip_atomic_fetch_add(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        if constexpr (MODE == kSample) resid_block<DT, VEC>(P, g, idx, dyn);
+        group_resid_block<DT, VEC>(P, g, idx, dyn);
     }
 }
+
+// --------------------------------------------------------------------------
+// The kernel: one launch per call.
+// --------------------------------------------------------------------------
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kBlock) void k_verify(Params P) {
+    const Role U = role_of<MODE>(P);
+    if constexpr (MODE == kSample) {
+        if (U.kind == kResidBlock) {
+            resid_block<DT, VEC>(P, U);
+            return;
+        }
+    }
+    stats_block<DT, VEC, MODE>(P, U);
+}
+
 
 // ==========================================================================
 // Host side
@@ -1530,15 +2325,18 @@ int fail(int code, const std::string& msg) {
 }
 
 // Library-owned device memory of one (device, stream). `data` holds the
-// partial slots and residual masses, laid out per call shape. `sync` holds the
-// group counters at fixed addresses (capacity `groups`): it is cleared when
-// allocated and every call leaves its counters at zero again, so calls of any
-// shape can follow one another on it.
+// partial slots and residual block masses, laid out per call shape. `sync`
+// holds the counters, the decision words, the draw records and the error word
+// at fixed addresses: it is cleared when allocated, every call leaves its
+// counters at zero again, and decision words and draw records are told apart
+// by the call's epoch, so calls of any shape can follow one another on it.
 struct Workspace {
     void* data = nullptr;
     size_t bytes = 0;
     uint32_t* sync = nullptr;
-    int64_t groups = 0;
+    int64_t cnt_cap = 0;  // counter words
+    int64_t dec_cap = 0;  // decision words and draw records (64-bit)
+    uint32_t epoch = 0;   // of the last call
 };
 
 std::mutex g_mu;
@@ -1549,9 +2347,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
     Params p;  // geometry filled; pointers added at launch
-    size_t off_pm, off_pr, off_ps, off_pi, off_subr, bytes;
+    bool group;      // the group-major kernel (else the position-major one)
+    int64_t units;
     int64_t blocks;
-    uint32_t lds;
+    uint32_t lds;    // dynamic LDS of the group-major kernel
+    size_t off_pm, off_pr, off_ps, off_pi, off_tok, off_msum, off_subr, bytes;
+    int64_t cnt_words, dec_words;
 };
 
 int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
@@ -1559,51 +2360,114 @@ int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
 // Chunk geometry: vector chunks are 1 KiB; scalar chunks are 64 x 4 elements.
 int32_t chunk_elems(int32_t dtype, bool vec) { return vec ? kWave * (16 / elem_bytes(dtype)) : kWave * 4; }
 
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 // Statistics wavefronts take about kChunksPerWave chunks (many more wavefronts
-// than the chip holds at once, which keeps its tail short), but the whole
-// problem gets at least 16 wavefronts per compute unit so that small problems
-// still spread over the chip. Residual wavefronts take subs_per_wave()
-// subsegments of row k each.
+// than the chip holds at once), but the whole problem gets at least 16
+// wavefronts per compute unit so that small problems still spread over the
+// chip. Residual wavefronts hold kPairCw chunks of each of the two rows.
 Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus) {
     Layout L{};
     Params& p = L.p;
-    const int32_t rps = mode == kSample ? 2 * gamma + 1 : (mode == kGreedy ? gamma + 1 : 1);
-    p.G = static_cast<int32_t>(G);
-    p.rps = rps;
+    p.B = static_cast<int32_t>(G);
     p.gamma = gamma;
     p.V = V;
     const int32_t CH = chunk_elems(dtype, vec);
-    p.nchunk = (V + CH - 1) / CH;
-    const int64_t per_group = static_cast<int64_t>(rps) * p.nchunk;
-    const int64_t total = G * per_group;
+    p.nchunk = static_cast<int32_t>(ceil_div(V, CH));
+    const int64_t rows = mode == kSample ? G * (2 * gamma + 1) : (mode == kGreedy ? G * (gamma + 1) : G);
+    const int64_t total = rows * p.nchunk;
     const int64_t min_waves = static_cast<int64_t>(cus) * 16;
     int64_t cpw = kChunksPerWave;
-    if ((total + cpw - 1) / cpw < min_waves) cpw = (total + min_waves - 1) / min_waves;
+    if (ceil_div(total, cpw) < min_waves) cpw = ceil_div(total, min_waves);
+    if (cpw < 1) cpw = 1;
+    p.cpw = static_cast<int32_t>(cpw);
+    p.maxp = static_cast<int32_t>(ceil_div(p.nchunk, cpw) + 1);
+    p.nw2 = mode == kSample ? static_cast<int32_t>(ceil_div(2 * static_cast<int64_t>(p.nchunk), cpw)) : 0;
+    p.nb2 = static_cast<int32_t>(ceil_div(p.nw2, kWavesPerBlock));
+    p.nw1 = static_cast<int32_t>(ceil_div(p.nchunk, cpw));
+    p.nb1 = static_cast<int32_t>(ceil_div(p.nw1, kWavesPerBlock));
+    p.nbr = mode == kSample ? static_cast<int32_t>(ceil_div(ceil_div(p.nchunk, kPairCw), kWavesPerBlock)) : 0;
+    p.cstride = mode == kRows ? 1 : kSyncStride;
+    L.units = mode == kRows ? G : G * (gamma + 1);
+    L.blocks = mode == kSample ? G * (static_cast<int64_t>(gamma) * p.nb2 + p.nb1 + p.nbr) : L.units * p.nb1;
+    const size_t slots = static_cast<size_t>(L.units) * 2 * p.maxp;
+    size_t o = 0;
+    L.off_pm = o;
+    o = align_up(o + slots * sizeof(float), 256);
+    L.off_pr = o;
+    o = align_up(o + (mode == kGreedy ? 0 : slots) * sizeof(float), 256);
+    L.off_ps = o;
+    o = align_up(o + (mode == kGreedy ? 0 : slots) * sizeof(double), 256);
+    L.off_pi = o;
+    o = align_up(o + (mode == kGreedy ? slots : 0) * sizeof(int32_t), 256);
+    L.off_tok = o;
+    o = align_up(o + (mode == kSample ? static_cast<size_t>(L.units) * 2 : 0) * sizeof(float), 256);
+    L.off_msum = o;
+    o = align_up(o + static_cast<size_t>(G) * p.nbr * kWavesPerBlock * sizeof(double), 256);
+    L.bytes = o;
+    L.cnt_words = L.units * p.cstride;
+    L.dec_words = mode == kRows ? 0 : G * (gamma + 1) + (mode == kSample ? G * kRecWords : 0);
+    return L;
+}
+
+// Group-major layout (T > 0): a group is one sequence's 2*gamma+1 rows, its
+// statistics wavefronts take about kChunksPerWave chunks each (at least 16
+// wavefronts per compute unit over the whole problem), and its residual
+// wavefronts take subs_per_wave() subsegments of row k each.
+Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus) {
+    Layout L{};
+    Params& p = L.p;
+    L.group = true;
+    p.B = static_cast<int32_t>(G);
+    p.gamma = gamma;
+    p.V = V;
+    p.rps = 2 * gamma + 1;
+    const int32_t CH = chunk_elems(dtype, vec);
+    p.nchunk = static_cast<int32_t>(ceil_div(V, CH));
+    const int64_t per_group = static_cast<int64_t>(p.rps) * p.nchunk;
+    const int64_t min_waves = static_cast<int64_t>(cus) * 16;
+    int64_t cpw = kChunksPerWave;
+    if (ceil_div(G * per_group, cpw) < min_waves) cpw = ceil_div(G * per_group, min_waves);
     if (cpw > static_cast<int64_t>(kMaxPieces - 1) * p.nchunk) cpw = static_cast<int64_t>(kMaxPieces - 1) * p.nchunk;
     if (cpw < 1) cpw = 1;
     p.cpw = static_cast<int32_t>(cpw);
-    p.nw = static_cast<int32_t>((per_group + cpw - 1) / cpw);
-    p.sb = (p.nw + kWavesPerBlock - 1) / kWavesPerBlock;
-    p.maxp = static_cast<int32_t>((p.nchunk + cpw - 1) / cpw + 1);
-    p.nsub = static_cast<int32_t>((static_cast<int64_t>(V) + kSub - 1) / kSub);
+    p.nw = static_cast<int32_t>(ceil_div(per_group, cpw));
+    p.sb = static_cast<int32_t>(ceil_div(p.nw, kWavesPerBlock));
+    p.maxp = static_cast<int32_t>(ceil_div(p.nchunk, cpw) + 1);
+    p.nsub = static_cast<int32_t>(ceil_div(V, kSub));
     const int spw = vec ? (dtype == SPEC_BF16 ? subs_per_wave<SPEC_BF16, true>() : subs_per_wave<SPEC_F32, true>())
                         : subs_per_wave<SPEC_F32, false>();
-    p.rb = mode == kSample ? (p.nsub + kWavesPerBlock * spw - 1) / (kWavesPerBlock * spw) : 0;
-    p.lag = p.rb > 0 ? static_cast<int32_t>(G < kLag ? G : kLag) : 0;
-    const int64_t gslots = static_cast<int64_t>(rps) * p.maxp;
-    p.stage = mode != kRows && gslots <= kMaxStage ? static_cast<int32_t>(gslots) : 0;
+    p.rb = static_cast<int32_t>(ceil_div(p.nsub, kWavesPerBlock * spw));
+    p.lag = static_cast<int32_t>(G < kLag ? G : kLag);
+    p.cstride = kSyncStride;
+    const int64_t gslots = static_cast<int64_t>(p.rps) * p.maxp;
+    p.stage = gslots <= kMaxStage ? static_cast<int32_t>(gslots) : 0;
+    L.units = G;
     L.blocks = G * (p.sb + p.rb);
     L.lds = static_cast<uint32_t>(p.stage) * 20u;
     const size_t slots = static_cast<size_t>(G) * gslots;
-    const size_t subs = mode == kSample ? static_cast<size_t>(G) * p.nsub : 0;
     size_t o = 0;
-    L.off_pm = o; o = align_up(o + slots * sizeof(float), 256);
-    L.off_pr = o; o = align_up(o + (mode == kGreedy ? 0 : slots) * sizeof(float), 256);
-    L.off_ps = o; o = align_up(o + (mode == kGreedy ? 0 : slots) * sizeof(double), 256);
-    L.off_pi = o; o = align_up(o + (mode == kGreedy ? slots : 0) * sizeof(int32_t), 256);
-    L.off_subr = o; o = align_up(o + subs * sizeof(double), 256);
+    L.off_pm = o;
+    o = align_up(o + slots * sizeof(float), 256);
+    L.off_pr = o;
+    o = align_up(o + slots * sizeof(float), 256);
+    L.off_ps = o;
+    o = align_up(o + slots * sizeof(double), 256);
+    L.off_pi = L.off_tok = L.off_msum = o;
+    L.off_subr = o;
+    o = align_up(o + static_cast<size_t>(G) * p.nsub * sizeof(double), 256);
     L.bytes = o;
+    L.cnt_words = 2 * G * kSyncStride;
+    L.dec_words = 0;
     return L;
+}
+
+// The automatic schedule at T > 0: position-major with the early stop once
+// one position's row-pair blocks fill the chip (four per compute unit; below
+// that, decisions lag too many positions behind the stream to save reads),
+// else group-major. L is the position-major layout.
+bool auto_position_major(int64_t B, const Layout& L, int cus) {
+    return B * L.p.nb2 >= 4 * static_cast<int64_t>(cus);
 }
 
 int compute_units(int dev) {
@@ -1615,19 +2479,24 @@ int compute_units(int dev) {
     return n;
 }
 
-// Caller holds g_mu. Grows the buffers of (dev, stream) to `bytes` of data and
-// `groups` groups of counters; a new sync buffer is cleared on the stream.
-int get_workspace(int dev, hipStream_t stream, size_t bytes, int64_t groups, Workspace** out) {
+size_t sync_bytes(int64_t cnt_words, int64_t dec_words) {
+    return align_up(static_cast<size_t>(cnt_words) * sizeof(uint32_t), 256) +
+           static_cast<size_t>(dec_words) * sizeof(uint64_t) + 256;
+}
+
+// Caller holds g_mu. Grows the buffers of (dev, stream) to fit L (a new sync
+// buffer is cleared on the stream) and advances the epoch.
+int get_workspace(int dev, hipStream_t stream, const Layout& L, Workspace** out) {
     Workspace& ws = g_ws[std::make_pair(dev, static_cast<void*>(stream))];
-    if (ws.bytes < bytes || ws.groups < groups) {
-        if (ws.data || ws.sync)
-            if (hipStreamSynchronize(stream) != hipSuccess) return fail(SPEC_EHIP, "hipStreamSynchronize failed");
-    }
-    if (ws.bytes < bytes) {
+    const bool grow_data = ws.bytes < L.bytes;
+    const bool grow_sync = ws.cnt_cap < L.cnt_words || ws.dec_cap < L.dec_words;
+    if ((grow_data && ws.data) || (grow_sync && ws.sync))
+        if (hipStreamSynchronize(stream) != hipSuccess) return fail(SPEC_EHIP, "hipStreamSynchronize failed");
+    if (grow_data) {
         if (ws.data) (void)hipFree(ws.data);
         ws.data = nullptr;
         ws.bytes = 0;
-        const size_t want = align_up(bytes + bytes / 4, 1 << 20);
+        const size_t want = align_up(L.bytes + L.bytes / 4, 1 << 20);
         if (hipMalloc(&ws.data, want) != hipSuccess) {
             ws.data = nullptr;
             (void)hipGetLastError();
@@ -1635,40 +2504,57 @@ int get_workspace(int dev, hipStream_t stream, size_t bytes, int64_t groups, Wor
         }
         ws.bytes = want;
     }
-    if (ws.groups < groups) {
+    if (grow_sync) {
         if (ws.sync) (void)hipFree(ws.sync);
         ws.sync = nullptr;
-        ws.groups = 0;
-        const int64_t want = static_cast<int64_t>(align_up(static_cast<size_t>(groups + groups / 4), 1024));
-        const size_t sbytes = (2 * static_cast<size_t>(want) * kSyncStride + 64) * sizeof(uint32_t);
-        if (hipMalloc(reinterpret_cast<void**>(&ws.sync), sbytes) != hipSuccess) {
+        ws.cnt_cap = ws.dec_cap = 0;
+        const int64_t cw = std::max<int64_t>(L.cnt_words + L.cnt_words / 4, 1024);
+        const int64_t dw = std::max<int64_t>(L.dec_words + L.dec_words / 4, 1024);
+        const size_t sb = sync_bytes(cw, dw);
+        if (hipMalloc(reinterpret_cast<void**>(&ws.sync), sb) != hipSuccess) {
             ws.sync = nullptr;
             (void)hipGetLastError();
             return fail(SPEC_ENOMEM, "hipMalloc of the workspace failed");
         }
-        if (hipMemsetAsync(ws.sync, 0, sbytes, stream) != hipSuccess) {
+        if (hipMemsetAsync(ws.sync, 0, sb, stream) != hipSuccess) {
             (void)hipFree(ws.sync);
             ws.sync = nullptr;
             return fail(SPEC_EHIP, "hipMemsetAsync of the workspace failed");
         }
-        ws.groups = want;
+        ws.cnt_cap = cw;
+        ws.dec_cap = dw;
+        ws.epoch = 0;
+    }
+    if (++ws.epoch == 0) {
+        // 2^32 calls on this workspace: clear the decision words before the tag repeats
+        char* dec = reinterpret_cast<char*>(ws.sync) + align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256);
+        if (hipMemsetAsync(dec, 0, static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t), stream) != hipSuccess)
+            return fail(SPEC_EHIP, "hipMemsetAsync of the workspace failed");
+        ws.epoch = 1;
     }
     *out = &ws;
     return SPEC_OK;
 }
 
-void bind_workspace(Layout& L, Workspace& ws) {
+void bind_workspace(Layout& L, const Workspace& ws) {
     char* base = static_cast<char*>(ws.data);
     Params& p = L.p;
     p.part_m = reinterpret_cast<float*>(base + L.off_pm);
     p.part_r = reinterpret_cast<float*>(base + L.off_pr);
     p.part_s = reinterpret_cast<double*>(base + L.off_ps);
     p.part_i = reinterpret_cast<int32_t*>(base + L.off_pi);
+    p.tok_l = reinterpret_cast<float*>(base + L.off_tok);
+    p.msum = reinterpret_cast<double*>(base + L.off_msum);
     p.sub_r = reinterpret_cast<double*>(base + L.off_subr);
-    const int64_t words = ws.groups * kSyncStride;
     p.cnt_s = ws.sync;
-    p.cnt_r = ws.sync + words;
-    p.err = ws.sync + 2 * words;
+    p.cnt_r = ws.sync + static_cast<int64_t>(p.B) * kSyncStride;
+    char* s = reinterpret_cast<char*>(ws.sync);
+    p.cnt = ws.sync;
+    const size_t off_dec = align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256);
+    p.dec = reinterpret_cast<uint64_t*>(s + off_dec);
+    p.rec = p.dec + static_cast<int64_t>(p.B) * (p.gamma + 1);
+    p.err = reinterpret_cast<uint32_t*>(s + off_dec + static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t));
+    p.epoch = ws.epoch;
 }
 
 // Timing events, when given, are bound to the kernel dispatch itself (its
@@ -1676,12 +2562,14 @@ void bind_workspace(Layout& L, Workspace& ws) {
 template <int DT, bool VEC>
 void launch_t(int mode, const Layout& L, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid(static_cast<unsigned>(L.blocks)), block(kBlock);
-    if (mode == kSample)
-        hipExtLaunchKernelGGL((k_verify<DT, VEC, kSample>), grid, block, L.lds, st, e0, e1, 0, L.p);
+    if (L.group)
+        hipExtLaunchKernelGGL((k_group<DT, VEC>), grid, block, L.lds, st, e0, e1, 0, L.p);
+    else if (mode == kSample)
+        hipExtLaunchKernelGGL((k_verify<DT, VEC, kSample>), grid, block, 0, st, e0, e1, 0, L.p);
     else if (mode == kGreedy)
-        hipExtLaunchKernelGGL((k_verify<DT, VEC, kGreedy>), grid, block, L.lds, st, e0, e1, 0, L.p);
+        hipExtLaunchKernelGGL((k_verify<DT, VEC, kGreedy>), grid, block, 0, st, e0, e1, 0, L.p);
     else
-        hipExtLaunchKernelGGL((k_verify<DT, VEC, kRows>), grid, block, L.lds, st, e0, e1, 0, L.p);
+        hipExtLaunchKernelGGL((k_verify<DT, VEC, kRows>), grid, block, 0, st, e0, e1, 0, L.p);
 }
 
 void launch(int32_t dtype, bool vec, int mode, const Layout& L, hipStream_t st, hipEvent_t e0 = nullptr,
@@ -1707,9 +2595,9 @@ int check_launch(const char* what) {
 
 // Size limits: chunk counts are 32-bit on the device, and a dispatch holds
 // fewer than 2^32 work-items.
-int check_size(const Layout& L) {
-    const int64_t chunks = static_cast<int64_t>(L.p.G) * L.p.rps * L.p.nchunk;
-    if (chunks >= (int64_t(1) << 31) || L.blocks * kBlock >= (int64_t(1) << 32) || L.blocks < 1)
+int check_size(int, const Layout& L) {
+    const int64_t chunks = L.units * (L.group ? L.p.rps : 2) * static_cast<int64_t>(L.p.nchunk);
+    if (chunks >= (int64_t(1) << 31) || L.blocks < 1 || L.blocks * kBlock >= (int64_t(1) << 32))
         return fail(SPEC_EINVAL, "problem too large");
     return SPEC_OK;
 }
@@ -1721,19 +2609,36 @@ int check_size(const Layout& L) {
 // ==========================================================================
 extern "C" {
 
-int32_t spec_verify_abi_version(void) { return 1; }
+int32_t spec_verify_abi_version(void) { return 2; }
 
 const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
+
+int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature) {
+    if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || (dtype != SPEC_F32 && dtype != SPEC_BF16) ||
+        !(temperature >= 0.0f))
+        return fail(SPEC_EINVAL, "bad shape, dtype or temperature");
+    if (temperature == 0.0f) return SPEC_SCHEDULE_EARLY_STOP;
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lk(g_mu);
+    const int cus = compute_units(dev);
+    const Layout L = plan(kSample, B, gamma, V, dtype, vec, cus);
+    return auto_position_major(B, L, cus) ? SPEC_SCHEDULE_EARLY_STOP : SPEC_SCHEDULE_GROUP;
+}
 
 size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature) {
     if (B < 1 || gamma < 1 || gamma > SPEC_MAX_GAMMA || V < 1 || (dtype != SPEC_F32 && dtype != SPEC_BF16))
         return 0;
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0;
     std::lock_guard<std::mutex> lk(g_mu);
-    const Layout L = plan(temperature == 0.0f ? kGreedy : kSample, B, gamma, V, dtype, vec, compute_units(dev));
-    return L.bytes + (2 * static_cast<size_t>(B) * kSyncStride + 64) * sizeof(uint32_t);
+    const int cus = compute_units(dev);
+    const Layout Lp = plan(temperature == 0.0f ? kGreedy : kSample, B, gamma, V, dtype, vec, cus);
+    if (temperature == 0.0f) return Lp.bytes + sync_bytes(Lp.cnt_words, Lp.dec_words);
+    const Layout Lg = plan_group(B, gamma, V, dtype, vec, cus);
+    return std::max(Lp.bytes, Lg.bytes) + sync_bytes(std::max(Lp.cnt_words, Lg.cnt_words), Lp.dec_words);
 }
 
 void spec_verify_release_workspace(void) {
@@ -1769,16 +2674,34 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
         return fail(SPEC_EINVAL, "temperature too small or too large for fp32 exponent scaling");
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
                      (greedy || aligned16(draft_logits));
+    const int mode = greedy ? kGreedy : kSample;
+    const int32_t sched = extras ? extras->schedule : SPEC_SCHEDULE_AUTO;
+    if (sched < SPEC_SCHEDULE_AUTO || sched > SPEC_SCHEDULE_POSITION)
+        return fail(SPEC_EINVAL, "extras->schedule must be one of the spec_schedule_t values");
+    const bool per_row = extras && (extras->row_max || extras->row_sumexp || extras->p_draft || extras->q_draft ||
+                                    extras->argmax);
+    // the size limits do not depend on the device: checked before any HIP call
+    if (int rc = check_size(mode, plan(mode, B, gamma, V, dtype, vec, 1))) return rc;
+    if (!greedy) {
+        if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1))) return rc;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
-    const int mode = greedy ? kGreedy : kSample;
 
     std::lock_guard<std::mutex> lk(g_mu);
-    Layout L = plan(mode, B, gamma, V, dtype, vec, compute_units(dev));
-    if (int rc = check_size(L)) return rc;
+    const int cus = compute_units(dev);
+    Layout L = plan(mode, B, gamma, V, dtype, vec, cus);
+    bool early = true;
+    if (!greedy) {
+        // auto: position-major with the early stop once one position's units
+        // fill the chip (about four blocks per compute unit), else group-major
+        const bool pos = sched == SPEC_SCHEDULE_AUTO ? auto_position_major(B, L, cus) : sched != SPEC_SCHEDULE_GROUP;
+        if (!pos) L = plan_group(B, gamma, V, dtype, vec, cus);
+        early = sched != SPEC_SCHEDULE_POSITION;
+    }
     Workspace* ws = nullptr;
-    if (int rc = get_workspace(dev, st, L.bytes, L.p.G, &ws)) return rc;
+    if (int rc = get_workspace(dev, st, L, &ws)) return rc;
     bind_workspace(L, *ws);
     Params& p = L.p;
     p.c32 = c32;
@@ -1789,6 +2712,8 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     p.tokens = draft_tokens;
     p.out_tokens = out_tokens;
     p.out_n = out_n_accepted;
+    // per-row values are wanted for every row: then every row is read
+    p.skip = early && !per_row ? 1 : 0;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (extras) {
         p.dbg_row_max = extras->row_max;
@@ -1821,14 +2746,14 @@ int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype, f
     const float c32 = fold_temperature(temperature);
     if (!(std::isfinite(c32) && c32 > 0.0f)) return fail(SPEC_EINVAL, "temperature out of range");
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(logits);
+    if (int rc = check_size(kRows, plan(kRows, rows, 1, V, dtype, vec, 1))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
     Layout L = plan(kRows, rows, 1, V, dtype, vec, compute_units(dev));
-    if (int rc = check_size(L)) return rc;
     Workspace* ws = nullptr;
-    if (int rc = get_workspace(dev, st, L.bytes, L.p.G, &ws)) return rc;
+    if (int rc = get_workspace(dev, st, L, &ws)) return rc;
     bind_workspace(L, *ws);
     L.p.c32 = c32;
     L.p.tgt = logits;

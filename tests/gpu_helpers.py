@@ -19,8 +19,9 @@ class GpuRun:
     pass
 
 
-def run(inp, seed, b_offset=0, tensors=None, stream=None):
-    """Run spec_verify_ex on `inp`; return numpy outputs and debug values."""
+def run(inp, seed, b_offset=0, tensors=None, stream=None, schedule=0):
+    """Run spec_verify_ex on `inp` with every debug output (so every row is
+    read) and the given schedule; return numpy outputs and debug values."""
     wl = inp.wl
     B, g, V = wl.B, wl.gamma, wl.V
     dev = torch.device("cuda:0")
@@ -45,6 +46,7 @@ def run(inp, seed, b_offset=0, tensors=None, stream=None):
     ex.Z = Z.data_ptr()
     ex.argmax = am.data_ptr()
     ex.b_offset = b_offset
+    ex.schedule = schedule
     out_t, out_n = sv.verify(tgt, dft, tok, wl.T, seed, extras=ex, stream=stream)
     torch.cuda.synchronize()
     r = GpuRun()

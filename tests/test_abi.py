@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = sv.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_verify_abi_version() == 1
+    assert lib.spec_verify_abi_version() == 2
 
 
 def _call(B=2, gamma=3, V=10, dtype=0, T=1.0, tgt=1, dft=1, tok=1, out_t=1, out_n=1):
@@ -60,3 +60,12 @@ def test_row_stats_argument_checks():
     assert lib.spec_row_stats(None, 4, 10, 0, 1.0, None, None, None) == sv.SPEC_EINVAL
     assert lib.spec_row_stats(ctypes.c_void_p(1), 4, 10, 5, 1.0, ctypes.c_void_p(1), ctypes.c_void_p(1), None) == sv.SPEC_EDTYPE
     assert lib.spec_row_stats(ctypes.c_void_p(1), 4, 10, 0, 0.0, ctypes.c_void_p(1), ctypes.c_void_p(1), None) == sv.SPEC_EINVAL
+
+
+def test_schedule_out_of_range_is_rejected():
+    ex = sv.Extras()
+    ex.schedule = 7
+    P = ctypes.c_void_p
+    rc = sv.load_library().spec_verify_ex(P(1), P(1), P(1), 2, 3, 10, 0, 1.0, 0, P(1), P(1), None, ctypes.byref(ex))
+    assert rc == sv.SPEC_EINVAL
+    assert "schedule" in sv.last_error()

@@ -44,8 +44,12 @@ def check_values(inp, orc, gpu):
     assert np.abs(gpu.Z[small] - orc.Z[small]).max(initial=0) <= 1e-8
 
 
-def parity(inp, seed, b_offset=0, report=None):
-    gpu = G.run(inp, seed, b_offset=b_offset)
+# the two grid orders of the T > 0 kernel (T == 0 has one)
+SCHEDULES = [sv.SCHEDULE_GROUP, sv.SCHEDULE_POSITION] if torch.cuda.is_available() else []
+
+
+def parity(inp, seed, b_offset=0, report=None, schedule=0):
+    gpu = G.run(inp, seed, b_offset=b_offset, schedule=schedule)
     wl = inp.wl
     orc = oracle.verify(inp.target, inp.draft if wl.T > 0 else None, inp.tokens, wl.dtype, wl.T,
                         seed, b_offset=b_offset)
@@ -70,18 +74,21 @@ POOL_SEEDS = {
 }
 
 
+@pytest.mark.parametrize("schedule", [1, 3])
 @pytest.mark.parametrize("name", list(POOL_SEEDS))
-def test_workload_parity_pooled(name):
+def test_workload_parity_pooled(name, schedule):
     """Several seeds per workload at a batch the oracle finishes quickly; the
-    near-boundary count is pooled over the seeds."""
+    near-boundary count is pooled over the seeds. Both grid orders."""
     seeds, B = POOL_SEEDS[name]
     wl = W.WORKLOADS[name]
     if B is not None:
         wl = wl.scaled(B=B)
+    if wl.T == 0.0 and schedule == 1:
+        pytest.skip("T == 0 has one schedule")
     rep = TokenReport()
     for s in seeds:
         inp = W.make_inputs(wl, s)
-        parity(inp, seed=1000 + s, report=rep)
+        parity(inp, seed=1000 + s, report=rep, schedule=schedule)
     print(name, rep)
     assert rep.ok(), str(rep)
 
@@ -110,14 +117,17 @@ EDGE_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("schedule", [1, 3])
 @pytest.mark.parametrize("shape", EDGE_SHAPES)
 @pytest.mark.parametrize("T", [0.0, 0.6, 1.7])
-def test_edge_shapes(shape, T):
+def test_edge_shapes(shape, T, schedule):
     B, g, V, dt = shape
+    if T == 0.0 and schedule == 1:
+        pytest.skip("T == 0 has one schedule")
     rep = TokenReport()
     for s in range(3):
         inp = W.small_random_inputs(B, g, V, dt, T, seed=100 + s)
-        parity(inp, seed=s, report=rep)
+        parity(inp, seed=s, report=rep, schedule=schedule)
     assert rep.mismatches <= 1, str(rep)
 
 
@@ -271,3 +281,38 @@ def test_workspace_reuse_across_shapes_and_modes():
         for r in range(7):
             ok, _, om, oS = oracle.row_softmax(logits[r], W.BF16, 0.9)
             assert ok and m[r] == om and abs(s[r] - oS) <= 1e-5 * oS
+
+
+@pytest.mark.parametrize("name", list(POOL_SEEDS))
+def test_schedules_give_the_same_outputs(name):
+    """Every schedule - group-major, position-major reading every row, and the
+    early stop, which skips the rows of sequences already known to have
+    stopped - returns exactly the same tokens and counts (and the oracle's)."""
+    seeds, B = POOL_SEEDS[name]
+    wl = W.WORKLOADS[name]
+    if B is not None:
+        wl = wl.scaled(B=B)
+    for s in list(seeds)[:3]:
+        inp = W.make_inputs(wl, s)
+        full = G.run(inp, 1000 + s, schedule=sv.SCHEDULE_POSITION)
+        tgt, dft = G.to_device(inp.target, wl.dtype), G.to_device(inp.draft, wl.dtype)
+        tok = torch.from_numpy(inp.tokens).to("cuda:0")
+        for sched in (sv.SCHEDULE_AUTO, sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION):
+            ex = sv.Extras()
+            ex.schedule = sched
+            for rep_call in range(2):
+                out_t, out_n = sv.verify(tgt, dft if wl.T > 0 else None, tok, wl.T, 1000 + s, extras=ex)
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(out_n.cpu().numpy(), full.n)
+                np.testing.assert_array_equal(out_t.cpu().numpy(), full.tokens)
+        orc = oracle.verify(inp.target, inp.draft if wl.T > 0 else None, inp.tokens, wl.dtype, wl.T, 1000 + s)
+        rep = compare_tokens(inp, orc, full.tokens, full.n, 1000 + s)
+        assert not rep.hard_fail, rep.hard_fail[:5]
+
+
+def test_auto_schedule_rule():
+    """The automatic choice: group-major for the B=64 headline shape, the early
+    stop once one position's blocks fill the chip (the B=256 shape)."""
+    assert sv.auto_schedule(64, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP
+    assert sv.auto_schedule(256, 8, 152064, sv.SPEC_BF16, 0.7) == sv.SCHEDULE_EARLY_STOP
+    assert sv.auto_schedule(32, 8, 128256, sv.SPEC_F32, 0.0) == sv.SCHEDULE_EARLY_STOP
