@@ -40,17 +40,17 @@ KERNEL_SRC = os.path.join(ROOT, "speculative_sampling_verification_05_amd", "csr
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def measured_traffic(workload):
+def measured_traffic(kernel, workload):
     """HBM bytes per launch of the verification kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy's counts),
-    or None if they were taken on another workload or another kernel source."""
+    or None if they were taken on another kernel source."""
     import hashlib
     try:
-        rec = json.load(open(TRAFFIC_FILE))["k_verify"]
+        rec = json.load(open(TRAFFIC_FILE))[f"{kernel}@{workload}"]
         sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sha:
         return None
     return rec["traffic_bytes"]
 
@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--event-stride", type=int, default=16,
                     help="time the kernels of every N-th step of the timed region with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--auto-only", action="store_true",
+                    help="time the automatic schedule only (no per-schedule legs; for counter runs)")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the oracle sample (0: auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, run --steps plain device-to-device copies of the "
@@ -267,6 +269,7 @@ def main():
         return [compulsory for _ in steps]
 
     auto = sv.auto_schedule(B, g, V, dtc, wl.T)
+    kname = "k_group" if auto == sv.SCHEDULE_GROUP else "k_verify"
     names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position"}
     k_bytes = algo_bytes(auto, evd)
     rows_per_step = B * g
@@ -275,8 +278,9 @@ def main():
     achieved = float(np.sum(k_bytes)) / (float(np.sum(k_ms)) * 1e-3) / 1e9
 
     schedules = {}
-    for sched in ((sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION) if wl.T == 0.0 else
-                  (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION)):
+    legs = () if args.auto_only else ((sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION) if wl.T == 0.0 else
+                                      (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION))
+    for sched in legs:
         ms_s, km_s, ev_s = timed(with_schedule(sched))
         a_s = float(np.sum(algo_bytes(sched, ev_s))) / (float(np.sum(km_s)) * 1e-3) / 1e9
         schedules[names[sched]] = {"ms_per_step": ms_s, "kernel_us": float(np.mean(km_s)) * 1e3,
@@ -313,9 +317,9 @@ def main():
         "accepted_hist": n_hist,
         "needed_bytes_per_set": set_bytes,
         "compulsory_bytes": compulsory,
-        "roofline": {"bound": "hbm", "kernel": "k_verify" if auto != sv.SCHEDULE_GROUP else "k_group",
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name),
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(kname, wl.name),
                      "bytes_per_launch": float(np.mean(k_bytes)), "avg_launch_us": k_avg_ms * 1e3,
                      "launches_timed": len(k_ms)},
         "schedules": schedules,
