@@ -95,12 +95,22 @@ def test_workload_parity_pooled(name, schedule):
 
 @pytest.mark.parametrize("name", ["greedy_b32_g8_v128256_f32", "zipf_b256_g8_v152064_bf16"])
 def test_full_size_parity(name):
-    """The full workload in the launch configuration the benchmark times."""
+    """The full workload: every row's values against the oracle (the debug
+    outputs read every row), and the call the benchmark times (the automatic
+    schedule, no extras: the early stop at these sizes) returning exactly the
+    same tokens."""
     wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl, 0)
-    _, _, rep = parity(inp, seed=0)
+    gpu, _, rep = parity(inp, seed=0)
     print(name, rep)
     assert rep.mismatches <= max(1, int(1e-3 * rep.draws)), str(rep)
+    assert sv.auto_schedule(wl.B, wl.gamma, wl.V, wl.dtype, wl.T) == sv.SCHEDULE_EARLY_STOP
+    tgt, dft = G.to_device(inp.target, wl.dtype), G.to_device(inp.draft, wl.dtype)
+    tok = torch.from_numpy(inp.tokens).to("cuda:0")
+    out_t, out_n = sv.verify(tgt, dft if wl.T > 0 else None, tok, wl.T, 0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out_n.cpu().numpy(), gpu.n)
+    np.testing.assert_array_equal(out_t.cpu().numpy(), gpu.tokens)
 
 
 EDGE_SHAPES = [
