@@ -16,7 +16,7 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
-ACCEPT, SAMPLE = 0, 1
+ACCEPT, SAMPLE, DRAFT = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -66,6 +66,9 @@ def lib():
         L.orc_verify.argtypes = [vp, vp, vp, i32, i32, i64, ctypes.c_int, f64, u64, i64,
                                  vp, vp, ctypes.POINTER(_Diag)]
         L.orc_verify.restype = ctypes.c_int
+        L.orc_draft_sample.argtypes = [vp, i32, i32, i64, ctypes.c_int, f64, u64, i64, i64, vp, vp,
+                                       vp, vp]
+        L.orc_draft_sample.restype = ctypes.c_int
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
@@ -186,6 +189,31 @@ def verify_u(target, draft, tokens, dtype, T, u_accept, u_sample, diag=True):
     rc = lib().orc_verify_u(_ptr(target), _ptr(draft), _ptr(tokens), B, g, V, dtype, float(T),
                             _ptr(ua), _ptr(us), _ptr(res.tokens), _ptr(res.n),
                             ctypes.byref(d) if d is not None else None)
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return res
+
+
+class DraftResult:
+    """Draft-side sampling outputs of one oracle call, each [B, n]."""
+
+    def __init__(self, B, n):
+        self.tokens = np.full((B, n), -7, np.int32)
+        self.q = np.full((B, n), np.nan)
+        self.cdf_lo = np.full((B, n), np.nan)
+        self.cdf_hi = np.full((B, n), np.nan)
+
+
+def draft_sample(logits, dtype, T, seed=0, pos0=0, b_offset=0):
+    """Draft tokens drawn from softmax(logits / T) (argmax at T == 0) for
+    logits [B, n, V] in storage form; row (b, t) draws with the DRAFT uniform
+    of counter (b + b_offset, pos0 + t)."""
+    logits = _storage(logits, dtype)
+    B, n, V = logits.shape
+    res = DraftResult(B, n)
+    rc = lib().orc_draft_sample(_ptr(logits), B, n, V, dtype, float(T), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                int(pos0), int(b_offset), _ptr(res.tokens), _ptr(res.q),
+                                _ptr(res.cdf_lo), _ptr(res.cdf_hi))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return res

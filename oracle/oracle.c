@@ -12,6 +12,8 @@
  *  - accept test and early stop: [Ch15] 15.1.2 step 3; [CSDN] 2.1 (r < alpha).
  *  - correction draw from max(0, p - q)/Z: [Ch15] 15.1.2 step 4; [CSDN] 2.1.
  *  - bonus draw from the last target row after full acceptance: [HSD] 3.3.
+ *  - draft-side sampling (the step before verification): [Ch15] 15.1.2 step 1
+ *    (draw from q, keep q of the drawn token); [CSDN] 2.1 stage 1.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - accept iff u < alpha with u on the 2^-53 grid in [0, 1) ([CSDN] uses
@@ -346,6 +348,58 @@ int orc_verify(const void* target, const void* draft, const int32_t* tokens,
     free(ua);
     free(us);
     return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Draft-side sampling ([Ch15] 15.1.2 step 1; [CSDN] 2.1 stage 1)              */
+/* ------------------------------------------------------------------------- */
+static void draft_one(const void* row, int64_t V, int dtype, double T, double u,
+                      int32_t* tok, double* q, double* lo, double* hi) {
+    *tok = -1;
+    *q = NAN;
+    *lo = NAN;
+    *hi = NAN;
+    if (T == 0.0) {
+        int64_t a;
+        if (argmax_row(row, dtype, V, &a)) {
+            *tok = (int32_t)a;
+            *q = 1.0;
+        }
+        return;
+    }
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    double* cdf = (double*)malloc(sizeof(double) * (size_t)V);
+    if (orc_row_softmax(row, dtype, V, T, p, NULL, NULL)) {
+        double Z;
+        int64_t j = draw_from(p, V, u, cdf, &Z);
+        *tok = (int32_t)j;
+        *q = p[j];
+        *lo = (j > 0 ? cdf[j - 1] : 0.0) / Z;
+        *hi = cdf[j] / Z;
+    }
+    free(p);
+    free(cdf);
+}
+
+int orc_draft_sample(const void* logits, int32_t B, int32_t n, int64_t V, int dtype, double T,
+                     uint64_t seed, int64_t pos0, int64_t b_offset, int32_t* out_tokens,
+                     double* out_q, double* cdf_lo, double* cdf_hi) {
+    if (!logits || !out_tokens) return -1;
+    if (B < 0 || n < 1 || V < 1 || pos0 < 0 || (dtype != ORC_F32 && dtype != ORC_BF16)) return -1;
+    if (!(T >= 0.0)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < (int64_t)B * n; ++r) {
+        const int64_t b = r / n, t = r % n;
+        const double u = T > 0.0 ? orc_uniform(seed, (uint32_t)(b + b_offset), (uint32_t)(pos0 + t),
+                                                ORC_PURPOSE_DRAFT)
+                                 : 0.0;
+        double q, lo, hi;
+        draft_one(row_ptr(logits, dtype, r, V), V, dtype, T, u, out_tokens + r, &q, &lo, &hi);
+        if (out_q) out_q[r] = q;
+        if (cdf_lo) cdf_lo[r] = lo;
+        if (cdf_hi) cdf_hi[r] = hi;
+    }
+    return 0;
 }
 
 int orc_max_threads(void) {

@@ -28,7 +28,7 @@ extern "C" {
 #endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
-enum { ORC_PURPOSE_ACCEPT = 0, ORC_PURPOSE_SAMPLE = 1 };
+enum { ORC_PURPOSE_ACCEPT = 0, ORC_PURPOSE_SAMPLE = 1, ORC_PURPOSE_DRAFT = 2 };
 
 /* Philox4x32-10 block function: out = Philox(counter, key). */
 void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
@@ -89,6 +89,22 @@ int orc_verify_u(const void* target, const void* draft, const int32_t* tokens,
 int orc_verify(const void* target, const void* draft, const int32_t* tokens,
                int32_t B, int32_t gamma, int64_t V, int dtype, double T, uint64_t seed,
                int64_t b_offset, int32_t* out_tokens, int32_t* out_n, const orc_diag_t* diag);
+
+/* Draft-side sampling, the step before verification ([Ch15] 15.1.2 step 1:
+ * draw each draft token from the draft distribution and keep its probability;
+ * [CSDN] 2.1, stage 1 of speculative_decode()). Row (b, t) of logits
+ * [B, n, V] (positions pos0 .. pos0 + n - 1 of sequence b):
+ *   T > 0:  x = smallest j with C_j > u * Z, C the ascending cumulative sum of
+ *           p = softmax(l / T) and Z its total, with
+ *           u = orc_uniform(seed, b + b_offset, pos0 + t, DRAFT); q = p_x;
+ *   T == 0: x = argmax_j l_j (lowest index on ties), q = 1;
+ *   a row with NaN, +inf or no finite entry: x = -1, q = NaN.
+ * out_q, cdf_lo, cdf_hi may be NULL; cdf_lo/cdf_hi receive the normalised
+ * cumulative mass just below x and at x (NaN at T == 0 or for unusable rows).
+ * Returns 0, or -1 on bad arguments. */
+int orc_draft_sample(const void* logits, int32_t B, int32_t n, int64_t V, int dtype, double T,
+                     uint64_t seed, int64_t pos0, int64_t b_offset, int32_t* out_tokens,
+                     double* out_q, double* cdf_lo, double* cdf_hi);
 
 /* Threads the OpenMP runtime will use (1 when built without OpenMP). */
 int orc_max_threads(void);

@@ -29,6 +29,10 @@ MUTANTS = {
                                    "us[b * (gamma + 1) + k] = orc_uniform(seed, gb, (uint32_t)k, ORC_PURPOSE_ACCEPT);"),
     "no_early_stop": ("            k = i;\n            break;\n        }\n    }\n    if (k == gamma && !usable[gamma])",
                       "            if (k == gamma) k = i;\n        }\n    }\n    if (k == gamma && !usable[gamma])"),
+    "draft_purpose": ("ORC_PURPOSE_DRAFT)\n", "ORC_PURPOSE_SAMPLE)\n"),
+    "draft_position": ("(uint32_t)(b + b_offset), (uint32_t)(pos0 + t),", "(uint32_t)(b + b_offset), (uint32_t)(t),"),
+    "draft_sequence": ("(uint32_t)(b + b_offset), (uint32_t)(pos0 + t),", "(uint32_t)(b), (uint32_t)(pos0 + t),"),
+    "draft_q_cumulative": ("*q = p[j];", "*q = cdf[j] / Z;"),
     "max_ignores_first": ("for (int64_t j = 0; j < V; ++j) {\n        double l = widen(row, dtype, j);\n        if (isnan(l) || l == INFINITY) usable = 0;\n        if (l > mx) mx = l;",
                           "for (int64_t j = 1; j < V; ++j) {\n        double l = widen(row, dtype, j);\n        if (isnan(l) || l == INFINITY) usable = 0;\n        if (l > mx) mx = l;"),
 }

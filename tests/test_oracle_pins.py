@@ -452,3 +452,107 @@ def test_bonus_row_checked_only_when_reached():
     a = np.argmax(inp.target[0, :3], axis=1)
     if (a == inp.tokens[0]).all():
         assert r.n[0] == -1
+
+
+# ---------------------------------------------------------------------------
+# Draft-side sampling ([Ch15] 15.1.2 step 1: each draft token is drawn from the
+# draft distribution and its probability kept; [CSDN] 2.1 stage 1)
+# ---------------------------------------------------------------------------
+def _draft_u(seed, B, n, pos0=0, b_offset=0):
+    b = np.repeat(np.arange(B, dtype=np.int64) + b_offset, n)
+    t = np.tile(np.arange(n, dtype=np.int64) + pos0, B)
+    return oracle.uniforms(seed, b.astype(np.uint32), t.astype(np.uint32), oracle.DRAFT).reshape(B, n)
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 10, 1000, 4097])
+def test_draft_uniform_row_is_floor_uV(V):
+    # equal logits: p_j = 1/V, C_j = (j+1)/V, so the inverse CDF picks floor(u*V)
+    B, n, seed = 40, 5, 99
+    logits = np.full((B, n, V), 0.75, np.float32)
+    r = oracle.draft_sample(logits, W.F32, 1.7, seed=seed, pos0=3, b_offset=11)
+    u = _draft_u(seed, B, n, pos0=3, b_offset=11)
+    want = np.floor(u * V).astype(np.int64)
+    near = np.abs(u * V - np.round(u * V)) < 1e-9
+    assert ((r.tokens == want) | near).all()
+    np.testing.assert_allclose(r.q, 1.0 / V, rtol=1e-14)
+
+
+@pytest.mark.parametrize("T", [0.4, 1.0, 2.3])
+def test_draft_two_token_closed_form(T):
+    # p_0 = 1 / (1 + exp((l_1 - l_0)/T)); the draw is token 0 exactly when u < p_0
+    rng = np.random.default_rng(5)
+    B, n, seed = 300, 4, 1234
+    logits = rng.normal(0, 2, (B, n, 2)).astype(np.float32)
+    r = oracle.draft_sample(logits, W.F32, T, seed=seed)
+    u = _draft_u(seed, B, n)
+    l = logits.astype(np.float64)
+    p0 = 1.0 / (1.0 + np.exp((l[..., 1] - l[..., 0]) / T))
+    clear = np.abs(u - p0) > 1e-12
+    assert clear.sum() > 0.99 * B * n
+    np.testing.assert_array_equal(r.tokens[clear], np.where(u < p0, 0, 1)[clear])
+    np.testing.assert_allclose(r.q, np.where(r.tokens == 0, p0, 1.0 - p0), rtol=1e-12)
+
+
+def test_draft_distribution_chi_square():
+    # many draws of one row (distinct counters) against softmax(l/T) from scipy
+    rng = np.random.default_rng(8)
+    V, T = 16, 0.7
+    row = rng.normal(0, 1.5, V).astype(np.float32)
+    B, n = 25000, 8
+    logits = np.broadcast_to(row, (B, n, V))
+    r = oracle.draft_sample(logits, W.F32, T, seed=77)
+    p = scipy.special.softmax(row.astype(np.float64) / T)
+    counts = np.bincount(r.tokens.ravel(), minlength=V)
+    assert scipy.stats.chisquare(counts, p * B * n).pvalue > 1e-3
+    np.testing.assert_allclose(r.q.ravel(), p[r.tokens.ravel()], rtol=1e-12)
+
+
+def test_draft_cdf_interval_holds_u():
+    inp = W.small_random_inputs(6, 5, 3000, W.BF16, 0.9, seed=4)
+    r = oracle.draft_sample(inp.draft, W.BF16, 0.9, seed=21, pos0=2, b_offset=7)
+    u = _draft_u(21, 6, 5, pos0=2, b_offset=7)
+    assert ((r.cdf_lo <= u) & (u < r.cdf_hi)).all()
+    np.testing.assert_allclose(r.cdf_hi - r.cdf_lo, r.q, rtol=1e-9, atol=1e-15)
+
+
+def test_draft_counters_split_across_calls():
+    # positions pos0 + t and sequences b + b_offset name the counters: splitting
+    # a call over positions or sequences changes nothing
+    inp = W.small_random_inputs(6, 6, 500, W.F32, 1.0, seed=3)
+    d = inp.draft
+    whole = oracle.draft_sample(d, W.F32, 1.0, seed=5)
+    left = oracle.draft_sample(d[:, :2], W.F32, 1.0, seed=5)
+    right = oracle.draft_sample(d[:, 2:], W.F32, 1.0, seed=5, pos0=2)
+    np.testing.assert_array_equal(whole.tokens, np.concatenate([left.tokens, right.tokens], axis=1))
+    top = oracle.draft_sample(d[:4], W.F32, 1.0, seed=5)
+    bot = oracle.draft_sample(d[4:], W.F32, 1.0, seed=5, b_offset=4)
+    np.testing.assert_array_equal(whole.tokens, np.concatenate([top.tokens, bot.tokens], axis=0))
+    assert len(np.unique(whole.tokens)) > 10
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_draft_greedy_is_first_argmax(dtype):
+    rng = np.random.default_rng(6)
+    l64 = np.round(rng.normal(0, 1, (5, 3, 300)), 1)   # coarse values: many ties
+    logits = W.to_storage(l64, dtype)
+    r = oracle.draft_sample(logits, dtype, 0.0)
+    np.testing.assert_array_equal(r.tokens, np.argmax(W.storage_to_f64(logits, dtype), axis=-1))
+    assert (r.q == 1.0).all()
+
+
+def test_draft_unusable_and_masked_rows():
+    logits = np.zeros((1, 5, 6), np.float32)
+    logits[0, 0, 2] = np.nan
+    logits[0, 1, 4] = np.inf
+    logits[0, 2, :] = -np.inf
+    logits[0, 3, :] = -np.inf
+    logits[0, 3, 5] = 1.0                                # one finite entry: always drawn, q = 1
+    logits[0, 4, ::2] = -np.inf                          # masked entries are never drawn
+    for T in (1.0, 0.0):
+        r = oracle.draft_sample(logits, W.F32, T, seed=2)
+        assert list(r.tokens[0, :3]) == [-1, -1, -1] and np.isnan(r.q[0, :3]).all()
+        assert r.tokens[0, 3] == 5 and r.q[0, 3] == 1.0
+        assert r.tokens[0, 4] % 2 == 1
+    many = oracle.draft_sample(np.broadcast_to(logits[0, 4], (400, 1, 6)), W.F32, 1.0, seed=9)
+    assert set(np.unique(many.tokens)) == {1, 3, 5}
+    np.testing.assert_allclose(many.q, 1.0 / 3, rtol=1e-14)
