@@ -159,6 +159,38 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits,
 int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype,
                    float temperature, float* row_max, double* row_sumexp, void* stream);
 
+/* spec_draft_sample: draft-side sampling, the step before verification
+ * ([Ch15] 15.1.2 step 1: each draft token is drawn from the draft model's
+ * distribution and its probability kept; [CSDN] 2.1, stage 1 of
+ * speculative_decode()).
+ *  logits [B, n, V] dtype, DEVICE, row-major contiguous: row (b, t) holds the
+ *      draft model's logits for position pos0 + t of sequence b (n = 1 for one
+ *      autoregressive step, or a block of positions at once).
+ *  temperature > 0: x = the smallest j whose ascending cumulative mass of
+ *      softmax(l/T) exceeds u*S (S the total), with u the Philox4x32-10 uniform
+ *      of counter (b + b_offset, pos0 + t, 2 = DRAFT, 0) keyed by seed (the
+ *      verification's accept and correction draws use purposes 0 and 1, so
+ *      the streams never meet); q = softmax(l/T)_x. temperature == 0: x = the
+ *      first index of the maximum, q = 1.
+ *  out_tokens [B, n] int32, DEVICE: x, or -1 for a row holding NaN, +inf or no
+ *      finite entry (-inf entries are masked tokens and never drawn).
+ *  out_q [B, n] double, DEVICE, or NULL: q, NaN where the token is -1.
+ *  pos0 >= 0 and b_offset >= 0 (counter words are taken mod 2^32);
+ *  B * n < 2^31. Enqueued on stream; returns without synchronising. Errors as
+ *  spec_verify (checked before any launch). Uses the library's workspace of
+ *  (device, stream), like spec_verify. Every row's logits are read once, plus
+ *  one 4 KiB range again at T > 0. */
+int spec_draft_sample(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype,
+                      float temperature, uint64_t seed, int64_t pos0, int64_t b_offset,
+                      int32_t* out_tokens, double* out_q, void* stream);
+
+/* spec_draft_sample, with events[0] and events[1] (hipEvent_t, may be NULL;
+ * events may be NULL) bound to the start and end of the kernel dispatch, for
+ * timing. */
+int spec_draft_sample_ex(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype,
+                         float temperature, uint64_t seed, int64_t pos0, int64_t b_offset,
+                         int32_t* out_tokens, double* out_q, void* stream, void* const events[2]);
+
 /* The schedule SPEC_SCHEDULE_AUTO takes for this shape on the current device
  * (SPEC_SCHEDULE_GROUP or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
 int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature);
@@ -174,7 +206,7 @@ void spec_verify_release_workspace(void);
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* spec_verify_last_error(void);
 
-/* ABI version: 2 (spec_extras_t gained schedule). */
+/* ABI version: 3 (2: spec_extras_t gained schedule; 3: spec_draft_sample). */
 int32_t spec_verify_abi_version(void);
 
 #ifdef __cplusplus

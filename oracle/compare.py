@@ -111,3 +111,65 @@ def rel_err(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return np.abs(a - b) / np.maximum(np.abs(b), 1e-300)
+
+
+@dataclasses.dataclass
+class DraftReport:
+    rows: int = 0
+    draws: int = 0
+    boundary: int = 0
+    hard_fail: list = dataclasses.field(default_factory=list)
+    max_q_rel: float = 0.0
+
+    def ok(self, max_rate=1e-3):
+        return not self.hard_fail and self.boundary <= max(1, int(max_rate * max(self.draws, 1)))
+
+    def __str__(self):
+        return (f"rows={self.rows} draws={self.draws} near-boundary {self.boundary}; max q rel err "
+                f"{self.max_q_rel:.2e}; hard failures {len(self.hard_fail)}")
+
+
+def compare_draft(logits, dtype, T, orc, gpu_tokens, gpu_q, seed, pos0=0, b_offset=0, q_rtol=1e-5) -> DraftReport:
+    """Draft-side sampling against the oracle. logits [B, n, V] storage arrays;
+    orc: oracle.DraftResult. Tokens are exact (T == 0: always; T > 0: except a
+    draw whose uniform lies within BAND of the oracle's CDF interval of the GPU
+    token, counted); q within q_rtol relative (exactly 1 at T == 0); unusable
+    rows give -1 and NaN on both sides."""
+    from . import DRAFT
+    B, n, V = logits.shape
+    rep = DraftReport()
+    for b in range(B):
+        for t in range(n):
+            rep.rows += 1
+            to, tg = int(orc.tokens[b, t]), int(gpu_tokens[b, t])
+            qg = None if gpu_q is None else float(gpu_q[b, t])
+            if to < 0:
+                if tg != -1 or (qg is not None and not np.isnan(qg)):
+                    rep.hard_fail.append((b, t, "unusable row", tg, qg))
+                continue
+            if T > 0:
+                rep.draws += 1
+            if tg == to:
+                if qg is not None:
+                    if T == 0:
+                        if qg != 1.0:
+                            rep.hard_fail.append((b, t, "greedy q", qg))
+                    else:
+                        e = abs(qg - orc.q[b, t]) / orc.q[b, t]
+                        rep.max_q_rel = max(rep.max_q_rel, e)
+                        if not e <= q_rtol:
+                            rep.hard_fail.append((b, t, "q", qg, float(orc.q[b, t])))
+                continue
+            if T == 0 or not (0 <= tg < V):
+                rep.hard_fail.append((b, t, "token", to, tg))
+                continue
+            u = uniform(seed, b + b_offset, pos0 + t, DRAFT)
+            _, cdf = residual_cdf(logits[b, t], None, dtype, T)
+            lo = cdf[tg - 1] if tg > 0 else 0.0
+            hi = cdf[tg]
+            dist = 0.0 if lo <= u < hi else min(abs(u - lo), abs(u - hi))
+            if dist < BAND:
+                rep.boundary += 1
+            else:
+                rep.hard_fail.append((b, t, "sample", to, tg, float(u), float(lo), float(hi)))
+    return rep

@@ -23,6 +23,8 @@ EXPORTS = (
     "spec_verify",
     "spec_verify_ex",
     "spec_row_stats",
+    "spec_draft_sample",
+    "spec_draft_sample_ex",
     "spec_verify_schedule",
     "spec_verify_workspace_bytes",
     "spec_verify_release_workspace",
@@ -71,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     L.spec_verify_ex.restype = ctypes.c_int
     L.spec_row_stats.argtypes = [vp, i64, i32, i32, f32, vp, vp, vp]
     L.spec_row_stats.restype = ctypes.c_int
+    L.spec_draft_sample.argtypes = [vp, i32, i32, i32, i32, f32, u64, i64, i64, vp, vp, vp]
+    L.spec_draft_sample.restype = ctypes.c_int
+    L.spec_draft_sample_ex.argtypes = [vp, i32, i32, i32, i32, f32, u64, i64, i64, vp, vp, vp, vp]
+    L.spec_draft_sample_ex.restype = ctypes.c_int
     L.spec_verify_schedule.argtypes = [i32, i32, i32, i32, f32]
     L.spec_verify_schedule.restype = i32
     L.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
@@ -181,6 +187,36 @@ def row_stats(logits, temperature: float, stream=None):
     _check(L.spec_row_stats(_ptr(logits), rows, V, _dtype_code(logits), float(temperature),
                             _ptr(m), _ptr(s), _stream_handle(stream)))
     return m, s
+
+
+def draft_sample(logits, temperature: float, seed: int, pos0: int = 0, b_offset: int = 0,
+                 want_q: bool = True, out_tokens=None, out_q=None, stream=None, events=None):
+    """Draft tokens drawn from softmax(logits / T) (the first argmax at T == 0)
+    for logits [B, n, V] (or [B, V], one position), float32 or bfloat16,
+    contiguous, on the GPU; row (b, t) draws with the DRAFT uniform of counter
+    (b + b_offset, pos0 + t). Returns (tokens int32, q float64 or None), each
+    [B, n] (or [B]); -1 and NaN mark unusable rows."""
+    import torch
+    L = load_library()
+    if logits.dim() not in (2, 3) or not logits.is_cuda or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [B, n, V] or [B, V] GPU tensor")
+    shape = tuple(logits.shape[:-1])
+    B = shape[0]
+    n = shape[1] if logits.dim() == 3 else 1
+    V = logits.shape[-1]
+    dev = logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty(shape, dtype=torch.int32, device=dev)
+    if want_q and out_q is None:
+        out_q = torch.empty(shape, dtype=torch.float64, device=dev)
+    args = (_ptr(logits), B, n, V, _dtype_code(logits), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+            int(pos0), int(b_offset), _ptr(out_tokens), _ptr(out_q if want_q else None), _stream_handle(stream))
+    if events is None:
+        _check(L.spec_draft_sample(*args))
+    else:
+        ev = (ctypes.c_void_p * 2)(*[ctypes.c_void_p(e) for e in events])
+        _check(L.spec_draft_sample_ex(*args, ev))
+    return out_tokens, (out_q if want_q else None)
 
 
 def auto_schedule(B, gamma, V, dtype, temperature) -> int:

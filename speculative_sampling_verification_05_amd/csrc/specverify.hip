@@ -85,6 +85,9 @@ namespace {
 #ifndef SPECVERIFY_SLEEP
 #define SPECVERIFY_SLEEP 2
 #endif
+#ifndef SPECVERIFY_DRAFT_CW
+#define SPECVERIFY_DRAFT_CW 4
+#endif
 #ifndef SPECVERIFY_SYNC_STRIDE
 #define SPECVERIFY_SYNC_STRIDE 64
 #endif
@@ -642,6 +645,25 @@ __device__ inline float group_max(const typename Chunk<DT, VEC>::Raw* raw) {
         for (int v = 0; v < C::EPL; ++v) mx = fmaxf(mx, x[v]);
     }
     return mx;
+}
+
+// Sum of 2^(fl(x*c - R)) over N chunks in two fp32 accumulators (no maximum).
+template <int DT, bool VEC, int N>
+__device__ inline float group_exp_sum(const typename Chunk<DT, VEC>::Raw* raw, float c, float R) {
+    using C = Chunk<DT, VEC>;
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float x[C::EPL];
+        C::expand(raw[u], x);
+#pragma unroll
+        for (int v = 0; v < C::EPL; ++v) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(x[v], c, -R));
+            if (v & 1) a1 += e;
+            else a0 += e;
+        }
+    }
+    return a0 + a1;
 }
 
 template <int DT, bool VEC, int N>
@@ -1998,21 +2020,23 @@ __device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int3
 // load round trip); the totals and prefix sums are formed exactly as above.
 constexpr int kDrawTiles = 4;
 
+template <int NT = kDrawTiles>
 __device__ inline double regs_scan(const double* v, double* incl, int lane) {
     double base = 0.0;
 #pragma unroll
-    for (int t = 0; t < kDrawTiles; ++t) {
+    for (int t = 0; t < NT; ++t) {
         incl[t] = base + wave_scan_incl(v[t]);
         base = lane_f64(incl[t], kWave - 1);
     }
     return base;
 }
 
+template <int NT = kDrawTiles>
 __device__ inline int32_t regs_find(const double* v, const double* incl, double t, int lane, double& before) {
     int32_t last = -1;
     double last_before = 0.0;
 #pragma unroll
-    for (int k = 0; k < kDrawTiles; ++k) {
+    for (int k = 0; k < NT; ++k) {
         const double prev = lane_before(incl[k]);
         const double base = k == 0 ? 0.0 : lane_f64(incl[k - 1], kWave - 1);
         const double excl = lane == 0 ? base : prev;
@@ -2315,6 +2339,404 @@ __global__ __launch_bounds__(kBlock) void k_verify(Params P) {
 
 
 // ==========================================================================
+// Draft-side sampling ([Ch15] 15.1.2 step 1: each draft token is drawn from
+// the draft model's distribution and its probability kept; [CSDN] 2.1, stage 1
+// of speculative_decode()). Row (b, t) of a [B, n, V] block of draft logits
+// gives x, the smallest j whose ascending cumulative mass of softmax(l/T)
+// exceeds u*S, with u the Philox uniform of counter (b + b_offset, pos0 + t,
+// DRAFT), and q = p(x); at T == 0, x = the first argmax and q = 1.
+//
+// Rows are independent, so nothing waits. Wavefront w of a row loads its range
+// of kDraftCw chunks in one go and writes one partial: at T > 0 (max, integer
+// reference R, sum of 2^(fl(x*c - R)) in fp64 over fp32 groups), at T == 0
+// (max, first index of it). The row's last block to count in folds the
+// partials, finds the range where the cumulative mass crosses u*S, loads that
+// range again (one wavefront, 16 KiB) and finds the element in ascending
+// order from the same fp32 element values, scaled to the row's reference by
+// an exact power of two.
+// ==========================================================================
+constexpr int kDraftCw = SPECVERIFY_DRAFT_CW;  // chunks per wavefront range
+constexpr int kFinTiles = 2;  // range sums the finishing wavefront holds: 64 * kFinTiles (more: three passes)
+constexpr int kDraftStride = 32;    // words between two row counters
+constexpr uint32_t kPurposeDraft = 2u;
+
+struct DraftParams {
+    const void* logits;  // [rows, V], row r = b * n + t
+    int64_t rows;
+    int32_t n, V, nchunk;
+    int32_t nw;   // wavefront ranges per row
+    int32_t nbr;  // blocks per row
+    float c32;    // log2(e) / T
+    uint64_t seed;
+    int64_t pos0, b_offset;
+    int32_t* out_tokens;  // [rows]
+    double* out_q;        // [rows] or null
+    double* part_s;       // T > 0: [rows, nw] sum of 2^(fl(x*c - R)) per range
+    float* part_r;        //        and its integer reference R
+    float* part_m;        // T == 0: [rows, nw] maximum and its first index per range
+    int32_t* part_i;
+    uint32_t* cnt;        // [rows] counters, kDraftStride words apart
+    uint32_t* err;        // sticky error word (a bounded wait ran out)
+};
+
+// The token of range `sel` (chunks c0 .. c0 + kDraftCw - 1 of the row, loaded
+// into q): elements visited in ascending index order as tiles (Tiles), each
+// lane's tile mass the fp64 sum of 2^(fl(x*c - rs)) * sc (sc = 2^(rs - R), an
+// exact rescaling to the row's reference), the first element where the
+// cumulative mass, starting at `before`, exceeds `target`; if rounding leaves
+// none, the last element with mass. Returns (in every lane) the token and, in
+// `mass`, its scaled mass.
+template <int DT, bool VEC, int N>
+__device__ __attribute__((always_inline)) inline int32_t draft_pick(const typename Chunk<DT, VEC>::Raw* q, int64_t c0, float c, float rs, double sc,
+                                     double before, double target, int lane, double& mass) {
+    using C = Chunk<DT, VEC>;
+    using TL = Tiles<DT, VEC>;
+    int32_t last = -1;
+    double last_m = 0.0;
+    double run = before;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float x[C::EPL];
+        typename C::Raw r = q[u];
+        opaque(r);  // expanded here, one chunk at a time
+        C::expand(r, x);
+#pragma unroll
+        for (int t = 0; t < TL::PER_CHUNK; ++t) {
+            double lm = 0.0, ml = 0.0;
+            int32_t mylast = -1;
+#pragma unroll
+            for (int e = 0; e < TL::EPT; ++e) {
+                const int v = VEC ? e : t;
+                const double m = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x[v], c, -rs))) * sc;
+                lm += m;
+                if (m > 0.0) {
+                    mylast = static_cast<int32_t>(C::index_of(c0 + u, lane, v));
+                    ml = m;
+                }
+            }
+            const double incl = run + wave_scan_incl(lm);
+            const double prev = lane_before(incl);
+            const double excl = lane == 0 ? run : prev;
+            const uint64_t hit = __ballot(lm > 0.0 && excl <= target && target < incl);
+            if (hit) {
+                const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                int32_t pick = -1;
+                double pm = 0.0;
+                if (lane == l) {
+                    double r2 = excl;
+#pragma unroll
+                    for (int e = 0; e < TL::EPT; ++e) {
+                        const int v = VEC ? e : t;
+                        const double m = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x[v], c, -rs))) * sc;
+                        r2 += m;
+                        if (pick < 0 && m > 0.0 && r2 > target) {
+                            pick = static_cast<int32_t>(C::index_of(c0 + u, lane, v));
+                            pm = m;
+                        }
+                    }
+                    if (pick < 0) {
+                        pick = mylast;
+                        pm = ml;
+                    }
+                }
+                mass = __shfl(pm, l, kWave);
+                return __shfl(pick, l, kWave);
+            }
+            const uint64_t any = __ballot(mylast >= 0);
+            if (any) {
+                const int l = 63 - __clzll(static_cast<unsigned long long>(any));
+                last = __shfl(mylast, l, kWave);
+                last_m = __shfl(ml, l, kWave);
+            }
+            run = lane_f64(incl, kWave - 1);
+        }
+    }
+    mass = last_m;
+    return last;
+}
+
+// The token of an N-chunk range starting at chunk c0 (loaded into q): the
+// chunks' masses first, independently of one another (fp64, tiles in
+// ascending order), then the chunk where the cumulative mass, starting at
+// `before`, first exceeds `target` (if rounding leaves none, the last chunk
+// with mass), then the element in that chunk (draft_pick). -1 if the range
+// has no mass.
+template <int DT, bool VEC, int N>
+__device__ __attribute__((always_inline)) inline int32_t draft_pick_range(const typename Chunk<DT, VEC>::Raw* q, int64_t c0, float c, float rs,
+                                           double sc, double before, double target, int lane, double& mass) {
+    using C = Chunk<DT, VEC>;
+    using TL = Tiles<DT, VEC>;
+    double cm[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float x[C::EPL];
+        typename C::Raw r = q[u];
+        opaque(r);
+        C::expand(r, x);
+        double lm = 0.0;
+#pragma unroll
+        for (int v = 0; v < C::EPL; ++v) lm += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x[v], c, -rs))) * sc;
+        cm[u] = lm;
+    }
+#pragma unroll
+    for (int u = 0; u < N; ++u) cm[u] = wave_sum(cm[u]);  // independent reductions
+    // (VEC: a chunk is one tile, so these equal the tile totals the element
+    // scan forms; scalar: the chunk's four tiles summed in one go)
+    int32_t ch = -1, last = -1;
+    double cb = 0.0, last_b = 0.0, run = before;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        if (ch < 0 && cm[u] > 0.0) {
+            if (run <= target && target < run + cm[u]) {
+                ch = u;
+                cb = run;
+            }
+            last = u;
+            last_b = run;
+        }
+        run += cm[u];
+    }
+    if (ch < 0) {
+        ch = last;
+        cb = last_b;
+    }
+    int32_t tok = -1;
+#pragma unroll
+    for (int u = 0; u < N; ++u)  // (a branch per chunk keeps the register indices constant)
+        if (ch == u) tok = draft_pick<DT, VEC, 1>(q + u, c0 + u, c, rs, sc, cb, target, lane, mass);
+    (void)TL::EPT;
+    return tok;
+}
+
+template <int DT, bool VEC, bool GREEDY>
+__device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane);
+
+template <int DT, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
+    using C = Chunk<DT, VEC>;
+    using Raw = typename C::Raw;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));  // (uniform: scalar branches)
+    const int64_t sblocks = D.rows * D.nbr;
+    if (blockIdx.x >= sblocks) {  // closing blocks: wavefront w finishes one row
+        const int64_t row = (blockIdx.x - sblocks) * kWavesPerBlock + w;
+        if (row < D.rows) draft_finish<DT, VEC, GREEDY>(D, row, lane);
+        return;
+    }
+    const int64_t row = blockIdx.x / D.nbr;
+    const int32_t wl = static_cast<int32_t>(blockIdx.x - row * D.nbr) * kWavesPerBlock + w;
+    const char* rp = row_at<DT>(D.logits, row * D.V);
+    const int64_t pb = row * D.nw;  // the row's partials
+    if (wl < D.nw) {
+        const int64_t c0 = static_cast<int64_t>(wl) * kDraftCw;
+        Raw q[kDraftCw];
+        load_slots<DT, VEC, kDraftCw>(q, rp, c0, D.nchunk, D.V, lane);
+        mask_slots<DT, VEC, kDraftCw>(q, c0, D.nchunk, D.V, lane);
+        if constexpr (GREEDY) {
+            ArgLane a;
+            a.init();
+#pragma unroll
+            for (int g = 0; g < kDraftCw / kUnroll; ++g)  // ascending: the first maximum is kept
+                consume_group<DT, VEC, kUnroll>(a, q + g * kUnroll, c0 + g * kUnroll, lane, 0.0f);
+            const bool nan = __ballot(a.nan) != 0;
+            ArgPart f{a.best, a.at};
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) f = fold_arg(f, ArgPart{__shfl_xor(f.m, o, kWave), __shfl_xor(f.at, o, kWave)});
+            if (lane == 0) {
+                cst(D.part_m + pb + wl, nan ? NAN : f.m);
+                cst(D.part_i + pb + wl, f.at);
+            }
+        } else {
+            // one pass: the reference R comes from the first group with a
+            // finite maximum; a later group whose fp32 sum overflows (a value
+            // far above R, or +inf) or is NaN takes the rare path, which
+            // raises R (rescaling the sum so far by an exact power of two) and
+            // sums the group again
+            const float c = D.c32;
+            float R = kRUnset;
+            bool bad = false;
+            double S = 0.0;
+#pragma unroll
+            for (int g = 0; g < kDraftCw / kUnroll; ++g) {
+                const Raw* qg = q + g * kUnroll;
+                if (R == kRUnset) {
+                    const float mx = wave_max(group_max<DT, VEC, kUnroll>(qg));  // (NaN is not a maximum)
+                    if (mx * c > kRUnset + 1.0f) {
+                        const float Rn = ceilf(mx * c);
+                        if (Rn < 3.0e38f) R = Rn;
+                        else bad = true;  // +inf logit, or x*c overflows: the row is unusable
+                    }
+                }
+                float acc = group_exp_sum<DT, VEC, kUnroll>(qg, c, R);
+                if (__any(!(acc <= 3.0e38f))) {
+                    const float Rn = ceilf(wave_max(group_max<DT, VEC, kUnroll>(qg)) * c);
+                    if (!(Rn < 3.0e38f)) {
+                        bad = true;
+                    } else if (Rn > R) {
+                        S = rebase(S, R, Rn);
+                        R = Rn;
+                        acc = group_exp_sum<DT, VEC, kUnroll>(qg, c, R);
+                    }  // else a NaN logit: the sum stays NaN
+                }
+                S += static_cast<double>(acc);
+            }
+            S = wave_sum(S);
+            if (lane == 0) {
+                cst(D.part_s + pb + wl, bad ? static_cast<double>(NAN) : S);
+                cst(D.part_r + pb + wl, R);
+            }
+        }
+    }
+    // this wavefront's range has counted in once its partial is stored
+    // (no-return atomic, ordered after the stores by waiting for them)
+    if (wl < D.nw) {
+        complete_before();
+        if (lane == 0) (void)__hip_atomic_fetch_add(D.cnt + row * kDraftStride, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// The closing wavefront of a row: waits (bounded) until all of the row's
+// ranges have counted in, clears the counter for the next call, and draws.
+template <int DT, bool VEC, bool GREEDY>
+__device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane) {
+    using C = Chunk<DT, VEC>;
+    using Raw = typename C::Raw;
+    uint32_t* cnt = D.cnt + row * kDraftStride;
+    const uint32_t want = static_cast<uint32_t>(D.nw);
+    int ok = 1;
+    if (lane == 0) {
+        if (cld(cnt) < want) {
+            const uint64_t t0 = wall_clock64();
+            for (;;) {
+                __builtin_amdgcn_s_sleep(kSleep);
+                if (cld(cnt) >= want) break;
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    cst(D.err, 1u);
+                    ok = 0;
+                    break;
+                }
+            }
+        }
+        if (ok) cst(cnt, 0u);
+    }
+    ok = __shfl(ok, 0, kWave);
+    after_complete();
+    if (!ok) {  // the wait ran out (not expected): the row is reported unusable
+        if (lane == 0) {
+            D.out_tokens[row] = -1;
+            if (D.out_q) D.out_q[row] = NAN;
+        }
+        return;
+    }
+    const char* rp = row_at<DT>(D.logits, row * D.V);
+    if constexpr (GREEDY) {
+        const int64_t pb = row * D.nw;
+        ArgPart f{-INFINITY, INT32_MAX};
+        for (int32_t k = lane; k < D.nw; k += kWave) f = fold_arg(f, ArgPart{cld(D.part_m + pb + k), cld(D.part_i + pb + k)});
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) f = fold_arg(f, ArgPart{__shfl_xor(f.m, o, kWave), __shfl_xor(f.at, o, kWave)});
+        if (lane == 0) {
+            const bool good = isfinite(f.m);
+            D.out_tokens[row] = good ? f.at : -1;
+            if (D.out_q) D.out_q[row] = good ? 1.0 : static_cast<double>(NAN);
+        }
+    } else {
+        // the ranges' sums at the row's reference R (an exact power-of-two
+        // rescaling of each range's own), their total S, the range where the
+        // ascending cumulative mass crosses u*S; then that range again, and
+        // the element in it
+        const double* ps = D.part_s + row * D.nw;
+        const float* pr = D.part_r + row * D.nw;
+        const int32_t nw = D.nw;
+        double S = 0.0, before = 0.0, target = 0.0;
+        float R = kRUnset, rs = kRUnset;
+        int32_t sel = -1;
+        const int64_t b = row / D.n, t = row - b * D.n;
+        const double u = philox_uniform(D.seed, static_cast<uint32_t>(b + D.b_offset),
+                                        static_cast<uint32_t>(D.pos0 + t), kPurposeDraft);
+        if (nw <= kFinTiles * kWave) {  // held in registers: one load round trip
+            float r[kFinTiles];
+            double v[kFinTiles], incl[kFinTiles];
+#pragma unroll
+            for (int t2 = 0; t2 < kFinTiles; ++t2) {
+                const int32_t k = t2 * kWave + lane;
+                r[t2] = k < nw ? cld(pr + k) : kRUnset;
+                v[t2] = k < nw ? cld(ps + k) : 0.0;
+            }
+#pragma unroll
+            for (int t2 = 0; t2 < kFinTiles; ++t2) R = fmaxf(R, r[t2]);
+            R = wave_max(R);
+#pragma unroll
+            for (int t2 = 0; t2 < kFinTiles; ++t2) v[t2] = rebase(v[t2], r[t2], R);
+            S = regs_scan<kFinTiles>(v, incl, lane);
+            if (isfinite(S) && S > 0.0) {  // else NaN, +inf or no finite entry: the row is unusable
+                target = u * S;
+                sel = regs_find<kFinTiles>(v, incl, target, lane, before);
+                if (sel >= 0) {
+#pragma unroll
+                    for (int t2 = 0; t2 < kFinTiles; ++t2)
+                        if (sel / kWave == t2) rs = r[t2];  // (constant register indices)
+                    rs = __shfl(rs, sel % kWave, kWave);
+                }
+            }
+        } else {  // many ranges: three passes over them in tiles of 64
+            for (int32_t t0 = 0; t0 < nw; t0 += kWave)
+                if (t0 + lane < nw) R = fmaxf(R, cld(pr + t0 + lane));
+            R = wave_max(R);
+            auto val = [&](int32_t k) { return k < nw ? rebase(cld(ps + k), cld(pr + k), R) : 0.0; };
+            for (int32_t t0 = 0; t0 < nw; t0 += kWave) S += lane_f64(wave_scan_incl(val(t0 + lane)), kWave - 1);
+            if (isfinite(S) && S > 0.0) {
+                target = u * S;
+                double base = 0.0, last_before = 0.0;
+                int32_t last = -1;
+                for (int32_t t0 = 0; t0 < nw && sel < 0; t0 += kWave) {
+                    const double v = val(t0 + lane);
+                    const double incl = base + wave_scan_incl(v);
+                    const double prev = lane_before(incl);
+                    const double excl = lane == 0 ? base : prev;
+                    const uint64_t hit = __ballot(v > 0.0 && excl <= target && target < incl);
+                    if (hit) {
+                        const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                        sel = t0 + l;
+                        before = __shfl(excl, l, kWave);
+                    } else {
+                        const uint64_t any = __ballot(v > 0.0);
+                        if (any) {
+                            const int l = 63 - __clzll(static_cast<unsigned long long>(any));
+                            last = t0 + l;
+                            last_before = __shfl(excl, l, kWave);
+                        }
+                    }
+                    base = lane_f64(incl, kWave - 1);
+                }
+                if (sel < 0) {
+                    sel = last;
+                    before = last_before;
+                }
+                if (sel >= 0) rs = cld(pr + sel);
+            }
+        }
+        int32_t tok = -1;
+        double qv = NAN;
+        if (sel >= 0) {
+            const int64_t c0 = static_cast<int64_t>(sel) * kDraftCw;
+            Raw q[kDraftCw];
+            load_slots<DT, VEC, kDraftCw>(q, rp, c0, D.nchunk, D.V, lane);
+            mask_slots<DT, VEC, kDraftCw>(q, c0, D.nchunk, D.V, lane);
+            const double sc = ldexp(1.0, static_cast<int>(fmaxf(rs - R, -1100.0f)));
+            double mass = 0.0;
+            tok = draft_pick_range<DT, VEC, kDraftCw>(q, c0, D.c32, rs, sc, before, target, lane, mass);
+            if (tok >= 0) qv = mass / S;
+        }
+        if (lane == 0) {
+            D.out_tokens[row] = tok;
+            if (D.out_q) D.out_q[row] = qv;
+        }
+    }
+}
+
+// ==========================================================================
 // Host side
 // ==========================================================================
 thread_local std::string g_last_error;
@@ -2602,6 +3024,73 @@ int check_size(int, const Layout& L) {
     return SPEC_OK;
 }
 
+// Draft sampler geometry: rows of nw wavefront ranges of kDraftCw chunks,
+// four ranges per block. Partials and counters live in the call's workspace
+// (its counters, like every call's, are back at zero when the kernel ends).
+struct DraftLayout {
+    DraftParams d;
+    int64_t blocks;
+    Layout ws;  // the sizes the workspace must hold
+};
+
+DraftLayout plan_draft(int64_t rows, int32_t V, int32_t dtype, bool vec) {
+    DraftLayout L{};
+    DraftParams& d = L.d;
+    d.rows = rows;
+    d.V = V;
+    d.nchunk = static_cast<int32_t>(ceil_div(V, chunk_elems(dtype, vec)));
+    d.nw = static_cast<int32_t>(ceil_div(d.nchunk, kDraftCw));
+    d.nbr = static_cast<int32_t>(ceil_div(d.nw, kWavesPerBlock));
+    L.blocks = rows * d.nbr + ceil_div(rows, kWavesPerBlock);  // statistics blocks, then closing blocks
+    const size_t slots = static_cast<size_t>(rows) * d.nw;
+    size_t o = 0;
+    o = align_up(o + slots * sizeof(double), 256);   // part_s
+    o = align_up(o + slots * sizeof(float), 256);    // part_r
+    o = align_up(o + slots * sizeof(float), 256);    // part_m
+    o = align_up(o + slots * sizeof(int32_t), 256);  // part_i
+    L.ws.bytes = o;
+    L.ws.cnt_words = rows * kDraftStride;
+    L.ws.dec_words = 0;
+    return L;
+}
+
+void bind_draft(DraftLayout& L, const Workspace& ws) {
+    char* base = static_cast<char*>(ws.data);
+    DraftParams& d = L.d;
+    const size_t slots = static_cast<size_t>(d.rows) * d.nw;
+    const size_t f4 = align_up(slots * sizeof(float), 256);
+    size_t o = 0;
+    d.part_s = reinterpret_cast<double*>(base + o);
+    o += align_up(slots * sizeof(double), 256);
+    d.part_r = reinterpret_cast<float*>(base + o);
+    o += f4;
+    d.part_m = reinterpret_cast<float*>(base + o);
+    o += f4;
+    d.part_i = reinterpret_cast<int32_t*>(base + o);
+    d.cnt = ws.sync;
+    const size_t off_dec = align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256);
+    d.err = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws.sync) + off_dec +
+                                        static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t));
+}
+
+template <int DT, bool VEC>
+void launch_draft_t(bool greedy, const DraftLayout& L, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const dim3 grid(static_cast<unsigned>(L.blocks)), block(kBlock);
+    if (greedy) hipExtLaunchKernelGGL((k_draft<DT, VEC, true>), grid, block, 0, st, e0, e1, 0, L.d);
+    else hipExtLaunchKernelGGL((k_draft<DT, VEC, false>), grid, block, 0, st, e0, e1, 0, L.d);
+}
+
+void launch_draft(int32_t dtype, bool vec, bool greedy, const DraftLayout& L, hipStream_t st, hipEvent_t e0,
+                  hipEvent_t e1) {
+    if (dtype == SPEC_F32) {
+        if (vec) launch_draft_t<SPEC_F32, true>(greedy, L, st, e0, e1);
+        else launch_draft_t<SPEC_F32, false>(greedy, L, st, e0, e1);
+    } else {
+        if (vec) launch_draft_t<SPEC_BF16, true>(greedy, L, st, e0, e1);
+        else launch_draft_t<SPEC_BF16, false>(greedy, L, st, e0, e1);
+    }
+}
+
 }  // namespace
 
 // ==========================================================================
@@ -2609,7 +3098,7 @@ int check_size(int, const Layout& L) {
 // ==========================================================================
 extern "C" {
 
-int32_t spec_verify_abi_version(void) { return 2; }
+int32_t spec_verify_abi_version(void) { return 3; }
 
 const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
 
@@ -2761,6 +3250,53 @@ int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype, f
     L.p.rows_sumexp = row_sumexp;
     launch(dtype, vec, kRows, L, st);
     return check_launch("statistics kernel");
+}
+
+int spec_draft_sample_ex(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype, float temperature,
+                         uint64_t seed, int64_t pos0, int64_t b_offset, int32_t* out_tokens, double* out_q,
+                         void* stream, void* const events[2]) {
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EDTYPE, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (B < 1 || n < 1 || V < 1) return fail(SPEC_EINVAL, "B, n and V must be >= 1");
+    if (pos0 < 0 || b_offset < 0) return fail(SPEC_EINVAL, "pos0 and b_offset must be >= 0");
+    if (!(temperature >= 0.0f)) return fail(SPEC_EINVAL, "temperature must be >= 0 and not NaN");
+    if (!logits || !out_tokens) return fail(SPEC_EINVAL, "null pointer argument");
+    const bool greedy = temperature == 0.0f;
+    const float c32 = greedy ? 0.0f : fold_temperature(temperature);
+    if (!greedy && !(std::isfinite(c32) && c32 > 0.0f))
+        return fail(SPEC_EINVAL, "temperature too small or too large for fp32 exponent scaling");
+    const int64_t rows = static_cast<int64_t>(B) * n;
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(logits);
+    DraftLayout L = plan_draft(rows, V, dtype, vec);
+
+    if (rows >= (int64_t(1) << 31) || L.blocks * kBlock >= (int64_t(1) << 32))
+        return fail(SPEC_EINVAL, "problem too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace* ws = nullptr;
+    if (int rc = get_workspace(dev, st, L.ws, &ws)) return rc;
+    bind_draft(L, *ws);
+    DraftParams& d = L.d;
+    d.logits = logits;
+    d.n = n;
+    d.c32 = c32;
+    d.seed = seed;
+    d.pos0 = pos0;
+    d.b_offset = b_offset;
+    d.out_tokens = out_tokens;
+    d.out_q = out_q;
+    hipEvent_t e0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
+    hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+    launch_draft(dtype, vec, greedy, L, st, e0, e1);
+    return check_launch("draft sampling kernel");
+}
+
+int spec_draft_sample(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype, float temperature,
+                      uint64_t seed, int64_t pos0, int64_t b_offset, int32_t* out_tokens, double* out_q,
+                      void* stream) {
+    return spec_draft_sample_ex(logits, B, n, V, dtype, temperature, seed, pos0, b_offset, out_tokens, out_q,
+                                stream, nullptr);
 }
 
 }  // extern "C"

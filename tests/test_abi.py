@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = sv.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_verify_abi_version() == 2
+    assert lib.spec_verify_abi_version() == 3
 
 
 def _call(B=2, gamma=3, V=10, dtype=0, T=1.0, tgt=1, dft=1, tok=1, out_t=1, out_n=1):
@@ -69,3 +69,27 @@ def test_schedule_out_of_range_is_rejected():
     rc = sv.load_library().spec_verify_ex(P(1), P(1), P(1), 2, 3, 10, 0, 1.0, 0, P(1), P(1), None, ctypes.byref(ex))
     assert rc == sv.SPEC_EINVAL
     assert "schedule" in sv.last_error()
+
+
+def _draft(B=2, n=3, V=10, dtype=0, T=1.0, pos0=0, b_offset=0, logits=1, out_t=1):
+    P = lambda v: ctypes.c_void_p(v) if v else None  # noqa: E731 (non-null dummies are never dereferenced)
+    return sv.load_library().spec_draft_sample(P(logits), B, n, V, dtype, T, 0, pos0, b_offset, P(out_t), None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), sv.SPEC_EDTYPE),
+    (dict(B=0), sv.SPEC_EINVAL),
+    (dict(n=0), sv.SPEC_EINVAL),
+    (dict(V=0), sv.SPEC_EINVAL),
+    (dict(T=-1.0), sv.SPEC_EINVAL),
+    (dict(T=float("nan")), sv.SPEC_EINVAL),
+    (dict(T=1e-45), sv.SPEC_EINVAL),
+    (dict(pos0=-1), sv.SPEC_EINVAL),
+    (dict(b_offset=-1), sv.SPEC_EINVAL),
+    (dict(logits=0), sv.SPEC_EINVAL),
+    (dict(out_t=0), sv.SPEC_EINVAL),
+    (dict(B=1 << 16, n=1 << 15), sv.SPEC_EINVAL),   # 2^31 rows
+])
+def test_draft_sample_argument_checks(kw, code):
+    assert _draft(**kw) == code
+    assert sv.last_error() != ""
