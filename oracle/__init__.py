@@ -69,6 +69,10 @@ def lib():
         L.orc_draft_sample.argtypes = [vp, i32, i32, i64, ctypes.c_int, f64, u64, i64, i64, vp, vp,
                                        vp, vp]
         L.orc_draft_sample.restype = ctypes.c_int
+        L.orc_row_entropy.argtypes = [vp, ctypes.c_int, i64, f64]
+        L.orc_row_entropy.restype = f64
+        L.orc_expected_accept.argtypes = [vp, vp, i32, i32, i64, ctypes.c_int, f64, vp]
+        L.orc_expected_accept.restype = ctypes.c_int
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
@@ -217,6 +221,31 @@ def draft_sample(logits, dtype, T, seed=0, pos0=0, b_offset=0):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return res
+
+
+def row_entropy(row, dtype, T):
+    """H = -sum p ln p of softmax(row / T) (0 at T == 0; NaN if unusable)."""
+    row = _storage(row, dtype)
+    return lib().orc_row_entropy(_ptr(row), dtype, row.shape[-1], float(T))
+
+
+def entropies(logits, dtype, T):
+    """row_entropy of every row of logits [..., V]."""
+    a = _storage(logits, dtype)
+    flat = a.reshape(-1, a.shape[-1])
+    return np.array([row_entropy(r, dtype, T) for r in flat]).reshape(a.shape[:-1])
+
+
+def expected_accept(target, draft, dtype, T):
+    """beta [B, g] = sum_x min(p_i(x), q_i(x)) for target [B, g+1, V], draft [B, g, V]."""
+    target = _storage(target, dtype)
+    draft = _storage(draft, dtype)
+    B, g1, V = target.shape
+    out = np.full((B, g1 - 1), np.nan)
+    rc = lib().orc_expected_accept(_ptr(target), _ptr(draft), B, g1 - 1, V, dtype, float(T), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
 
 
 def max_threads():

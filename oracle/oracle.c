@@ -402,6 +402,48 @@ int orc_draft_sample(const void* logits, int32_t B, int32_t n, int64_t V, int dt
     return 0;
 }
 
+/* ------------------------------------------------------------------------- */
+/* Diagnostics: entropy of a row, expected acceptance per position             */
+/* ------------------------------------------------------------------------- */
+double orc_row_entropy(const void* row, int dtype, int64_t V, double T) {
+    if (T == 0.0) {
+        int64_t a;
+        return argmax_row(row, dtype, V, &a) ? 0.0 : NAN;
+    }
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    double H = NAN;
+    if (orc_row_softmax(row, dtype, V, T, p, NULL, NULL)) {
+        H = 0.0;
+        for (int64_t j = 0; j < V; ++j)
+            if (p[j] > 0.0) H -= p[j] * log(p[j]);
+    }
+    free(p);
+    return H;
+}
+
+int orc_expected_accept(const void* target, const void* draft, int32_t B, int32_t gamma,
+                        int64_t V, int dtype, double T, double* beta) {
+    if (!target || !draft || !beta) return -1;
+    if (B < 0 || gamma < 1 || V < 1 || (dtype != ORC_F32 && dtype != ORC_BF16)) return -1;
+    if (!(T > 0.0)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < (int64_t)B * gamma; ++r) {
+        const int64_t b = r / gamma, i = r % gamma;
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        double* q = (double*)malloc(sizeof(double) * (size_t)V);
+        double s = NAN;
+        if (orc_row_softmax(row_ptr(target, dtype, b * (gamma + 1) + i, V), dtype, V, T, p, NULL, NULL) &&
+            orc_row_softmax(row_ptr(draft, dtype, b * gamma + i, V), dtype, V, T, q, NULL, NULL)) {
+            s = 0.0;
+            for (int64_t j = 0; j < V; ++j) s += fmin(p[j], q[j]);
+        }
+        beta[r] = s;
+        free(p);
+        free(q);
+    }
+    return 0;
+}
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

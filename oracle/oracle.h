@@ -106,6 +106,22 @@ int orc_draft_sample(const void* logits, int32_t B, int32_t n, int64_t V, int dt
                      uint64_t seed, int64_t pos0, int64_t b_offset, int32_t* out_tokens,
                      double* out_q, double* cdf_lo, double* cdf_hi);
 
+/* Per-row diagnostics for choosing the draft length ([Ch15] 15.1.2, dynamic
+ * strategy adjustment: the acceptance-rate window rule; 15.2.3, adaptive
+ * draft length from the prediction entropy; Lemma 1 for the expected
+ * acceptance).
+ * orc_row_entropy: H = -sum_j p_j ln p_j of p = softmax(l / T) (natural log;
+ *   0 terms for p_j = 0); NaN for an unusable row. At T == 0 the distribution
+ *   is the point mass on the first argmax: H = 0 (NaN if unusable).
+ * orc_expected_accept: beta[b, i] = sum_x min(p_i(x), q_i(x)) for every
+ *   position i < gamma (target row i against draft row i; T > 0), the
+ *   probability that position i accepts its draft token given that it is
+ *   reached; NaN when either row is unusable. Returns 0, or -1 on bad
+ *   arguments. */
+double orc_row_entropy(const void* row, int dtype, int64_t V, double T);
+int orc_expected_accept(const void* target, const void* draft, int32_t B, int32_t gamma,
+                        int64_t V, int dtype, double T, double* beta);
+
 /* Threads the OpenMP runtime will use (1 when built without OpenMP). */
 int orc_max_threads(void);
 void orc_set_threads(int n);

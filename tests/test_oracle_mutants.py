@@ -33,6 +33,10 @@ MUTANTS = {
     "draft_position": ("(uint32_t)(b + b_offset), (uint32_t)(pos0 + t),", "(uint32_t)(b + b_offset), (uint32_t)(t),"),
     "draft_sequence": ("(uint32_t)(b + b_offset), (uint32_t)(pos0 + t),", "(uint32_t)(b), (uint32_t)(pos0 + t),"),
     "draft_q_cumulative": ("*q = p[j];", "*q = cdf[j] / Z;"),
+    "entropy_sign": ("if (p[j] > 0.0) H -= p[j] * log(p[j]);", "if (p[j] > 0.0) H += p[j] * log(p[j]);"),
+    "entropy_base2": ("if (p[j] > 0.0) H -= p[j] * log(p[j]);", "if (p[j] > 0.0) H -= p[j] * log2(p[j]);"),
+    "overlap_max": ("for (int64_t j = 0; j < V; ++j) s += fmin(p[j], q[j]);", "for (int64_t j = 0; j < V; ++j) s += fmax(p[j], q[j]);"),
+    "overlap_next_row": ("row_ptr(target, dtype, b * (gamma + 1) + i, V)", "row_ptr(target, dtype, b * (gamma + 1) + i + 1, V)"),
     "max_ignores_first": ("for (int64_t j = 0; j < V; ++j) {\n        double l = widen(row, dtype, j);\n        if (isnan(l) || l == INFINITY) usable = 0;\n        if (l > mx) mx = l;",
                           "for (int64_t j = 1; j < V; ++j) {\n        double l = widen(row, dtype, j);\n        if (isnan(l) || l == INFINITY) usable = 0;\n        if (l > mx) mx = l;"),
 }

@@ -556,3 +556,70 @@ def test_draft_unusable_and_masked_rows():
     many = oracle.draft_sample(np.broadcast_to(logits[0, 4], (400, 1, 6)), W.F32, 1.0, seed=9)
     assert set(np.unique(many.tokens)) == {1, 3, 5}
     np.testing.assert_allclose(many.q, 1.0 / 3, rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics for the draft length ([Ch15] 15.1.2 dynamic strategy adjustment;
+# 15.2.3 adaptive draft length from the prediction entropy; Lemma 1)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("V", [1, 2, 7, 1000])
+def test_entropy_of_equal_logits_is_log_V(V):
+    for T in (0.5, 1.0, 3.0):
+        assert abs(oracle.row_entropy(np.full(V, -1.25, np.float32), W.F32, T) - math.log(V)) <= 1e-12 * max(1, math.log(V))
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+@pytest.mark.parametrize("T", [0.4, 1.0, 2.5])
+def test_entropy_matches_scipy(dtype, T):
+    rng = np.random.default_rng(int(T * 10) + dtype)
+    for V in (2, 50, 3000):
+        l64 = rng.normal(0, 3, V)
+        if V > 10:
+            l64[rng.choice(V, 4, replace=False)] = -np.inf
+        row = W.to_storage(l64, dtype)
+        p = scipy.special.softmax(W.storage_to_f64(row, dtype) / T)
+        assert abs(oracle.row_entropy(row, dtype, T) - scipy.stats.entropy(p)) <= 1e-11
+
+
+def test_entropy_special_rows():
+    # two tokens: the binary entropy of p0 = 1 / (1 + e^((l1 - l0)/T))
+    l0, l1, T = 0.3, -1.1, 0.7
+    p0 = 1.0 / (1.0 + math.exp((float(np.float32(l1)) - float(np.float32(l0))) / T))
+    want = -p0 * math.log(p0) - (1 - p0) * math.log(1 - p0)
+    assert abs(oracle.row_entropy(np.array([l0, l1], np.float32), W.F32, T) - want) < 1e-14
+    one = np.full(9, -np.inf, np.float32)
+    one[4] = 2.0
+    assert oracle.row_entropy(one, W.F32, 1.0) == 0.0
+    assert oracle.row_entropy(np.array([1.0, 3.0, 3.0], np.float32), W.F32, 0.0) == 0.0
+    for bad in ([0.0, np.nan], [np.inf, 0.0], [-np.inf, -np.inf]):
+        for T in (1.0, 0.0):
+            assert math.isnan(oracle.row_entropy(np.array(bad, np.float32), W.F32, T))
+
+
+def test_expected_accept_worked_example():
+    g = json.load(open(os.path.join(HERE, "golden", "ex2_worked_vectors.json")))
+    t_row = W.log_probs(np.array(g["p"])).astype(np.float32)
+    d_row = W.log_probs(np.array(g["q"])).astype(np.float32)
+    beta = oracle.expected_accept(np.stack([t_row, t_row])[None], d_row[None, None], W.F32, 1.0)
+    assert abs(beta[0, 0] - g["accept_mass_num"] / g["accept_mass_den"]) < 1e-6
+
+
+def test_expected_accept_special_cases_and_lemma1():
+    inp = W.small_random_inputs(3, 4, 500, W.F32, 1.0, seed=6)
+    t = inp.target.copy()
+    d = inp.draft.copy()
+    d[0] = t[0, :4]                                  # identical rows: beta = 1
+    t[1, 1, :250] = -np.inf                          # disjoint supports: beta = 0
+    d[1, 1, 250:] = -np.inf
+    t[2, 2, 7] = np.nan                              # unusable: NaN
+    for T in (0.6, 1.0, 1.7):
+        beta = oracle.expected_accept(t, d, W.F32, T)
+        np.testing.assert_allclose(beta[0], 1.0, rtol=0, atol=1e-12)
+        assert beta[1, 1] == 0.0
+        assert math.isnan(beta[2, 2])
+        for b, i in ((1, 0), (1, 3), (2, 0), (2, 3)):
+            Z, _ = oracle.residual_cdf(t[b, i], d[b, i], W.F32, T)   # Lemma 1: sum min + sum max(0, p - q) = 1
+            assert abs(beta[b, i] + Z - 1.0) < 1e-12
+            p = scipy.special.softmax(t[b, i].astype(np.float64) / T)
+            q = scipy.special.softmax(d[b, i].astype(np.float64) / T)
+            assert abs(beta[b, i] - np.minimum(p, q).sum()) < 1e-12
