@@ -128,8 +128,10 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
     K, Wm, E = args.steps, args.warmup, max(1, args.event_stride)
     esz = 4 if wl.dtype == W.F32 else 2
     out = {}
-    for label, n, logits in (("all_positions", g, [s[1] for s in sets]),
-                             ("one_position", 1, [s[1][:, 0].contiguous() for s in sets])):
+    one = [s[1][:, 0].contiguous() for s in sets]
+    for label, n, logits, ent in (("all_positions", g, [s[1] for s in sets], False),
+                                  ("one_position", 1, one, False),
+                                  ("all_positions_with_entropy", g, [s[1] for s in sets], True)):
         dev = logits[0].device
         shape = (B, n) if n > 1 else (B,)
         toks = [torch.empty(shape, dtype=torch.int32, device=dev) for _ in logits]
@@ -138,7 +140,7 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
         def run(step, events=None):
             k = step % len(logits)
             sv.draft_sample(logits[k], wl.T, args.seed + k, out_tokens=toks[k], out_q=qs[k], stream=stream,
-                            events=events)
+                            events=events, want_entropy=ent)
         for s in range(Wm):
             run(s)
         evd = [i for i in range(K) if i % E == 0]
@@ -174,6 +176,37 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
     out["kernel"] = "k_draft"
     out["roofline_bound"] = "hbm"
     return out
+
+
+def expected_accept_leg(sv, sets, wl, args, stream):
+    """spec_expected_accept (every position's sum of min(p, q)) on the
+    workload: K calls rotating the input sets, timed by stream events around
+    the calls (three launches each: two statistics passes, the overlap)."""
+    import torch
+    B, g, V = wl.B, wl.gamma, wl.V
+    esz = 4 if wl.dtype == W.F32 else 2
+    outs = [torch.empty((B, g), dtype=torch.float64, device=sets[0][0].device) for _ in sets]
+
+    def run(step):
+        k = step % len(sets)
+        sv.expected_accept(sets[k][0], sets[k][1], wl.T, out=outs[k], stream=stream)
+    for s_ in range(args.warmup):
+        run(s_)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s_ in range(args.steps):
+        run(args.warmup + s_)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / args.steps * 1e3
+    read = ((g + 1) * B + g * B + 2 * g * B) * V * esz   # statistics of every row, then both rows of every pair
+    minimum = 2 * g * B * V * esz                          # every needed row once
+    beta = outs[0].cpu().numpy()
+    return {"us_per_call": us, "positions_per_s": B * g / (us * 1e-6), "bytes_read": read,
+            "achieved_GBps": read / (us * 1e-6) / 1e9, "frac": read / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+            "min_bytes": minimum, "mean_beta": float(np.nanmean(beta)), "roofline_bound": "hbm",
+            "kernels": ["k_verify (row statistics, twice)", "k_overlap"]}
 
 
 def main():
@@ -350,6 +383,7 @@ def main():
     # the draft-side sampler on the same workload's draft logits: all B x gamma
     # rows per call, and one position (B rows, one autoregressive step)
     draft = None if args.auto_only or wl.T == 0.0 else draft_leg(sv, hip, sets, host0, wl, args, stream)
+    overlap = None if args.auto_only or wl.T == 0.0 else expected_accept_leg(sv, sets, wl, args, stream)
 
     # one validation of the outputs of set 0 against the oracle (outside the timed region)
     call(0)
@@ -389,6 +423,8 @@ def main():
     }
     if draft is not None:
         result["draft_sampler"] = draft
+    if overlap is not None:
+        result["expected_accept"] = overlap
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or min(B, 64)
         result["cpu_baseline"] = cpu_baseline(host0, args.seed, sample, gpu_t, gpu_n)

@@ -184,12 +184,38 @@ int spec_draft_sample(const void* logits, int32_t B, int32_t n, int32_t V, int32
                       float temperature, uint64_t seed, int64_t pos0, int64_t b_offset,
                       int32_t* out_tokens, double* out_q, void* stream);
 
-/* spec_draft_sample, with events[0] and events[1] (hipEvent_t, may be NULL;
- * events may be NULL) bound to the start and end of the kernel dispatch, for
- * timing. */
+/* Optional outputs and timing of spec_draft_sample_ex; every field may be
+ * NULL. */
+typedef struct {
+    double* entropy;  /* [B, n] DEVICE: H = -sum_j p_j ln p_j of softmax(l/T) per row
+                         (natural log; 0 at T == 0; NaN for an unusable row), the
+                         confidence measure for choosing the draft length ([Ch15]
+                         15.2.3, adaptive draft length). Formed in the same pass. */
+    void* events[2];  /* hipEvent_t bound to the start and end of the dispatch */
+} spec_draft_extras_t;
+
+/* spec_draft_sample with optional extras (extras may be NULL). */
 int spec_draft_sample_ex(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype,
                          float temperature, uint64_t seed, int64_t pos0, int64_t b_offset,
-                         int32_t* out_tokens, double* out_q, void* stream, void* const events[2]);
+                         int32_t* out_tokens, double* out_q, void* stream,
+                         const spec_draft_extras_t* extras);
+
+/* spec_expected_accept: the probability that position i accepts its draft
+ * token when it is reached, beta[b, i] = sum_x min(p_i(x), q_i(x)) (Lemma 1
+ * of [Ch15] 15.1.2; 1 - beta_i is the residual mass of the correction step),
+ * for every position i < gamma: the per-position diagnostic behind the
+ * acceptance-rate rule for the draft length ([Ch15] 15.1.2, dynamic strategy
+ * adjustment).
+ *  target_logits [B, gamma+1, V], draft_logits [B, gamma, V]: dtype, DEVICE,
+ *      row-major contiguous (the bonus rows are not read); temperature > 0.
+ *  out_beta [B, gamma] double, DEVICE: beta, NaN where either row holds NaN
+ *      or +inf or no finite entry.
+ *  B * (gamma + 1) < 2^31. Reads every row twice (statistics, then the
+ *  overlap); three launches on stream, no synchronisation. Errors as
+ *  spec_verify. Uses the library's workspace of (device, stream). */
+int spec_expected_accept(const void* target_logits, const void* draft_logits, int32_t B,
+                         int32_t gamma, int32_t V, int32_t dtype, float temperature,
+                         double* out_beta, void* stream);
 
 /* The schedule SPEC_SCHEDULE_AUTO takes for this shape on the current device
  * (SPEC_SCHEDULE_GROUP or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
@@ -206,7 +232,8 @@ void spec_verify_release_workspace(void);
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* spec_verify_last_error(void);
 
-/* ABI version: 3 (2: spec_extras_t gained schedule; 3: spec_draft_sample). */
+/* ABI version: 4 (2: spec_extras_t gained schedule; 3: spec_draft_sample;
+ * 4: spec_draft_extras_t and spec_expected_accept). */
 int32_t spec_verify_abi_version(void);
 
 #ifdef __cplusplus

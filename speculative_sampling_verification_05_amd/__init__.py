@@ -25,6 +25,7 @@ EXPORTS = (
     "spec_row_stats",
     "spec_draft_sample",
     "spec_draft_sample_ex",
+    "spec_expected_accept",
     "spec_verify_schedule",
     "spec_verify_workspace_bytes",
     "spec_verify_release_workspace",
@@ -54,6 +55,14 @@ class Extras(ctypes.Structure):
     ]
 
 
+class DraftExtras(ctypes.Structure):
+    """Mirror of spec_draft_extras_t."""
+    _fields_ = [
+        ("entropy", ctypes.c_void_p),
+        ("events", ctypes.c_void_p * 2),
+    ]
+
+
 _lib = None
 
 
@@ -75,8 +84,11 @@ def load_library(path: str = LIB_PATH):
     L.spec_row_stats.restype = ctypes.c_int
     L.spec_draft_sample.argtypes = [vp, i32, i32, i32, i32, f32, u64, i64, i64, vp, vp, vp]
     L.spec_draft_sample.restype = ctypes.c_int
-    L.spec_draft_sample_ex.argtypes = [vp, i32, i32, i32, i32, f32, u64, i64, i64, vp, vp, vp, vp]
+    L.spec_draft_sample_ex.argtypes = [vp, i32, i32, i32, i32, f32, u64, i64, i64, vp, vp, vp,
+                                       ctypes.POINTER(DraftExtras)]
     L.spec_draft_sample_ex.restype = ctypes.c_int
+    L.spec_expected_accept.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp]
+    L.spec_expected_accept.restype = ctypes.c_int
     L.spec_verify_schedule.argtypes = [i32, i32, i32, i32, f32]
     L.spec_verify_schedule.restype = i32
     L.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
@@ -190,12 +202,14 @@ def row_stats(logits, temperature: float, stream=None):
 
 
 def draft_sample(logits, temperature: float, seed: int, pos0: int = 0, b_offset: int = 0,
-                 want_q: bool = True, out_tokens=None, out_q=None, stream=None, events=None):
+                 want_q: bool = True, out_tokens=None, out_q=None, stream=None, events=None,
+                 want_entropy: bool = False):
     """Draft tokens drawn from softmax(logits / T) (the first argmax at T == 0)
     for logits [B, n, V] (or [B, V], one position), float32 or bfloat16,
     contiguous, on the GPU; row (b, t) draws with the DRAFT uniform of counter
     (b + b_offset, pos0 + t). Returns (tokens int32, q float64 or None), each
-    [B, n] (or [B]); -1 and NaN mark unusable rows."""
+    [B, n] (or [B]); -1 and NaN mark unusable rows. With want_entropy, a third
+    tensor holds each row's entropy (float64, natural log)."""
     import torch
     L = load_library()
     if logits.dim() not in (2, 3) or not logits.is_cuda or not logits.is_contiguous():
@@ -211,12 +225,39 @@ def draft_sample(logits, temperature: float, seed: int, pos0: int = 0, b_offset:
         out_q = torch.empty(shape, dtype=torch.float64, device=dev)
     args = (_ptr(logits), B, n, V, _dtype_code(logits), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
             int(pos0), int(b_offset), _ptr(out_tokens), _ptr(out_q if want_q else None), _stream_handle(stream))
-    if events is None:
+    ent = torch.empty(shape, dtype=torch.float64, device=dev) if want_entropy else None
+    if events is None and ent is None:
         _check(L.spec_draft_sample(*args))
     else:
-        ev = (ctypes.c_void_p * 2)(*[ctypes.c_void_p(e) for e in events])
-        _check(L.spec_draft_sample_ex(*args, ev))
+        ex = DraftExtras()
+        ex.entropy = ent.data_ptr() if ent is not None else None
+        if events is not None:
+            ex.events[0], ex.events[1] = events
+        _check(L.spec_draft_sample_ex(*args, ctypes.byref(ex)))
+    if want_entropy:
+        return out_tokens, (out_q if want_q else None), ent
     return out_tokens, (out_q if want_q else None)
+
+
+def expected_accept(target_logits, draft_logits, temperature: float, out=None, stream=None):
+    """beta [B, gamma] float64: sum_x min(p_i(x), q_i(x)) for every position,
+    the probability that a reached position accepts its draft token; target
+    [B, gamma+1, V] and draft [B, gamma, V] on the GPU, same dtype, T > 0."""
+    import torch
+    L = load_library()
+    if target_logits.dim() != 3 or draft_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, V] and draft_logits [B, gamma, V]")
+    B, g1, V = target_logits.shape
+    for t in (target_logits, draft_logits):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("logits must be contiguous GPU tensors")
+    if draft_logits.dtype != target_logits.dtype or tuple(draft_logits.shape) != (B, g1 - 1, V):
+        raise ValueError("draft_logits must be [B, gamma, V] with the target's dtype")
+    if out is None:
+        out = torch.empty((B, g1 - 1), dtype=torch.float64, device=target_logits.device)
+    _check(L.spec_expected_accept(_ptr(target_logits), _ptr(draft_logits), B, g1 - 1, V, _dtype_code(target_logits),
+                                  float(temperature), _ptr(out), _stream_handle(stream)))
+    return out
 
 
 def auto_schedule(B, gamma, V, dtype, temperature) -> int:

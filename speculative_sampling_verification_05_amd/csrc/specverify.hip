@@ -666,6 +666,35 @@ __device__ inline float group_exp_sum(const typename Chunk<DT, VEC>::Raw* raw, f
     return a0 + a1;
 }
 
+// The same sum and, beside it, the sum of 2^t * t (t = fl(x*c - R)), for the
+// entropy (a zero mass contributes zero, also where t = -inf).
+template <int DT, bool VEC, int N>
+__device__ inline void group_exp_tsum(const typename Chunk<DT, VEC>::Raw* raw, float c, float R, float& sum,
+                                      float& tsum) {
+    using C = Chunk<DT, VEC>;
+    float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        float x[C::EPL];
+        C::expand(raw[u], x);
+#pragma unroll
+        for (int v = 0; v < C::EPL; ++v) {
+            const float t = fmaf(x[v], c, -R);
+            const float e = __builtin_amdgcn_exp2f(t);
+            const float et = e > 0.0f ? e * t : 0.0f;
+            if (v & 1) {
+                a1 += e;
+                b1 += et;
+            } else {
+                a0 += e;
+                b0 += et;
+            }
+        }
+    }
+    sum = a0 + a1;
+    tsum = b0 + b1;
+}
+
 template <int DT, bool VEC, int N>
 __device__ inline void consume_group(SoftLane& s, const typename Chunk<DT, VEC>::Raw* raw, int64_t, int,
                                      float c) {
@@ -2373,6 +2402,8 @@ struct DraftParams {
     double* out_q;        // [rows] or null
     double* part_s;       // T > 0: [rows, nw] sum of 2^(fl(x*c - R)) per range
     float* part_r;        //        and its integer reference R
+    double* part_h;       //        and the sum of 2^t * t, t = fl(x*c - R) (entropy wanted)
+    double* out_h;        // [rows] or null: entropy of softmax(l/T) per row
     float* part_m;        // T == 0: [rows, nw] maximum and its first index per range
     int32_t* part_i;
     uint32_t* cnt;        // [rows] counters, kDraftStride words apart
@@ -2508,10 +2539,10 @@ __device__ __attribute__((always_inline)) inline int32_t draft_pick_range(const 
     return tok;
 }
 
-template <int DT, bool VEC, bool GREEDY>
+template <int DT, bool VEC, bool GREEDY, bool ENT>
 __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane);
 
-template <int DT, bool VEC, bool GREEDY>
+template <int DT, bool VEC, bool GREEDY, bool ENT>
 __global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
@@ -2520,7 +2551,7 @@ __global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
     const int64_t sblocks = D.rows * D.nbr;
     if (blockIdx.x >= sblocks) {  // closing blocks: wavefront w finishes one row
         const int64_t row = (blockIdx.x - sblocks) * kWavesPerBlock + w;
-        if (row < D.rows) draft_finish<DT, VEC, GREEDY>(D, row, lane);
+        if (row < D.rows) draft_finish<DT, VEC, GREEDY, ENT>(D, row, lane);
         return;
     }
     const int64_t row = blockIdx.x / D.nbr;
@@ -2555,7 +2586,11 @@ __global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
             const float c = D.c32;
             float R = kRUnset;
             bool bad = false;
-            double S = 0.0;
+            double S = 0.0, SH = 0.0;  // (SH: sum of 2^t * t, for the entropy)
+            auto sums = [&](const Raw* qg, float& acc, float& acc_t) {
+                if constexpr (ENT) group_exp_tsum<DT, VEC, kUnroll>(qg, c, R, acc, acc_t);
+                else acc = group_exp_sum<DT, VEC, kUnroll>(qg, c, R);
+            };
 #pragma unroll
             for (int g = 0; g < kDraftCw / kUnroll; ++g) {
                 const Raw* qg = q + g * kUnroll;
@@ -2567,23 +2602,29 @@ __global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
                         else bad = true;  // +inf logit, or x*c overflows: the row is unusable
                     }
                 }
-                float acc = group_exp_sum<DT, VEC, kUnroll>(qg, c, R);
+                float acc = 0.0f, acc_t = 0.0f;
+                sums(qg, acc, acc_t);
                 if (__any(!(acc <= 3.0e38f))) {
                     const float Rn = ceilf(wave_max(group_max<DT, VEC, kUnroll>(qg)) * c);
                     if (!(Rn < 3.0e38f)) {
                         bad = true;
                     } else if (Rn > R) {
+                        // t shifts by R - Rn and every mass scales by 2^(R - Rn)
+                        if constexpr (ENT) SH = S == 0.0 ? 0.0 : rebase(SH + static_cast<double>(R - Rn) * S, R, Rn);
                         S = rebase(S, R, Rn);
                         R = Rn;
-                        acc = group_exp_sum<DT, VEC, kUnroll>(qg, c, R);
+                        sums(qg, acc, acc_t);
                     }  // else a NaN logit: the sum stays NaN
                 }
                 S += static_cast<double>(acc);
+                if constexpr (ENT) SH += static_cast<double>(acc_t);
             }
             S = wave_sum(S);
+            if constexpr (ENT) SH = wave_sum(SH);
             if (lane == 0) {
                 cst(D.part_s + pb + wl, bad ? static_cast<double>(NAN) : S);
                 cst(D.part_r + pb + wl, R);
+                if constexpr (ENT) cst(D.part_h + pb + wl, SH);
             }
         }
     }
@@ -2598,7 +2639,7 @@ __global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
 
 // The closing wavefront of a row: waits (bounded) until all of the row's
 // ranges have counted in, clears the counter for the next call, and draws.
-template <int DT, bool VEC, bool GREEDY>
+template <int DT, bool VEC, bool GREEDY, bool ENT>
 __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane) {
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
@@ -2640,6 +2681,7 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
             const bool good = isfinite(f.m);
             D.out_tokens[row] = good ? f.at : -1;
             if (D.out_q) D.out_q[row] = good ? 1.0 : static_cast<double>(NAN);
+            if (D.out_h) D.out_h[row] = good ? 0.0 : static_cast<double>(NAN);  // a point mass
         }
     } else {
         // the ranges' sums at the row's reference R (an exact power-of-two
@@ -2649,24 +2691,35 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
         const double* ps = D.part_s + row * D.nw;
         const float* pr = D.part_r + row * D.nw;
         const int32_t nw = D.nw;
-        double S = 0.0, before = 0.0, target = 0.0;
+        double S = 0.0, SH = 0.0, before = 0.0, target = 0.0;
         float R = kRUnset, rs = kRUnset;
         int32_t sel = -1;
         const int64_t b = row / D.n, t = row - b * D.n;
         const double u = philox_uniform(D.seed, static_cast<uint32_t>(b + D.b_offset),
                                         static_cast<uint32_t>(D.pos0 + t), kPurposeDraft);
+        // a range's sum of 2^t * t at the row's reference: 2^(r - R) * (h + (r - R) * s)
+        auto sh_at = [&](double h, double sv, float r) {
+            return sv == 0.0 ? 0.0 : rebase(h, r, R) + static_cast<double>(r - R) * rebase(sv, r, R);
+        };
         if (nw <= kFinTiles * kWave) {  // held in registers: one load round trip
             float r[kFinTiles];
-            double v[kFinTiles], incl[kFinTiles];
+            double v[kFinTiles], incl[kFinTiles], h[kFinTiles];
 #pragma unroll
             for (int t2 = 0; t2 < kFinTiles; ++t2) {
                 const int32_t k = t2 * kWave + lane;
                 r[t2] = k < nw ? cld(pr + k) : kRUnset;
                 v[t2] = k < nw ? cld(ps + k) : 0.0;
+                if constexpr (ENT) h[t2] = k < nw ? cld(D.part_h + row * D.nw + k) : 0.0;
             }
 #pragma unroll
             for (int t2 = 0; t2 < kFinTiles; ++t2) R = fmaxf(R, r[t2]);
             R = wave_max(R);
+            if constexpr (ENT) {
+                double sh = 0.0;
+#pragma unroll
+                for (int t2 = 0; t2 < kFinTiles; ++t2) sh += sh_at(h[t2], v[t2], r[t2]);
+                SH = wave_sum(sh);
+            }
 #pragma unroll
             for (int t2 = 0; t2 < kFinTiles; ++t2) v[t2] = rebase(v[t2], r[t2], R);
             S = regs_scan<kFinTiles>(v, incl, lane);
@@ -2686,6 +2739,12 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
             R = wave_max(R);
             auto val = [&](int32_t k) { return k < nw ? rebase(cld(ps + k), cld(pr + k), R) : 0.0; };
             for (int32_t t0 = 0; t0 < nw; t0 += kWave) S += lane_f64(wave_scan_incl(val(t0 + lane)), kWave - 1);
+            if constexpr (ENT) {
+                for (int32_t t0 = 0; t0 < nw; t0 += kWave) {
+                    const int32_t k = t0 + lane;
+                    SH += wave_sum(k < nw ? sh_at(cld(D.part_h + row * D.nw + k), cld(ps + k), cld(pr + k)) : 0.0);
+                }
+            }
             if (isfinite(S) && S > 0.0) {
                 target = u * S;
                 double base = 0.0, last_before = 0.0;
@@ -2732,8 +2791,115 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
         if (lane == 0) {
             D.out_tokens[row] = tok;
             if (D.out_q) D.out_q[row] = qv;
+            // H = -sum p ln p with p = 2^t / S: ln S - ln 2 * (sum 2^t t) / S
+            if (ENT && D.out_h)
+                D.out_h[row] = isfinite(S) && S > 0.0 ? log(S) - 0.69314718055994530942 * SH / S : static_cast<double>(NAN);
         }
     }
+}
+
+// ==========================================================================
+// Expected acceptance per position (Lemma 1 of [Ch15] 15.1.2: a draft token
+// drawn from q_i is accepted with probability beta_i = sum_x min(p_i(x),
+// q_i(x))), the diagnostic behind the acceptance-rate rule for the draft
+// length ([Ch15] 15.1.2, dynamic strategy adjustment). Given each row's
+// (max m, S = sum exp((l - m)/T)) from the statistics pass, p_j = 2^(fl(x_j*c)
+// - mc) * sp with mc = fl(m*c) and sp = 2^(mc - m*c)/S (likewise q). One
+// launch: wavefront ranges of kDraftCw chunks of both rows of a pair sum
+// min(p_j, q_j) (fp32 per load group, fp64 across); a closing wavefront per
+// pair adds the ranges in order.
+// ==========================================================================
+struct OverlapParams {
+    const void* tgt;  // [B, gamma + 1, V]
+    const void* dft;  // [B, gamma, V]
+    int32_t B, gamma, V, nchunk, nw, nbr;
+    float c32;
+    const float* m_t;   // [B * (gamma + 1)] row maxima and sums of the target rows
+    const double* s_t;
+    const float* m_d;   // [B * gamma] of the draft rows
+    const double* s_d;
+    double* part;       // [pairs, nw]
+    uint32_t* cnt;      // [pairs] counters, kDraftStride words apart
+    uint32_t* err;
+    double* out_beta;   // [B * gamma]
+};
+
+template <int DT, bool VEC>
+__device__ inline void overlap_finish(const OverlapParams& O, int64_t pair, int lane) {
+    uint32_t* cnt = O.cnt + pair * kDraftStride;
+    const uint32_t want = static_cast<uint32_t>(O.nw);
+    int ok = 1;
+    if (lane == 0) {
+        if (cld(cnt) < want) {
+            const uint64_t t0 = wall_clock64();
+            for (;;) {
+                __builtin_amdgcn_s_sleep(kSleep);
+                if (cld(cnt) >= want) break;
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    cst(O.err, 1u);
+                    ok = 0;
+                    break;
+                }
+            }
+        }
+        if (ok) cst(cnt, 0u);
+    }
+    ok = __shfl(ok, 0, kWave);
+    after_complete();
+    double acc = 0.0;
+    for (int32_t k = lane; k < O.nw; k += kWave) acc += cld(O.part + pair * O.nw + k);
+    acc = wave_sum(acc);
+    if (lane == 0) O.out_beta[pair] = ok ? acc : static_cast<double>(NAN);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_overlap(OverlapParams O) {
+    using C = Chunk<DT, VEC>;
+    using Raw = typename C::Raw;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+    const int64_t pairs = static_cast<int64_t>(O.B) * O.gamma;
+    const int64_t sblocks = pairs * O.nbr;
+    if (blockIdx.x >= sblocks) {  // closing blocks: wavefront w finishes one pair
+        const int64_t pair = (blockIdx.x - sblocks) * kWavesPerBlock + w;
+        if (pair < pairs) overlap_finish<DT, VEC>(O, pair, lane);
+        return;
+    }
+    const int64_t pair = blockIdx.x / O.nbr;
+    const int32_t wl = static_cast<int32_t>(blockIdx.x - pair * O.nbr) * kWavesPerBlock + w;
+    if (wl >= O.nw) return;
+    const int64_t b = pair / O.gamma, i = pair - b * O.gamma;
+    const int64_t rt = b * (O.gamma + 1) + i;
+    const float c = O.c32;
+    const float mp = O.m_t[rt], mq = O.m_d[pair];
+    const double Sp = O.s_t[rt], Sq = O.s_d[pair];
+    const bool ok = isfinite(Sp) && isfinite(Sq) && Sp > 0.0 && Sq > 0.0;
+    const float mcp = mp * c, mcq = mq * c;
+    const float sp = ok ? static_cast<float>(exp2(static_cast<double>(mcp) - static_cast<double>(mp) * c) / Sp) : 0.0f;
+    const float sq = ok ? static_cast<float>(exp2(static_cast<double>(mcq) - static_cast<double>(mq) * c) / Sq) : 0.0f;
+    const int64_t c0 = static_cast<int64_t>(wl) * kDraftCw;
+    Raw qp[kDraftCw], qq[kDraftCw];
+    load_slots<DT, VEC, kDraftCw>(qp, row_at<DT>(O.tgt, rt * O.V), c0, O.nchunk, O.V, lane);
+    load_slots<DT, VEC, kDraftCw>(qq, row_at<DT>(O.dft, pair * O.V), c0, O.nchunk, O.V, lane);
+    mask_slots<DT, VEC, kDraftCw>(qp, c0, O.nchunk, O.V, lane);
+    mask_slots<DT, VEC, kDraftCw>(qq, c0, O.nchunk, O.V, lane);
+    double S = 0.0;
+#pragma unroll
+    for (int u = 0; u < kDraftCw; ++u) {
+        float xp[C::EPL], xq[C::EPL];
+        C::expand(qp[u], xp);
+        C::expand(qq[u], xq);
+        float a = 0.0f;
+#pragma unroll
+        for (int v = 0; v < C::EPL; ++v)
+            a += fminf(__builtin_amdgcn_exp2f(fmaf(xp[v], c, -mcp)) * sp, __builtin_amdgcn_exp2f(fmaf(xq[v], c, -mcq)) * sq);
+        S += static_cast<double>(a);
+    }
+    S = wave_sum(S);
+    if (lane == 0) cst(O.part + pair * O.nw + wl, ok ? S : static_cast<double>(NAN));
+    complete_before();
+    if (lane == 0)
+        (void)__hip_atomic_fetch_add(O.cnt + pair * kDraftStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ==========================================================================
@@ -3045,6 +3211,7 @@ DraftLayout plan_draft(int64_t rows, int32_t V, int32_t dtype, bool vec) {
     const size_t slots = static_cast<size_t>(rows) * d.nw;
     size_t o = 0;
     o = align_up(o + slots * sizeof(double), 256);   // part_s
+    o = align_up(o + slots * sizeof(double), 256);   // part_h
     o = align_up(o + slots * sizeof(float), 256);    // part_r
     o = align_up(o + slots * sizeof(float), 256);    // part_m
     o = align_up(o + slots * sizeof(int32_t), 256);  // part_i
@@ -3062,6 +3229,8 @@ void bind_draft(DraftLayout& L, const Workspace& ws) {
     size_t o = 0;
     d.part_s = reinterpret_cast<double*>(base + o);
     o += align_up(slots * sizeof(double), 256);
+    d.part_h = reinterpret_cast<double*>(base + o);
+    o += align_up(slots * sizeof(double), 256);
     d.part_r = reinterpret_cast<float*>(base + o);
     o += f4;
     d.part_m = reinterpret_cast<float*>(base + o);
@@ -3076,8 +3245,9 @@ void bind_draft(DraftLayout& L, const Workspace& ws) {
 template <int DT, bool VEC>
 void launch_draft_t(bool greedy, const DraftLayout& L, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid(static_cast<unsigned>(L.blocks)), block(kBlock);
-    if (greedy) hipExtLaunchKernelGGL((k_draft<DT, VEC, true>), grid, block, 0, st, e0, e1, 0, L.d);
-    else hipExtLaunchKernelGGL((k_draft<DT, VEC, false>), grid, block, 0, st, e0, e1, 0, L.d);
+    if (greedy) hipExtLaunchKernelGGL((k_draft<DT, VEC, true, false>), grid, block, 0, st, e0, e1, 0, L.d);
+    else if (L.d.out_h) hipExtLaunchKernelGGL((k_draft<DT, VEC, false, true>), grid, block, 0, st, e0, e1, 0, L.d);
+    else hipExtLaunchKernelGGL((k_draft<DT, VEC, false, false>), grid, block, 0, st, e0, e1, 0, L.d);
 }
 
 void launch_draft(int32_t dtype, bool vec, bool greedy, const DraftLayout& L, hipStream_t st, hipEvent_t e0,
@@ -3091,6 +3261,12 @@ void launch_draft(int32_t dtype, bool vec, bool greedy, const DraftLayout& L, hi
     }
 }
 
+template <int DT, bool VEC>
+void launch_overlap_t(const OverlapParams& O, int64_t blocks, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    hipExtLaunchKernelGGL((k_overlap<DT, VEC>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st, e0, e1, 0,
+                          O);
+}
+
 }  // namespace
 
 // ==========================================================================
@@ -3098,7 +3274,7 @@ void launch_draft(int32_t dtype, bool vec, bool greedy, const DraftLayout& L, hi
 // ==========================================================================
 extern "C" {
 
-int32_t spec_verify_abi_version(void) { return 3; }
+int32_t spec_verify_abi_version(void) { return 4; }
 
 const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
 
@@ -3254,7 +3430,7 @@ int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype, f
 
 int spec_draft_sample_ex(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype, float temperature,
                          uint64_t seed, int64_t pos0, int64_t b_offset, int32_t* out_tokens, double* out_q,
-                         void* stream, void* const events[2]) {
+                         void* stream, const spec_draft_extras_t* extras) {
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EDTYPE, "dtype must be SPEC_F32 or SPEC_BF16");
     if (B < 1 || n < 1 || V < 1) return fail(SPEC_EINVAL, "B, n and V must be >= 1");
     if (pos0 < 0 || b_offset < 0) return fail(SPEC_EINVAL, "pos0 and b_offset must be >= 0");
@@ -3286,10 +3462,98 @@ int spec_draft_sample_ex(const void* logits, int32_t B, int32_t n, int32_t V, in
     d.b_offset = b_offset;
     d.out_tokens = out_tokens;
     d.out_q = out_q;
-    hipEvent_t e0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
-    hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+    d.out_h = extras ? extras->entropy : nullptr;
+    hipEvent_t e0 = extras ? static_cast<hipEvent_t>(extras->events[0]) : nullptr;
+    hipEvent_t e1 = extras ? static_cast<hipEvent_t>(extras->events[1]) : nullptr;
     launch_draft(dtype, vec, greedy, L, st, e0, e1);
     return check_launch("draft sampling kernel");
+}
+
+int spec_expected_accept(const void* target_logits, const void* draft_logits, int32_t B, int32_t gamma, int32_t V,
+                         int32_t dtype, float temperature, double* out_beta, void* stream) {
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EDTYPE, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (B < 1 || gamma < 1 || V < 1) return fail(SPEC_EINVAL, "B, gamma and V must be >= 1");
+    if (!(temperature > 0.0f)) return fail(SPEC_EINVAL, "temperature must be > 0");
+    if (!target_logits || !draft_logits || !out_beta) return fail(SPEC_EINVAL, "null pointer argument");
+    const float c32 = fold_temperature(temperature);
+    if (!(std::isfinite(c32) && c32 > 0.0f)) return fail(SPEC_EINVAL, "temperature out of range");
+    const int64_t pairs = static_cast<int64_t>(B) * gamma;
+    const int64_t trows = static_cast<int64_t>(B) * (gamma + 1);
+    if (trows >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
+                     aligned16(draft_logits);
+    Layout Lt = plan(kRows, trows, 1, V, dtype, vec, 1), Ld = plan(kRows, pairs, 1, V, dtype, vec, 1);
+    if (int rc = check_size(kRows, Lt)) return rc;
+    const int32_t nchunk = static_cast<int32_t>(ceil_div(V, chunk_elems(dtype, vec)));
+    const int32_t nw = static_cast<int32_t>(ceil_div(nchunk, kDraftCw));
+    const int32_t nbr = static_cast<int32_t>(ceil_div(nw, kWavesPerBlock));
+    const int64_t blocks = pairs * nbr + ceil_div(pairs, kWavesPerBlock);
+    if (blocks * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_mu);
+    const int cus = compute_units(dev);
+    Lt = plan(kRows, trows, 1, V, dtype, vec, cus);
+    Ld = plan(kRows, pairs, 1, V, dtype, vec, cus);
+    // the statistics passes use the front of the workspace; the row statistics
+    // and the overlap partials follow
+    const size_t o_mt = align_up(std::max(Lt.bytes, Ld.bytes), 256);
+    const size_t o_st = align_up(o_mt + static_cast<size_t>(trows) * sizeof(float), 256);
+    const size_t o_md = align_up(o_st + static_cast<size_t>(trows) * sizeof(double), 256);
+    const size_t o_sd = align_up(o_md + static_cast<size_t>(pairs) * sizeof(float), 256);
+    const size_t o_pt = align_up(o_sd + static_cast<size_t>(pairs) * sizeof(double), 256);
+    Layout need{};
+    need.bytes = align_up(o_pt + static_cast<size_t>(pairs) * nw * sizeof(double), 256);
+    need.cnt_words = std::max({Lt.cnt_words, Ld.cnt_words, pairs * kDraftStride});
+    need.dec_words = std::max(Lt.dec_words, Ld.dec_words);
+    Workspace* ws = nullptr;
+    if (int rc = get_workspace(dev, st, need, &ws)) return rc;
+    char* base = static_cast<char*>(ws->data);
+    OverlapParams O{};
+    O.tgt = target_logits;
+    O.dft = draft_logits;
+    O.B = B;
+    O.gamma = gamma;
+    O.V = V;
+    O.nchunk = nchunk;
+    O.nw = nw;
+    O.nbr = nbr;
+    O.c32 = c32;
+    O.m_t = reinterpret_cast<float*>(base + o_mt);
+    O.s_t = reinterpret_cast<double*>(base + o_st);
+    O.m_d = reinterpret_cast<float*>(base + o_md);
+    O.s_d = reinterpret_cast<double*>(base + o_sd);
+    O.part = reinterpret_cast<double*>(base + o_pt);
+    O.cnt = ws->sync;
+    const size_t off_dec = align_up(static_cast<size_t>(ws->cnt_cap) * sizeof(uint32_t), 256);
+    O.err = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws->sync) + off_dec +
+                                        static_cast<size_t>(ws->dec_cap) * sizeof(uint64_t));
+    O.out_beta = out_beta;
+    // the statistics of every target row and every draft row (the same kernel
+    // and code as spec_row_stats), then the overlap
+    bind_workspace(Lt, *ws);
+    Lt.p.c32 = c32;
+    Lt.p.tgt = target_logits;
+    Lt.p.rows_max = const_cast<float*>(O.m_t);
+    Lt.p.rows_sumexp = const_cast<double*>(O.s_t);
+    launch(dtype, vec, kRows, Lt, st);
+    if (int rc = check_launch("statistics kernel")) return rc;
+    bind_workspace(Ld, *ws);
+    Ld.p.c32 = c32;
+    Ld.p.tgt = draft_logits;
+    Ld.p.rows_max = const_cast<float*>(O.m_d);
+    Ld.p.rows_sumexp = const_cast<double*>(O.s_d);
+    launch(dtype, vec, kRows, Ld, st);
+    if (int rc = check_launch("statistics kernel")) return rc;
+    if (dtype == SPEC_F32) {
+        if (vec) launch_overlap_t<SPEC_F32, true>(O, blocks, st, nullptr, nullptr);
+        else launch_overlap_t<SPEC_F32, false>(O, blocks, st, nullptr, nullptr);
+    } else {
+        if (vec) launch_overlap_t<SPEC_BF16, true>(O, blocks, st, nullptr, nullptr);
+        else launch_overlap_t<SPEC_BF16, false>(O, blocks, st, nullptr, nullptr);
+    }
+    return check_launch("overlap kernel");
 }
 
 int spec_draft_sample(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype, float temperature,

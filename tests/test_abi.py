@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = sv.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_verify_abi_version() == 3
+    assert lib.spec_verify_abi_version() == 4
 
 
 def _call(B=2, gamma=3, V=10, dtype=0, T=1.0, tgt=1, dft=1, tok=1, out_t=1, out_n=1):
@@ -93,3 +93,16 @@ def _draft(B=2, n=3, V=10, dtype=0, T=1.0, pos0=0, b_offset=0, logits=1, out_t=1
 def test_draft_sample_argument_checks(kw, code):
     assert _draft(**kw) == code
     assert sv.last_error() != ""
+
+
+def test_expected_accept_argument_checks():
+    lib = sv.load_library()
+    P = ctypes.c_void_p
+    ok = (P(1), P(1), 2, 3, 10, 0, 1.0, P(1), None)
+    for i, bad, code in ((5, 4, sv.SPEC_EDTYPE), (2, 0, sv.SPEC_EINVAL), (3, 0, sv.SPEC_EINVAL),
+                         (4, 0, sv.SPEC_EINVAL), (6, 0.0, sv.SPEC_EINVAL), (6, float("nan"), sv.SPEC_EINVAL),
+                         (0, None, sv.SPEC_EINVAL), (1, None, sv.SPEC_EINVAL), (7, None, sv.SPEC_EINVAL)):
+        args = list(ok)
+        args[i] = bad
+        assert lib.spec_expected_accept(*args) == code, (i, bad)
+        assert sv.last_error() != ""

@@ -125,3 +125,89 @@ def test_draft_two_dim_input_and_no_q():
     assert q is None and tuple(tok.shape) == (4,)
     orc = oracle.draft_sample(inp.draft, W.F32, 1.0, seed=4, pos0=3)
     assert (tok.cpu().numpy() == orc.tokens[:, 0]).mean() >= 0.75
+
+
+@pytest.mark.parametrize("B,n,V,dtype", [(3, 4, 1000, W.F32), (2, 3, 40000, W.BF16), (2, 2, 1003, W.F32),
+                                         (1, 2, 262144, W.F32), (2, 2, 128256, W.BF16)])
+@pytest.mark.parametrize("T", [0.7, 1.3, 0.0])
+def test_draft_entropy(B, n, V, dtype, T):
+    # the entropy beside the draw ([Ch15] 15.2.3): the same tokens as without
+    # it, and H within 1e-5 of the oracle's (absolute, plus 1e-5 relative)
+    inp = W.small_random_inputs(B, n, V, dtype, 1.0, seed=V % 31 + n)
+    l64 = W.storage_to_f64(inp.draft, dtype)
+    l64[0, 0, : V // 2] = -np.inf                     # masked half
+    logits = W.to_storage(l64, dtype)
+    x = G.to_device(logits, dtype)
+    tok, q, H = sv.draft_sample(x, T, 3, want_entropy=True)
+    tok2, q2 = sv.draft_sample(x, T, 3)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(tok.cpu().numpy(), tok2.cpu().numpy())
+    np.testing.assert_array_equal(q.cpu().numpy(), q2.cpu().numpy())
+    want = oracle.entropies(logits, dtype, T)
+    got = H.cpu().numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-5)
+
+
+def test_draft_entropy_edge_rows():
+    V = 3000
+    l64 = np.random.default_rng(2).normal(0, 1, (1, 5, V))
+    l64[0, 0, 5] = np.nan
+    l64[0, 1, :] = -np.inf
+    l64[0, 2, :] = -np.inf
+    l64[0, 2, 2999] = 4.0                                # one token: H = 0
+    l64[0, 3, :] = 0.25                                  # equal logits: H = ln V
+    logits = W.to_storage(l64, W.BF16)
+    for T in (1.0, 0.0):
+        tok, q, H = sv.draft_sample(G.to_device(logits, W.BF16), T, 1, want_entropy=True)
+        torch.cuda.synchronize()
+        H = H.cpu().numpy()[0]
+        assert np.isnan(H[0]) and np.isnan(H[1])
+        assert abs(H[2]) < 1e-6
+        assert abs(H[3] - (np.log(V) if T > 0 else 0.0)) < 1e-5
+
+
+
+# ---------------------------------------------------------------------------
+# Expected acceptance per position (Lemma 1): sum_x min(p_i(x), q_i(x))
+# ---------------------------------------------------------------------------
+def gpu_beta(target, draft, dtype, T):
+    print(f"expected_accept B={target.shape[0]} gamma={draft.shape[1]} V={target.shape[2]} dtype={dtype} T={T}",
+          flush=True)
+    out = sv.expected_accept(G.to_device(target, dtype), G.to_device(draft, dtype), T)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,g,V,dtype", [(3, 4, 1000, W.F32), (2, 3, 40000, W.BF16), (2, 2, 1003, W.F32),
+                                         (2, 2, 1001, W.BF16), (1, 1, 1, W.F32), (1, 2, 152064, W.BF16)])
+@pytest.mark.parametrize("T", [0.6, 1.0, 1.8])
+def test_expected_accept_shapes(B, g, V, dtype, T):
+    inp = W.small_random_inputs(B, g, V, dtype, T, seed=V % 13 + g)
+    got = gpu_beta(inp.target, inp.draft, dtype, T)
+    want = oracle.expected_accept(inp.target, inp.draft, dtype, T)
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
+
+
+def test_expected_accept_edge_rows_and_workload():
+    inp = W.small_random_inputs(3, 4, 5000, W.BF16, 1.0, seed=6)
+    t, d = inp.target.copy(), inp.draft.copy()
+    d[0] = t[0, :4]                                  # identical rows: 1
+    t64 = W.storage_to_f64(t, W.BF16)
+    d64 = W.storage_to_f64(d, W.BF16)
+    t64[1, 1, :2500] = -np.inf                       # disjoint supports: 0
+    d64[1, 1, 2500:] = -np.inf
+    t64[2, 2, 77] = np.nan                           # unusable: NaN
+    d64[2, 3, :] = -np.inf
+    t, d = W.to_storage(t64, W.BF16), W.to_storage(d64, W.BF16)
+    got = gpu_beta(t, d, W.BF16, 1.0)
+    np.testing.assert_allclose(got[0], 1.0, atol=1e-6)
+    assert got[1, 1] == 0.0
+    assert np.isnan(got[2, 2]) and np.isnan(got[2, 3])
+    want = oracle.expected_accept(t, d, W.BF16, 1.0)
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
+    # every position of the 64 x 8 x 128256 bf16 workload
+    wl = W.WORKLOADS[W.HEADLINE]
+    full = W.make_inputs(wl, 0)
+    got = gpu_beta(full.target, full.draft, wl.dtype, wl.T)
+    want = oracle.expected_accept(full.target, full.draft, wl.dtype, wl.T)
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
