@@ -73,6 +73,8 @@ def lib():
         L.orc_row_entropy.restype = f64
         L.orc_expected_accept.argtypes = [vp, vp, i32, i32, i64, ctypes.c_int, f64, vp]
         L.orc_expected_accept.restype = ctypes.c_int
+        L.orc_tree_verify.argtypes = [vp, vp, vp, vp, i32, i32, i64, ctypes.c_int, f64, f64, vp, vp, vp]
+        L.orc_tree_verify.restype = ctypes.c_int
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
@@ -246,6 +248,25 @@ def expected_accept(target, draft, dtype, T):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+def tree_verify(target, draft, parent, token, dtype, T, threshold):
+    """Token-tree verification (the pages' heuristic): target/draft [B, N, V]
+    storage arrays (draft may be None at T == 0), parent/token [B, N] int32.
+    Returns (tokens [B, N-1], nodes [B, N-1], n [B])."""
+    target = _storage(target, dtype)
+    draft = _storage(draft, dtype)
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    token = np.ascontiguousarray(token, dtype=np.int32)
+    B, N, V = target.shape
+    tok = np.full((B, N - 1), -7, np.int32)
+    nodes = np.full((B, N - 1), -7, np.int32)
+    n = np.full(B, -7, np.int32)
+    rc = lib().orc_tree_verify(_ptr(target), _ptr(draft), _ptr(parent), _ptr(token), B, N, V, dtype, float(T),
+                               float(threshold), _ptr(tok), _ptr(nodes), _ptr(n))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return tok, nodes, n
 
 
 def max_threads():

@@ -444,6 +444,94 @@ int orc_expected_accept(const void* target, const void* draft, int32_t B, int32_
     return 0;
 }
 
+/* ------------------------------------------------------------------------- */
+/* Token-tree verification ([CSDN] 3.2; [Ch15] 15.2.4), the page's heuristic  */
+/* ------------------------------------------------------------------------- */
+static void tree_one(const void* target, const void* draft, const int32_t* parent, const int32_t* token,
+                     int64_t b, int32_t N, int64_t V, int dtype, double T, double threshold,
+                     int32_t* out_tokens, int32_t* out_nodes, int32_t* out_n) {
+    const int32_t* par = parent + b * N;
+    const int32_t* tok = token + b * N;
+    int32_t* ot = out_tokens + b * (N - 1);
+    int32_t* on = out_nodes ? out_nodes + b * (N - 1) : NULL;
+    for (int32_t j = 0; j < N - 1; ++j) {
+        ot[j] = -1;
+        if (on) on[j] = -1;
+    }
+    for (int32_t j = 1; j < N; ++j)
+        if (par[j] < 0 || par[j] >= j) goto invalid;
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    double* q = (double*)malloc(sizeof(double) * (size_t)V);
+    int32_t v = 0, n = 0;
+    for (;;) {
+        int32_t best = -1;
+        double best_score = -1.0;
+        int has_child = 0;
+        for (int32_t c = v + 1; c < N; ++c)
+            if (par[c] == v) has_child = 1;
+        if (!has_child) break;
+        const void* trow = row_ptr(target, dtype, b * N + v, V);
+        if (T == 0.0) {
+            int64_t a;
+            if (!argmax_row(trow, dtype, V, &a)) goto invalid_free;
+            for (int32_t c = v + 1; c < N; ++c) {
+                if (par[c] != v) continue;
+                if (tok[c] < 0 || (int64_t)tok[c] >= V) goto invalid_free;
+                if (best < 0 && (int64_t)tok[c] == a) best = c;
+            }
+            if (best < 0) break;
+        } else {
+            if (!orc_row_softmax(trow, dtype, V, T, p, NULL, NULL) ||
+                !orc_row_softmax(row_ptr(draft, dtype, b * N + v, V), dtype, V, T, q, NULL, NULL))
+                goto invalid_free;
+            for (int32_t c = v + 1; c < N; ++c) {
+                if (par[c] != v) continue;
+                if (tok[c] < 0 || (int64_t)tok[c] >= V) goto invalid_free;
+                const double pp = p[tok[c]], qq = q[tok[c]];
+                double score;
+                if (pp == 0.0) score = 0.0;
+                else if (qq == 0.0) score = 1.0;
+                else score = fmin(1.0, pp / qq);
+                if (score > best_score) {
+                    best_score = score;
+                    best = c;
+                }
+            }
+            if (best_score < threshold) break;
+        }
+        ot[n] = tok[best];
+        if (on) on[n] = best;
+        ++n;
+        v = best;
+    }
+    out_n[b] = n;
+    free(p);
+    free(q);
+    return;
+invalid_free:
+    free(p);
+    free(q);
+invalid:
+    for (int32_t j = 0; j < N - 1; ++j) {
+        ot[j] = -1;
+        if (on) on[j] = -1;
+    }
+    out_n[b] = -1;
+}
+
+int orc_tree_verify(const void* target, const void* draft, const int32_t* parent,
+                    const int32_t* token, int32_t B, int32_t N, int64_t V, int dtype,
+                    double T, double threshold, int32_t* out_tokens, int32_t* out_nodes,
+                    int32_t* out_n) {
+    if (!target || !parent || !token || !out_tokens || !out_n) return -1;
+    if (B < 0 || N < 2 || V < 1 || (dtype != ORC_F32 && dtype != ORC_BF16)) return -1;
+    if (!(T >= 0.0) || (T > 0.0 && !draft)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b)
+        tree_one(target, draft, parent, token, b, N, V, dtype, T, threshold, out_tokens, out_nodes, out_n);
+    return 0;
+}
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -122,6 +122,32 @@ double orc_row_entropy(const void* row, int dtype, int64_t V, double T);
 int orc_expected_accept(const void* target, const void* draft, int32_t B, int32_t gamma,
                         int64_t V, int dtype, double T, double* beta);
 
+/* Token-tree verification, a labelled heuristic mode ([CSDN] 3.2
+ * TokenTreeVerifier.parallel_verify; [Ch15] 15.2.4 candidate trees). It does
+ * NOT preserve the target distribution: it follows the page's rule.
+ * Sequence b has a tree of N nodes: node 0 is the root (the context), node
+ * j >= 1 holds token[b, j] and its parent parent[b, j] (0 <= parent < j).
+ * target [B, N, V] row j scores the children of node j (the target model's
+ * logits after the path to j); draft [B, N, V] row j likewise for the draft
+ * model (unused at T == 0).
+ * Walk from the root: among the children c of the current node v (ascending
+ * index), T > 0: score(c) = min(1, p_v(token c) / q_v(token c)) with
+ *   p_v = softmax(target row v / T), q_v = softmax(draft row v / T) (the
+ *   acceptance rule, R5 for zeros); the best child is the first with the
+ *   largest score; stop if there is no child or score(best) < threshold;
+ * T == 0: the first child whose token is the argmax of target row v (lowest
+ *   index on ties); stop if none.
+ * Otherwise append the best child's token and node and continue from it.
+ * Outputs: out_tokens [B, N-1] and out_nodes [B, N-1] (-1 after the path),
+ * out_n [B] = path length, or -1 when the walk reaches a node whose row (at
+ * T > 0 both rows) is unusable, a child token outside [0, V), or a parent
+ * index outside [0, j). out_nodes may be NULL. Returns 0, or -1 on bad
+ * arguments. */
+int orc_tree_verify(const void* target, const void* draft, const int32_t* parent,
+                    const int32_t* token, int32_t B, int32_t N, int64_t V, int dtype,
+                    double T, double threshold, int32_t* out_tokens, int32_t* out_nodes,
+                    int32_t* out_n);
+
 /* Threads the OpenMP runtime will use (1 when built without OpenMP). */
 int orc_max_threads(void);
 void orc_set_threads(int n);

@@ -37,6 +37,11 @@ MUTANTS = {
     "entropy_base2": ("if (p[j] > 0.0) H -= p[j] * log(p[j]);", "if (p[j] > 0.0) H -= p[j] * log2(p[j]);"),
     "overlap_max": ("for (int64_t j = 0; j < V; ++j) s += fmin(p[j], q[j]);", "for (int64_t j = 0; j < V; ++j) s += fmax(p[j], q[j]);"),
     "overlap_next_row": ("row_ptr(target, dtype, b * (gamma + 1) + i, V)", "row_ptr(target, dtype, b * (gamma + 1) + i + 1, V)"),
+    "tree_last_tie": ("if (score > best_score) {", "if (score >= best_score) {"),
+    "tree_threshold_inclusive": ("if (best_score < threshold) break;", "if (best_score <= threshold) break;"),
+    "tree_child_row": ("const void* trow = row_ptr(target, dtype, b * N + v, V);",
+                       "const void* trow = row_ptr(target, dtype, b * N + (v + 1 < N ? v + 1 : v), V);"),
+    "tree_target_only": ("else score = fmin(1.0, pp / qq);", "else score = fmin(1.0, pp);"),
     "max_ignores_first": ("for (int64_t j = 0; j < V; ++j) {\n        double l = widen(row, dtype, j);\n        if (isnan(l) || l == INFINITY) usable = 0;\n        if (l > mx) mx = l;",
                           "for (int64_t j = 1; j < V; ++j) {\n        double l = widen(row, dtype, j);\n        if (isnan(l) || l == INFINITY) usable = 0;\n        if (l > mx) mx = l;"),
 }

@@ -623,3 +623,99 @@ def test_expected_accept_special_cases_and_lemma1():
             p = scipy.special.softmax(t[b, i].astype(np.float64) / T)
             q = scipy.special.softmax(d[b, i].astype(np.float64) / T)
             assert abs(beta[b, i] - np.minimum(p, q).sum()) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Token-tree verification, the labelled heuristic mode ([CSDN] 3.2
+# TokenTreeVerifier.parallel_verify; [Ch15] 15.2.4)
+# ---------------------------------------------------------------------------
+def _hand_tree():
+    # root (node 0) -> node 1 (token 1), node 2 (token 2); node 1 -> node 3 (token 3)
+    p0, q0 = [0.1, 0.6, 0.2, 0.1], [0.3, 0.2, 0.4, 0.1]      # scores: node 1 min(1, .6/.2) = 1, node 2 .2/.4 = .5
+    p1, q1 = [0.5, 0.25, 0.125, 0.125], [0.25] * 4           # node 3: .125/.25 = .5; argmax of p1 is token 0
+    rows_t = np.stack([W.log_probs(p0), W.log_probs(p1), W.log_probs(p0), W.log_probs(p0)]).astype(np.float32)
+    rows_d = np.stack([W.log_probs(q0), W.log_probs(q1), W.log_probs(q0), W.log_probs(q0)]).astype(np.float32)
+    parent = np.array([[-1, 0, 0, 1]], np.int32)
+    token = np.array([[-1, 1, 2, 3]], np.int32)
+    return rows_t[None], rows_d[None], parent, token
+
+
+@pytest.mark.parametrize("threshold,path", [(0.4, [1, 3]), (0.6, [1]), (1.0, [1]), (1.01, []), (0.0, [1, 3])])
+def test_tree_hand_example(threshold, path):
+    t, d, parent, token = _hand_tree()
+    tok, nodes, n = oracle.tree_verify(t, d, parent, token, W.F32, 1.0, threshold)
+    assert n[0] == len(path)
+    assert list(nodes[0, :n[0]]) == path and (nodes[0, n[0]:] == -1).all()
+    assert list(tok[0, :n[0]]) == [int(token[0, j]) for j in path]
+
+
+def test_tree_hand_example_greedy_and_ties():
+    t, d, parent, token = _hand_tree()
+    tok, nodes, n = oracle.tree_verify(t, None, parent, token, W.F32, 0.0, 0.5)
+    assert n[0] == 1 and nodes[0, 0] == 1                  # root argmax = token 1; node 1's argmax 0 is no child
+    # two children with score 1: the first (lower index) is taken
+    token2 = token.copy()
+    token2[0, 2] = 3                                         # p0(3) = q0(3): score 1, like node 1
+    tok, nodes, n = oracle.tree_verify(t, d, parent, token2, W.F32, 1.0, 0.9)
+    assert nodes[0, 0] == 1
+    parent2 = np.array([[-1, 0, 0, 0]], np.int32)            # three root children: tokens 2, 1, 1
+    tok, nodes, n = oracle.tree_verify(t, d, parent2, np.array([[-1, 2, 1, 1]], np.int32), W.F32, 1.0, 0.9)
+    assert nodes[0, 0] == 2 and n[0] == 1                    # scores .5, 1, 1 (exactly): node 2 first at 1
+
+
+def test_tree_chain_equals_linear_verification():
+    # a chain (one child per node) with threshold tau accepts exactly where the
+    # linear rule with every accept uniform equal to tau does (alpha != tau)
+    for seed, T in ((1, 1.0), (2, 0.7)):
+        inp = W.small_random_inputs(40, 6, 300, W.F32, T, seed=seed)
+        g = 6
+        N = g + 1
+        parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (40, 1))
+        token = np.concatenate([np.full((40, 1), -1, np.int32), inp.tokens], axis=1)
+        t = inp.target[:, :N]
+        d = np.concatenate([inp.draft, inp.draft[:, -1:]], axis=1)   # row g has no child: unused
+        for tau in (0.3, 0.8):
+            tok, nodes, n = oracle.tree_verify(t, d, parent, token, W.F32, T, tau)
+            lin = oracle.verify_u(inp.target, inp.draft, inp.tokens, W.F32, T, np.full((40, g), tau),
+                                  np.full((40, g + 1), 0.5))
+            assert (lin.alpha[np.isfinite(lin.alpha)] != tau).all()
+            np.testing.assert_array_equal(n, lin.n)
+            for b in range(40):
+                assert list(tok[b, :n[b]]) == list(inp.tokens[b, :n[b]])
+                assert list(nodes[b, :n[b]]) == list(range(1, n[b] + 1))
+
+
+def test_tree_greedy_follows_argmax_and_zero_threshold_reaches_a_leaf():
+    tr = W.tree_inputs(6, 3, 3, 40, W.BF16, 1.0, seed=4)
+    t64 = W.storage_to_f64(tr.target, W.BF16)
+    tok, nodes, n = oracle.tree_verify(tr.target, None, tr.parent, tr.token, W.BF16, 0.0, 0.5)
+    for b in range(6):
+        v, path = 0, []
+        while True:
+            kids = [c for c in range(1, tr.parent.shape[1]) if tr.parent[b, c] == v]
+            a = int(np.argmax(t64[b, v]))
+            hit = [c for c in kids if tr.token[b, c] == a]
+            if not kids or not hit:
+                break
+            v = hit[0]
+            path.append(v)
+        assert list(nodes[b, :n[b]]) == path
+    tok, nodes, n = oracle.tree_verify(tr.target, tr.draft, tr.parent, tr.token, W.BF16, 1.0, 0.0)
+    assert (n == 3).all()
+
+
+def test_tree_invalid_inputs():
+    t, d, parent, token = _hand_tree()
+    bad_parent = parent.copy()
+    bad_parent[0, 2] = 2                                     # a parent must come before its child
+    assert oracle.tree_verify(t, d, bad_parent, token, W.F32, 1.0, 0.4)[2][0] == -1
+    bad_tok = token.copy()
+    bad_tok[0, 3] = 4                                        # out of range, on the walk
+    assert oracle.tree_verify(t, d, parent, bad_tok, W.F32, 1.0, 0.4)[2][0] == -1
+    assert oracle.tree_verify(t, d, parent, bad_tok, W.F32, 1.0, 1.01)[2][0] == 0  # node 1's children never scored
+    t2 = t.copy()
+    t2[0, 1, 0] = np.nan                                     # node 1's row, on the walk
+    assert oracle.tree_verify(t2, d, parent, token, W.F32, 1.0, 0.4)[2][0] == -1
+    t3 = t.copy()
+    t3[0, 2, 0] = np.nan                                     # node 2's row: never read
+    assert oracle.tree_verify(t3, d, parent, token, W.F32, 1.0, 0.4)[2][0] == 2

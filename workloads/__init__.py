@@ -242,3 +242,53 @@ def small_random_inputs(B: int, gamma: int, V: int, dtype: int, T: float, seed: 
     """Small i.i.d. Gaussian case of arbitrary shape (ragged V, odd gamma)."""
     wl = Workload(f"small_b{B}_g{gamma}_v{V}", B, gamma, V, dtype, T, "iid", sd, 0.0, draft_sd)
     return make_inputs(wl, seed)
+
+
+# ---------------------------------------------------------------------------
+# Token trees (the tree-verification mode's inputs)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class TreeInputs:
+    target: np.ndarray   # [B, N, V] storage: row j = the target model's logits after the path to node j
+    draft: np.ndarray    # [B, N, V] storage: the draft model's
+    parent: np.ndarray   # [B, N] int32: node 0 is the root (-1), node j >= 1 has parent < j
+    token: np.ndarray    # [B, N] int32: node j's token (-1 at the root)
+    dtype: int
+    T: float
+
+
+def tree_inputs(B: int, depth: int, branch: int, V: int, dtype: int, T: float, seed: int,
+                sd: float = 2.0, draft_sd: float = 0.7) -> TreeInputs:
+    """Full trees of `depth` levels below the root with `branch` children per
+    node, built level by level as a draft model's beam would: each node's
+    children are `branch` distinct tokens drawn without replacement from
+    softmax(draft row / T) (Gumbel top-k on the stored draft row). Rows are
+    i.i.d. Gaussian logits, the draft row the target row plus noise."""
+    N = sum(branch ** d for d in range(depth + 1))
+    st = np.float32 if dtype == F32 else np.uint16
+    target = np.empty((B, N, V), st)
+    draft = np.empty((B, N, V), st)
+    parent = np.full((B, N), -1, np.int32)
+    token = np.full((B, N), -1, np.int32)
+    for b in range(B):
+        rng = _seq_rng(seed, b, stream=7)
+        t = rng.normal(0.0, sd, size=(N, V))
+        d = t + rng.normal(0.0, draft_sd, size=(N, V))
+        target[b] = to_storage(t, dtype)
+        draft[b] = to_storage(d, dtype)
+        d_st = storage_to_f64(draft[b], dtype)
+        nxt = 1
+        level = [0]
+        for _ in range(depth):
+            new_level = []
+            for v in level:
+                g = -np.log(-np.log(rng.random(V)))
+                kids = np.argsort(-(d_st[v] / (T if T > 0 else 1.0) + g), kind="stable")[:branch]
+                for x in kids:
+                    parent[b, nxt] = v
+                    token[b, nxt] = int(x)
+                    new_level.append(nxt)
+                    nxt += 1
+            level = new_level
+        assert nxt == N
+    return TreeInputs(target, draft, parent, token, dtype, T)
