@@ -209,6 +209,54 @@ def expected_accept_leg(sv, sets, wl, args, stream):
             "kernels": ["k_verify (row statistics, twice)", "k_overlap"]}
 
 
+def tree_leg(sv, wl, args, stream):
+    """spec_tree_verify (the pages' token-tree heuristic) on seeded trees of
+    depth 3 and branching factor 3 ([CSDN] 3.2 uses 3) over the workload's
+    vocabulary and dtype: B = 8 trees of 40 nodes, every node's target and
+    draft rows (two sets of 164 MB at the headline shape, rotated). Timed by
+    stream events around the calls (three launches each)."""
+    import torch
+    dev = torch.device("cuda:0")
+    depth, branch, B = 3, 3, 8
+    tdt = torch.float32 if wl.dtype == W.F32 else torch.bfloat16
+
+    def to_dev(a):
+        if wl.dtype == W.BF16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+        return torch.from_numpy(a).to(dev)
+    sets = []
+    for k in range(2):
+        tr = W.tree_inputs(B, depth, branch, wl.V, wl.dtype, wl.T, seed=args.seed + 100 + k)
+        sets.append((to_dev(tr.target), to_dev(tr.draft), torch.from_numpy(tr.parent).to(dev),
+                     torch.from_numpy(tr.token).to(dev)))
+    N = sets[0][2].shape[1]
+    threshold = 0.3
+    res = {}
+
+    def run(step):
+        t, d, p, tk = sets[step % 2]
+        return sv.tree_verify(t, d, p, tk, wl.T, threshold, stream=stream)
+    for s_ in range(args.warmup):
+        run(s_)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s_ in range(args.steps):
+        run(args.warmup + s_)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / args.steps * 1e3
+    _, _, n = run(0)
+    nbytes = 2 * B * N * wl.V * (4 if wl.dtype == W.F32 else 2)
+    res = {"trees_per_call": B, "nodes_per_tree": N, "depth": depth, "branch": branch, "threshold": threshold,
+           "us_per_call": us, "nodes_per_s": B * N / (us * 1e-6), "bytes_per_call": nbytes,
+           "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+           "mean_accepted_path": float(n.float().mean().item()), "roofline_bound": "hbm",
+           "kernels": ["k_verify (row statistics, twice)", "k_tree_walk"],
+           "mode": "heuristic: not distribution-preserving"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,6 +432,7 @@ def main():
     # rows per call, and one position (B rows, one autoregressive step)
     draft = None if args.auto_only or wl.T == 0.0 else draft_leg(sv, hip, sets, host0, wl, args, stream)
     overlap = None if args.auto_only or wl.T == 0.0 else expected_accept_leg(sv, sets, wl, args, stream)
+    tree = None if args.auto_only or wl.T == 0.0 else tree_leg(sv, wl, args, stream)
 
     # one validation of the outputs of set 0 against the oracle (outside the timed region)
     call(0)
@@ -425,6 +474,8 @@ def main():
         result["draft_sampler"] = draft
     if overlap is not None:
         result["expected_accept"] = overlap
+    if tree is not None:
+        result["tree_verify"] = tree
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or min(B, 64)
         result["cpu_baseline"] = cpu_baseline(host0, args.seed, sample, gpu_t, gpu_n)

@@ -217,6 +217,34 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
                          int32_t gamma, int32_t V, int32_t dtype, float temperature,
                          double* out_beta, void* stream);
 
+/* spec_tree_verify: token-tree verification, a LABELLED HEURISTIC MODE that
+ * does not preserve the target distribution ([CSDN] 3.2,
+ * TokenTreeVerifier.parallel_verify; [Ch15] 15.2.4 candidate trees). From
+ * the root, among the children of the last accepted node the first child
+ * with the largest score is taken while its score reaches `threshold`;
+ * score = min(1, p_v(token)/q_v(token)) under the parent v's target and draft
+ * rows at temperature > 0; at temperature == 0 the child whose token is the
+ * target argmax of row v (lowest index on ties) is taken, if any. No
+ * correction or bonus token is emitted.
+ *  target_logits [B, N, V], draft_logits [B, N, V] (NULL allowed only at
+ *      temperature 0): dtype, DEVICE; row j = the model's logits after the
+ *      path to node j (scores node j's children).
+ *  parent [B, N], token [B, N] int32, DEVICE: node 0 is the root (its
+ *      entries are ignored); node j >= 1 has parent 0 <= parent[j] < j and
+ *      token token[j].
+ *  out_tokens [B, N-1], out_nodes [B, N-1] (may be NULL) int32, DEVICE: the
+ *      accepted path's tokens and nodes, -1 after it; out_n [B]: its length,
+ *      or -1 when a parent index is out of order, or the walk meets a child
+ *      token outside [0, V) or a needed row holding NaN, +inf or no finite
+ *      entry.
+ *  N >= 2, B * N < 2^31, threshold not NaN. Reads every row once (the
+ *  statistics of all nodes), then walks each tree with one wavefront. Errors
+ *  as spec_verify. Uses the library's workspace of (device, stream). */
+int spec_tree_verify(const void* target_logits, const void* draft_logits, const int32_t* parent,
+                     const int32_t* token, int32_t B, int32_t N, int32_t V, int32_t dtype,
+                     float temperature, float threshold, int32_t* out_tokens, int32_t* out_nodes,
+                     int32_t* out_n, void* stream);
+
 /* The schedule SPEC_SCHEDULE_AUTO takes for this shape on the current device
  * (SPEC_SCHEDULE_GROUP or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
 int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature);
@@ -232,8 +260,8 @@ void spec_verify_release_workspace(void);
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* spec_verify_last_error(void);
 
-/* ABI version: 4 (2: spec_extras_t gained schedule; 3: spec_draft_sample;
- * 4: spec_draft_extras_t and spec_expected_accept). */
+/* ABI version: 5 (2: spec_extras_t gained schedule; 3: spec_draft_sample;
+ * 4: spec_draft_extras_t and spec_expected_accept; 5: spec_tree_verify). */
 int32_t spec_verify_abi_version(void);
 
 #ifdef __cplusplus

@@ -173,3 +173,45 @@ def compare_draft(logits, dtype, T, orc, gpu_tokens, gpu_q, seed, pos0=0, b_offs
             else:
                 rep.hard_fail.append((b, t, "sample", to, tg, float(u), float(lo), float(hi)))
     return rep
+
+
+
+def tree_scores(target, draft, parent, token, dtype, T, b, v):
+    """The oracle's scores of node v's children in sequence b (index, score),
+    T > 0: min(1, p/q) in fp64; T == 0: 1 for the argmax child, else -1."""
+    from . import row_softmax
+    kids = [j for j in range(v + 1, parent.shape[1]) if parent[b, j] == v]
+    if T == 0:
+        a = int(np.argmax(np.asarray(target[b, v]).astype(np.float64) if dtype == 0 else
+                          (np.asarray(target[b, v]).astype(np.uint32) << 16).view(np.float32)))
+        return [(j, 1.0 if token[b, j] == a else -1.0) for j in kids]
+    _, p, _, _ = row_softmax(target[b, v], dtype, T)
+    _, q, _, _ = row_softmax(draft[b, v], dtype, T)
+    out = []
+    for j in kids:
+        pp, qq = p[token[b, j]], q[token[b, j]]
+        out.append((j, 0.0 if pp == 0 else (1.0 if qq == 0 else min(1.0, pp / qq))))
+    return out
+
+
+def compare_tree(target, draft, parent, token, dtype, T, threshold, orc, gpu_nodes, gpu_n):
+    """Tree walks against the oracle: identical paths, except where the first
+    differing step was a decision within BAND (the best two children's scores,
+    or the best score and the threshold). Returns (near, hard) lists."""
+    o_tok, o_nodes, o_n = orc
+    near, hard = [], []
+    for b in range(parent.shape[0]):
+        no, ng = int(o_n[b]), int(gpu_n[b])
+        if no == ng and np.array_equal(o_nodes[b, :max(no, 0)], gpu_nodes[b, :max(ng, 0)]):
+            continue
+        if no < 0 or ng < 0:
+            hard.append((b, "invalid", no, ng))
+            continue
+        k = 0
+        while k < min(no, ng) and o_nodes[b, k] == gpu_nodes[b, k]:
+            k += 1
+        v = 0 if k == 0 else int(o_nodes[b, k - 1])
+        sc = sorted((s_ for _, s_ in tree_scores(target, draft, parent, token, dtype, T, b, v)), reverse=True)
+        margin = min([abs(sc[0] - threshold)] + ([sc[0] - sc[1]] if len(sc) > 1 else []))
+        (near if T > 0 and margin < BAND else hard).append((b, k, margin))
+    return near, hard

@@ -26,6 +26,7 @@ EXPORTS = (
     "spec_draft_sample",
     "spec_draft_sample_ex",
     "spec_expected_accept",
+    "spec_tree_verify",
     "spec_verify_schedule",
     "spec_verify_workspace_bytes",
     "spec_verify_release_workspace",
@@ -89,6 +90,8 @@ def load_library(path: str = LIB_PATH):
     L.spec_draft_sample_ex.restype = ctypes.c_int
     L.spec_expected_accept.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp]
     L.spec_expected_accept.restype = ctypes.c_int
+    L.spec_tree_verify.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp, vp, vp]
+    L.spec_tree_verify.restype = ctypes.c_int
     L.spec_verify_schedule.argtypes = [i32, i32, i32, i32, f32]
     L.spec_verify_schedule.restype = i32
     L.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
@@ -258,6 +261,36 @@ def expected_accept(target_logits, draft_logits, temperature: float, out=None, s
     _check(L.spec_expected_accept(_ptr(target_logits), _ptr(draft_logits), B, g1 - 1, V, _dtype_code(target_logits),
                                   float(temperature), _ptr(out), _stream_handle(stream)))
     return out
+
+
+def tree_verify(target_logits, draft_logits, parent, token, temperature: float, threshold: float, stream=None):
+    """Token-tree verification, the pages' heuristic mode (not distribution-
+    preserving): target/draft [B, N, V] (draft may be None at T == 0), parent
+    and token [B, N] int32, all on the GPU. Returns (tokens [B, N-1], nodes
+    [B, N-1], n [B]) int32: the accepted path, -1 after it; n = -1 marks
+    invalid input."""
+    import torch
+    L = load_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, N, V]")
+    B, N, V = target_logits.shape
+    for t in (target_logits, draft_logits, parent, token):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("inputs must be contiguous GPU tensors")
+    if draft_logits is not None and (draft_logits.dtype != target_logits.dtype or
+                                     tuple(draft_logits.shape) != (B, N, V)):
+        raise ValueError("draft_logits must be [B, N, V] with the target's dtype")
+    for name, t in (("parent", parent), ("token", token)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B, N):
+            raise ValueError(f"{name} must be int32 [B, N]")
+    dev = target_logits.device
+    tok = torch.empty((B, N - 1), dtype=torch.int32, device=dev)
+    nodes = torch.empty((B, N - 1), dtype=torch.int32, device=dev)
+    n = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(L.spec_tree_verify(_ptr(target_logits), _ptr(draft_logits), _ptr(parent), _ptr(token), B, N, V,
+                              _dtype_code(target_logits), float(temperature), float(threshold), _ptr(tok),
+                              _ptr(nodes), _ptr(n), _stream_handle(stream)))
+    return tok, nodes, n
 
 
 def auto_schedule(B, gamma, V, dtype, temperature) -> int:

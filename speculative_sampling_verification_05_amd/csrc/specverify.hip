@@ -2903,6 +2903,124 @@ __global__ __launch_bounds__(kBlock) void k_overlap(OverlapParams O) {
 }
 
 // ==========================================================================
+// Token-tree verification, a labelled heuristic mode ([CSDN] 3.2
+// TokenTreeVerifier.parallel_verify; [Ch15] 15.2.4 candidate trees). Not
+// distribution-preserving: from the root, the children of the last accepted
+// node are scored by the acceptance probability min(1, p/q) of their tokens
+// under the parent's target and draft rows (T == 0: 1 for the child whose
+// token is the parent row's target argmax), the first child with the largest
+// score is taken while it reaches the threshold. The rows' statistics (or
+// argmaxes) come from the statistics kernels over every node's rows; the walk
+// itself is one wavefront per sequence gathering two logits per child.
+// ==========================================================================
+struct TreeParams {
+    const void* tgt;       // [B, N, V]
+    const void* dft;       // [B, N, V] (T > 0)
+    const int32_t* parent; // [B, N]
+    const int32_t* token;  // [B, N]
+    int32_t B, N, V;
+    double T;              // the temperature (0: greedy)
+    double threshold;
+    const float* m_t;      // [B * N] row maxima and sums (T > 0)
+    const double* s_t;
+    const float* m_d;
+    const double* s_d;
+    const int32_t* amax;   // [B * N] target argmax per row, -1 if unusable (T == 0)
+    int32_t* out_tokens;   // [B, N - 1]
+    int32_t* out_nodes;    // [B, N - 1] or null
+    int32_t* out_n;        // [B]
+};
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w;
+    if (b >= Q.B) return;
+    const int32_t N = Q.N;
+    const int32_t* par = Q.parent + b * N;
+    const int32_t* tok = Q.token + b * N;
+    int32_t* ot = Q.out_tokens + b * (N - 1);
+    int32_t* on = Q.out_nodes ? Q.out_nodes + b * (N - 1) : nullptr;
+    // every parent must come before its child
+    bool bad = false;
+    for (int32_t j = 1 + lane; j < N; j += kWave) bad |= par[j] < 0 || par[j] >= j;
+    bool invalid = __ballot(bad) != 0;
+    int32_t v = 0, n = 0;
+    while (!invalid) {
+        const int64_t rv = b * N + v;
+        bool usable_v = true;
+        double lmt = 0.0, lmd = 0.0, St = 0.0, Sd = 0.0;
+        int32_t av = -1;
+        if (Q.T > 0.0) {
+            lmt = Q.m_t[rv];
+            lmd = Q.m_d[rv];
+            St = Q.s_t[rv];
+            Sd = Q.s_d[rv];
+            usable_v = isfinite(St) && isfinite(Sd) && St > 0.0 && Sd > 0.0;
+        } else {
+            av = Q.amax[rv];
+            usable_v = av >= 0;
+        }
+        // the children of v, 64 at a time: (score desc, index asc)
+        double best_s = -2.0;
+        int32_t best = INT32_MAX;
+        bool any_child = false, bad_tok = false;
+        for (int32_t t0 = v + 1; t0 < N; t0 += kWave) {
+            const int32_t j = t0 + lane;
+            const bool child = j < N && par[j] == v;
+            double sc = -2.0;
+            if (child) {
+                const int32_t x = tok[j];
+                if (x < 0 || x >= Q.V) {
+                    bad_tok = true;
+                } else if (usable_v) {
+                    if (Q.T > 0.0) {
+                        // acceptance probability in fp64 from the two gathered logits
+                        const double lt = load_one<DT>(row_at<DT>(Q.tgt, rv * Q.V), x);
+                        const double ld = load_one<DT>(row_at<DT>(Q.dft, rv * Q.V), x);
+                        const double p = exp((lt - lmt) / Q.T) / St, q = exp((ld - lmd) / Q.T) / Sd;
+                        sc = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+                    } else {
+                        sc = x == av ? 1.0 : -1.0;
+                    }
+                }
+            }
+            any_child |= __ballot(child) != 0;
+            // fold this tile's candidates into (best_s, best): a later tile
+            // replaces the best only with a strictly larger score
+            double tile_max = sc;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) tile_max = fmax(tile_max, __shfl_xor(tile_max, o, kWave));
+            if (tile_max > best_s) {
+                const uint64_t at = __ballot(child && sc == tile_max);
+                best_s = tile_max;
+                best = t0 + (__ffsll(static_cast<unsigned long long>(at)) - 1);
+            }
+        }
+        if (__ballot(bad_tok) != 0 || (any_child && !usable_v)) {
+            invalid = true;
+            break;
+        }
+        if (!any_child) break;
+        if (Q.T > 0.0 ? best_s < Q.threshold : best_s < 1.0) break;
+        if (lane == 0) {
+            ot[n] = tok[best];
+            if (on) on[n] = best;
+        }
+        ++n;
+        v = best;
+    }
+    for (int32_t j = lane; j < N - 1; j += kWave) {
+        if (invalid || j >= n) {
+            ot[j] = -1;
+            if (on) on[j] = -1;
+        }
+    }
+    if (lane == 0) Q.out_n[b] = invalid ? -1 : n;
+}
+
+// ==========================================================================
 // Host side
 // ==========================================================================
 thread_local std::string g_last_error;
@@ -3274,7 +3392,7 @@ void launch_overlap_t(const OverlapParams& O, int64_t blocks, hipStream_t st, hi
 // ==========================================================================
 extern "C" {
 
-int32_t spec_verify_abi_version(void) { return 4; }
+int32_t spec_verify_abi_version(void) { return 5; }
 
 const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
 
@@ -3554,6 +3672,99 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
         else launch_overlap_t<SPEC_BF16, false>(O, blocks, st, nullptr, nullptr);
     }
     return check_launch("overlap kernel");
+}
+
+int spec_tree_verify(const void* target_logits, const void* draft_logits, const int32_t* parent,
+                     const int32_t* token, int32_t B, int32_t N, int32_t V, int32_t dtype, float temperature,
+                     float threshold, int32_t* out_tokens, int32_t* out_nodes, int32_t* out_n, void* stream) {
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EDTYPE, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (B < 1 || N < 2 || V < 1) return fail(SPEC_EINVAL, "need B >= 1, N >= 2 and V >= 1");
+    if (!(temperature >= 0.0f)) return fail(SPEC_EINVAL, "temperature must be >= 0 and not NaN");
+    if (std::isnan(threshold)) return fail(SPEC_EINVAL, "threshold must not be NaN");
+    const bool greedy = temperature == 0.0f;
+    if (!target_logits || !parent || !token || !out_tokens || !out_n || (!greedy && !draft_logits))
+        return fail(SPEC_EINVAL, "null pointer argument");
+    const float c32 = greedy ? 0.0f : fold_temperature(temperature);
+    if (!greedy && !(std::isfinite(c32) && c32 > 0.0f)) return fail(SPEC_EINVAL, "temperature out of range");
+    const int64_t rows = static_cast<int64_t>(B) * N;
+    if (rows >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
+                     (greedy || aligned16(draft_logits));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_mu);
+    const int cus = compute_units(dev);
+    TreeParams Q{};
+    Q.tgt = target_logits;
+    Q.dft = greedy ? nullptr : draft_logits;
+    Q.parent = parent;
+    Q.token = token;
+    Q.B = B;
+    Q.N = N;
+    Q.V = V;
+    Q.T = greedy ? 0.0 : static_cast<double>(temperature);
+    Q.threshold = threshold;
+    Q.out_tokens = out_tokens;
+    Q.out_nodes = out_nodes;
+    Q.out_n = out_n;
+    // every node's row statistics (T > 0: both models; T == 0: the target
+    // argmax) in front of the walk; the statistics kernels use the front of
+    // the workspace, the per-row results follow
+    if (!greedy) {
+        Layout L = plan(kRows, rows, 1, V, dtype, vec, cus);
+        if (int rc = check_size(kRows, L)) return rc;
+        const size_t o_mt = align_up(L.bytes, 256);
+        const size_t o_st = align_up(o_mt + static_cast<size_t>(rows) * sizeof(float), 256);
+        const size_t o_md = align_up(o_st + static_cast<size_t>(rows) * sizeof(double), 256);
+        const size_t o_sd = align_up(o_md + static_cast<size_t>(rows) * sizeof(float), 256);
+        Layout need = L;
+        need.bytes = align_up(o_sd + static_cast<size_t>(rows) * sizeof(double), 256);
+        Workspace* ws = nullptr;
+        if (int rc = get_workspace(dev, st, need, &ws)) return rc;
+        char* base = static_cast<char*>(ws->data);
+        float* mt = reinterpret_cast<float*>(base + o_mt);
+        double* stt = reinterpret_cast<double*>(base + o_st);
+        float* md = reinterpret_cast<float*>(base + o_md);
+        double* sd = reinterpret_cast<double*>(base + o_sd);
+        for (int k = 0; k < 2; ++k) {
+            Layout Lk = L;
+            bind_workspace(Lk, *ws);
+            Lk.p.c32 = c32;
+            Lk.p.tgt = k == 0 ? target_logits : draft_logits;
+            Lk.p.rows_max = k == 0 ? mt : md;
+            Lk.p.rows_sumexp = k == 0 ? stt : sd;
+            launch(dtype, vec, kRows, Lk, st);
+            if (int rc = check_launch("statistics kernel")) return rc;
+        }
+        Q.m_t = mt;
+        Q.s_t = stt;
+        Q.m_d = md;
+        Q.s_d = sd;
+    } else {
+        DraftLayout L = plan_draft(rows, V, dtype, vec);
+        if (L.blocks * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
+        const size_t o_am = align_up(L.ws.bytes, 256);
+        Layout need = L.ws;
+        need.bytes = align_up(o_am + static_cast<size_t>(rows) * sizeof(int32_t), 256);
+        Workspace* ws = nullptr;
+        if (int rc = get_workspace(dev, st, need, &ws)) return rc;
+        bind_draft(L, *ws);
+        int32_t* am = reinterpret_cast<int32_t*>(static_cast<char*>(ws->data) + o_am);
+        L.d.logits = target_logits;
+        L.d.n = 1;
+        L.d.c32 = 0.0f;
+        L.d.out_tokens = am;
+        L.d.out_q = nullptr;
+        L.d.out_h = nullptr;
+        launch_draft(dtype, vec, true, L, st, nullptr, nullptr);
+        if (int rc = check_launch("argmax kernel")) return rc;
+        Q.amax = am;
+    }
+    const dim3 grid(static_cast<unsigned>(ceil_div(B, kWavesPerBlock))), block(kBlock);
+    if (dtype == SPEC_F32) hipLaunchKernelGGL((k_tree_walk<SPEC_F32>), grid, block, 0, st, Q);
+    else hipLaunchKernelGGL((k_tree_walk<SPEC_BF16>), grid, block, 0, st, Q);
+    return check_launch("tree walk kernel");
 }
 
 int spec_draft_sample(const void* logits, int32_t B, int32_t n, int32_t V, int32_t dtype, float temperature,

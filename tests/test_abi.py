@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = sv.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_verify_abi_version() == 4
+    assert lib.spec_verify_abi_version() == 5
 
 
 def _call(B=2, gamma=3, V=10, dtype=0, T=1.0, tgt=1, dft=1, tok=1, out_t=1, out_n=1):
@@ -105,4 +105,18 @@ def test_expected_accept_argument_checks():
         args = list(ok)
         args[i] = bad
         assert lib.spec_expected_accept(*args) == code, (i, bad)
+        assert sv.last_error() != ""
+
+
+def test_tree_verify_argument_checks():
+    lib = sv.load_library()
+    P = ctypes.c_void_p
+    ok = [P(1), P(1), P(1), P(1), 2, 5, 10, 0, 1.0, 0.5, P(1), None, P(1), None]
+    for i, bad, code in ((7, 2, sv.SPEC_EDTYPE), (4, 0, sv.SPEC_EINVAL), (5, 1, sv.SPEC_EINVAL), (6, 0, sv.SPEC_EINVAL),
+                         (8, -1.0, sv.SPEC_EINVAL), (8, float("nan"), sv.SPEC_EINVAL), (9, float("nan"), sv.SPEC_EINVAL),
+                         (0, None, sv.SPEC_EINVAL), (1, None, sv.SPEC_EINVAL), (2, None, sv.SPEC_EINVAL),
+                         (3, None, sv.SPEC_EINVAL), (10, None, sv.SPEC_EINVAL), (12, None, sv.SPEC_EINVAL)):
+        args = list(ok)
+        args[i] = bad
+        assert lib.spec_tree_verify(*args) == code, (i, bad)
         assert sv.last_error() != ""

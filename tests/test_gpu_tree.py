@@ -1,0 +1,90 @@
+"""GPU parity of the token-tree verification mode ([CSDN] 3.2
+TokenTreeVerifier.parallel_verify; [Ch15] 15.2.4), a labelled heuristic that
+does not preserve the target distribution, through the C ABI against the
+oracle's walk on the same seeded trees.
+
+Tolerance: identical paths and lengths; at T > 0 a path may differ only where
+the oracle's decision at the first differing step was within 1e-6 (the best
+two scores, or the best score and the threshold), at most one such sequence
+per call or 0.1% of sequences; T == 0 and invalid inputs exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.compare import compare_tree
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import gpu_helpers as G
+    import speculative_sampling_verification_05_amd as sv
+
+
+def run_tree(tr, T, threshold, target=None, draft=None, parent=None, token=None):
+    target = tr.target if target is None else target
+    draft = tr.draft if draft is None else draft
+    parent = tr.parent if parent is None else parent
+    token = tr.token if token is None else token
+    B, N, V = target.shape
+    print(f"tree_verify B={B} N={N} V={V} dtype={tr.dtype} T={T} threshold={threshold}", flush=True)
+    dev = torch.device("cuda:0")
+    tok, nodes, n = sv.tree_verify(G.to_device(target, tr.dtype), G.to_device(draft, tr.dtype) if T > 0 else None,
+                                   torch.from_numpy(np.ascontiguousarray(parent)).to(dev),
+                                   torch.from_numpy(np.ascontiguousarray(token)).to(dev), T, threshold)
+    torch.cuda.synchronize()
+    gpu = (tok.cpu().numpy(), nodes.cpu().numpy(), n.cpu().numpy())
+    orc = oracle.tree_verify(target, draft if T > 0 else None, parent, token, tr.dtype, T, threshold)
+    near, hard = compare_tree(target, draft, parent, token, tr.dtype, T, threshold, orc, gpu[1], gpu[2])
+    assert not hard, hard[:5]
+    assert len(near) <= max(1, B // 1000), near
+    same = np.array([b not in {x[0] for x in near} for b in range(B)])
+    np.testing.assert_array_equal(gpu[0][same], orc[0][same])
+    np.testing.assert_array_equal(gpu[2][same], orc[2][same])
+    return gpu, orc
+
+
+TREES = [(8, 3, 3, 1000, W.F32), (6, 4, 2, 3000, W.BF16), (4, 2, 5, 1003, W.F32), (3, 5, 2, 40000, W.BF16),
+         (2, 3, 4, 128256, W.BF16), (5, 1, 70, 500, W.F32)]   # the last: 70 children of the root (two tiles)
+
+
+@pytest.mark.parametrize("B,depth,branch,V,dtype", TREES)
+@pytest.mark.parametrize("T,threshold", [(0.7, 0.3), (1.0, 0.0), (1.0, 0.9), (0.0, 0.5)])
+def test_tree_shapes(B, depth, branch, V, dtype, T, threshold):
+    tr = W.tree_inputs(B, depth, branch, V, dtype, T if T > 0 else 1.0, seed=V % 17 + depth)
+    gpu, orc = run_tree(tr, T, threshold)
+    if threshold == 0.0:
+        assert (gpu[2] == depth).all()      # every walk reaches a leaf
+
+
+def test_tree_invalid_and_unused_rows():
+    tr = W.tree_inputs(6, 3, 2, 2000, W.F32, 1.0, seed=3)
+    parent, token = tr.parent.copy(), tr.token.copy()
+    target, draft = tr.target.copy(), tr.draft.copy()
+    parent[0, 5] = 5                                   # a parent that does not come first
+    token[1, 1] = 2000                                 # a root child out of range: always scored
+    target[2, 0, 17] = np.nan                          # the root row
+    last = parent.shape[1] - 1
+    target[3, last, 3] = np.nan                        # a leaf's row: never needed
+    draft[4, last, 3] = np.inf
+    for T in (1.0, 0.0):
+        gpu, orc = run_tree(tr, T, 0.2, target=target, draft=draft, parent=parent, token=token)
+        assert list(gpu[2][:3]) == [-1, -1, -1]
+        assert (gpu[2][3:] >= 0).all()
+        assert (gpu[0][:3] == -1).all() and (gpu[1][:3] == -1).all()
+
+
+def test_tree_chain_matches_oracle_and_padding():
+    # a chain of 9 nodes: the walk is the linear accept loop with a fixed threshold
+    inp = W.small_random_inputs(16, 8, 5000, W.BF16, 1.0, seed=8)
+    N = 9
+    parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (16, 1))
+    token = np.concatenate([np.full((16, 1), -1, np.int32), inp.tokens], axis=1)
+    draft = np.concatenate([inp.draft, inp.draft[:, -1:]], axis=1)
+    tr = W.TreeInputs(inp.target, draft, parent, token, W.BF16, 1.0)
+    gpu, orc = run_tree(tr, 1.0, 0.5)
+    for b in range(16):
+        n = gpu[2][b]
+        assert list(gpu[1][b, :n]) == list(range(1, n + 1))
+        assert (gpu[0][b, n:] == -1).all() and (gpu[1][b, n:] == -1).all()

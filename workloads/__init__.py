@@ -263,7 +263,8 @@ def tree_inputs(B: int, depth: int, branch: int, V: int, dtype: int, T: float, s
     node, built level by level as a draft model's beam would: each node's
     children are `branch` distinct tokens drawn without replacement from
     softmax(draft row / T) (Gumbel top-k on the stored draft row). Rows are
-    i.i.d. Gaussian logits, the draft row the target row plus noise."""
+    i.i.d. Gaussian logits (drawn in fp32), the draft row the target row plus
+    noise."""
     N = sum(branch ** d for d in range(depth + 1))
     st = np.float32 if dtype == F32 else np.uint16
     target = np.empty((B, N, V), st)
@@ -272,8 +273,8 @@ def tree_inputs(B: int, depth: int, branch: int, V: int, dtype: int, T: float, s
     token = np.full((B, N), -1, np.int32)
     for b in range(B):
         rng = _seq_rng(seed, b, stream=7)
-        t = rng.normal(0.0, sd, size=(N, V))
-        d = t + rng.normal(0.0, draft_sd, size=(N, V))
+        t = rng.standard_normal((N, V), dtype=np.float32) * np.float32(sd)
+        d = t + rng.standard_normal((N, V), dtype=np.float32) * np.float32(draft_sd)
         target[b] = to_storage(t, dtype)
         draft[b] = to_storage(d, dtype)
         d_st = storage_to_f64(draft[b], dtype)
@@ -283,7 +284,9 @@ def tree_inputs(B: int, depth: int, branch: int, V: int, dtype: int, T: float, s
             new_level = []
             for v in level:
                 g = -np.log(-np.log(rng.random(V)))
-                kids = np.argsort(-(d_st[v] / (T if T > 0 else 1.0) + g), kind="stable")[:branch]
+                score = d_st[v] / (T if T > 0 else 1.0) + g
+                top = np.argpartition(-score, branch - 1)[:branch] if branch < V else np.arange(V)
+                kids = top[np.argsort(-score[top], kind="stable")]
                 for x in kids:
                     parent[b, nxt] = v
                     token[b, nxt] = int(x)
