@@ -2496,7 +2496,6 @@ template <int DT, bool VEC, int N>
 __device__ __attribute__((always_inline)) inline int32_t draft_pick_range(const typename Chunk<DT, VEC>::Raw* q, int64_t c0, float c, float rs,
                                            double sc, double before, double target, int lane, double& mass) {
     using C = Chunk<DT, VEC>;
-    using TL = Tiles<DT, VEC>;
     double cm[N];
 #pragma unroll
     for (int u = 0; u < N; ++u) {
@@ -2535,7 +2534,6 @@ __device__ __attribute__((always_inline)) inline int32_t draft_pick_range(const 
 #pragma unroll
     for (int u = 0; u < N; ++u)  // (a branch per chunk keeps the register indices constant)
         if (ch == u) tok = draft_pick<DT, VEC, 1>(q + u, c0 + u, c, rs, sc, cb, target, lane, mass);
-    (void)TL::EPT;
     return tok;
 }
 
