@@ -166,13 +166,17 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
         lg = host0.draft[:nb, :n]
         t = toks[0].cpu().numpy().reshape(B, n)[:nb]
         q = qs[0].cpu().numpy().reshape(B, n)[:nb]
+        t0 = time.perf_counter()
         orc = oracle.draft_sample(lg, wl.dtype, wl.T, seed=args.seed)
+        t_orc = time.perf_counter() - t0
         rep = compare_draft(lg, wl.dtype, wl.T, orc, t, q, args.seed)
         out[label] = {"rows_per_call": B * n, "ms_per_call": ms, "rows_per_s": B * n / (ms * 1e-3),
                       "kernel_us": k_us, "bytes_per_launch": nbytes, "achieved_GBps": achieved,
                       "frac": achieved / PEAK_HBM_GBPS, "launches_timed": len(kms),
                       "parity_vs_oracle": {"rows": rep.rows, "hard_failures": len(rep.hard_fail),
-                                           "near_boundary": rep.boundary}}
+                                           "near_boundary": rep.boundary},
+                      "cpu_baseline": {"value": rep.rows / t_orc, "unit": "rows/s", "cores": oracle.max_threads(),
+                                       "kind": "oracle", "sample": f"the first {nb} sequences' rows, one run"}}
     out["kernel"] = "k_draft"
     out["roofline_bound"] = "hbm"
     return out
@@ -181,7 +185,7 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
 def expected_accept_leg(sv, sets, wl, args, stream):
     """spec_expected_accept (every position's sum of min(p, q)) on the
     workload: K calls rotating the input sets, timed by stream events around
-    the calls (three launches each: two statistics passes, the overlap)."""
+    the calls (two launches each: the statistics pass, the overlap)."""
     import torch
     B, g, V = wl.B, wl.gamma, wl.V
     esz = 4 if wl.dtype == W.F32 else 2
@@ -203,10 +207,20 @@ def expected_accept_leg(sv, sets, wl, args, stream):
     read = ((g + 1) * B + g * B + 2 * g * B) * V * esz   # statistics of every row, then both rows of every pair
     minimum = 2 * g * B * V * esz                          # every needed row once
     beta = outs[0].cpu().numpy()
+    import oracle
+    host = W.make_inputs(wl, args.seed)
+    nb = 4
+    t0 = time.perf_counter()
+    ref = oracle.expected_accept(host.target[:nb], host.draft[:nb], wl.dtype, wl.T)
+    t_orc = time.perf_counter() - t0
+    err = float(np.nanmax(np.abs(beta[:nb] - ref)))
     return {"us_per_call": us, "positions_per_s": B * g / (us * 1e-6), "bytes_read": read,
             "achieved_GBps": read / (us * 1e-6) / 1e9, "frac": read / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
             "min_bytes": minimum, "mean_beta": float(np.nanmean(beta)), "roofline_bound": "hbm",
-            "kernels": ["k_verify (row statistics, twice)", "k_overlap"]}
+            "kernels": ["k_verify (row statistics of the target and the draft rows, one launch)", "k_overlap"],
+            "parity_vs_oracle": {"positions": nb * g, "max_abs_err": err},
+            "cpu_baseline": {"value": nb * g / t_orc, "unit": "positions/s", "cores": oracle.max_threads(),
+                             "kind": "oracle", "sample": f"the first {nb} sequences of input set 0, one run"}}
 
 
 def tree_leg(sv, wl, args, stream):
@@ -214,7 +228,7 @@ def tree_leg(sv, wl, args, stream):
     depth 3 and branching factor 3 ([CSDN] 3.2 uses 3) over the workload's
     vocabulary and dtype: B = 8 trees of 40 nodes, every node's target and
     draft rows (two sets of 164 MB at the headline shape, rotated). Timed by
-    stream events around the calls (three launches each)."""
+    stream events around the calls (two launches each)."""
     import torch
     dev = torch.device("cuda:0")
     depth, branch, B = 3, 3, 8
@@ -227,6 +241,8 @@ def tree_leg(sv, wl, args, stream):
     sets = []
     for k in range(2):
         tr = W.tree_inputs(B, depth, branch, wl.V, wl.dtype, wl.T, seed=args.seed + 100 + k)
+        if k == 0:
+            tr0 = tr
         sets.append((to_dev(tr.target), to_dev(tr.draft), torch.from_numpy(tr.parent).to(dev),
                      torch.from_numpy(tr.token).to(dev)))
     N = sets[0][2].shape[1]
@@ -246,14 +262,24 @@ def tree_leg(sv, wl, args, stream):
     end.record(stream)
     torch.cuda.synchronize()
     us = start.elapsed_time(end) / args.steps * 1e3
-    _, _, n = run(0)
+    _, nodes, n = run(0)
+    import oracle
+    from oracle.compare import compare_tree
+    t0 = time.perf_counter()
+    orc = oracle.tree_verify(tr0.target, tr0.draft, tr0.parent, tr0.token, wl.dtype, wl.T, threshold)
+    t_orc = time.perf_counter() - t0
+    near, hard = compare_tree(tr0.target, tr0.draft, tr0.parent, tr0.token, wl.dtype, wl.T, threshold, orc,
+                              nodes.cpu().numpy(), n.cpu().numpy())
     nbytes = 2 * B * N * wl.V * (4 if wl.dtype == W.F32 else 2)
     res = {"trees_per_call": B, "nodes_per_tree": N, "depth": depth, "branch": branch, "threshold": threshold,
            "us_per_call": us, "nodes_per_s": B * N / (us * 1e-6), "bytes_per_call": nbytes,
            "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
            "mean_accepted_path": float(n.float().mean().item()), "roofline_bound": "hbm",
-           "kernels": ["k_verify (row statistics, twice)", "k_tree_walk"],
-           "mode": "heuristic: not distribution-preserving"}
+           "kernels": ["k_verify (row statistics of every node's two rows, one launch)", "k_tree_walk"],
+           "mode": "heuristic: not distribution-preserving",
+           "parity_vs_oracle": {"trees": B, "hard_failures": len(hard), "near_threshold": len(near)},
+           "cpu_baseline": {"value": B / t_orc, "unit": "trees/s", "cores": oracle.max_threads(), "kind": "oracle",
+                            "sample": "the trees of input set 0, one run (the oracle walks only the visited nodes' rows)"}}
     return res
 
 

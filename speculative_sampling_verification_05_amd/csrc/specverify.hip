@@ -375,6 +375,7 @@ struct Params {
     const int32_t* tokens;
     int32_t* out_tokens;
     int32_t* out_n;
+    int64_t rows_split;   // row statistics: rows from here on are read from dft (row - rows_split)
     float* rows_max;      // row statistics outputs
     double* rows_sumexp;
     float* part_m;        // [units][2][maxp] per partial slot: max of the piece
@@ -483,7 +484,8 @@ __device__ inline Role role_of(const Params& P) {
 template <int DT, int MODE>
 __device__ inline const char* unit_row(const Params& P, const Role& U, int32_t j) {
     if constexpr (MODE == kRows) {
-        return row_at<DT>(P.tgt, static_cast<int64_t>(U.b) * P.V);
+        const int64_t r = U.b;
+        return r < P.rows_split ? row_at<DT>(P.tgt, r * P.V) : row_at<DT>(P.dft, (r - P.rows_split) * P.V);
     } else {
         if (j == 0) return row_at<DT>(P.tgt, (static_cast<int64_t>(U.b) * (P.gamma + 1) + U.i) * P.V);
         return row_at<DT>(P.dft, (static_cast<int64_t>(U.b) * P.gamma + U.i) * P.V);
@@ -2929,7 +2931,13 @@ struct TreeParams {
     int32_t* out_n;        // [B]
 };
 
-template <int DT>
+// Trees of at most kTreeHold * 64 nodes keep their parent and token arrays in
+// registers (lane l, slot t: node 64 t + l), so that a level costs one round
+// trip (the row statistics of v and its children's two logits, issued
+// together); larger trees read them from memory at every level.
+constexpr int kTreeHold = 4;
+
+template <int DT, bool HOLD>
 __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
@@ -2940,9 +2948,27 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
     const int32_t* tok = Q.token + b * N;
     int32_t* ot = Q.out_tokens + b * (N - 1);
     int32_t* on = Q.out_nodes ? Q.out_nodes + b * (N - 1) : nullptr;
+    constexpr int NT = HOLD ? kTreeHold : 1;
+    int32_t hp[NT], ht[NT];
+    if constexpr (HOLD) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int32_t j = t * kWave + lane;
+            hp[t] = j < N ? par[j] : -1;
+            ht[t] = j < N ? tok[j] : -1;
+        }
+    }
     // every parent must come before its child
     bool bad = false;
-    for (int32_t j = 1 + lane; j < N; j += kWave) bad |= par[j] < 0 || par[j] >= j;
+    if constexpr (HOLD) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int32_t j = t * kWave + lane;
+            bad |= j >= 1 && j < N && (hp[t] < 0 || hp[t] >= j);
+        }
+    } else {
+        for (int32_t j = 1 + lane; j < N; j += kWave) bad |= par[j] < 0 || par[j] >= j;
+    }
     bool invalid = __ballot(bad) != 0;
     int32_t v = 0, n = 0;
     while (!invalid) {
@@ -2964,12 +2990,9 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
         double best_s = -2.0;
         int32_t best = INT32_MAX;
         bool any_child = false, bad_tok = false;
-        for (int32_t t0 = v + 1; t0 < N; t0 += kWave) {
-            const int32_t j = t0 + lane;
-            const bool child = j < N && par[j] == v;
+        auto visit = [&](int32_t j, bool child, int32_t x) {
             double sc = -2.0;
             if (child) {
-                const int32_t x = tok[j];
                 if (x < 0 || x >= Q.V) {
                     bad_tok = true;
                 } else if (usable_v) {
@@ -2993,7 +3016,20 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
             if (tile_max > best_s) {
                 const uint64_t at = __ballot(child && sc == tile_max);
                 best_s = tile_max;
-                best = t0 + (__ffsll(static_cast<unsigned long long>(at)) - 1);
+                best = (j - lane) + (__ffsll(static_cast<unsigned long long>(at)) - 1);
+            }
+        };
+        if constexpr (HOLD) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int32_t j = t * kWave + lane;
+                visit(j, j > v && j < N && hp[t] == v, ht[t]);
+            }
+        } else {
+            for (int32_t t0 = v + 1; t0 < N; t0 += kWave) {
+                const int32_t j = t0 + lane;
+                const bool child = j < N && par[j] == v;
+                visit(j, child, child ? tok[j] : 0);
             }
         }
         if (__ballot(bad_tok) != 0 || (any_child && !usable_v)) {
@@ -3002,8 +3038,16 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
         }
         if (!any_child) break;
         if (Q.T > 0.0 ? best_s < Q.threshold : best_s < 1.0) break;
+        int32_t tb = 0;
+        if constexpr (HOLD) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (best / kWave == t) tb = __shfl(ht[t], best % kWave, kWave);  // (constant register indices)
+        } else {
+            tb = tok[best];
+        }
         if (lane == 0) {
-            ot[n] = tok[best];
+            ot[n] = tb;
             if (on) on[n] = best;
         }
         ++n;
@@ -3093,6 +3137,7 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
     p.nbr = mode == kSample ? static_cast<int32_t>(ceil_div(ceil_div(p.nchunk, kPairCw), kWavesPerBlock)) : 0;
     p.cstride = mode == kRows ? 1 : kSyncStride;
     L.units = mode == kRows ? G : G * (gamma + 1);
+    p.rows_split = G;  // (row statistics: every row from tgt unless the caller splits)
     L.blocks = mode == kSample ? G * (static_cast<int64_t>(gamma) * p.nb2 + p.nb1 + p.nbr) : L.units * p.nb1;
     const size_t slots = static_cast<size_t>(L.units) * 2 * p.maxp;
     size_t o = 0;
@@ -3598,8 +3643,9 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     if (trows >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
                      aligned16(draft_logits);
-    Layout Lt = plan(kRows, trows, 1, V, dtype, vec, 1), Ld = plan(kRows, pairs, 1, V, dtype, vec, 1);
-    if (int rc = check_size(kRows, Lt)) return rc;
+    if (trows + pairs >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
+    Layout Ls = plan(kRows, trows + pairs, 1, V, dtype, vec, 1);
+    if (int rc = check_size(kRows, Ls)) return rc;
     const int32_t nchunk = static_cast<int32_t>(ceil_div(V, chunk_elems(dtype, vec)));
     const int32_t nw = static_cast<int32_t>(ceil_div(nchunk, kDraftCw));
     const int32_t nbr = static_cast<int32_t>(ceil_div(nw, kWavesPerBlock));
@@ -3610,19 +3656,17 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
     const int cus = compute_units(dev);
-    Lt = plan(kRows, trows, 1, V, dtype, vec, cus);
-    Ld = plan(kRows, pairs, 1, V, dtype, vec, cus);
-    // the statistics passes use the front of the workspace; the row statistics
-    // and the overlap partials follow
-    const size_t o_mt = align_up(std::max(Lt.bytes, Ld.bytes), 256);
-    const size_t o_st = align_up(o_mt + static_cast<size_t>(trows) * sizeof(float), 256);
-    const size_t o_md = align_up(o_st + static_cast<size_t>(trows) * sizeof(double), 256);
-    const size_t o_sd = align_up(o_md + static_cast<size_t>(pairs) * sizeof(float), 256);
-    const size_t o_pt = align_up(o_sd + static_cast<size_t>(pairs) * sizeof(double), 256);
+    Ls = plan(kRows, trows + pairs, 1, V, dtype, vec, cus);
+    // the statistics pass uses the front of the workspace; the row statistics
+    // (target rows, then draft rows) and the overlap partials follow
+    const int64_t srows = trows + pairs;
+    const size_t o_m = align_up(Ls.bytes, 256);
+    const size_t o_s = align_up(o_m + static_cast<size_t>(srows) * sizeof(float), 256);
+    const size_t o_pt = align_up(o_s + static_cast<size_t>(srows) * sizeof(double), 256);
     Layout need{};
     need.bytes = align_up(o_pt + static_cast<size_t>(pairs) * nw * sizeof(double), 256);
-    need.cnt_words = std::max({Lt.cnt_words, Ld.cnt_words, pairs * kDraftStride});
-    need.dec_words = std::max(Lt.dec_words, Ld.dec_words);
+    need.cnt_words = std::max(Ls.cnt_words, pairs * kDraftStride);
+    need.dec_words = Ls.dec_words;
     Workspace* ws = nullptr;
     if (int rc = get_workspace(dev, st, need, &ws)) return rc;
     char* base = static_cast<char*>(ws->data);
@@ -3636,31 +3680,28 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     O.nw = nw;
     O.nbr = nbr;
     O.c32 = c32;
-    O.m_t = reinterpret_cast<float*>(base + o_mt);
-    O.s_t = reinterpret_cast<double*>(base + o_st);
-    O.m_d = reinterpret_cast<float*>(base + o_md);
-    O.s_d = reinterpret_cast<double*>(base + o_sd);
+    float* m_all = reinterpret_cast<float*>(base + o_m);
+    double* s_all = reinterpret_cast<double*>(base + o_s);
+    O.m_t = m_all;
+    O.s_t = s_all;
+    O.m_d = m_all + trows;
+    O.s_d = s_all + trows;
     O.part = reinterpret_cast<double*>(base + o_pt);
     O.cnt = ws->sync;
     const size_t off_dec = align_up(static_cast<size_t>(ws->cnt_cap) * sizeof(uint32_t), 256);
     O.err = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws->sync) + off_dec +
                                         static_cast<size_t>(ws->dec_cap) * sizeof(uint64_t));
     O.out_beta = out_beta;
-    // the statistics of every target row and every draft row (the same kernel
-    // and code as spec_row_stats), then the overlap
-    bind_workspace(Lt, *ws);
-    Lt.p.c32 = c32;
-    Lt.p.tgt = target_logits;
-    Lt.p.rows_max = const_cast<float*>(O.m_t);
-    Lt.p.rows_sumexp = const_cast<double*>(O.s_t);
-    launch(dtype, vec, kRows, Lt, st);
-    if (int rc = check_launch("statistics kernel")) return rc;
-    bind_workspace(Ld, *ws);
-    Ld.p.c32 = c32;
-    Ld.p.tgt = draft_logits;
-    Ld.p.rows_max = const_cast<float*>(O.m_d);
-    Ld.p.rows_sumexp = const_cast<double*>(O.s_d);
-    launch(dtype, vec, kRows, Ld, st);
+    // the statistics of every target row and every draft row in one launch
+    // (the same kernel and code as spec_row_stats), then the overlap
+    bind_workspace(Ls, *ws);
+    Ls.p.c32 = c32;
+    Ls.p.tgt = target_logits;
+    Ls.p.dft = draft_logits;
+    Ls.p.rows_split = trows;
+    Ls.p.rows_max = m_all;
+    Ls.p.rows_sumexp = s_all;
+    launch(dtype, vec, kRows, Ls, st);
     if (int rc = check_launch("statistics kernel")) return rc;
     if (dtype == SPEC_F32) {
         if (vec) launch_overlap_t<SPEC_F32, true>(O, blocks, st, nullptr, nullptr);
@@ -3710,35 +3751,31 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
     // argmax) in front of the walk; the statistics kernels use the front of
     // the workspace, the per-row results follow
     if (!greedy) {
-        Layout L = plan(kRows, rows, 1, V, dtype, vec, cus);
+        if (2 * rows >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
+        Layout L = plan(kRows, 2 * rows, 1, V, dtype, vec, cus);  // target rows, then draft rows
         if (int rc = check_size(kRows, L)) return rc;
-        const size_t o_mt = align_up(L.bytes, 256);
-        const size_t o_st = align_up(o_mt + static_cast<size_t>(rows) * sizeof(float), 256);
-        const size_t o_md = align_up(o_st + static_cast<size_t>(rows) * sizeof(double), 256);
-        const size_t o_sd = align_up(o_md + static_cast<size_t>(rows) * sizeof(float), 256);
+        const size_t o_m = align_up(L.bytes, 256);
+        const size_t o_s = align_up(o_m + static_cast<size_t>(2 * rows) * sizeof(float), 256);
         Layout need = L;
-        need.bytes = align_up(o_sd + static_cast<size_t>(rows) * sizeof(double), 256);
+        need.bytes = align_up(o_s + static_cast<size_t>(2 * rows) * sizeof(double), 256);
         Workspace* ws = nullptr;
         if (int rc = get_workspace(dev, st, need, &ws)) return rc;
         char* base = static_cast<char*>(ws->data);
-        float* mt = reinterpret_cast<float*>(base + o_mt);
-        double* stt = reinterpret_cast<double*>(base + o_st);
-        float* md = reinterpret_cast<float*>(base + o_md);
-        double* sd = reinterpret_cast<double*>(base + o_sd);
-        for (int k = 0; k < 2; ++k) {
-            Layout Lk = L;
-            bind_workspace(Lk, *ws);
-            Lk.p.c32 = c32;
-            Lk.p.tgt = k == 0 ? target_logits : draft_logits;
-            Lk.p.rows_max = k == 0 ? mt : md;
-            Lk.p.rows_sumexp = k == 0 ? stt : sd;
-            launch(dtype, vec, kRows, Lk, st);
-            if (int rc = check_launch("statistics kernel")) return rc;
-        }
-        Q.m_t = mt;
-        Q.s_t = stt;
-        Q.m_d = md;
-        Q.s_d = sd;
+        float* m_all = reinterpret_cast<float*>(base + o_m);
+        double* s_all = reinterpret_cast<double*>(base + o_s);
+        bind_workspace(L, *ws);
+        L.p.c32 = c32;
+        L.p.tgt = target_logits;
+        L.p.dft = draft_logits;
+        L.p.rows_split = rows;
+        L.p.rows_max = m_all;
+        L.p.rows_sumexp = s_all;
+        launch(dtype, vec, kRows, L, st);
+        if (int rc = check_launch("statistics kernel")) return rc;
+        Q.m_t = m_all;
+        Q.s_t = s_all;
+        Q.m_d = m_all + rows;
+        Q.s_d = s_all + rows;
     } else {
         DraftLayout L = plan_draft(rows, V, dtype, vec);
         if (L.blocks * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
@@ -3760,8 +3797,14 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
         Q.amax = am;
     }
     const dim3 grid(static_cast<unsigned>(ceil_div(B, kWavesPerBlock))), block(kBlock);
-    if (dtype == SPEC_F32) hipLaunchKernelGGL((k_tree_walk<SPEC_F32>), grid, block, 0, st, Q);
-    else hipLaunchKernelGGL((k_tree_walk<SPEC_BF16>), grid, block, 0, st, Q);
+    const bool hold = N <= kTreeHold * kWave;
+    if (dtype == SPEC_F32) {
+        if (hold) hipLaunchKernelGGL((k_tree_walk<SPEC_F32, true>), grid, block, 0, st, Q);
+        else hipLaunchKernelGGL((k_tree_walk<SPEC_F32, false>), grid, block, 0, st, Q);
+    } else {
+        if (hold) hipLaunchKernelGGL((k_tree_walk<SPEC_BF16, true>), grid, block, 0, st, Q);
+        else hipLaunchKernelGGL((k_tree_walk<SPEC_BF16, false>), grid, block, 0, st, Q);
+    }
     return check_launch("tree walk kernel");
 }
 
