@@ -14,6 +14,12 @@
  *  [HSD]  "LLM inference optimisation: hidden-state speculative decoding"
  *         (jsqmd.com), 3.3: after full acceptance the target's last row yields
  *         one more (bonus) token.
+ * Around that step: the draft-side draw with its probabilities
+ * (spec_draft_sample; [Ch15] 15.1.2 step 1), the diagnostics for choosing
+ * the draft length (the row entropy beside that draw, the per-position
+ * expected acceptance spec_expected_accept; [Ch15] 15.1.2 dynamic strategy
+ * adjustment, 15.2.3), and token-tree verification as a labelled heuristic
+ * mode (spec_tree_verify; [CSDN] 3.2, [Ch15] 15.2.4).
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -26,7 +32,8 @@
  *  - Randomness: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key =
  *    (seed low 32 bits, seed high 32 bits) and counter (b, i, purpose, 0);
  *    purpose 0 = accept test at position i, purpose 1 = correction draw at the
- *    rejected row k or the bonus draw (i = k = gamma). The uniform is
+ *    rejected row k or the bonus draw (i = k = gamma), purpose 2 = the draft
+ *    draw of spec_draft_sample at position i. The uniform is
  *    ((x1 << 32 | x0) >> 11) * 2^-53 in [0, 1). Results are a pure function of
  *    (inputs, seed): no state is carried between calls.
  *  - Host-detectable errors return a negative status before anything is
