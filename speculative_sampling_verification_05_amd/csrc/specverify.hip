@@ -74,7 +74,10 @@ namespace {
 #define SPECVERIFY_STATS_UNROLL 4
 #endif
 #ifndef SPECVERIFY_CHUNKS_PER_WAVE
-#define SPECVERIFY_CHUNKS_PER_WAVE 16
+#define SPECVERIFY_CHUNKS_PER_WAVE 32
+#endif
+#ifndef SPECVERIFY_GROUP_CHUNKS_PER_WAVE
+#define SPECVERIFY_GROUP_CHUNKS_PER_WAVE 24
 #endif
 #ifndef SPECVERIFY_LAG
 #define SPECVERIFY_LAG 1024
@@ -96,7 +99,9 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kUnroll = SPECVERIFY_STATS_UNROLL;           // chunks per pipelined load group
-constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE;  // 1 KiB chunks per statistics wavefront
+constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE;  // 1 KiB chunks per statistics wavefront (position-major)
+constexpr int kGreedyChunksPerWave = 16;                        // (position-major at T == 0)
+constexpr int kGroupChunksPerWave = SPECVERIFY_GROUP_CHUNKS_PER_WAVE;  // (group-major)
 constexpr int kLag = SPECVERIFY_LAG;        // group-major: groups between statistics and residual blocks
 constexpr int kSub = kWave * 16;            // group-major: elements per residual subsegment
 constexpr int kMaxStage = 1024;             // group-major: partial slots of one group staged in LDS
@@ -3110,7 +3115,7 @@ int32_t chunk_elems(int32_t dtype, bool vec) { return vec ? kWave * (16 / elem_b
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Statistics wavefronts take about kChunksPerWave chunks (many more wavefronts
+// Statistics wavefronts take about kChunksPerWave chunks (16 at T == 0; many more wavefronts
 // than the chip holds at once), but the whole problem gets at least 16
 // wavefronts per compute unit so that small problems still spread over the
 // chip. Residual wavefronts hold kPairCw chunks of each of the two rows.
@@ -3125,7 +3130,7 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
     const int64_t rows = mode == kSample ? G * (2 * gamma + 1) : (mode == kGreedy ? G * (gamma + 1) : G);
     const int64_t total = rows * p.nchunk;
     const int64_t min_waves = static_cast<int64_t>(cus) * 16;
-    int64_t cpw = kChunksPerWave;
+    int64_t cpw = mode == kGreedy ? kGreedyChunksPerWave : kChunksPerWave;
     if (ceil_div(total, cpw) < min_waves) cpw = ceil_div(total, min_waves);
     if (cpw < 1) cpw = 1;
     p.cpw = static_cast<int32_t>(cpw);
@@ -3175,7 +3180,7 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     p.nchunk = static_cast<int32_t>(ceil_div(V, CH));
     const int64_t per_group = static_cast<int64_t>(p.rps) * p.nchunk;
     const int64_t min_waves = static_cast<int64_t>(cus) * 16;
-    int64_t cpw = kChunksPerWave;
+    int64_t cpw = kGroupChunksPerWave;
     if (ceil_div(G * per_group, cpw) < min_waves) cpw = ceil_div(G * per_group, min_waves);
     if (cpw > static_cast<int64_t>(kMaxPieces - 1) * p.nchunk) cpw = static_cast<int64_t>(kMaxPieces - 1) * p.nchunk;
     if (cpw < 1) cpw = 1;
@@ -3212,11 +3217,15 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
 }
 
 // The automatic schedule at T > 0: position-major with the early stop once
-// one position's row-pair blocks fill the chip (four per compute unit; below
-// that, decisions lag too many positions behind the stream to save reads),
-// else group-major. L is the position-major layout.
+// one position's row pairs, cut into 16-chunk wavefront ranges, fill four
+// blocks per compute unit (below that, decisions lag too many positions behind
+// the stream to save reads), else group-major. The rule is stated on 16-chunk
+// ranges whatever range the kernel streams with. L is the position-major
+// layout.
+constexpr int kAutoChunksPerWave = 16;
 bool auto_position_major(int64_t B, const Layout& L, int cus) {
-    return B * L.p.nb2 >= 4 * static_cast<int64_t>(cus);
+    const int64_t nb2 = ceil_div(ceil_div(2 * static_cast<int64_t>(L.p.nchunk), kAutoChunksPerWave), kWavesPerBlock);
+    return B * nb2 >= 4 * static_cast<int64_t>(cus);
 }
 
 int compute_units(int dev) {
