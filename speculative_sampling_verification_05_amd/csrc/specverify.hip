@@ -2407,15 +2407,19 @@ struct DraftParams {
     int64_t pos0, b_offset;
     int32_t* out_tokens;  // [rows]
     double* out_q;        // [rows] or null
-    double* part_s;       // T > 0: [rows, nw] sum of 2^(fl(x*c - R)) per range
-    float* part_r;        //        and its integer reference R
-    double* part_h;       //        and the sum of 2^t * t, t = fl(x*c - R) (entropy wanted)
+    // per range k of row r, kDraftWords 64-bit words at part[(r * nw + k) * kDraftWords],
+    // each (epoch << 32 | payload): T > 0 the fp32 sum of 2^(fl(x*c - R)), the
+    // integer reference R, the fp32 sum of 2^t * t (t = fl(x*c - R), entropy
+    // wanted); T == 0 the maximum and its first index
+    uint64_t* part;
+    uint32_t epoch;       // this call's tag
     double* out_h;        // [rows] or null: entropy of softmax(l/T) per row
-    float* part_m;        // T == 0: [rows, nw] maximum and its first index per range
-    int32_t* part_i;
-    uint32_t* cnt;        // [rows] counters, kDraftStride words apart
     uint32_t* err;        // sticky error word (a bounded wait ran out)
 };
+constexpr int kDraftWords = 3;
+__device__ inline uint64_t tagged(uint32_t epoch, uint32_t payload) {
+    return (static_cast<uint64_t>(epoch) << 32) | payload;
+}
 
 // The token of range `sel` (chunks c0 .. c0 + kDraftCw - 1 of the row, loaded
 // into q): elements visited in ascending index order as tiles (Tiles), each
@@ -2579,8 +2583,9 @@ __global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) f = fold_arg(f, ArgPart{__shfl_xor(f.m, o, kWave), __shfl_xor(f.at, o, kWave)});
             if (lane == 0) {
-                cst(D.part_m + pb + wl, nan ? NAN : f.m);
-                cst(D.part_i + pb + wl, f.at);
+                uint64_t* pw = D.part + (pb + wl) * kDraftWords;
+                cst64(pw, tagged(D.epoch, __float_as_uint(nan ? NAN : f.m)));
+                cst64(pw + 1, tagged(D.epoch, static_cast<uint32_t>(f.at)));
             }
         } else {
             // one pass: the reference R comes from the first group with a
@@ -2627,59 +2632,85 @@ __global__ __launch_bounds__(kBlock) void k_draft(DraftParams D) {
             S = wave_sum(S);
             if constexpr (ENT) SH = wave_sum(SH);
             if (lane == 0) {
-                cst(D.part_s + pb + wl, bad ? static_cast<double>(NAN) : S);
-                cst(D.part_r + pb + wl, R);
-                if constexpr (ENT) cst(D.part_h + pb + wl, SH);
+                uint64_t* pw = D.part + (pb + wl) * kDraftWords;
+                cst64(pw, tagged(D.epoch, __float_as_uint(bad ? NAN : static_cast<float>(S))));
+                cst64(pw + 1, tagged(D.epoch, __float_as_uint(R)));
+                if constexpr (ENT) cst64(pw + 2, tagged(D.epoch, __float_as_uint(static_cast<float>(SH))));
             }
         }
     }
-    // this wavefront's range has counted in once its partial is stored
-    // (no-return atomic, ordered after the stores by waiting for them)
-    if (wl < D.nw) {
-        complete_before();
-        if (lane == 0) (void)__hip_atomic_fetch_add(D.cnt + row * kDraftStride, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // (the tagged words are this range's arrival: nothing else to count)
 }
 
 // The closing wavefront of a row: waits (bounded) until all of the row's
 // ranges have counted in, clears the counter for the next call, and draws.
+// The closing wavefront of a row: reads the row's tagged range words until
+// every one carries this call's epoch (bounded), then draws. Rows of at most
+// kFinTiles * 64 ranges keep the words of the read that found them all
+// current, so a row that is already complete costs one round trip here.
 template <int DT, bool VEC, bool GREEDY, bool ENT>
 __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane) {
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
-    uint32_t* cnt = D.cnt + row * kDraftStride;
-    const uint32_t want = static_cast<uint32_t>(D.nw);
-    int ok = 1;
-    if (lane == 0) {
-        if (cld(cnt) < want) {
-            const uint64_t t0 = wall_clock64();
-            for (;;) {
-                __builtin_amdgcn_s_sleep(kSleep);
-                if (cld(cnt) >= want) break;
-                if (wall_clock64() - t0 > kWaitTicks) {
-                    cst(D.err, 1u);
-                    ok = 0;
-                    break;
+    const int32_t nw = D.nw;
+    const uint64_t* pw = D.part + row * nw * kDraftWords;
+    constexpr int NWD = GREEDY ? 2 : (ENT ? 3 : 2);  // words per range in use
+    const uint32_t ep = D.epoch;
+    auto current = [&](uint64_t e) { return static_cast<uint32_t>(e >> 32) == ep; };
+    auto f32 = [](uint64_t e) { return __uint_as_float(static_cast<uint32_t>(e)); };
+    const bool hold = nw <= kFinTiles * kWave;
+    uint64_t e[kFinTiles][3];
+    bool ok = true;
+    {
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            bool stale = false;
+            if (hold) {
+#pragma unroll
+                for (int t = 0; t < kFinTiles; ++t) {
+                    const int32_t k = t * kWave + lane;
+#pragma unroll
+                    for (int wd = 0; wd < 3; ++wd) {
+                        e[t][wd] = k < nw && wd < NWD ? cld64(pw + static_cast<int64_t>(k) * kDraftWords + wd)
+                                                      : tagged(ep, 0u);
+                        stale |= !current(e[t][wd]);
+                    }
                 }
+            } else {
+                for (int32_t k = lane; k < nw; k += kWave)
+                    for (int wd = 0; wd < NWD; ++wd) stale |= !current(cld64(pw + static_cast<int64_t>(k) * kDraftWords + wd));
             }
+            if (__ballot(stale) == 0) break;
+            if (wall_clock64() - t0 > kWaitTicks) {
+                if (lane == 0) cst(D.err, 1u);
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(kSleep);
         }
-        if (ok) cst(cnt, 0u);
     }
-    ok = __shfl(ok, 0, kWave);
     after_complete();
     if (!ok) {  // the wait ran out (not expected): the row is reported unusable
         if (lane == 0) {
             D.out_tokens[row] = -1;
             if (D.out_q) D.out_q[row] = NAN;
+            if (D.out_h) D.out_h[row] = NAN;
         }
         return;
     }
+    // (a range's words, from the held read or from memory; all current now)
+    auto word = [&](int32_t k, int wd) { return cld64(pw + static_cast<int64_t>(k) * kDraftWords + wd); };
     const char* rp = row_at<DT>(D.logits, row * D.V);
     if constexpr (GREEDY) {
-        const int64_t pb = row * D.nw;
         ArgPart f{-INFINITY, INT32_MAX};
-        for (int32_t k = lane; k < D.nw; k += kWave) f = fold_arg(f, ArgPart{cld(D.part_m + pb + k), cld(D.part_i + pb + k)});
+        if (hold) {
+#pragma unroll
+            for (int t = 0; t < kFinTiles; ++t)
+                if (t * kWave + lane < nw) f = fold_arg(f, ArgPart{f32(e[t][0]), static_cast<int32_t>(e[t][1])});
+        } else {
+            for (int32_t k = lane; k < nw; k += kWave)
+                f = fold_arg(f, ArgPart{f32(word(k, 0)), static_cast<int32_t>(word(k, 1))});
+        }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) f = fold_arg(f, ArgPart{__shfl_xor(f.m, o, kWave), __shfl_xor(f.at, o, kWave)});
         if (lane == 0) {
@@ -2693,9 +2724,6 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
         // rescaling of each range's own), their total S, the range where the
         // ascending cumulative mass crosses u*S; then that range again, and
         // the element in it
-        const double* ps = D.part_s + row * D.nw;
-        const float* pr = D.part_r + row * D.nw;
-        const int32_t nw = D.nw;
         double S = 0.0, SH = 0.0, before = 0.0, target = 0.0;
         float R = kRUnset, rs = kRUnset;
         int32_t sel = -1;
@@ -2706,15 +2734,14 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
         auto sh_at = [&](double h, double sv, float r) {
             return sv == 0.0 ? 0.0 : rebase(h, r, R) + static_cast<double>(r - R) * rebase(sv, r, R);
         };
-        if (nw <= kFinTiles * kWave) {  // held in registers: one load round trip
+        if (hold) {
             float r[kFinTiles];
-            double v[kFinTiles], incl[kFinTiles], h[kFinTiles];
+            double v[kFinTiles], incl[kFinTiles];
 #pragma unroll
             for (int t2 = 0; t2 < kFinTiles; ++t2) {
-                const int32_t k = t2 * kWave + lane;
-                r[t2] = k < nw ? cld(pr + k) : kRUnset;
-                v[t2] = k < nw ? cld(ps + k) : 0.0;
-                if constexpr (ENT) h[t2] = k < nw ? cld(D.part_h + row * D.nw + k) : 0.0;
+                const bool in = t2 * kWave + lane < nw;
+                r[t2] = in ? f32(e[t2][1]) : kRUnset;
+                v[t2] = in ? static_cast<double>(f32(e[t2][0])) : 0.0;
             }
 #pragma unroll
             for (int t2 = 0; t2 < kFinTiles; ++t2) R = fmaxf(R, r[t2]);
@@ -2722,7 +2749,8 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
             if constexpr (ENT) {
                 double sh = 0.0;
 #pragma unroll
-                for (int t2 = 0; t2 < kFinTiles; ++t2) sh += sh_at(h[t2], v[t2], r[t2]);
+                for (int t2 = 0; t2 < kFinTiles; ++t2)
+                    if (t2 * kWave + lane < nw) sh += sh_at(static_cast<double>(f32(e[t2][2])), v[t2], r[t2]);
                 SH = wave_sum(sh);
             }
 #pragma unroll
@@ -2740,14 +2768,18 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
             }
         } else {  // many ranges: three passes over them in tiles of 64
             for (int32_t t0 = 0; t0 < nw; t0 += kWave)
-                if (t0 + lane < nw) R = fmaxf(R, cld(pr + t0 + lane));
+                if (t0 + lane < nw) R = fmaxf(R, f32(word(t0 + lane, 1)));
             R = wave_max(R);
-            auto val = [&](int32_t k) { return k < nw ? rebase(cld(ps + k), cld(pr + k), R) : 0.0; };
+            auto val = [&](int32_t k) {
+                return k < nw ? rebase(static_cast<double>(f32(word(k, 0))), f32(word(k, 1)), R) : 0.0;
+            };
             for (int32_t t0 = 0; t0 < nw; t0 += kWave) S += lane_f64(wave_scan_incl(val(t0 + lane)), kWave - 1);
             if constexpr (ENT) {
                 for (int32_t t0 = 0; t0 < nw; t0 += kWave) {
                     const int32_t k = t0 + lane;
-                    SH += wave_sum(k < nw ? sh_at(cld(D.part_h + row * D.nw + k), cld(ps + k), cld(pr + k)) : 0.0);
+                    SH += wave_sum(k < nw ? sh_at(static_cast<double>(f32(word(k, 2))),
+                                                  static_cast<double>(f32(word(k, 0))), f32(word(k, 1)))
+                                          : 0.0);
                 }
             }
             if (isfinite(S) && S > 0.0) {
@@ -2778,7 +2810,7 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
                     sel = last;
                     before = last_before;
                 }
-                if (sel >= 0) rs = cld(pr + sel);
+                if (sel >= 0) rs = f32(word(sel, 1));
             }
         }
         int32_t tok = -1;
@@ -3089,6 +3121,7 @@ struct Workspace {
     uint32_t* sync = nullptr;
     int64_t cnt_cap = 0;  // counter words
     int64_t dec_cap = 0;  // decision words and draw records (64-bit)
+    int64_t tag_cap = 0;  // epoch-tagged range words of the draft sampler (64-bit)
     uint32_t epoch = 0;   // of the last call
 };
 
@@ -3106,6 +3139,7 @@ struct Layout {
     uint32_t lds;    // dynamic LDS of the group-major kernel
     size_t off_pm, off_pr, off_ps, off_pi, off_tok, off_msum, off_subr, bytes;
     int64_t cnt_words, dec_words;
+    int64_t tag_words;  // epoch-tagged 64-bit words of the draft sampler's ranges
 };
 
 int elem_bytes(int32_t dtype) { return dtype == SPEC_F32 ? 4 : 2; }
@@ -3237,9 +3271,16 @@ int compute_units(int dev) {
     return n;
 }
 
-size_t sync_bytes(int64_t cnt_words, int64_t dec_words) {
+// sync layout: counters, decision words and draw records, the error word
+// (256 bytes), the draft sampler's tagged range words
+size_t sync_bytes(int64_t cnt_words, int64_t dec_words, int64_t tag_words = 0) {
     return align_up(static_cast<size_t>(cnt_words) * sizeof(uint32_t), 256) +
-           static_cast<size_t>(dec_words) * sizeof(uint64_t) + 256;
+           static_cast<size_t>(dec_words) * sizeof(uint64_t) + 256 + static_cast<size_t>(tag_words) * sizeof(uint64_t);
+}
+uint64_t* tag_region(const Workspace& ws) {
+    return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws.sync) +
+                                       align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256) +
+                                       static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t) + 256);
 }
 
 // Caller holds g_mu. Grows the buffers of (dev, stream) to fit L (a new sync
@@ -3247,7 +3288,7 @@ size_t sync_bytes(int64_t cnt_words, int64_t dec_words) {
 int get_workspace(int dev, hipStream_t stream, const Layout& L, Workspace** out) {
     Workspace& ws = g_ws[std::make_pair(dev, static_cast<void*>(stream))];
     const bool grow_data = ws.bytes < L.bytes;
-    const bool grow_sync = ws.cnt_cap < L.cnt_words || ws.dec_cap < L.dec_words;
+    const bool grow_sync = ws.cnt_cap < L.cnt_words || ws.dec_cap < L.dec_words || ws.tag_cap < L.tag_words;
     if ((grow_data && ws.data) || (grow_sync && ws.sync))
         if (hipStreamSynchronize(stream) != hipSuccess) return fail(SPEC_EHIP, "hipStreamSynchronize failed");
     if (grow_data) {
@@ -3265,10 +3306,12 @@ int get_workspace(int dev, hipStream_t stream, const Layout& L, Workspace** out)
     if (grow_sync) {
         if (ws.sync) (void)hipFree(ws.sync);
         ws.sync = nullptr;
-        ws.cnt_cap = ws.dec_cap = 0;
-        const int64_t cw = std::max<int64_t>(L.cnt_words + L.cnt_words / 4, 1024);
-        const int64_t dw = std::max<int64_t>(L.dec_words + L.dec_words / 4, 1024);
-        const size_t sb = sync_bytes(cw, dw);
+        // (keeps what earlier calls needed: the buffer serves every entry point)
+        const int64_t cw = std::max<int64_t>(std::max(L.cnt_words + L.cnt_words / 4, ws.cnt_cap), 1024);
+        const int64_t dw = std::max<int64_t>(std::max(L.dec_words + L.dec_words / 4, ws.dec_cap), 1024);
+        const int64_t tw = std::max<int64_t>(L.tag_words + L.tag_words / 4, ws.tag_cap);
+        ws.cnt_cap = ws.dec_cap = ws.tag_cap = 0;
+        const size_t sb = sync_bytes(cw, dw, tw);
         if (hipMalloc(reinterpret_cast<void**>(&ws.sync), sb) != hipSuccess) {
             ws.sync = nullptr;
             (void)hipGetLastError();
@@ -3281,12 +3324,16 @@ int get_workspace(int dev, hipStream_t stream, const Layout& L, Workspace** out)
         }
         ws.cnt_cap = cw;
         ws.dec_cap = dw;
+        ws.tag_cap = tw;
         ws.epoch = 0;
     }
     if (++ws.epoch == 0) {
-        // 2^32 calls on this workspace: clear the decision words before the tag repeats
+        // 2^32 calls on this workspace: clear the tagged words before the tag repeats
         char* dec = reinterpret_cast<char*>(ws.sync) + align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256);
         if (hipMemsetAsync(dec, 0, static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t), stream) != hipSuccess)
+            return fail(SPEC_EHIP, "hipMemsetAsync of the workspace failed");
+        if (ws.tag_cap > 0 &&
+            hipMemsetAsync(tag_region(ws), 0, static_cast<size_t>(ws.tag_cap) * sizeof(uint64_t), stream) != hipSuccess)
             return fail(SPEC_EHIP, "hipMemsetAsync of the workspace failed");
         ws.epoch = 1;
     }
@@ -3361,8 +3408,9 @@ int check_size(int, const Layout& L) {
 }
 
 // Draft sampler geometry: rows of nw wavefront ranges of kDraftCw chunks,
-// four ranges per block. Partials and counters live in the call's workspace
-// (its counters, like every call's, are back at zero when the kernel ends).
+// four ranges per block, then one closing wavefront per row. The ranges'
+// tagged words live in the workspace's tag region (cleared when allocated and
+// when the epoch wraps; each call's words carry its own epoch).
 struct DraftLayout {
     DraftParams d;
     int64_t blocks;
@@ -3378,35 +3426,17 @@ DraftLayout plan_draft(int64_t rows, int32_t V, int32_t dtype, bool vec) {
     d.nw = static_cast<int32_t>(ceil_div(d.nchunk, kDraftCw));
     d.nbr = static_cast<int32_t>(ceil_div(d.nw, kWavesPerBlock));
     L.blocks = rows * d.nbr + ceil_div(rows, kWavesPerBlock);  // statistics blocks, then closing blocks
-    const size_t slots = static_cast<size_t>(rows) * d.nw;
-    size_t o = 0;
-    o = align_up(o + slots * sizeof(double), 256);   // part_s
-    o = align_up(o + slots * sizeof(double), 256);   // part_h
-    o = align_up(o + slots * sizeof(float), 256);    // part_r
-    o = align_up(o + slots * sizeof(float), 256);    // part_m
-    o = align_up(o + slots * sizeof(int32_t), 256);  // part_i
-    L.ws.bytes = o;
-    L.ws.cnt_words = rows * kDraftStride;
+    L.ws.bytes = 0;
+    L.ws.cnt_words = 0;
     L.ws.dec_words = 0;
+    L.ws.tag_words = rows * d.nw * kDraftWords;
     return L;
 }
 
 void bind_draft(DraftLayout& L, const Workspace& ws) {
-    char* base = static_cast<char*>(ws.data);
     DraftParams& d = L.d;
-    const size_t slots = static_cast<size_t>(d.rows) * d.nw;
-    const size_t f4 = align_up(slots * sizeof(float), 256);
-    size_t o = 0;
-    d.part_s = reinterpret_cast<double*>(base + o);
-    o += align_up(slots * sizeof(double), 256);
-    d.part_h = reinterpret_cast<double*>(base + o);
-    o += align_up(slots * sizeof(double), 256);
-    d.part_r = reinterpret_cast<float*>(base + o);
-    o += f4;
-    d.part_m = reinterpret_cast<float*>(base + o);
-    o += f4;
-    d.part_i = reinterpret_cast<int32_t*>(base + o);
-    d.cnt = ws.sync;
+    d.part = tag_region(ws);
+    d.epoch = ws.epoch;
     const size_t off_dec = align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256);
     d.err = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws.sync) + off_dec +
                                         static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t));
