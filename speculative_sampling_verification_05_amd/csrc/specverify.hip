@@ -2968,10 +2968,11 @@ struct TreeParams {
     int32_t* out_n;        // [B]
 };
 
-// Trees of at most kTreeHold * 64 nodes keep their parent and token arrays in
-// registers (lane l, slot t: node 64 t + l), so that a level costs one round
-// trip (the row statistics of v and its children's two logits, issued
-// together); larger trees read them from memory at every level.
+// Trees of at most kTreeHold * 64 nodes are loaded whole at the start (lane
+// l, slot t: node 64 t + l): its parent and token, the statistics of its own
+// rows, and the two logits of its token under its parent's rows. The walk is
+// then register and cross-lane work only. Larger trees read the parent and
+// token arrays and gather the logits at every level.
 constexpr int kTreeHold = 4;
 
 template <int DT, bool HOLD>
@@ -2981,18 +2982,36 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
     const int64_t b = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w;
     if (b >= Q.B) return;
     const int32_t N = Q.N;
+    const bool sample = Q.T > 0.0;
     const int32_t* par = Q.parent + b * N;
     const int32_t* tok = Q.token + b * N;
     int32_t* ot = Q.out_tokens + b * (N - 1);
     int32_t* on = Q.out_nodes ? Q.out_nodes + b * (N - 1) : nullptr;
     constexpr int NT = HOLD ? kTreeHold : 1;
-    int32_t hp[NT], ht[NT];
+    int32_t hp[NT], ht[NT], ham[NT];
+    float hmt[NT], hmd[NT], glt[NT], gld[NT];
+    double hst[NT], hsd[NT];
     if constexpr (HOLD) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int32_t j = t * kWave + lane;
-            hp[t] = j < N ? par[j] : -1;
-            ht[t] = j < N ? tok[j] : -1;
+            const bool in = j < N;
+            const int64_t rj = b * N + j;
+            hp[t] = in ? par[j] : -1;
+            ht[t] = in ? tok[j] : -1;
+            hmt[t] = in && sample ? Q.m_t[rj] : 0.0f;
+            hmd[t] = in && sample ? Q.m_d[rj] : 0.0f;
+            hst[t] = in && sample ? Q.s_t[rj] : 0.0;
+            hsd[t] = in && sample ? Q.s_d[rj] : 0.0;
+            ham[t] = in && !sample ? Q.amax[rj] : -1;
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {  // the node's token under its parent's rows
+            const int32_t j = t * kWave + lane;
+            const bool ok = sample && j >= 1 && j < N && hp[t] >= 0 && hp[t] < j && ht[t] >= 0 && ht[t] < Q.V;
+            const int64_t rp = (b * N + (ok ? hp[t] : 0)) * Q.V;
+            glt[t] = ok ? load_one<DT>(row_at<DT>(Q.tgt, rp), ht[t]) : 0.0f;
+            gld[t] = ok ? load_one<DT>(row_at<DT>(Q.dft, rp), ht[t]) : 0.0f;
         }
     }
     // every parent must come before its child
@@ -3010,34 +3029,43 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
     int32_t v = 0, n = 0;
     while (!invalid) {
         const int64_t rv = b * N + v;
-        bool usable_v = true;
         double lmt = 0.0, lmd = 0.0, St = 0.0, Sd = 0.0;
         int32_t av = -1;
-        if (Q.T > 0.0) {
+        if constexpr (HOLD) {  // node v's statistics from the lane holding v
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (v / kWave == t) {  // (constant register indices)
+                    const int src = v % kWave;
+                    lmt = __shfl(hmt[t], src, kWave);
+                    lmd = __shfl(hmd[t], src, kWave);
+                    St = __shfl(hst[t], src, kWave);
+                    Sd = __shfl(hsd[t], src, kWave);
+                    av = __shfl(ham[t], src, kWave);
+                }
+            }
+        } else if (sample) {
             lmt = Q.m_t[rv];
             lmd = Q.m_d[rv];
             St = Q.s_t[rv];
             Sd = Q.s_d[rv];
-            usable_v = isfinite(St) && isfinite(Sd) && St > 0.0 && Sd > 0.0;
         } else {
             av = Q.amax[rv];
-            usable_v = av >= 0;
         }
+        const bool usable_v = sample ? isfinite(St) && isfinite(Sd) && St > 0.0 && Sd > 0.0 : av >= 0;
         // the children of v, 64 at a time: (score desc, index asc)
         double best_s = -2.0;
         int32_t best = INT32_MAX;
         bool any_child = false, bad_tok = false;
-        auto visit = [&](int32_t j, bool child, int32_t x) {
+        auto visit = [&](int32_t j, bool child, int32_t x, float lt, float ld) {
             double sc = -2.0;
             if (child) {
                 if (x < 0 || x >= Q.V) {
                     bad_tok = true;
                 } else if (usable_v) {
-                    if (Q.T > 0.0) {
-                        // acceptance probability in fp64 from the two gathered logits
-                        const double lt = load_one<DT>(row_at<DT>(Q.tgt, rv * Q.V), x);
-                        const double ld = load_one<DT>(row_at<DT>(Q.dft, rv * Q.V), x);
-                        const double p = exp((lt - lmt) / Q.T) / St, q = exp((ld - lmd) / Q.T) / Sd;
+                    if (sample) {
+                        // acceptance probability in fp64 from the two logits of the child's token
+                        const double p = exp((static_cast<double>(lt) - lmt) / Q.T) / St;
+                        const double q = exp((static_cast<double>(ld) - lmd) / Q.T) / Sd;
                         sc = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
                     } else {
                         sc = x == av ? 1.0 : -1.0;
@@ -3060,13 +3088,19 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int32_t j = t * kWave + lane;
-                visit(j, j > v && j < N && hp[t] == v, ht[t]);
+                visit(j, j > v && j < N && hp[t] == v, ht[t], glt[t], gld[t]);
             }
         } else {
             for (int32_t t0 = v + 1; t0 < N; t0 += kWave) {
                 const int32_t j = t0 + lane;
                 const bool child = j < N && par[j] == v;
-                visit(j, child, child ? tok[j] : 0);
+                const int32_t x = child ? tok[j] : 0;
+                float lt = 0.0f, ld = 0.0f;
+                if (child && sample && x >= 0 && x < Q.V && usable_v) {
+                    lt = load_one<DT>(row_at<DT>(Q.tgt, rv * Q.V), x);
+                    ld = load_one<DT>(row_at<DT>(Q.dft, rv * Q.V), x);
+                }
+                visit(j, child, x, lt, ld);
             }
         }
         if (__ballot(bad_tok) != 0 || (any_child && !usable_v)) {
@@ -3074,7 +3108,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
             break;
         }
         if (!any_child) break;
-        if (Q.T > 0.0 ? best_s < Q.threshold : best_s < 1.0) break;
+        if (sample ? best_s < Q.threshold : best_s < 1.0) break;
         int32_t tb = 0;
         if constexpr (HOLD) {
 #pragma unroll
