@@ -3014,6 +3014,38 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
             gld[t] = ok ? load_one<DT>(row_at<DT>(Q.dft, rp), ht[t]) : 0.0f;
         }
     }
+    // every node's score under its parent's rows (T > 0), computed once: the
+    // parent's statistics come from the lane holding the parent, and the walk
+    // then only compares (tiles past the last node are skipped)
+    double hsc[NT];
+    if constexpr (HOLD) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            hsc[t] = -2.0;
+            if (!sample || t * kWave >= N) continue;
+            const int32_t j = t * kWave + lane, pj = hp[t];
+            const int src = pj >= 0 ? pj % kWave : 0;
+            double pmt = 0.0, pmd = 0.0, pst = 0.0, psd = 0.0;
+#pragma unroll
+            for (int ts = 0; ts < NT; ++ts) {
+                if (ts * kWave >= N) break;
+                const float a = __shfl(hmt[ts], src, kWave), d = __shfl(hmd[ts], src, kWave);
+                const double sa = __shfl(hst[ts], src, kWave), sd = __shfl(hsd[ts], src, kWave);
+                if (pj >= 0 && pj / kWave == ts) {
+                    pmt = a;
+                    pmd = d;
+                    pst = sa;
+                    psd = sd;
+                }
+            }
+            const bool node = j >= 1 && j < N && pj >= 0 && pj < j && ht[t] >= 0 && ht[t] < Q.V;
+            if (node && isfinite(pst) && isfinite(psd) && pst > 0.0 && psd > 0.0) {
+                const double pp = exp((static_cast<double>(glt[t]) - pmt) / Q.T) / pst;
+                const double qq = exp((static_cast<double>(gld[t]) - pmd) / Q.T) / psd;
+                hsc[t] = pp == 0.0 ? 0.0 : (qq == 0.0 ? 1.0 : fmin(1.0, pp / qq));
+            }
+        }
+    }
     // every parent must come before its child
     bool bad = false;
     if constexpr (HOLD) {
@@ -3056,17 +3088,21 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
         double best_s = -2.0;
         int32_t best = INT32_MAX;
         bool any_child = false, bad_tok = false;
-        auto visit = [&](int32_t j, bool child, int32_t x, float lt, float ld) {
+        auto visit = [&](int32_t j, bool child, int32_t x, float lt, float ld, double pre) {
             double sc = -2.0;
             if (child) {
                 if (x < 0 || x >= Q.V) {
                     bad_tok = true;
                 } else if (usable_v) {
                     if (sample) {
-                        // acceptance probability in fp64 from the two logits of the child's token
-                        const double p = exp((static_cast<double>(lt) - lmt) / Q.T) / St;
-                        const double q = exp((static_cast<double>(ld) - lmd) / Q.T) / Sd;
-                        sc = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+                        if constexpr (HOLD) {
+                            sc = pre;
+                        } else {
+                            // acceptance probability in fp64 from the two logits of the child's token
+                            const double p = exp((static_cast<double>(lt) - lmt) / Q.T) / St;
+                            const double q = exp((static_cast<double>(ld) - lmd) / Q.T) / Sd;
+                            sc = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+                        }
                     } else {
                         sc = x == av ? 1.0 : -1.0;
                     }
@@ -3087,8 +3123,9 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
         if constexpr (HOLD) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
+                if (t * kWave >= N) break;
                 const int32_t j = t * kWave + lane;
-                visit(j, j > v && j < N && hp[t] == v, ht[t], glt[t], gld[t]);
+                visit(j, j > v && j < N && hp[t] == v, ht[t], glt[t], gld[t], hsc[t]);
             }
         } else {
             for (int32_t t0 = v + 1; t0 < N; t0 += kWave) {
@@ -3100,7 +3137,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
                     lt = load_one<DT>(row_at<DT>(Q.tgt, rv * Q.V), x);
                     ld = load_one<DT>(row_at<DT>(Q.dft, rv * Q.V), x);
                 }
-                visit(j, child, x, lt, ld);
+                visit(j, child, x, lt, ld, 0.0);
             }
         }
         if (__ballot(bad_tok) != 0 || (any_child && !usable_v)) {
