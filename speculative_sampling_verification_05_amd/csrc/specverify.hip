@@ -1189,6 +1189,18 @@ __device__ inline void write_record(const Params& P, int32_t b, uint32_t kind, i
 
 // T > 0: the accept step of position i from the unit's folded rows (one
 // wavefront). The bonus unit (i == gamma) only checks that its row is usable.
+// The acceptance probability alpha = min(1, p/q) of a draft token from its
+// exponents ep = (l_t - m_t)*c and eq = (l_d - m_d)*c (both <= 0) and the two
+// rows' sums (both >= 1): where neither p = 2^ep/st nor q = 2^eq/sd can be
+// zero or subnormal, alpha = min(1, 2^(ep - eq) * sd/st) (one exp2, one
+// division); otherwise p and q are formed first and the zero rules apply
+// (p = 0: 0; q = 0: 1).
+__device__ inline double accept_prob(double ep, double st, double eq, double sd) {
+    if (ep > -900.0 && eq > -900.0) return fmin(1.0, exp2(ep - eq) * (sd / st));
+    const double p = exp2(ep) / st, q = exp2(eq) / sd;
+    return p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
+}
+
 template <int DT>
 __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
     const int32_t gamma = P.gamma, V = P.V, nt = gamma + 1;
@@ -1197,6 +1209,9 @@ __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
     if (lane < gamma) xj = P.tokens[static_cast<int64_t>(U.b) * gamma + lane];
     const int32_t x = pair ? __shfl(xj, U.i, kWave) : 0;
     const bool tok_ok = x >= 0 && x < V;
+    // the accept uniform does not depend on the statistics: drawn before the loads
+    const double u = pair ? philox_uniform(P.seed, static_cast<uint32_t>(U.b + P.b_offset), static_cast<uint32_t>(U.i), 0u)
+                          : 0.0;
     float lt = 0.0f, ld = 0.0f;
     if (pair) {
         lt = cld(P.tok_l + static_cast<int64_t>(U.unit) * 2);
@@ -1218,12 +1233,13 @@ __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
         if (!ut || !ud || !tok_ok) {
             status = kBad;
         } else {
-            p = exp2((static_cast<double>(lt) - static_cast<double>(Mt)) * cd) / st;
-            qv = exp2((static_cast<double>(ld) - static_cast<double>(Md)) * cd) / sd;
-            const double alpha = p == 0.0 ? 0.0 : (qv == 0.0 ? 1.0 : fmin(1.0, p / qv));
-            const double u = philox_uniform(P.seed, static_cast<uint32_t>(U.b + P.b_offset),
-                                            static_cast<uint32_t>(U.i), 0u);
-            status = u < alpha ? kAcc : kRej;
+            const double ep = (static_cast<double>(lt) - static_cast<double>(Mt)) * cd;
+            const double eq = (static_cast<double>(ld) - static_cast<double>(Md)) * cd;
+            status = u < accept_prob(ep, st, eq, sd) ? kAcc : kRej;
+            if (P.dbg_p || P.dbg_q) {
+                p = exp2(ep) / st;
+                qv = exp2(eq) / sd;
+            }
         }
     } else if (!ut) {
         status = kBad;
@@ -1252,7 +1268,9 @@ __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
     mr.mcp = Mt * c;
     const double scale_p = exp2(static_cast<double>(mr.mcp) - static_cast<double>(Mt) * cd) / st;
     mr.mcq = pair ? Md * c : 0.0f;
-    const double rho = pair ? exp2(static_cast<double>(mr.mcq) - static_cast<double>(Md) * cd) / sd / scale_p : 0.0;
+    const double rho = pair ? exp2((static_cast<double>(mr.mcq) - static_cast<double>(Md) * cd) -
+                                   (static_cast<double>(mr.mcp) - static_cast<double>(Mt) * cd)) * (st / sd)
+                            : 0.0;
     mr.rhi = static_cast<float>(rho);
     mr.rlo = static_cast<float>(rho - static_cast<double>(mr.rhi));
     if (state == kTimedOut) {
@@ -1830,7 +1848,9 @@ __device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float
     si.mcp = mp * c32;
     si.scale_p = exp2(static_cast<double>(si.mcp) - static_cast<double>(mp) * c) / sp;
     si.mcq = has_q ? mq * c32 : 0.0f;
-    si.rho = has_q ? exp2(static_cast<double>(si.mcq) - static_cast<double>(mq) * c) / sq / si.scale_p : 0.0;
+    si.rho = has_q ? exp2((static_cast<double>(si.mcq) - static_cast<double>(mq) * c) -
+                          (static_cast<double>(si.mcp) - static_cast<double>(mp) * c)) * (sp / sq)
+                   : 0.0;
     return si;
 }
 
@@ -1838,14 +1858,15 @@ __device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float
 // The accept step, by one wavefront after the group's rows are folded into rs
 // (target rows 0..gamma, then draft rows at T > 0): lane i takes draft token
 // i, forms alpha in fp64 (greedy: compares the token with the row's argmax),
-// draws its Philox uniform, and a ballot finds the first rejection k. With
+// compares it with its Philox uniform u (drawn by the caller), and a ballot
+// finds the first rejection k. With
 // `emit` it writes k, the accepted tokens and the -1 padding (greedy also the
 // emitted argmax; the sampled token at k is left to the draw) and the debug
 // values. Returns the sequence record the residual needs.
 // --------------------------------------------------------------------------
 template <bool GREEDY>
 __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat* rs, int32_t x, float lt, float ld,
-                                      bool emit) {
+                                      double u, bool emit) {
     const int32_t gamma = P.gamma, V = P.V;
     const int nt = gamma + 1;
     const int i = static_cast<int>(threadIdx.x & (kWave - 1));
@@ -1886,12 +1907,13 @@ __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat
                 status = kBad;
             } else {
                 const double c = static_cast<double>(P.c32);
-                p = exp2((static_cast<double>(lt) - static_cast<double>(mt)) * c) / st;
-                q = exp2((static_cast<double>(ld) - static_cast<double>(md)) * c) / sd;
-                const double alpha = p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
-                const double u = philox_uniform(P.seed, static_cast<uint32_t>(b + P.b_offset),
-                                                static_cast<uint32_t>(i), 0u);
-                status = u < alpha ? kAcc : kRej;
+                const double ep = (static_cast<double>(lt) - static_cast<double>(mt)) * c;
+                const double eq = (static_cast<double>(ld) - static_cast<double>(md)) * c;
+                status = u < accept_prob(ep, st, eq, sd) ? kAcc : kRej;
+                if (emit && (P.dbg_p || P.dbg_q)) {
+                    p = exp2(ep) / st;
+                    q = exp2(eq) / sd;
+                }
             }
             if (emit && P.dbg_p) P.dbg_p[b * gamma + i] = p;
             if (emit && P.dbg_q) P.dbg_q[b * gamma + i] = q;
@@ -2219,11 +2241,13 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     const int w = static_cast<int>(threadIdx.x / kWave);
     const int32_t gamma = P.gamma;
-    // the draft tokens and their two logits do not depend on the statistics:
-    // they are loaded before the wait
+    // the draft tokens, their two logits and the accept uniforms do not
+    // depend on the statistics: they are loaded and drawn before the wait
     int32_t x = 0;
     float lt = 0.0f, ld = 0.0f;
+    double u = 0.0;  // the accept uniform of position lane
     if (w == 0 && lane < gamma) {
+        u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(lane), 0u);
         x = P.tokens[static_cast<int64_t>(g) * gamma + lane];
         if (x >= 0 && x < P.V) {
             lt = load_one<DT>(group_row<DT>(P, g, static_cast<uint32_t>(lane)), x);
@@ -2238,7 +2262,7 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     if (s_ok) {
         merge_group<false, kBlock>(P, g, dyn, rs);
         if (w == 0) {
-            const SeqInfo si = accept_wave<false>(P, g, rs, x, lt, ld, idx == 0);
+            const SeqInfo si = accept_wave<false>(P, g, rs, x, lt, ld, u, idx == 0);
             if (lane == 0) shi = si;
         }
         __syncthreads();
