@@ -383,6 +383,9 @@ struct Params {
     int64_t rows_split;   // row statistics: rows from here on are read from dft (row - rows_split)
     float* rows_max;      // row statistics outputs
     double* rows_sumexp;
+    uint32_t* tree_done;  // row statistics of a tree call, or null: per tree (kSyncStride words apart) the
+                          //   finished rows, counted after their coherent stores
+    int32_t tree_n;       //   nodes per tree (row r < rows_split belongs to tree r / tree_n)
     float* part_m;        // [units][2][maxp] per partial slot: max of the piece
     float* part_r;        //   integer reference of the piece (T > 0)
     double* part_s;       //   sum of 2^(x*c - reference) (T > 0)
@@ -1334,8 +1337,14 @@ __device__ inline void finish_rows(const Params& P, const Role& U, int lane) {
     merge_rows(P, U.unit, 1, lane, rs);
     if (lane == 0) {
         const double s = row_sum(rs[0], P.c32);
-        P.rows_max[U.b] = rs[0].m;
-        P.rows_sumexp[U.b] = usable(rs[0].m, s) ? s : NAN;
+        cst(P.rows_max + U.b, rs[0].m);
+        cst(P.rows_sumexp + U.b, usable(rs[0].m, s) ? s : static_cast<double>(NAN));
+        if (P.tree_done) {  // the tree's closing wavefront waits for all 2*tree_n of its rows
+            complete_before();
+            const int64_t r = U.b < P.rows_split ? U.b : U.b - P.rows_split;
+            (void)__hip_atomic_fetch_add(P.tree_done + (r / P.tree_n) * kSyncStride, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -2990,6 +2999,11 @@ struct TreeParams {
     int32_t* out_tokens;   // [B, N - 1]
     int32_t* out_nodes;    // [B, N - 1] or null
     int32_t* out_n;        // [B]
+    // the fused launch: blocks from first_block on walk the trees; tree b's
+    // rows are finished once done[b * kSyncStride] reaches 2N (reset by the walk)
+    int64_t first_block;
+    uint32_t* done;
+    uint32_t* err;         // sticky: a wait ran out
 };
 
 // Trees of at most kTreeHold * 64 nodes are loaded whole at the start (lane
@@ -2999,12 +3013,13 @@ struct TreeParams {
 // token arrays and gather the logits at every level.
 constexpr int kTreeHold = 4;
 
-template <int DT, bool HOLD>
-__global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
-    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
-    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w;
-    if (b >= Q.B) return;
+// The walk of tree b by one wavefront. FUSED (HOLD, T > 0): the statistics
+// are produced by the same launch, so the parents, tokens and gathered logits
+// are loaded first, then the wavefront waits (bounded) until the tree's 2N rows
+// are finished and reads their statistics with coherent loads.
+template <int DT, bool HOLD, bool FUSED>
+__device__ inline void walk_tree(const TreeParams& Q, int64_t b, int lane) {
+    static_assert(!FUSED || HOLD, "the fused walk holds the tree");
     const int32_t N = Q.N;
     const bool sample = Q.T > 0.0;
     const int32_t* par = Q.parent + b * N;
@@ -3023,11 +3038,13 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
             const int64_t rj = b * N + j;
             hp[t] = in ? par[j] : -1;
             ht[t] = in ? tok[j] : -1;
-            hmt[t] = in && sample ? Q.m_t[rj] : 0.0f;
-            hmd[t] = in && sample ? Q.m_d[rj] : 0.0f;
-            hst[t] = in && sample ? Q.s_t[rj] : 0.0;
-            hsd[t] = in && sample ? Q.s_d[rj] : 0.0;
-            ham[t] = in && !sample ? Q.amax[rj] : -1;
+            if constexpr (!FUSED) {
+                hmt[t] = in && sample ? Q.m_t[rj] : 0.0f;
+                hmd[t] = in && sample ? Q.m_d[rj] : 0.0f;
+                hst[t] = in && sample ? Q.s_t[rj] : 0.0;
+                hsd[t] = in && sample ? Q.s_d[rj] : 0.0;
+                ham[t] = in && !sample ? Q.amax[rj] : -1;
+            }
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {  // the node's token under its parent's rows
@@ -3036,6 +3053,36 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
             const int64_t rp = (b * N + (ok ? hp[t] : 0)) * Q.V;
             glt[t] = ok ? load_one<DT>(row_at<DT>(Q.tgt, rp), ht[t]) : 0.0f;
             gld[t] = ok ? load_one<DT>(row_at<DT>(Q.dft, rp), ht[t]) : 0.0f;
+        }
+    }
+    bool lost = false;  // FUSED: the wait for the tree's rows ran out (not expected)
+    if constexpr (FUSED) {
+        uint32_t* cnt = Q.done + b * kSyncStride;
+        const uint32_t want = 2u * static_cast<uint32_t>(N);
+        if (cld(cnt) != want) {
+            const uint64_t t0 = wall_clock64();
+            for (;;) {
+                __builtin_amdgcn_s_sleep(kSleep);
+                if (cld(cnt) == want) break;
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    if (lane == 0) cst(Q.err, 1u);
+                    lost = true;
+                    break;
+                }
+            }
+        }
+        after_complete();
+        if (!lost && lane == 0) cst(cnt, 0u);  // every row of the tree has counted in
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int32_t j = t * kWave + lane;
+            const bool in = j < N;
+            const int64_t rj = b * N + j;
+            hmt[t] = in ? cld(Q.m_t + rj) : 0.0f;
+            hmd[t] = in ? cld(Q.m_d + rj) : 0.0f;
+            hst[t] = in ? cld(Q.s_t + rj) : 0.0;
+            hsd[t] = in ? cld(Q.s_d + rj) : 0.0;
+            ham[t] = -1;
         }
     }
     // every node's score under its parent's rows (T > 0), computed once: the
@@ -3081,7 +3128,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
     } else {
         for (int32_t j = 1 + lane; j < N; j += kWave) bad |= par[j] < 0 || par[j] >= j;
     }
-    bool invalid = __ballot(bad) != 0;
+    bool invalid = __ballot(bad) != 0 || lost;
     int32_t v = 0, n = 0;
     while (!invalid) {
         const int64_t rv = b * N + v;
@@ -3192,6 +3239,33 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
         }
     }
     if (lane == 0) Q.out_n[b] = invalid ? -1 : n;
+}
+
+template <int DT, bool HOLD>
+__global__ __launch_bounds__(kBlock) void k_tree_walk(TreeParams Q) {
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + w;
+    if (b >= Q.B) return;
+    walk_tree<DT, HOLD, false>(Q, b, lane);
+}
+
+// T > 0, trees of up to kTreeHold*64 nodes: one launch. Blocks before
+// Q.first_block are the row-statistics blocks over every node's target rows,
+// then its draft rows (each row's finisher counts the row in at its tree);
+// the blocks after them hold one walking wavefront per tree. They come last in
+// the grid, so every statistics block has started before any of them waits.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_tree(Params P, TreeParams Q) {
+    if (static_cast<int64_t>(blockIdx.x) < Q.first_block) {
+        stats_block<DT, VEC, kRows>(P, role_of<kRows>(P));
+        return;
+    }
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+    const int64_t b = (static_cast<int64_t>(blockIdx.x) - Q.first_block) * kWavesPerBlock + w;
+    if (b >= Q.B) return;
+    walk_tree<DT, true, true>(Q, b, lane);
 }
 
 // ==========================================================================
@@ -3881,17 +3955,24 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
     Q.out_tokens = out_tokens;
     Q.out_nodes = out_nodes;
     Q.out_n = out_n;
+    const bool hold = N <= kTreeHold * kWave;
+    const dim3 grid(static_cast<unsigned>(ceil_div(B, kWavesPerBlock))), block(kBlock);
     // every node's row statistics (T > 0: both models; T == 0: the target
     // argmax) in front of the walk; the statistics kernels use the front of
-    // the workspace, the per-row results follow
+    // the workspace, the per-row results follow. At T > 0 a tree that the walk
+    // holds whole is walked by closing wavefronts of the statistics launch.
     if (!greedy) {
         if (2 * rows >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
         Layout L = plan(kRows, 2 * rows, 1, V, dtype, vec, cus);  // target rows, then draft rows
         if (int rc = check_size(kRows, L)) return rc;
+        const int64_t tree_blocks = ceil_div(B, kWavesPerBlock);
+        if ((L.blocks + tree_blocks) * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
         const size_t o_m = align_up(L.bytes, 256);
         const size_t o_s = align_up(o_m + static_cast<size_t>(2 * rows) * sizeof(float), 256);
         Layout need = L;
         need.bytes = align_up(o_s + static_cast<size_t>(2 * rows) * sizeof(double), 256);
+        const int64_t o_tree = ceil_div(L.cnt_words, kSyncStride) * kSyncStride;  // the trees' row counters
+        if (hold) need.cnt_words = o_tree + static_cast<int64_t>(B) * kSyncStride;
         Workspace* ws = nullptr;
         if (int rc = get_workspace(dev, st, need, &ws)) return rc;
         char* base = static_cast<char*>(ws->data);
@@ -3904,12 +3985,28 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
         L.p.rows_split = rows;
         L.p.rows_max = m_all;
         L.p.rows_sumexp = s_all;
-        launch(dtype, vec, kRows, L, st);
-        if (int rc = check_launch("statistics kernel")) return rc;
         Q.m_t = m_all;
         Q.s_t = s_all;
         Q.m_d = m_all + rows;
         Q.s_d = s_all + rows;
+        if (hold) {
+            L.p.tree_done = ws->sync + o_tree;
+            L.p.tree_n = N;
+            Q.first_block = L.blocks;
+            Q.done = L.p.tree_done;
+            Q.err = L.p.err;
+            const dim3 g2(static_cast<unsigned>(L.blocks + tree_blocks));
+            if (dtype == SPEC_F32) {
+                if (vec) hipLaunchKernelGGL((k_tree<SPEC_F32, true>), g2, block, 0, st, L.p, Q);
+                else hipLaunchKernelGGL((k_tree<SPEC_F32, false>), g2, block, 0, st, L.p, Q);
+            } else {
+                if (vec) hipLaunchKernelGGL((k_tree<SPEC_BF16, true>), g2, block, 0, st, L.p, Q);
+                else hipLaunchKernelGGL((k_tree<SPEC_BF16, false>), g2, block, 0, st, L.p, Q);
+            }
+            return check_launch("tree kernel");
+        }
+        launch(dtype, vec, kRows, L, st);
+        if (int rc = check_launch("statistics kernel")) return rc;
     } else {
         DraftLayout L = plan_draft(rows, V, dtype, vec);
         if (L.blocks * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
@@ -3930,8 +4027,6 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
         if (int rc = check_launch("argmax kernel")) return rc;
         Q.amax = am;
     }
-    const dim3 grid(static_cast<unsigned>(ceil_div(B, kWavesPerBlock))), block(kBlock);
-    const bool hold = N <= kTreeHold * kWave;
     if (dtype == SPEC_F32) {
         if (hold) hipLaunchKernelGGL((k_tree_walk<SPEC_F32, true>), grid, block, 0, st, Q);
         else hipLaunchKernelGGL((k_tree_walk<SPEC_F32, false>), grid, block, 0, st, Q);
