@@ -275,7 +275,7 @@ def tree_leg(sv, wl, args, stream):
            "us_per_call": us, "nodes_per_s": B * N / (us * 1e-6), "bytes_per_call": nbytes,
            "achieved_GBps": nbytes / (us * 1e-6) / 1e9, "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
            "mean_accepted_path": float(n.float().mean().item()), "roofline_bound": "hbm",
-           "kernels": ["k_verify (row statistics of every node's two rows, one launch)", "k_tree_walk"],
+           "kernels": ["k_tree (row statistics of every node's two rows, then one walking wavefront per tree, one launch)"],
            "mode": "heuristic: not distribution-preserving",
            "parity_vs_oracle": {"trees": B, "hard_failures": len(hard), "near_threshold": len(near)},
            "cpu_baseline": {"value": B / t_orc, "unit": "trees/s", "cores": oracle.max_threads(), "kind": "oracle",

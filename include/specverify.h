@@ -245,8 +245,9 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
  *      token outside [0, V) or a needed row holding NaN, +inf or no finite
  *      entry.
  *  N >= 2, B * N < 2^31, threshold not NaN. Reads every row once (the
- *  statistics of all nodes), then walks each tree with one wavefront. Errors
- *  as spec_verify. Uses the library's workspace of (device, stream). */
+ *  statistics of all nodes), then walks each tree with one wavefront (at
+ *  temperature > 0 with N <= 256, in the same launch). Errors as
+ *  spec_verify. Uses the library's workspace of (device, stream). */
 int spec_tree_verify(const void* target_logits, const void* draft_logits, const int32_t* parent,
                      const int32_t* token, int32_t B, int32_t N, int32_t V, int32_t dtype,
                      float temperature, float threshold, int32_t* out_tokens, int32_t* out_nodes,
