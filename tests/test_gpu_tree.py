@@ -89,3 +89,47 @@ def test_tree_chain_matches_oracle_and_padding():
         n = gpu[2][b]
         assert list(gpu[1][b, :n]) == list(range(1, n + 1))
         assert (gpu[0][b, n:] == -1).all() and (gpu[1][b, n:] == -1).all()
+
+
+def _first_nodes(tr, N):
+    """The first N nodes of each tree (still a tree: every parent precedes its child)."""
+    c = np.ascontiguousarray
+    return W.TreeInputs(c(tr.target[:, :N]), c(tr.draft[:, :N]), c(tr.parent[:, :N]), c(tr.token[:, :N]),
+                        tr.dtype, tr.T)
+
+
+@pytest.mark.parametrize("N", [255, 256, 257])
+def test_tree_size_boundary_of_the_single_launch(N):
+    """At T > 0 a tree of up to 256 nodes is walked by the statistics launch's
+    closing wavefronts, a larger one by a second launch; both sides of the
+    boundary walk the oracle's paths (and at T == 0, the argmax walk)."""
+    full = W.tree_inputs(3, 2, 17, 700, W.F32, 1.0, seed=29)      # 307 nodes, cut to N
+    tr = _first_nodes(full, N)
+    for T, threshold in ((1.0, 0.0), (0.8, 0.4), (0.0, 0.5)):
+        run_tree(tr, T, threshold)
+
+
+def test_tree_calls_interleaved_with_verification_share_the_workspace():
+    """Tree calls (whose per-tree row counters overlap the addresses other
+    calls use for their counters) alternate with verification and row
+    statistics calls on one stream: every call leaves its counters at zero,
+    so each still matches the oracle."""
+    from oracle.compare import compare_tokens
+    trees = [W.tree_inputs(8, 3, 3, 1000, W.F32, 1.0, seed=41), W.tree_inputs(5, 2, 4, 3000, W.BF16, 0.9, seed=42)]
+    verifies = [W.small_random_inputs(8, 5, 4000, W.F32, 1.0, seed=43),
+                W.small_random_inputs(12, 3, 2048, W.BF16, 0.8, seed=44)]
+    for rep in range(2):
+        for k in range(2):
+            run_tree(trees[k], 1.0 if k == 0 else 0.9, 0.3)
+            inp = verifies[k]
+            for schedule in (0, 1, 2):
+                gpu = G.run(inp, 7 + rep, schedule=schedule)
+                orc = oracle.verify(inp.target, inp.draft, inp.tokens, inp.wl.dtype, inp.wl.T, 7 + rep)
+                r = compare_tokens(inp, orc, gpu.tokens, gpu.n, 7 + rep)
+                assert not r.hard_fail, r.hard_fail[:5]
+            logits = inp.target.reshape(-1, inp.wl.V)[:5]
+            m, s = sv.row_stats(G.to_device(logits, inp.wl.dtype), inp.wl.T)
+            m = m.cpu().numpy()
+            for r_ in range(5):
+                ok, _, om, _ = oracle.row_softmax(logits[r_], inp.wl.dtype, inp.wl.T)
+                assert ok and m[r_] == om
