@@ -218,7 +218,7 @@ int spec_draft_sample_ex(const void* logits, int32_t B, int32_t n, int32_t V, in
  *  out_beta [B, gamma] double, DEVICE: beta, NaN where either row holds NaN
  *      or +inf or no finite entry.
  *  B * (gamma + 1) < 2^31. Reads every row twice (statistics, then the
- *  overlap); two launches on stream, no synchronisation. Errors as
+ *  overlap) in one launch on stream, no synchronisation. Errors as
  *  spec_verify. Uses the library's workspace of (device, stream). */
 int spec_expected_accept(const void* target_logits, const void* draft_logits, int32_t B,
                          int32_t gamma, int32_t V, int32_t dtype, float temperature,

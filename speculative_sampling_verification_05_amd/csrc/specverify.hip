@@ -386,6 +386,8 @@ struct Params {
     uint32_t* tree_done;  // row statistics of a tree call, or null: per tree (kSyncStride words apart) the
                           //   finished rows, counted after their coherent stores
     int32_t tree_n;       //   nodes per tree (row r < rows_split belongs to tree r / tree_n)
+    int32_t tgt_group;    // row statistics: 0, or row r < rows_split is target row
+                          //   (r / tgt_group) * (tgt_group + 1) + r % tgt_group (each sequence's bonus row skipped)
     float* part_m;        // [units][2][maxp] per partial slot: max of the piece
     float* part_r;        //   integer reference of the piece (T > 0)
     double* part_s;       //   sum of 2^(x*c - reference) (T > 0)
@@ -493,7 +495,9 @@ template <int DT, int MODE>
 __device__ inline const char* unit_row(const Params& P, const Role& U, int32_t j) {
     if constexpr (MODE == kRows) {
         const int64_t r = U.b;
-        return r < P.rows_split ? row_at<DT>(P.tgt, r * P.V) : row_at<DT>(P.dft, (r - P.rows_split) * P.V);
+        if (r >= P.rows_split) return row_at<DT>(P.dft, (r - P.rows_split) * P.V);
+        const int64_t g = P.tgt_group;
+        return row_at<DT>(P.tgt, (g > 0 ? (r / g) * (g + 1) + r % g : r) * P.V);
     } else {
         if (j == 0) return row_at<DT>(P.tgt, (static_cast<int64_t>(U.b) * (P.gamma + 1) + U.i) * P.V);
         return row_at<DT>(P.dft, (static_cast<int64_t>(U.b) * P.gamma + U.i) * P.V);
@@ -2892,6 +2896,8 @@ struct OverlapParams {
     uint32_t* cnt;      // [pairs] counters, kDraftStride words apart
     uint32_t* err;
     double* out_beta;   // [B * gamma]
+    int64_t first_block;   // blocks before this one compute the row statistics
+    uint32_t* rows_done;   // [pairs] finished rows of the pair (two), kSyncStride words apart
 };
 
 template <int DT, bool VEC>
@@ -2912,7 +2918,10 @@ __device__ inline void overlap_finish(const OverlapParams& O, int64_t pair, int 
                 }
             }
         }
-        if (ok) cst(cnt, 0u);
+        if (ok) {  // every range of the pair has counted in, so none waits on rows_done any more
+            cst(cnt, 0u);
+            cst(O.rows_done + pair * kSyncStride, 0u);
+        }
     }
     ok = __shfl(ok, 0, kWave);
     after_complete();
@@ -2922,28 +2931,58 @@ __device__ inline void overlap_finish(const OverlapParams& O, int64_t pair, int 
     if (lane == 0) O.out_beta[pair] = ok ? acc : static_cast<double>(NAN);
 }
 
+// One launch: blocks before O.first_block are the row-statistics blocks over
+// the pairs' target rows, then their draft rows (each row's finisher counts
+// the row in at its pair); then nbr blocks per pair whose wavefronts wait
+// (bounded) until both rows of their pair are finished; then the closing
+// blocks. Every block of a kind starts after all blocks of the kinds before
+// it have been dispatched, so no wait depends on a block that cannot start.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_overlap(OverlapParams O) {
+__global__ __launch_bounds__(kBlock) void k_overlap(Params P, OverlapParams O) {
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
+    if (static_cast<int64_t>(blockIdx.x) < O.first_block) {
+        stats_block<DT, VEC, kRows>(P, role_of<kRows>(P));
+        return;
+    }
+    const int64_t x = static_cast<int64_t>(blockIdx.x) - O.first_block;
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
     const int64_t pairs = static_cast<int64_t>(O.B) * O.gamma;
     const int64_t sblocks = pairs * O.nbr;
-    if (blockIdx.x >= sblocks) {  // closing blocks: wavefront w finishes one pair
-        const int64_t pair = (blockIdx.x - sblocks) * kWavesPerBlock + w;
+    if (x >= sblocks) {  // closing blocks: wavefront w finishes one pair
+        const int64_t pair = (x - sblocks) * kWavesPerBlock + w;
         if (pair < pairs) overlap_finish<DT, VEC>(O, pair, lane);
         return;
     }
-    const int64_t pair = blockIdx.x / O.nbr;
-    const int32_t wl = static_cast<int32_t>(blockIdx.x - pair * O.nbr) * kWavesPerBlock + w;
+    const int64_t pair = x / O.nbr;
+    const int32_t wl = static_cast<int32_t>(x - pair * O.nbr) * kWavesPerBlock + w;
     if (wl >= O.nw) return;
     const int64_t b = pair / O.gamma, i = pair - b * O.gamma;
     const int64_t rt = b * (O.gamma + 1) + i;
+    // the pair's two rows are finished once its count reaches two
+    int ready = 1;
+    if (lane == 0) {
+        const uint32_t* rd = O.rows_done + pair * kSyncStride;
+        if (cld(rd) < 2u) {
+            const uint64_t t0 = wall_clock64();
+            for (;;) {
+                __builtin_amdgcn_s_sleep(kSleep);
+                if (cld(rd) >= 2u) break;
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    cst(O.err, 1u);
+                    ready = 0;
+                    break;
+                }
+            }
+        }
+    }
+    ready = __shfl(ready, 0, kWave);
+    after_complete();
     const float c = O.c32;
-    const float mp = O.m_t[rt], mq = O.m_d[pair];
-    const double Sp = O.s_t[rt], Sq = O.s_d[pair];
-    const bool ok = isfinite(Sp) && isfinite(Sq) && Sp > 0.0 && Sq > 0.0;
+    const float mp = cld(O.m_t + pair), mq = cld(O.m_d + pair);
+    const double Sp = cld(O.s_t + pair), Sq = cld(O.s_d + pair);
+    const bool ok = ready && isfinite(Sp) && isfinite(Sq) && Sp > 0.0 && Sq > 0.0;
     const float mcp = mp * c, mcq = mq * c;
     const float sp = ok ? static_cast<float>(exp2(static_cast<double>(mcp) - static_cast<double>(mp) * c) / Sp) : 0.0f;
     const float sq = ok ? static_cast<float>(exp2(static_cast<double>(mcq) - static_cast<double>(mq) * c) / Sq) : 0.0f;
@@ -3631,9 +3670,10 @@ void launch_draft(int32_t dtype, bool vec, bool greedy, const DraftLayout& L, hi
 }
 
 template <int DT, bool VEC>
-void launch_overlap_t(const OverlapParams& O, int64_t blocks, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+void launch_overlap_t(const Params& P, const OverlapParams& O, int64_t blocks, hipStream_t st, hipEvent_t e0,
+                      hipEvent_t e1) {
     hipExtLaunchKernelGGL((k_overlap<DT, VEC>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st, e0, e1, 0,
-                          O);
+                          P, O);
 }
 
 }  // namespace
@@ -3848,36 +3888,53 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     if (!(std::isfinite(c32) && c32 > 0.0f)) return fail(SPEC_EINVAL, "temperature out of range");
     const int64_t pairs = static_cast<int64_t>(B) * gamma;
     const int64_t trows = static_cast<int64_t>(B) * (gamma + 1);
-    if (trows >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
+    if (trows >= (int64_t(1) << 31) || 2 * pairs >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
                      aligned16(draft_logits);
-    if (trows + pairs >= (int64_t(1) << 31)) return fail(SPEC_EINVAL, "problem too large");
-    Layout Ls = plan(kRows, trows + pairs, 1, V, dtype, vec, 1);
+    Layout Ls = plan(kRows, 2 * pairs, 1, V, dtype, vec, 1);
     if (int rc = check_size(kRows, Ls)) return rc;
     const int32_t nchunk = static_cast<int32_t>(ceil_div(V, chunk_elems(dtype, vec)));
     const int32_t nw = static_cast<int32_t>(ceil_div(nchunk, kDraftCw));
     const int32_t nbr = static_cast<int32_t>(ceil_div(nw, kWavesPerBlock));
-    const int64_t blocks = pairs * nbr + ceil_div(pairs, kWavesPerBlock);
-    if (blocks * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
     const int cus = compute_units(dev);
-    Ls = plan(kRows, trows + pairs, 1, V, dtype, vec, cus);
-    // the statistics pass uses the front of the workspace; the row statistics
-    // (target rows, then draft rows) and the overlap partials follow
-    const int64_t srows = trows + pairs;
+    // the statistics of the pairs' target rows (each sequence's bonus row is
+    // not read), then of their draft rows
+    Ls = plan(kRows, 2 * pairs, 1, V, dtype, vec, cus);
+    const int64_t blocks = Ls.blocks + pairs * nbr + ceil_div(pairs, kWavesPerBlock);
+    if (blocks * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
+    // data: the statistics blocks' slots, then the row statistics and the
+    // overlap partials; sync: the statistics blocks' row counters, the pairs'
+    // range counters, then the pairs' finished-row counters (one launch uses
+    // all three at once)
+    const int64_t srows = 2 * pairs;
     const size_t o_m = align_up(Ls.bytes, 256);
     const size_t o_s = align_up(o_m + static_cast<size_t>(srows) * sizeof(float), 256);
     const size_t o_pt = align_up(o_s + static_cast<size_t>(srows) * sizeof(double), 256);
+    const int64_t o_cnt = ceil_div(Ls.cnt_words, kSyncStride) * kSyncStride;
+    const int64_t o_done = o_cnt + ceil_div(pairs * kDraftStride, kSyncStride) * kSyncStride;
     Layout need{};
     need.bytes = align_up(o_pt + static_cast<size_t>(pairs) * nw * sizeof(double), 256);
-    need.cnt_words = std::max(Ls.cnt_words, pairs * kDraftStride);
+    need.cnt_words = o_done + pairs * kSyncStride;
     need.dec_words = Ls.dec_words;
     Workspace* ws = nullptr;
     if (int rc = get_workspace(dev, st, need, &ws)) return rc;
     char* base = static_cast<char*>(ws->data);
+    float* m_all = reinterpret_cast<float*>(base + o_m);
+    double* s_all = reinterpret_cast<double*>(base + o_s);
+    bind_workspace(Ls, *ws);
+    Ls.p.c32 = c32;
+    Ls.p.tgt = target_logits;
+    Ls.p.dft = draft_logits;
+    Ls.p.rows_split = pairs;
+    Ls.p.tgt_group = gamma;
+    Ls.p.rows_max = m_all;
+    Ls.p.rows_sumexp = s_all;
+    Ls.p.tree_done = ws->sync + o_done;  // each row counts in at its pair
+    Ls.p.tree_n = 1;
     OverlapParams O{};
     O.tgt = target_logits;
     O.dft = draft_logits;
@@ -3888,37 +3945,24 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     O.nw = nw;
     O.nbr = nbr;
     O.c32 = c32;
-    float* m_all = reinterpret_cast<float*>(base + o_m);
-    double* s_all = reinterpret_cast<double*>(base + o_s);
     O.m_t = m_all;
     O.s_t = s_all;
-    O.m_d = m_all + trows;
-    O.s_d = s_all + trows;
+    O.m_d = m_all + pairs;
+    O.s_d = s_all + pairs;
     O.part = reinterpret_cast<double*>(base + o_pt);
-    O.cnt = ws->sync;
-    const size_t off_dec = align_up(static_cast<size_t>(ws->cnt_cap) * sizeof(uint32_t), 256);
-    O.err = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws->sync) + off_dec +
-                                        static_cast<size_t>(ws->dec_cap) * sizeof(uint64_t));
+    O.cnt = ws->sync + o_cnt;
+    O.err = Ls.p.err;
     O.out_beta = out_beta;
-    // the statistics of every target row and every draft row in one launch
-    // (the same kernel and code as spec_row_stats), then the overlap
-    bind_workspace(Ls, *ws);
-    Ls.p.c32 = c32;
-    Ls.p.tgt = target_logits;
-    Ls.p.dft = draft_logits;
-    Ls.p.rows_split = trows;
-    Ls.p.rows_max = m_all;
-    Ls.p.rows_sumexp = s_all;
-    launch(dtype, vec, kRows, Ls, st);
-    if (int rc = check_launch("statistics kernel")) return rc;
+    O.first_block = Ls.blocks;
+    O.rows_done = Ls.p.tree_done;
     if (dtype == SPEC_F32) {
-        if (vec) launch_overlap_t<SPEC_F32, true>(O, blocks, st, nullptr, nullptr);
-        else launch_overlap_t<SPEC_F32, false>(O, blocks, st, nullptr, nullptr);
+        if (vec) launch_overlap_t<SPEC_F32, true>(Ls.p, O, blocks, st, nullptr, nullptr);
+        else launch_overlap_t<SPEC_F32, false>(Ls.p, O, blocks, st, nullptr, nullptr);
     } else {
-        if (vec) launch_overlap_t<SPEC_BF16, true>(O, blocks, st, nullptr, nullptr);
-        else launch_overlap_t<SPEC_BF16, false>(O, blocks, st, nullptr, nullptr);
+        if (vec) launch_overlap_t<SPEC_BF16, true>(Ls.p, O, blocks, st, nullptr, nullptr);
+        else launch_overlap_t<SPEC_BF16, false>(Ls.p, O, blocks, st, nullptr, nullptr);
     }
-    return check_launch("overlap kernel");
+    return check_launch("expected acceptance kernel");
 }
 
 int spec_tree_verify(const void* target_logits, const void* draft_logits, const int32_t* parent,
