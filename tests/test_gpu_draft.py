@@ -211,3 +211,32 @@ def test_expected_accept_edge_rows_and_workload():
     got = gpu_beta(full.target, full.draft, wl.dtype, wl.T)
     want = oracle.expected_accept(full.target, full.draft, wl.dtype, wl.T)
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
+
+
+def test_expected_accept_never_reads_the_bonus_rows():
+    """beta needs target rows 0..gamma-1 only: NaN in every bonus row (row
+    gamma of each sequence) leaves every beta finite and equal to the
+    oracle's."""
+    inp = W.small_random_inputs(5, 3, 3000, W.F32, 0.9, seed=12)
+    t = inp.target.copy()
+    t[:, -1, :] = np.nan
+    got = gpu_beta(t, inp.draft, W.F32, 0.9)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, oracle.expected_accept(inp.target, inp.draft, W.F32, 0.9), rtol=1e-5, atol=1e-6)
+
+
+def test_expected_accept_alternating_with_verification_on_one_workspace():
+    """The expected-acceptance launch keeps three sets of counters at once;
+    calls of it alternate with verification calls (whose counters share those
+    addresses) on one stream, and each call still matches the oracle."""
+    from oracle.compare import compare_tokens
+    a = W.small_random_inputs(16, 6, 2048, W.BF16, 0.8, seed=21)
+    v = W.small_random_inputs(8, 5, 4000, W.F32, 1.0, seed=22)
+    want = oracle.expected_accept(a.target, a.draft, W.BF16, 0.8)
+    orc = oracle.verify(v.target, v.draft, v.tokens, W.F32, 1.0, 5)
+    for _ in range(3):
+        np.testing.assert_allclose(gpu_beta(a.target, a.draft, W.BF16, 0.8), want, rtol=1e-5, atol=1e-6)
+        for schedule in (1, 2):
+            gpu = G.run(v, 5, schedule=schedule)
+            r = compare_tokens(v, orc, gpu.tokens, gpu.n, 5)
+            assert not r.hard_fail, r.hard_fail[:5]
