@@ -185,7 +185,7 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
 def expected_accept_leg(sv, sets, wl, args, stream):
     """spec_expected_accept (every position's sum of min(p, q)) on the
     workload: K calls rotating the input sets, timed by stream events around
-    the calls (two launches each: the statistics pass, the overlap)."""
+    the calls (one launch each: the statistics pass, then the overlap)."""
     import torch
     B, g, V = wl.B, wl.gamma, wl.V
     esz = 4 if wl.dtype == W.F32 else 2
@@ -228,7 +228,7 @@ def tree_leg(sv, wl, args, stream):
     depth 3 and branching factor 3 ([CSDN] 3.2 uses 3) over the workload's
     vocabulary and dtype: B = 8 trees of 40 nodes, every node's target and
     draft rows (two sets of 164 MB at the headline shape, rotated). Timed by
-    stream events around the calls (two launches each)."""
+    stream events around the calls (one launch each)."""
     import torch
     dev = torch.device("cuda:0")
     depth, branch, B = 3, 3, 8
