@@ -88,7 +88,7 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def cpu_baseline(inp, seed, sample_b, gpu_tokens=None, gpu_n=None, min_reps=3, min_wall_s=3.0, max_reps=400):
+def cpu_baseline(inp, seed, sample_b, gpu_tokens=None, gpu_n=None, min_reps=3, min_wall_s=10.0, max_reps=1000):
     """The fp64 oracle, as it stands, on the first `sample_b` sequences of the
     workload (same seed, same b indices), timed on the host cores: repeated
     until at least `min_wall_s` of wall time (and `min_reps` runs), median."""
