@@ -47,7 +47,8 @@ def run_tree(tr, T, threshold, target=None, draft=None, parent=None, token=None)
 
 TREES = [(8, 3, 3, 1000, W.F32), (6, 4, 2, 3000, W.BF16), (4, 2, 5, 1003, W.F32), (3, 5, 2, 40000, W.BF16),
          (2, 3, 4, 128256, W.BF16), (5, 1, 70, 500, W.F32),   # 70 children of the root (two tiles)
-         (3, 2, 17, 600, W.BF16)]                             # 307 nodes: parents and tokens read from memory
+         (3, 2, 17, 600, W.BF16),                             # 307 nodes: parents and tokens read from memory
+         (4, 3, 2, 1001, W.BF16)]                             # bf16 rows not a multiple of 16 bytes: scalar loads
 
 
 @pytest.mark.parametrize("B,depth,branch,V,dtype", TREES)
