@@ -124,12 +124,14 @@ typedef struct {
     int32_t schedule;      /* a spec_schedule_t (0 = SPEC_SCHEDULE_AUTO), see below */
 } spec_extras_t;
 
-/* Grid schedules of the T > 0 kernel (T == 0 always takes the position-major
- * schedule with the early stop). Outputs do not depend on the schedule.
- *  SPEC_SCHEDULE_GROUP       group-major: a sequence's 2*gamma+1 rows are
- *                            streamed together, every row is read; the
- *                            sequence's residual blocks (at the end of the
- *                            grid) take the accept step and the draw.
+/* Grid schedules. Outputs do not depend on the schedule. At T == 0 GROUP
+ * selects the group-major order and every other value the position-major
+ * order with the early stop.
+ *  SPEC_SCHEDULE_GROUP       group-major: a sequence's 2*gamma+1 rows (T == 0:
+ *                            its gamma+1 target rows) are streamed together,
+ *                            every row is read; the sequence's closing blocks
+ *                            (at the end of the grid) take the accept step and
+ *                            the draw (T == 0: one block, the greedy step).
  *  SPEC_SCHEDULE_EARLY_STOP  position-major: all sequences' position 0, then
  *                            position 1, ...; each position is decided as soon
  *                            as its rows are streamed, and a block whose

@@ -2350,9 +2350,38 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     if (in.k >= 0) draw<DT, VEC>(P, g, in, lane);
 }
 
-// The group-major kernel (T > 0): statistics blocks stream whole groups, the
-// group's residual blocks take the accept step and the draw.
-template <int DT, bool VEC>
+// T == 0: the one closing block of group g (the sequence's gamma + 1 target
+// rows). Once every statistics block of g has counted in, it folds the rows'
+// argmax partials and takes the greedy step (accept while the draft token is
+// the row's argmax, emit the argmax at the first mismatch or the bonus row),
+// then resets the group's count for the next call.
+__device__ inline void group_greedy_block(const Params& P, uint32_t g, char* dyn) {
+    __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
+    __shared__ int s_ok;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(threadIdx.x / kWave);
+    const int32_t gamma = P.gamma;
+    int32_t x = 0;  // the draft tokens do not depend on the statistics: loaded before the wait
+    if (w == 0 && lane < gamma) x = P.tokens[static_cast<int64_t>(g) * gamma + lane];
+    if (threadIdx.x == 0) s_ok = wait_published(P, g) ? 1 : 0;
+    __syncthreads();
+    after_complete();
+    if (s_ok) {
+        merge_group<true, kBlock>(P, g, dyn, rs);
+        if (w == 0) {
+            (void)accept_wave<true>(P, g, rs, x, 0.0f, 0.0f, 0.0, true);
+            if (lane == 0) cst(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 0u);
+        }
+    } else if (w == 0) {  // the wait ran out (not expected): the sequence is reported invalid
+        if (lane <= gamma) cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, -1);
+        if (lane == 0) cst(P.out_n + g, -1);
+    }
+}
+
+// The group-major kernel: statistics blocks stream whole groups; at T > 0 the
+// group's residual blocks take the accept step and the draw, at T == 0 one
+// block per group takes the greedy step.
+template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kBlock) void k_group(Params P) {
     extern __shared__ __align__(16) char dyn[];
     int kind;
@@ -2375,7 +2404,7 @@ __global__ __launch_bounds__(kBlock) void k_group(Params P) {
         U.rows = P.rps;
         U.nw = P.nw;
         U.nb = P.sb;
-        const int n = stats_wave<DT, VEC, kSample, true>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
+        const int n = stats_wave<DT, VEC, MODE, true>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
         // count this wavefront in at the block; the last one writes the block's pieces
         if (lane == 0) bp.n[w] = n;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -2384,12 +2413,14 @@ __global__ __launch_bounds__(kBlock) void k_group(Params P) {
         old = __shfl(old, 0, kWave);
         if (old + 1u != static_cast<uint32_t>(nwb)) return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        write_pieces<kSample>(P, bp, nwb, lane);
-        // the residual blocks of g watch this count reach sb
+        write_pieces<MODE>(P, bp, nwb, lane);
+        // the closing blocks of g watch this count reach sb
         complete_before();
         if (lane == 0)
             (void)__hip_atomic_fetch_add(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 1u, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (MODE == kGreedy) {
+        group_greedy_block(P, g, dyn);
     } else {
         group_resid_block<DT, VEC>(P, g, idx, dyn);
     }
@@ -3410,14 +3441,15 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
 // statistics wavefronts take about kChunksPerWave chunks each (at least 16
 // wavefronts per compute unit over the whole problem), and its residual
 // wavefronts take subs_per_wave() subsegments of row k each.
-Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus) {
+Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus, int mode = kSample) {
     Layout L{};
     Params& p = L.p;
     L.group = true;
+    const bool greedy = mode == kGreedy;  // the target rows only, and one closing block per group
     p.B = static_cast<int32_t>(G);
     p.gamma = gamma;
     p.V = V;
-    p.rps = 2 * gamma + 1;
+    p.rps = greedy ? gamma + 1 : 2 * gamma + 1;
     const int32_t CH = chunk_elems(dtype, vec);
     p.nchunk = static_cast<int32_t>(ceil_div(V, CH));
     const int64_t per_group = static_cast<int64_t>(p.rps) * p.nchunk;
@@ -3433,7 +3465,7 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     p.nsub = static_cast<int32_t>(ceil_div(V, kSub));
     const int spw = vec ? (dtype == SPEC_BF16 ? subs_per_wave<SPEC_BF16, true>() : subs_per_wave<SPEC_F32, true>())
                         : subs_per_wave<SPEC_F32, false>();
-    p.rb = static_cast<int32_t>(ceil_div(p.nsub, kWavesPerBlock * spw));
+    p.rb = greedy ? 1 : static_cast<int32_t>(ceil_div(p.nsub, kWavesPerBlock * spw));
     p.lag = static_cast<int32_t>(G < kLag ? G : kLag);
     p.cstride = kSyncStride;
     const int64_t gslots = static_cast<int64_t>(p.rps) * p.maxp;
@@ -3446,10 +3478,12 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     L.off_pm = o;
     o = align_up(o + slots * sizeof(float), 256);
     L.off_pr = o;
-    o = align_up(o + slots * sizeof(float), 256);
+    o = align_up(o + (greedy ? 0 : slots) * sizeof(float), 256);
     L.off_ps = o;
-    o = align_up(o + slots * sizeof(double), 256);
-    L.off_pi = L.off_tok = L.off_msum = o;
+    o = align_up(o + (greedy ? 0 : slots) * sizeof(double), 256);
+    L.off_pi = o;
+    o = align_up(o + (greedy ? slots : 0) * sizeof(int32_t), 256);
+    L.off_tok = L.off_msum = o;
     L.off_subr = o;
     o = align_up(o + static_cast<size_t>(G) * p.nsub * sizeof(double), 256);
     L.bytes = o;
@@ -3575,8 +3609,10 @@ void bind_workspace(Layout& L, const Workspace& ws) {
 template <int DT, bool VEC>
 void launch_t(int mode, const Layout& L, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid(static_cast<unsigned>(L.blocks)), block(kBlock);
-    if (L.group)
-        hipExtLaunchKernelGGL((k_group<DT, VEC>), grid, block, L.lds, st, e0, e1, 0, L.p);
+    if (L.group && mode == kGreedy)
+        hipExtLaunchKernelGGL((k_group<DT, VEC, kGreedy>), grid, block, L.lds, st, e0, e1, 0, L.p);
+    else if (L.group)
+        hipExtLaunchKernelGGL((k_group<DT, VEC, kSample>), grid, block, L.lds, st, e0, e1, 0, L.p);
     else if (mode == kSample)
         hipExtLaunchKernelGGL((k_verify<DT, VEC, kSample>), grid, block, 0, st, e0, e1, 0, L.p);
     else if (mode == kGreedy)
@@ -3756,8 +3792,8 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
                                     extras->argmax);
     // the size limits do not depend on the device: checked before any HIP call
     if (int rc = check_size(mode, plan(mode, B, gamma, V, dtype, vec, 1))) return rc;
-    if (!greedy) {
-        if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1))) return rc;
+    if (!greedy || sched == SPEC_SCHEDULE_GROUP) {
+        if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode))) return rc;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
@@ -3767,7 +3803,9 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     const int cus = compute_units(dev);
     Layout L = plan(mode, B, gamma, V, dtype, vec, cus);
     bool early = true;
-    if (!greedy) {
+    if (greedy && sched == SPEC_SCHEDULE_GROUP) {
+        L = plan_group(B, gamma, V, dtype, vec, cus, kGreedy);
+    } else if (!greedy) {
         // auto: position-major with the early stop once one position's units
         // fill the chip (about four blocks per compute unit), else group-major
         const bool pos = sched == SPEC_SCHEDULE_AUTO ? auto_position_major(B, L, cus) : sched != SPEC_SCHEDULE_GROUP;
