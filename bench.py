@@ -444,7 +444,8 @@ def main():
     achieved = float(np.sum(k_bytes)) / (float(np.sum(k_ms)) * 1e-3) / 1e9
 
     schedules = {}
-    legs = () if args.auto_only else ((sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION) if wl.T == 0.0 else
+    # (at T == 0 every schedule but GROUP is the position-major order with the early stop)
+    legs = () if args.auto_only else ((sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP) if wl.T == 0.0 else
                                       (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION))
     for sched in legs:
         ms_s, km_s, ev_s = timed(with_schedule(sched))
