@@ -3745,9 +3745,9 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t 
     (void)hipGetDevice(&dev);
     std::lock_guard<std::mutex> lk(g_mu);
     const int cus = compute_units(dev);
-    const Layout Lp = plan(temperature == 0.0f ? kGreedy : kSample, B, gamma, V, dtype, vec, cus);
-    if (temperature == 0.0f) return Lp.bytes + sync_bytes(Lp.cnt_words, Lp.dec_words);
-    const Layout Lg = plan_group(B, gamma, V, dtype, vec, cus);
+    const int mode = temperature == 0.0f ? kGreedy : kSample;
+    const Layout Lp = plan(mode, B, gamma, V, dtype, vec, cus);
+    const Layout Lg = plan_group(B, gamma, V, dtype, vec, cus, mode);  // (T == 0: the selectable group-major order)
     return std::max(Lp.bytes, Lg.bytes) + sync_bytes(std::max(Lp.cnt_words, Lg.cnt_words), Lp.dec_words);
 }
 
