@@ -106,8 +106,8 @@ int orc_draft_sample(const void* logits, int32_t B, int32_t n, int64_t V, int dt
                      uint64_t seed, int64_t pos0, int64_t b_offset, int32_t* out_tokens,
                      double* out_q, double* cdf_lo, double* cdf_hi);
 
-/* Per-row diagnostics for choosing the draft length ([Ch15] 15.1.2, dynamic
- * strategy adjustment: the acceptance-rate window rule; 15.2.3, adaptive
+/* Per-row diagnostics for choosing the draft length ([Ch15] 15.1.4, dynamic
+ * strategy adjustment: the acceptance-rate window rule; 15.2.4, adaptive
  * draft length from the prediction entropy; Lemma 1 for the expected
  * acceptance).
  * orc_row_entropy: H = -sum_j p_j ln p_j of p = softmax(l / T) (natural log;

@@ -1,10 +1,10 @@
 """Host-side choice of the draft length gamma between verification calls.
 
 Two rules from "Chapter 15: Decoding acceleration techniques" (zsc.github.io):
-  - 15.1.2, dynamic strategy adjustment, adaptive draft length: the mean
+  - 15.1.4, dynamic strategy adjustment, adaptive draft length: the mean
     acceptance rate over a sliding window of recent calls raises gamma by one
     above 0.85 and lowers it by one below 0.6, within [gamma_min, gamma_max];
-  - 15.2.3, adaptive draft length from the prediction entropy: an entropy below
+  - 15.2.4, adaptive draft length from the prediction entropy: an entropy below
     0.5 allows up to 8 draft tokens, below 1.0 up to 4, otherwise 1.
 Both are plain host logic; the inputs come from the GPU path (the accepted
 counts spec_verify returns, the entropy spec_draft_sample_ex returns, or the

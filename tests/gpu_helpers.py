@@ -1,5 +1,6 @@
 """Helpers shared by the GPU tests: move seeded inputs to the device and run
-the HIP path through the C ABI with every debug output enabled."""
+the HIP path through the C ABI, with every debug output enabled (every row is
+then read) or with none (the early stop then skips rows)."""
 import ctypes
 
 import numpy as np
@@ -19,9 +20,12 @@ class GpuRun:
     pass
 
 
-def run(inp, seed, b_offset=0, tensors=None, stream=None, schedule=0):
-    """Run spec_verify_ex on `inp` with every debug output (so every row is
-    read) and the given schedule; return numpy outputs and debug values."""
+def run(inp, seed, b_offset=0, tensors=None, stream=None, schedule=0, debug=True):
+    """Run spec_verify_ex on `inp` with the given schedule; return numpy
+    outputs and debug values. With debug, every per-row debug output is asked
+    for, which makes the early-stop schedule read every row; without it only
+    the schedule and the offset are passed (the per-row fields stay NaN / -7),
+    so the early stop skips the rows of sequences that already stopped."""
     wl = inp.wl
     B, g, V = wl.B, wl.gamma, wl.V
     dev = torch.device("cuda:0")
@@ -39,14 +43,17 @@ def run(inp, seed, b_offset=0, tensors=None, stream=None, schedule=0):
     Z = torch.full((B,), float("nan"), dtype=torch.float64, device=dev)
     am = torch.full((B, g + 1), -7, dtype=torch.int32, device=dev)
     ex = sv.Extras()
-    ex.row_max = row_max.data_ptr()
-    ex.row_sumexp = row_s.data_ptr()
-    ex.p_draft = p.data_ptr()
-    ex.q_draft = q.data_ptr()
-    ex.Z = Z.data_ptr()
-    ex.argmax = am.data_ptr()
+    if debug:
+        ex.row_max = row_max.data_ptr()
+        ex.row_sumexp = row_s.data_ptr()
+        ex.p_draft = p.data_ptr()
+        ex.q_draft = q.data_ptr()
+        ex.Z = Z.data_ptr()
+        ex.argmax = am.data_ptr()
     ex.b_offset = b_offset
     ex.schedule = schedule
+    print(f"verify B={B} gamma={g} V={V} dtype={wl.dtype} T={wl.T} seed={seed} schedule={schedule} "
+          f"debug={debug}", flush=True)
     out_t, out_n = sv.verify(tgt, dft, tok, wl.T, seed, extras=ex, stream=stream)
     torch.cuda.synchronize()
     r = GpuRun()

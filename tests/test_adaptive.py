@@ -1,5 +1,5 @@
-"""The host-side draft-length rules ([Ch15] 15.1.2 dynamic strategy adjustment;
-15.2.3 adaptive draft length from the entropy), on the CPU."""
+"""The host-side draft-length rules ([Ch15] 15.1.4 dynamic strategy adjustment;
+15.2.4 adaptive draft length from the entropy), on the CPU."""
 import math
 
 import pytest

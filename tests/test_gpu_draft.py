@@ -114,7 +114,9 @@ def test_draft_split_calls_and_reuse():
     np.testing.assert_array_equal(qw, qa)
     r = G.run(vinp, seed=1)
     o = oracle.verify(vinp.target, vinp.draft, vinp.tokens, W.F32, 0.9, seed=1)
-    assert (r.n == o.n).mean() > 0.99
+    from oracle.compare import compare_tokens
+    rep = compare_tokens(vinp, o, r.tokens, r.n, 1)
+    assert rep.ok() and not rep.hard_fail, str(rep) + " " + str(rep.hard_fail[:5])
 
 
 def test_draft_two_dim_input_and_no_q():
@@ -124,14 +126,15 @@ def test_draft_two_dim_input_and_no_q():
     torch.cuda.synchronize()
     assert q is None and tuple(tok.shape) == (4,)
     orc = oracle.draft_sample(inp.draft, W.F32, 1.0, seed=4, pos0=3)
-    assert (tok.cpu().numpy() == orc.tokens[:, 0]).mean() >= 0.75
+    rep = compare_draft(inp.draft, W.F32, 1.0, orc, tok.cpu().numpy()[:, None], None, 4, pos0=3)
+    assert rep.ok(), str(rep) + " " + str(rep.hard_fail[:5])
 
 
 @pytest.mark.parametrize("B,n,V,dtype", [(3, 4, 1000, W.F32), (2, 3, 40000, W.BF16), (2, 2, 1003, W.F32),
                                          (1, 2, 262144, W.F32), (2, 2, 128256, W.BF16)])
 @pytest.mark.parametrize("T", [0.7, 1.3, 0.0])
 def test_draft_entropy(B, n, V, dtype, T):
-    # the entropy beside the draw ([Ch15] 15.2.3): the same tokens as without
+    # the entropy beside the draw ([Ch15] 15.2.4): the same tokens as without
     # it, and H within 1e-5 of the oracle's (absolute, plus 1e-5 relative)
     inp = W.small_random_inputs(B, n, V, dtype, 1.0, seed=V % 31 + n)
     l64 = W.storage_to_f64(inp.draft, dtype)

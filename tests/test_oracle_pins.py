@@ -559,8 +559,8 @@ def test_draft_unusable_and_masked_rows():
 
 
 # ---------------------------------------------------------------------------
-# Diagnostics for the draft length ([Ch15] 15.1.2 dynamic strategy adjustment;
-# 15.2.3 adaptive draft length from the prediction entropy; Lemma 1)
+# Diagnostics for the draft length ([Ch15] 15.1.4 dynamic strategy adjustment;
+# 15.2.4 adaptive draft length from the prediction entropy; Lemma 1)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("V", [1, 2, 7, 1000])
 def test_entropy_of_equal_logits_is_log_V(V):
