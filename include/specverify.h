@@ -17,8 +17,8 @@
  * Around that step: the draft-side draw with its probabilities
  * (spec_draft_sample; [Ch15] 15.1.2 step 1), the diagnostics for choosing
  * the draft length (the row entropy beside that draw, the per-position
- * expected acceptance spec_expected_accept; [Ch15] 15.1.2 dynamic strategy
- * adjustment, 15.2.3), and token-tree verification as a labelled heuristic
+ * expected acceptance spec_expected_accept; [Ch15] 15.1.4 dynamic strategy
+ * adjustment, 15.2.4), and token-tree verification as a labelled heuristic
  * mode (spec_tree_verify; [CSDN] 3.2, [Ch15] 15.2.4).
  *
  * Conventions shared by every entry point:
@@ -43,6 +43,18 @@
  *    no finite entry; at T > 0 both rows of the position, at T == 0 the target
  *    row) or an out-of-range draft token gets out_n_accepted[b] = -1 and an
  *    all -1 out_tokens row. -inf logits are legal (masked tokens).
+ *  - Failure detection ([Ch15] 15.1.4, failure-mode detection and recovery:
+ *    the host must be able to see that the fast path misbehaved and fall
+ *    back). Inside a kernel, blocks wait for other blocks of the same launch
+ *    (always blocks of lower index, which in-order dispatch has started, so
+ *    in correct operation every wait ends). Every such wait is bounded (about
+ *    2 s by default, see spec_verify_set_wait_limit). A wait that runs out
+ *    sets a sticky word in the (device, stream) workspace, reports the
+ *    sequence, row, pair or tree it was computing as invalid (-1, or NaN for
+ *    the diagnostics) where it owns that output, and then drains: it goes on
+ *    waiting, up to the default bound, for what it waited for, so that the
+ *    workspace's counters are left at zero and the next call on the stream is
+ *    unaffected. spec_verify_status reads and clears the sticky word.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -95,9 +107,9 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
  *  library keeps a device workspace per (device, stream), grown on demand
  *  under a lock; concurrent calls on different streams are safe, calls on one
  *  stream are ordered. One kernel is launched per call. Inside it, blocks
- *  wait (bounded, about 2 s) for other blocks of the same sequence; should
- *  that bound ever run out the sequence is reported as -1 rather than the
- *  kernel waiting on. */
+ *  wait (bounded) for other blocks of the same sequence; should that bound
+ *  ever run out, the failure is reported as described above (failure
+ *  detection) rather than the kernel waiting on. */
 int spec_verify(const void* target_logits, const void* draft_logits,
                 const int32_t* draft_tokens, int32_t B, int32_t gamma, int32_t V,
                 int32_t dtype, float temperature, uint64_t seed,
@@ -199,7 +211,7 @@ typedef struct {
     double* entropy;  /* [B, n] DEVICE: H = -sum_j p_j ln p_j of softmax(l/T) per row
                          (natural log; 0 at T == 0; NaN for an unusable row), the
                          confidence measure for choosing the draft length ([Ch15]
-                         15.2.3, adaptive draft length). Formed in the same pass. */
+                         15.2.4, adaptive draft length). Formed in the same pass. */
     void* events[2];  /* hipEvent_t bound to the start and end of the dispatch */
 } spec_draft_extras_t;
 
@@ -213,7 +225,7 @@ int spec_draft_sample_ex(const void* logits, int32_t B, int32_t n, int32_t V, in
  * token when it is reached, beta[b, i] = sum_x min(p_i(x), q_i(x)) (Lemma 1
  * of [Ch15] 15.1.2; 1 - beta_i is the residual mass of the correction step),
  * for every position i < gamma: the per-position diagnostic behind the
- * acceptance-rate rule for the draft length ([Ch15] 15.1.2, dynamic strategy
+ * acceptance-rate rule for the draft length ([Ch15] 15.1.4, dynamic strategy
  * adjustment).
  *  target_logits [B, gamma+1, V], draft_logits [B, gamma, V]: dtype, DEVICE,
  *      row-major contiguous (the bonus rows are not read); temperature > 0.
@@ -259,6 +271,27 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
  * (SPEC_SCHEDULE_GROUP or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
 int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature);
 
+/* spec_verify_status: whether any bounded wait of a kernel enqueued on
+ * `stream` (current device) ran out since the last status call on that
+ * stream ([Ch15] 15.1.4, failure-mode detection: the host's view of it).
+ * Synchronises the stream, then sets *timed_out to 1 (and clears the word,
+ * scrubbing the workspace's counters) or 0. With a timed-out wait, the
+ * affected sequences of the calls since the last status call may be -1
+ * (invalid), or may have been computed correctly after the wait drained;
+ * no sequence holds a wrong token or count. Returns SPEC_OK, SPEC_EINVAL for
+ * a NULL timed_out, or SPEC_EHIP. Every entry point on one (device, stream)
+ * shares the word. */
+int spec_verify_status(void* stream, int32_t* timed_out);
+
+/* spec_verify_set_wait_limit: the bound on every in-kernel wait of calls
+ * made after it, in ticks of the device's constant-rate wall clock (100 MHz
+ * on gfx950); ticks < 0 restores the default (2e8 ticks, about 2 s).
+ * Process-wide; returns the previous setting (-1 for the default). Meant for
+ * tests of the failure path (0 makes every wait that is not satisfied at
+ * its first poll give up), never needed for correct operation. The drain
+ * after a wait gives up always uses the default bound. */
+int64_t spec_verify_set_wait_limit(int64_t ticks);
+
 /* Bytes of device workspace one call of this shape needs (the library
  * allocates and owns it). */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
@@ -270,8 +303,9 @@ void spec_verify_release_workspace(void);
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* spec_verify_last_error(void);
 
-/* ABI version: 5 (2: spec_extras_t gained schedule; 3: spec_draft_sample;
- * 4: spec_draft_extras_t and spec_expected_accept; 5: spec_tree_verify). */
+/* ABI version: 6 (2: spec_extras_t gained schedule; 3: spec_draft_sample;
+ * 4: spec_draft_extras_t and spec_expected_accept; 5: spec_tree_verify;
+ * 6: spec_verify_status and spec_verify_set_wait_limit). */
 int32_t spec_verify_abi_version(void);
 
 #ifdef __cplusplus

@@ -28,6 +28,8 @@ EXPORTS = (
     "spec_expected_accept",
     "spec_tree_verify",
     "spec_verify_schedule",
+    "spec_verify_status",
+    "spec_verify_set_wait_limit",
     "spec_verify_workspace_bytes",
     "spec_verify_release_workspace",
     "spec_verify_last_error",
@@ -94,6 +96,10 @@ def load_library(path: str = LIB_PATH):
     L.spec_tree_verify.restype = ctypes.c_int
     L.spec_verify_schedule.argtypes = [i32, i32, i32, i32, f32]
     L.spec_verify_schedule.restype = i32
+    L.spec_verify_status.argtypes = [vp, ctypes.POINTER(i32)]
+    L.spec_verify_status.restype = ctypes.c_int
+    L.spec_verify_set_wait_limit.argtypes = [i64]
+    L.spec_verify_set_wait_limit.restype = i64
     L.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, f32]
     L.spec_verify_workspace_bytes.restype = ctypes.c_size_t
     L.spec_verify_release_workspace.argtypes = []
@@ -299,6 +305,22 @@ def auto_schedule(B, gamma, V, dtype, temperature) -> int:
     if rc < 0:
         raise SpecVerifyError(rc, last_error())
     return rc
+
+
+def status(stream=None) -> bool:
+    """Whether a bounded in-kernel wait on `stream` (default: torch's current
+    stream) ran out since the last status call; synchronises the stream and
+    clears the flag."""
+    flag = ctypes.c_int32(0)
+    _check(load_library().spec_verify_status(_stream_handle(stream), ctypes.byref(flag)))
+    return bool(flag.value)
+
+
+def set_wait_limit(ticks: int) -> int:
+    """Bound on every in-kernel wait of later calls, in device wall-clock ticks
+    (100 MHz); negative restores the default. Returns the previous setting.
+    For tests of the failure path only."""
+    return int(load_library().spec_verify_set_wait_limit(int(ticks)))
 
 
 def workspace_bytes(B, gamma, V, dtype, temperature) -> int:

@@ -56,6 +56,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -108,7 +109,7 @@ constexpr int kMaxStage = 1024;             // group-major: partial slots of one
 constexpr int kHold = 8;                    // chunks a draw wavefront holds in registers
 constexpr int kPairCw = kHold / 2;          // of each row: target and draft
 constexpr float kRUnset = -1.0e30f;         // reference before the first finite value
-constexpr uint64_t kWaitTicks = 200000000ull;        // bound on any wait: 2 s at 100 MHz
+constexpr uint64_t kWaitTicks = 200000000ull;        // default bound on a wait, and the drain bound: 2 s at 100 MHz
 constexpr int kSleep = SPECVERIFY_SLEEP;             // s_sleep argument between polls (64 cycles each)
 constexpr int kSyncStride = SPECVERIFY_SYNC_STRIDE;  // words between two counters
 constexpr int kRecWords = 32;               // per sequence: draw record (tag + 3 data words), then its two
@@ -347,6 +348,25 @@ __device__ inline void after_complete() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
+// Bounded spin: polls pred() (wave-uniform, or called by a single lane), with
+// a short sleep between polls, until it holds (true) or more than `ticks` of
+// the device's constant-rate wall clock have passed since the first failed
+// poll (false). Every wait below waits only for blocks of lower index, which
+// in-order dispatch has already started, so in correct operation it ends; the
+// bound is the failure detector. A wait that gives up sets the sticky error
+// word, reports what it owns as invalid, and then drains: it goes on waiting,
+// up to kWaitTicks, for the same condition, so that the counters it would
+// reset are left at zero for the next call.
+template <class Pred>
+__device__ inline bool spin_until(Pred pred, uint64_t ticks) {
+    if (pred()) return true;
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+        __builtin_amdgcn_s_sleep(kSleep);
+        if (pred()) return true;
+        if (wall_clock64() - t0 > ticks) return false;
+    }
+}
 // --------------------------------------------------------------------------
 // Launch geometry and arguments
 // --------------------------------------------------------------------------
@@ -372,6 +392,7 @@ struct Params {
     int32_t stage;   //   a group's partial slots staged in LDS, or 0 (fold from memory)
     int32_t skip;    // early stop: wavefronts of sequences already stopped load nothing
     uint32_t epoch;  // tag of this call's decision words and draw records (never 0)
+    uint64_t wait;   // bound on a wait, in wall-clock ticks (kWaitTicks unless the host set another)
     float c32;       // log2(e)/T
     uint64_t seed;
     int64_t b_offset;
@@ -579,18 +600,20 @@ __device__ inline int sequence_state(const Params& P, int32_t b, int32_t i, int 
     return state_of(P, decision_word(P, b, i, lane), i, lane);
 }
 // `s` is the state from an earlier read (kUnknown: read again until known).
-__device__ inline int wait_sequence_state(const Params& P, int32_t b, int32_t i, int lane, int s) {
+// If the bound runs out, the sticky error word is set and `late` raised, and
+// the read goes on (drains) up to kWaitTicks, so that the caller still learns
+// whether its position ends the sequence; kTimedOut if that runs out too.
+__device__ inline int wait_sequence_state(const Params& P, int32_t b, int32_t i, int lane, int s, bool& late) {
+    late = false;
     if (s != kUnknown) return s;
-    const uint64_t t0 = wall_clock64();
-    for (;;) {
-        __builtin_amdgcn_s_sleep(kSleep);
+    auto known = [&] {
         s = sequence_state(P, b, i, lane);
-        if (s != kUnknown) return s;
-        if (wall_clock64() - t0 > kWaitTicks) {
-            cst(P.err, 1u);
-            return kTimedOut;
-        }
-    }
+        return s != kUnknown;
+    };
+    if (spin_until(known, P.wait)) return s;
+    late = true;
+    if (lane == 0) cst(P.err, 1u);
+    return spin_until(known, kWaitTicks) ? s : kTimedOut;
 }
 __device__ inline void publish(const Params& P, int32_t b, int32_t i, uint32_t status) {
     cst64(P.dec + static_cast<int64_t>(b) * (P.gamma + 1) + i, (static_cast<uint64_t>(P.epoch) << 32) | status);
@@ -1267,7 +1290,8 @@ __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
     // for the earlier positions' outcomes
     if (pair && lane == 0) publish(P, U.b, U.i, status);
     if (pair && status == kAcc) return;
-    const int state = U.i > 0 ? wait_sequence_state(P, U.b, U.i, lane, state_of(P, wd, U.i, lane)) : kLive;
+    bool late = false;
+    const int state = U.i > 0 ? wait_sequence_state(P, U.b, U.i, lane, state_of(P, wd, U.i, lane), late) : kLive;
     if (state == kStopped) return;
     MassRow mr;
     mr.c32 = c;
@@ -1280,7 +1304,9 @@ __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
                             : 0.0;
     mr.rhi = static_cast<float>(rho);
     mr.rlo = static_cast<float>(rho - static_cast<double>(mr.rhi));
-    if (state == kTimedOut) {
+    if (state == kTimedOut || late) {
+        // this position ends the sequence, but its wait for the earlier
+        // positions ran out: the sequence is reported invalid
         write_outputs(P, U.b, U.i, true, xj, lane);
         if (lane == 0) write_record(P, U.b, kNoDraw, U.i, mr, scale_p);
         return;
@@ -1325,9 +1351,10 @@ __device__ inline void decide_greedy(const Params& P, const Role& U, int lane) {
         status = ut ? kRej : kBad;  // the bonus row ends the sequence either way
     }
     if (status == kAcc) return;
-    const int state = U.i > 0 ? wait_sequence_state(P, U.b, U.i, lane, state_of(P, wd, U.i, lane)) : kLive;
+    bool late = false;
+    const int state = U.i > 0 ? wait_sequence_state(P, U.b, U.i, lane, state_of(P, wd, U.i, lane), late) : kLive;
     if (state == kStopped) return;
-    if (state == kTimedOut) {
+    if (state == kTimedOut || late) {  // ends the sequence, but its wait ran out: reported invalid
         write_outputs(P, U.b, U.i, true, xj, lane);
         return;
     }
@@ -1548,20 +1575,13 @@ __device__ inline void resid_block(const Params& P, const Role& U) {
     if (w == 0) {
         DrawInfo d;
         d.kind = kNoDraw;
-        bool ok = read_record(P, b, lane, d);
+        auto got = [&] { return read_record(P, b, lane, d); };
+        bool ok = spin_until(got, P.wait);
         if (!ok) {
-            const uint64_t t0 = wall_clock64();
-            for (;;) {
-                __builtin_amdgcn_s_sleep(kSleep);
-                if (read_record(P, b, lane, d)) {
-                    ok = true;
-                    break;
-                }
-                if (wall_clock64() - t0 > kWaitTicks) {
-                    cst(P.err, 1u);
-                    break;
-                }
-            }
+            // flagged; the record is still awaited (drained) and, if it
+            // comes, drawn as usual, so the sequence's outputs stay whole
+            if (lane == 0) cst(P.err, 1u);
+            ok = spin_until(got, kWaitTicks);
         }
         if (lane == 0) {
             s_ok = ok ? 1 : 0;
@@ -1569,7 +1589,7 @@ __device__ inline void resid_block(const Params& P, const Role& U) {
         }
     }
     __syncthreads();
-    if (!s_ok) {  // the record never came (not expected): report the sequence invalid
+    if (!s_ok) {  // the record never came, even after the drain: report the sequence invalid
         if (U.r == 0 && w == 0) write_outputs(P, b, 0, true, 0, lane);
         return;
     }
@@ -2222,22 +2242,22 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
 // --------------------------------------------------------------------------
 // Group finishers and the residual block
 // --------------------------------------------------------------------------
-// Waits until every statistics block of group g has counted in; false if the
-// bounded wait ran out (then the sticky error word is set).
-__device__ inline bool wait_published(const Params& P, uint32_t g) {
+// Waits (one lane) until every statistics block of group g has counted in.
+// Returns 0 if they did within the bound; 1 if the bound ran out (the sticky
+// error word is then set) but they did within the drain that follows; 2 if
+// not even then.
+__device__ inline int wait_published(const Params& P, uint32_t g) {
     const uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
     const uint32_t want = static_cast<uint32_t>(P.sb);
-    if (cld(cnt) == want) return true;
-    const uint64_t t0 = wall_clock64();
-    for (;;) {
-        __builtin_amdgcn_s_sleep(kSleep);
-        if (cld(cnt) == want) return true;
-        if (wall_clock64() - t0 > kWaitTicks) {
-            cst(P.err, 1u);
-            return false;
-        }
-    }
+    auto all_in = [&] { return cld(cnt) == want; };
+    if (spin_until(all_in, P.wait)) return 0;
+    cst(P.err, 1u);
+    return spin_until(all_in, kWaitTicks) ? 1 : 2;
 }
+// Group-major: the word that marks group g's outputs void in this call (a wait
+// of one of its closing blocks ran out); the group's last closing block then
+// writes the whole row as invalid.
+__device__ inline uint64_t* void_word(const Params& P, uint32_t g) { return P.dec + g; }
 
 // T > 0: one residual block of group g (idx in [0, rb)). Once every
 // statistics block of g has counted in, the block folds g's partials and
@@ -2249,7 +2269,7 @@ template <int DT, bool VEC>
 __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t idx, char* dyn) {
     __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
     __shared__ SeqInfo shi;
-    __shared__ int s_ok;
+    __shared__ int s_st;
     __shared__ uint32_t s_last;
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     const int w = static_cast<int>(threadIdx.x / kWave);
@@ -2267,12 +2287,16 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
             ld = load_one<DT>(group_row<DT>(P, g, static_cast<uint32_t>(gamma + 1 + lane)), x);
         }
     }
-    if (threadIdx.x == 0) s_ok = wait_published(P, g) ? 1 : 0;
+    if (threadIdx.x == 0) {
+        const int st = wait_published(P, g);
+        if (st != 0) cst64(void_word(P, g), tagged(P, 1u));  // the wait ran out: the group's outputs are void
+        s_st = st;
+    }
     __syncthreads();
     after_complete();
     SeqInfo in;
     in.k = -1;
-    if (s_ok) {
+    if (s_st == 0) {
         merge_group<false, kBlock>(P, g, dyn, rs);
         if (w == 0) {
             const SeqInfo si = accept_wave<false>(P, g, rs, x, lt, ld, u, idx == 0);
@@ -2280,10 +2304,6 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
         }
         __syncthreads();
         in = shi;
-    } else if (idx == 0 && w == 0) {
-        // the wait ran out (not expected): the sequence is reported invalid
-        if (lane <= gamma) cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, -1);
-        if (lane == 0) cst(P.out_n + g, -1);
     }
     if (in.k >= 0) {
         constexpr int NS = subs_per_wave<DT, VEC>();
@@ -2343,11 +2363,24 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     __syncthreads();
     if (!s_last || w != 0) return;
     after_complete();
-    if (lane == 0) {  // every statistics and residual block of g has counted in
-        cst(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 0u);
+    // every residual block of g has counted in, each after seeing the
+    // statistics count complete (unless even its drain ran out: then the
+    // count is left for the status call's scrub)
+    uint32_t* cnt_s = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
+    const bool dead = static_cast<uint32_t>(cld64(void_word(P, g)) >> 32) == P.epoch;
+    if (lane == 0) {
+        if (cld(cnt_s) == static_cast<uint32_t>(P.sb)) cst(cnt_s, 0u);
         cst(cnt_r, 0u);
     }
-    if (in.k >= 0) draw<DT, VEC>(P, g, in, lane);
+    if (dead) {  // a closing block's wait ran out: the whole row is reported invalid
+        if (lane <= gamma) cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, -1);
+        if (lane == 0) {
+            cst(P.out_n + g, -1);
+            if (P.dbg_z) P.dbg_z[g] = NAN;
+        }
+    } else if (in.k >= 0) {
+        draw<DT, VEC>(P, g, in, lane);
+    }
 }
 
 // T == 0: the one closing block of group g (the sequence's gamma + 1 target
@@ -2357,25 +2390,25 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
 // then resets the group's count for the next call.
 __device__ inline void group_greedy_block(const Params& P, uint32_t g, char* dyn) {
     __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
-    __shared__ int s_ok;
+    __shared__ int s_st;
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     const int w = static_cast<int>(threadIdx.x / kWave);
     const int32_t gamma = P.gamma;
     int32_t x = 0;  // the draft tokens do not depend on the statistics: loaded before the wait
     if (w == 0 && lane < gamma) x = P.tokens[static_cast<int64_t>(g) * gamma + lane];
-    if (threadIdx.x == 0) s_ok = wait_published(P, g) ? 1 : 0;
+    if (threadIdx.x == 0) s_st = wait_published(P, g);
     __syncthreads();
     after_complete();
-    if (s_ok) {
+    if (s_st == 0) {
         merge_group<true, kBlock>(P, g, dyn, rs);
-        if (w == 0) {
-            (void)accept_wave<true>(P, g, rs, x, 0.0f, 0.0f, 0.0, true);
-            if (lane == 0) cst(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 0u);
-        }
-    } else if (w == 0) {  // the wait ran out (not expected): the sequence is reported invalid
+        if (w == 0) (void)accept_wave<true>(P, g, rs, x, 0.0f, 0.0f, 0.0, true);
+    } else if (w == 0) {  // the wait ran out: the sequence is reported invalid
         if (lane <= gamma) cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, -1);
         if (lane == 0) cst(P.out_n + g, -1);
     }
+    // every statistics block has counted in (unless even the drain ran out:
+    // then the count is left for the status call's scrub)
+    if (w == 0 && lane == 0 && s_st != 2) cst(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 0u);
 }
 
 // The group-major kernel: statistics blocks stream whole groups; at T > 0 the
@@ -2483,6 +2516,7 @@ struct DraftParams {
     uint32_t epoch;       // this call's tag
     double* out_h;        // [rows] or null: entropy of softmax(l/T) per row
     uint32_t* err;        // sticky error word (a bounded wait ran out)
+    uint64_t wait;        // bound on the closing wavefront's wait, in wall-clock ticks
 };
 constexpr int kDraftWords = 3;
 __device__ inline uint64_t tagged(uint32_t epoch, uint32_t payload) {
@@ -2749,7 +2783,9 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
                     for (int wd = 0; wd < NWD; ++wd) stale |= !current(cld64(pw + static_cast<int64_t>(k) * kDraftWords + wd));
             }
             if (__ballot(stale) == 0) break;
-            if (wall_clock64() - t0 > kWaitTicks) {
+            if (wall_clock64() - t0 > D.wait) {
+                // (the range words are tagged with the call's epoch, so nothing
+                // needs draining: the row is reported unusable)
                 if (lane == 0) cst(D.err, 1u);
                 ok = false;
                 break;
@@ -2758,7 +2794,7 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
         }
     }
     after_complete();
-    if (!ok) {  // the wait ran out (not expected): the row is reported unusable
+    if (!ok) {  // the wait ran out: the row is reported unusable
         if (lane == 0) {
             D.out_tokens[row] = -1;
             if (D.out_q) D.out_q[row] = NAN;
@@ -2907,7 +2943,7 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
 // Expected acceptance per position (Lemma 1 of [Ch15] 15.1.2: a draft token
 // drawn from q_i is accepted with probability beta_i = sum_x min(p_i(x),
 // q_i(x))), the diagnostic behind the acceptance-rate rule for the draft
-// length ([Ch15] 15.1.2, dynamic strategy adjustment). Given each row's
+// length ([Ch15] 15.1.4, dynamic strategy adjustment). Given each row's
 // (max m, S = sum exp((l - m)/T)) from the statistics pass, p_j = 2^(fl(x_j*c)
 // - mc) * sp with mc = fl(m*c) and sp = 2^(mc - m*c)/S (likewise q). One
 // launch: wavefront ranges of kDraftCw chunks of both rows of a pair sum
@@ -2929,6 +2965,7 @@ struct OverlapParams {
     double* out_beta;   // [B * gamma]
     int64_t first_block;   // blocks before this one compute the row statistics
     uint32_t* rows_done;   // [pairs] finished rows of the pair (two), kSyncStride words apart
+    uint64_t wait;         // bound on a wait, in wall-clock ticks
 };
 
 template <int DT, bool VEC>
@@ -2937,19 +2974,14 @@ __device__ inline void overlap_finish(const OverlapParams& O, int64_t pair, int 
     const uint32_t want = static_cast<uint32_t>(O.nw);
     int ok = 1;
     if (lane == 0) {
-        if (cld(cnt) < want) {
-            const uint64_t t0 = wall_clock64();
-            for (;;) {
-                __builtin_amdgcn_s_sleep(kSleep);
-                if (cld(cnt) >= want) break;
-                if (wall_clock64() - t0 > kWaitTicks) {
-                    cst(O.err, 1u);
-                    ok = 0;
-                    break;
-                }
-            }
+        auto all_in = [&] { return cld(cnt) >= want; };
+        bool drained = true;
+        if (!spin_until(all_in, O.wait)) {  // the pair is reported NaN; drain before resetting
+            cst(O.err, 1u);
+            ok = 0;
+            drained = spin_until(all_in, kWaitTicks);
         }
-        if (ok) {  // every range of the pair has counted in, so none waits on rows_done any more
+        if (drained) {  // every range of the pair has counted in, each after its rows were finished
             cst(cnt, 0u);
             cst(O.rows_done + pair * kSyncStride, 0u);
         }
@@ -2995,17 +3027,13 @@ __global__ __launch_bounds__(kBlock) void k_overlap(Params P, OverlapParams O) {
     int ready = 1;
     if (lane == 0) {
         const uint32_t* rd = O.rows_done + pair * kSyncStride;
-        if (cld(rd) < 2u) {
-            const uint64_t t0 = wall_clock64();
-            for (;;) {
-                __builtin_amdgcn_s_sleep(kSleep);
-                if (cld(rd) >= 2u) break;
-                if (wall_clock64() - t0 > kWaitTicks) {
-                    cst(O.err, 1u);
-                    ready = 0;
-                    break;
-                }
-            }
+        auto both = [&] { return cld(rd) >= 2u; };
+        if (!spin_until(both, O.wait)) {
+            // the pair is reported NaN; the rows are still awaited (drained), so
+            // that the pair's finisher resets their count only after both came
+            cst(O.err, 1u);
+            ready = 0;
+            (void)spin_until(both, kWaitTicks);
         }
     }
     ready = __shfl(ready, 0, kWave);
@@ -3074,6 +3102,7 @@ struct TreeParams {
     int64_t first_block;
     uint32_t* done;
     uint32_t* err;         // sticky: a wait ran out
+    uint64_t wait;         // bound on the walk's wait, in wall-clock ticks
 };
 
 // Trees of at most kTreeHold * 64 nodes are loaded whole at the start (lane
@@ -3125,24 +3154,19 @@ __device__ inline void walk_tree(const TreeParams& Q, int64_t b, int lane) {
             gld[t] = ok ? load_one<DT>(row_at<DT>(Q.dft, rp), ht[t]) : 0.0f;
         }
     }
-    bool lost = false;  // FUSED: the wait for the tree's rows ran out (not expected)
+    bool lost = false;  // FUSED: the wait for the tree's rows ran out
     if constexpr (FUSED) {
         uint32_t* cnt = Q.done + b * kSyncStride;
         const uint32_t want = 2u * static_cast<uint32_t>(N);
-        if (cld(cnt) != want) {
-            const uint64_t t0 = wall_clock64();
-            for (;;) {
-                __builtin_amdgcn_s_sleep(kSleep);
-                if (cld(cnt) == want) break;
-                if (wall_clock64() - t0 > kWaitTicks) {
-                    if (lane == 0) cst(Q.err, 1u);
-                    lost = true;
-                    break;
-                }
-            }
+        auto all_in = [&] { return cld(cnt) == want; };
+        bool drained = true;
+        if (!spin_until(all_in, Q.wait)) {  // the tree is reported invalid; drain before resetting
+            if (lane == 0) cst(Q.err, 1u);
+            lost = true;
+            drained = spin_until(all_in, kWaitTicks);
         }
         after_complete();
-        if (!lost && lane == 0) cst(cnt, 0u);  // every row of the tree has counted in
+        if (drained && lane == 0) cst(cnt, 0u);  // every row of the tree has counted in
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int32_t j = t * kWave + lane;
@@ -3367,6 +3391,12 @@ struct Workspace {
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> buffers
 std::map<int, int> g_cus;                         // device -> compute units
+std::atomic<int64_t> g_wait_limit{-1};            // host-set bound on a wait (ticks); < 0: kWaitTicks
+
+uint64_t wait_ticks() {
+    const int64_t v = g_wait_limit.load(std::memory_order_relaxed);
+    return v < 0 ? kWaitTicks : static_cast<uint64_t>(v);
+}
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -3488,7 +3518,7 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     o = align_up(o + static_cast<size_t>(G) * p.nsub * sizeof(double), 256);
     L.bytes = o;
     L.cnt_words = 2 * G * kSyncStride;
-    L.dec_words = 0;
+    L.dec_words = G;  // per group the word that marks its outputs void (a closing block's wait ran out)
     return L;
 }
 
@@ -3518,6 +3548,11 @@ int compute_units(int dev) {
 size_t sync_bytes(int64_t cnt_words, int64_t dec_words, int64_t tag_words = 0) {
     return align_up(static_cast<size_t>(cnt_words) * sizeof(uint32_t), 256) +
            static_cast<size_t>(dec_words) * sizeof(uint64_t) + 256 + static_cast<size_t>(tag_words) * sizeof(uint64_t);
+}
+uint32_t* err_word(const Workspace& ws) {
+    return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws.sync) +
+                                       align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256) +
+                                       static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t));
 }
 uint64_t* tag_region(const Workspace& ws) {
     return reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws.sync) +
@@ -3600,8 +3635,9 @@ void bind_workspace(Layout& L, const Workspace& ws) {
     const size_t off_dec = align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256);
     p.dec = reinterpret_cast<uint64_t*>(s + off_dec);
     p.rec = p.dec + static_cast<int64_t>(p.B) * (p.gamma + 1);
-    p.err = reinterpret_cast<uint32_t*>(s + off_dec + static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t));
+    p.err = err_word(ws);
     p.epoch = ws.epoch;
+    p.wait = wait_ticks();
 }
 
 // Timing events, when given, are bound to the kernel dispatch itself (its
@@ -3681,9 +3717,8 @@ void bind_draft(DraftLayout& L, const Workspace& ws) {
     DraftParams& d = L.d;
     d.part = tag_region(ws);
     d.epoch = ws.epoch;
-    const size_t off_dec = align_up(static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), 256);
-    d.err = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws.sync) + off_dec +
-                                        static_cast<size_t>(ws.dec_cap) * sizeof(uint64_t));
+    d.err = err_word(ws);
+    d.wait = wait_ticks();
 }
 
 template <int DT, bool VEC>
@@ -3719,7 +3754,36 @@ void launch_overlap_t(const Params& P, const OverlapParams& O, int64_t blocks, h
 // ==========================================================================
 extern "C" {
 
-int32_t spec_verify_abi_version(void) { return 5; }
+int32_t spec_verify_abi_version(void) { return 6; }
+
+int64_t spec_verify_set_wait_limit(int64_t ticks) {
+    return g_wait_limit.exchange(ticks < 0 ? -1 : ticks);
+}
+
+int spec_verify_status(void* stream, int32_t* timed_out) {
+    if (!timed_out) return fail(SPEC_EINVAL, "null pointer argument");
+    *timed_out = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_ws.find(std::make_pair(dev, stream));
+    if (it == g_ws.end() || !it->second.sync) return SPEC_OK;  // nothing ran on this stream
+    Workspace& ws = it->second;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, err_word(ws), sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return fail(SPEC_EHIP, "reading the workspace's error word failed");
+    if (word == 0) return SPEC_OK;
+    *timed_out = 1;
+    // clear the word, and scrub the counters (a wait whose drain also ran out
+    // may have left one behind)
+    if (hipMemsetAsync(err_word(ws), 0, sizeof(uint32_t), st) != hipSuccess ||
+        hipMemsetAsync(ws.sync, 0, static_cast<size_t>(ws.cnt_cap) * sizeof(uint32_t), st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return fail(SPEC_EHIP, "clearing the workspace's error word failed");
+    return SPEC_OK;
+}
 
 const char* spec_verify_last_error(void) { return g_last_error.c_str(); }
 
@@ -3993,6 +4057,7 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     O.out_beta = out_beta;
     O.first_block = Ls.blocks;
     O.rows_done = Ls.p.tree_done;
+    O.wait = Ls.p.wait;
     if (dtype == SPEC_F32) {
         if (vec) launch_overlap_t<SPEC_F32, true>(Ls.p, O, blocks, st, nullptr, nullptr);
         else launch_overlap_t<SPEC_F32, false>(Ls.p, O, blocks, st, nullptr, nullptr);
@@ -4077,6 +4142,7 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
             Q.first_block = L.blocks;
             Q.done = L.p.tree_done;
             Q.err = L.p.err;
+            Q.wait = L.p.wait;
             const dim3 g2(static_cast<unsigned>(L.blocks + tree_blocks));
             if (dtype == SPEC_F32) {
                 if (vec) hipLaunchKernelGGL((k_tree<SPEC_F32, true>), g2, block, 0, st, L.p, Q);

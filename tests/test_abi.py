@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = sv.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_verify_abi_version() == 5
+    assert lib.spec_verify_abi_version() == 6
 
 
 def _call(B=2, gamma=3, V=10, dtype=0, T=1.0, tgt=1, dft=1, tok=1, out_t=1, out_n=1):
@@ -120,3 +120,16 @@ def test_tree_verify_argument_checks():
         args[i] = bad
         assert lib.spec_tree_verify(*args) == code, (i, bad)
         assert sv.last_error() != ""
+
+
+def test_wait_limit_setting_round_trips():
+    """The host-set bound on in-kernel waits (a test knob for the failure
+    path): negative means the default, the previous value is returned."""
+    assert sv.set_wait_limit(0) == -1
+    assert sv.set_wait_limit(12345) == 0
+    assert sv.set_wait_limit(-7) == 12345
+    assert sv.set_wait_limit(-1) == -1
+
+
+def test_status_rejects_a_null_flag_pointer():
+    assert sv.load_library().spec_verify_status(None, None) == sv.SPEC_EINVAL

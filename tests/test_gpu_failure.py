@@ -1,0 +1,156 @@
+"""Failure detection on the GPU ([Ch15] 15.1.4, failure-mode detection and
+recovery): every in-kernel wait is bounded; a wait that runs out is reported
+to the host through spec_verify_status and as invalid (-1 / NaN) outputs, and
+leaves the workspace clean for the next call.
+
+The host sets the bound to 0 ticks (spec_verify_set_wait_limit), so every wait
+that is not satisfied at its first poll gives up; the kernels still exit
+normally (each such wait then drains with the default bound). Each test
+checks:
+  - the status call reports the timeout, and reads clear afterwards;
+  - every sequence / row / pair / tree is either exactly the oracle's result
+    or reported invalid (never a wrong token, count or value);
+  - the next call on the same stream, with the default bound, matches the
+    oracle and raises no flag.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.compare import compare_draft, compare_tokens, compare_tree
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import gpu_helpers as G
+    import speculative_sampling_verification_05_amd as sv
+
+
+class bound_zero:
+    """Every wait of the calls inside gives up unless satisfied at once."""
+
+    def __enter__(self):
+        torch.cuda.synchronize()
+        assert not sv.status(), "a flag was left over from an earlier test"
+        self.prev = sv.set_wait_limit(0)
+
+    def __exit__(self, *exc):
+        torch.cuda.synchronize()
+        sv.set_wait_limit(self.prev)
+
+
+def check_verify_rows(inp, gpu, seed):
+    """Rows reported invalid are -1 throughout; every other row is the
+    oracle's (the usual near-boundary rule). Returns the invalid count."""
+    wl = inp.wl
+    orc = oracle.verify(inp.target, inp.draft if wl.T > 0 else None, inp.tokens, wl.dtype, wl.T, seed)
+    tok, n = gpu.tokens.copy(), gpu.n.copy()
+    bad = np.flatnonzero(n == -1)
+    for b in bad:
+        assert (tok[b] == -1).all(), (b, tok[b])
+        tok[b], n[b] = orc.tokens[b], orc.n[b]
+    rep = compare_tokens(inp, orc, tok, n, seed)
+    assert not rep.hard_fail, rep.hard_fail[:5]
+    assert rep.mismatches <= 1, str(rep)
+    return len(bad)
+
+
+VERIFY_CASES = {
+    # name: (inputs, schedule)
+    "group_sampling": (lambda: W.make_inputs(W.WORKLOADS["zipf_b8_g5_v32000_f32"], 3), 1),
+    "early_stop_sampling": (lambda: W.make_inputs(W.WORKLOADS["zipf_b8_g5_v32000_f32"], 3), 2),
+    "group_greedy": (lambda: W.make_inputs(W.WORKLOADS["greedy_b32_g8_v128256_f32"].scaled(V=20000), 4), 1),
+    "early_stop_greedy": (lambda: W.make_inputs(W.WORKLOADS["greedy_b32_g8_v128256_f32"].scaled(V=20000), 4), 2),
+}
+
+
+@pytest.mark.parametrize("case", list(VERIFY_CASES))
+def test_verification_wait_timeouts(case):
+    make, schedule = VERIFY_CASES[case]
+    inp = make()
+    seed = 17
+    with bound_zero():
+        gpu = G.run(inp, seed, schedule=schedule, debug=False)
+    flag = sv.status()
+    bad = check_verify_rows(inp, gpu, seed)
+    print(f"{case}: flag={flag} invalid sequences={bad} of {inp.wl.B}")
+    if case.startswith("group") or case == "early_stop_sampling":
+        # the closing blocks sit at the end of a grid that is resident at
+        # once, so they poll before the statistics are in: certain to give up
+        assert flag
+    if case.startswith("group"):
+        assert bad > 0      # a group whose closing wait ran out is reported whole as -1
+    if bad:
+        assert flag
+    assert not sv.status()  # read clears it
+    for _ in range(2):      # the workspace is clean: the next calls are exact
+        again = G.run(inp, seed, schedule=schedule, debug=False)
+        assert check_verify_rows(inp, again, seed) == 0
+        assert not sv.status()
+
+
+def test_draft_sampler_wait_timeouts():
+    inp = W.small_random_inputs(6, 6, 30000, W.BF16, 1.0, seed=12)
+    x = G.to_device(inp.draft, W.BF16)
+    with bound_zero():
+        tok, q = sv.draft_sample(x, 1.0, 9)
+    flag = sv.status()
+    tok, q = tok.cpu().numpy(), q.cpu().numpy()
+    orc = oracle.draft_sample(inp.draft, W.BF16, 1.0, seed=9)
+    bad = tok == -1
+    assert np.isnan(q[bad]).all()
+    assert flag and bad.any()
+    t2, q2 = tok.copy(), q.copy()
+    t2[bad], q2[bad] = orc.tokens[bad], orc.q[bad]
+    rep = compare_draft(inp.draft, W.BF16, 1.0, orc, t2, q2, 9)
+    assert rep.ok(), str(rep)
+    assert not sv.status()
+    tok, q = sv.draft_sample(x, 1.0, 9)
+    torch.cuda.synchronize()
+    rep = compare_draft(inp.draft, W.BF16, 1.0, orc, tok.cpu().numpy(), q.cpu().numpy(), 9)
+    assert rep.ok(), str(rep)
+    assert not sv.status()
+
+
+def test_expected_accept_wait_timeouts():
+    inp = W.small_random_inputs(16, 6, 2048, W.BF16, 0.8, seed=21)
+    t, d = G.to_device(inp.target, W.BF16), G.to_device(inp.draft, W.BF16)
+    want = oracle.expected_accept(inp.target, inp.draft, W.BF16, 0.8)
+    with bound_zero():
+        got = sv.expected_accept(t, d, 0.8).cpu().numpy()
+    flag = sv.status()
+    bad = np.isnan(got)
+    assert flag and bad.any()
+    np.testing.assert_allclose(got[~bad], want[~bad], rtol=1e-5, atol=1e-6)
+    assert not sv.status()
+    for _ in range(2):
+        got = sv.expected_accept(t, d, 0.8).cpu().numpy()
+        np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
+        assert not sv.status()
+
+
+def test_tree_wait_timeouts():
+    tr = W.tree_inputs(6, 3, 3, 5000, W.BF16, 0.8, seed=5)
+    dev = "cuda:0"
+    args = (G.to_device(tr.target, W.BF16), G.to_device(tr.draft, W.BF16), torch.from_numpy(tr.parent).to(dev),
+            torch.from_numpy(tr.token).to(dev))
+    orc = oracle.tree_verify(tr.target, tr.draft, tr.parent, tr.token, W.BF16, 0.8, 0.3)
+    with bound_zero():
+        _, nodes, n = sv.tree_verify(*args, 0.8, 0.3)
+    flag = sv.status()
+    nodes, n = nodes.cpu().numpy(), n.cpu().numpy()
+    bad = n == -1
+    assert flag and bad.any()
+    n2, nodes2 = n.copy(), nodes.copy()
+    n2[bad], nodes2[bad] = orc[2][bad], orc[1][bad]
+    near, hard = compare_tree(tr.target, tr.draft, tr.parent, tr.token, W.BF16, 0.8, 0.3, orc, nodes2, n2)
+    assert not hard, hard[:5]
+    assert not sv.status()
+    _, nodes, n = sv.tree_verify(*args, 0.8, 0.3)
+    torch.cuda.synchronize()
+    near, hard = compare_tree(tr.target, tr.draft, tr.parent, tr.token, W.BF16, 0.8, 0.3, orc, nodes.cpu().numpy(),
+                              n.cpu().numpy())
+    assert not hard and len(near) <= 1
+    assert not sv.status()
