@@ -163,6 +163,29 @@ typedef enum {
     SPEC_SCHEDULE_POSITION = 3
 } spec_schedule_t;
 
+/* spec_verify_noalloc: spec_verify for callers that cannot allocate device
+ * memory - code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, same results (the outputs do not depend
+ * on the schedule). It calls no hipMalloc, hipFree or allocating library
+ * routine: its kernel's scratch (partial slots, residual masses, counters,
+ * the error word) is a fixed device array of the library, about 8.6 MiB per
+ * GPU it runs on, held until the process ends; its address is looked up once
+ * per device, and that first call also clears the array's counter words on
+ * `stream` with a small kernel. Always the group-major order
+ * (SPEC_SCHEDULE_GROUP), whose counters are reset by their last user, so the
+ * array needs no clearing between calls.
+ * Limits: B <= 1024, and the call's partial slots and residual masses within
+ * 8 MiB (B = 1024, gamma = 8, V = 152064 in bf16 fits); larger problems get
+ * SPEC_EINVAL before anything is launched. Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (different streams, or
+ * threads) race and must be serialised by the caller. The sticky error word
+ * of spec_verify_status is the array's own (read with any stream of the
+ * device that has no workspace of its own). */
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, int32_t B, int32_t gamma, int32_t V,
+                        int32_t dtype, float temperature, uint64_t seed,
+                        int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
+
 /* spec_verify with extras (NULL extras == spec_verify, SPEC_SCHEDULE_AUTO).
  * SPEC_EINVAL for a schedule outside spec_schedule_t. */
 int spec_verify_ex(const void* target_logits, const void* draft_logits,

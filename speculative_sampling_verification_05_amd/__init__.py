@@ -22,6 +22,7 @@ MAX_GAMMA = 63
 EXPORTS = (
     "spec_verify",
     "spec_verify_ex",
+    "spec_verify_noalloc",
     "spec_row_stats",
     "spec_draft_sample",
     "spec_draft_sample_ex",
@@ -83,6 +84,8 @@ def load_library(path: str = LIB_PATH):
     L.spec_verify_ex.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, u64, vp, vp, vp,
                                  ctypes.POINTER(Extras)]
     L.spec_verify_ex.restype = ctypes.c_int
+    L.spec_verify_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, u64, vp, vp, vp]
+    L.spec_verify_noalloc.restype = ctypes.c_int
     L.spec_row_stats.argtypes = [vp, i64, i32, i32, f32, vp, vp, vp]
     L.spec_row_stats.restype = ctypes.c_int
     L.spec_draft_sample.argtypes = [vp, i32, i32, i32, i32, f32, u64, i64, i64, vp, vp, vp]
@@ -179,6 +182,30 @@ def verify(target_logits, draft_logits, draft_tokens, temperature: float, seed: 
         _check(L.spec_verify(*args))
     else:
         _check(L.spec_verify_ex(*args, ctypes.byref(extras)))
+    return out_tokens, out_n_accepted
+
+
+def verify_noalloc(target_logits, draft_logits, draft_tokens, temperature: float, seed: int,
+                   out_tokens, out_n_accepted, stream=None):
+    """spec_verify_noalloc: the verification step with no device allocation,
+    in the library or here. The caller passes every tensor, outputs included
+    (out_tokens [B, gamma+1], out_n_accepted [B], int32, contiguous, on the
+    GPU); shapes as verify()."""
+    import torch
+    L = load_library()
+    B, g1, V = target_logits.shape
+    for t in (target_logits, draft_logits, draft_tokens, out_tokens, out_n_accepted):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous GPU tensors")
+    if tuple(out_tokens.shape) != (B, g1) or tuple(out_n_accepted.shape) != (B,) or \
+            out_tokens.dtype != torch.int32 or out_n_accepted.dtype != torch.int32:
+        raise ValueError("out_tokens must be int32 [B, gamma+1] and out_n_accepted int32 [B]")
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, g1 - 1):
+        raise ValueError("draft_tokens must be int32 [B, gamma]")
+    _check(L.spec_verify_noalloc(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), B, g1 - 1, V,
+                                 _dtype_code(target_logits), float(temperature),
+                                 int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out_tokens), _ptr(out_n_accepted),
+                                 _stream_handle(stream)))
     return out_tokens, out_n_accepted
 
 

@@ -2371,6 +2371,7 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     if (lane == 0) {
         if (cld(cnt_s) == static_cast<uint32_t>(P.sb)) cst(cnt_s, 0u);
         cst(cnt_r, 0u);
+        if (dead) cst64(void_word(P, g), 0ull);  // (a mark never outlives its call)
     }
     if (dead) {  // a closing block's wait ran out: the whole row is reported invalid
         if (lane <= gamma) cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, -1);
@@ -3618,6 +3619,66 @@ int get_workspace(int dev, hipStream_t stream, const Layout& L, Workspace** out)
     return SPEC_OK;
 }
 
+// --------------------------------------------------------------------------
+// The scratch of spec_verify_noalloc: a fixed device array (one copy per GPU
+// the library runs on, held until the process ends) that stands in for the
+// allocated workspace: partial slots and residual masses first, then the
+// counters, the group void words and the error word. Host code never passes
+// the array's name to a kernel (on the host it is a stand-in, not a device
+// address): the address comes from hipGetSymbolAddress, once per device.
+// --------------------------------------------------------------------------
+constexpr size_t kScratchData = size_t(8) << 20;        // partial slots and residual masses
+constexpr int64_t kScratchCntWords = int64_t(128) << 10;  // counters (two per group, kSyncStride words apart)
+constexpr int64_t kScratchDecWords = int64_t(16) << 10;   // group void words (64-bit)
+constexpr size_t kScratchSync = size_t(kScratchCntWords) * sizeof(uint32_t) +
+                                size_t(kScratchDecWords) * sizeof(uint64_t) + 256;
+constexpr size_t kScratchBytes = kScratchData + kScratchSync;
+
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+namespace {
+
+std::map<int, unsigned char*> g_scratch;  // device -> device address of `scratch` (under g_mu)
+
+__global__ void k_zero_words(uint32_t* p, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = 0u;
+}
+
+// Caller holds g_mu. The device address of this device's scratch; the first
+// call on a device looks it up and clears its counter, void and error words
+// on `stream` (with a kernel, so that a capturing caller records no memset).
+int scratch_workspace(int dev, hipStream_t stream, Workspace* out) {
+    auto it = g_scratch.find(dev);
+    unsigned char* base = nullptr;
+    if (it != g_scratch.end()) {
+        base = it->second;
+    } else {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(SPEC_EHIP, "hipGetSymbolAddress of the scratch array failed");
+        }
+        base = static_cast<unsigned char*>(ptr);
+        const int64_t words = static_cast<int64_t>(kScratchSync / sizeof(uint32_t));
+        hipLaunchKernelGGL(k_zero_words, dim3(256), dim3(256), 0, stream,
+                           reinterpret_cast<uint32_t*>(base + kScratchData), words);
+        if (hipGetLastError() != hipSuccess) return fail(SPEC_EHIP, "clearing the scratch array failed");
+        g_scratch[dev] = base;
+    }
+    Workspace ws;
+    ws.data = base;
+    ws.bytes = kScratchData;
+    ws.sync = reinterpret_cast<uint32_t*>(base + kScratchData);
+    ws.cnt_cap = kScratchCntWords;
+    ws.dec_cap = kScratchDecWords;
+    ws.tag_cap = 0;
+    ws.epoch = 1;  // the group-major order's words are reset by their last user, not told apart by epoch
+    *out = ws;
+    return SPEC_OK;
+}
+
 void bind_workspace(Layout& L, const Workspace& ws) {
     char* base = static_cast<char*>(ws.data);
     Params& p = L.p;
@@ -3767,9 +3828,15 @@ int spec_verify_status(void* stream, int32_t* timed_out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
+    Workspace ws;
     auto it = g_ws.find(std::make_pair(dev, stream));
-    if (it == g_ws.end() || !it->second.sync) return SPEC_OK;  // nothing ran on this stream
-    Workspace& ws = it->second;
+    if (it != g_ws.end() && it->second.sync) {
+        ws = it->second;
+    } else if (g_scratch.count(dev)) {  // spec_verify_noalloc's scratch on this device
+        if (int rc = scratch_workspace(dev, st, &ws)) return rc;
+    } else {
+        return SPEC_OK;  // nothing ran on this stream
+    }
     uint32_t word = 0;
     if (hipMemcpyAsync(&word, err_word(ws), sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
@@ -3910,6 +3977,52 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
                 int32_t* out_tokens, int32_t* out_n_accepted, void* stream) {
     return spec_verify_ex(target_logits, draft_logits, draft_tokens, B, gamma, V, dtype, temperature, seed,
                           out_tokens, out_n_accepted, stream, nullptr);
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature, uint64_t seed,
+                        int32_t* out_tokens, int32_t* out_n_accepted, void* stream) {
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EDTYPE, "dtype must be SPEC_F32 or SPEC_BF16");
+    if (B < 1) return fail(SPEC_EINVAL, "B must be >= 1");
+    if (gamma < 1 || gamma > SPEC_MAX_GAMMA) return fail(SPEC_EINVAL, "gamma must be in [1, 63]");
+    if (V < 1) return fail(SPEC_EINVAL, "V must be >= 1");
+    if (!(temperature >= 0.0f)) return fail(SPEC_EINVAL, "temperature must be >= 0 and not NaN");
+    const bool greedy = temperature == 0.0f;
+    if (!target_logits || !draft_tokens || !out_tokens || !out_n_accepted)
+        return fail(SPEC_EINVAL, "null pointer argument");
+    if (!greedy && !draft_logits) return fail(SPEC_EINVAL, "draft_logits may be NULL only at temperature 0");
+    const float c32 = greedy ? 0.0f : fold_temperature(temperature);
+    if (!greedy && !(std::isfinite(c32) && c32 > 0.0f))
+        return fail(SPEC_EINVAL, "temperature too small or too large for fp32 exponent scaling");
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
+                     (greedy || aligned16(draft_logits));
+    const int mode = greedy ? kGreedy : kSample;
+    if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_mu);
+    // always the group-major order: its counters are reset by their last user
+    // and nothing on its normal path is told apart by the call's epoch
+    Layout L = plan_group(B, gamma, V, dtype, vec, compute_units(dev), mode);
+    if (L.bytes > kScratchData || L.cnt_words > kScratchCntWords || L.dec_words > kScratchDecWords)
+        return fail(SPEC_EINVAL, "problem exceeds the no-alloc scratch (at most 1024 sequences and 8 MiB of "
+                                 "partial slots and residual masses)");
+    Workspace ws;
+    if (int rc = scratch_workspace(dev, st, &ws)) return rc;
+    bind_workspace(L, ws);
+    Params& p = L.p;
+    p.c32 = c32;
+    p.seed = seed;
+    p.b_offset = 0;
+    p.tgt = target_logits;
+    p.dft = greedy ? nullptr : draft_logits;
+    p.tokens = draft_tokens;
+    p.out_tokens = out_tokens;
+    p.out_n = out_n_accepted;
+    p.skip = 0;
+    launch(dtype, vec, mode, L, st);
+    return check_launch("verification kernel");
 }
 
 int spec_row_stats(const void* logits, int64_t rows, int32_t V, int32_t dtype, float temperature,
