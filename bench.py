@@ -14,8 +14,10 @@ bandwidth against the 8 TB/s peak on that schedule's algorithmic bytes (every
 row, (2*gamma+1)*B*V*sizeof, for the group-major and position-major orders;
 for the early stop the rows it needs: target and draft rows up to each
 sequence's stopping position, plus the bonus row after gamma acceptances);
-the same figures for each schedule forced in turn; and the fp64 CPU oracle
-timed on the host cores on a bounded sample of the same workload.
+the same figures for each schedule forced in turn; a plain streaming read of
+the same number of bytes (the practical HBM read ceiling); and the fp64 CPU
+oracle timed on the host cores, at all cores and at one thread, on bounded
+samples of the same workload.
 """
 from __future__ import annotations
 
@@ -88,33 +90,100 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def cpu_baseline(inp, seed, sample_b, gpu_tokens=None, gpu_n=None, min_reps=3, min_wall_s=10.0, max_reps=1000):
+def cpu_model():
+    """The host CPU's model name and logical CPU count (from /proc/cpuinfo)."""
+    try:
+        names = [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")]
+    except OSError:
+        names = []
+    return {"model": names[0] if names else "unknown", "logical_cpus": len(names) or os.cpu_count()}
+
+
+def cpu_baseline(inp, seed, sample_b, gpu_tokens=None, gpu_n=None, min_reps=3, min_wall_s=6.0, max_reps=1000,
+                 threads=None):
     """The fp64 oracle, as it stands, on the first `sample_b` sequences of the
-    workload (same seed, same b indices), timed on the host cores: repeated
-    until at least `min_wall_s` of wall time (and `min_reps` runs), median."""
+    workload (same seed, same b indices), timed on the host cores (all of
+    them, or `threads`): repeated until at least `min_wall_s` of wall time
+    (and `min_reps` runs), median."""
     import oracle
     from oracle.compare import compare_tokens
     wl = inp.wl.scaled(B=sample_b)
     sub = W.Inputs(wl, inp.seed, inp.target[:sample_b], inp.draft[:sample_b], inp.tokens[:sample_b])
     oracle.lib()
+    all_threads = oracle.max_threads()
+    if threads is not None:
+        oracle.set_threads(threads)
     times = []
     res = None
-    t_start = time.perf_counter()
-    while len(times) < max_reps and (len(times) < min_reps or time.perf_counter() - t_start < min_wall_s):
-        t0 = time.perf_counter()
-        res = oracle.verify(sub.target, sub.draft if wl.T > 0 else None, sub.tokens, wl.dtype, wl.T, seed,
-                            diag=True)
-        times.append(time.perf_counter() - t0)
+    try:
+        used = oracle.max_threads()
+        t_start = time.perf_counter()
+        while len(times) < max_reps and (len(times) < min_reps or time.perf_counter() - t_start < min_wall_s):
+            t0 = time.perf_counter()
+            res = oracle.verify(sub.target, sub.draft if wl.T > 0 else None, sub.tokens, wl.dtype, wl.T, seed,
+                                diag=True)
+            times.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_threads(all_threads)
     t = float(np.median(times))
-    out = {"value": sample_b * wl.gamma / t, "unit": "verified draft rows/s", "cores": oracle.max_threads(),
+    out = {"value": sample_b * wl.gamma / t, "unit": "verified draft rows/s", "cores": used,
            "kind": "oracle",
            "sample": f"first {sample_b} of {inp.wl.B} sequences of the timed workload, median of {len(times)} runs "
-                     f"({t:.2f} s per run, fp64, OpenMP over sequences)"}
+                     f"({t:.3f} s per run, fp64, " +
+                     ("one thread" if used == 1 else f"OpenMP over sequences, {used} threads") + ")"}
     if gpu_tokens is not None:
         rep = compare_tokens(sub, res, gpu_tokens[:sample_b], gpu_n[:sample_b], seed)
         out["parity_vs_gpu"] = {"hard_failures": len(rep.hard_fail), "near_boundary": rep.mismatches,
                                 "draws": rep.draws}
     return out
+
+
+class StreamRead:
+    """The plain streaming-read kernel (libstreamread.so, measurement only)."""
+
+    def __init__(self):
+        path = os.path.join(ROOT, "speculative_sampling_verification_05_amd", "libstreamread.so")
+        self.lib = ctypes.CDLL(path)
+        vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+        self.lib.stream_read.argtypes = [vp, i64, i32, u32, vp, vp, vp, vp]
+        self.lib.stream_read.restype = ctypes.c_int
+        self.lib.stream_read_waves.argtypes = [i64, i32]
+        self.lib.stream_read_waves.restype = i64
+
+
+def read_ceiling(hip, nbytes, args, stream, cpws=(8, 16, 24, 32, 64)):
+    """A plain read of `nbytes` per launch (the verification's compulsory
+    bytes) with 16-byte non-temporal loads, two buffers alternating so that
+    every launch reads what the previous one did not touch; every launch
+    carries HIP events bound to its dispatch. Returns GB/s per chunks-per-
+    wavefront setting and the best."""
+    import torch
+    sr = StreamRead()
+    dev = torch.device("cuda:0")
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_() for _ in range(2)]
+    sink = torch.empty(int(sr.lib.stream_read_waves(nbytes, 8)), dtype=torch.int32, device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+    K = max(10, min(args.steps, 100))
+    for cpw in cpws:
+        for s_ in range(3):
+            sr.lib.stream_read(bufs[s_ % 2].data_ptr(), nbytes, cpw, 0x9E3779B9, sink.data_ptr(), sh, None, None)
+        ev = hip.create(2 * K)
+        torch.cuda.synchronize()
+        for k in range(K):
+            rc = sr.lib.stream_read(bufs[k % 2].data_ptr(), nbytes, cpw, 0x9E3779B9, sink.data_ptr(), sh,
+                                    ctypes.c_void_p(ev[2 * k]), ctypes.c_void_p(ev[2 * k + 1]))
+            if rc != 0:
+                raise RuntimeError(f"stream_read returned {rc}")
+        torch.cuda.synchronize()
+        us = float(np.mean([hip.ms(ev[2 * k], ev[2 * k + 1]) for k in range(K)])) * 1e3
+        hip.destroy(ev)
+        out[f"cpw{cpw}"] = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
+    best = max(out.values(), key=lambda v: v["GBps"])
+    del bufs
+    return {"bytes": nbytes, "launches_timed_each": K, "per_chunks_per_wave": out, "best_us": best["us"],
+            "best_GBps": best["GBps"], "best_frac": best["GBps"] / PEAK_HBM_GBPS,
+            "kernel": "stream_read (16-byte non-temporal loads, contiguous 1 KiB chunks per wavefront)"}
 
 
 def draft_leg(sv, hip, sets, host0, wl, args, stream):
@@ -125,7 +194,8 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
     import oracle
     from oracle.compare import compare_draft
     B, g, V = wl.B, wl.gamma, wl.V
-    K, Wm, E = args.steps, args.warmup, max(1, args.event_stride)
+    K, Wm = args.steps, args.warmup
+    E = args.event_stride if args.event_stride > 0 else max(1, K // 20)
     esz = 4 if wl.dtype == W.F32 else 2
     out = {}
     one = [s[1][:, 0].contiguous() for s in sets]
@@ -291,8 +361,13 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE, choices=list(W.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
-    ap.add_argument("--event-stride", type=int, default=16,
-                    help="time the kernels of every N-th step of the timed region with HIP events")
+    ap.add_argument("--event-stride", type=int, default=0,
+                    help="time the kernels of every N-th step of the timed region with HIP events "
+                         "(0: steps // 20, so that about 20 launches are timed)")
+    ap.add_argument("--vocab", type=int, default=0,
+                    help="run the workload at this vocabulary size instead (e.g. 50257: rows whose byte "
+                         "length is not a multiple of 16 take the per-element load path)")
+    ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--auto-only", action="store_true",
                     help="time the automatic schedule only (no per-schedule legs; for counter runs)")
@@ -312,6 +387,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.workload]
+    if args.vocab:
+        wl = wl.scaled(V=args.vocab, name=f"{wl.name.rsplit('_v', 1)[0]}_v{args.vocab}_{wl.name.rsplit('_', 1)[1]}")
     if args.copy_calibration:
         nbytes = wl.compulsory_bytes()
         src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
@@ -397,7 +474,7 @@ def main():
             return e
         return make
 
-    E = max(1, args.event_stride)
+    E = args.event_stride if args.event_stride > 0 else max(1, K // 20)
     ms_per_step, k_ms, evd = timed(with_schedule(sv.SCHEDULE_AUTO))
 
     # the same steps with no events at all (reported beside the timed value)
@@ -425,6 +502,9 @@ def main():
         torch.cuda.synchronize()
         set_bytes.append(needed_bytes(outs[k][1].cpu().numpy()))
     compulsory = wl.compulsory_bytes()
+    # the metric's formula, (2 gamma + 1) B V s; at T == 0 the draft rows are
+    # never read, so the compulsory bytes are the target rows alone
+    formula_bytes = (2 * g + 1) * B * V * wl.elem_bytes
 
     def algo_bytes(sched, steps):
         """Algorithmic bytes of each listed step: the early stop needs the rows
@@ -479,17 +559,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the arithmetic type: fp32 exponentials, fp64 sums and comparisons
+        # (the logits' storage type is config.logits)
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "gamma": g, "V": V, "temperature": wl.T,
                    "logits": W.DTYPE_NAMES[wl.dtype], "input_sets": args.sets},
-        "kernel_us": {"k_verify": k_avg_ms * 1e3},
+        "kernel_us": {kname: k_avg_ms * 1e3},
         "ms_per_step_no_events": ms_plain,
         "event_stride": E,
         "schedule": names[auto],
         "accepted_hist": n_hist,
         "needed_bytes_per_set": set_bytes,
         "compulsory_bytes": compulsory,
+        "metric_formula_bytes": formula_bytes,
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(kname, wl.name),
@@ -503,9 +586,17 @@ def main():
         result["expected_accept"] = overlap
     if tree is not None:
         result["tree_verify"] = tree
+    if not args.no_read_ceiling:
+        rc_ = read_ceiling(hip, compulsory, args, stream)
+        rc_["verification_kernel_vs_ceiling"] = (float(np.mean(k_bytes)) / (k_avg_ms * 1e-3) / 1e9) / rc_["best_GBps"]
+        result["read_ceiling"] = rc_
+        print(f"[bench] read ceiling {rc_['best_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or min(B, 64)
-        result["cpu_baseline"] = cpu_baseline(host0, args.seed, sample, gpu_t, gpu_n)
+        cb = cpu_baseline(host0, args.seed, sample, gpu_t, gpu_n)
+        cb["one_thread"] = cpu_baseline(host0, args.seed, min(sample, 8), gpu_t, gpu_n, threads=1)
+        cb["host_cpu"] = cpu_model()
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 
