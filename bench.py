@@ -18,6 +18,10 @@ the same figures for each schedule forced in turn; a plain streaming read of
 the same number of bytes (the practical HBM read ceiling); and the fp64 CPU
 oracle timed on the host cores, at all cores and at one thread, on bounded
 samples of the same workload.
+
+Order on the GPU: the read ceiling, the per-schedule and side legs (each
+with its own warm-up), then the headline's W warm-up steps and its K timed
+steps, so that the timed steps run at the GPU's steady clocks.
 """
 from __future__ import annotations
 
@@ -151,6 +155,37 @@ class StreamRead:
         self.lib.stream_read_waves.restype = i64
 
 
+def launch_floor(hip, nbytes, stream, K=50):
+    """The latency floor of a one-launch call that reads `nbytes`: the mean
+    duration of an almost empty launch (one wavefront reading 16 bytes) and of
+    a plain streaming read of `nbytes` (best range length), each timed with
+    HIP events bound to the dispatch."""
+    import torch
+    sr = StreamRead()
+    dev = torch.device("cuda:0")
+    buf = torch.empty(max(nbytes, 16) // 4, dtype=torch.int32, device=dev).random_()
+    sink = torch.empty(int(sr.lib.stream_read_waves(max(nbytes, 16), 8)), dtype=torch.int32, device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def time_it(nb, cpw):
+        for _ in range(5):
+            sr.lib.stream_read(buf.data_ptr(), nb, cpw, 0x9E3779B9, sink.data_ptr(), sh, None, None)
+        ev = hip.create(2 * K)
+        torch.cuda.synchronize()
+        for k in range(K):
+            sr.lib.stream_read(buf.data_ptr(), nb, cpw, 0x9E3779B9, sink.data_ptr(), sh, ctypes.c_void_p(ev[2 * k]),
+                               ctypes.c_void_p(ev[2 * k + 1]))
+        torch.cuda.synchronize()
+        us = float(np.mean([hip.ms(ev[2 * k], ev[2 * k + 1]) for k in range(K)])) * 1e3
+        hip.destroy(ev)
+        return us
+    empty = time_it(16, 8)
+    reads = {cpw: time_it(nbytes, cpw) for cpw in (8, 16, 32)}
+    best = min(reads.values())
+    return {"empty_launch_us": empty, "plain_read_us": best, "plain_read_bytes": nbytes,
+            "plain_read_per_chunks_per_wave_us": {str(k): v for k, v in reads.items()}}
+
+
 def read_ceiling(hip, nbytes, args, stream, cpws=(8, 16, 24, 32, 64)):
     """A plain read of `nbytes` per launch (the verification's compulsory
     bytes) with 16-byte non-temporal loads, two buffers alternating so that
@@ -247,6 +282,13 @@ def draft_leg(sv, hip, sets, host0, wl, args, stream):
                                            "near_boundary": rep.boundary},
                       "cpu_baseline": {"value": rep.rows / t_orc, "unit": "rows/s", "cores": oracle.max_threads(),
                                        "kind": "oracle", "sample": f"the first {nb} sequences' rows, one run"}}
+    # the floor of the one-position call: a plain read of its bytes (which
+    # includes the launch) and an almost empty launch
+    fl = launch_floor(hip, B * V * esz, stream)
+    fl["one_position_vs_plain_read"] = out["one_position"]["kernel_us"] / fl["plain_read_us"]
+    fl["one_position_vs_empty_plus_plain_read"] = out["one_position"]["kernel_us"] / (fl["plain_read_us"] +
+                                                                                     fl["empty_launch_us"])
+    out["one_position"]["floor"] = fl
     out["kernel"] = "k_draft"
     out["roofline_bound"] = "hbm"
     return out
@@ -437,10 +479,12 @@ def main():
 
     hip = HipEvents()
     K, Wm = args.steps, args.warmup
-    for s in range(Wm):
-        call(s)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({Wm} steps)", file=sys.stderr, flush=True)
+    # the plain streaming read of the same byte count first: the practical
+    # ceiling, measured on an idle GPU, which also brings it to its steady
+    # clocks before the verification's warm-up and timed steps
+    rc_ = None if args.no_read_ceiling else read_ceiling(hip, wl.compulsory_bytes(), args, stream)
+    if rc_ is not None:
+        print(f"[bench] read ceiling {rc_['best_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
     def timed(make_extras):
         """K steps of the call (the timed region, bracketed by stream events);
@@ -475,16 +519,6 @@ def main():
         return make
 
     E = args.event_stride if args.event_stride > 0 else max(1, K // 20)
-    ms_per_step, k_ms, evd = timed(with_schedule(sv.SCHEDULE_AUTO))
-
-    # the same steps with no events at all (reported beside the timed value)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for s in range(K):
-        call(Wm + s)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_plain = start.elapsed_time(end) / K
 
     # bytes the early-stopping algorithm needs for each input set (its outputs
     # are the same on every step: same inputs, same seed)
@@ -514,15 +548,8 @@ def main():
             return [set_bytes[(Wm + i) % args.sets] for i in steps]
         return [compulsory for _ in steps]
 
-    auto = sv.auto_schedule(B, g, V, dtc, wl.T)
-    kname = "k_group" if auto == sv.SCHEDULE_GROUP else "k_verify"
     names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position"}
-    k_bytes = algo_bytes(auto, evd)
     rows_per_step = B * g
-    value = rows_per_step / (ms_per_step * 1e-3)
-    k_avg_ms = float(np.mean(k_ms))
-    achieved = float(np.sum(k_bytes)) / (float(np.sum(k_ms)) * 1e-3) / 1e9
-
     schedules = {}
     # (at T == 0 every schedule but GROUP is the position-major order with the early stop)
     legs = () if args.auto_only else ((sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP) if wl.T == 0.0 else
@@ -540,6 +567,32 @@ def main():
     draft = None if args.auto_only or wl.T == 0.0 else draft_leg(sv, hip, sets, host0, wl, args, stream)
     overlap = None if args.auto_only or wl.T == 0.0 else expected_accept_leg(sv, sets, wl, args, stream)
     tree = None if args.auto_only or wl.T == 0.0 else tree_leg(sv, wl, args, stream)
+
+    # the headline: the automatic schedule, W warm-up steps, then exactly K
+    # timed steps (after the legs above, so that the GPU is at its steady clocks)
+    for s in range(Wm):
+        call(s)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({Wm} steps)", file=sys.stderr, flush=True)
+    ms_per_step, k_ms, evd = timed(with_schedule(sv.SCHEDULE_AUTO))
+
+    # the same steps with no events at all (reported beside the timed value)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(K):
+        call(Wm + s)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_plain = start.elapsed_time(end) / K
+
+    auto = sv.auto_schedule(B, g, V, dtc, wl.T)
+    kname = "k_group" if auto == sv.SCHEDULE_GROUP else "k_verify"
+    names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position"}
+    k_bytes = algo_bytes(auto, evd)
+    rows_per_step = B * g
+    value = rows_per_step / (ms_per_step * 1e-3)
+    k_avg_ms = float(np.mean(k_ms))
+    achieved = float(np.sum(k_bytes)) / (float(np.sum(k_ms)) * 1e-3) / 1e9
 
     # one validation of the outputs of set 0 against the oracle (outside the timed region)
     call(0)
@@ -586,11 +639,9 @@ def main():
         result["expected_accept"] = overlap
     if tree is not None:
         result["tree_verify"] = tree
-    if not args.no_read_ceiling:
-        rc_ = read_ceiling(hip, compulsory, args, stream)
+    if rc_ is not None:
         rc_["verification_kernel_vs_ceiling"] = (float(np.mean(k_bytes)) / (k_avg_ms * 1e-3) / 1e9) / rc_["best_GBps"]
         result["read_ceiling"] = rc_
-        print(f"[bench] read ceiling {rc_['best_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or min(B, 64)
         cb = cpu_baseline(host0, args.seed, sample, gpu_t, gpu_n)

@@ -169,10 +169,15 @@ __device__ inline float load_one(const char* row, int64_t j) {
     }
 }
 
-// Logits are read once, straight into registers: 16-byte non-temporal loads.
+// Logits read once go straight into registers: 16-byte non-temporal loads.
+// Rows read twice in close succession (the expected-acceptance launch) use
+// ordinary loads (NT false), so that the second read finds them in the cache.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT = true>
 __device__ inline uint4 load_stream(const char* p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    u32x4 v;
+    if constexpr (NT) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else v = *reinterpret_cast<const u32x4*>(p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -185,9 +190,10 @@ template <int DT, bool VEC> struct Chunk {
     static constexpr int CH = kWave * EPL;
     using Raw = typename std::conditional<VEC, uint4, float4>::type;
 
+    template <bool NT = true>
     __device__ static inline Raw load_full(const char* row, int64_t c, int lane) {
         if constexpr (VEC) {
-            return load_stream(row + (c * CH + lane * EPL) * ElemBytes<DT>::value);
+            return load_stream<NT>(row + (c * CH + lane * EPL) * ElemBytes<DT>::value);
         } else {
             const int64_t j = c * CH + lane;
             return make_float4(load_one<DT>(row, j), load_one<DT>(row, j + kWave),
@@ -198,11 +204,12 @@ template <int DT, bool VEC> struct Chunk {
     // past c_last, and elements at or beyond V, load from a valid address of
     // chunk min(c, c_last); mask() then replaces them by -inf where the group
     // is consumed.
+    template <bool NT = true>
     __device__ static inline Raw load_clamped(const char* row, int64_t c, int64_t c_last, int lane, int32_t V) {
         const int64_t cc = c <= c_last ? c : c_last;
         if constexpr (VEC) {
             const int64_t e = cc * CH + lane * EPL;
-            return load_stream(row + (e < V ? e : cc * CH) * ElemBytes<DT>::value);  // V % EPL == 0 here
+            return load_stream<NT>(row + (e < V ? e : cc * CH) * ElemBytes<DT>::value);  // V % EPL == 0 here
         } else {
             float v[4];
 #pragma unroll
@@ -409,6 +416,8 @@ struct Params {
     int32_t tree_n;       //   nodes per tree (row r < rows_split belongs to tree r / tree_n)
     int32_t tgt_group;    // row statistics: 0, or row r < rows_split is target row
                           //   (r / tgt_group) * (tgt_group + 1) + r % tgt_group (each sequence's bonus row skipped)
+    int32_t pair_rows;    // row statistics: 1 if row r is row r % 2 (0 target, 1 draft) of position pair r / 2
+                          //   (the target row mapped with tgt_group)
     float* part_m;        // [units][2][maxp] per partial slot: max of the piece
     float* part_r;        //   integer reference of the piece (T > 0)
     double* part_s;       //   sum of 2^(x*c - reference) (T > 0)
@@ -445,8 +454,11 @@ struct Role {
     int32_t nb;     // blocks of the unit
 };
 template <int MODE>
-__device__ inline Role role_of(const Params& P) {
-    uint32_t x = blockIdx.x;
+__device__ inline Role role_at(const Params& P, uint32_t x);
+template <int MODE>
+__device__ inline Role role_of(const Params& P) { return role_at<MODE>(P, blockIdx.x); }
+template <int MODE>
+__device__ inline Role role_at(const Params& P, uint32_t x) {
     const uint32_t B = static_cast<uint32_t>(P.B);
     Role o;
     o.kind = kStatsBlock;
@@ -515,8 +527,13 @@ __device__ inline Role role_of(const Params& P) {
 template <int DT, int MODE>
 __device__ inline const char* unit_row(const Params& P, const Role& U, int32_t j) {
     if constexpr (MODE == kRows) {
-        const int64_t r = U.b;
-        if (r >= P.rows_split) return row_at<DT>(P.dft, (r - P.rows_split) * P.V);
+        int64_t r = U.b;
+        if (P.pair_rows) {
+            if (r & 1) return row_at<DT>(P.dft, (r >> 1) * P.V);
+            r >>= 1;
+        } else if (r >= P.rows_split) {
+            return row_at<DT>(P.dft, (r - P.rows_split) * P.V);
+        }
         const int64_t g = P.tgt_group;
         return row_at<DT>(P.tgt, (g > 0 ? (r / g) * (g + 1) + r % g : r) * P.V);
     } else {
@@ -801,7 +818,7 @@ struct BlockPieces {
 // also covers the row's unused slots (a row spans maxp - 1 or maxp
 // wavefronts), which are written with neutral values, so folds read every
 // slot. Returns the number of pieces placed in `out` (lane 0 writes them).
-template <int DT, bool VEC, int MODE, bool GROUP = false>
+template <int DT, bool VEC, int MODE, bool GROUP = false, bool NT = true>
 __device__ inline int stats_wave(const Params& P, const Role& U, uint32_t wl, int lane, Piece* out) {
     int npieces = 0;
     using C = Chunk<DT, VEC>;
@@ -834,12 +851,12 @@ __device__ inline int stats_wave(const Params& P, const Role& U, uint32_t wl, in
         // consumption of the previous group)
         auto load = [&](Raw* q, int64_t gi) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) q[u] = C::load_full(row, c0 + gi * kUnroll + u, lane);
+            for (int u = 0; u < kUnroll; ++u) q[u] = C::template load_full<NT>(row, c0 + gi * kUnroll + u, lane);
             __builtin_amdgcn_sched_barrier(0);
         };
         auto load_last = [&](Raw* q, int64_t gi) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) q[u] = C::load_clamped(row, c0 + gi * kUnroll + u, c_last, lane, P.V);
+            for (int u = 0; u < kUnroll; ++u) q[u] = C::template load_clamped<NT>(row, c0 + gi * kUnroll + u, c_last, lane, P.V);
             __builtin_amdgcn_sched_barrier(0);
         };
         auto eat = [&](const Raw* q, int64_t gi) { consume_group<DT, VEC, kUnroll>(st, q, c0 + gi * kUnroll, lane, c); };
@@ -1029,7 +1046,7 @@ __device__ inline void opaque(float4& r) { asm volatile("" : "+v"(r.x), "+v"(r.y
 // past the row read as -inf without a load. All loads are issued before any
 // is consumed.
 // --------------------------------------------------------------------------
-template <int DT, bool VEC, int N>
+template <int DT, bool VEC, int N, bool NT = true>
 __device__ inline void load_slots(typename Chunk<DT, VEC>::Raw* q, const char* row, int64_t c0, int32_t nchunk,
                                   int32_t V, int lane) {
     using C = Chunk<DT, VEC>;
@@ -1037,8 +1054,8 @@ __device__ inline void load_slots(typename Chunk<DT, VEC>::Raw* q, const char* r
 #pragma unroll
     for (int u = 0; u < N; ++u) {
         const int64_t c = c0 + u;
-        if (c < c_last) q[u] = C::load_full(row, c, lane);
-        else if (c == c_last) q[u] = C::load_clamped(row, c, c_last, lane, V);
+        if (c < c_last) q[u] = C::template load_full<NT>(row, c, lane);
+        else if (c == c_last) q[u] = C::template load_clamped<NT>(row, c, c_last, lane, V);
         else q[u] = C::blank();
     }
 }
@@ -1603,7 +1620,7 @@ __device__ inline void resid_block(const Params& P, const Role& U) {
 // sequence's draw instead. Otherwise each wavefront streams its chunk range,
 // the block's last wavefront writes the block's pieces and counts the block
 // in, and the unit's last block decides.
-template <int DT, bool VEC, int MODE>
+template <int DT, bool VEC, int MODE, bool NT = true>
 __device__ inline void stats_block(const Params& P, const Role& U) {
     __shared__ BlockPieces bp;
     __shared__ int32_t s_stop;
@@ -1650,7 +1667,7 @@ __device__ inline void stats_block(const Params& P, const Role& U) {
     const bool fetch = MODE == kSample && U.rows == 2 && U.r == 0 && w == 0;
     int32_t x = -1;
     if (fetch && lane == 0) x = P.tokens[static_cast<int64_t>(U.b) * P.gamma + U.i];
-    const int n = stats_wave<DT, VEC, MODE>(P, U, U.r * kWavesPerBlock + w, lane, bp.p[w]);
+    const int n = stats_wave<DT, VEC, MODE, false, NT>(P, U, U.r * kWavesPerBlock + w, lane, bp.p[w]);
     if (fetch) {
         if (lane == 0) {
             const bool ok = x >= 0 && x < P.V;
@@ -2951,20 +2968,30 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
 // min(p_j, q_j) (fp32 per load group, fp64 across); a closing wavefront per
 // pair adds the ranges in order.
 // ==========================================================================
+// Overlap blocks trail their pair's statistics blocks by this many pairs in
+// the grid: about two chip-fulls of blocks, so the statistics are done when
+// the overlap blocks start, while the rows read in between (about 66 MB at
+// the headline shape) stay well below the 256 MB memory-side cache. Chosen
+// by timing on the headline shape (lag 64: 122 us; 128: 91; 192: 91; 256:
+// 92; 384: 95; all statistics first: 98, against 103 with non-temporal loads).
+#ifndef SPECVERIFY_OVERLAP_LAG
+#define SPECVERIFY_OVERLAP_LAG 128
+#endif
+constexpr int64_t kOverlapLag = SPECVERIFY_OVERLAP_LAG;
+
 struct OverlapParams {
     const void* tgt;  // [B, gamma + 1, V]
     const void* dft;  // [B, gamma, V]
     int32_t B, gamma, V, nchunk, nw, nbr;
     float c32;
-    const float* m_t;   // [B * (gamma + 1)] row maxima and sums of the target rows
+    const float* m_t;   // row maxima and sums: pair p's target row at [2p], its draft row at [2p + 1]
     const double* s_t;
-    const float* m_d;   // [B * gamma] of the draft rows
-    const double* s_d;
     double* part;       // [pairs, nw]
     uint32_t* cnt;      // [pairs] counters, kDraftStride words apart
     uint32_t* err;
     double* out_beta;   // [B * gamma]
-    int64_t first_block;   // blocks before this one compute the row statistics
+    int64_t sbp;           // row-statistics blocks per pair (its target row's, then its draft row's)
+    int64_t lag;           // pairs between a pair's statistics blocks and its overlap blocks
     uint32_t* rows_done;   // [pairs] finished rows of the pair (two), kSyncStride words apart
     uint64_t wait;         // bound on a wait, in wall-clock ticks
 };
@@ -2995,32 +3022,56 @@ __device__ inline void overlap_finish(const OverlapParams& O, int64_t pair, int 
     if (lane == 0) O.out_beta[pair] = ok ? acc : static_cast<double>(NAN);
 }
 
-// One launch: blocks before O.first_block are the row-statistics blocks over
-// the pairs' target rows, then their draft rows (each row's finisher counts
-// the row in at its pair); then nbr blocks per pair whose wavefronts wait
-// (bounded) until both rows of their pair are finished; then the closing
-// blocks. Every block of a kind starts after all blocks of the kinds before
-// it have been dispatched, so no wait depends on a block that cannot start.
+// One launch. Each pair has sbp row-statistics blocks (its target row's, then
+// its draft row's; each row's finisher counts the row in at the pair) and nbr
+// overlap blocks, whose wavefronts wait (bounded) until both rows of their
+// pair are finished and then read the rows again. The overlap blocks of pair
+// p come lag pairs after its statistics blocks in the grid (statistics of
+// pairs [0, lag); then for each later pair t its statistics followed by the
+// overlap blocks of pair t - lag; then the overlap blocks of the last lag
+// pairs), so the second read follows the first by about lag pairs' rows and
+// finds them in the memory-side cache; the closing blocks come last. A block
+// waits only for blocks before it in the grid, which in-order dispatch has
+// started, so no wait depends on a block that cannot start.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_overlap(Params P, OverlapParams O) {
     using C = Chunk<DT, VEC>;
     using Raw = typename C::Raw;
-    if (static_cast<int64_t>(blockIdx.x) < O.first_block) {
-        stats_block<DT, VEC, kRows>(P, role_of<kRows>(P));
+    const int64_t pairs = static_cast<int64_t>(O.B) * O.gamma;
+    const int64_t SB = O.sbp, R = O.nbr, D = O.lag;
+    int64_t x = static_cast<int64_t>(blockIdx.x);
+    int64_t pair, idx;
+    bool stats = false;
+    const int64_t head = D * SB, mid = (pairs - D) * (SB + R), tail = D * R;
+    if (x < head) {
+        stats = true;
+        pair = x / SB;
+        idx = x - pair * SB;
+    } else if ((x -= head) < mid) {
+        const int64_t t = x / (SB + R), o = x - t * (SB + R);
+        stats = o < SB;
+        pair = stats ? D + t : t;
+        idx = stats ? o : o - SB;
+    } else if ((x -= mid) < tail) {
+        pair = pairs - D + x / R;
+        idx = x - (x / R) * R;
+    } else {
+        x -= tail;
+        pair = -1;
+        idx = x;
+    }
+    if (stats) {
+        stats_block<DT, VEC, kRows, false>(P, role_at<kRows>(P, static_cast<uint32_t>(pair * SB + idx)));
         return;
     }
-    const int64_t x = static_cast<int64_t>(blockIdx.x) - O.first_block;
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
-    const int64_t pairs = static_cast<int64_t>(O.B) * O.gamma;
-    const int64_t sblocks = pairs * O.nbr;
-    if (x >= sblocks) {  // closing blocks: wavefront w finishes one pair
-        const int64_t pair = (x - sblocks) * kWavesPerBlock + w;
-        if (pair < pairs) overlap_finish<DT, VEC>(O, pair, lane);
+    if (pair < 0) {  // closing blocks: wavefront w finishes one pair
+        const int64_t p = idx * kWavesPerBlock + w;
+        if (p < pairs) overlap_finish<DT, VEC>(O, p, lane);
         return;
     }
-    const int64_t pair = x / O.nbr;
-    const int32_t wl = static_cast<int32_t>(x - pair * O.nbr) * kWavesPerBlock + w;
+    const int32_t wl = static_cast<int32_t>(idx) * kWavesPerBlock + w;
     if (wl >= O.nw) return;
     const int64_t b = pair / O.gamma, i = pair - b * O.gamma;
     const int64_t rt = b * (O.gamma + 1) + i;
@@ -3040,16 +3091,16 @@ __global__ __launch_bounds__(kBlock) void k_overlap(Params P, OverlapParams O) {
     ready = __shfl(ready, 0, kWave);
     after_complete();
     const float c = O.c32;
-    const float mp = cld(O.m_t + pair), mq = cld(O.m_d + pair);
-    const double Sp = cld(O.s_t + pair), Sq = cld(O.s_d + pair);
+    const float mp = cld(O.m_t + 2 * pair), mq = cld(O.m_t + 2 * pair + 1);
+    const double Sp = cld(O.s_t + 2 * pair), Sq = cld(O.s_t + 2 * pair + 1);
     const bool ok = ready && isfinite(Sp) && isfinite(Sq) && Sp > 0.0 && Sq > 0.0;
     const float mcp = mp * c, mcq = mq * c;
     const float sp = ok ? static_cast<float>(exp2(static_cast<double>(mcp) - static_cast<double>(mp) * c) / Sp) : 0.0f;
     const float sq = ok ? static_cast<float>(exp2(static_cast<double>(mcq) - static_cast<double>(mq) * c) / Sq) : 0.0f;
     const int64_t c0 = static_cast<int64_t>(wl) * kDraftCw;
     Raw qp[kDraftCw], qq[kDraftCw];
-    load_slots<DT, VEC, kDraftCw>(qp, row_at<DT>(O.tgt, rt * O.V), c0, O.nchunk, O.V, lane);
-    load_slots<DT, VEC, kDraftCw>(qq, row_at<DT>(O.dft, pair * O.V), c0, O.nchunk, O.V, lane);
+    load_slots<DT, VEC, kDraftCw, false>(qp, row_at<DT>(O.tgt, rt * O.V), c0, O.nchunk, O.V, lane);
+    load_slots<DT, VEC, kDraftCw, false>(qq, row_at<DT>(O.dft, pair * O.V), c0, O.nchunk, O.V, lane);
     mask_slots<DT, VEC, kDraftCw>(qp, c0, O.nchunk, O.V, lane);
     mask_slots<DT, VEC, kDraftCw>(qq, c0, O.nchunk, O.V, lane);
     double S = 0.0;
@@ -4116,10 +4167,11 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
     const int cus = compute_units(dev);
-    // the statistics of the pairs' target rows (each sequence's bonus row is
-    // not read), then of their draft rows
+    // the statistics of each pair's target row (each sequence's bonus row is
+    // not read) and draft row, row 2p and 2p + 1
     Ls = plan(kRows, 2 * pairs, 1, V, dtype, vec, cus);
-    const int64_t blocks = Ls.blocks + pairs * nbr + ceil_div(pairs, kWavesPerBlock);
+    const int64_t sbp = 2 * static_cast<int64_t>(Ls.p.nb1);
+    const int64_t blocks = pairs * (sbp + nbr) + ceil_div(pairs, kWavesPerBlock);
     if (blocks * kBlock >= (int64_t(1) << 32)) return fail(SPEC_EINVAL, "problem too large");
     // data: the statistics blocks' slots, then the row statistics and the
     // overlap partials; sync: the statistics blocks' row counters, the pairs'
@@ -4144,12 +4196,13 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     Ls.p.c32 = c32;
     Ls.p.tgt = target_logits;
     Ls.p.dft = draft_logits;
-    Ls.p.rows_split = pairs;
+    Ls.p.rows_split = 2 * pairs;
+    Ls.p.pair_rows = 1;
     Ls.p.tgt_group = gamma;
     Ls.p.rows_max = m_all;
     Ls.p.rows_sumexp = s_all;
     Ls.p.tree_done = ws->sync + o_done;  // each row counts in at its pair
-    Ls.p.tree_n = 1;
+    Ls.p.tree_n = 2;
     OverlapParams O{};
     O.tgt = target_logits;
     O.dft = draft_logits;
@@ -4162,13 +4215,12 @@ int spec_expected_accept(const void* target_logits, const void* draft_logits, in
     O.c32 = c32;
     O.m_t = m_all;
     O.s_t = s_all;
-    O.m_d = m_all + pairs;
-    O.s_d = s_all + pairs;
     O.part = reinterpret_cast<double*>(base + o_pt);
     O.cnt = ws->sync + o_cnt;
     O.err = Ls.p.err;
     O.out_beta = out_beta;
-    O.first_block = Ls.blocks;
+    O.sbp = sbp;
+    O.lag = std::min<int64_t>(pairs, kOverlapLag);
     O.rows_done = Ls.p.tree_done;
     O.wait = Ls.p.wait;
     if (dtype == SPEC_F32) {
