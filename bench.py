@@ -410,6 +410,8 @@ def main():
                     help="run the workload at this vocabulary size instead (e.g. 50257: rows whose byte "
                          "length is not a multiple of 16 take the per-element load path)")
     ap.add_argument("--no-read-ceiling", action="store_true")
+    ap.add_argument("--only", choices=("expected_accept", "draft", "tree"), default=None,
+                    help="run only this side leg on the workload and print its JSON (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--auto-only", action="store_true",
                     help="time the automatic schedule only (no per-schedule legs; for counter runs)")
@@ -479,6 +481,12 @@ def main():
 
     hip = HipEvents()
     K, Wm = args.steps, args.warmup
+    if args.only:
+        leg = {"expected_accept": lambda: expected_accept_leg(sv, sets, wl, args, stream),
+               "draft": lambda: draft_leg(sv, hip, sets, host0, wl, args, stream),
+               "tree": lambda: tree_leg(sv, wl, args, stream)}[args.only]()
+        print(json.dumps({"only": args.only, "workload": wl.name, args.only: leg}), flush=True)
+        return
     # the plain streaming read of the same byte count first: the practical
     # ceiling, measured on an idle GPU, which also brings it to its steady
     # clocks before the verification's warm-up and timed steps
