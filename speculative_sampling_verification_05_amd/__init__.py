@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspecverify.so")
+# SPECVERIFY_LIB names another build of the same library (e.g. one whose host
+# code carries address and undefined-behaviour checks)
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(HERE, "libspecverify.so")
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EHIP, SPEC_ENOMEM = 0, -1, -2, -3, -4
 SPEC_F32, SPEC_BF16 = 0, 1

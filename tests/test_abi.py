@@ -133,3 +133,43 @@ def test_wait_limit_setting_round_trips():
 
 def test_status_rejects_a_null_flag_pointer():
     assert sv.load_library().spec_verify_status(None, None) == sv.SPEC_EINVAL
+
+
+INT32_MAX = (1 << 31) - 1
+
+
+def test_planning_over_the_shape_range():
+    """The schedule and workspace size are defined for every shape the argument
+    checks accept, up to the int32 limits: the host's layout arithmetic stays in
+    range (built with undefined-behaviour checks, an overflow here aborts)."""
+    lib = sv.load_library()
+    for B in (1, 7, 64, 1000, 1 << 20, INT32_MAX):
+        for V in (1, 15, 16, 4096, 50257, 128256, 152064, 1 << 24, INT32_MAX):
+            for g in (1, 8, 63):
+                for dt in (0, 1):
+                    for T in (0.0, 0.8):
+                        s = lib.spec_verify_schedule(B, g, V, dt, T)
+                        assert s in (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP), (B, V, g, dt, T, s)
+                        if T == 0.0:
+                            assert s == sv.SCHEDULE_EARLY_STOP
+                        assert lib.spec_verify_workspace_bytes(B, g, V, dt, T) > 0, (B, V, g, dt, T)
+    assert lib.spec_verify_workspace_bytes(0, 8, 100, 0, 1.0) == 0
+    assert lib.spec_verify_schedule(1, 64, 100, 0, 1.0) == sv.SPEC_EINVAL
+
+
+@pytest.mark.parametrize("B,gamma,V", [(INT32_MAX, 63, INT32_MAX), (1 << 24, 63, 1 << 20), (1 << 20, 8, INT32_MAX)])
+@pytest.mark.parametrize("T", [0.0, 0.8])
+def test_oversized_problems_are_rejected_before_any_hip_call(B, gamma, V, T):
+    """Shapes whose chunk or block counts leave the kernels' 32-bit index range
+    return SPEC_EINVAL from the size check (the pointers are never used)."""
+    P = ctypes.c_void_p
+    lib = sv.load_library()
+    for f in (lib.spec_verify, lib.spec_verify_noalloc):
+        rc = f(P(16), P(16), P(16), B, gamma, V, 1, T, 0, P(16), P(16), None)
+        assert rc == sv.SPEC_EINVAL, (f, rc, sv.last_error())
+        assert "too large" in sv.last_error()
+    for sched in (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION):
+        ex = sv.Extras()
+        ex.schedule = sched
+        rc = lib.spec_verify_ex(P(16), P(16), P(16), B, gamma, V, 1, T, 0, P(16), P(16), None, ctypes.byref(ex))
+        assert rc == sv.SPEC_EINVAL and "too large" in sv.last_error(), (sched, rc, sv.last_error())
