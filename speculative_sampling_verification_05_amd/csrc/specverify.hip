@@ -92,6 +92,9 @@ namespace {
 #ifndef SPECVERIFY_DRAFT_CW
 #define SPECVERIFY_DRAFT_CW 4
 #endif
+#ifndef SPECVERIFY_CACHED_TAIL_MB
+#define SPECVERIFY_CACHED_TAIL_MB 128
+#endif
 #ifndef SPECVERIFY_SYNC_STRIDE
 #define SPECVERIFY_SYNC_STRIDE 64
 #endif
@@ -104,6 +107,10 @@ constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE;  // 1 KiB chunks per 
 constexpr int kGreedyChunksPerWave = 16;                        // (position-major at T == 0)
 constexpr int kGroupChunksPerWave = SPECVERIFY_GROUP_CHUNKS_PER_WAVE;  // (group-major)
 constexpr int kLag = SPECVERIFY_LAG;        // group-major: groups between statistics and residual blocks
+// group-major, T > 0: the last groups, about this many bytes of rows, are
+// streamed with ordinary loads (the rest non-temporal), so that the closing
+// steps, which follow the end of the stream, re-read row k from the caches
+constexpr int64_t kCachedTailBytes = static_cast<int64_t>(SPECVERIFY_CACHED_TAIL_MB) << 20;
 constexpr int kSub = kWave * 16;            // group-major: elements per residual subsegment
 constexpr int kMaxStage = 1024;             // group-major: partial slots of one group staged in LDS
 constexpr int kHold = 8;                    // chunks a draw wavefront holds in registers
@@ -397,6 +404,8 @@ struct Params {
     int32_t lag;     //   groups between a group's statistics blocks and its residual blocks
     int32_t nsub;    //   residual subsegments per row
     int32_t stage;   //   a group's partial slots staged in LDS, or 0 (fold from memory)
+    int32_t cached_from;  // group-major: groups from here on stream with ordinary loads, which keep
+                          //   the rows in the caches for the residual blocks' re-read of row k
     int32_t skip;    // early stop: wavefronts of sequences already stopped load nothing
     uint32_t epoch;  // tag of this call's decision words and draw records (never 0)
     uint64_t wait;   // bound on a wait, in wall-clock ticks (kWaitTicks unless the host set another)
@@ -2455,7 +2464,11 @@ __global__ __launch_bounds__(kBlock) void k_group(Params P) {
         U.rows = P.rps;
         U.nw = P.nw;
         U.nb = P.sb;
-        const int n = stats_wave<DT, VEC, MODE, true>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
+        int n;
+        if (static_cast<int32_t>(g) >= P.cached_from)  // (the last groups: their rows k are read again soon)
+            n = stats_wave<DT, VEC, MODE, true, false>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
+        else
+            n = stats_wave<DT, VEC, MODE, true>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
         // count this wavefront in at the block; the last one writes the block's pieces
         if (lane == 0) bp.n[w] = n;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -3549,6 +3562,11 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
                         : subs_per_wave<SPEC_F32, false>();
     p.rb = greedy ? 1 : static_cast<int32_t>(ceil_div(p.nsub, kWavesPerBlock * spw));
     p.lag = static_cast<int32_t>(G < kLag ? G : kLag);
+    {
+        const int64_t group_bytes = static_cast<int64_t>(p.rps) * V * elem_bytes(dtype);
+        const int64_t tail = greedy ? 0 : std::min<int64_t>(G, kCachedTailBytes / std::max<int64_t>(group_bytes, 1));
+        p.cached_from = static_cast<int32_t>(G - tail);
+    }
     p.cstride = kSyncStride;
     const int64_t gslots = static_cast<int64_t>(p.rps) * p.maxp;
     p.stage = gslots <= kMaxStage ? static_cast<int32_t>(gslots) : 0;
