@@ -602,6 +602,7 @@ def main():
     k_avg_ms = float(np.mean(k_ms))
     achieved = float(np.sum(k_bytes)) / (float(np.sum(k_ms)) * 1e-3) / 1e9
 
+    traffic = measured_traffic(kname, wl.name)
     # one validation of the outputs of set 0 against the oracle (outside the timed region)
     call(0)
     torch.cuda.synchronize()
@@ -634,9 +635,15 @@ def main():
         "needed_bytes_per_set": set_bytes,
         "compulsory_bytes": compulsory,
         "metric_formula_bytes": formula_bytes,
+        # the same step counted in sequences and in logit rows read (other
+        # readings of "verified rows"), and the HBM bytes the counters measured
+        # per launch (re-read of row k included) over the kernel's time
+        "sequences_per_s": B / (ms_per_step * 1e-3),
+        "logit_rows_per_s": ((g + 1) if wl.T == 0.0 else (2 * g + 1)) * B / (ms_per_step * 1e-3),
+        "actual_GBps": (traffic / (k_avg_ms * 1e-3) / 1e9) if traffic else None,
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(kname, wl.name),
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "bytes_per_launch": float(np.mean(k_bytes)), "avg_launch_us": k_avg_ms * 1e3,
                      "launches_timed": len(k_ms)},
         "schedules": schedules,
