@@ -538,11 +538,22 @@ def main():
             rows = np.where((n < 0) | (n >= g), 2 * g + 1, 2 * (n + 1))
         return int(rows.sum()) * row
 
-    set_bytes = []
+    # bytes the group-major order needs at T > 0 with no per-row outputs asked
+    # for: every row but the bonus row, which only the sequences that accept
+    # every draft token read (an invalid sequence is counted as reading it)
+    def group_bytes(n):
+        if wl.T == 0.0:
+            return wl.compulsory_bytes()
+        row = V * (4 if wl.dtype == W.F32 else 2)
+        return int(2 * g * B + np.sum((n < 0) | (n >= g))) * row
+
+    set_bytes, set_group_bytes = [], []
     for k in range(args.sets):
         call(k)
         torch.cuda.synchronize()
-        set_bytes.append(needed_bytes(outs[k][1].cpu().numpy()))
+        n_k = outs[k][1].cpu().numpy()
+        set_bytes.append(needed_bytes(n_k))
+        set_group_bytes.append(group_bytes(n_k))
     compulsory = wl.compulsory_bytes()
     # the metric's formula, (2 gamma + 1) B V s; at T == 0 the draft rows are
     # never read, so the compulsory bytes are the target rows alone
@@ -550,10 +561,14 @@ def main():
 
     def algo_bytes(sched, steps):
         """Algorithmic bytes of each listed step: the early stop needs the rows
-        up to each sequence's stopping position, the other schedules read every
-        row (the compulsory bytes)."""
+        up to each sequence's stopping position; the group-major order every
+        row but the bonus rows of the sequences that stop before it; the
+        position-major order without the early stop every row (the compulsory
+        bytes)."""
         if sched == sv.SCHEDULE_EARLY_STOP:
             return [set_bytes[(Wm + i) % args.sets] for i in steps]
+        if sched == sv.SCHEDULE_GROUP:
+            return [set_group_bytes[(Wm + i) % args.sets] for i in steps]
         return [compulsory for _ in steps]
 
     names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position"}
@@ -633,6 +648,7 @@ def main():
         "schedule": names[auto],
         "accepted_hist": n_hist,
         "needed_bytes_per_set": set_bytes,
+        "group_bytes_per_set": set_group_bytes,
         "compulsory_bytes": compulsory,
         "metric_formula_bytes": formula_bytes,
         # the same step counted in sequences and in logit rows read (other
@@ -641,6 +657,10 @@ def main():
         "sequences_per_s": B / (ms_per_step * 1e-3),
         "logit_rows_per_s": ((g + 1) if wl.T == 0.0 else (2 * g + 1)) * B / (ms_per_step * 1e-3),
         "actual_GBps": (traffic / (k_avg_ms * 1e-3) / 1e9) if traffic else None,
+        # the metric's own reading: its formula bytes over the kernel's time
+        # (above the rate on the bytes read when the schedule skips rows)
+        "metric_formula_GBps": formula_bytes / (k_avg_ms * 1e-3) / 1e9,
+        "metric_formula_frac": formula_bytes / (k_avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,

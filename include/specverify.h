@@ -140,10 +140,13 @@ typedef struct {
  * selects the group-major order and every other value the position-major
  * order with the early stop.
  *  SPEC_SCHEDULE_GROUP       group-major: a sequence's 2*gamma+1 rows (T == 0:
- *                            its gamma+1 target rows) are streamed together,
- *                            every row is read; the sequence's closing blocks
- *                            (at the end of the grid) take the accept step and
- *                            the draw (T == 0: one block, the greedy step).
+ *                            its gamma+1 target rows) are streamed together;
+ *                            the sequence's closing blocks (at the end of the
+ *                            grid) take the accept step and the draw (T == 0:
+ *                            one block, the greedy step). At T > 0 the bonus
+ *                            row (target row gamma) is not streamed: only the
+ *                            closing blocks of a sequence that accepts all
+ *                            gamma draft tokens read it, for the bonus draw.
  *  SPEC_SCHEDULE_EARLY_STOP  position-major: all sequences' position 0, then
  *                            position 1, ...; each position is decided as soon
  *                            as its rows are streamed, and a block whose
@@ -155,7 +158,8 @@ typedef struct {
  *                            chip (B times the blocks of one row pair at least
  *                            four per compute unit), else GROUP.
  * Any of row_max, row_sumexp, p_draft, q_draft or argmax turns EARLY_STOP into
- * POSITION (the per-row values are then defined for every row). */
+ * POSITION, and any of them or Z makes GROUP stream the bonus row with the
+ * others (the per-row values are then defined for every row). */
 typedef enum {
     SPEC_SCHEDULE_AUTO = 0,
     SPEC_SCHEDULE_GROUP = 1,

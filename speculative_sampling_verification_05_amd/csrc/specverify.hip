@@ -406,6 +406,10 @@ struct Params {
     int32_t stage;   //   a group's partial slots staged in LDS, or 0 (fold from memory)
     int32_t cached_from;  // group-major: groups from here on stream with ordinary loads, which keep
                           //   the rows in the caches for the residual blocks' re-read of row k
+    int32_t srows;   // group-major: rows of a group the statistics blocks stream (rps, or rps - 1
+                     //   when the bonus row is deferred)
+    int32_t defer;   // group-major, T > 0: the bonus row is not streamed; the closing blocks of a
+                     //   sequence that accepts all gamma tokens read it (no per-row debug output)
     int32_t skip;    // early stop: wavefronts of sequences already stopped load nothing
     uint32_t epoch;  // tag of this call's decision words and draw records (never 0)
     uint64_t wait;   // bound on a wait, in wall-clock ticks (kWaitTicks unless the host set another)
@@ -437,6 +441,7 @@ struct Params {
     uint64_t* dec;        // [B][gamma+1] decision words: epoch << 32 | status
     uint64_t* rec;        // [B][kRecWords] draw records and their ticket counters
     double* sub_r;        // group-major: [B][nsub] residual mass per subsegment (t units)
+    float* sub_R;         // group-major, deferred bonus row: [B][nsub] each subsegment mass's reference
     uint32_t* cnt_s;      // group-major: [B] statistics blocks counted in, kSyncStride words apart
     uint32_t* cnt_r;      // group-major: [B] residual blocks counted in
     uint32_t* err;        // sticky: a wait ran out
@@ -844,7 +849,10 @@ __device__ inline int stats_wave(const Params& P, const Role& U, uint32_t wl, in
     int32_t k = static_cast<int32_t>(wl - first / cpw);
     while (cc < c_end) {
         const uint32_t ce = first + nchunk < c_end ? first + nchunk : c_end;
-        const char* row = GROUP ? group_row<DT>(P, U.unit, j) : unit_row<DT, MODE>(P, U, static_cast<int32_t>(j));
+        // (group-major with the bonus row deferred: the streamed rows after
+        // target row gamma are the draft rows, one index further on)
+        const uint32_t jr = GROUP && P.defer && j >= static_cast<uint32_t>(P.gamma) ? j + 1 : j;
+        const char* row = GROUP ? group_row<DT>(P, U.unit, jr) : unit_row<DT, MODE>(P, U, static_cast<int32_t>(j));
         const int64_t c0 = cc - first, c1 = ce - first;  // this piece: chunks [c0, c1) of row j
         Lane st;
         st.init();
@@ -905,7 +913,7 @@ __device__ inline int stats_wave(const Params& P, const Role& U, uint32_t wl, in
             }
         }
         Piece pc;
-        pc.slot = (GROUP ? (static_cast<int64_t>(U.unit) * P.rps + j) * P.maxp
+        pc.slot = (GROUP ? (static_cast<int64_t>(U.unit) * P.rps + jr) * P.maxp
                          : slot_base(P, U.unit, static_cast<int32_t>(j))) + k;
         pc.npad = ce == first + nchunk ? P.maxp - 1 - k : 0;
         if constexpr (MODE == kGreedy) {
@@ -1947,7 +1955,9 @@ __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat
             if (emit && P.dbg_argmax) P.dbg_argmax[b * nt + i] = amax;
         } else {
             st = t.s;
-            ut = usable(mt, st);
+            // (a deferred bonus row is not folded here: its usability is
+            // found by the closing blocks that read it)
+            ut = (P.defer && i == gamma) || usable(mt, st);
             if (emit && P.dbg_row_sumexp) P.dbg_row_sumexp[b * R + i] = st;
         }
     }
@@ -1988,7 +1998,10 @@ __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat
     const bool bonus_ok = __shfl(ut ? 1 : 0, gamma, kWave) != 0;
     const bool invalid = f < gamma ? (fstat == kBad) : !bonus_ok;
     const int k = invalid ? -1 : f;
-    if (emit) {
+    // (all gamma accepted with the bonus row deferred: the outputs are written
+    // with the bonus draw, once the row is known to be usable)
+    const bool later = !GREEDY && P.defer && k == gamma;
+    if (emit && !later) {
         if (i <= gamma) {
             int32_t o = -1;
             bool write = true;
@@ -2266,6 +2279,179 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
 }
 
 // --------------------------------------------------------------------------
+// Deferred bonus row (group-major, T > 0, no per-row debug output): the
+// statistics blocks do not stream target row gamma, which only a sequence
+// that accepts all gamma draft tokens needs; that sequence's closing blocks
+// read it instead of a residual row. A subsegment's mass is formed at its own
+// integer reference R_s = ceil(max_s * c) from its maximum: the sum of
+// 2^(fl(x*c - R_s)) (fp32 per element, fp64 in element order per lane, then
+// across the wavefront), stored with R_s. The draw rebases the masses to the
+// largest reference by exact powers of two, so the draw from p (its
+// normalisation cancels) needs neither the row's maximum nor its sum first. A
+// NaN or +inf logit, or one whose x*c overflows, marks its subsegment (mass
+// NaN): the row is then unusable and the sequence reported invalid, as when
+// the bonus row is folded with the others.
+// --------------------------------------------------------------------------
+template <int DT, bool VEC>
+__device__ inline void bonus_masses(const Params& P, uint32_t g, int32_t i0, int32_t stride, int lane) {
+    const float c = P.c32;
+    ResidRow rr{};
+    rr.prow = group_row<DT>(P, g, static_cast<uint32_t>(P.gamma));
+    rr.qrow = nullptr;
+    double* sr = P.sub_r + static_cast<int64_t>(g) * P.nsub;
+    float* sR = P.sub_R + static_cast<int64_t>(g) * P.nsub;
+    for (int32_t i = i0; i < P.nsub; i += stride) {
+        float x[16], none[16];
+        load_sub<DT, VEC>(rr, false, static_cast<int64_t>(i) * kSub + 16 * lane, P.V, x, none);
+        float mx = -INFINITY;
+        bool bad = false;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            bad |= !(x[v] == x[v]) || x[v] == INFINITY;
+            mx = fmaxf(mx, x[v]);
+        }
+        mx = wave_max(mx);
+        bad = __ballot(bad) != 0;
+        float R = kRUnset;
+        if (mx * c > kRUnset + 1.0f) {
+            const float Rn = ceilf(mx * c);
+            if (Rn < 3.0e38f) R = Rn;
+            else bad = true;
+        }
+        double t = 0.0;
+        if (R > kRUnset) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) t += static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x[v], c, -R)));
+        }
+        t = wave_sum(t);
+        if (lane == 0) {
+            cst(sr + i, bad ? static_cast<double>(NAN) : t);
+            cst(sR + i, R);
+        }
+    }
+}
+
+// The deferred bonus draw and the sequence's outputs (the group's last
+// closing wavefront, every closing block counted in): x is lane's draft
+// token (lane < gamma). The masses, rebased to the largest reference, are
+// scanned as in draw(); the chosen subsegment is read again and its elements'
+// masses formed exactly as in bonus_masses, scaled by the same power of two.
+template <int DT, bool VEC>
+__device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int lane) {
+    const int32_t gamma = P.gamma, nsub = P.nsub, nt = gamma + 1;
+    const float c = P.c32;
+    const double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
+    const float* sR = P.sub_R + static_cast<int64_t>(g) * nsub;
+    const double u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(gamma), 1u);
+    float R = kRUnset;
+    bool bad = false;
+    for (int32_t i = lane; i < nsub; i += kWave) {
+        const double m = cld(sr + i);
+        bad |= !(m == m);
+        R = fmaxf(R, cld(sR + i));
+    }
+    R = wave_max(R);
+    bad = __ballot(bad) != 0;
+    auto val = [&](int32_t i) {
+        if (i >= nsub) return 0.0;
+        const float r = cld(sR + i);
+        return r > kRUnset ? ldexp(cld(sr + i), static_cast<int>(fmaxf(r - R, -1100.0f))) : 0.0;
+    };
+    double Z = 0.0, target = 0.0, before = 0.0;
+    int32_t sel = -1;
+    if (!bad) {
+        if (nsub <= kDrawTiles * kWave) {
+            double v[kDrawTiles], incl[kDrawTiles];
+#pragma unroll
+            for (int t = 0; t < kDrawTiles; ++t) v[t] = val(t * kWave + lane);
+            Z = regs_scan(v, incl, lane);
+            if (Z > 0.0) {
+                target = u * Z;
+                sel = regs_find(v, incl, target, lane, before);
+            }
+        } else {  // many subsegments: tiles of 64 in order, the total first, then the crossing
+            for (int32_t t0 = 0; t0 < nsub; t0 += kWave) Z += lane_f64(wave_scan_incl(val(t0 + lane)), kWave - 1);
+            if (Z > 0.0) {
+                target = u * Z;
+                double base = 0.0, last_before = 0.0;
+                int32_t last = -1;
+                for (int32_t t0 = 0; t0 < nsub && sel < 0; t0 += kWave) {
+                    const double v = val(t0 + lane);
+                    const double incl = base + wave_scan_incl(v);
+                    const double prev = lane_before(incl);
+                    const double excl = lane == 0 ? base : prev;
+                    const uint64_t hit = __ballot(v > 0.0 && excl <= target && target < incl);
+                    if (hit) {
+                        const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                        sel = t0 + l;
+                        before = __shfl(excl, l, kWave);
+                    } else {
+                        const uint64_t any = __ballot(v > 0.0);
+                        if (any) {
+                            const int l = 63 - __clzll(static_cast<unsigned long long>(any));
+                            last = t0 + l;
+                            last_before = __shfl(excl, l, kWave);
+                        }
+                    }
+                    base = lane_f64(incl, kWave - 1);
+                }
+                if (sel < 0) {
+                    sel = last;
+                    before = last_before;
+                }
+            }
+        }
+    }
+    const bool ok = !bad && Z > 0.0 && sel >= 0;
+    int32_t pick = -1;
+    if (ok) {
+        const float Rs = cld(sR + sel);
+        const double sc = ldexp(1.0, static_cast<int>(fmaxf(Rs - R, -1100.0f)));
+        ResidRow rr{};
+        rr.prow = group_row<DT>(P, g, static_cast<uint32_t>(gamma));
+        rr.qrow = nullptr;
+        const int64_t j0 = static_cast<int64_t>(sel) * kSub + 16 * lane;
+        float xs[16], none[16];
+        load_sub<DT, VEC>(rr, false, j0, P.V, xs, none);
+        double mv[16];
+        double local = 0.0;
+        int32_t mylast = -1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            mv[v] = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(xs[v], c, -Rs))) * sc;
+            local += mv[v];
+            if (mv[v] > 0.0) mylast = static_cast<int32_t>(j0 + v);
+        }
+        const double incl = before + wave_scan_incl(local);
+        const double prev = lane_before(incl);
+        const double excl = lane == 0 ? before : prev;
+        const uint64_t hit = __ballot(local > 0.0 && excl <= target && target < incl);
+        if (hit) {
+            const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+            int32_t p = -1;
+            if (lane == l) {
+                double run = excl;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    run += mv[v];
+                    if (p < 0 && mv[v] > 0.0 && run > target) p = static_cast<int32_t>(j0 + v);
+                }
+                if (p < 0) p = mylast;
+            }
+            pick = __shfl(p, l, kWave);
+        } else {  // rounding: the last element with mass in the subsegment
+            const uint64_t mass = __ballot(mylast >= 0);
+            const int l = mass ? 63 - __clzll(static_cast<unsigned long long>(mass)) : 0;
+            pick = __shfl(mylast, l, kWave);
+        }
+    }
+    int32_t* out = P.out_tokens + static_cast<int64_t>(g) * nt;
+    if (lane < gamma) cst(out + lane, ok ? x : -1);
+    if (lane == gamma) cst(out + gamma, ok ? pick : -1);
+    if (lane == 0) cst(P.out_n + g, ok ? gamma : -1);
+}
+
+// --------------------------------------------------------------------------
 // Group finishers and the residual block
 // --------------------------------------------------------------------------
 // Waits (one lane) until every statistics block of group g has counted in.
@@ -2331,7 +2517,9 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
         __syncthreads();
         in = shi;
     }
-    if (in.k >= 0) {
+    if (in.k >= 0 && P.defer && in.k == gamma) {
+        bonus_masses<DT, VEC>(P, g, static_cast<int32_t>(idx) * kWavesPerBlock + w, P.rb * kWavesPerBlock, lane);
+    } else if (in.k >= 0) {
         constexpr int NS = subs_per_wave<DT, VEC>();
         const float c32 = P.c32;
         const ResidRow rr = resid_row<DT>(P, in, g);
@@ -2405,6 +2593,8 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
             cst(P.out_n + g, -1);
             if (P.dbg_z) P.dbg_z[g] = NAN;
         }
+    } else if (in.k >= 0 && P.defer && in.k == gamma) {
+        draw_bonus<DT, VEC>(P, g, x, lane);
     } else if (in.k >= 0) {
         draw<DT, VEC>(P, g, in, lane);
     }
@@ -2461,7 +2651,7 @@ __global__ __launch_bounds__(kBlock) void k_group(Params P) {
         U.i = 0;
         U.b = static_cast<int32_t>(g);
         U.r = static_cast<int32_t>(idx);
-        U.rows = P.rps;
+        U.rows = P.srows;
         U.nw = P.nw;
         U.nb = P.sb;
         int n;
@@ -3473,7 +3663,7 @@ struct Layout {
     int64_t units;
     int64_t blocks;
     uint32_t lds;    // dynamic LDS of the group-major kernel
-    size_t off_pm, off_pr, off_ps, off_pi, off_tok, off_msum, off_subr, bytes;
+    size_t off_pm, off_pr, off_ps, off_pi, off_tok, off_msum, off_subr, off_subR, bytes;
     int64_t cnt_words, dec_words;
     int64_t tag_words;  // epoch-tagged 64-bit words of the draft sampler's ranges
 };
@@ -3538,7 +3728,8 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
 // statistics wavefronts take about kChunksPerWave chunks each (at least 16
 // wavefronts per compute unit over the whole problem), and its residual
 // wavefronts take subs_per_wave() subsegments of row k each.
-Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus, int mode = kSample) {
+Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus, int mode = kSample,
+                  bool defer = false) {
     Layout L{};
     Params& p = L.p;
     L.group = true;
@@ -3547,9 +3738,11 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     p.gamma = gamma;
     p.V = V;
     p.rps = greedy ? gamma + 1 : 2 * gamma + 1;
+    p.defer = defer && !greedy ? 1 : 0;
+    p.srows = p.rps - p.defer;
     const int32_t CH = chunk_elems(dtype, vec);
     p.nchunk = static_cast<int32_t>(ceil_div(V, CH));
-    const int64_t per_group = static_cast<int64_t>(p.rps) * p.nchunk;
+    const int64_t per_group = static_cast<int64_t>(p.srows) * p.nchunk;
     const int64_t min_waves = static_cast<int64_t>(cus) * 16;
     int64_t cpw = kGroupChunksPerWave;
     if (ceil_div(G * per_group, cpw) < min_waves) cpw = ceil_div(G * per_group, min_waves);
@@ -3565,7 +3758,7 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     p.rb = greedy ? 1 : static_cast<int32_t>(ceil_div(p.nsub, kWavesPerBlock * spw));
     p.lag = static_cast<int32_t>(G < kLag ? G : kLag);
     {
-        const int64_t group_bytes = static_cast<int64_t>(p.rps) * V * elem_bytes(dtype);
+        const int64_t group_bytes = static_cast<int64_t>(p.srows) * V * elem_bytes(dtype);
         const int64_t tail = greedy ? 0 : std::min<int64_t>(G, kCachedTailBytes / std::max<int64_t>(group_bytes, 1));
         p.cached_from = static_cast<int32_t>(G - tail);
     }
@@ -3588,6 +3781,8 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     L.off_tok = L.off_msum = o;
     L.off_subr = o;
     o = align_up(o + static_cast<size_t>(G) * p.nsub * sizeof(double), 256);
+    L.off_subR = o;
+    o = align_up(o + (p.defer ? static_cast<size_t>(G) * p.nsub * sizeof(float) : 0), 256);
     L.bytes = o;
     L.cnt_words = 2 * G * kSyncStride;
     L.dec_words = G;  // per group the word that marks its outputs void (a closing block's wait ran out)
@@ -3760,6 +3955,7 @@ void bind_workspace(Layout& L, const Workspace& ws) {
     p.tok_l = reinterpret_cast<float*>(base + L.off_tok);
     p.msum = reinterpret_cast<double*>(base + L.off_msum);
     p.sub_r = reinterpret_cast<double*>(base + L.off_subr);
+    p.sub_R = reinterpret_cast<float*>(base + L.off_subR);
     p.cnt_s = ws.sync;
     p.cnt_r = ws.sync + static_cast<int64_t>(p.B) * kSyncStride;
     char* s = reinterpret_cast<char*>(ws.sync);
@@ -3949,7 +4145,9 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t 
     const int cus = compute_units(dev);
     const int mode = temperature == 0.0f ? kGreedy : kSample;
     const Layout Lp = plan(mode, B, gamma, V, dtype, vec, cus);
-    const Layout Lg = plan_group(B, gamma, V, dtype, vec, cus, mode);  // (T == 0: the selectable group-major order)
+    // (T == 0: the selectable group-major order; T > 0: with the bonus row
+    // deferred, whose layout adds the subsegment references)
+    const Layout Lg = plan_group(B, gamma, V, dtype, vec, cus, mode, mode == kSample);
     return std::max(Lp.bytes, Lg.bytes) + sync_bytes(std::max(Lp.cnt_words, Lg.cnt_words), Lp.dec_words);
 }
 
@@ -3992,10 +4190,14 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
         return fail(SPEC_EINVAL, "extras->schedule must be one of the spec_schedule_t values");
     const bool per_row = extras && (extras->row_max || extras->row_sumexp || extras->p_draft || extras->q_draft ||
                                     extras->argmax);
+    // group-major at T > 0: the bonus row is left to the closing blocks of the
+    // sequences that accept every draft token, unless per-row values or Z are
+    // asked for (they are defined for every row and sequence)
+    const bool defer = !greedy && !per_row && !(extras && extras->Z);
     // the size limits do not depend on the device: checked before any HIP call
     if (int rc = check_size(mode, plan(mode, B, gamma, V, dtype, vec, 1))) return rc;
     if (!greedy || sched == SPEC_SCHEDULE_GROUP) {
-        if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode))) return rc;
+        if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode, defer))) return rc;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
@@ -4011,7 +4213,7 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
         // auto: position-major with the early stop once one position's units
         // fill the chip (about four blocks per compute unit), else group-major
         const bool pos = sched == SPEC_SCHEDULE_AUTO ? auto_position_major(B, L, cus) : sched != SPEC_SCHEDULE_GROUP;
-        if (!pos) L = plan_group(B, gamma, V, dtype, vec, cus);
+        if (!pos) L = plan_group(B, gamma, V, dtype, vec, cus, kSample, defer);
         early = sched != SPEC_SCHEDULE_POSITION;
     }
     Workspace* ws = nullptr;
@@ -4068,14 +4270,14 @@ int spec_verify_noalloc(const void* target_logits, const void* draft_logits, con
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0 && aligned16(target_logits) &&
                      (greedy || aligned16(draft_logits));
     const int mode = greedy ? kGreedy : kSample;
-    if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode))) return rc;
+    if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode, !greedy))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "hipGetDevice failed");
     std::lock_guard<std::mutex> lk(g_mu);
     // always the group-major order: its counters are reset by their last user
     // and nothing on its normal path is told apart by the call's epoch
-    Layout L = plan_group(B, gamma, V, dtype, vec, compute_units(dev), mode);
+    Layout L = plan_group(B, gamma, V, dtype, vec, compute_units(dev), mode, !greedy);
     if (L.bytes > kScratchData || L.cnt_words > kScratchCntWords || L.dec_words > kScratchDecWords)
         return fail(SPEC_EINVAL, "problem exceeds the no-alloc scratch (at most 1024 sequences and 8 MiB of "
                                  "partial slots and residual masses)");

@@ -50,8 +50,11 @@ def check_values(inp, orc, gpu):
 #  position   the position-major order reading every row, every debug output;
 #  early      the position-major order with the early stop and no per-row
 #             debug output, so that rows after a sequence's first rejection are
-#             really skipped (the default call's path at T == 0 and at large B).
-LEGS = {"group": (1, True), "position": (3, True), "early": (2, False)}
+#             really skipped (the default call's path at T == 0 and at large B);
+#  plain      the group-major order with no debug output (the default call's
+#             path at small B): at T > 0 the bonus row is then read only by the
+#             closing blocks of sequences that accept every draft token.
+LEGS = {"group": (1, True), "position": (3, True), "early": (2, False), "plain": (1, False)}
 
 
 def parity(inp, seed, b_offset=0, report=None, schedule=0, debug=True):
