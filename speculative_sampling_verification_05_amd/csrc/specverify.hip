@@ -406,6 +406,7 @@ struct Params {
     int32_t stage;   //   a group's partial slots staged in LDS, or 0 (fold from memory)
     int32_t cached_from;  // group-major: groups from here on stream with ordinary loads, which keep
                           //   the rows in the caches for the residual blocks' re-read of row k
+    int32_t spw;     // group-major: residual subsegments per wavefront (1, or subs_per_wave())
     int32_t srows;   // group-major: rows of a group the statistics blocks stream (rps, or rps - 1
                      //   when the bonus row is deferred)
     int32_t defer;   // group-major, T > 0: the bonus row is not streamed; the closing blocks of a
@@ -2541,12 +2542,12 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
                 const int32_t i = i0 + t * stride;
-                if (i < P.nsub) raw[t].load(rr, has_q, static_cast<int64_t>(i) * kSub + 16 * lane, P.V);
+                if (t < P.spw && i < P.nsub) raw[t].load(rr, has_q, static_cast<int64_t>(i) * kSub + 16 * lane, P.V);
             }
 #pragma unroll
             for (int t = 0; t < NS; ++t) {
                 const int32_t i = i0 + t * stride;
-                if (i >= P.nsub) break;
+                if (t >= P.spw || i >= P.nsub) break;
                 double tr = 0.0;
 #pragma unroll
                 for (int u = 0; u < SR::NV; ++u) {
@@ -3753,8 +3754,18 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     p.sb = static_cast<int32_t>(ceil_div(p.nw, kWavesPerBlock));
     p.maxp = static_cast<int32_t>(ceil_div(p.nchunk, cpw) + 1);
     p.nsub = static_cast<int32_t>(ceil_div(V, kSub));
-    const int spw = vec ? (dtype == SPEC_BF16 ? subs_per_wave<SPEC_BF16, true>() : subs_per_wave<SPEC_F32, true>())
-                        : subs_per_wave<SPEC_F32, false>();
+    // residual subsegments per wavefront: one when the closing blocks of all
+    // groups, so spread, come to between two and four per compute unit (the
+    // chip then holds them all, each shorter), else as many as the kernel
+    // holds in flight. Measured on the headline shape, one against two: 33.5
+    // against 36.0 us at 32 groups (1024 closing blocks); 59.0 against 55.0 at
+    // 64 groups (2048), 27.6 against 27.6 at 16 (512), 26.4 against 26.2 at 4,
+    // and 17.4 against 16.9 on the 8-sequence fp32 workload (64).
+    const int spw_max = vec ? (dtype == SPEC_BF16 ? subs_per_wave<SPEC_BF16, true>() : subs_per_wave<SPEC_F32, true>())
+                            : subs_per_wave<SPEC_F32, false>();
+    const int64_t closing1 = G * ceil_div(p.nsub, kWavesPerBlock);  // closing blocks at one subsegment each
+    const int spw = closing1 > 2 * static_cast<int64_t>(cus) && closing1 <= 4 * static_cast<int64_t>(cus) ? 1 : spw_max;
+    p.spw = spw;
     p.rb = greedy ? 1 : static_cast<int32_t>(ceil_div(p.nsub, kWavesPerBlock * spw));
     p.lag = static_cast<int32_t>(G < kLag ? G : kLag);
     {

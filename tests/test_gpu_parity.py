@@ -81,6 +81,9 @@ POOL_SEEDS = {
     "zipf_b64_g8_v128256_bf16": (range(8), None),
     "greedy_b32_g8_v128256_f32": (range(3), 8),
     "zipf_b256_g8_v152064_bf16": (range(12), 64),
+    # the headline recipe at 24 sequences: the group-major closing blocks then
+    # take one residual subsegment per wavefront
+    "zipf_b64_g8_v128256_bf16@24": (range(4), 24),
 }
 
 
@@ -91,7 +94,7 @@ def test_workload_parity_pooled(name):
     grid orders, and the early stop with its row skipping) runs on the same
     inputs."""
     seeds, B = POOL_SEEDS[name]
-    wl = W.WORKLOADS[name]
+    wl = W.WORKLOADS[name.split("@")[0]]
     if B is not None:
         wl = wl.scaled(B=B)
     reps = {leg: TokenReport() for leg in LEGS}
@@ -321,7 +324,7 @@ def test_schedules_give_the_same_outputs(name):
     early stop, which skips the rows of sequences already known to have
     stopped - returns exactly the same tokens and counts (and the oracle's)."""
     seeds, B = POOL_SEEDS[name]
-    wl = W.WORKLOADS[name]
+    wl = W.WORKLOADS[name.split("@")[0]]
     if B is not None:
         wl = wl.scaled(B=B)
     for s in list(seeds)[:3]:
