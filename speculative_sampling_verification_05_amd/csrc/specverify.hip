@@ -1265,6 +1265,26 @@ __device__ inline double accept_prob(double ep, double st, double eq, double sd)
     const double p = exp2(ep) / st, q = exp2(eq) / sd;
     return p == 0.0 ? 0.0 : (q == 0.0 ? 1.0 : fmin(1.0, p / q));
 }
+// The accept test u < alpha with alpha = accept_prob(...): first in fp32, the
+// exponent ep - eq split exactly (fp64) into an integer n and a fraction in
+// [-1/2, 1/2], so that alpha comes within about 5e-7 (relative) of its fp64
+// value; that settles every u farther than 1e-5 (relative) from alpha, with
+// the fp64 test's outcome. The rest, and whatever the fp32 form cannot hold,
+// take the fp64 test.
+__device__ inline bool accept_test(double u, double ep, double st, double eq, double sd) {
+    if (ep > -900.0 && eq > -900.0) {
+        const double a = ep - eq;
+        const double n = rint(a);
+        if (fabs(n) < 100.0) {
+            const float r = ldexpf(__builtin_amdgcn_exp2f(static_cast<float>(a - n)), static_cast<int>(n)) *
+                            (static_cast<float>(sd) / static_cast<float>(st));
+            const double alpha = static_cast<double>(fminf(1.0f, r));
+            if (u < alpha * (1.0 - 1e-5)) return true;
+            if (u > alpha * (1.0 + 1e-5)) return false;
+        }
+    }
+    return u < accept_prob(ep, st, eq, sd);
+}
 
 template <int DT>
 __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
@@ -1300,7 +1320,7 @@ __device__ inline void decide_sample(const Params& P, const Role& U, int lane) {
         } else {
             const double ep = (static_cast<double>(lt) - static_cast<double>(Mt)) * cd;
             const double eq = (static_cast<double>(ld) - static_cast<double>(Md)) * cd;
-            status = u < accept_prob(ep, st, eq, sd) ? kAcc : kRej;
+            status = accept_test(u, ep, st, eq, sd) ? kAcc : kRej;
             if (P.dbg_p || P.dbg_q) {
                 p = exp2(ep) / st;
                 qv = exp2(eq) / sd;
@@ -1907,6 +1927,15 @@ struct SeqInfo {
     double scale_p;  // 2^(mcp - max_p*c) / S_p: probability per t unit
 };
 
+// 2^d for the small exponents below (the rounding error of fl(m*c), |d| at
+// most 2^-24 |m*c|): the series of e^(d ln 2) to the fifth power, whose
+// remainder is below fp64 precision for |d| <= 2^-10; larger d take exp2.
+__device__ inline double exp2_small(double d) {
+    if (!(fabs(d) <= 0x1.0p-10)) return exp2(d);
+    const double x = d * 0.69314718055994530942;
+    return 1.0 + x * (1.0 + x * (0.5 + x * (1.0 / 6.0 + x * (1.0 / 24.0 + x * (1.0 / 120.0)))));
+}
+
 // The residual constants of a row pair from its folded stats (max m, sum S).
 __device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float mq, double sq, float c32) {
     SeqInfo si;
@@ -1914,10 +1943,10 @@ __device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float
     si.k = k;
     si.has_q = has_q ? 1 : 0;
     si.mcp = mp * c32;
-    si.scale_p = exp2(static_cast<double>(si.mcp) - static_cast<double>(mp) * c) / sp;
+    si.scale_p = exp2_small(static_cast<double>(si.mcp) - static_cast<double>(mp) * c) / sp;
     si.mcq = has_q ? mq * c32 : 0.0f;
-    si.rho = has_q ? exp2((static_cast<double>(si.mcq) - static_cast<double>(mq) * c) -
-                          (static_cast<double>(si.mcp) - static_cast<double>(mp) * c)) * (sp / sq)
+    si.rho = has_q ? exp2_small((static_cast<double>(si.mcq) - static_cast<double>(mq) * c) -
+                                (static_cast<double>(si.mcp) - static_cast<double>(mp) * c)) * (sp / sq)
                    : 0.0;
     return si;
 }
@@ -1979,7 +2008,7 @@ __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat
                 const double c = static_cast<double>(P.c32);
                 const double ep = (static_cast<double>(lt) - static_cast<double>(mt)) * c;
                 const double eq = (static_cast<double>(ld) - static_cast<double>(md)) * c;
-                status = u < accept_prob(ep, st, eq, sd) ? kAcc : kRej;
+                status = accept_test(u, ep, st, eq, sd) ? kAcc : kRej;
                 if (emit && (P.dbg_p || P.dbg_q)) {
                     p = exp2(ep) / st;
                     q = exp2(eq) / sd;
