@@ -1731,10 +1731,12 @@ __device__ inline void stats_block(const Params& P, const Role& U) {
 }
 
 // ==========================================================================
-// Group-major schedule (T > 0): a group is one sequence's 2*gamma+1 rows; its
-// residual blocks (at the end of the grid by default) fold the group's
+// Group-major schedule (T > 0): a group is one sequence's 2*gamma+1 rows (the
+// statistics blocks stream 2*gamma of them when the bonus row is deferred);
+// its residual blocks (at the end of the grid by default) fold the group's
 // partials, repeat the accept step for all gamma positions, sum the residual
-// of row k over 1024-element subsegments and draw.
+// of row k (or, deferred, the bonus row's masses) over 1024-element
+// subsegments and draw.
 // ==========================================================================
 // Folding a group's partials (the same exact ldexp combination as above).
 struct RowStat {
@@ -3754,10 +3756,12 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
     return L;
 }
 
-// Group-major layout (T > 0): a group is one sequence's 2*gamma+1 rows, its
-// statistics wavefronts take about kChunksPerWave chunks each (at least 16
-// wavefronts per compute unit over the whole problem), and its residual
-// wavefronts take subs_per_wave() subsegments of row k each.
+// Group-major layout (T > 0): a group is one sequence's 2*gamma+1 rows (with
+// `defer`, the statistics stream 2*gamma of them and the bonus row is left to
+// the closing blocks), its statistics wavefronts take about
+// kGroupChunksPerWave chunks each (at least 16 wavefronts per compute unit over
+// the whole problem), and its residual wavefronts take spw subsegments of row
+// k each.
 Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus, int mode = kSample,
                   bool defer = false) {
     Layout L{};
