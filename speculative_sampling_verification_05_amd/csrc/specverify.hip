@@ -81,7 +81,7 @@ namespace {
 #define SPECVERIFY_GROUP_CHUNKS_PER_WAVE 24
 #endif
 #ifndef SPECVERIFY_LAG
-#define SPECVERIFY_LAG 1024
+#define SPECVERIFY_LAG 56
 #endif
 #ifndef SPECVERIFY_BF16_SUBS
 #define SPECVERIFY_BF16_SUBS 2
@@ -95,6 +95,9 @@ namespace {
 #ifndef SPECVERIFY_CACHED_TAIL_MB
 #define SPECVERIFY_CACHED_TAIL_MB 128
 #endif
+#ifndef SPECVERIFY_NEAR_COUNT
+#define SPECVERIFY_NEAR_COUNT 4
+#endif
 #ifndef SPECVERIFY_SYNC_STRIDE
 #define SPECVERIFY_SYNC_STRIDE 64
 #endif
@@ -106,7 +109,12 @@ constexpr int kUnroll = SPECVERIFY_STATS_UNROLL;           // chunks per pipelin
 constexpr int kChunksPerWave = SPECVERIFY_CHUNKS_PER_WAVE;  // 1 KiB chunks per statistics wavefront (position-major)
 constexpr int kGreedyChunksPerWave = 16;                        // (position-major at T == 0)
 constexpr int kGroupChunksPerWave = SPECVERIFY_GROUP_CHUNKS_PER_WAVE;  // (group-major)
-constexpr int kLag = SPECVERIFY_LAG;        // group-major: groups between statistics and residual blocks
+// group-major: groups between a group's statistics blocks and its residual
+// blocks. Past that many groups the first groups' closing steps start before
+// the stream ends. Measured on the headline recipe against all residual
+// blocks at the end: 53.7 against 54.1 us at 64 sequences, 76.5 against 78.7
+// at 96 (lags 40 and 48: 55.8 and 54.3 at 64, 77.7 and 76.2 at 96).
+constexpr int kLag = SPECVERIFY_LAG;
 // group-major, T > 0: the last groups, about this many bytes of rows, are
 // streamed with ordinary loads (the rest non-temporal), so that the closing
 // steps, which follow the end of the stream, re-read row k from the caches
@@ -379,6 +387,36 @@ __device__ inline bool spin_until(Pred pred, uint64_t ticks) {
         __builtin_amdgcn_s_sleep(kSleep);
         if (pred()) return true;
         if (wall_clock64() - t0 > ticks) return false;
+    }
+}
+// The same wait for *cnt == want (one lane). While more than kNearCount
+// counts are missing it polls one at a time; then with three polls in flight,
+// a poll issued whenever the oldest returns, so that the last count is seen
+// about one round trip after it lands rather than up to two (polling that fast
+// all along would load the memory system while the stream runs).
+__device__ inline bool spin_count(const uint32_t* cnt, uint32_t want, uint64_t ticks) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+        const uint32_t v = cld(cnt);
+        if (v == want) return true;
+        if (v + SPECVERIFY_NEAR_COUNT >= want) break;
+        if (wall_clock64() - t0 > ticks) return false;
+        __builtin_amdgcn_s_sleep(kSleep);
+    }
+    uint32_t a = cld(cnt);
+    __builtin_amdgcn_s_sleep(kSleep);
+    uint32_t b = cld(cnt);
+    __builtin_amdgcn_s_sleep(kSleep);
+    uint32_t c = cld(cnt);
+    for (;;) {
+        if (a == want) return true;
+        a = cld(cnt);
+        if (b == want) return true;
+        b = cld(cnt);
+        if (c == want) return true;
+        c = cld(cnt);
+        if (wall_clock64() - t0 > ticks) return false;
+        __builtin_amdgcn_s_sleep(kSleep);
     }
 }
 // --------------------------------------------------------------------------
@@ -1733,10 +1771,10 @@ __device__ inline void stats_block(const Params& P, const Role& U) {
 // ==========================================================================
 // Group-major schedule (T > 0): a group is one sequence's 2*gamma+1 rows (the
 // statistics blocks stream 2*gamma of them when the bonus row is deferred);
-// its residual blocks (at the end of the grid by default) fold the group's
-// partials, repeat the accept step for all gamma positions, sum the residual
-// of row k (or, deferred, the bonus row's masses) over 1024-element
-// subsegments and draw.
+// its residual blocks (placed kLag groups later in the grid, or at its end)
+// fold the group's partials, repeat the accept step for all gamma positions,
+// sum the residual of row k (or, deferred, the bonus row's masses) over
+// 1024-element subsegments and draw.
 // ==========================================================================
 // Folding a group's partials (the same exact ldexp combination as above).
 struct RowStat {
@@ -1965,7 +2003,7 @@ __device__ inline SeqInfo seq_info(int k, bool has_q, float mp, double sp, float
 // --------------------------------------------------------------------------
 template <bool GREEDY>
 __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat* rs, int32_t x, float lt, float ld,
-                                      double u, bool emit) {
+                                      double u, bool emit, bool info = true) {
     const int32_t gamma = P.gamma, V = P.V;
     const int nt = gamma + 1;
     const int i = static_cast<int>(threadIdx.x & (kWave - 1));
@@ -2022,7 +2060,7 @@ __device__ inline SeqInfo accept_wave(const Params& P, uint32_t g, const RowStat
     }
     SeqInfo mine{};
     if constexpr (!GREEDY) {
-        if (i <= gamma) mine = seq_info(i, i < gamma, mt, st, md, sd, P.c32);
+        if (info && i <= gamma) mine = seq_info(i, i < gamma, mt, st, md, sd, P.c32);
     }
     const uint64_t stop = __ballot(i < gamma && status != kAcc);
     const int f = stop ? __ffsll(static_cast<unsigned long long>(stop)) - 1 : gamma;
@@ -2237,10 +2275,10 @@ __device__ inline void p_masses(const Params& P, uint32_t g, const SeqInfo& in, 
 }
 
 template <int DT, bool VEC>
-__device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int lane) {
+__device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int lane, double ud) {
     const int32_t nsub = P.nsub;
     double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
-    const double u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(in.k), 1u);
+    const double u = __shfl(ud, in.k, kWave);  // lane i holds the draw's uniform for k = i
     double Z, target, before = 0.0;
     int32_t sel;
     bool from_p = false;  // no residual mass left by rounding: draw from p_k
@@ -2369,12 +2407,12 @@ __device__ inline void bonus_masses(const Params& P, uint32_t g, int32_t i0, int
 // scanned as in draw(); the chosen subsegment is read again and its elements'
 // masses formed exactly as in bonus_masses, scaled by the same power of two.
 template <int DT, bool VEC>
-__device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int lane) {
+__device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int lane, double ud) {
     const int32_t gamma = P.gamma, nsub = P.nsub, nt = gamma + 1;
     const float c = P.c32;
     const double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
     const float* sR = P.sub_R + static_cast<int64_t>(g) * nsub;
-    const double u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(gamma), 1u);
+    const double u = __shfl(ud, gamma, kWave);  // lane i holds the draw's uniform for k = i
     float R = kRUnset;
     bool bad = false;
     for (int32_t i = lane; i < nsub; i += kWave) {
@@ -2493,10 +2531,9 @@ __device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int la
 __device__ inline int wait_published(const Params& P, uint32_t g) {
     const uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
     const uint32_t want = static_cast<uint32_t>(P.sb);
-    auto all_in = [&] { return cld(cnt) == want; };
-    if (spin_until(all_in, P.wait)) return 0;
+    if (spin_count(cnt, want, P.wait)) return 0;
     cst(P.err, 1u);
-    return spin_until(all_in, kWaitTicks) ? 1 : 2;
+    return spin_count(cnt, want, kWaitTicks) ? 1 : 2;
 }
 // Group-major: the word that marks group g's outputs void in this call (a wait
 // of one of its closing blocks ran out); the group's last closing block then
@@ -2513,16 +2550,21 @@ template <int DT, bool VEC>
 __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t idx, char* dyn) {
     __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
     __shared__ SeqInfo shi;
+    __shared__ SeqInfo s_info[SPEC_MAX_GAMMA + 1];
     __shared__ int s_st;
     __shared__ uint32_t s_last;
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     const int w = static_cast<int>(threadIdx.x / kWave);
     const int32_t gamma = P.gamma;
-    // the draft tokens, their two logits and the accept uniforms do not
-    // depend on the statistics: they are loaded and drawn before the wait
+    // the draft tokens, their two logits, the accept uniforms and the draw's
+    // uniform for every possible k do not depend on the statistics: they are
+    // loaded and drawn before the wait
     int32_t x = 0;
     float lt = 0.0f, ld = 0.0f;
-    double u = 0.0;  // the accept uniform of position lane
+    double u = 0.0;   // the accept uniform of position lane
+    double ud = 0.0;  // the draw's uniform if k = lane
+    if (w == 0 && lane <= gamma)
+        ud = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(lane), 1u);
     if (w == 0 && lane < gamma) {
         u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(lane), 0u);
         x = P.tokens[static_cast<int64_t>(g) * gamma + lane];
@@ -2542,12 +2584,19 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     in.k = -1;
     if (s_st == 0) {
         merge_group<false, kBlock>(P, g, dyn, rs);
+        // wavefront 0 takes the accept step while wavefront 1 forms the
+        // residual constants of every row pair (the accept step's ballot
+        // picks one)
         if (w == 0) {
-            const SeqInfo si = accept_wave<false>(P, g, rs, x, lt, ld, u, idx == 0);
+            const SeqInfo si = accept_wave<false>(P, g, rs, x, lt, ld, u, idx == 0, false);
             if (lane == 0) shi = si;
+        } else if (w == 1 && lane <= gamma) {
+            s_info[lane] = seq_info(lane, lane < gamma, rs[lane].m, rs[lane].s, lane < gamma ? rs[gamma + 1 + lane].m : 0.0f,
+                                    lane < gamma ? rs[gamma + 1 + lane].s : 0.0, P.c32);
         }
         __syncthreads();
         in = shi;
+        if (in.k >= 0) in = s_info[in.k];
     }
     if (in.k >= 0 && P.defer && in.k == gamma) {
         bonus_masses<DT, VEC>(P, g, static_cast<int32_t>(idx) * kWavesPerBlock + w, P.rb * kWavesPerBlock, lane);
@@ -2626,9 +2675,9 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
             if (P.dbg_z) P.dbg_z[g] = NAN;
         }
     } else if (in.k >= 0 && P.defer && in.k == gamma) {
-        draw_bonus<DT, VEC>(P, g, x, lane);
+        draw_bonus<DT, VEC>(P, g, x, lane, ud);
     } else if (in.k >= 0) {
-        draw<DT, VEC>(P, g, in, lane);
+        draw<DT, VEC>(P, g, in, lane, ud);
     }
 }
 

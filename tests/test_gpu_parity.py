@@ -138,6 +138,8 @@ EDGE_SHAPES = [
     (3, 2, 8192, W.BF16),
     (7, 5, 33000, W.F32),
     (1, 8, 128256, W.BF16),
+    (60, 2, 1003, W.BF16),     # more groups than the group-major lag: residual blocks interleaved
+    (61, 1, 4096, W.F32),      #   with the stream (scalar and vector path)
 ]
 
 
