@@ -2235,23 +2235,31 @@ __device__ inline void load_sub(const ResidRow& rr, bool has_q, int64_t j0, int3
 // load round trip); the totals and prefix sums are formed exactly as above.
 constexpr int kDrawTiles = 4;
 
+// Tiles from nt on (wave-uniform) hold only zeros: their scans are skipped,
+// which leaves every result as it would be.
 template <int NT = kDrawTiles>
-__device__ inline double regs_scan(const double* v, double* incl, int lane) {
+__device__ inline double regs_scan(const double* v, double* incl, int lane, int nt = NT) {
     double base = 0.0;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        incl[t] = base + wave_scan_incl(v[t]);
-        base = lane_f64(incl[t], kWave - 1);
+        if (t < nt) {
+            incl[t] = base + wave_scan_incl(v[t]);
+            base = lane_f64(incl[t], kWave - 1);
+        } else {
+            incl[t] = base;
+        }
     }
     return base;
 }
 
 template <int NT = kDrawTiles>
-__device__ inline int32_t regs_find(const double* v, const double* incl, double t, int lane, double& before) {
+__device__ inline int32_t regs_find(const double* v, const double* incl, double t, int lane, double& before,
+                                    int nt = NT) {
     int32_t last = -1;
     double last_before = 0.0;
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
+        if (k >= nt) break;
         const double prev = lane_before(incl[k]);
         const double base = k == 0 ? 0.0 : lane_f64(incl[k - 1], kWave - 1);
         const double excl = lane == 0 ? base : prev;
@@ -2301,17 +2309,18 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
         double v[kDrawTiles], incl[kDrawTiles];
 #pragma unroll
         for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? cld(sr + t * kWave + lane) : 0.0;
-        Z = regs_scan(v, incl, lane);
+        const int nt = static_cast<int>((nsub + kWave - 1) / kWave);
+        Z = regs_scan(v, incl, lane, nt);
         from_p = !(Z > 0.0);
         if (from_p) {
             p_masses<DT, VEC>(P, g, in, sr, lane);
 #pragma unroll
             for (int t = 0; t < kDrawTiles; ++t) v[t] = t * kWave + lane < nsub ? cld(sr + t * kWave + lane) : 0.0;
-            target = u * regs_scan(v, incl, lane);
+            target = u * regs_scan(v, incl, lane, nt);
         } else {
             target = u * Z;
         }
-        sel = regs_find(v, incl, target, lane, before);
+        sel = regs_find(v, incl, target, lane, before, nt);
     } else {
         Z = scan_total(sr, nsub, lane);
         from_p = !(Z > 0.0);
@@ -2449,10 +2458,11 @@ __device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int la
             double v[kDrawTiles], incl[kDrawTiles];
 #pragma unroll
             for (int t = 0; t < kDrawTiles; ++t) v[t] = val(t * kWave + lane);
-            Z = regs_scan(v, incl, lane);
+            const int nt = static_cast<int>((nsub + kWave - 1) / kWave);
+            Z = regs_scan(v, incl, lane, nt);
             if (Z > 0.0) {
                 target = u * Z;
-                sel = regs_find(v, incl, target, lane, before);
+                sel = regs_find(v, incl, target, lane, before, nt);
             }
         } else {  // many subsegments: tiles of 64 in order, the total first, then the crossing
             for (int32_t t0 = 0; t0 < nsub; t0 += kWave) Z += lane_f64(wave_scan_incl(val(t0 + lane)), kWave - 1);
@@ -3178,10 +3188,11 @@ __device__ inline void draft_finish(const DraftParams& D, int64_t row, int lane)
             }
 #pragma unroll
             for (int t2 = 0; t2 < kFinTiles; ++t2) v[t2] = rebase(v[t2], r[t2], R);
-            S = regs_scan<kFinTiles>(v, incl, lane);
+            const int nt = static_cast<int>((nw + kWave - 1) / kWave);
+            S = regs_scan<kFinTiles>(v, incl, lane, nt);
             if (isfinite(S) && S > 0.0) {  // else NaN, +inf or no finite entry: the row is unusable
                 target = u * S;
-                sel = regs_find<kFinTiles>(v, incl, target, lane, before);
+                sel = regs_find<kFinTiles>(v, incl, target, lane, before, nt);
                 if (sel >= 0) {
 #pragma unroll
                     for (int t2 = 0; t2 < kFinTiles; ++t2)
