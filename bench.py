@@ -10,10 +10,13 @@ that every step reads data the previous step did not touch (each set is
 
 Prints one JSON line: verified draft rows/s (B*gamma per step) with the
 library's automatic schedule; the verification kernel's achieved HBM
-bandwidth against the 8 TB/s peak on that schedule's algorithmic bytes (every
-row, (2*gamma+1)*B*V*sizeof, for the group-major and position-major orders;
-for the early stop the rows it needs: target and draft rows up to each
-sequence's stopping position, plus the bonus row after gamma acceptances);
+bandwidth against the 8 TB/s peak on that schedule's algorithmic bytes (for
+the position-major order every row, (2*gamma+1)*B*V*sizeof; for the
+group-major order every row but the bonus rows of the sequences that stop
+before them; in two phases the first phase's row pairs of every sequence and
+the rest only where all of those were accepted; for the early stop the rows it
+needs: target and draft rows up to each sequence's stopping position, plus the
+bonus row after gamma acceptances);
 the same figures for each schedule forced in turn; a plain streaming read of
 the same number of bytes (the practical HBM read ceiling); and the fp64 CPU
 oracle timed on the host cores, at all cores and at one thread, on bounded
@@ -547,13 +550,29 @@ def main():
         row = V * (4 if wl.dtype == W.F32 else 2)
         return int(2 * g * B + np.sum((n < 0) | (n >= g))) * row
 
-    set_bytes, set_group_bytes = [], []
+    # bytes the group-major order in two phases needs at T > 0: the first p0
+    # row pairs of every sequence, the other pairs only for the sequences that
+    # accept all of those, and the bonus row for those that accept every
+    # token (p0 as the header states it; an invalid sequence is counted as
+    # reading every row)
+    p0 = 0 if g < 2 else max(1, min((3 * g + 4) // 8, g - 1))
+
+    def two_phase_bytes(n):
+        if wl.T == 0.0 or p0 == 0:
+            return group_bytes(n)
+        row = V * (4 if wl.dtype == W.F32 else 2)
+        bad = n < 0
+        rows = 2 * p0 + np.where(bad | (n >= p0), 2 * (g - p0), 0) + np.where(bad | (n >= g), 1, 0)
+        return int(rows.sum()) * row
+
+    set_bytes, set_group_bytes, set_two_bytes = [], [], []
     for k in range(args.sets):
         call(k)
         torch.cuda.synchronize()
         n_k = outs[k][1].cpu().numpy()
         set_bytes.append(needed_bytes(n_k))
         set_group_bytes.append(group_bytes(n_k))
+        set_two_bytes.append(two_phase_bytes(n_k))
     compulsory = wl.compulsory_bytes()
     # the metric's formula, (2 gamma + 1) B V s; at T == 0 the draft rows are
     # never read, so the compulsory bytes are the target rows alone
@@ -569,14 +588,18 @@ def main():
             return [set_bytes[(Wm + i) % args.sets] for i in steps]
         if sched == sv.SCHEDULE_GROUP:
             return [set_group_bytes[(Wm + i) % args.sets] for i in steps]
+        if sched == sv.SCHEDULE_GROUP_TWO_PHASE:
+            return [set_two_bytes[(Wm + i) % args.sets] for i in steps]
         return [compulsory for _ in steps]
 
-    names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position"}
+    names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position",
+             sv.SCHEDULE_GROUP_TWO_PHASE: "two_phase"}
     rows_per_step = B * g
     schedules = {}
     # (at T == 0 every schedule but GROUP is the position-major order with the early stop)
     legs = () if args.auto_only else ((sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP) if wl.T == 0.0 else
-                                      (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION))
+                                      (sv.SCHEDULE_GROUP, sv.SCHEDULE_GROUP_TWO_PHASE, sv.SCHEDULE_EARLY_STOP,
+                                       sv.SCHEDULE_POSITION))
     for sched in legs:
         ms_s, km_s, ev_s = timed(with_schedule(sched))
         a_s = float(np.sum(algo_bytes(sched, ev_s))) / (float(np.sum(km_s)) * 1e-3) / 1e9
@@ -609,8 +632,7 @@ def main():
     ms_plain = start.elapsed_time(end) / K
 
     auto = sv.auto_schedule(B, g, V, dtc, wl.T)
-    kname = "k_group" if auto == sv.SCHEDULE_GROUP else "k_verify"
-    names = {sv.SCHEDULE_GROUP: "group", sv.SCHEDULE_EARLY_STOP: "early_stop", sv.SCHEDULE_POSITION: "position"}
+    kname = "k_group" if auto in (sv.SCHEDULE_GROUP, sv.SCHEDULE_GROUP_TWO_PHASE) else "k_verify"
     k_bytes = algo_bytes(auto, evd)
     rows_per_step = B * g
     value = rows_per_step / (ms_per_step * 1e-3)
@@ -649,6 +671,7 @@ def main():
         "accepted_hist": n_hist,
         "needed_bytes_per_set": set_bytes,
         "group_bytes_per_set": set_group_bytes,
+        "two_phase_bytes_per_set": set_two_bytes,
         "compulsory_bytes": compulsory,
         "metric_formula_bytes": formula_bytes,
         # the same step counted in sequences and in logit rows read (other

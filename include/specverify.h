@@ -136,9 +136,9 @@ typedef struct {
     int32_t schedule;      /* a spec_schedule_t (0 = SPEC_SCHEDULE_AUTO), see below */
 } spec_extras_t;
 
-/* Grid schedules. Outputs do not depend on the schedule. At T == 0 GROUP
- * selects the group-major order and every other value the position-major
- * order with the early stop.
+/* Grid schedules. Outputs do not depend on the schedule. At T == 0 GROUP and
+ * GROUP_TWO_PHASE select the group-major order and every other value the
+ * position-major order with the early stop.
  *  SPEC_SCHEDULE_GROUP       group-major: a sequence's 2*gamma+1 rows (T == 0:
  *                            its gamma+1 target rows) are streamed together;
  *                            the sequence's closing blocks (at the end of the
@@ -154,17 +154,34 @@ typedef struct {
  *                            reads nothing (the early stop of [Ch15] 15.1.2
  *                            step 3) and helps with that sequence's draw.
  *  SPEC_SCHEDULE_POSITION    the same order, reading every row.
+ *  SPEC_SCHEDULE_GROUP_TWO_PHASE
+ *                            group-major in two phases (T > 0, gamma >= 2):
+ *                            every sequence's first p0 row pairs (p0 =
+ *                            max(1, min((3 gamma + 4) / 8, gamma - 1)), in
+ *                            integer division), then a
+ *                            decider per sequence takes the accept step for
+ *                            them; then the other row pairs, read only for
+ *                            the sequences that accepted all of the first
+ *                            (the early stop of [Ch15] 15.1.2 step 3 applied
+ *                            per sequence); then the closing blocks. The
+ *                            closing blocks of a sequence that stopped early
+ *                            take k and row k's constants from its decider.
  *  SPEC_SCHEDULE_AUTO        EARLY_STOP once one position's blocks fill the
- *                            chip (B times the blocks of one row pair at least
- *                            four per compute unit), else GROUP.
+ *                            chip twice over (B times the blocks of one row
+ *                            pair at least eight per compute unit), else
+ *                            GROUP_TWO_PHASE where the rows come to at least
+ *                            200 MiB (2 gamma B V times the element size;
+ *                            gamma >= 2), else GROUP.
  * Any of row_max, row_sumexp, p_draft, q_draft or argmax turns EARLY_STOP into
  * POSITION, and any of them or Z makes GROUP stream the bonus row with the
- * others (the per-row values are then defined for every row). */
+ * others and GROUP_TWO_PHASE run as GROUP (the per-row values are then
+ * defined for every row). */
 typedef enum {
     SPEC_SCHEDULE_AUTO = 0,
     SPEC_SCHEDULE_GROUP = 1,
     SPEC_SCHEDULE_EARLY_STOP = 2,
-    SPEC_SCHEDULE_POSITION = 3
+    SPEC_SCHEDULE_POSITION = 3,
+    SPEC_SCHEDULE_GROUP_TWO_PHASE = 4
 } spec_schedule_t;
 
 /* spec_verify_noalloc: spec_verify for callers that cannot allocate device
@@ -295,7 +312,8 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
                      int32_t* out_n, void* stream);
 
 /* The schedule SPEC_SCHEDULE_AUTO takes for this shape on the current device
- * (SPEC_SCHEDULE_GROUP or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
+ * with no per-row outputs (SPEC_SCHEDULE_GROUP_TWO_PHASE, SPEC_SCHEDULE_GROUP
+ * or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
 int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature);
 
 /* spec_verify_status: whether any bounded wait of a kernel enqueued on

@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(HERE, "libspecverify
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EHIP, SPEC_ENOMEM = 0, -1, -2, -3, -4
 SPEC_F32, SPEC_BF16 = 0, 1
-SCHEDULE_AUTO, SCHEDULE_GROUP, SCHEDULE_EARLY_STOP, SCHEDULE_POSITION = 0, 1, 2, 3
+SCHEDULE_AUTO, SCHEDULE_GROUP, SCHEDULE_EARLY_STOP, SCHEDULE_POSITION, SCHEDULE_GROUP_TWO_PHASE = 0, 1, 2, 3, 4
 MAX_GAMMA = 63
 
 # every symbol include/specverify.h declares

@@ -148,7 +148,7 @@ constexpr int kClaimWord = 16;              // tickets handed out for the draw's
 constexpr int kPieceWord = 24;              // pieces counted in
 
 enum : int { kSample = 0, kGreedy = 1, kRows = 2 };
-enum : int { kStatsBlock = 0, kResidBlock = 1 };
+enum : int { kStatsBlock = 0, kResidBlock = 1, kDecideBlock = 2 };
 // decision word status (low bits; the high 32 bits hold the call's epoch)
 enum : uint32_t { kPending = 0, kAcc = 1, kRej = 2, kBad = 3 };
 // what the decision words of positions < i say about a sequence
@@ -464,6 +464,9 @@ struct Params {
                      //   when the bonus row is deferred)
     int32_t defer;   // group-major, T > 0: the bonus row is not streamed; the closing blocks of a
                      //   sequence that accepts all gamma tokens read it (no per-row debug output)
+    int32_t p0;      // group-major in two phases (0: one phase): the first p0 row pairs of every
+    int32_t pnw2;    //   group, then the group's decider, then the other pairs (their wavefronts
+    int32_t psb2;    //   and blocks per group), read only for sequences not stopped within p0
     int32_t skip;    // early stop: wavefronts of sequences already stopped load nothing
     uint32_t epoch;  // tag of this call's decision words and draw records (never 0)
     uint64_t wait;   // bound on a wait, in wall-clock ticks (kWaitTicks unless the host set another)
@@ -619,9 +622,37 @@ __device__ inline int64_t slot_base(const Params& P, uint32_t unit, int32_t j) {
 // residual blocks of group j - lag; the residual blocks of the last lag groups
 // close the grid. A group's residual blocks thus always follow all of its
 // statistics blocks.
-__device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint32_t& g, uint32_t& idx) {
+// In two phases (p0 > 0) the order is: every group's first-phase statistics
+// blocks, one decider per group, every group's second-phase statistics
+// blocks, every group's residual blocks; each waits only for earlier blocks.
+__device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint32_t& g, uint32_t& idx, int& phase) {
     const uint32_t S = static_cast<uint32_t>(P.sb), R = static_cast<uint32_t>(P.rb);
     const uint32_t D = static_cast<uint32_t>(P.lag), G = static_cast<uint32_t>(P.B);
+    phase = 0;
+    if (P.p0 > 0) {
+        const uint32_t S2 = static_cast<uint32_t>(P.psb2);
+        if (x < G * S) {
+            kind = kStatsBlock;
+            phase = 1;
+            g = x / S;
+            idx = x - g * S;
+        } else if ((x -= G * S) < G) {
+            kind = kDecideBlock;
+            g = x;
+            idx = 0;
+        } else if ((x -= G) < G * S2) {
+            kind = kStatsBlock;
+            phase = 2;
+            g = x / S2;
+            idx = x - g * S2;
+        } else {
+            x -= G * S2;
+            kind = kResidBlock;
+            g = x / R;
+            idx = x - g * R;
+        }
+        return;
+    }
     const uint32_t head = D * S;
     if (x < head) {
         kind = kStatsBlock;
@@ -650,6 +681,18 @@ __device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint
     const uint32_t t = x / R;
     g = (G - D) + t;
     idx = x - t * R;
+}
+
+// The group row (target rows 0..gamma, then draft rows) of stream row j of a
+// group's statistics blocks. One phase: every row, but with the bonus row
+// deferred the rows after target row gamma - 1 are the draft rows. First
+// phase (1): target rows 0..p0-1, then draft rows 0..p0-1; second phase (2):
+// target rows p0..gamma-1, then draft rows p0..gamma-1.
+__device__ inline uint32_t group_stream_row(const Params& P, int phase, uint32_t j) {
+    const uint32_t gamma = static_cast<uint32_t>(P.gamma), nt = gamma + 1u, p0 = static_cast<uint32_t>(P.p0);
+    if (phase == 1) return j < p0 ? j : nt + (j - p0);
+    if (phase == 2) return j < gamma - p0 ? p0 + j : nt + p0 + (j - (gamma - p0));
+    return P.defer && j >= gamma ? j + 1u : j;
 }
 
 // Row j of group g: target rows 0..gamma, then draft rows 0..gamma-1.
@@ -877,6 +920,7 @@ struct BlockPieces {
     Piece p[kWavesPerBlock][kMaxPieces];
     int32_t n[kWavesPerBlock];
     uint32_t done;
+    uint32_t skip;  // (second phase: the sequence stopped within the first)
 };
 
 // Statistics of one wavefront's chunk range [wl*cpw, (wl+1)*cpw) of the unit's
@@ -903,9 +947,7 @@ __device__ inline int stats_wave(const Params& P, const Role& U, uint32_t wl, in
     int32_t k = static_cast<int32_t>(wl - first / cpw);
     while (cc < c_end) {
         const uint32_t ce = first + nchunk < c_end ? first + nchunk : c_end;
-        // (group-major with the bonus row deferred: the streamed rows after
-        // target row gamma are the draft rows, one index further on)
-        const uint32_t jr = GROUP && P.defer && j >= static_cast<uint32_t>(P.gamma) ? j + 1 : j;
+        const uint32_t jr = GROUP ? group_stream_row(P, U.i, j) : j;
         const char* row = GROUP ? group_row<DT>(P, U.unit, jr) : unit_row<DT, MODE>(P, U, static_cast<int32_t>(j));
         const int64_t c0 = cc - first, c1 = ce - first;  // this piece: chunks [c0, c1) of row j
         Lane st;
@@ -2553,17 +2595,156 @@ __device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int la
 // Returns 0 if they did within the bound; 1 if the bound ran out (the sticky
 // error word is then set) but they did within the drain that follows; 2 if
 // not even then.
-__device__ inline int wait_published(const Params& P, uint32_t g) {
-    const uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
-    const uint32_t want = static_cast<uint32_t>(P.sb);
+// (phase 2: the second phase's count, the word after the first's)
+__device__ inline int wait_published(const Params& P, uint32_t g, int phase = 0) {
+    const uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride + (phase == 2 ? 1 : 0);
+    const uint32_t want = static_cast<uint32_t>(phase == 2 ? P.psb2 : P.sb);
     if (spin_count(cnt, want, P.wait)) return 0;
     cst(P.err, 1u);
     return spin_count(cnt, want, kWaitTicks) ? 1 : 2;
+}
+
+// Two phases: group g's decision record, kGroupRecWords 64-bit words after
+// the groups' void words, each carrying this call's epoch in its high half
+// (a reader that sees the epoch in all of them has the whole record): the
+// status (kind << 8 | k), then fl(max*c) of target and draft row k, rho and
+// scale_p (each fp64 as two halves). Written once per call by the group's
+// decider; nothing needs clearing between calls.
+constexpr int kGroupRecWords = 8;
+enum : uint32_t { kRecStop = 1, kRecCont = 2, kRecVoid = 3 };
+__device__ inline uint64_t* group_rec(const Params& P, uint32_t g) {
+    return P.dec + P.B + static_cast<int64_t>(g) * kGroupRecWords;
+}
+struct GroupRec {
+    uint32_t kind;
+    int32_t k;
+    float mcp, mcq;
+    double rho, scale_p;
+};
+// One read of the record (one wavefront): false until every word is current.
+__device__ inline bool read_group_rec(const Params& P, uint32_t g, int lane, GroupRec& r) {
+    const uint64_t* w = group_rec(P, g);
+    const uint64_t v = lane < 7 ? cld64(w + lane) : (static_cast<uint64_t>(P.epoch) << 32);
+    if (__ballot(static_cast<uint32_t>(v >> 32) != P.epoch) != 0) return false;
+    const uint32_t x = static_cast<uint32_t>(v);
+    const uint32_t w0 = __shfl(x, 0, kWave);
+    r.kind = w0 >> 8;
+    r.k = static_cast<int32_t>(w0 & 0xFFu);
+    r.mcp = __uint_as_float(__shfl(x, 1, kWave));
+    r.mcq = __uint_as_float(__shfl(x, 2, kWave));
+    r.rho = __hiloint2double(static_cast<int>(__shfl(x, 4, kWave)), static_cast<int>(__shfl(x, 3, kWave)));
+    r.scale_p = __hiloint2double(static_cast<int>(__shfl(x, 6, kWave)), static_cast<int>(__shfl(x, 5, kWave)));
+    return true;
 }
 // Group-major: the word that marks group g's outputs void in this call (a wait
 // of one of its closing blocks ran out); the group's last closing block then
 // writes the whole row as invalid.
 __device__ inline uint64_t* void_word(const Params& P, uint32_t g) { return P.dec + g; }
+
+// Two phases, T > 0: the decider of group g (one block, after every group's
+// first-phase statistics blocks). Once the first phase's rows have counted
+// in, it folds them and takes the accept step for positions 0..p0-1 exactly
+// as the residual blocks do for all positions. A rejection or an unusable row
+// there ends the sequence: the decider writes its outputs (the draw writes the
+// token at k) and a record with k and row k's residual constants; the second
+// phase's statistics blocks of the group then load nothing, and its residual
+// blocks skip the fold. All p0 accepted: the record says so, and the residual
+// blocks fold the whole group as in one phase. A wait that runs out makes the
+// record void (the outputs -1). The decider resets the first phase's count.
+template <int DT, bool VEC>
+__device__ inline void decide_block(const Params& P, uint32_t g, char* dyn) {
+    __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
+    __shared__ int s_st;
+    const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
+    const int w = static_cast<int>(threadIdx.x / kWave);
+    const int32_t gamma = P.gamma, p0 = P.p0, nt = gamma + 1;
+    int32_t x = 0;
+    float lt = 0.0f, ld = 0.0f;
+    double u = 0.0;
+    if (w == 0 && lane < p0) {
+        u = philox_uniform(P.seed, static_cast<uint32_t>(g + P.b_offset), static_cast<uint32_t>(lane), 0u);
+        x = P.tokens[static_cast<int64_t>(g) * gamma + lane];
+        if (x >= 0 && x < P.V) {
+            lt = load_one<DT>(group_row<DT>(P, g, static_cast<uint32_t>(lane)), x);
+            ld = load_one<DT>(group_row<DT>(P, g, static_cast<uint32_t>(nt + lane)), x);
+        }
+    }
+    uint32_t* cnt = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
+    if (threadIdx.x == 0) {
+        int st = 0;
+        if (!spin_count(cnt, static_cast<uint32_t>(P.sb), P.wait)) {
+            cst(P.err, 1u);
+            st = spin_count(cnt, static_cast<uint32_t>(P.sb), kWaitTicks) ? 1 : 2;
+        }
+        s_st = st;
+    }
+    __syncthreads();
+    after_complete();
+    if (s_st == 0) merge_group<false, kBlock>(P, g, dyn, rs);  // (the second phase's rows are not used)
+    if (w != 0) return;
+    const int i = lane;
+    const int64_t b = g;
+    uint32_t kind = kRecVoid;
+    int32_t k = -1;
+    double rho = 0.0, scale_p = 0.0;
+    float mcp = 0.0f, mcq = 0.0f;
+    if (s_st == 0) {
+        int status = kAcc;
+        float mt = NAN, md = NAN;
+        double st = NAN, sd = NAN;
+        if (i < p0) {
+            mt = rs[i].m;
+            st = rs[i].s;
+            md = rs[nt + i].m;
+            sd = rs[nt + i].s;
+            if (!usable(mt, st) || !usable(md, sd) || !(x >= 0 && x < P.V)) {
+                status = kBad;
+            } else {
+                const double c = static_cast<double>(P.c32);
+                const double ep = (static_cast<double>(lt) - static_cast<double>(mt)) * c;
+                const double eq = (static_cast<double>(ld) - static_cast<double>(md)) * c;
+                status = accept_test(u, ep, st, eq, sd) ? kAcc : kRej;
+            }
+        }
+        const uint64_t stop = __ballot(i < p0 && status != kAcc);
+        if (stop) {
+            const int f = __ffsll(static_cast<unsigned long long>(stop)) - 1;
+            const bool invalid = __shfl(status, f, kWave) == kBad;
+            k = invalid ? -1 : f;
+            kind = invalid ? kRecVoid : kRecStop;
+            if (!invalid) {
+                SeqInfo mine{};
+                if (i == f) mine = seq_info(i, true, mt, st, md, sd, P.c32);
+                mcp = __shfl(mine.mcp, f, kWave);
+                mcq = __shfl(mine.mcq, f, kWave);
+                rho = __shfl(mine.rho, f, kWave);
+                scale_p = __shfl(mine.scale_p, f, kWave);
+            }
+        } else {
+            kind = kRecCont;
+        }
+    }
+    if (kind != kRecCont) {  // the outputs: k, the accepted tokens, -1 after k (the draw writes the token at k)
+        if (i <= gamma && (kind == kRecVoid || i != k))
+            cst(P.out_tokens + b * nt + i, kind == kRecStop && i < k ? x : -1);
+        if (i == 0) cst(P.out_n + b, k);
+    }
+    complete_before();
+    uint64_t* r = group_rec(P, g);
+    const uint64_t rb = __double_as_longlong(rho), sb = __double_as_longlong(scale_p);
+    uint32_t v = 0u;
+    if (i == 0) v = (kind << 8) | static_cast<uint32_t>(k < 0 ? 0 : k);
+    if (i == 1) v = __float_as_uint(mcp);
+    if (i == 2) v = __float_as_uint(mcq);
+    if (i == 3) v = static_cast<uint32_t>(rb);
+    if (i == 4) v = static_cast<uint32_t>(rb >> 32);
+    if (i == 5) v = static_cast<uint32_t>(sb);
+    if (i == 6) v = static_cast<uint32_t>(sb >> 32);
+    if (i < 7) cst64(r + i, tagged(P, v));
+    // every first-phase block has counted in (unless even the drain ran out:
+    // then the count is left for the status call's scrub)
+    if (i == 0 && s_st != 2) cst(cnt, 0u);
+}
 
 // T > 0: one residual block of group g (idx in [0, rb)). Once every
 // statistics block of g has counted in, the block folds g's partials and
@@ -2598,8 +2779,32 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
             ld = load_one<DT>(group_row<DT>(P, g, static_cast<uint32_t>(gamma + 1 + lane)), x);
         }
     }
-    if (threadIdx.x == 0) {
-        const int st = wait_published(P, g);
+    // two phases: the decider's record first. A sequence that stopped within
+    // the first phase takes k and its constants from it; one that did not
+    // waits for the second phase's statistics and folds the group below.
+    __shared__ GroupRec s_rec;
+    bool fold = true;
+    if (P.p0 > 0) {
+        if (w == 0) {
+            GroupRec r;
+            auto got = [&] { return read_group_rec(P, g, lane, r); };
+            if (!spin_until(got, P.wait)) {
+                // flagged and the group voided; the record is still awaited, so
+                // that the decider's outputs precede the void row
+                if (lane == 0) {
+                    cst(P.err, 1u);
+                    cst64(void_word(P, g), tagged(P, 1u));
+                }
+                (void)spin_until(got, kWaitTicks);
+                r.kind = kRecVoid;
+            }
+            if (lane == 0) s_rec = r;
+        }
+        __syncthreads();
+        fold = s_rec.kind == kRecCont;
+    }
+    if (fold && threadIdx.x == 0) {
+        const int st = wait_published(P, g, P.p0 > 0 ? 2 : 0);
         if (st != 0) cst64(void_word(P, g), tagged(P, 1u));  // the wait ran out: the group's outputs are void
         s_st = st;
     }
@@ -2607,7 +2812,16 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     after_complete();
     SeqInfo in;
     in.k = -1;
-    if (s_st == 0) {
+    if (!fold && s_rec.kind == kRecStop) {
+        const GroupRec r = s_rec;
+        in.k = r.k;
+        in.has_q = 1;
+        in.mcp = r.mcp;
+        in.mcq = r.mcq;
+        in.rho = r.rho;
+        in.scale_p = r.scale_p;
+    }
+    if (fold && s_st == 0) {
         merge_group<false, kBlock>(P, g, dyn, rs);
         // wavefront 0 takes the accept step while wavefront 1 forms the
         // residual constants of every row pair (the accept step's ballot
@@ -2704,6 +2918,13 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     } else if (in.k >= 0) {
         draw<DT, VEC>(P, g, in, lane, ud);
     }
+    // two phases: the second phase's count is reset once all its blocks have
+    // counted in (those of a stopped sequence load nothing and come soon);
+    // the first phase's count was reset by the decider
+    if (P.p0 > 0 && lane == 0) {
+        uint32_t* cnt2 = cnt_s + 1;
+        if (spin_count(cnt2, static_cast<uint32_t>(P.psb2), kWaitTicks)) cst(cnt2, 0u);
+    }
 }
 
 // T == 0: the one closing block of group g (the sequence's gamma + 1 target
@@ -2742,26 +2963,36 @@ __global__ __launch_bounds__(kBlock) void k_group(Params P) {
     extern __shared__ __align__(16) char dyn[];
     int kind;
     uint32_t g, idx;
-    decode_block(P, blockIdx.x, kind, g, idx);
+    int phase;
+    decode_block(P, blockIdx.x, kind, g, idx, phase);
     const int lane = static_cast<int>(threadIdx.x & (kWave - 1));
     if (kind == kStatsBlock) {
         __shared__ BlockPieces bp;
         const int w = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
-        const int nwb = min(kWavesPerBlock, P.nw - static_cast<int>(idx) * kWavesPerBlock);  // wavefronts with work
-        if (threadIdx.x == 0) bp.done = 0u;
+        const int pnw = phase == 2 ? P.pnw2 : P.nw;
+        const int nwb = min(kWavesPerBlock, pnw - static_cast<int>(idx) * kWavesPerBlock);  // wavefronts with work
+        if (threadIdx.x == 0) {
+            bp.done = 0u;
+            bp.skip = 0u;
+            if (phase == 2) {  // the sequence stopped within the first phase: nothing to load
+                const uint64_t w0 = cld64(group_rec(P, g));
+                bp.skip = static_cast<uint32_t>(w0 >> 32) == P.epoch && (static_cast<uint32_t>(w0) >> 8) != kRecCont;
+            }
+        }
         __syncthreads();
         if (w >= nwb) return;
         Role U;
         U.kind = kStatsBlock;
         U.unit = g;
-        U.i = 0;
+        U.i = phase;
         U.b = static_cast<int32_t>(g);
         U.r = static_cast<int32_t>(idx);
-        U.rows = P.srows;
-        U.nw = P.nw;
-        U.nb = P.sb;
-        int n;
-        if (static_cast<int32_t>(g) >= P.cached_from)  // (the last groups: their rows k are read again soon)
+        U.rows = phase == 1 ? 2 * P.p0 : (phase == 2 ? 2 * (P.gamma - P.p0) : P.srows);
+        U.nw = pnw;
+        U.nb = phase == 2 ? P.psb2 : P.sb;
+        int n = 0;
+        if (bp.skip) n = 0;
+        else if (static_cast<int32_t>(g) >= P.cached_from)  // (the last groups: their rows k are read again soon)
             n = stats_wave<DT, VEC, MODE, true, false>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
         else
             n = stats_wave<DT, VEC, MODE, true>(P, U, idx * kWavesPerBlock + w, lane, bp.p[w]);
@@ -2774,13 +3005,15 @@ __global__ __launch_bounds__(kBlock) void k_group(Params P) {
         if (old + 1u != static_cast<uint32_t>(nwb)) return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         write_pieces<MODE>(P, bp, nwb, lane);
-        // the closing blocks of g watch this count reach sb
+        // the closing blocks of g watch this count reach sb (psb2: the second phase's, the next word)
         complete_before();
         if (lane == 0)
-            (void)__hip_atomic_fetch_add(P.cnt_s + static_cast<int64_t>(g) * kSyncStride, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+            (void)__hip_atomic_fetch_add(P.cnt_s + static_cast<int64_t>(g) * kSyncStride + (phase == 2 ? 1 : 0), 1u,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if constexpr (MODE == kGreedy) {
         group_greedy_block(P, g, dyn);
+    } else if (kind == kDecideBlock) {
+        decide_block<DT, VEC>(P, g, dyn);
     } else {
         group_resid_block<DT, VEC>(P, g, idx, dyn);
     }
@@ -3838,7 +4071,7 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
 // the whole problem), and its residual wavefronts take spw subsegments of row
 // k each.
 Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, int cus, int mode = kSample,
-                  bool defer = false) {
+                  bool defer = false, int32_t p0 = 0) {
     Layout L{};
     Params& p = L.p;
     L.group = true;
@@ -3858,8 +4091,14 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     if (cpw > static_cast<int64_t>(kMaxPieces - 1) * p.nchunk) cpw = static_cast<int64_t>(kMaxPieces - 1) * p.nchunk;
     if (cpw < 1) cpw = 1;
     p.cpw = static_cast<int32_t>(cpw);
-    p.nw = static_cast<int32_t>(ceil_div(per_group, cpw));
+    // two phases (T > 0, bonus row deferred, 0 < p0 < gamma): the first
+    // phase's pairs, then the rest, each cut into ranges of its own
+    p.p0 = !greedy && p.defer && p0 > 0 && p0 < gamma ? p0 : 0;
+    const int64_t per_group1 = p.p0 ? 2 * static_cast<int64_t>(p.p0) * p.nchunk : per_group;
+    p.nw = static_cast<int32_t>(ceil_div(per_group1, cpw));
     p.sb = static_cast<int32_t>(ceil_div(p.nw, kWavesPerBlock));
+    p.pnw2 = p.p0 ? static_cast<int32_t>(ceil_div(2 * static_cast<int64_t>(gamma - p.p0) * p.nchunk, cpw)) : 0;
+    p.psb2 = static_cast<int32_t>(ceil_div(p.pnw2, kWavesPerBlock));
     p.maxp = static_cast<int32_t>(ceil_div(p.nchunk, cpw) + 1);
     p.nsub = static_cast<int32_t>(ceil_div(V, kSub));
     // residual subsegments per wavefront: one when the closing blocks of all
@@ -3885,7 +4124,7 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     const int64_t gslots = static_cast<int64_t>(p.rps) * p.maxp;
     p.stage = gslots <= kMaxStage ? static_cast<int32_t>(gslots) : 0;
     L.units = G;
-    L.blocks = G * (p.sb + p.rb);
+    L.blocks = G * (p.sb + p.rb) + (p.p0 ? G * (1 + p.psb2) : 0);
     L.lds = static_cast<uint32_t>(p.stage) * 20u;
     const size_t slots = static_cast<size_t>(G) * gslots;
     size_t o = 0;
@@ -3904,20 +4143,46 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     o = align_up(o + (p.defer ? static_cast<size_t>(G) * p.nsub * sizeof(float) : 0), 256);
     L.bytes = o;
     L.cnt_words = 2 * G * kSyncStride;
-    L.dec_words = G;  // per group the word that marks its outputs void (a closing block's wait ran out)
+    // per group the word that marks its outputs void (a closing block's wait
+    // ran out), then (two phases) the groups' decision records
+    L.dec_words = G + (p.p0 ? G * kGroupRecWords : 0);
     return L;
 }
 
 // The automatic schedule at T > 0: position-major with the early stop once
-// one position's row pairs, cut into 16-chunk wavefront ranges, fill four
+// one position's row pairs, cut into 16-chunk wavefront ranges, fill eight
 // blocks per compute unit (below that, decisions lag too many positions behind
-// the stream to save reads), else group-major. The rule is stated on 16-chunk
-// ranges whatever range the kernel streams with. L is the position-major
-// layout.
+// the stream to save reads), else group-major (in two phases where its rows
+// are long enough, below). The rule is stated on 16-chunk ranges whatever
+// range the kernel streams with. L is the position-major layout.
 constexpr int kAutoChunksPerWave = 16;
+// Measured on the headline recipe (V = 128256, bf16), two phases against
+// the early stop: 78.5 against 90.7 us at B = 128, 109.4 against 115.2 at
+// 192; on the 256-sequence workload (V = 152064) 147.7 against 143.6.
 bool auto_position_major(int64_t B, const Layout& L, int cus) {
     const int64_t nb2 = ceil_div(ceil_div(2 * static_cast<int64_t>(L.p.nchunk), kAutoChunksPerWave), kWavesPerBlock);
-    return B * nb2 >= 4 * static_cast<int64_t>(cus);
+    return B * nb2 >= 8 * static_cast<int64_t>(cus);
+}
+
+// Two phases: the first phase's row pairs, about 3/8 of gamma (at least one,
+// at most gamma - 1; 0 at gamma = 1: one phase). Measured with 2, 3, 4 pairs
+// at gamma = 8 (headline recipe): 50.7, 50.3, 52.9 us at B = 64, 67.0, 63.2,
+// 66.4 at B = 96; at gamma = 5 (8-sequence fp32 recipe, B = 256) 62.7 against
+// 68.2 with 3.
+int32_t phase1_pairs(int32_t gamma) {
+    if (gamma < 2) return 0;
+    return std::max<int32_t>(1, std::min<int32_t>((3 * gamma + 4) / 8, gamma - 1));
+}
+// ... and only where the group-major stream is long enough for the rows it
+// skips to outweigh the decider's step in the closing chain: at least this
+// many bytes of the groups' rows (2 gamma B V s). Measured on the headline
+// recipe, two phases against one: 47.7 against 49.8 us at B = 56 (230 MB),
+// 44.7 against 43.9 at B = 48 (197 MB), 63.2 against 76.6 at B = 96; 29.2
+// against 26.9 on 64 sequences of the 8-sequence fp32 recipe (82 MB).
+constexpr int64_t kTwoPhaseBytes = int64_t(200) << 20;
+int32_t auto_phase1_pairs(int64_t B, int32_t gamma, int32_t V, int32_t dtype) {
+    const int64_t bytes = 2 * static_cast<int64_t>(gamma) * B * V * elem_bytes(dtype);
+    return bytes >= kTwoPhaseBytes ? phase1_pairs(gamma) : 0;
 }
 
 int compute_units(int dev) {
@@ -4251,7 +4516,8 @@ int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
     std::lock_guard<std::mutex> lk(g_mu);
     const int cus = compute_units(dev);
     const Layout L = plan(kSample, B, gamma, V, dtype, vec, cus);
-    return auto_position_major(B, L, cus) ? SPEC_SCHEDULE_EARLY_STOP : SPEC_SCHEDULE_GROUP;
+    if (auto_position_major(B, L, cus)) return SPEC_SCHEDULE_EARLY_STOP;
+    return auto_phase1_pairs(B, gamma, V, dtype) > 0 ? SPEC_SCHEDULE_GROUP_TWO_PHASE : SPEC_SCHEDULE_GROUP;
 }
 
 size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature) {
@@ -4305,7 +4571,7 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
                      (greedy || aligned16(draft_logits));
     const int mode = greedy ? kGreedy : kSample;
     const int32_t sched = extras ? extras->schedule : SPEC_SCHEDULE_AUTO;
-    if (sched < SPEC_SCHEDULE_AUTO || sched > SPEC_SCHEDULE_POSITION)
+    if (sched < SPEC_SCHEDULE_AUTO || sched > SPEC_SCHEDULE_GROUP_TWO_PHASE)
         return fail(SPEC_EINVAL, "extras->schedule must be one of the spec_schedule_t values");
     const bool per_row = extras && (extras->row_max || extras->row_sumexp || extras->p_draft || extras->q_draft ||
                                     extras->argmax);
@@ -4315,8 +4581,9 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     const bool defer = !greedy && !per_row && !(extras && extras->Z);
     // the size limits do not depend on the device: checked before any HIP call
     if (int rc = check_size(mode, plan(mode, B, gamma, V, dtype, vec, 1))) return rc;
-    if (!greedy || sched == SPEC_SCHEDULE_GROUP) {
-        if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode, defer))) return rc;
+    if (!greedy || sched == SPEC_SCHEDULE_GROUP || sched == SPEC_SCHEDULE_GROUP_TWO_PHASE) {
+        if (int rc = check_size(mode, plan_group(B, gamma, V, dtype, vec, 1, mode, defer, phase1_pairs(gamma))))
+            return rc;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
@@ -4326,13 +4593,17 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     const int cus = compute_units(dev);
     Layout L = plan(mode, B, gamma, V, dtype, vec, cus);
     bool early = true;
-    if (greedy && sched == SPEC_SCHEDULE_GROUP) {
+    if (greedy && (sched == SPEC_SCHEDULE_GROUP || sched == SPEC_SCHEDULE_GROUP_TWO_PHASE)) {
         L = plan_group(B, gamma, V, dtype, vec, cus, kGreedy);
     } else if (!greedy) {
         // auto: position-major with the early stop once one position's units
         // fill the chip (about four blocks per compute unit), else group-major
-        const bool pos = sched == SPEC_SCHEDULE_AUTO ? auto_position_major(B, L, cus) : sched != SPEC_SCHEDULE_GROUP;
-        if (!pos) L = plan_group(B, gamma, V, dtype, vec, cus, kSample, defer);
+        // in two phases
+        const bool group = sched == SPEC_SCHEDULE_AUTO ? !auto_position_major(B, L, cus)
+                                                       : sched == SPEC_SCHEDULE_GROUP || sched == SPEC_SCHEDULE_GROUP_TWO_PHASE;
+        const int32_t p0 = sched == SPEC_SCHEDULE_AUTO ? auto_phase1_pairs(B, gamma, V, dtype)
+                                                       : (sched == SPEC_SCHEDULE_GROUP_TWO_PHASE ? phase1_pairs(gamma) : 0);
+        if (group) L = plan_group(B, gamma, V, dtype, vec, cus, kSample, defer, p0);
         early = sched != SPEC_SCHEDULE_POSITION;
     }
     Workspace* ws = nullptr;

@@ -149,7 +149,8 @@ def test_planning_over_the_shape_range():
                 for dt in (0, 1):
                     for T in (0.0, 0.8):
                         s = lib.spec_verify_schedule(B, g, V, dt, T)
-                        assert s in (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP), (B, V, g, dt, T, s)
+                        assert s in (sv.SCHEDULE_GROUP, sv.SCHEDULE_GROUP_TWO_PHASE, sv.SCHEDULE_EARLY_STOP), \
+                            (B, V, g, dt, T, s)
                         if T == 0.0:
                             assert s == sv.SCHEDULE_EARLY_STOP
                         assert lib.spec_verify_workspace_bytes(B, g, V, dt, T) > 0, (B, V, g, dt, T)
@@ -168,7 +169,7 @@ def test_oversized_problems_are_rejected_before_any_hip_call(B, gamma, V, T):
         rc = f(P(16), P(16), P(16), B, gamma, V, 1, T, 0, P(16), P(16), None)
         assert rc == sv.SPEC_EINVAL, (f, rc, sv.last_error())
         assert "too large" in sv.last_error()
-    for sched in (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION):
+    for sched in (sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION, sv.SCHEDULE_GROUP_TWO_PHASE):
         ex = sv.Extras()
         ex.schedule = sched
         rc = lib.spec_verify_ex(P(16), P(16), P(16), B, gamma, V, 1, T, 0, P(16), P(16), None, ctypes.byref(ex))

@@ -60,6 +60,7 @@ def check_verify_rows(inp, gpu, seed):
 VERIFY_CASES = {
     # name: (inputs, schedule)
     "group_sampling": (lambda: W.make_inputs(W.WORKLOADS["zipf_b8_g5_v32000_f32"], 3), 1),
+    "two_phase_sampling": (lambda: W.make_inputs(W.WORKLOADS["zipf_b8_g5_v32000_f32"], 3), 4),
     "early_stop_sampling": (lambda: W.make_inputs(W.WORKLOADS["zipf_b8_g5_v32000_f32"], 3), 2),
     "group_greedy": (lambda: W.make_inputs(W.WORKLOADS["greedy_b32_g8_v128256_f32"].scaled(V=20000), 4), 1),
     "early_stop_greedy": (lambda: W.make_inputs(W.WORKLOADS["greedy_b32_g8_v128256_f32"].scaled(V=20000), 4), 2),

@@ -54,7 +54,7 @@ def check_values(inp, orc, gpu):
 #  plain      the group-major order with no debug output (the default call's
 #             path at small B): at T > 0 the bonus row is then read only by the
 #             closing blocks of sequences that accept every draft token.
-LEGS = {"group": (1, True), "position": (3, True), "early": (2, False), "plain": (1, False)}
+LEGS = {"group": (1, True), "position": (3, True), "early": (2, False), "plain": (1, False), "two_phase": (4, False)}
 
 
 def parity(inp, seed, b_offset=0, report=None, schedule=0, debug=True):
@@ -334,7 +334,8 @@ def test_schedules_give_the_same_outputs(name):
         full = G.run(inp, 1000 + s, schedule=sv.SCHEDULE_POSITION)
         tgt, dft = G.to_device(inp.target, wl.dtype), G.to_device(inp.draft, wl.dtype)
         tok = torch.from_numpy(inp.tokens).to("cuda:0")
-        for sched in (sv.SCHEDULE_AUTO, sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION):
+        for sched in (sv.SCHEDULE_AUTO, sv.SCHEDULE_GROUP, sv.SCHEDULE_EARLY_STOP, sv.SCHEDULE_POSITION,
+                      sv.SCHEDULE_GROUP_TWO_PHASE):
             ex = sv.Extras()
             ex.schedule = sched
             for rep_call in range(2):
@@ -348,8 +349,12 @@ def test_schedules_give_the_same_outputs(name):
 
 
 def test_auto_schedule_rule():
-    """The automatic choice: group-major for the B=64 headline shape, the early
-    stop once one position's blocks fill the chip (the B=256 shape)."""
-    assert sv.auto_schedule(64, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP
+    """The automatic choice: group-major in two phases for the B=64 headline
+    shape (one phase at gamma = 1), the early stop once one position's blocks
+    fill the chip (the B=256 shape)."""
+    assert sv.auto_schedule(64, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE
+    assert sv.auto_schedule(64, 1, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP
+    assert sv.auto_schedule(8, 5, 32000, sv.SPEC_F32, 1.0) == sv.SCHEDULE_GROUP  # (rows below 200 MiB)
+    assert sv.auto_schedule(192, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE
     assert sv.auto_schedule(256, 8, 152064, sv.SPEC_BF16, 0.7) == sv.SCHEDULE_EARLY_STOP
     assert sv.auto_schedule(32, 8, 128256, sv.SPEC_F32, 0.0) == sv.SCHEDULE_EARLY_STOP
