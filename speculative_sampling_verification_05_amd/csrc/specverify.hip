@@ -130,6 +130,16 @@ constexpr int kGroupChunksPerWave = SPECVERIFY_GROUP_CHUNKS_PER_WAVE;  // (group
 // blocks at the end: 53.7 against 54.1 us at 64 sequences, 76.5 against 78.7
 // at 96 (lags 40 and 48: 55.8 and 54.3 at 64, 77.7 and 76.2 at 96).
 constexpr int kLag = SPECVERIFY_LAG;
+// group-major in two phases: groups between a group's first-phase statistics
+// blocks and its decider, once there are more than twice as many groups (else
+// all deciders follow the first phase). Measured on the headline recipe
+// against all deciders after the first phase: 72.3 against 78.6 us at
+// B = 128, 104.5 against 109.2 at 192, 61.4 against 62.9 at 96, but 50.8
+// against 50.3 at 64 (lags 8, 16, 24 within 0.5 us of 32).
+#ifndef SPECVERIFY_DECIDE_LAG
+#define SPECVERIFY_DECIDE_LAG 32
+#endif
+constexpr int kDecideLag = SPECVERIFY_DECIDE_LAG;
 // group-major, T > 0: the last groups, about this many bytes of rows, are
 // streamed with ordinary loads (the rest non-temporal), so that the closing
 // steps, which follow the end of the stream, re-read row k from the caches
@@ -630,17 +640,32 @@ __device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint
     const uint32_t D = static_cast<uint32_t>(P.lag), G = static_cast<uint32_t>(P.B);
     phase = 0;
     if (P.p0 > 0) {
+        // (the decider of group g follows the first-phase blocks of group
+        // g + D, D = P.lag, so that it decides while the first phase streams)
         const uint32_t S2 = static_cast<uint32_t>(P.psb2);
-        if (x < G * S) {
+        const uint32_t head = D * S, mid = (G - D) * (S + 1);
+        if (x < head) {
             kind = kStatsBlock;
             phase = 1;
             g = x / S;
             idx = x - g * S;
-        } else if ((x -= G * S) < G) {
+        } else if ((x -= head) < mid) {
+            const uint32_t t = x / (S + 1), o = x - t * (S + 1);
+            if (o < S) {
+                kind = kStatsBlock;
+                phase = 1;
+                g = D + t;
+                idx = o;
+            } else {
+                kind = kDecideBlock;
+                g = t;
+                idx = 0;
+            }
+        } else if ((x -= mid) < D) {
             kind = kDecideBlock;
-            g = x;
+            g = G - D + x;
             idx = 0;
-        } else if ((x -= G) < G * S2) {
+        } else if ((x -= D) < G * S2) {
             kind = kStatsBlock;
             phase = 2;
             g = x / S2;
@@ -4115,6 +4140,7 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     p.spw = spw;
     p.rb = greedy ? 1 : static_cast<int32_t>(ceil_div(p.nsub, kWavesPerBlock * spw));
     p.lag = static_cast<int32_t>(G < kLag ? G : kLag);
+    if (p.p0) p.lag = static_cast<int32_t>(G > 2 * kDecideLag ? kDecideLag : G);
     {
         const int64_t group_bytes = static_cast<int64_t>(p.srows) * V * elem_bytes(dtype);
         const int64_t tail = greedy ? 0 : std::min<int64_t>(G, kCachedTailBytes / std::max<int64_t>(group_bytes, 1));

@@ -140,6 +140,7 @@ EDGE_SHAPES = [
     (1, 8, 128256, W.BF16),
     (60, 2, 1003, W.BF16),     # more groups than the group-major lag: residual blocks interleaved
     (61, 1, 4096, W.F32),      #   with the stream (scalar and vector path)
+    (70, 3, 1003, W.BF16),     # two phases with the deciders interleaved with the first phase
 ]
 
 
