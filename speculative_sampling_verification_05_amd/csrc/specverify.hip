@@ -140,6 +140,11 @@ constexpr int kLag = SPECVERIFY_LAG;
 #define SPECVERIFY_DECIDE_LAG 32
 #endif
 constexpr int kDecideLag = SPECVERIFY_DECIDE_LAG;
+// Two phases: a second-phase statistics block waits for its group's record
+// before it loads (1), or reads it once and loads unless it already says stop (0).
+#ifndef SPECVERIFY_PHASE2_WAIT
+#define SPECVERIFY_PHASE2_WAIT 1
+#endif
 // group-major, T > 0: the last groups, about this many bytes of rows, are
 // streamed with ordinary loads (the rest non-temporal), so that the closing
 // steps, which follow the end of the stream, re-read row k from the caches
@@ -3000,8 +3005,15 @@ __global__ __launch_bounds__(kBlock) void k_group(Params P) {
             bp.done = 0u;
             bp.skip = 0u;
             if (phase == 2) {  // the sequence stopped within the first phase: nothing to load
-                const uint64_t w0 = cld64(group_rec(P, g));
-                bp.skip = static_cast<uint32_t>(w0 >> 32) == P.epoch && (static_cast<uint32_t>(w0) >> 8) != kRecCont;
+                uint64_t w0 = 0;
+                auto known = [&] {
+                    w0 = cld64(group_rec(P, g));
+                    return static_cast<uint32_t>(w0 >> 32) == P.epoch;
+                };
+                // (the decider precedes every second-phase block in the grid;
+                // a wait that runs out loads the rows, which is never wrong)
+                const bool k = SPECVERIFY_PHASE2_WAIT ? spin_until(known, P.wait) : known();
+                bp.skip = k && (static_cast<uint32_t>(w0) >> 8) != kRecCont;
             }
         }
         __syncthreads();
