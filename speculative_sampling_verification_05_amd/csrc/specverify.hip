@@ -2675,12 +2675,14 @@ __device__ inline uint64_t* void_word(const Params& P, uint32_t g) { return P.de
 // first-phase statistics blocks). Once the first phase's rows have counted
 // in, it folds them and takes the accept step for positions 0..p0-1 exactly
 // as the residual blocks do for all positions. A rejection or an unusable row
-// there ends the sequence: the decider writes its outputs (the draw writes the
-// token at k) and a record with k and row k's residual constants; the second
-// phase's statistics blocks of the group then load nothing, and its residual
-// blocks skip the fold. All p0 accepted: the record says so, and the residual
-// blocks fold the whole group as in one phase. A wait that runs out makes the
-// record void (the outputs -1). The decider resets the first phase's count.
+// there ends the sequence: the decider writes a record with k and row k's
+// residual constants; the second phase's statistics blocks of the group then
+// load nothing, and its residual blocks skip the fold (the first of them
+// writes the outputs, the draw the token at k). All p0 accepted: the record
+// says so, and the residual blocks fold the whole group as in one phase. A
+// wait that runs out makes the record void (the outputs -1). The decider
+// writes nothing else, so the record leaves as soon as it is known, and
+// resets the first phase's count.
 template <int DT, bool VEC>
 __device__ inline void decide_block(const Params& P, uint32_t g, char* dyn) {
     __shared__ RowStat rs[2 * SPEC_MAX_GAMMA + 1];
@@ -2713,7 +2715,6 @@ __device__ inline void decide_block(const Params& P, uint32_t g, char* dyn) {
     if (s_st == 0) merge_group<false, kBlock>(P, g, dyn, rs);  // (the second phase's rows are not used)
     if (w != 0) return;
     const int i = lane;
-    const int64_t b = g;
     uint32_t kind = kRecVoid;
     int32_t k = -1;
     double rho = 0.0, scale_p = 0.0;
@@ -2754,12 +2755,6 @@ __device__ inline void decide_block(const Params& P, uint32_t g, char* dyn) {
             kind = kRecCont;
         }
     }
-    if (kind != kRecCont) {  // the outputs: k, the accepted tokens, -1 after k (the draw writes the token at k)
-        if (i <= gamma && (kind == kRecVoid || i != k))
-            cst(P.out_tokens + b * nt + i, kind == kRecStop && i < k ? x : -1);
-        if (i == 0) cst(P.out_n + b, k);
-    }
-    complete_before();
     uint64_t* r = group_rec(P, g);
     const uint64_t rb = __double_as_longlong(rho), sb = __double_as_longlong(scale_p);
     uint32_t v = 0u;
@@ -2818,14 +2813,11 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
         if (w == 0) {
             GroupRec r;
             auto got = [&] { return read_group_rec(P, g, lane, r); };
-            if (!spin_until(got, P.wait)) {
-                // flagged and the group voided; the record is still awaited, so
-                // that the decider's outputs precede the void row
+            if (!spin_until(got, P.wait)) {  // flagged, and the group's outputs void
                 if (lane == 0) {
                     cst(P.err, 1u);
                     cst64(void_word(P, g), tagged(P, 1u));
                 }
-                (void)spin_until(got, kWaitTicks);
                 r.kind = kRecVoid;
             }
             if (lane == 0) s_rec = r;
@@ -2850,6 +2842,12 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
         in.mcq = r.mcq;
         in.rho = r.rho;
         in.scale_p = r.scale_p;
+    }
+    if (!fold && idx == 0 && w == 0) {  // stopped (or void) within the first phase: k, the accepted tokens, -1 after k
+        const int32_t k = in.k;
+        if (lane <= gamma && (k < 0 || lane != k))
+            cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, lane < k ? x : -1);
+        if (lane == 0) cst(P.out_n + g, k);
     }
     if (fold && s_st == 0) {
         merge_group<false, kBlock>(P, g, dyn, rs);
