@@ -2370,7 +2370,7 @@ __device__ inline void p_masses(const Params& P, uint32_t g, const SeqInfo& in, 
 }
 
 template <int DT, bool VEC>
-__device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int lane, double ud) {
+__device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int lane, double ud, bool dead) {
     const int32_t nsub = P.nsub;
     double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
     const double u = __shfl(ud, in.k, kWave);  // lane i holds the draw's uniform for k = i
@@ -2400,6 +2400,7 @@ __device__ inline void draw(const Params& P, uint32_t g, const SeqInfo& in, int 
         target = u * (from_p ? scan_total(sr, nsub, lane) : Z);
         sel = scan_find(sr, nsub, target, lane, before);
     }
+    if (dead) return;  // (the caller writes the whole row as invalid)
     if (P.dbg_z && lane == 0) P.dbg_z[g] = Z * in.scale_p;
     int32_t* out = P.out_tokens + static_cast<int64_t>(g) * (P.gamma + 1) + in.k;
     if (sel < 0) {  // no mass at all (cannot happen for a usable row); keep the output defined
@@ -2503,7 +2504,7 @@ __device__ inline void bonus_masses(const Params& P, uint32_t g, int32_t i0, int
 // scanned as in draw(); the chosen subsegment is read again and its elements'
 // masses formed exactly as in bonus_masses, scaled by the same power of two.
 template <int DT, bool VEC>
-__device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int lane, double ud) {
+__device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int lane, double ud, bool dead) {
     const int32_t gamma = P.gamma, nsub = P.nsub, nt = gamma + 1;
     const float c = P.c32;
     const double* sr = P.sub_r + static_cast<int64_t>(g) * nsub;
@@ -2569,6 +2570,7 @@ __device__ inline void draw_bonus(const Params& P, uint32_t g, int32_t x, int la
             }
         }
     }
+    if (dead) return;  // (the caller writes the whole row as invalid)
     const bool ok = !bad && Z > 0.0 && sel >= 0;
     int32_t pick = -1;
     if (ok) {
@@ -2925,15 +2927,21 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
     __syncthreads();
     if (!s_last || w != 0) return;
     after_complete();
-    // every residual block of g has counted in, each after seeing the
-    // statistics count complete (unless even its drain ran out: then the
-    // count is left for the status call's scrub)
+    // every residual block of g has counted in. The void word and the counts
+    // this block resets are loaded beside the draw's first loads: only the
+    // draw's writes wait for the word, and the resets follow the draw.
     uint32_t* cnt_s = P.cnt_s + static_cast<int64_t>(g) * kSyncStride;
-    const bool dead = static_cast<uint32_t>(cld64(void_word(P, g)) >> 32) == P.epoch;
+    const uint64_t vw = cld64(void_word(P, g));
+    uint32_t c1 = 0, c2 = 0;
     if (lane == 0) {
-        if (cld(cnt_s) == static_cast<uint32_t>(P.sb)) cst(cnt_s, 0u);
-        cst(cnt_r, 0u);
-        if (dead) cst64(void_word(P, g), 0ull);  // (a mark never outlives its call)
+        c1 = cld(cnt_s);
+        if (P.p0 > 0) c2 = cld(cnt_s + 1);
+    }
+    const bool dead = static_cast<uint32_t>(vw >> 32) == P.epoch;
+    if (in.k >= 0 && P.defer && in.k == gamma) {
+        draw_bonus<DT, VEC>(P, g, x, lane, ud, dead);
+    } else if (in.k >= 0) {
+        draw<DT, VEC>(P, g, in, lane, ud, dead);
     }
     if (dead) {  // a closing block's wait ran out: the whole row is reported invalid
         if (lane <= gamma) cst(P.out_tokens + static_cast<int64_t>(g) * (gamma + 1) + lane, -1);
@@ -2941,17 +2949,21 @@ __device__ inline void group_resid_block(const Params& P, uint32_t g, uint32_t i
             cst(P.out_n + g, -1);
             if (P.dbg_z) P.dbg_z[g] = NAN;
         }
-    } else if (in.k >= 0 && P.defer && in.k == gamma) {
-        draw_bonus<DT, VEC>(P, g, x, lane, ud);
-    } else if (in.k >= 0) {
-        draw<DT, VEC>(P, g, in, lane, ud);
     }
-    // two phases: the second phase's count is reset once all its blocks have
-    // counted in (those of a stopped sequence load nothing and come soon);
-    // the first phase's count was reset by the decider
-    if (P.p0 > 0 && lane == 0) {
-        uint32_t* cnt2 = cnt_s + 1;
-        if (spin_count(cnt2, static_cast<uint32_t>(P.psb2), kWaitTicks)) cst(cnt2, 0u);
+    if (lane == 0) {
+        // the statistics count, once complete (unless even a drain ran out:
+        // then it is left for the status call's scrub; in two phases the
+        // decider has reset it)
+        if (c1 == static_cast<uint32_t>(P.sb)) cst(cnt_s, 0u);
+        cst(cnt_r, 0u);
+        if (dead) cst64(void_word(P, g), 0ull);  // (a mark never outlives its call)
+        // two phases: the second phase's count, once all its blocks have
+        // counted in (those of a stopped sequence load nothing and come soon)
+        if (P.p0 > 0) {
+            uint32_t* cnt2 = cnt_s + 1;
+            if (c2 == static_cast<uint32_t>(P.psb2) || spin_count(cnt2, static_cast<uint32_t>(P.psb2), kWaitTicks))
+                cst(cnt2, 0u);
+        }
     }
 }
 
