@@ -4213,10 +4213,10 @@ bool auto_position_major(int64_t B, const Layout& L, int cus) {
 }
 
 // Two phases: the first phase's row pairs, about 3/8 of gamma (at least one,
-// at most gamma - 1; 0 at gamma = 1: one phase). Measured with 2, 3, 4 pairs
-// at gamma = 8 (headline recipe): 50.7, 50.3, 52.9 us at B = 64, 67.0, 63.2,
-// 66.4 at B = 96; at gamma = 5 (8-sequence fp32 recipe, B = 256) 62.7 against
-// 68.2 with 3.
+// at most gamma - 1; 0 at gamma = 1: one phase). Measured with 1, 2, 3, 4
+// pairs at gamma = 8 (headline recipe): 52.3, 47.7, 46.3, 47.3 us at B = 64,
+// 71.0, 62.6, 58.1, 60.4 at B = 96; at gamma = 5 (8-sequence fp32 recipe,
+// B = 256) 59.1, 54.6, 54.7, 67.0.
 int32_t phase1_pairs(int32_t gamma) {
     if (gamma < 2) return 0;
     return std::max<int32_t>(1, std::min<int32_t>((3 * gamma + 4) / 8, gamma - 1));
@@ -4224,10 +4224,15 @@ int32_t phase1_pairs(int32_t gamma) {
 // ... and only where the group-major stream is long enough for the rows it
 // skips to outweigh the decider's step in the closing chain: at least this
 // many bytes of the groups' rows (2 gamma B V s). Measured on the headline
-// recipe, two phases against one: 47.7 against 49.8 us at B = 56 (230 MB),
-// 44.7 against 43.9 at B = 48 (197 MB), 63.2 against 76.6 at B = 96; 29.2
-// against 26.9 on 64 sequences of the 8-sequence fp32 recipe (82 MB).
-constexpr int64_t kTwoPhaseBytes = int64_t(200) << 20;
+// recipe, two phases against one: 35.2 against 34.0 us at B = 32 (131 MB),
+// 40.2 against 42.0 at B = 40 (164 MB), 42.7 against 45.5 at 48, 44.3
+// against 49.8 at 56, 58.0 against 76.7 at 96; on the 8-sequence fp32
+// recipe 29.8 against 27.1 at B = 64 (82 MB), 37.1 against 40.2 at 128
+// (164 MB). With 2, 3, 4 pairs in the first phase: 47.7, 46.3, 47.3 at
+// B = 64; 62.6, 58.1, 60.4 at 96; 37.1, 37.1, 42.3 at 128 of the fp32
+// recipe; 4 is ahead only at B = 24 (31.8 against 32.1, where one phase
+// takes 30.4).
+constexpr int64_t kTwoPhaseBytes = int64_t(144) << 20;
 int32_t auto_phase1_pairs(int64_t B, int32_t gamma, int32_t V, int32_t dtype) {
     const int64_t bytes = 2 * static_cast<int64_t>(gamma) * B * V * elem_bytes(dtype);
     return bytes >= kTwoPhaseBytes ? phase1_pairs(gamma) : 0;

@@ -355,7 +355,9 @@ def test_auto_schedule_rule():
     fill the chip (the B=256 shape)."""
     assert sv.auto_schedule(64, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE
     assert sv.auto_schedule(64, 1, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP
-    assert sv.auto_schedule(8, 5, 32000, sv.SPEC_F32, 1.0) == sv.SCHEDULE_GROUP  # (rows below 200 MiB)
+    assert sv.auto_schedule(8, 5, 32000, sv.SPEC_F32, 1.0) == sv.SCHEDULE_GROUP  # (rows below 144 MiB)
+    assert sv.auto_schedule(32, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP  # 131 MB
+    assert sv.auto_schedule(40, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE  # 164 MB
     assert sv.auto_schedule(192, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE
     assert sv.auto_schedule(256, 8, 152064, sv.SPEC_BF16, 0.7) == sv.SCHEDULE_EARLY_STOP
     assert sv.auto_schedule(32, 8, 128256, sv.SPEC_F32, 0.0) == sv.SCHEDULE_EARLY_STOP
