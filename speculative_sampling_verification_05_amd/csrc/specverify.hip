@@ -4135,6 +4135,15 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     const int64_t min_waves = static_cast<int64_t>(cus) * 16;
     int64_t cpw = kGroupChunksPerWave;
     if (ceil_div(G * per_group, cpw) < min_waves) cpw = ceil_div(G * per_group, min_waves);
+    // but not so short that a group's partial slots (rps rows of
+    // ceil(nchunk / cpw) + 1) overflow the LDS stage: a fold from memory takes
+    // one round trip per 8 slots of a row. Measured on the headline recipe:
+    // 18.6 against 56.6 us at B = 1, 20.0 against 36.3 at 2, 21.7 against
+    // 26.6 at 4 (from B = 8 on the ranges are long enough already).
+    {
+        const int64_t per_row = kMaxStage / p.rps - 1;
+        if (per_row >= 1) cpw = std::max<int64_t>(cpw, ceil_div(p.nchunk, per_row));
+    }
     if (cpw > static_cast<int64_t>(kMaxPieces - 1) * p.nchunk) cpw = static_cast<int64_t>(kMaxPieces - 1) * p.nchunk;
     if (cpw < 1) cpw = 1;
     p.cpw = static_cast<int32_t>(cpw);
