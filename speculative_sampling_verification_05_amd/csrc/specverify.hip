@@ -4079,6 +4079,11 @@ Layout plan(int mode, int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool v
     const int64_t min_waves = static_cast<int64_t>(cus) * 16;
     int64_t cpw = mode != kGreedy ? kChunksPerWave : dtype == SPEC_BF16 ? kGreedyChunksPerWaveBf16 : kGreedyChunksPerWave;
     if (ceil_div(total, cpw) < min_waves) cpw = ceil_div(total, min_waves);
+    // but long enough that a row has at most one wavefront's worth of slots
+    // (the unit's fold takes a round trip per 64 slots of a row). Measured on
+    // the greedy recipe: 7.15 against 8.35 us at B = 1, 7.5 against 8.4 at
+    // 2, 8.9 against 9.45 at 4, unchanged from 8 on.
+    cpw = std::max<int64_t>(cpw, ceil_div(p.nchunk, kWave - 1));
     if (cpw < 1) cpw = 1;
     p.cpw = static_cast<int32_t>(cpw);
     p.maxp = static_cast<int32_t>(ceil_div(p.nchunk, cpw) + 1);
