@@ -107,6 +107,24 @@ def test_workload_parity_pooled(name):
         assert rep.ok(), f"{leg}: {rep}"
 
 
+@pytest.mark.parametrize("B", [1, 2, 4])
+@pytest.mark.parametrize("name", ["zipf_b64_g8_v128256_bf16", "greedy_b32_g8_v128256_f32"])
+def test_small_batches_full_vocabulary(name, B):
+    """One to four sequences at the full 128256-entry vocabulary: the ranges
+    are then as short as a group's partial slots in the LDS stage (group-major)
+    or one wavefront's worth of slots per row (position-major) allow. Every
+    leg against the oracle, several seeds pooled per leg."""
+    wl = W.WORKLOADS[name].scaled(B=B)
+    reps = {leg: TokenReport() for leg in LEGS}
+    for s in range(4):
+        inp = W.make_inputs(wl, 50 + s)
+        for leg, (schedule, debug) in LEGS.items():
+            parity(inp, seed=70 + s, report=reps[leg], schedule=schedule, debug=debug)
+    for leg, rep in reps.items():
+        print(name, B, leg, rep)
+        assert rep.mismatches <= 1, f"{leg}: {rep}"
+
+
 @pytest.mark.parametrize("name", ["greedy_b32_g8_v128256_f32", "zipf_b256_g8_v152064_bf16"])
 def test_full_size_parity(name):
     """The full workload: every row's values against the oracle (the debug
