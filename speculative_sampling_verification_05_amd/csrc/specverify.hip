@@ -140,6 +140,13 @@ constexpr int kLag = SPECVERIFY_LAG;
 #define SPECVERIFY_DECIDE_LAG 32
 #endif
 constexpr int kDecideLag = SPECVERIFY_DECIDE_LAG;
+// Two phases: chunks per second-phase wavefront from this many groups on
+// (below it the first phase's). Measured on the headline recipe, 48 against
+// 24: 70.9 against 72.2 us at B = 128, 101.6 against 104.5 at 192, but 58.9
+// against 58.2 at 96 and 50.5 against 46.2 at 64 (32 and 64 chunks: 47.7
+// and 51.8 at 64, 72.3 and 72.1 at 128).
+constexpr int64_t kLongPhase2Groups = 128;
+constexpr int64_t kPhase2ChunksPerWave = 48;
 // Two phases: a second-phase statistics block waits for its group's record
 // before it loads (1), or reads it once and loads unless it already says stop (0).
 #ifndef SPECVERIFY_PHASE2_WAIT
@@ -482,6 +489,7 @@ struct Params {
     int32_t p0;      // group-major in two phases (0: one phase): the first p0 row pairs of every
     int32_t pnw2;    //   group, then the group's decider, then the other pairs (their wavefronts
     int32_t psb2;    //   and blocks per group), read only for sequences not stopped within p0
+    int32_t cpw2;    //   chunks per statistics wavefront in the second phase
     int32_t skip;    // early stop: wavefronts of sequences already stopped load nothing
     uint32_t epoch;  // tag of this call's decision words and draw records (never 0)
     uint64_t wait;   // bound on a wait, in wall-clock ticks (kWaitTicks unless the host set another)
@@ -968,7 +976,8 @@ __device__ inline int stats_wave(const Params& P, const Role& U, uint32_t wl, in
     using Lane = typename std::conditional<MODE == kGreedy, ArgLane, SoftLane>::type;
     const float c = P.c32;
     const bool watch = !GROUP && MODE != kRows && P.skip && U.i > 0;
-    const uint32_t nchunk = static_cast<uint32_t>(P.nchunk), cpw = static_cast<uint32_t>(P.cpw);
+    const uint32_t nchunk = static_cast<uint32_t>(P.nchunk);
+    const uint32_t cpw = static_cast<uint32_t>(GROUP && U.i == 2 ? P.cpw2 : P.cpw);
     const uint32_t total = static_cast<uint32_t>(U.rows) * nchunk;
     uint32_t cc = wl * cpw;
     const uint32_t c_end = cc + cpw < total ? cc + cpw : total;
@@ -4158,7 +4167,14 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
     const int64_t per_group1 = p.p0 ? 2 * static_cast<int64_t>(p.p0) * p.nchunk : per_group;
     p.nw = static_cast<int32_t>(ceil_div(per_group1, cpw));
     p.sb = static_cast<int32_t>(ceil_div(p.nw, kWavesPerBlock));
-    p.pnw2 = p.p0 ? static_cast<int32_t>(ceil_div(2 * static_cast<int64_t>(gamma - p.p0) * p.nchunk, cpw)) : 0;
+    // the second phase's ranges: longer from kLongPhase2Groups groups on
+    // (fewer blocks wait for their group's decision while holding slots)
+    {
+        int64_t c2 = G >= kLongPhase2Groups ? std::max<int64_t>(cpw, kPhase2ChunksPerWave) : cpw;
+        if (c2 > static_cast<int64_t>(kMaxPieces - 1) * p.nchunk) c2 = static_cast<int64_t>(kMaxPieces - 1) * p.nchunk;
+        p.cpw2 = static_cast<int32_t>(c2);
+    }
+    p.pnw2 = p.p0 ? static_cast<int32_t>(ceil_div(2 * static_cast<int64_t>(gamma - p.p0) * p.nchunk, p.cpw2)) : 0;
     p.psb2 = static_cast<int32_t>(ceil_div(p.pnw2, kWavesPerBlock));
     p.maxp = static_cast<int32_t>(ceil_div(p.nchunk, cpw) + 1);
     p.nsub = static_cast<int32_t>(ceil_div(V, kSub));

@@ -159,6 +159,8 @@ EDGE_SHAPES = [
     (60, 2, 1003, W.BF16),     # more groups than the group-major lag: residual blocks interleaved
     (61, 1, 4096, W.F32),      #   with the stream (scalar and vector path)
     (70, 3, 1003, W.BF16),     # two phases with the deciders interleaved with the first phase
+    (130, 3, 1003, W.BF16),    # two phases from 128 groups: second-phase ranges longer than the first's
+    (128, 4, 4096, W.F32),     #   (scalar path: 12 chunks against 1; vector path: 48 against 16)
 ]
 
 
