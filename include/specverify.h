@@ -167,8 +167,8 @@ typedef struct {
  *                            closing blocks of a sequence that stopped early
  *                            take k and row k's constants from its decider.
  *  SPEC_SCHEDULE_AUTO        EARLY_STOP once one position's blocks fill the
- *                            chip twice over (B times the blocks of one row
- *                            pair at least eight per compute unit), else
+ *                            chip more than twice over (B times the blocks of
+ *                            one row pair at least nine per compute unit), else
  *                            GROUP_TWO_PHASE where the rows come to at least
  *                            144 MiB (2 gamma B V times the element size;
  *                            gamma >= 2), else GROUP.

@@ -4228,18 +4228,20 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
 }
 
 // The automatic schedule at T > 0: position-major with the early stop once
-// one position's row pairs, cut into 16-chunk wavefront ranges, fill eight
+// one position's row pairs, cut into 16-chunk wavefront ranges, fill nine
 // blocks per compute unit (below that, decisions lag too many positions behind
 // the stream to save reads), else group-major (in two phases where its rows
 // are long enough, below). The rule is stated on 16-chunk ranges whatever
 // range the kernel streams with. L is the position-major layout.
 constexpr int kAutoChunksPerWave = 16;
 // Measured on the headline recipe (V = 128256, bf16), two phases against
-// the early stop: 78.5 against 90.7 us at B = 128, 109.4 against 115.2 at
-// 192; on the 256-sequence workload (V = 152064) 147.7 against 143.6.
+// the early stop: 70.7 against 90.7 us at B = 128, 102.0 against 115.2 at
+// 192, 135.6 against 138.7 at 256 (eight blocks per compute unit), 206.3
+// against 190.3 at 384 (twelve); on the 256-sequence workload (V = 152064,
+// ten) 142.5 against 143.8, and at 160 sequences 88.2 against 106.2.
 bool auto_position_major(int64_t B, const Layout& L, int cus) {
     const int64_t nb2 = ceil_div(ceil_div(2 * static_cast<int64_t>(L.p.nchunk), kAutoChunksPerWave), kWavesPerBlock);
-    return B * nb2 >= 8 * static_cast<int64_t>(cus);
+    return B * nb2 >= 9 * static_cast<int64_t>(cus);
 }
 
 // Two phases: the first phase's row pairs, about 3/8 of gamma (at least one,

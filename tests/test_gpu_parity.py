@@ -379,5 +379,7 @@ def test_auto_schedule_rule():
     assert sv.auto_schedule(32, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP  # 131 MB
     assert sv.auto_schedule(40, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE  # 164 MB
     assert sv.auto_schedule(192, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE
+    assert sv.auto_schedule(256, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE  # 8 per CU
+    assert sv.auto_schedule(384, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_EARLY_STOP  # 12 per CU
     assert sv.auto_schedule(256, 8, 152064, sv.SPEC_BF16, 0.7) == sv.SCHEDULE_EARLY_STOP
     assert sv.auto_schedule(32, 8, 128256, sv.SPEC_F32, 0.0) == sv.SCHEDULE_EARLY_STOP
