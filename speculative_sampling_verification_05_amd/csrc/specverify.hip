@@ -705,10 +705,13 @@ __device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint
             g = x / S2;
             idx = x - g * S2;
         } else {
+            // (the residual blocks too with one XCD per group: 45.0 against
+            // 45.4 us on the headline recipe, 69.9 against 71.0 at B = 128,
+            // 100.0 against 102.3 at 192; the second-phase blocks placed so
+            // measured 48.7 against 45.4 at the headline)
             x -= G * S2;
             kind = kResidBlock;
-            g = x / R;
-            idx = x - g * R;
+            head_block(x, R, G, g, idx);
         }
         return;
     }
@@ -736,6 +739,9 @@ __device__ inline void decode_block(const Params& P, uint32_t x, int& kind, uint
     }
     x -= mid;  // only reached when R > 0
     kind = kResidBlock;
+    // (one XCD per group here too measured mixed: 33.8 against 34.4 us at
+    // B = 32 and 15.8 against 16.7 on the 8-sequence fp32 workload, but 27.0
+    // against 26.8 at B = 16 and 22.1 against 21.7 at B = 4; not kept)
     const uint32_t t = x / R;
     g = (G - D) + t;
     idx = x - t * R;
