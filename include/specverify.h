@@ -166,9 +166,9 @@ typedef struct {
  *                            per sequence); then the closing blocks. The
  *                            closing blocks of a sequence that stopped early
  *                            take k and row k's constants from its decider.
- *  SPEC_SCHEDULE_AUTO        EARLY_STOP once one position's blocks fill the
- *                            chip more than twice over (B times the blocks of
- *                            one row pair at least nine per compute unit), else
+ *  SPEC_SCHEDULE_AUTO        EARLY_STOP once one position's row pairs come
+ *                            to at least 152 MiB (2 B V times the element
+ *                            size), else
  *                            GROUP_TWO_PHASE where the rows come to at least
  *                            144 MiB (2 gamma B V times the element size;
  *                            gamma >= 2), else GROUP.

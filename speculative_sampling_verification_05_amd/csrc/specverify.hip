@@ -4254,20 +4254,18 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
 }
 
 // The automatic schedule at T > 0: position-major with the early stop once
-// one position's row pairs, cut into 16-chunk wavefront ranges, fill nine
-// blocks per compute unit (below that, decisions lag too many positions behind
-// the stream to save reads), else group-major (in two phases where its rows
-// are long enough, below). The rule is stated on 16-chunk ranges whatever
-// range the kernel streams with. L is the position-major layout.
-constexpr int kAutoChunksPerWave = 16;
-// Measured on the headline recipe (V = 128256, bf16), two phases against
-// the early stop: 70.7 against 90.7 us at B = 128, 102.0 against 115.2 at
-// 192, 135.6 against 138.7 at 256 (eight blocks per compute unit), 206.3
-// against 190.3 at 384 (twelve); on the 256-sequence workload (V = 152064,
-// ten) 142.5 against 143.8, and at 160 sequences 88.2 against 106.2.
-bool auto_position_major(int64_t B, const Layout& L, int cus) {
-    const int64_t nb2 = ceil_div(ceil_div(2 * static_cast<int64_t>(L.p.nchunk), kAutoChunksPerWave), kWavesPerBlock);
-    return B * nb2 >= 9 * static_cast<int64_t>(cus);
+// one position's row pairs come to at least kEarlyStopBytes (2 B V s):
+// below that, decisions lag too many positions behind the stream to save
+// reads; else group-major (in two phases where its rows are long enough,
+// below). Measured, two phases against the early stop: on the headline
+// recipe (V = 128256, bf16; 256.5 KB rows) 70.7 against 90.7 us at B = 128,
+// 102.0 against 115.2 at 192, 131.5 against 139.7 at 256 (131 MB per
+// position), 168.3 against 164.6 at 320 (164 MB), 200.2 against 190.4 at
+// 384; on the 256-sequence recipe (V = 152064; 304 KB rows) 137.4 against
+// 143.9 at B = 256 (156 MB), 173.1 against 168.7 at 320 (195 MB).
+constexpr int64_t kEarlyStopBytes = int64_t(152) << 20;
+bool auto_position_major(int64_t B, int32_t V, int32_t dtype) {
+    return 2 * B * static_cast<int64_t>(V) * elem_bytes(dtype) >= kEarlyStopBytes;
 }
 
 // Two phases: the first phase's row pairs, about 3/8 of gamma (at least one,
@@ -4621,13 +4619,7 @@ int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype,
         !(temperature >= 0.0f))
         return fail(SPEC_EINVAL, "bad shape, dtype or temperature");
     if (temperature == 0.0f) return SPEC_SCHEDULE_EARLY_STOP;
-    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dtype)) % 16 == 0;
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    std::lock_guard<std::mutex> lk(g_mu);
-    const int cus = compute_units(dev);
-    const Layout L = plan(kSample, B, gamma, V, dtype, vec, cus);
-    if (auto_position_major(B, L, cus)) return SPEC_SCHEDULE_EARLY_STOP;
+    if (auto_position_major(B, V, dtype)) return SPEC_SCHEDULE_EARLY_STOP;
     return auto_phase1_pairs(B, gamma, V, dtype) > 0 ? SPEC_SCHEDULE_GROUP_TWO_PHASE : SPEC_SCHEDULE_GROUP;
 }
 
@@ -4707,10 +4699,10 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
     if (greedy && (sched == SPEC_SCHEDULE_GROUP || sched == SPEC_SCHEDULE_GROUP_TWO_PHASE)) {
         L = plan_group(B, gamma, V, dtype, vec, cus, kGreedy);
     } else if (!greedy) {
-        // auto: position-major with the early stop once one position's units
-        // fill the chip (about four blocks per compute unit), else group-major
-        // in two phases
-        const bool group = sched == SPEC_SCHEDULE_AUTO ? !auto_position_major(B, L, cus)
+        // auto: position-major with the early stop once one position's row
+        // pairs are long enough, else group-major (in two phases where its
+        // rows are)
+        const bool group = sched == SPEC_SCHEDULE_AUTO ? !auto_position_major(B, V, dtype)
                                                        : sched == SPEC_SCHEDULE_GROUP || sched == SPEC_SCHEDULE_GROUP_TWO_PHASE;
         const int32_t p0 = sched == SPEC_SCHEDULE_AUTO ? auto_phase1_pairs(B, gamma, V, dtype)
                                                        : (sched == SPEC_SCHEDULE_GROUP_TWO_PHASE ? phase1_pairs(gamma) : 0);
