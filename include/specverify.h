@@ -170,7 +170,7 @@ typedef struct {
  *                            to at least 152 MiB (2 B V times the element
  *                            size), else
  *                            GROUP_TWO_PHASE where the rows come to at least
- *                            144 MiB (2 gamma B V times the element size;
+ *                            112 MiB (2 gamma B V times the element size;
  *                            gamma >= 2), else GROUP.
  * Any of row_max, row_sumexp, p_draft, q_draft or argmax turns EARLY_STOP into
  * POSITION, and any of them or Z makes GROUP stream the bonus row with the

@@ -4279,16 +4279,15 @@ int32_t phase1_pairs(int32_t gamma) {
 }
 // ... and only where the group-major stream is long enough for the rows it
 // skips to outweigh the decider's step in the closing chain: at least this
-// many bytes of the groups' rows (2 gamma B V s). Measured on the headline
-// recipe, two phases against one: 35.2 against 34.0 us at B = 32 (131 MB),
-// 40.2 against 42.0 at B = 40 (164 MB), 42.7 against 45.5 at 48, 44.3
-// against 49.8 at 56, 58.0 against 76.7 at 96; on the 8-sequence fp32
-// recipe 29.8 against 27.1 at B = 64 (82 MB), 37.1 against 40.2 at 128
-// (164 MB). With 2, 3, 4 pairs in the first phase: 47.7, 46.3, 47.3 at
-// B = 64; 62.6, 58.1, 60.4 at 96; 37.1, 37.1, 42.3 at 128 of the fp32
-// recipe; 4 is ahead only at B = 24 (31.8 against 32.1, where one phase
-// takes 30.4).
-constexpr int64_t kTwoPhaseBytes = int64_t(144) << 20;
+// many bytes of the groups' rows (2 gamma B V s). Measured, two phases
+// against one: on the headline recipe 30.4 against 30.1 us at B = 24 (98
+// MB), 32.4 against 32.5 at 28 (115 MB), 33.3 against 34.3 at 32 (131 MB),
+// 38.4 against 41.9 at 40, 44.9 against 54.9 at 64; on the 8-sequence fp32
+// recipe 30.1 against 30.3 at B = 80 (102 MB), 32.1 against 33.4 at 96 (123
+// MB), 34.6 against 37.4 at 112 (143 MB). With 2, 3, 4 pairs in the first
+// phase: 46.8, 44.9, 46.2 at B = 64, 72.8, 70.3, 72.6 at 128; 4 ties 3 only
+// at B = 24.
+constexpr int64_t kTwoPhaseBytes = int64_t(112) << 20;
 int32_t auto_phase1_pairs(int64_t B, int32_t gamma, int32_t V, int32_t dtype) {
     const int64_t bytes = 2 * static_cast<int64_t>(gamma) * B * V * elem_bytes(dtype);
     return bytes >= kTwoPhaseBytes ? phase1_pairs(gamma) : 0;

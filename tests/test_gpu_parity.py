@@ -375,9 +375,10 @@ def test_auto_schedule_rule():
     pairs come to 152 MiB (from 320 sequences of both recipes)."""
     assert sv.auto_schedule(64, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE
     assert sv.auto_schedule(64, 1, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP
-    assert sv.auto_schedule(8, 5, 32000, sv.SPEC_F32, 1.0) == sv.SCHEDULE_GROUP  # (rows below 144 MiB)
-    assert sv.auto_schedule(32, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP  # 131 MB
-    assert sv.auto_schedule(40, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE  # 164 MB
+    assert sv.auto_schedule(8, 5, 32000, sv.SPEC_F32, 1.0) == sv.SCHEDULE_GROUP  # (rows below 112 MiB)
+    assert sv.auto_schedule(24, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP  # 98 MB
+    assert sv.auto_schedule(32, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE  # 131 MB
+    assert sv.auto_schedule(96, 5, 32000, sv.SPEC_F32, 1.0) == sv.SCHEDULE_GROUP_TWO_PHASE  # 123 MB
     assert sv.auto_schedule(192, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE
     # the early stop from 152 MiB of one position's row pairs (2 B V s)
     assert sv.auto_schedule(256, 8, 128256, sv.SPEC_BF16, 0.8) == sv.SCHEDULE_GROUP_TWO_PHASE  # 131 MB
