@@ -4265,7 +4265,8 @@ Layout plan_group(int64_t G, int32_t gamma, int32_t V, int32_t dtype, bool vec, 
 // 143.9 at B = 256 (156 MB), 173.1 against 168.7 at 320 (195 MB).
 constexpr int64_t kEarlyStopBytes = int64_t(152) << 20;
 bool auto_position_major(int64_t B, int32_t V, int32_t dtype) {
-    return 2 * B * static_cast<int64_t>(V) * elem_bytes(dtype) >= kEarlyStopBytes;
+    // (B V stays below 2^62 for int32 shapes; the byte count may not)
+    return B * static_cast<int64_t>(V) >= ceil_div(kEarlyStopBytes, 2 * static_cast<int64_t>(elem_bytes(dtype)));
 }
 
 // Two phases: the first phase's row pairs, about 3/8 of gamma (at least one,
@@ -4289,8 +4290,9 @@ int32_t phase1_pairs(int32_t gamma) {
 // at B = 24.
 constexpr int64_t kTwoPhaseBytes = int64_t(112) << 20;
 int32_t auto_phase1_pairs(int64_t B, int32_t gamma, int32_t V, int32_t dtype) {
-    const int64_t bytes = 2 * static_cast<int64_t>(gamma) * B * V * elem_bytes(dtype);
-    return bytes >= kTwoPhaseBytes ? phase1_pairs(gamma) : 0;
+    // (compared as B V, below 2^62 for int32 shapes, so nothing overflows)
+    const int64_t per = 2 * static_cast<int64_t>(gamma) * elem_bytes(dtype);
+    return B * static_cast<int64_t>(V) >= ceil_div(kTwoPhaseBytes, per) ? phase1_pairs(gamma) : 0;
 }
 
 int compute_units(int dev) {
