@@ -311,9 +311,10 @@ int spec_tree_verify(const void* target_logits, const void* draft_logits, const 
                      float temperature, float threshold, int32_t* out_tokens, int32_t* out_nodes,
                      int32_t* out_n, void* stream);
 
-/* The schedule SPEC_SCHEDULE_AUTO takes for this shape on the current device
- * with no per-row outputs (SPEC_SCHEDULE_GROUP_TWO_PHASE, SPEC_SCHEDULE_GROUP
- * or SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. */
+/* The schedule SPEC_SCHEDULE_AUTO takes for this shape with no per-row
+ * outputs (SPEC_SCHEDULE_GROUP_TWO_PHASE, SPEC_SCHEDULE_GROUP or
+ * SPEC_SCHEDULE_EARLY_STOP), or SPEC_EINVAL. A rule of the shape alone (see
+ * SPEC_SCHEDULE_AUTO): it makes no HIP call. */
 int32_t spec_verify_schedule(int32_t B, int32_t gamma, int32_t V, int32_t dtype, float temperature);
 
 /* spec_verify_status: whether any bounded wait of a kernel enqueued on

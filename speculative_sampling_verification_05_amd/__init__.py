@@ -329,7 +329,8 @@ def tree_verify(target_logits, draft_logits, parent, token, temperature: float, 
 
 
 def auto_schedule(B, gamma, V, dtype, temperature) -> int:
-    """The schedule SCHEDULE_AUTO takes for this shape on the current device."""
+    """The schedule SCHEDULE_AUTO takes for this shape (a rule of the shape
+    alone, evaluated on the host)."""
     rc = load_library().spec_verify_schedule(B, gamma, V, dtype, float(temperature))
     if rc < 0:
         raise SpecVerifyError(rc, last_error())

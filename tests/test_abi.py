@@ -158,6 +158,31 @@ def test_planning_over_the_shape_range():
     assert lib.spec_verify_schedule(1, 64, 100, 0, 1.0) == sv.SPEC_EINVAL
 
 
+def test_automatic_schedule_boundaries():
+    """The automatic choice at T > 0 as the header states it: the early stop
+    once one position's row pairs (2 B V s bytes) come to 152 MiB, else two
+    phases once all row pairs (2 gamma B V s) come to 112 MiB with gamma >= 2,
+    else one phase; at T == 0 always the early stop. Checked on both sides of
+    each boundary (host logic: no HIP call)."""
+    lib = sv.load_library()
+    MiB = 1 << 20
+    for dt, s in ((sv.SPEC_F32, 4), (sv.SPEC_BF16, 2)):
+        for V, g in ((128256, 8), (152064, 8), (32000, 5), (1000, 4), (4096, 2)):
+            b_early = -(-152 * MiB // (2 * s * V))       # least B with 2 B V s >= 152 MiB
+            b_two = -(-112 * MiB // (2 * g * s * V))     # least B with 2 g B V s >= 112 MiB
+            assert 2 * b_early * V * s >= 152 * MiB > 2 * (b_early - 1) * V * s
+            for B in (b_two - 1, b_two, b_early - 1, b_early, b_early + 1):
+                if B < 1:
+                    continue
+                want = (sv.SCHEDULE_EARLY_STOP if B >= b_early else
+                        sv.SCHEDULE_GROUP_TWO_PHASE if B >= b_two else sv.SCHEDULE_GROUP)
+                assert lib.spec_verify_schedule(B, g, V, dt, 0.8) == want, (B, g, V, dt)
+                assert lib.spec_verify_schedule(B, g, V, dt, 0.0) == sv.SCHEDULE_EARLY_STOP, (B, g, V, dt)
+            # gamma = 1: no second phase, one phase below the early stop
+            assert lib.spec_verify_schedule(b_early - 1, 1, V, dt, 0.8) == sv.SCHEDULE_GROUP
+            assert lib.spec_verify_schedule(b_early, 1, V, dt, 0.8) == sv.SCHEDULE_EARLY_STOP
+
+
 @pytest.mark.parametrize("B,gamma,V", [(INT32_MAX, 63, INT32_MAX), (1 << 24, 63, 1 << 20), (1 << 20, 8, INT32_MAX)])
 @pytest.mark.parametrize("T", [0.0, 0.8])
 def test_oversized_problems_are_rejected_before_any_hip_call(B, gamma, V, T):
